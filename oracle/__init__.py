@@ -1,0 +1,261 @@
+"""CPU oracle for the fused GEMM / implicit-GEMM convolution path.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+CPU-baseline leg of the benchmark import this package.  The product library
+(libox, package ``conv_implicit_gemm_amd``) never imports it, and the two share
+no code: this is a ctypes wrapper over ``liboxref.so`` (plain C, fp64), which
+``oracle/build.py`` compiles with gcc.
+
+Every function takes and returns numpy arrays.  Floating inputs are widened to
+float64 exactly (fp32 and bf16 values are representable in float64); the
+oracle's sums run in float64 in a fixed order.  What each function computes,
+and the passage of the pages it follows, is stated in ``oxref.h``.
+"""
+import ctypes as C
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "liboxref.so")
+
+ACT = {"none": 0, "relu": 1, "relu6": 2, "gelu": 3}
+
+OK, EARG, ESHAPE, ERANGE = 0, -1, -2, -3
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code, what):
+        super().__init__("oracle %s returned %d" % (what, code))
+        self.code = code
+
+
+class _Conv(C.Structure):
+    _fields_ = [(n, C.c_int64) for n in
+                ("N", "C", "H", "W", "M", "kH", "kW", "s_h", "s_w",
+                 "p_t", "p_l", "p_b", "p_r", "d_h", "d_w", "group")]
+
+
+_lib = None
+
+
+def lib():
+    """Load liboxref.so (building it first if it is missing)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        L = C.CDLL(_LIB_PATH)
+        P, I64, I32, D, F = C.c_void_p, C.c_int64, C.c_int32, C.c_double, C.c_float
+        sig = {
+            "oxref_set_threads": (C.c_int, [C.c_int]),
+            "oxref_get_threads": (C.c_int, []),
+            "oxref_act1": (D, [C.c_int, D]),
+            "oxref_act": (C.c_int, [C.c_int, I64, P]),
+            "oxref_matmul": (C.c_int, [I64, I64, I64, I64, P, I64, P, I64, P]),
+            "oxref_gemm": (C.c_int, [I64, I64, I64, C.c_int, C.c_int, D, P, P, D, P, C.c_int, P]),
+            "oxref_gemm_at": (C.c_int, [I64, I64, I64, C.c_int, C.c_int, D, P, P, D, P, C.c_int,
+                                        I64, P, P]),
+            "oxref_conv_out_dims": (C.c_int, [P, P, P]),
+            "oxref_conv2d": (C.c_int, [P, P, P, P, C.c_int, P]),
+            "oxref_conv2d_at": (C.c_int, [P, P, P, P, C.c_int, I64, P, P]),
+            "oxref_batchnorm": (C.c_int, [I64, I64, I64, P, P, P, P, P, D]),
+            "oxref_fold_batchnorm": (C.c_int, [I64, I64, P, P, P, P, P, P, D, P, P]),
+            "oxref_conv2d_int8": (C.c_int, [P, P, P, P, I32, F, P, F, I32, P, P]),
+            "oxref_gemm_int8": (C.c_int, [I64, I64, I64, P, P, P, I32, F, P, F, I32, P, P]),
+            "oxref_requant1": (I32, [I64, F, F, F, I32]),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def _f64(a):
+    if a is None:
+        return None
+    return np.ascontiguousarray(np.asarray(a, dtype=np.float64))
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise OracleError(rc, what)
+
+
+def set_threads(n):
+    """Set the OpenMP thread count; returns the previous maximum."""
+    return lib().oxref_set_threads(int(n))
+
+
+def get_threads():
+    return lib().oxref_get_threads()
+
+
+def act(name, v):
+    """Apply an activation to an array (float64)."""
+    v = _f64(v).copy()
+    _check(lib().oxref_act(ACT[name], v.size, _p(v)), "act")
+    return v
+
+
+def matmul(A, B):
+    """ONNX MatMul: A [batch,M,K] x B [batch,K,N] or [K,N] (broadcast) -> [batch,M,N]."""
+    A = _f64(A)
+    B = _f64(B)
+    batch, M, K = A.shape
+    if B.ndim == 2:
+        sB = 0
+        K2, N = B.shape
+    else:
+        assert B.shape[0] in (batch, 1)
+        _, K2, N = B.shape
+        sB = 0 if (B.shape[0] == 1 and batch != 1) else K2 * N
+    assert K2 == K
+    Cm = np.empty((batch, M, N), dtype=np.float64)
+    _check(lib().oxref_matmul(batch, M, N, K, _p(A), M * K, _p(B), sB, _p(Cm)), "matmul")
+    return Cm
+
+
+def gemm(A, B, bias=None, alpha=1.0, beta=1.0, transA=False, transB=False,
+         act="none", at=None):
+    """ONNX Gemm + activation.  With ``at`` (flat output indices) only those
+    outputs are computed and returned as a 1-D array."""
+    A = _f64(A)
+    B = _f64(B)
+    bias = _f64(bias)
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    L = lib()
+    if at is None:
+        Y = np.empty((M, N), dtype=np.float64)
+        _check(L.oxref_gemm(M, N, K, int(transA), int(transB), float(alpha), _p(A), _p(B),
+                            float(beta), _p(bias), ACT[act], _p(Y)), "gemm")
+        return Y
+    idx = np.ascontiguousarray(np.asarray(at, dtype=np.int64))
+    out = np.empty(idx.size, dtype=np.float64)
+    _check(L.oxref_gemm_at(M, N, K, int(transA), int(transB), float(alpha), _p(A), _p(B),
+                           float(beta), _p(bias), ACT[act], idx.size, _p(idx), _p(out)),
+           "gemm_at")
+    return out
+
+
+def conv_desc(N, Cin, H, W, M, kH, kW, stride=(1, 1), pads=(0, 0, 0, 0),
+              dilation=(1, 1), group=1):
+    """Build the oracle's conv shape.  pads are ONNX order (top, left, bottom, right)."""
+    d = _Conv()
+    d.N, d.C, d.H, d.W, d.M, d.kH, d.kW = N, Cin, H, W, M, kH, kW
+    d.s_h, d.s_w = stride
+    d.p_t, d.p_l, d.p_b, d.p_r = pads
+    d.d_h, d.d_w = dilation
+    d.group = group
+    return d
+
+
+def conv_out_dims(d):
+    ho, wo = C.c_int64(0), C.c_int64(0)
+    rc = lib().oxref_conv_out_dims(C.byref(d), C.byref(ho), C.byref(wo))
+    return rc, ho.value, wo.value
+
+
+def conv2d(X, Wt, b=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
+           group=1, act="none", at=None):
+    """ONNX Conv (direct summation) + bias + activation.  X [N,C,H,W],
+    Wt [M,C/g,kH,kW].  With ``at`` only those flat output indices."""
+    X = _f64(X)
+    Wt = _f64(Wt)
+    b = _f64(b)
+    N, Cin, H, W = X.shape
+    M, cpg, kH, kW = Wt.shape
+    assert cpg * group == Cin, "weight channels do not match C/group"
+    d = conv_desc(N, Cin, H, W, M, kH, kW, stride, pads, dilation, group)
+    rc, Ho, Wo = conv_out_dims(d)
+    _check(rc, "conv_out_dims")
+    L = lib()
+    if at is None:
+        Y = np.empty((N, M, Ho, Wo), dtype=np.float64)
+        _check(L.oxref_conv2d(C.byref(d), _p(X), _p(Wt), _p(b), ACT[act], _p(Y)), "conv2d")
+        return Y
+    idx = np.ascontiguousarray(np.asarray(at, dtype=np.int64))
+    out = np.empty(idx.size, dtype=np.float64)
+    _check(L.oxref_conv2d_at(C.byref(d), _p(X), _p(Wt), _p(b), ACT[act], idx.size, _p(idx),
+                             _p(out)), "conv2d_at")
+    return out
+
+
+def batchnorm(Y, gamma, beta, mean, var, eps=1e-5):
+    """ONNX BatchNormalization (inference) on Y [N,M,...] (returns a new array)."""
+    Y = _f64(Y).copy()
+    N, M = Y.shape[0], Y.shape[1]
+    HW = int(np.prod(Y.shape[2:])) if Y.ndim > 2 else 1
+    g, bt, mu, v = (_f64(t) for t in (gamma, beta, mean, var))
+    _check(lib().oxref_batchnorm(N, M, HW, _p(Y), _p(g), _p(bt), _p(mu), _p(v), float(eps)),
+           "batchnorm")
+    return Y
+
+
+def fold_batchnorm(Wt, gamma, beta, mean, var, eps=1e-5, b0=None):
+    """Offline BatchNorm fold in float64: returns (W', b') with W' shaped like Wt."""
+    Wt = _f64(Wt)
+    M = Wt.shape[0]
+    Kper = int(Wt.size // M)
+    g, bt, mu, v = (_f64(t) for t in (gamma, beta, mean, var))
+    b0 = _f64(b0)
+    Wo = np.empty_like(Wt)
+    bo = np.empty(M, dtype=np.float64)
+    _check(lib().oxref_fold_batchnorm(M, Kper, _p(Wt), _p(b0), _p(g), _p(bt), _p(mu), _p(v),
+                                      float(eps), _p(Wo), _p(bo)), "fold_batchnorm")
+    return Wo, bo
+
+
+def _i8(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int8))
+
+
+def conv2d_int8(Xq, Wq, bias_q, x_zp, x_s, w_s, y_s, y_zp, stride=(1, 1),
+                pads=(0, 0, 0, 0), dilation=(1, 1), group=1):
+    """Static int8 conv: returns (acc int64 [N,M,Ho,Wo], y int8 [N,M,Ho,Wo])."""
+    Xq = _i8(Xq)
+    Wq = _i8(Wq)
+    N, Cin, H, W = Xq.shape
+    M, cpg, kH, kW = Wq.shape
+    d = conv_desc(N, Cin, H, W, M, kH, kW, stride, pads, dilation, group)
+    rc, Ho, Wo = conv_out_dims(d)
+    _check(rc, "conv_out_dims")
+    bq = None if bias_q is None else np.ascontiguousarray(np.asarray(bias_q, dtype=np.int32))
+    ws = np.ascontiguousarray(np.asarray(w_s, dtype=np.float32))
+    acc = np.empty((N, M, Ho, Wo), dtype=np.int64)
+    y = np.empty((N, M, Ho, Wo), dtype=np.int8)
+    _check(lib().oxref_conv2d_int8(C.byref(d), _p(Xq), _p(Wq), _p(bq), int(x_zp),
+                                   float(np.float32(x_s)), _p(ws), float(np.float32(y_s)),
+                                   int(y_zp), _p(acc), _p(y)), "conv2d_int8")
+    return acc, y
+
+
+def gemm_int8(Xq, Wq, bias_q, x_zp, x_s, w_s, y_s, y_zp):
+    """Static int8 Gemm, X [M,K], W [N,K]: returns (acc int64 [M,N], y int8 [M,N])."""
+    Xq = _i8(Xq)
+    Wq = _i8(Wq)
+    M, K = Xq.shape
+    N = Wq.shape[0]
+    bq = None if bias_q is None else np.ascontiguousarray(np.asarray(bias_q, dtype=np.int32))
+    ws = np.ascontiguousarray(np.asarray(w_s, dtype=np.float32))
+    acc = np.empty((M, N), dtype=np.int64)
+    y = np.empty((M, N), dtype=np.int8)
+    _check(lib().oxref_gemm_int8(M, N, K, _p(Xq), _p(Wq), _p(bq), int(x_zp),
+                                 float(np.float32(x_s)), _p(ws), float(np.float32(y_s)),
+                                 int(y_zp), _p(acc), _p(y)), "gemm_int8")
+    return acc, y
+
+
+def requant1(acc, x_s, w_s, y_s, y_zp):
+    """The oracle's requantisation of a single accumulator."""
+    return lib().oxref_requant1(int(acc), float(np.float32(x_s)), float(np.float32(w_s)),
+                                float(np.float32(y_s)), int(y_zp))
