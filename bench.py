@@ -1,0 +1,371 @@
+"""Throughput of the fused GEMM / implicit-GEMM convolution path on one MI355X.
+
+A step is one pass over every layer of a workload with inputs resident in HBM:
+by default the ResNet-50-v2 convolution layers (7x7 stem, 1x1 and 3x3
+bottleneck convs of all four stages, stride-2 3x3 at stage entry) at batch 32
+in bf16 with fp32 accumulation, BatchNorm folded into the weights and a
+bias + ReLU epilogue.  Prints one JSON line: whole-job TFLOP/s (TOPS for
+int8), the roofline object of the dominant kernel (measured with HIP events
+on the launch stream inside the timed region) and the CPU oracle timed on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload resnet50|mobilenetv2|mlp|matmul|int8]
+"""
+import argparse
+import ctypes as C
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK = {"bf16": 2516.6, "f32": 157.3, "i8": 5033.0}   # dense MFMA TFLOP/s (TOPS int8)
+HBM_PEAK = 8000.0                                      # GB/s
+ESIZE = {"bf16": 2, "f32": 4, "i8": 1}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="resnet50",
+                   choices=["resnet50", "mobilenetv2", "mlp", "matmul", "int8"])
+    p.add_argument("--dtype", default=None, help="bf16 or f32 (float workloads)")
+    p.add_argument("--batch", type=int, default=None)
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="target CPU time of the oracle baseline sample (0 = skip)")
+    p.add_argument("--rows", default=None, help="write per-layer rows as JSON to this file")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------- layers --
+
+class Layer:
+    """One launch of the hot path with its algorithmic work and host inputs."""
+
+    def __init__(self, name, flops, nbytes, variant, launch, oracle_at, nout, kred):
+        self.name, self.flops, self.nbytes, self.variant = name, flops, nbytes, variant
+        self.launch = launch          # () -> status
+        self.oracle_at = oracle_at    # (idx) -> values (CPU oracle on sampled outputs)
+        self.nout, self.kred = nout, kred
+
+
+def conv_layers(ox, synth, torch, cfg, layers, dtype, stream):
+    import oracle
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    out = []
+    for li, l in enumerate(layers):
+        t = synth.conv_inputs(l, cfg, li)
+        # offline BatchNorm fold with the library's own host helper (untimed)
+        W32 = t["W"].astype(np.float32)
+        Wf, bf = ox.ox_fold_batchnorm(W32, *[t[k].astype(np.float32)
+                                             for k in ("gamma", "beta", "mean", "var")], eps=1e-5)
+        X64 = synth.round_to(t["X"], dtype)
+        Xd = torch.from_numpy(X64.astype(np.float32)).cuda().to(tdt)
+        Wd = torch.from_numpy(Wf).cuda().to(tdt)
+        bd = torch.from_numpy(bf).cuda().to(tdt)
+        ho, wo = l.out_hw()
+        Yd = torch.empty((l.N, l.M, ho, wo), dtype=tdt, device="cuda")
+        d = ox.conv_desc(l.N, l.C, l.H, l.W, l.M, l.kh, l.kw, (l.stride, l.stride), l.onnx_pads,
+                         (1, 1), l.group)
+        code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
+        act = ox.ACT[l.act]
+        args = (code, C.byref(d), Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(), act,
+                Yd.data_ptr(), stream)
+        fn = ox.lib.ox_conv2d_fused
+        variant = ox.ox_conv2d_variant(dtype, l.N, l.C, l.H, l.W, l.M, l.kh, l.kw,
+                                       (l.stride, l.stride), l.onnx_pads, (1, 1), l.group)
+        # the oracle reads the bits the GPU reads: X as rounded, W' and b' as
+        # the device holds them
+        Wh = Wd.float().cpu().numpy().astype(np.float64)
+        bh = bd.float().cpu().numpy().astype(np.float64)
+        keep = (Xd, Wd, bd, Yd, d)
+
+        def launch(fn=fn, args=args, keep=keep):
+            return fn(*args)
+
+        def oracle_at(idx, X64=X64, Wh=Wh, bh=bh, l=l):
+            return oracle.conv2d(X64, Wh, bh, (l.stride, l.stride), l.onnx_pads, (1, 1), l.group,
+                                 l.act, at=idx)
+        kred = (l.C // l.group) * l.kh * l.kw
+        out.append(Layer(l.name, l.flops(), l.nbytes(ESIZE[dtype]), variant, launch, oracle_at,
+                         l.N * l.M * ho * wo, kred))
+    return out
+
+
+def gemm_layers(ox, synth, torch, rows, dtype, stream):
+    import oracle
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    out = []
+    for li, r in enumerate(rows):
+        X, W, b = (synth.round_to(a, dtype) for a in synth.gemm_inputs(r, 1, li))
+        Xd, Wd, bd = (torch.from_numpy(a.astype(np.float32)).cuda().to(tdt) for a in (X, W, b))
+        Yd = torch.empty((r.M, r.N), dtype=tdt, device="cuda")
+        code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
+        args = (code, r.M, r.N, r.K, 0, 1, 1.0, Xd.data_ptr(), Wd.data_ptr(), 1.0, bd.data_ptr(),
+                ox.ACT[r.act], Yd.data_ptr(), None, stream)
+        keep = (Xd, Wd, bd, Yd)
+        variant = ("gemv/%s" % dtype) if r.M == 1 else ("mfma/%s" % dtype)
+
+        def launch(args=args, keep=keep):
+            return ox.lib.ox_gemm_fused(*args)
+
+        def oracle_at(idx, X=X, W=W, b=b, r=r):
+            return oracle.gemm(X, W, b, transB=True, act=r.act, at=idx)
+        nbytes = (r.M * r.K + r.N * r.K + r.N + r.M * r.N) * ESIZE[dtype]
+        out.append(Layer(r.name, 2.0 * r.M * r.N * r.K, nbytes, variant, launch, oracle_at,
+                         r.M * r.N, r.K))
+    return out
+
+
+def matmul_layers(ox, synth, torch, stream):
+    import oracle
+    A, B = synth.matmul_inputs()
+    Ad, Bd = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    Cd = torch.empty((16, 64, 64), device="cuda")
+    args = (ox.OX_F32, 16, 64, 64, 128, Ad.data_ptr(), 64 * 128, Bd.data_ptr(), 128 * 64,
+            Cd.data_ptr(), stream)
+    keep = (Ad, Bd, Cd)
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+
+    def launch(args=args, keep=keep):
+        return ox.lib.ox_matmul_batched(*args)
+
+    def oracle_at(idx):
+        return oracle.matmul(A64, B64).ravel()[idx]
+    nbytes = (A.size + B.size + 16 * 64 * 64) * 4
+    return [Layer("matmul_16x64x128x64", 2.0 * 16 * 64 * 64 * 128, nbytes, "mfma/f32", launch,
+                  oracle_at, 16 * 64 * 64, 128)]
+
+
+def int8_layers(ox, synth, torch, stream):
+    import oracle
+    out = []
+    for li, l in enumerate(synth.conformer_int8_layers()):
+        t = synth.int8_inputs(l, 4, li)
+        blk = torch.from_numpy(ox.ox_int8_prepare(t["wq"], t["w_s"], t["x_s"], t["x_zp"], t["y_s"],
+                                                  t["y_zp"], t["bias_q"])).cuda()
+        xq, wq = torch.from_numpy(t["xq"]).cuda(), torch.from_numpy(t["wq"]).cuda()
+        if l.kind == "gemm":
+            Y = torch.empty((l.M, l.N), dtype=torch.int8, device="cuda")
+            args = (ox.OX_I8, l.M, l.N, l.K, 0, 1, 1.0, xq.data_ptr(), wq.data_ptr(), 1.0, None, 0,
+                    Y.data_ptr(), blk.data_ptr(), stream)
+            fn = ox.lib.ox_gemm_fused
+            flops = 2.0 * l.M * l.N * l.K
+            nout = l.M * l.N
+            variant = "mfma/i8"
+            nbytes = l.M * l.K + l.N * l.K + l.M * l.N + 12 * l.N
+        else:
+            c = l.conv
+            ho, wo = c.out_hw()
+            Y = torch.empty((c.N, c.M, ho, wo), dtype=torch.int8, device="cuda")
+            d = ox.conv_desc(c.N, c.C, c.H, c.W, c.M, c.kh, c.kw, (c.stride, c.stride), c.onnx_pads,
+                             (1, 1), c.group)
+            args = (C.byref(d), xq.data_ptr(), wq.data_ptr(), blk.data_ptr(), ox.OX_I8,
+                    Y.data_ptr(), stream)
+            fn = ox.lib.ox_conv2d_int8
+            flops = c.flops()
+            nout = c.N * c.M * ho * wo
+            variant = ox.ox_conv2d_variant("i8", c.N, c.C, c.H, c.W, c.M, c.kh, c.kw,
+                                           (c.stride, c.stride), c.onnx_pads, (1, 1), c.group)
+            nbytes = c.nbytes(1) - c.M + 12 * c.M
+        keep = (blk, xq, wq, Y, args)
+
+        def launch(fn=fn, args=args, keep=keep):
+            return fn(*args)
+
+        def oracle_at(idx, l=l, t=t):
+            if l.kind == "gemm":
+                acc, y = oracle.gemm_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"],
+                                          t["w_s"], t["y_s"], t["y_zp"])
+            else:
+                c = l.conv
+                acc, y = oracle.conv2d_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"],
+                                            t["w_s"], t["y_s"], t["y_zp"], (c.stride, c.stride),
+                                            c.onnx_pads, (1, 1), c.group)
+            return y.ravel()[idx]
+        out.append(Layer(l.name, flops, nbytes, variant, launch, oracle_at, nout,
+                         l.K if l.kind == "gemm" else (l.conv.C // l.conv.group) * l.conv.kh * l.conv.kw))
+    return out
+
+
+# ------------------------------------------------------------ CPU baseline --
+
+def cpu_baseline(layers, seconds, int8):
+    """Time the CPU oracle on a bounded sample of every layer's outputs and
+    scale to the metric's unit (TFLOP/s or TOPS of the sampled outputs)."""
+    import oracle
+    threads = oracle.get_threads()
+    if int8:
+        # the int8 oracle has no point-sample entry: time whole small layers
+        t0 = time.perf_counter()
+        fl = 0.0
+        for L in layers:
+            if time.perf_counter() - t0 > seconds:
+                break
+            L.oracle_at(np.arange(1))
+            fl += L.flops
+        dt = time.perf_counter() - t0
+        return {"value": fl / dt / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+                "sample": "whole int8 layers in order until %.0f s of CPU time (%.1f s spent)"
+                          % (seconds, dt)}
+    macs_per_layer = 2e6
+    rng = np.random.default_rng(0)
+    for attempt in range(3):
+        t0 = time.perf_counter()
+        fl = 0.0
+        npts = 0
+        for L in layers:
+            n = max(16, int(macs_per_layer / max(1, L.kred)))
+            n = min(n, L.nout)
+            idx = rng.integers(0, L.nout, n)
+            L.oracle_at(idx)
+            fl += 2.0 * n * L.kred
+            npts += n
+        dt = time.perf_counter() - t0
+        if dt >= 0.5 * seconds or attempt == 2:
+            break
+        macs_per_layer *= min(50.0, seconds / max(dt, 1e-3))
+    return {"value": fl / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": "%d sampled outputs (about %.2g MAC per layer) over all %d layers, %.1f s"
+                      % (npts, macs_per_layer, len(layers), dt)}
+
+
+# -------------------------------------------------------------------- main --
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+              "(the per-GPU path is the same kernel at one GPU's share)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import conv_implicit_gemm_amd as ox
+    import synth
+
+    torch.cuda.set_device(0)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    wl = args.workload
+    if wl == "resnet50":
+        dtype = args.dtype or "bf16"
+        batch = args.batch or 32
+        layers = conv_layers(ox, synth, torch, 3, synth.resnet50_layers(batch), dtype, sp)
+        cfg = {"workload": "resnet50-v2 convolutions (16 layers), NCHW", "batch": batch,
+               "input": "3x224x224", "epilogue": "folded BN bias + ReLU"}
+    elif wl == "mobilenetv2":
+        dtype = args.dtype or "f32"
+        batch = args.batch or 64
+        layers = conv_layers(ox, synth, torch, 2, synth.mobilenetv2_layers(batch), dtype, sp)
+        cfg = {"workload": "mobilenetv2 convolutions (51 layers), NCHW", "batch": batch,
+               "input": "3x224x224", "epilogue": "folded BN bias + ReLU6 / linear"}
+    elif wl == "mlp":
+        dtype = args.dtype or "bf16"
+        layers = gemm_layers(ox, synth, torch, synth.mlp_rows(), dtype, sp)
+        cfg = {"workload": "MLP Gemm rows M in {1,64,256} x (1024->4096 GELU, 4096->1024, "
+                           "1024->1024 ReLU)"}
+    elif wl == "matmul":
+        dtype = "f32"
+        layers = matmul_layers(ox, synth, torch, sp)
+        cfg = {"workload": "batched MatMul [16,64,128] x [16,128,64]"}
+    else:
+        dtype = "i8"
+        layers = int8_layers(ox, synth, torch, sp)
+        cfg = {"workload": "static int8 conformer block, T=1000, d_model=1024 "
+                           "(FFN, QKV, depthwise 1-D k9, pointwise)"}
+
+    def step():
+        for L in layers:
+            st = L.launch()
+            if st != 0:
+                raise RuntimeError("%s: %s" % (L.name, ox.ox_last_error()))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # timed region: K steps, an event pair around every launch (same stream)
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in layers] for _ in range(K)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for s in range(K):
+        for i, L in enumerate(layers):
+            ev[s][i][0].record(stream)
+            st = L.launch()
+            ev[s][i][1].record(stream)
+            if st != 0:
+                raise RuntimeError("%s: %s" % (L.name, ox.ox_last_error()))
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    per_layer_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)]))
+                    for i in range(len(layers))]
+
+    step_flops = sum(L.flops for L in layers)
+    ms_per_step = total_ms / K
+    value = step_flops / (ms_per_step * 1e-3) / 1e12
+
+    # dominant kernel: the variant with the largest share of the step
+    groups = {}
+    for L, t in zip(layers, per_layer_ms):
+        g = groups.setdefault(L.variant, {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0})
+        g["ms"] += t
+        g["flops"] += L.flops
+        g["bytes"] += L.nbytes
+        g["n"] += 1
+    dom = max(groups, key=lambda k: groups[k]["ms"])
+    g = groups[dom]
+    avg_us = g["ms"] / g["n"] * 1e3
+    if dom.startswith("dw") or dom.startswith("gemv"):
+        ach = g["bytes"] / (g["ms"] * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK, "unit": "GB/s",
+                "frac": ach / HBM_PEAK, "traffic": None}
+    else:
+        ach = g["flops"] / (g["ms"] * 1e-3) / 1e12
+        pk = PEAK[dtype]
+        roof = {"bound": "mfma", "achieved": ach, "peak": pk, "unit": "TOPS" if dtype == "i8" else "TFLOP/s",
+                "frac": ach / pk, "traffic": None}
+    roof["kernel"] = dom
+    roof["launches_per_step"] = g["n"]
+    roof["avg_launch_us"] = avg_us
+
+    cpu = None
+    if args.cpu_seconds > 0:
+        cpu = cpu_baseline(layers, args.cpu_seconds, dtype == "i8")
+
+    unit = "TOPS" if dtype == "i8" else "TFLOP/s"
+    out = {
+        "metric": "TFLOP/s (TOPS int8) per fused GEMM/conv shape + % of MFMA or HBM roofline",
+        "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": ms_per_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dtype if dtype != "i8" else "int8",
+        "data": "synthetic (seeded; shapes and value distributions of the workload)",
+        "config": cfg, "roofline": roof, "cpu_baseline": cpu,
+        "host_wall_s": wall,
+    }
+    if args.rows:
+        rows = []
+        for L, t in zip(layers, per_layer_ms):
+            rows.append({"layer": L.name, "variant": L.variant, "us": t * 1e3, "flop": L.flops,
+                         "bytes": L.nbytes, "tflops": L.flops / (t * 1e-3) / 1e12,
+                         "gbs": L.nbytes / (t * 1e-3) / 1e9,
+                         "mfma_frac": L.flops / (t * 1e-3) / 1e12 / PEAK[dtype],
+                         "hbm_frac": L.nbytes / (t * 1e-3) / 1e9 / HBM_PEAK})
+        with open(args.rows, "w") as f:
+            json.dump({"workload": wl, "dtype": dtype, "rows": rows}, f, indent=1)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

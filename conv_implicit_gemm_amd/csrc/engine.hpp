@@ -1,0 +1,384 @@
+// engine.hpp -- the MFMA tile engine for gfx950.
+//
+// One kernel template computes every dense contraction of the library:
+// batched MatMul and Gemm, the 1x1 convolution and the implicit-GEMM
+// convolution ("OxiONNX 0.1.7 Released", Technical Deep Dive item 2, picks
+// among these three per shape; the implicit GEMM replaces the im2col + GEMM
+// of tensorforge's Conv milestone M3 without materialising im2col).
+//
+//   out[r][c] = epilogue( sum_k L[r][k] * R[k][c] )
+//
+// Block: 256 threads = 4 wave64s in a 2x2 grid, block tile BM x BN, each wave
+// a (BM/2) x (BN/2) tile of 16x16 MFMA blocks.  K advances in "K-units" of
+// 64 bytes per row (32 bf16, 16 fp32 or 64 int8), the depth of one
+// v_mfma_f32_16x16x32_bf16 / i32_16x16x64_i8 and of four f32_16x16x4f32.
+//
+// Both operands are staged in LDS K-contiguous per row/column, so that each
+// lane's MFMA fragment (16 consecutive bytes of K for one row or column) is a
+// single 128-bit LDS read.  Operands stored K-strided in memory (a [K, cols]
+// matrix, an NCHW image) are transposed on the way in: a thread gathers one
+// column's chunk of K with loads that are coalesced across the wave (lanes
+// take consecutive columns) and writes it to LDS as one 128-bit store.
+// Rows are padded by 16 bytes, which keeps both the 128-bit reads and the
+// column-gather writes free of LDS bank conflicts.
+//
+// Pipeline: global -> registers for stage s+1 is issued before the MFMAs of
+// stage s, registers -> LDS after them, one barrier per stage (double buffer).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "ox_internal.h"
+
+namespace ox {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kThreads = 256;
+
+template <int DT> struct Traits;
+template <> struct Traits<DT_F32> {
+  typedef float T;
+  typedef f32x4_t Acc;
+  enum { EPC = 4 };           // elements per 16-byte chunk
+};
+template <> struct Traits<DT_BF16> {
+  typedef uint16_t T;         // raw bfloat16 bits
+  typedef f32x4_t Acc;
+  enum { EPC = 8 };
+};
+template <> struct Traits<DT_I8> {
+  typedef int8_t T;
+  typedef i32x4_t Acc;
+  enum { EPC = 16 };
+};
+
+// ------------------------------------------------------------ conversions --
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float((uint32_t)b << 16);
+}
+
+// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f32(T v);
+template <> __device__ __forceinline__ float to_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f32<uint16_t>(uint16_t v) { return bf16_to_f32(v); }
+
+template <typename T, int N>
+__device__ __forceinline__ u32x4_t pack16(const T (&e)[N]) {
+  static_assert(sizeof(T) * N == 16, "a chunk is 16 bytes");
+  u32x4_t r;
+  __builtin_memcpy(&r, e, 16);
+  return r;
+}
+
+// ------------------------------------------------------------------- MFMA --
+
+template <int DT> struct Mma;
+template <> struct Mma<DT_F32> {
+  __device__ __forceinline__ static void run(f32x4_t& c, u32x4_t a, u32x4_t b) {
+    // four K=4 steps; lane group g holds k = 4g..4g+3 of the 16-k unit, and
+    // step i takes component i from A and B alike.
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[0]), __uint_as_float(b[0]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[1]), __uint_as_float(b[1]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[2]), __uint_as_float(b[2]), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[3]), __uint_as_float(b[3]), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<DT_BF16> {
+  __device__ __forceinline__ static void run(f32x4_t& c, u32x4_t a, u32x4_t b) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<DT_I8> {
+  __device__ __forceinline__ static void run(i32x4_t& c, u32x4_t a, u32x4_t b) {
+    c = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4_t, a),
+                                              __builtin_bit_cast(i32x4_t, b), c, 0, 0, 0);
+  }
+};
+
+// ------------------------------------------------------------ activations --
+
+__device__ __forceinline__ float apply_act(int act, float v) {
+  switch (act) {
+    case ACT_RELU: return fmaxf(v, 0.0f);
+    case ACT_RELU6: return fminf(fmaxf(v, 0.0f), 6.0f);
+    case ACT_GELU: return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+    default: return v;
+  }
+}
+
+// Static int8 requantisation: round half to even in fp64 (rint), add the
+// output zero point, saturate.  mult is the host-computed fp64 multiplier.
+__device__ __forceinline__ int8_t requant(int acc, double mult, int yzp) {
+  double r = rint((double)acc * mult) + (double)yzp;
+  r = fmin(fmax(r, -128.0), 127.0);
+  return (int8_t)(int)r;
+}
+
+struct I8View {
+  const double* mult;
+  const int32_t* bias;
+  int xzp, yzp;
+  __device__ __forceinline__ void init(const void* p) {
+    const Int8Header* h = (const Int8Header*)p;
+    xzp = h->x_zp;
+    yzp = h->y_zp;
+    mult = (const double*)((const char*)p + sizeof(Int8Header));
+    bias = (const int32_t*)((const char*)p + sizeof(Int8Header) + 8 * h->M);
+  }
+};
+
+// ---------------------------------------------------------------- loaders --
+//
+// Each loader owns one operand's tile for this block.  load() fetches the
+// stage starting at k0 into registers, store() writes them to the LDS stage.
+// LDS layout: row (or column) i of the tile at i*ROWB bytes, chunk ch (16
+// bytes, EPC consecutive k) at ch*16 within the row.
+
+template <int BKU> struct Lds {
+  enum { ROWB = BKU * 64 + 16, CPR = 4 * BKU };
+};
+
+// Operand stored K-contiguous: [rows, K] with row stride ld.
+template <int DT, int BROWS, int BKU>
+struct LoadRowK {
+  typedef typename Traits<DT>::T T;
+  enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         TOTAL = BROWS * CPR, NCH = (TOTAL + kThreads - 1) / kThreads };
+  const T* base;
+  int64_t ld;
+  int nrows, K;
+  bool vec;
+  u32x4_t r[NCH];
+
+  __device__ __forceinline__ void init(const T* p, int64_t ld_, int row0, int rows, int K_, bool vec_) {
+    base = p + (int64_t)row0 * ld_;
+    ld = ld_;
+    nrows = rows - row0;
+    K = K_;
+    vec = vec_;
+  }
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      const int row = q / CPR, ch = q % CPR;
+      const int k = k0 + ch * EPC;
+      u32x4_t v = {0u, 0u, 0u, 0u};
+      if ((TOTAL % kThreads == 0 || q < TOTAL) && row < nrows) {
+        const T* src = base + (int64_t)row * ld + k;
+        if (vec && k + EPC <= K) {
+          v = *(const u32x4_t*)src;
+        } else {
+          T e[EPC];
+#pragma unroll
+          for (int j = 0; j < EPC; ++j) e[j] = (k + j < K) ? src[j] : (T)0;
+          v = pack16(e);
+        }
+      }
+      r[i] = v;
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      if (TOTAL % kThreads == 0 || q < TOTAL)
+        *(u32x4_t*)(lds + (q / CPR) * ROWB + (q % CPR) * 16) = r[i];
+    }
+  }
+};
+
+// Operand stored K-strided: element k of this thread's column at
+// colbase[k*ld].  The thread keeps one column (tid % BCOLS) for the whole
+// kernel and gathers whole chunks of K for it.
+template <int DT, int BCOLS, int BKU>
+struct LoadColK {
+  typedef typename Traits<DT>::T T;
+  enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         STEP = kThreads / BCOLS,                       // chunk stride per thread
+         NCH = (CPR + STEP - 1) / STEP };
+  static_assert(kThreads % BCOLS == 0, "columns must divide the block");
+  const T* colbase;
+  int64_t ld;
+  int K;
+  bool valid;
+  u32x4_t r[NCH];
+
+  __device__ __forceinline__ void init_col(const T* cb, bool ok, int64_t ld_, int K_) {
+    colbase = cb;
+    valid = ok;
+    ld = ld_;
+    K = K_;
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      const int k = k0 + ch * EPC;
+      T e[EPC];
+#pragma unroll
+      for (int j = 0; j < EPC; ++j)
+        e[j] = (valid && (CPR % STEP == 0 || ch < CPR) && k + j < K) ? colbase[(int64_t)(k + j) * ld] : (T)0;
+      r[i] = pack16(e);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int col = threadIdx.x % BCOLS, ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = r[i];
+    }
+  }
+};
+
+// The implicit-GEMM operand of a convolution: column = one output pixel
+// (img, oh, ow), k = (c, kh, kw) in the weight's own order, element =
+// X[img, c, oh*sh - pt + kh*dh, ow*sw - pl + kw*dw], or `pad` outside the
+// image (0 for floats; x_zp for int8, whose zero-point fold expects it).
+template <int DT, int BCOLS, int BKU>
+struct LoadIm2col {
+  typedef typename Traits<DT>::T T;
+  enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         STEP = kThreads / BCOLS, NCH = (CPR + STEP - 1) / STEP };
+  const T* xb;          // X + (img*C + g*cpg) * H*W
+  int ih0, iw0;
+  bool valid;
+  int H, W, HW, kH, kW, KK, dh, dw, K;
+  T pad;
+  u32x4_t r[NCH];
+
+  __device__ __forceinline__ void load(int k0) {
+    const int ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      const int k = k0 + ch * EPC;
+      T e[EPC];
+      if (valid && (CPR % STEP == 0 || ch < CPR) && k < K) {
+        int c = k / KK;
+        int rr = k - c * KK;
+        int kh = rr / kW;
+        int kw = rr - kh * kW;
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) {
+          T v = (T)0;
+          if (k + j < K) {
+            const int ih = ih0 + kh * dh, iw = iw0 + kw * dw;
+            v = ((unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W) ? xb[c * HW + ih * W + iw] : pad;
+          }
+          e[j] = v;
+          if (++kw == kW) {
+            kw = 0;
+            if (++kh == kH) {
+              kh = 0;
+              ++c;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) e[j] = (T)0;
+      }
+      r[i] = pack16(e);
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int col = threadIdx.x % BCOLS, ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = r[i];
+    }
+  }
+};
+
+// ------------------------------------------------------------ the kernel --
+
+template <int DT, int BM, int BN> struct WaveTile {
+  enum { TM = BM / 2, TN = BN / 2, FM = TM / 16, FN = TN / 16 };
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 16x16 block");
+};
+
+// The K loop shared by every problem: accumulates into acc[FM][FN].
+template <int DT, int BM, int BN, int BKU, class LA, class LB>
+__device__ __forceinline__ void engine_mainloop(LA& la, LB& lb, int K, char* smem,
+                                                typename Traits<DT>::Acc (&acc)[BM / 32][BN / 32]) {
+  typedef WaveTile<DT, BM, BN> WT;
+  enum { ROWB = Lds<BKU>::ROWB, A_BYTES = BM * ROWB, B_BYTES = BN * ROWB,
+         KSTEP = BKU * 4 * Traits<DT>::EPC };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lg = lane >> 4;
+  const int nk = (K + KSTEP - 1) / KSTEP;
+  if (nk == 0) return;
+
+  la.load(0);
+  lb.load(0);
+  la.store(smem);
+  lb.store(smem + A_BYTES);
+  __syncthreads();
+  for (int s = 0; s < nk; ++s) {
+    char* As = smem + (s & 1) * (A_BYTES + B_BYTES);
+    char* Bs = As + A_BYTES;
+    const bool more = s + 1 < nk;
+    if (more) {
+      la.load((s + 1) * KSTEP);
+      lb.load((s + 1) * KSTEP);
+    }
+#pragma unroll
+    for (int u = 0; u < BKU; ++u) {
+      u32x4_t a[WT::FM], b[WT::FN];
+#pragma unroll
+      for (int fm = 0; fm < WT::FM; ++fm)
+        a[fm] = *(const u32x4_t*)(As + (wm * WT::TM + fm * 16 + lr) * ROWB + u * 64 + lg * 16);
+#pragma unroll
+      for (int fn = 0; fn < WT::FN; ++fn)
+        b[fn] = *(const u32x4_t*)(Bs + (wn * WT::TN + fn * 16 + lr) * ROWB + u * 64 + lg * 16);
+#pragma unroll
+      for (int fm = 0; fm < WT::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < WT::FN; ++fn) Mma<DT>::run(acc[fm][fn], a[fm], b[fn]);
+    }
+    if (more) {
+      char* An = smem + ((s + 1) & 1) * (A_BYTES + B_BYTES);
+      la.store(An);
+      lb.store(An + A_BYTES);
+    }
+    __syncthreads();
+  }
+}
+
+// Calls f(row_in_tile, col_in_tile, value) for each of this lane's results.
+// MFMA 16x16 output layout: lane l holds rows 4*(l/16)+i (i = 0..3) of column
+// l%16 of its 16x16 block.
+template <int BM, int BN, typename Acc, class F>
+__device__ __forceinline__ void for_each_result(const Acc (&acc)[BM / 32][BN / 32], F&& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int fm = 0; fm < BM / 32; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < BN / 32; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f(wm * (BM / 2) + fm * 16 + lg * 4 + i, wn * (BN / 2) + fn * 16 + lr, acc[fm][fn][i]);
+}
+
+}  // namespace ox

@@ -1,0 +1,250 @@
+// gemm_conv.hpp -- the problems the MFMA tile engine runs: Gemm / batched
+// MatMul, and convolution as a GEMM over (output channel) x (output pixel).
+// Each *.hip unit instantiates these for one input type.
+#pragma once
+
+#include <type_traits>
+
+#include "engine.hpp"
+
+namespace ox {
+
+// ------------------------------------------------------------- epilogues --
+
+// Float path: v = alpha*acc + beta*bias[ch]; activation; store as T.
+template <typename T>
+__device__ __forceinline__ void store_float(T* y, float v);
+template <> __device__ __forceinline__ void store_float<float>(float* y, float v) { *y = v; }
+template <> __device__ __forceinline__ void store_float<uint16_t>(uint16_t* y, float v) {
+  *y = f32_to_bf16(v);
+}
+
+// ----------------------------------------------------- Gemm / MatMul kernel --
+//
+// L = A' (rows = i), R = B' (cols = j).  LK: A stored [M,K]; !LK: [K,M].
+// RK: B stored [N,K] (transB); !RK: [K,N].  z = batch index.
+
+template <int DT, int BM, int BN, int BKU, bool LK, bool RK>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
+  typedef typename Traits<DT>::T T;
+  typedef typename Traits<DT>::Acc Acc;
+  enum { ROWB = Lds<BKU>::ROWB };
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
+
+  const int z = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
+  const T* L = (const T*)a.L + (int64_t)z * a.sl;
+  const T* R = (const T*)a.R + (int64_t)z * a.sr;
+
+  typename std::conditional<LK, LoadRowK<DT, BM, BKU>, LoadColK<DT, BM, BKU>>::type la;
+  typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
+  if constexpr (LK) {
+    la.init(L, a.ldl, row0, a.rows, a.K, a.l_vec);
+  } else {
+    const int r = row0 + threadIdx.x % BM;
+    la.init_col(L + r, r < a.rows, a.ldl, a.K);
+  }
+  if constexpr (RK) {
+    lb.init(R, a.ldr, col0, a.cols, a.K, a.r_vec);
+  } else {
+    const int c = col0 + threadIdx.x % BN;
+    lb.init_col(R + c, c < a.cols, a.ldr, a.K);
+  }
+
+  Acc acc[BM / 32][BN / 32];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+  engine_mainloop<DT, BM, BN, BKU>(la, lb, a.K, smem, acc);
+
+  if constexpr (DT == DT_I8) {
+    I8View q;
+    q.init(a.i8);
+    if (a.out_dt == DT_I32) {
+      int32_t* Y = (int32_t*)a.Y + (int64_t)z * a.sy;
+      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
+        const int row = row0 + r, col = col0 + c;
+        if (row < a.rows && col < a.cols) Y[(int64_t)row * a.ldy + col] = v + q.bias[col];
+      });
+    } else {
+      int8_t* Y = (int8_t*)a.Y + (int64_t)z * a.sy;
+      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
+        const int row = row0 + r, col = col0 + c;
+        if (row < a.rows && col < a.cols)
+          Y[(int64_t)row * a.ldy + col] = requant(v + q.bias[col], q.mult[col], q.yzp);
+      });
+    }
+  } else {
+    T* Y = (T*)a.Y + (int64_t)z * a.sy;
+    const T* bias = (const T*)a.bias;
+    for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+      const int row = row0 + r, col = col0 + c;
+      if (row < a.rows && col < a.cols) {
+        float o = a.alpha * v;
+        if (bias) o += a.beta * to_f32(bias[col]);
+        store_float(Y + (int64_t)row * a.ldy + col, apply_act(a.act, o));
+      }
+    });
+  }
+}
+
+template <int DT, int BM, int BN>
+int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
+  constexpr int BKU = 1;
+  dim3 grid((a.cols + BN - 1) / BN, (a.rows + BM - 1) / BM, a.batch);
+  if constexpr (DT == DT_I8) {
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, true>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if (a.l_kmajor && a.r_kmajor)
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, true>), grid, dim3(kThreads), 0, s, a);
+    else if (a.l_kmajor)
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, false>), grid, dim3(kThreads), 0, s, a);
+    else if (a.r_kmajor)
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, false, true>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, false, false>), grid, dim3(kThreads), 0, s, a);
+  }
+  return (int)hipGetLastError();
+}
+
+template <int DT>
+int launch_gemm_dt(const GemmArgs& a, int tile, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  switch (tile) {
+    case TILE_128x128: return launch_gemm_tile<DT, 128, 128>(a, s);
+    case TILE_64x128: return launch_gemm_tile<DT, 64, 128>(a, s);
+    case TILE_128x64: return launch_gemm_tile<DT, 128, 64>(a, s);
+    case TILE_64x64: return launch_gemm_tile<DT, 64, 64>(a, s);
+    case TILE_32x64: return launch_gemm_tile<DT, 32, 64>(a, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+// ------------------------------------------------------------ conv kernel --
+//
+// rows = output channels of group z (L = weights [M/g, K], K contiguous),
+// cols = output pixels over the batch, n = (img*Ho + oh)*Wo + ow.
+// KIND 0: implicit GEMM (im2col gathered on the fly); KIND 1: 1x1, stride 1,
+// no pad, where column n of image img is X[img, c, p] with p = n % (H*W).
+
+template <int DT, int BM, int BN, int BKU, int KIND>
+__global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
+  typedef typename Traits<DT>::T T;
+  typedef typename Traits<DT>::Acc Acc;
+  enum { ROWB = Lds<BKU>::ROWB };
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
+
+  const int g = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
+  const int Mpg = a.M / a.group, cpg = a.C / a.group;
+  const int KK = a.kH * a.kW, K = cpg * KK;
+  const int HoWo = a.Ho * a.Wo, HW = a.H * a.W, NP = a.N * HoWo;
+
+  I8View q;
+  if constexpr (DT == DT_I8) q.init(a.i8);
+
+  LoadRowK<DT, BM, BKU> la;
+  la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K, a.w_vec);
+
+  const int n = col0 + threadIdx.x % BN;
+  const bool nvalid = n < NP;
+  const int img = nvalid ? n / HoWo : 0;
+  const int p = nvalid ? n - img * HoWo : 0;
+  const T* xg = (const T*)a.X + ((int64_t)img * a.C + (int64_t)g * cpg) * HW;
+
+  typename std::conditional<KIND == 1, LoadColK<DT, BN, BKU>, LoadIm2col<DT, BN, BKU>>::type lb;
+  if constexpr (KIND == 1) {
+    lb.init_col(xg + p, nvalid, HW, K);
+  } else {
+    const int oh = p / a.Wo, ow = p - (p / a.Wo) * a.Wo;
+    lb.xb = xg;
+    lb.ih0 = oh * a.sh - a.pt;
+    lb.iw0 = ow * a.sw - a.pl;
+    lb.valid = nvalid;
+    lb.H = a.H;
+    lb.W = a.W;
+    lb.HW = HW;
+    lb.kH = a.kH;
+    lb.kW = a.kW;
+    lb.KK = KK;
+    lb.dh = a.dh;
+    lb.dw = a.dw;
+    lb.K = K;
+    if constexpr (DT == DT_I8) lb.pad = (T)q.xzp;
+    else lb.pad = (T)0;
+  }
+
+  Acc acc[BM / 32][BN / 32];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+
+  engine_mainloop<DT, BM, BN, BKU>(la, lb, K, smem, acc);
+
+  auto out_index = [&](int m, int col) -> int64_t {
+    const int im = col / HoWo;
+    return ((int64_t)im * a.M + m) * HoWo + (col - im * HoWo);
+  };
+  if constexpr (DT == DT_I8) {
+    if (a.out_dt == DT_I32) {
+      int32_t* Y = (int32_t*)a.Y;
+      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
+        const int ml = row0 + r, col = col0 + c;
+        if (ml < Mpg && col < NP) {
+          const int m = g * Mpg + ml;
+          Y[out_index(m, col)] = v + q.bias[m];
+        }
+      });
+    } else {
+      int8_t* Y = (int8_t*)a.Y;
+      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
+        const int ml = row0 + r, col = col0 + c;
+        if (ml < Mpg && col < NP) {
+          const int m = g * Mpg + ml;
+          Y[out_index(m, col)] = requant(v + q.bias[m], q.mult[m], q.yzp);
+        }
+      });
+    }
+  } else {
+    T* Y = (T*)a.Y;
+    const T* bias = (const T*)a.bias;
+    for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+      const int ml = row0 + r, col = col0 + c;
+      if (ml < Mpg && col < NP) {
+        const int m = g * Mpg + ml;
+        float o = v;
+        if (bias) o += to_f32(bias[m]);
+        store_float(Y + out_index(m, col), apply_act(a.act, o));
+      }
+    });
+  }
+}
+
+template <int DT, int BM, int BN>
+int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
+  constexpr int BKU = 1;
+  const int Mpg = a.M / a.group;
+  const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
+  dim3 grid((unsigned)((NP + BN - 1) / BN), (Mpg + BM - 1) / BM, a.group);
+  if (kind == 1)
+    hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 1>), grid, dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 0>), grid, dim3(kThreads), 0, s, a);
+  return (int)hipGetLastError();
+}
+
+template <int DT>
+int launch_conv_dt(const ConvArgs& a, int kind, int tile, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  switch (tile) {
+    case TILE_128x128: return launch_conv_tile<DT, 128, 128>(a, kind, s);
+    case TILE_64x128: return launch_conv_tile<DT, 64, 128>(a, kind, s);
+    case TILE_128x64: return launch_conv_tile<DT, 128, 64>(a, kind, s);
+    case TILE_64x64: return launch_conv_tile<DT, 64, 64>(a, kind, s);
+    case TILE_32x64: return launch_conv_tile<DT, 32, 64>(a, kind, s);
+    default: return (int)hipErrorInvalidValue;
+  }
+}
+
+}  // namespace ox

@@ -1,0 +1,15 @@
+// k_bf16.hip -- tile-engine instantiations for bf16 inputs (Gemm / MatMul
+// and convolution); see gemm_conv.hpp.
+#include "gemm_conv.hpp"
+
+namespace ox {
+
+int launch_gemm_bf16(const GemmArgs& a, int tile, void* stream) {
+  return launch_gemm_dt<DT_BF16>(a, tile, stream);
+}
+
+int launch_conv_bf16(const ConvArgs& a, int kind, int tile, void* stream) {
+  return launch_conv_dt<DT_BF16>(a, kind, tile, stream);
+}
+
+}  // namespace ox

@@ -1,0 +1,578 @@
+// ox_api.cpp -- the C ABI of libox: argument validation, kernel selection and
+// the offline helpers.  Pure host code (no HIP runtime call happens before an
+// argument set has passed validation), so every error path runs without a
+// GPU.
+//
+// Validation is complete before anything is enqueued, and a refusal names the
+// offending argument -- the load-time policy of onnx-vulkan-rs ("refuses at
+// load time, naming every offender") applied per call.  An unsupported
+// combination is refused, never approximated, and there is no CPU fallback
+// (the OxiONNX 0.1.7 lesson: a quiet fallback hides a wrong answer).
+//
+// Selection follows "OxiONNX 0.1.7 Released" (Technical Deep Dive, items 2
+// and 4): per shape, depthwise / 1x1 / implicit-GEMM for convolutions, a
+// matrix-vector kernel for single-row Gemms, and the MFMA tile engine with a
+// tile size chosen from the output shape for everything else.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <string>
+
+#include "../../include/ox.h"
+#include "ox_internal.h"
+
+using namespace ox;
+
+namespace {
+
+thread_local std::string g_err;
+
+ox_status fail(ox_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+ox_status ok() {
+  g_err.clear();
+  return OX_OK;
+}
+
+ox_status hip_result(const char* fn, int rc) {
+  if (rc != 0) return fail(OX_ERR_HIP, "%s: kernel launch failed (hip error %d)", fn, rc);
+  return ok();
+}
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;   // per tensor, exclusive
+
+bool too_big(int64_t a, int64_t b = 1, int64_t c = 1, int64_t d = 1) {
+  // product of non-negative factors >= 2^31, without overflowing
+  long double p = (long double)a * b * c * d;
+  return p >= (long double)kMaxElems;
+}
+
+int esize(int dt) { return dt == DT_F32 || dt == DT_I32 ? 4 : dt == DT_BF16 ? 2 : 1; }
+
+bool aligned16(const void* p) { return (((uintptr_t)p) & 15) == 0; }
+
+const char* act_name(int a) {
+  static const char* n[] = {"none", "relu", "relu6", "gelu"};
+  return (a >= 0 && a <= 3) ? n[a] : "?";
+}
+
+// OX_FORCE_KERNEL: comma-separated tokens, e.g. "igemm,tile=64x64".
+struct Force {
+  const char* variant = nullptr;   // "dw", "1x1", "igemm", "gemv", "mfma"
+  int tile = -1;
+};
+
+Force read_force() {
+  Force f;
+  static thread_local std::string buf;
+  const char* e = getenv("OX_FORCE_KERNEL");
+  if (!e || !*e) return f;
+  buf = e;
+  size_t pos = 0;
+  static thread_local std::string variant;
+  variant.clear();
+  while (pos <= buf.size()) {
+    size_t end = buf.find(',', pos);
+    if (end == std::string::npos) end = buf.size();
+    std::string tok = buf.substr(pos, end - pos);
+    if (tok.rfind("tile=", 0) == 0) {
+      for (int t = 0; t < TILE_COUNT; ++t)
+        if (tok.substr(5) == tile_name(t)) f.tile = t;
+      if (f.tile < 0) f.tile = -2;   // unknown tile name
+    } else if (!tok.empty()) {
+      variant = tok;
+    }
+    pos = end + 1;
+  }
+  if (!variant.empty()) f.variant = variant.c_str();
+  return f;
+}
+
+bool log_on() {
+  const char* e = getenv("OX_LOG");
+  return e && *e && strcmp(e, "0") != 0;
+}
+
+// Tile choice: the largest tile that still gives two blocks per CU (the 256
+// CUs of an MI355X), never a tile taller than the problem.
+int choose_tile(int64_t rows, int64_t cols, int64_t z) {
+  static const int order[] = {TILE_128x128, TILE_64x128, TILE_128x64, TILE_64x64, TILE_32x64};
+  for (int t : order) {
+    const int bm = tile_bm(t), bn = tile_bn(t);
+    if (rows <= 64 && bm > 64) continue;
+    if (rows <= 32 && bm > 32) continue;
+    const int64_t blocks = ((rows + bm - 1) / bm) * ((cols + bn - 1) / bn) * z;
+    if (blocks >= 512) return t;
+  }
+  if (rows <= 32) return TILE_32x64;
+  return TILE_64x64;
+}
+
+ox_status pick_tile(const char* fn, const Force& f, int64_t rows, int64_t cols, int64_t z,
+                    int* tile) {
+  if (f.tile == -2) return fail(OX_ERR_INVALID_ARG, "%s: OX_FORCE_KERNEL names an unknown tile", fn);
+  *tile = f.tile >= 0 ? f.tile : choose_tile(rows, cols, z);
+  if ((rows + tile_bm(*tile) - 1) / tile_bm(*tile) > 65535 || z > 65535)
+    return fail(OX_ERR_UNSUPPORTED, "%s: %lld rows x batch %lld exceed the launch grid", fn,
+                (long long)rows, (long long)z);
+  return OX_OK;
+}
+
+ox_status check_float_dt(const char* fn, ox_dtype t) {
+  if (t != OX_F32 && t != OX_BF16)
+    return fail(OX_ERR_UNSUPPORTED, "%s: dtype %d is not OX_F32 or OX_BF16", fn, (int)t);
+  return OX_OK;
+}
+
+ox_status check_act(const char* fn, ox_act a) {
+  if ((int)a < 0 || (int)a > 3) return fail(OX_ERR_INVALID_ARG, "%s: unknown activation %d", fn, (int)a);
+  return OX_OK;
+}
+
+// ---------------------------------------------------------------- conv ----
+
+ox_status check_conv_desc(const char* fn, const ox_conv_desc* d, int64_t* Ho, int64_t* Wo) {
+  if (!d) return fail(OX_ERR_INVALID_ARG, "%s: d is NULL", fn);
+  if (d->N < 0) return fail(OX_ERR_INVALID_ARG, "%s: N=%lld < 0", fn, (long long)d->N);
+  const struct { const char* n; int64_t v; } pos[] = {
+      {"C", d->C}, {"H", d->H}, {"W", d->W}, {"M", d->M}, {"kH", d->kH}, {"kW", d->kW},
+      {"s_h", d->s_h}, {"s_w", d->s_w}, {"d_h", d->d_h}, {"d_w", d->d_w}, {"group", d->group}};
+  for (auto& p : pos)
+    if (p.v < 1) return fail(OX_ERR_INVALID_ARG, "%s: %s=%lld must be >= 1", fn, p.n, (long long)p.v);
+  const struct { const char* n; int64_t v; } pads[] = {
+      {"p_t", d->p_t}, {"p_l", d->p_l}, {"p_b", d->p_b}, {"p_r", d->p_r}};
+  for (auto& p : pads)
+    if (p.v < 0) return fail(OX_ERR_INVALID_ARG, "%s: %s=%lld must be >= 0", fn, p.n, (long long)p.v);
+  if (d->C % d->group)
+    return fail(OX_ERR_SHAPE, "%s: group=%lld does not divide C=%lld", fn, (long long)d->group,
+                (long long)d->C);
+  if (d->M % d->group)
+    return fail(OX_ERR_SHAPE, "%s: group=%lld does not divide M=%lld", fn, (long long)d->group,
+                (long long)d->M);
+  const int64_t lim = (int64_t)1 << 24;   // geometry limits keep kernel index math in int32
+  if (d->H >= lim || d->W >= lim || d->kH >= lim || d->kW >= lim || d->s_h >= lim ||
+      d->s_w >= lim || d->d_h >= lim || d->d_w >= lim || d->p_t >= lim || d->p_l >= lim ||
+      d->p_b >= lim || d->p_r >= lim)
+    return fail(OX_ERR_UNSUPPORTED, "%s: a size, stride, pad or dilation is >= 2^24", fn);
+  const int64_t eh = d->d_h * (d->kH - 1) + 1, ew = d->d_w * (d->kW - 1) + 1;
+  const int64_t sh = d->H + d->p_t + d->p_b - eh, sw = d->W + d->p_l + d->p_r - ew;
+  *Ho = sh < 0 ? 0 : sh / d->s_h + 1;
+  *Wo = sw < 0 ? 0 : sw / d->s_w + 1;
+  if (*Ho < 1 || *Wo < 1)
+    return fail(OX_ERR_SHAPE,
+                "%s: output size %lldx%lld < 1 (input %lldx%lld, pads %lld,%lld,%lld,%lld, "
+                "dilated kernel %lldx%lld)",
+                fn, (long long)*Ho, (long long)*Wo, (long long)d->H, (long long)d->W,
+                (long long)d->p_t, (long long)d->p_l, (long long)d->p_b, (long long)d->p_r,
+                (long long)eh, (long long)ew);
+  if (too_big(d->N, d->C, d->H, d->W)) return fail(OX_ERR_UNSUPPORTED, "%s: X has >= 2^31 elements", fn);
+  if (too_big(d->M, d->C / d->group, d->kH, d->kW))
+    return fail(OX_ERR_UNSUPPORTED, "%s: W has >= 2^31 elements", fn);
+  if (too_big(d->N, d->M, *Ho, *Wo)) return fail(OX_ERR_UNSUPPORTED, "%s: Y has >= 2^31 elements", fn);
+  return OX_OK;
+}
+
+ConvArgs conv_args(int dt, const ox_conv_desc* d, int64_t Ho, int64_t Wo, const void* X,
+                   const void* W, const void* bias, void* Y, int act) {
+  ConvArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dt = dt;
+  a.out_dt = dt;
+  a.N = (int)d->N;
+  a.C = (int)d->C;
+  a.H = (int)d->H;
+  a.W = (int)d->W;
+  a.M = (int)d->M;
+  a.kH = (int)d->kH;
+  a.kW = (int)d->kW;
+  a.sh = (int)d->s_h;
+  a.sw = (int)d->s_w;
+  a.pt = (int)d->p_t;
+  a.pl = (int)d->p_l;
+  a.dh = (int)d->d_h;
+  a.dw = (int)d->d_w;
+  a.group = (int)d->group;
+  a.Ho = (int)Ho;
+  a.Wo = (int)Wo;
+  a.X = X;
+  a.Wt = W;
+  a.bias = bias;
+  a.Y = Y;
+  a.act = act;
+  const int64_t K = (d->C / d->group) * d->kH * d->kW;
+  a.w_vec = aligned16(W) && (K * esize(dt)) % 16 == 0;
+  a.x_vec = aligned16(X) && (d->H * d->W * esize(dt)) % 16 == 0;
+  return a;
+}
+
+enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2 };
+
+ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, const Force& f,
+                      int* kind) {
+  const bool is_dw = d->group == d->C && d->group == d->M;
+  const bool is_1x1 = d->kH == 1 && d->kW == 1 && d->s_h == 1 && d->s_w == 1 && d->p_t == 0 &&
+                      d->p_l == 0 && d->p_b == 0 && d->p_r == 0 && d->group == 1;
+  if (f.variant) {
+    if (!strcmp(f.variant, "dw")) {
+      if (!is_dw) return fail(OX_ERR_UNSUPPORTED, "%s: forced 'dw' but group != C or C != M", fn);
+      if (!depthwise_fits(a))
+        return fail(OX_ERR_UNSUPPORTED, "%s: forced 'dw' but the row band does not fit LDS", fn);
+      *kind = KIND_DW;
+    } else if (!strcmp(f.variant, "1x1")) {
+      if (!is_1x1) return fail(OX_ERR_UNSUPPORTED, "%s: forced '1x1' on a conv that is not 1x1/s1/p0/g1", fn);
+      *kind = KIND_1X1;
+    } else if (!strcmp(f.variant, "igemm")) {
+      *kind = KIND_IGEMM;
+    } else {
+      return fail(OX_ERR_INVALID_ARG, "%s: OX_FORCE_KERNEL variant '%s' does not apply to Conv", fn,
+                  f.variant);
+    }
+    return OX_OK;
+  }
+  if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
+  else if (is_1x1) *kind = KIND_1X1;
+  else *kind = KIND_IGEMM;
+  return OX_OK;
+}
+
+}  // namespace
+
+// The stream-aware body of both convolution entry points.
+static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& a, void* stream) {
+  const Force f = read_force();
+  int kind;
+  ox_status st = select_conv(fn, d, a, f, &kind);
+  if (st) return st;
+  int tile = -1;
+  if (kind != KIND_DW) {
+    st = pick_tile(fn, f, d->M / d->group, d->N * a.Ho * a.Wo, d->group, &tile);
+    if (st) return st;
+  } else if (f.tile != -1) {
+    return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to the depthwise kernel", fn);
+  }
+  if (log_on())
+    fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s\n",
+            fn, a.dt, a.N, a.C, a.H, a.W, a.M, a.kH, a.kW, a.sh, a.sw, a.group, act_name(a.act),
+            kind == KIND_DW ? "dw" : kind == KIND_1X1 ? "1x1" : "igemm", tile >= 0 ? " tile=" : "",
+            tile >= 0 ? tile_name(tile) : "");
+  if (d->N == 0) return ok();
+  int rc;
+  if (kind == KIND_DW) {
+    rc = launch_conv_depthwise(a, stream);
+  } else {
+    const int k = kind == KIND_1X1 ? 1 : 0;
+    rc = a.dt == DT_F32 ? launch_conv_f32(a, k, tile, stream)
+       : a.dt == DT_BF16 ? launch_conv_bf16(a, k, tile, stream)
+                         : launch_conv_i8(a, k, tile, stream);
+  }
+  return hip_result(fn, rc);
+}
+
+// ------------------------------------------------------------------ API ----
+
+extern "C" {
+
+const char* ox_last_error(void) { return g_err.c_str(); }
+
+const char* ox_version(void) { return "ox 0.1.0 (gfx950)"; }
+
+ox_status ox_matmul_batched(ox_dtype t, int64_t batch, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t sA, const void* B, int64_t sB, void* C,
+                            void* stream) {
+  const char* fn = "ox_matmul_batched";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  if (batch < 0 || M < 0 || N < 0 || K < 0)
+    return fail(OX_ERR_INVALID_ARG, "%s: negative size (batch=%lld M=%lld N=%lld K=%lld)", fn,
+                (long long)batch, (long long)M, (long long)N, (long long)K);
+  if (batch > 1 && sA < M * K)
+    return fail(OX_ERR_INVALID_ARG, "%s: sA=%lld < M*K=%lld", fn, (long long)sA, (long long)(M * K));
+  if (batch > 1 && sB != 0 && sB < K * N)
+    return fail(OX_ERR_INVALID_ARG, "%s: sB=%lld is neither 0 (broadcast) nor >= K*N=%lld", fn,
+                (long long)sB, (long long)(K * N));
+  if (sA < 0 || sB < 0) return fail(OX_ERR_INVALID_ARG, "%s: negative batch stride", fn);
+  if (too_big(M, K) || too_big(K, N) || too_big(batch, M, N) ||
+      (batch > 1 && (too_big(sA, batch) || too_big(sB, batch))))
+    return fail(OX_ERR_UNSUPPORTED, "%s: a tensor has >= 2^31 elements", fn);
+  if (batch == 0 || M == 0 || N == 0) return ok();
+  if (!C) return fail(OX_ERR_INVALID_ARG, "%s: C is NULL", fn);
+  if (K > 0 && (!A || !B)) return fail(OX_ERR_INVALID_ARG, "%s: %s is NULL", fn, A ? "B" : "A");
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dt = a.out_dt = (int)t;
+  a.rows = (int)M;
+  a.cols = (int)N;
+  a.K = (int)K;
+  a.batch = (int)batch;
+  a.L = A;
+  a.ldl = K;
+  a.sl = sA;
+  a.l_kmajor = 1;
+  a.R = B;
+  a.ldr = N;
+  a.sr = sB;
+  a.r_kmajor = 0;
+  a.Y = C;
+  a.ldy = N;
+  a.sy = M * N;
+  a.alpha = 1.0f;
+  a.beta = 0.0f;
+  a.act = ACT_NONE;
+  const int es = esize(t);
+  a.l_vec = aligned16(A) && (K * es) % 16 == 0 && (sA * es) % 16 == 0;
+  a.r_vec = 0;
+  const Force f = read_force();
+  if (f.variant && strcmp(f.variant, "mfma"))
+    return fail(OX_ERR_UNSUPPORTED, "%s: OX_FORCE_KERNEL variant '%s' does not apply to MatMul", fn,
+                f.variant);
+  int tile;
+  st = pick_tile(fn, f, M, N, batch, &tile);
+  if (st) return st;
+  if (log_on())
+    fprintf(stderr, "[ox] %s dt=%d batch=%lld M=%lld N=%lld K=%lld sB=%lld -> mfma tile=%s\n", fn,
+            (int)t, (long long)batch, (long long)M, (long long)N, (long long)K, (long long)sB,
+            tile_name(tile));
+  const int rc = t == OX_F32 ? launch_gemm_f32(a, tile, stream) : launch_gemm_bf16(a, tile, stream);
+  return hip_result(fn, rc);
+}
+
+ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA, int transB,
+                        float alpha, const void* A, const void* B, float beta, const void* bias,
+                        ox_act act, void* Y, const void* int8_params, void* stream) {
+  const char* fn = "ox_gemm_fused";
+  const bool i8 = t == OX_I8 || t == OX_I32;
+  if (!i8) {
+    ox_status st = check_float_dt(fn, t);
+    if (st) return st;
+  }
+  ox_status st = check_act(fn, act);
+  if (st) return st;
+  if (M < 0 || N < 0 || K < 0)
+    return fail(OX_ERR_INVALID_ARG, "%s: negative size (M=%lld N=%lld K=%lld)", fn, (long long)M,
+                (long long)N, (long long)K);
+  if ((transA != 0 && transA != 1) || (transB != 0 && transB != 1))
+    return fail(OX_ERR_INVALID_ARG, "%s: transA/transB must be 0 or 1", fn);
+  if (!isfinite(alpha) || !isfinite(beta))
+    return fail(OX_ERR_INVALID_ARG, "%s: alpha and beta must be finite", fn);
+  if (too_big(M, K) || too_big(K, N) || too_big(M, N))
+    return fail(OX_ERR_UNSUPPORTED, "%s: a tensor has >= 2^31 elements", fn);
+  if (i8) {
+    if (transA != 0 || transB != 1)
+      return fail(OX_ERR_UNSUPPORTED, "%s: int8 Gemm needs transA=0 and transB=1 (W stored [N,K])", fn);
+    if (bias) return fail(OX_ERR_INVALID_ARG, "%s: int8 Gemm takes its int32 bias in int8_params; bias must be NULL", fn);
+    if (alpha != 1.0f || beta != 1.0f)
+      return fail(OX_ERR_UNSUPPORTED, "%s: int8 Gemm needs alpha = beta = 1", fn);
+    if (act != OX_ACT_NONE) return fail(OX_ERR_UNSUPPORTED, "%s: int8 Gemm takes no activation", fn);
+    if (!int8_params) return fail(OX_ERR_INVALID_ARG, "%s: int8_params is NULL", fn);
+  } else if (int8_params) {
+    return fail(OX_ERR_INVALID_ARG, "%s: int8_params must be NULL for a float Gemm", fn);
+  }
+  if (M == 0 || N == 0) return ok();
+  if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
+  if (K > 0 && (!A || !B)) return fail(OX_ERR_INVALID_ARG, "%s: %s is NULL", fn, A ? "B" : "A");
+
+  GemmArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dt = i8 ? DT_I8 : (int)t;
+  a.out_dt = (int)t;
+  a.rows = (int)M;
+  a.cols = (int)N;
+  a.K = (int)K;
+  a.batch = 1;
+  a.L = A;
+  a.l_kmajor = transA ? 0 : 1;
+  a.ldl = transA ? M : K;
+  a.R = B;
+  a.r_kmajor = transB ? 1 : 0;
+  a.ldr = transB ? K : N;
+  a.Y = Y;
+  a.ldy = N;
+  a.bias = bias;
+  a.alpha = alpha;
+  a.beta = beta;
+  a.act = (int)act;
+  a.i8 = int8_params;
+  const int es = esize(a.dt);
+  a.l_vec = aligned16(A) && (a.ldl * es) % 16 == 0;
+  a.r_vec = aligned16(B) && (a.ldr * es) % 16 == 0;
+
+  const Force f = read_force();
+  bool gemv = !i8 && M == 1;
+  if (f.variant) {
+    if (!strcmp(f.variant, "gemv")) {
+      if (i8 || M != 1) return fail(OX_ERR_UNSUPPORTED, "%s: forced 'gemv' needs a float Gemm with M=1", fn);
+      gemv = true;
+    } else if (!strcmp(f.variant, "mfma")) {
+      gemv = false;
+    } else {
+      return fail(OX_ERR_INVALID_ARG, "%s: OX_FORCE_KERNEL variant '%s' does not apply to Gemm", fn,
+                  f.variant);
+    }
+  }
+  if (gemv) {
+    if (f.tile != -1) return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to gemv", fn);
+    if (log_on())
+      fprintf(stderr, "[ox] %s dt=%d M=1 N=%lld K=%lld transB=%d act=%s -> gemv\n", fn, (int)t,
+              (long long)N, (long long)K, transB, act_name(act));
+    return hip_result(fn, launch_gemv(a, stream));
+  }
+  int tile;
+  st = pick_tile(fn, f, M, N, 1, &tile);
+  if (st) return st;
+  if (log_on())
+    fprintf(stderr, "[ox] %s dt=%d M=%lld N=%lld K=%lld tA=%d tB=%d act=%s -> mfma tile=%s\n", fn,
+            (int)t, (long long)M, (long long)N, (long long)K, transA, transB, act_name(act),
+            tile_name(tile));
+  const int rc = i8 ? launch_gemm_i8(a, tile, stream)
+               : t == OX_F32 ? launch_gemm_f32(a, tile, stream)
+                             : launch_gemm_bf16(a, tile, stream);
+  return hip_result(fn, rc);
+}
+
+ox_status ox_conv2d_fused(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                          const void* bias, ox_act act, void* Y, void* stream) {
+  const char* fn = "ox_conv2d_fused";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  st = check_act(fn, act);
+  if (st) return st;
+  int64_t Ho, Wo;
+  st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  if (d->N > 0) {
+    if (!X) return fail(OX_ERR_INVALID_ARG, "%s: X is NULL", fn);
+    if (!W) return fail(OX_ERR_INVALID_ARG, "%s: W is NULL", fn);
+    if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
+  }
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, X, W, bias, Y, (int)act);
+  return conv_dispatch(fn, d, a, stream);
+}
+
+ox_status ox_conv2d_int8(const ox_conv_desc* d, const int8_t* Xq, const int8_t* Wq,
+                         const void* int8_params, ox_dtype y_type, void* Y, void* stream) {
+  const char* fn = "ox_conv2d_int8";
+  if (y_type != OX_I8 && y_type != OX_I32)
+    return fail(OX_ERR_UNSUPPORTED, "%s: y_type %d is not OX_I8 or OX_I32", fn, (int)y_type);
+  int64_t Ho, Wo;
+  ox_status st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  if (!int8_params) return fail(OX_ERR_INVALID_ARG, "%s: int8_params is NULL", fn);
+  if (d->N > 0) {
+    if (!Xq) return fail(OX_ERR_INVALID_ARG, "%s: Xq is NULL", fn);
+    if (!Wq) return fail(OX_ERR_INVALID_ARG, "%s: Wq is NULL", fn);
+    if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
+  }
+  ConvArgs a = conv_args(DT_I8, d, Ho, Wo, Xq, Wq, nullptr, Y, ACT_NONE);
+  a.out_dt = (int)y_type;
+  a.i8 = int8_params;
+  return conv_dispatch(fn, d, a, stream);
+}
+
+ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_t cap) {
+  const char* fn = "ox_conv2d_variant";
+  if (t != OX_F32 && t != OX_BF16 && t != OX_I8)
+    return fail(OX_ERR_UNSUPPORTED, "%s: dtype %d is not OX_F32, OX_BF16 or OX_I8", fn, (int)t);
+  if (!name || cap == 0) return fail(OX_ERR_INVALID_ARG, "%s: name is NULL or cap is 0", fn);
+  int64_t Ho, Wo;
+  ox_status st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, nullptr, nullptr, nullptr, nullptr, ACT_NONE);
+  const Force f = read_force();
+  int kind;
+  st = select_conv(fn, d, a, f, &kind);
+  if (st) return st;
+  int tile = -1;
+  if (kind != KIND_DW) {
+    st = pick_tile(fn, f, d->M / d->group, d->N * Ho * Wo, d->group, &tile);
+    if (st) return st;
+  }
+  static const char* dtn[] = {"f32", "bf16", "i8"};
+  snprintf(name, cap, "%s/%s%s%s", kind == KIND_DW ? "dw" : kind == KIND_1X1 ? "1x1" : "igemm",
+           dtn[(int)t], tile >= 0 ? "/" : "", tile >= 0 ? tile_name(tile) : "");
+  return ok();
+}
+
+ox_status ox_fold_batchnorm(int64_t M, int64_t Kper, const float* W, const float* b0,
+                            const float* gamma, const float* beta, const float* mean,
+                            const float* var, float eps, float* W_out, float* b_out) {
+  const char* fn = "ox_fold_batchnorm";
+  if (M < 0 || Kper < 0) return fail(OX_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (M == 0) return ok();
+  if (!gamma || !beta || !mean || !var || !b_out)
+    return fail(OX_ERR_INVALID_ARG, "%s: gamma, beta, mean, var and b_out must not be NULL", fn);
+  if (Kper > 0 && (!W || !W_out)) return fail(OX_ERR_INVALID_ARG, "%s: W or W_out is NULL", fn);
+  if (!(eps >= 0.0f) || !isfinite(eps)) return fail(OX_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", fn);
+  for (int64_t m = 0; m < M; ++m) {
+    const double den = (double)var[m] + (double)eps;
+    if (!(den > 0.0))
+      return fail(OX_ERR_INVALID_ARG, "%s: var[%lld] + eps = %g is not > 0", fn, (long long)m, den);
+  }
+  for (int64_t m = 0; m < M; ++m) {
+    const double scale = (double)gamma[m] / sqrt((double)var[m] + (double)eps);
+    const double shift = (double)beta[m] - (double)mean[m] * scale;
+    for (int64_t k = 0; k < Kper; ++k) W_out[m * Kper + k] = (float)(scale * (double)W[m * Kper + k]);
+    b_out[m] = (float)(scale * (b0 ? (double)b0[m] : 0.0) + shift);
+  }
+  return ok();
+}
+
+size_t ox_int8_params_bytes(int64_t M) {
+  if (M < 0) return 0;
+  return sizeof(Int8Header) + (size_t)M * (sizeof(double) + sizeof(int32_t));
+}
+
+ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const float* w_scale,
+                          float x_scale, int32_t x_zp, float y_scale, int32_t y_zp,
+                          const int32_t* bias_q, void* params_host_out) {
+  const char* fn = "ox_int8_prepare";
+  if (M < 0 || Kper < 0) return fail(OX_ERR_INVALID_ARG, "%s: negative size", fn);
+  if (!params_host_out) return fail(OX_ERR_INVALID_ARG, "%s: params_host_out is NULL", fn);
+  if (M > 0 && !w_scale) return fail(OX_ERR_INVALID_ARG, "%s: w_scale is NULL", fn);
+  if (M > 0 && Kper > 0 && !Wq_host) return fail(OX_ERR_INVALID_ARG, "%s: Wq_host is NULL", fn);
+  if (x_zp < -128 || x_zp > 127) return fail(OX_ERR_INVALID_ARG, "%s: x_zp=%d outside [-128,127]", fn, x_zp);
+  if (y_zp < -128 || y_zp > 127) return fail(OX_ERR_INVALID_ARG, "%s: y_zp=%d outside [-128,127]", fn, y_zp);
+  if (!(x_scale > 0.0f) || !isfinite(x_scale)) return fail(OX_ERR_INVALID_ARG, "%s: x_scale must be finite and > 0", fn);
+  if (!(y_scale > 0.0f) || !isfinite(y_scale)) return fail(OX_ERR_INVALID_ARG, "%s: y_scale must be finite and > 0", fn);
+  for (int64_t m = 0; m < M; ++m)
+    if (!(w_scale[m] > 0.0f) || !isfinite(w_scale[m]))
+      return fail(OX_ERR_INVALID_ARG, "%s: w_scale[%lld] must be finite and > 0", fn, (long long)m);
+  if (Kper > 66000)
+    return fail(OX_ERR_UNSUPPORTED, "%s: Kper=%lld > 66000 could overflow the int32 accumulator", fn,
+                (long long)Kper);
+  char* out = (char*)params_host_out;
+  Int8Header h;
+  memset(&h, 0, sizeof(h));
+  h.magic = kInt8Magic;
+  h.version = 1;
+  h.M = M;
+  h.x_zp = x_zp;
+  h.y_zp = y_zp;
+  memcpy(out, &h, sizeof(h));
+  double* mult = (double*)(out + sizeof(Int8Header));
+  int32_t* bfold = (int32_t*)(out + sizeof(Int8Header) + 8 * M);
+  for (int64_t m = 0; m < M; ++m) {
+    int64_t wsum = 0;
+    for (int64_t k = 0; k < Kper; ++k) wsum += Wq_host[m * Kper + k];
+    const int64_t bf = (bias_q ? (int64_t)bias_q[m] : 0) - (int64_t)x_zp * wsum;
+    if (bf >= ((int64_t)1 << 31) || bf < -((int64_t)1 << 31))
+      return fail(OX_ERR_UNSUPPORTED, "%s: folded bias of channel %lld overflows int32", fn, (long long)m);
+    const double mm = ((double)x_scale * (double)w_scale[m]) / (double)y_scale;
+    memcpy(mult + m, &mm, sizeof(double));
+    const int32_t b32 = (int32_t)bf;
+    memcpy(bfold + m, &b32, sizeof(int32_t));
+  }
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,107 @@
+// ox_internal.h -- launch descriptions shared by the C-ABI front end
+// (ox_api.cpp, host only) and the kernel translation units (*.hip).
+//
+// The front end validates every argument and picks a kernel variant before
+// any of these structures reaches a launcher; launchers trust them.
+#pragma once
+
+#include <stdint.h>
+
+namespace ox {
+
+// storage types (same values as ox_dtype)
+enum Dt : int { DT_F32 = 0, DT_BF16 = 1, DT_I8 = 2, DT_I32 = 3 };
+
+// activations (same values as ox_act)
+enum Act : int { ACT_NONE = 0, ACT_RELU = 1, ACT_RELU6 = 2, ACT_GELU = 3 };
+
+// Tile shapes of the MFMA tile engine (block tile BM x BN, 4 waves in 2x2).
+enum Tile : int {
+  TILE_128x128 = 0,
+  TILE_64x128 = 1,
+  TILE_128x64 = 2,
+  TILE_64x64 = 3,
+  TILE_32x64 = 4,
+  TILE_COUNT = 5
+};
+
+inline int tile_bm(int t) {
+  static const int v[TILE_COUNT] = {128, 64, 128, 64, 32};
+  return v[t];
+}
+inline int tile_bn(int t) {
+  static const int v[TILE_COUNT] = {128, 128, 64, 64, 64};
+  return v[t];
+}
+inline const char* tile_name(int t) {
+  static const char* v[TILE_COUNT] = {"128x128", "64x128", "128x64", "64x64", "32x64"};
+  return v[t];
+}
+
+// Layout of the int8 parameter block (device copy of ox_int8_prepare's
+// output): a 32-byte header, then mult[M] (fp64), then bias_fold[M] (int32).
+struct Int8Header {
+  int32_t magic;       // 'OXI8'
+  int32_t version;     // 1
+  int64_t M;
+  int32_t x_zp;
+  int32_t y_zp;
+  int64_t reserved;
+};
+static_assert(sizeof(Int8Header) == 32, "int8 header is 32 bytes");
+constexpr int32_t kInt8Magic = 0x3849584F;  // "OXI8" little-endian
+
+// A GEMM on the tile engine: rows x cols output, reduction K, batch in z.
+//   out[z][r][c] = epi( sum_k L[z][r][k] * R[z][k][c] )
+// L: rows operand; l_kmajor = 1 when stored [rows, K] (K contiguous, row
+//    stride ldl), 0 when stored [K, rows] (rows contiguous, k stride ldl).
+// R: cols operand; r_kmajor = 1 when stored [cols, K] (K contiguous, col
+//    stride ldr), 0 when stored [K, cols] (cols contiguous, k stride ldr).
+struct GemmArgs {
+  int dt;                 // input type: DT_F32, DT_BF16 or DT_I8
+  int out_dt;             // DT_F32/DT_BF16 (= dt) or DT_I8/DT_I32 for int8 input
+  int rows, cols, K, batch;
+  const void* L; int64_t ldl, sl; int l_kmajor;
+  const void* R; int64_t ldr, sr; int r_kmajor;
+  void* Y; int64_t ldy, sy;
+  const void* bias;       // [cols] or null (float path)
+  float alpha, beta;
+  int act;
+  const void* i8;         // int8 parameter block (int8 path), channel = col
+  int l_vec, r_vec;       // 16-byte vector loads allowed for a K-major operand
+};
+
+// A convolution (NCHW) on the tile engine: rows = output channels of one
+// group, cols = N*Ho*Wo output pixels, K = C/group * kH * kW, group in z.
+struct ConvArgs {
+  int dt;                 // DT_F32, DT_BF16 or DT_I8
+  int out_dt;
+  int N, C, H, W, M, kH, kW, sh, sw, pt, pl, dh, dw, group, Ho, Wo;
+  const void* X;
+  const void* Wt;         // [M, C/group, kH, kW]
+  const void* bias;       // [M] or null (float path)
+  void* Y;
+  int act;
+  const void* i8;         // int8 parameter block, channel = m
+  int w_vec;              // weight rows allow 16-byte vector loads
+  int x_vec;              // (1x1 only) pixel rows allow 16-byte loads
+};
+
+// Launchers (return a hipError_t as int).  `stream` is a hipStream_t.
+// One translation unit per input type keeps the builds parallel.
+int launch_gemm_f32(const GemmArgs& a, int tile, void* stream);
+int launch_gemm_bf16(const GemmArgs& a, int tile, void* stream);
+int launch_gemm_i8(const GemmArgs& a, int tile, void* stream);
+// kind: 0 = implicit GEMM (any kernel / stride / pad / dilation / group),
+//       1 = 1x1 stride-1 unpadded convolution (a per-image GEMM on NCHW).
+int launch_conv_f32(const ConvArgs& a, int kind, int tile, void* stream);
+int launch_conv_bf16(const ConvArgs& a, int kind, int tile, void* stream);
+int launch_conv_i8(const ConvArgs& a, int kind, int tile, void* stream);
+// depthwise (group == C == M), VALU only
+int launch_conv_depthwise(const ConvArgs& a, void* stream);
+// whether the depthwise kernel's LDS band fits this geometry (host only)
+bool depthwise_fits(const ConvArgs& a);
+// Gemm with a single output row (M = 1): memory-bound, no MFMA
+int launch_gemv(const GemmArgs& a, void* stream);
+
+}  // namespace ox

@@ -1,0 +1,184 @@
+/*
+ * ox.h -- C ABI of libox, a fused GEMM / implicit-GEMM convolution library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The library computes the path that ONNX runtimes share for their heaviest
+ * operators: ONNX MatMul (batched) and Gemm, and ONNX Conv lowered to an
+ * implicit GEMM, each with a fused epilogue -- a bias (usually a BatchNorm
+ * folded offline into the weights), then ReLU, ReLU6 or GELU -- and a static
+ * int8 path with int32 accumulation and round-half-to-even requantisation.
+ *
+ * Conventions shared by every call below:
+ *   - Tensors are dense, row-major (ONNX / NCHW).  Element sizes: fp32 4 B,
+ *     bf16 2 B (raw bfloat16 bits), int8 1 B, int32 4 B.
+ *   - Pointers named as DEVICE pointers are caller-owned device memory that
+ *     must stay valid until the work enqueued on `stream` completes.  The
+ *     library keeps no reference after returning, allocates no memory,
+ *     creates no streams or events and holds no global mutable state beyond a
+ *     per-thread error message.  Calls are re-entrant.
+ *   - `stream` is a hipStream_t passed as void*; NULL means the default
+ *     stream.  Hot-path calls are asynchronous: they validate every argument
+ *     on the host, enqueue kernels on `stream` and return.  Nothing is
+ *     enqueued when validation fails.
+ *   - Any pointer alignment is accepted: kernels pick the widest vector
+ *     access the pointers and strides permit.
+ *   - Every tensor must hold fewer than 2^31 elements (OX_ERR_UNSUPPORTED
+ *     otherwise).  Empty tensors (a zero dimension) are accepted and enqueue
+ *     nothing (except a Gemm with K = 0, which still writes act(beta*bias)).
+ *   - Errors: a non-zero ox_status; ox_last_error() then names the offending
+ *     argument.  A failing HIP launch returns OX_ERR_HIP; device faults
+ *     surface at the caller's next synchronisation.  There is no fallback:
+ *     an unsupported combination is refused, never approximated.
+ *   - OX_FORCE_KERNEL=<variant> in the environment forces a kernel variant
+ *     where it is applicable (for A/B measurements); OX_LOG=1 prints the
+ *     selected variant of each call to stderr.
+ */
+#ifndef OX_H
+#define OX_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OX_OK = 0,
+  OX_ERR_INVALID_ARG = 1,   /* null pointer, negative size, unknown enum */
+  OX_ERR_SHAPE = 2,         /* shapes that do not fit together (e.g. output size < 1) */
+  OX_ERR_UNSUPPORTED = 3,   /* valid ONNX, but not a combination this library runs */
+  OX_ERR_HIP = 4            /* a HIP runtime call failed */
+} ox_status;
+
+typedef enum { OX_F32 = 0, OX_BF16 = 1, OX_I8 = 2, OX_I32 = 3 } ox_dtype;
+
+/* Fused activations.  ReLU = max(v,0); ReLU6 = min(max(v,0),6) (the clamp the
+ * Kyanite README "Optimizer" section merges relu/min/max into); GELU is the
+ * exact erf form 0.5*v*(1+erf(v/sqrt(2))) (the Gelu composite of the Onyxia
+ * README). */
+typedef enum { OX_ACT_NONE = 0, OX_ACT_RELU = 1, OX_ACT_RELU6 = 2, OX_ACT_GELU = 3 } ox_act;
+
+/* ONNX Conv geometry.  Input X [N, C, H, W], weights [M, C/group, kH, kW],
+ * output Y [N, M, Ho, Wo] with
+ *   Ho = floor((H + p_t + p_b - d_h*(kH-1) - 1) / s_h) + 1   (Wo likewise).
+ * Pads are explicit, in the ONNX order [top, left, bottom, right], and may be
+ * asymmetric; auto_pad is the caller's to resolve. */
+typedef struct {
+  int64_t N, C, H, W;
+  int64_t M, kH, kW;
+  int64_t s_h, s_w;
+  int64_t p_t, p_l, p_b, p_r;
+  int64_t d_h, d_w;
+  int64_t group;
+} ox_conv_desc;
+
+/* ---------------------------------------------------------------- hot path */
+
+/* ONNX MatMul, batched ("True batched MatMul/Gemm dispatch" of "OxiONNX 0.1.7
+ * Released": one launch for the whole batch, not one per batch element).
+ *   C[b,i,j] = sum_k A[b,i,k] * B[b',k,j],  b' = b, or 0 when sB == 0.
+ * t: OX_F32 or OX_BF16 (A, B and C all of type t; fp32 accumulation).
+ * A: DEVICE [batch, M, K], batch stride sA elements (sA >= M*K; A rows dense).
+ * B: DEVICE [batch, K, N], batch stride sB = 0 (broadcast) or >= K*N.
+ * C: DEVICE [batch, M, N], dense, written in full. */
+ox_status ox_matmul_batched(ox_dtype t, int64_t batch, int64_t M, int64_t N, int64_t K,
+                            const void* A, int64_t sA, const void* B, int64_t sB,
+                            void* C, void* stream);
+
+/* ONNX Gemm with a fused activation (the GEMM-epilogue fusion of the
+ * tensorforge "Status" table and "ResNet fusion" paragraph; transposed
+ * inputs and scalar operands as in the Kyanite "Cuda Executor" section):
+ *   Y[i,j] = act(alpha * sum_k A'[i,k] * B'[k,j] + beta * bias[j])
+ * A' = A^T when transA (A stored [K,M]) else A ([M,K]);
+ * B' = B^T when transB (B stored [N,K]) else B ([K,N]).
+ * t = OX_F32 / OX_BF16: A, B, bias and Y of type t, fp32 accumulation; bias
+ *   is DEVICE [N] or NULL; int8_params must be NULL.
+ * t = OX_I8 / OX_I32: static int8 (QLinearMatMul with an int32 bias):
+ *   A = x_q DEVICE int8 [M,K] (transA = 0), B = w_q DEVICE int8 [N,K]
+ *   (transB = 1), int8_params = DEVICE block made by ox_int8_prepare for N
+ *   channels, bias = NULL, alpha = beta = 1, act = OX_ACT_NONE.
+ *   OX_I8 writes requantised int8 Y [M,N]; OX_I32 writes the int32
+ *   accumulators acc[i,j] = bias_q[j] + sum_k (x_q[i,k] - x_zp) * w_q[j,k]. */
+ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA, int transB,
+                        float alpha, const void* A, const void* B, float beta,
+                        const void* bias, ox_act act, void* Y, const void* int8_params,
+                        void* stream);
+
+/* ONNX Conv + bias + activation, float path (Conv -> BatchNorm -> Relu folded
+ * into one fused convolution, tensorforge "ResNet fusion"; per-shape choice
+ * of an implicit-GEMM, a 1x1 and a depthwise kernel, "OxiONNX 0.1.7
+ * Released", Technical Deep Dive item 2):
+ *   Y[n,m,oh,ow] = act(bias[m] + sum_{c,kh,kw} X[n, g*C/group + c, ih, iw] * W[m,c,kh,kw])
+ *   ih = oh*s_h - p_t + kh*d_h, iw = ow*s_w - p_l + kw*d_w (zero outside),
+ *   g = m / (M/group).
+ * t: OX_F32 or OX_BF16 (X, W, bias, Y all of type t; fp32 accumulation).
+ * X: DEVICE [N,C,H,W]; W: DEVICE [M, C/group, kH, kW] (ONNX layout, e.g. the
+ * output of ox_fold_batchnorm); bias: DEVICE [M] or NULL; Y: DEVICE
+ * [N,M,Ho,Wo], written in full.  No im2col buffer is ever materialised. */
+ox_status ox_conv2d_fused(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                          const void* bias, ox_act act, void* Y, void* stream);
+
+/* Static int8 ONNX Conv (QLinearConv with an int32 bias, symmetric
+ * per-output-channel weights, per-tensor activation scale and zero point;
+ * onnx-vulkan-rs feature list, "Static int8 (QOperator)"):
+ *   acc[n,m,oh,ow] = bias_q[m] + sum over in-bounds taps (x_q - x_zp) * w_q
+ *   y = clamp(rint(acc * mult[m]) + y_zp, -128, 127),
+ *   mult[m] = ((double)x_s * (double)w_s[m]) / (double)y_s, rint half-to-even.
+ * Xq: DEVICE int8 [N,C,H,W]; Wq: DEVICE int8 [M, C/group, kH, kW];
+ * int8_params: DEVICE block from ox_int8_prepare for these weights;
+ * y_type: OX_I8 (requantised int8 Y) or OX_I32 (the int32 accumulators);
+ * Y: DEVICE [N,M,Ho,Wo]. */
+ox_status ox_conv2d_int8(const ox_conv_desc* d, const int8_t* Xq, const int8_t* Wq,
+                         const void* int8_params, ox_dtype y_type, void* Y, void* stream);
+
+/* The kernel variant ox_conv2d_fused (t = OX_F32 / OX_BF16) or ox_conv2d_int8
+ * (t = OX_I8) would launch for this geometry, as "<kind>/<dtype>[/<tile>]"
+ * with kind dw, 1x1 or igemm (e.g. "igemm/bf16/64x128"), honouring
+ * OX_FORCE_KERNEL.  Host only, enqueues nothing; the shape choice follows the
+ * per-shape selection of "OxiONNX 0.1.7 Released" (Technical Deep Dive, item
+ * 2).  name: HOST buffer of cap bytes (NUL-terminated, truncated to fit). */
+ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_t cap);
+
+/* ------------------------------------------------- offline, host, untimed */
+
+/* BatchNorm fold (tensorforge "ResNet fusion": W' = scale*W, bias = shift;
+ * Kyanite "Optimizer": consecutive affine ops merged into one scale + bias,
+ * division by a constant replaced by a multiplication).  Host memory, fp64
+ * arithmetic, fp32 results:
+ *   scale[m] = gamma[m] / sqrt(var[m] + eps);  shift[m] = beta[m] - mean[m]*scale[m]
+ *   W_out[m,k] = scale[m]*W[m,k];  b_out[m] = scale[m]*b0[m] + shift[m]
+ * W, W_out: HOST [M, Kper]; b0: HOST [M] or NULL (zero); gamma, beta, mean,
+ * var, b_out: HOST [M].  W_out may alias W. */
+ox_status ox_fold_batchnorm(int64_t M, int64_t Kper, const float* W, const float* b0,
+                            const float* gamma, const float* beta, const float* mean,
+                            const float* var, float eps, float* W_out, float* b_out);
+
+/* Size in bytes of the int8 parameter block for M output channels
+ * (a 32-byte header, then 8 B fp64 multiplier + 4 B folded int32 bias per
+ * channel). */
+size_t ox_int8_params_bytes(int64_t M);
+
+/* Prepare the int8 parameter block on the host, once per layer.  Host fp64:
+ *   mult[m]      = ((double)x_scale * (double)w_scale[m]) / (double)y_scale
+ *   bias_fold[m] = bias_q[m] - x_zp * sum_k Wq[m,k]
+ * The fold is the zero-point correction of the onnx-vulkan-rs design notes
+ * with a weight zero point of 0; the kernels therefore pad with x_zp.
+ * Wq_host: HOST int8 [M, Kper]; w_scale: HOST [M] (> 0); bias_q: HOST [M] or
+ * NULL; x_zp, y_zp in [-128, 127]; scales finite and > 0.
+ * params_host_out: HOST, ox_int8_params_bytes(M) bytes; the caller copies it
+ * to the device and passes that copy to the int8 calls. */
+ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const float* w_scale,
+                          float x_scale, int32_t x_zp, float y_scale, int32_t y_zp,
+                          const int32_t* bias_q, void* params_host_out);
+
+/* The message of the last failing call on this thread ("" if none). */
+const char* ox_last_error(void);
+
+/* Library version string. */
+const char* ox_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

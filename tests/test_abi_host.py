@@ -1,0 +1,216 @@
+"""Host-side tests of libox (no GPU needed): the library loads and exports every
+symbol include/ox.h declares; every validation error is reported before
+anything is enqueued (these calls never reach the HIP runtime); the offline
+helpers (BatchNorm fold, int8 parameter block) match the oracle or their
+definitions."""
+import ctypes as C
+import os
+import re
+import struct
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ox():
+    import conv_implicit_gemm_amd as ox
+    return ox
+
+
+def header_symbols():
+    src = open(os.path.join(ROOT, "include", "ox.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ox_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(ox):
+    syms = header_symbols()
+    assert set(syms) == set(ox.EXPORTS), syms
+    for s in syms:
+        assert hasattr(ox.lib, s), s
+    assert ox.ox_version().startswith("ox ")
+
+
+def test_package_has_no_oracle_dependency():
+    pkg = os.path.join(ROOT, "conv_implicit_gemm_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower().replace("no oracle", ""), f
+                assert "oxref" not in text, f
+
+
+# ------------------------------------------------------------ error paths --
+
+def raw(ox):
+    return ox.lib
+
+
+def desc(ox, **kw):
+    base = dict(N=1, Cin=4, H=8, W=8, M=8, kH=3, kW=3, stride=(1, 1), pads=(1, 1, 1, 1),
+                dilation=(1, 1), group=1)
+    base.update(kw)
+    return ox.conv_desc(base["N"], base["Cin"], base["H"], base["W"], base["M"], base["kH"],
+                        base["kW"], base["stride"], base["pads"], base["dilation"], base["group"])
+
+
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(group=3), 2, "group=3 does not divide C=4"),
+    (dict(Cin=4, M=6, group=4), 2, "does not divide M=6"),
+    (dict(H=2, W=2, kH=5, kW=5, pads=(0, 0, 0, 0)), 2, "output size"),
+    (dict(kH=0), 1, "kH=0"),
+    (dict(stride=(0, 1)), 1, "s_h=0"),
+    (dict(dilation=(1, 0)), 1, "d_w=0"),
+    (dict(pads=(0, -1, 0, 0)), 1, "p_l=-1"),
+    (dict(N=-1), 1, "N=-1"),
+    (dict(H=1 << 24), 3, "2^24"),
+    (dict(N=1 << 20, Cin=1 << 12, H=1, W=1, kH=1, kW=1, pads=(0, 0, 0, 0)), 3, "X has >= 2^31"),
+])
+def test_conv_shape_errors(ox, kw, status, needle):
+    d = desc(ox, **kw)
+    st = raw(ox).ox_conv2d_fused(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None)
+    assert st == status and needle in ox.ox_last_error(), ox.ox_last_error()
+
+
+def test_conv_argument_errors(ox):
+    L = raw(ox)
+    d = desc(ox)
+    assert L.ox_conv2d_fused(ox.OX_I8, C.byref(d), FAKE, FAKE, None, 0, FAKE, None) == 3
+    assert L.ox_conv2d_fused(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 7, FAKE, None) == 1
+    assert "activation" in ox.ox_last_error()
+    assert L.ox_conv2d_fused(ox.OX_F32, None, FAKE, FAKE, None, 0, FAKE, None) == 1
+    for args, name in (((None, FAKE, FAKE), "X"), ((FAKE, None, FAKE), "W"), ((FAKE, FAKE, None), "Y")):
+        st = L.ox_conv2d_fused(ox.OX_BF16, C.byref(d), args[0], args[1], None, 0, args[2], None)
+        assert st == 1 and ("%s is NULL" % name) in ox.ox_last_error()
+    # int8 entry
+    assert L.ox_conv2d_int8(C.byref(d), FAKE, FAKE, None, ox.OX_I8, FAKE, None) == 1
+    assert "int8_params" in ox.ox_last_error()
+    assert L.ox_conv2d_int8(C.byref(d), FAKE, FAKE, FAKE, ox.OX_F32, FAKE, None) == 3
+
+
+def test_forced_variant_must_apply(ox, monkeypatch):
+    L = raw(ox)
+    d = desc(ox)   # a 3x3 conv, not depthwise
+    monkeypatch.setenv("OX_FORCE_KERNEL", "dw")
+    assert L.ox_conv2d_fused(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None) == 3
+    monkeypatch.setenv("OX_FORCE_KERNEL", "1x1")
+    assert L.ox_conv2d_fused(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None) == 3
+    monkeypatch.setenv("OX_FORCE_KERNEL", "gemv")
+    assert L.ox_conv2d_fused(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None) == 1
+    monkeypatch.setenv("OX_FORCE_KERNEL", "igemm,tile=7x7")
+    assert L.ox_conv2d_fused(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None) == 1
+    assert "unknown tile" in ox.ox_last_error()
+    monkeypatch.setenv("OX_FORCE_KERNEL", "gemv")
+    st = L.ox_gemm_fused(ox.OX_F32, 4, 8, 8, 0, 1, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, None, None)
+    assert st == 3 and "M=1" in ox.ox_last_error()
+
+
+def test_gemm_argument_errors(ox):
+    L = raw(ox)
+    g = L.ox_gemm_fused
+    assert g(ox.OX_F32, -1, 4, 4, 0, 0, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, None, None) == 1
+    assert g(ox.OX_F32, 4, 4, 4, 2, 0, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, None, None) == 1
+    assert g(ox.OX_F32, 4, 4, 4, 0, 0, float("inf"), FAKE, FAKE, 1.0, None, 0, FAKE, None, None) == 1
+    assert g(ox.OX_F32, 4, 4, 4, 0, 0, 1.0, None, FAKE, 1.0, None, 0, FAKE, None, None) == 1
+    assert "A is NULL" in ox.ox_last_error()
+    assert g(ox.OX_F32, 4, 4, 4, 0, 0, 1.0, FAKE, FAKE, 1.0, None, 0, None, None, None) == 1
+    assert g(ox.OX_F32, 4, 4, 4, 0, 0, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, FAKE, None) == 1
+    assert "int8_params must be NULL" in ox.ox_last_error()
+    # int8 constraints
+    assert g(ox.OX_I8, 4, 4, 4, 0, 0, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, FAKE, None) == 3
+    assert "transB=1" in ox.ox_last_error()
+    assert g(ox.OX_I8, 4, 4, 4, 0, 1, 1.0, FAKE, FAKE, 1.0, FAKE, 0, FAKE, FAKE, None) == 1
+    assert g(ox.OX_I8, 4, 4, 4, 0, 1, 2.0, FAKE, FAKE, 1.0, None, 0, FAKE, FAKE, None) == 3
+    assert g(ox.OX_I8, 4, 4, 4, 0, 1, 1.0, FAKE, FAKE, 1.0, None, 1, FAKE, FAKE, None) == 3
+    assert g(ox.OX_I8, 4, 4, 4, 0, 1, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, None, None) == 1
+    assert g(ox.OX_F32, 1 << 16, 1 << 16, 4, 0, 0, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, None, None) == 3
+
+
+def test_matmul_argument_errors(ox):
+    L = raw(ox)
+    m = L.ox_matmul_batched
+    assert m(ox.OX_I8, 2, 4, 4, 4, FAKE, 16, FAKE, 16, FAKE, None) == 3
+    assert m(ox.OX_F32, 2, 4, 4, 4, FAKE, 8, FAKE, 16, FAKE, None) == 1
+    assert "sA=8" in ox.ox_last_error()
+    assert m(ox.OX_F32, 2, 4, 4, 4, FAKE, 16, FAKE, 5, FAKE, None) == 1
+    assert m(ox.OX_F32, 2, 4, 4, 4, FAKE, 16, FAKE, 16, None, None) == 1
+
+
+def test_empty_shapes_enqueue_nothing_and_succeed(ox):
+    L = raw(ox)
+    # zero-sized outputs return OX_OK without touching any pointer or the GPU
+    assert L.ox_matmul_batched(ox.OX_F32, 0, 4, 4, 4, None, 16, None, 16, None, None) == 0
+    assert L.ox_matmul_batched(ox.OX_F32, 3, 0, 4, 4, None, 0, None, 16, None, None) == 0
+    assert L.ox_gemm_fused(ox.OX_F32, 0, 4, 4, 0, 0, 1.0, None, None, 1.0, None, 0, None, None, None) == 0
+    d = desc(ox, N=0)
+    assert L.ox_conv2d_fused(ox.OX_F32, C.byref(d), None, None, None, 0, None, None) == 0
+
+
+# --------------------------------------------------------- offline helpers --
+
+def test_fold_batchnorm_matches_oracle_fold(ox):
+    layer = synth.ConvLayer("t", 1, 16, 5, 5, 24, 3, 1, 1, 1, "relu")
+    t = synth.conv_inputs(layer, 3, 5)
+    W32 = t["W"].astype(np.float32)
+    prm = [t[k].astype(np.float32) for k in ("gamma", "beta", "mean", "var")]
+    b0 = np.random.default_rng(0).standard_normal(24).astype(np.float32)
+    Wg, bg = ox.ox_fold_batchnorm(W32, *prm, eps=1e-5, b0=b0)
+    Wr, br = oracle.fold_batchnorm(W32.astype(np.float64), *[p.astype(np.float64) for p in prm],
+                                   eps=float(np.float32(1e-5)), b0=b0.astype(np.float64))
+    # the library folds in fp64 and rounds once to fp32
+    assert np.array_equal(Wg, Wr.astype(np.float32))
+    assert np.array_equal(bg, br.astype(np.float32))
+
+
+def test_fold_batchnorm_errors(ox):
+    L = raw(ox)
+    z = np.zeros(4, np.float32)
+    var = np.array([1, 1, -2, 1], np.float32)
+    st = L.ox_fold_batchnorm(4, 3, np.zeros(12, np.float32).ctypes.data, None, z.ctypes.data,
+                             z.ctypes.data, z.ctypes.data, var.ctypes.data, 1e-5,
+                             np.zeros(12, np.float32).ctypes.data, np.zeros(4, np.float32).ctypes.data)
+    assert st == 1 and "var[2]" in ox.ox_last_error()
+
+
+def test_int8_params_block_layout(ox):
+    r = np.random.default_rng(1)
+    M, K = 6, 37
+    wq = r.integers(-127, 128, (M, K)).astype(np.int8)
+    ws = r.uniform(1e-3, 1e-2, M).astype(np.float32)
+    bq = r.integers(-5000, 5000, M).astype(np.int32)
+    xs, ys, xzp, yzp = np.float32(0.05), np.float32(0.7), -9, 4
+    blk = ox.ox_int8_prepare(wq, ws, xs, xzp, ys, yzp, bq)
+    assert blk.size == ox.ox_int8_params_bytes(M) == 32 + 12 * M
+    magic, ver, m, xz, yz = struct.unpack_from("<iiqii", blk.tobytes(), 0)
+    assert (magic, ver, m, xz, yz) == (0x3849584F, 1, M, xzp, yzp)
+    mult = np.frombuffer(blk.tobytes(), np.float64, M, 32)
+    bfold = np.frombuffer(blk.tobytes(), np.int32, M, 32 + 8 * M)
+    # multiplier: ((double)x_s * (double)w_s) / (double)y_s, as the oracle defines it
+    assert np.array_equal(mult, (np.float64(xs) * ws.astype(np.float64)) / np.float64(ys))
+    # zero-point fold: bias_q - x_zp * sum_k w
+    assert np.array_equal(bfold, bq.astype(np.int64) - xzp * wq.astype(np.int64).sum(1))
+    # and the fold reproduces the oracle's accumulator on a Gemm
+    x = r.integers(-128, 128, (5, K)).astype(np.int8)
+    acc, _ = oracle.gemm_int8(x, wq, bq, xzp, xs, ws, ys, yzp)
+    folded = x.astype(np.int64) @ wq.astype(np.int64).T + bfold[None, :]
+    assert np.array_equal(acc, folded)
+
+
+def test_int8_prepare_errors(ox):
+    wq = np.zeros((2, 3), np.int8)
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(wq, [0.01, 0.0], 0.1, 0, 0.2, 0)       # w_scale 0
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(wq, [0.01, 0.01], 0.1, 200, 0.2, 0)    # x_zp out of range
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(wq, [0.01, 0.01], float("nan"), 0, 0.2, 0)

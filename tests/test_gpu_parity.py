@@ -1,0 +1,387 @@
+"""GPU parity: libox's HIP kernels against the CPU oracle, element by element
+on the same seeded inputs (the rule and tolerances are in tests/parity.py).
+
+Small shapes are compared in full; the full-size workload layers are
+compared on a seeded sample of outputs plus the head and ragged tail, after
+checking that no output was left at its NaN sentinel."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from parity import assert_close, sample_indices
+
+torch = pytest.importorskip("torch")
+
+pytestmark = [pytest.mark.gpu,
+              pytest.mark.skipif(not torch.cuda.is_available(), reason="needs a GPU")]
+
+
+@pytest.fixture(scope="module")
+def ox():
+    import conv_implicit_gemm_amd as ox
+    return ox
+
+
+def say(*a):
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+TD = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def dev(a64, dtype):
+    """float64 numpy holding values exact in `dtype` -> device tensor."""
+    return torch.from_numpy(np.ascontiguousarray(a64, dtype=np.float32)).to("cuda").to(TD[dtype])
+
+
+def host64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def nan_like(shape, dtype):
+    return torch.full(shape, float("nan"), dtype=TD[dtype], device="cuda")
+
+
+# ------------------------------------------------------------------ MatMul --
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_all_ones_64_cube_every_element_is_64(ox, dtype):
+    # "OxiONNX 0.1.7 Released": the 64x64x64 all-ones MatMul that its
+    # two-stream race returned with 3456 of 4096 elements reading 0.0.  Here
+    # the output starts as NaN, the call runs on a non-default stream, and only
+    # that stream is synchronised.
+    say("all-ones 64^3", dtype)
+    A = torch.ones((1, 64, 64), dtype=TD[dtype], device="cuda")
+    s = torch.cuda.Stream()
+    Cm = nan_like((1, 64, 64), dtype)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        ox.ox_matmul_batched(A, A, Cm, stream=s)
+        Y = nan_like((64, 64), dtype)
+        ox.ox_gemm_fused(A[0], A[0], transB=True, Y=Y, stream=s)
+    s.synchronize()
+    assert torch.all(Cm == 64).item() and torch.all(Y == 64).item()
+
+
+def test_matmul_c0_seeded_against_oracle(ox):
+    say("C0 batched matmul [16,64,128]x[16,128,64] f32")
+    A, B = synth.matmul_inputs()
+    Cg = ox.ox_matmul_batched(dev(A, "f32"), dev(B, "f32"))
+    torch.cuda.synchronize()
+    assert_close(host64(Cg), oracle.matmul(A, B), "f32", "C0")
+
+
+@pytest.mark.parametrize("shape", [(3, 37, 53, 71), (1, 1, 1, 1), (2, 130, 5, 300), (5, 64, 129, 16)])
+@pytest.mark.parametrize("bcast", [False, True])
+def test_matmul_integer_inputs_are_exact(ox, shape, bcast):
+    batch, M, N, K = shape
+    say("matmul exact", shape, "bcast", bcast)
+    r = np.random.default_rng(sum(shape) + bcast)
+    A = r.integers(-3, 4, (batch, M, K)).astype(np.float64)
+    B = r.integers(-3, 4, (1 if bcast else batch, K, N)).astype(np.float64)
+    Cg = ox.ox_matmul_batched(dev(A, "f32"), dev(B, "f32"))
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(Cg), oracle.matmul(A, B))
+    Cb = ox.ox_matmul_batched(dev(A, "bf16"), dev(B, "bf16"))
+    torch.cuda.synchronize()
+    ref = oracle.matmul(A, B)
+    # |sums| < 256 are exact in bf16
+    exact = np.abs(ref) < 256
+    assert np.array_equal(host64(Cb)[exact], ref[exact])
+
+
+# -------------------------------------------------------------------- Gemm --
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("act", ["none", "relu", "gelu", "relu6"])
+def test_gemm_layouts_and_scalars(ox, dtype, ta, tb, act):
+    M, N, K = 77, 45, 133
+    say("gemm", dtype, ta, tb, act)
+    r = np.random.default_rng(100 + 8 * ta + 4 * tb + len(act))
+    A = synth.round_to(r.standard_normal((K, M) if ta else (M, K)), dtype)
+    B = synth.round_to(r.standard_normal((N, K) if tb else (K, N)) / math.sqrt(K), dtype)
+    bias = synth.round_to(r.uniform(-1, 1, N), dtype)
+    Y = nan_like((M, N), dtype)
+    ox.ox_gemm_fused(dev(A, dtype), dev(B, dtype), dev(bias, dtype), alpha=0.5, beta=-2.0,
+                     transA=bool(ta), transB=bool(tb), act=act, Y=Y)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(A, B, bias, 0.5, -2.0, ta, tb, act)
+    assert_close(host64(Y), ref, dtype, "gemm")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("tb", [0, 1])
+@pytest.mark.parametrize("force", [None, "mfma"])
+def test_gemm_single_row(ox, dtype, tb, force, monkeypatch):
+    if force:
+        monkeypatch.setenv("OX_FORCE_KERNEL", force)
+    M, N, K = 1, 1000, 777
+    say("gemm M=1", dtype, tb, force)
+    r = np.random.default_rng(7 + tb)
+    A = synth.round_to(r.standard_normal((M, K)), dtype)
+    B = synth.round_to(r.standard_normal((N, K) if tb else (K, N)) / math.sqrt(K), dtype)
+    bias = synth.round_to(r.uniform(-0.1, 0.1, N), dtype)
+    Y = nan_like((M, N), dtype)
+    ox.ox_gemm_fused(dev(A, dtype), dev(B, dtype), dev(bias, dtype), transB=bool(tb), act="gelu", Y=Y)
+    torch.cuda.synchronize()
+    assert_close(host64(Y), oracle.gemm(A, B, bias, transB=tb, act="gelu"), dtype, "gemv")
+
+
+def test_gemm_empty_reduction_writes_activation_of_bias(ox):
+    say("gemm K=0")
+    bias = np.array([-1.0, 0.5, 7.0], np.float64)
+    Y = nan_like((4, 3), "f32")
+    A = torch.empty((4, 0), device="cuda")
+    B = torch.empty((3, 0), device="cuda")
+    ox.ox_gemm_fused(A, B, dev(bias, "f32"), beta=1.0, transB=True, act="relu6", Y=Y)
+    torch.cuda.synchronize()
+    assert np.array_equal(host64(Y), np.broadcast_to(oracle.act("relu6", bias), (4, 3)))
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_c1_mlp_rows(ox, dtype):
+    for li, row in enumerate(synth.mlp_rows()):
+        say("C1", row.name, dtype)
+        X, W, b = synth.gemm_inputs(row, 1, li)
+        X, W, b = (synth.round_to(t, dtype) for t in (X, W, b))
+        Y = nan_like((row.M, row.N), dtype)
+        ox.ox_gemm_fused(dev(X, dtype), dev(W, dtype), dev(b, dtype), transB=True, act=row.act, Y=Y)
+        torch.cuda.synchronize()
+        assert not torch.isnan(Y).any().item()
+        idx = sample_indices(row.M * row.N, 3000, li)
+        ref = oracle.gemm(X, W, b, transB=True, act=row.act, at=idx)
+        assert_close(host64(Y).ravel()[idx], ref, dtype, row.name)
+
+
+# -------------------------------------------------------------------- Conv --
+
+def conv_case_ok(N, Cin, H, W, M, kH, kW, s, pads, d, g):
+    rc, Ho, Wo = oracle.conv_out_dims(oracle.conv_desc(N, Cin, H, W, M, kH, kW, s, pads, d, g))
+    return rc == 0
+
+
+def sweep(n, seed):
+    from test_oracle_pins import sweep_cases
+    return [c for c in sweep_cases(n, seed) if conv_case_ok(*c[:11])]
+
+
+def run_conv(ox, X, Wt, b, dtype, s, pads, d, g, act):
+    ho, wo = ox.conv_out_hw(X.shape[2], X.shape[3], Wt.shape[2], Wt.shape[3], s, pads, d)
+    Y = nan_like((X.shape[0], Wt.shape[0], ho, wo), dtype)
+    ox.ox_conv2d_fused(dev(X, dtype), dev(Wt, dtype), None if b is None else dev(b, dtype),
+                       s, pads, d, g, act, Y=Y)
+    torch.cuda.synchronize()
+    return Y
+
+
+def test_conv_sweep_integer_inputs_exact(ox):
+    # fp32 with small integer inputs: every partial sum is exact, so any
+    # indexing mistake (tap, pad, stride, dilation, group) shows as a mismatch.
+    cases = sweep(400, 77)
+    for ci, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act) in enumerate(cases):
+        act = "relu6" if act == "gelu" else act
+        r = np.random.default_rng(ci)
+        X = r.integers(-3, 4, (N, Cin, H, W)).astype(np.float64)
+        Wt = r.integers(-2, 3, (M, Cin // g, kH, kW)).astype(np.float64)
+        b = r.integers(-4, 5, M).astype(np.float64)
+        say("conv sweep", ci, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act))
+        Y = run_conv(ox, X, Wt, b, "f32", s, pads, d, g, act)
+        ref = oracle.conv2d(X, Wt, b, s, pads, d, g, act)
+        assert np.array_equal(host64(Y), ref), (ci, N, Cin, H, W, M, kH, kW, s, pads, d, g, act)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_sweep_random_inputs(ox, dtype):
+    cases = sweep(250, 4242)
+    for ci, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act) in enumerate(cases):
+        r = np.random.default_rng(1000 + ci)
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), dtype)
+        Wt = synth.round_to(r.standard_normal((M, Cin // g, kH, kW)) / math.sqrt(kH * kW * Cin // g), dtype)
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), dtype)
+        say("conv sweep", dtype, ci, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act))
+        Y = run_conv(ox, X, Wt, b, dtype, s, pads, d, g, act)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, pads, d, g, act), dtype, str(ci))
+
+
+@pytest.mark.parametrize("force", [None, "dw", "igemm"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("geom", [
+    (2, 24, 19, 23, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1)),
+    (1, 40, 17, 18, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1)),
+    (1, 16, 1, 50, 1, 9, (1, 1), (0, 4, 0, 4), (1, 1)),
+    (3, 8, 13, 11, 5, 3, (2, 1), (2, 0, 1, 2), (2, 1)),
+])
+def test_depthwise_variants(ox, force, dtype, geom, monkeypatch):
+    if force:
+        monkeypatch.setenv("OX_FORCE_KERNEL", force)
+    N, Cc, H, W, kH, kW, s, pads, d = geom
+    say("depthwise", geom, dtype, force)
+    r = np.random.default_rng(H * W + Cc)
+    X = synth.round_to(r.standard_normal((N, Cc, H, W)), dtype)
+    Wt = synth.round_to(r.standard_normal((Cc, 1, kH, kW)) / 3.0, dtype)
+    b = synth.round_to(r.uniform(-0.5, 0.5, Cc), dtype)
+    Y = run_conv(ox, X, Wt, b, dtype, s, pads, d, Cc, "relu6")
+    assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, pads, d, Cc, "relu6"), dtype, "dw")
+
+
+@pytest.mark.parametrize("force", [None, "1x1", "igemm"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pointwise_variants(ox, force, dtype, monkeypatch):
+    if force:
+        monkeypatch.setenv("OX_FORCE_KERNEL", force)
+    say("1x1", dtype, force)
+    r = np.random.default_rng(5)
+    X = synth.round_to(r.standard_normal((3, 40, 9, 13)), dtype)
+    Wt = synth.round_to(r.standard_normal((70, 40, 1, 1)) / 6.0, dtype)
+    b = synth.round_to(r.uniform(-0.5, 0.5, 70), dtype)
+    Y = run_conv(ox, X, Wt, b, dtype, (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu")
+    assert_close(host64(Y), oracle.conv2d(X, Wt, b, act="relu"), dtype, "1x1")
+
+
+def conv_layer_tensors(layer, cfg, li, dtype):
+    t = synth.conv_inputs(layer, cfg, li)
+    Wf, bf = oracle.fold_batchnorm(t["W"], t["gamma"], t["beta"], t["mean"], t["var"], 1e-5)
+    return (synth.round_to(t["X"], dtype), synth.round_to(Wf, dtype), synth.round_to(bf, dtype))
+
+
+def check_layer(ox, layer, cfg, li, dtype, n_sample):
+    X, Wt, b = conv_layer_tensors(layer, cfg, li, dtype)
+    s = (layer.stride, layer.stride)
+    Y = run_conv(ox, X, Wt, b, dtype, s, layer.onnx_pads, (1, 1), layer.group, layer.act)
+    assert not torch.isnan(Y).any().item(), layer.name
+    got = host64(Y).ravel()
+    if n_sample is None:
+        ref = oracle.conv2d(X, Wt, b, s, layer.onnx_pads, (1, 1), layer.group, layer.act).ravel()
+        assert_close(got, ref, dtype, layer.name)
+    else:
+        idx = sample_indices(got.size, n_sample, li)
+        ref = oracle.conv2d(X, Wt, b, s, layer.onnx_pads, (1, 1), layer.group, layer.act, at=idx)
+        assert_close(got[idx], ref, dtype, layer.name)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 64])
+def test_c2_mobilenetv2_layers(ox, dtype, N):
+    for li, layer in enumerate(synth.unique_layers(synth.mobilenetv2_layers(N))):
+        say("C2", N, dtype, layer.name, layer.key())
+        check_layer(ox, layer, 2, li, dtype, None if N == 1 else 4096)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [1, 32])
+def test_c3_resnet50_layers(ox, dtype, N):
+    for li, layer in enumerate(synth.resnet50_layers(N)):
+        say("C3", N, dtype, layer.name, layer.key())
+        check_layer(ox, layer, 3, li, dtype, None if N == 1 else 4096)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gpu_fold_then_conv_equals_unfused_chain(ox, dtype):
+    # tensorforge "ResNet fusion": the library's own offline fold feeding its
+    # fused conv must match the oracle's Conv -> BatchNorm -> activation.
+    layer = synth.ConvLayer("e2e", 2, 32, 14, 14, 48, 3, 2, 1, 1, "relu6")
+    t = synth.conv_inputs(layer, 3, 99)
+    X = synth.round_to(t["X"], dtype)
+    W32 = t["W"].astype(np.float32)
+    prm = [t[k].astype(np.float32) for k in ("gamma", "beta", "mean", "var")]
+    Wf, bf = ox.ox_fold_batchnorm(W32, *prm, eps=1e-5)
+    Y = nan_like((2, 48, 7, 7), dtype)
+    ox.ox_conv2d_fused(dev(X, dtype), torch.from_numpy(Wf).cuda().to(TD[dtype]),
+                       torch.from_numpy(bf).cuda().to(TD[dtype]), (2, 2), (1, 1, 1, 1), act="relu6", Y=Y)
+    torch.cuda.synchronize()
+    chain = oracle.conv2d(X, W32.astype(np.float64), None, (2, 2), (1, 1, 1, 1))
+    chain = oracle.batchnorm(chain, *[p.astype(np.float64) for p in prm], eps=float(np.float32(1e-5)))
+    chain = oracle.act("relu6", chain)
+    assert_close(host64(Y), chain, dtype, "fold+conv")
+
+
+def test_repeat_runs_are_bitwise_identical(ox):
+    layer = synth.resnet50_layers(2)[5]   # stage-2 3x3
+    X, Wt, b = conv_layer_tensors(layer, 3, 5, "bf16")
+    outs = [host64(run_conv(ox, X, Wt, b, "bf16", (1, 1), (1, 1, 1, 1), (1, 1), 1, "relu"))
+            for _ in range(3)]
+    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+
+
+# -------------------------------------------------------------------- int8 --
+
+def int8_gpu(ox, layer, t, y_type):
+    blk = torch.from_numpy(ox.ox_int8_prepare(t["wq"], t["w_s"], t["x_s"], t["x_zp"], t["y_s"],
+                                              t["y_zp"], t["bias_q"])).cuda()
+    xq = torch.from_numpy(t["xq"]).cuda()
+    wq = torch.from_numpy(t["wq"]).cuda()
+    if layer.kind == "gemm":
+        Y = ox.ox_gemm_fused(xq, wq, transB=True, int8_params=blk,
+                             out_dtype=torch.int32 if y_type == "i32" else torch.int8)
+    else:
+        c = layer.conv
+        Y = ox.ox_conv2d_int8(xq, wq, blk, y_type, (c.stride, c.stride), c.onnx_pads, (1, 1), c.group)
+    torch.cuda.synchronize()
+    return Y.cpu().numpy()
+
+
+def int8_ref(layer, t):
+    if layer.kind == "gemm":
+        return oracle.gemm_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"], t["w_s"],
+                                t["y_s"], t["y_zp"])
+    c = layer.conv
+    return oracle.conv2d_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"], t["w_s"], t["y_s"],
+                              t["y_zp"], (c.stride, c.stride), c.onnx_pads, (1, 1), c.group)
+
+
+def test_c4_int8_conformer_block_bit_exact(ox):
+    for li, layer in enumerate(synth.conformer_int8_layers()):
+        say("C4", layer.name)
+        t = synth.int8_inputs(layer, 4, li)
+        acc, y = int8_ref(layer, t)
+        assert np.array_equal(int8_gpu(ox, layer, t, "i32").astype(np.int64), acc), layer.name
+        assert np.array_equal(int8_gpu(ox, layer, t, "i8"), y), layer.name
+
+
+@pytest.mark.parametrize("geom", [
+    (2, 6, 9, 11, 10, 3, 3, 1, (1, 1, 1, 1), 1),
+    (1, 12, 7, 8, 12, 3, 3, 2, (2, 1, 0, 3), 12),
+    (1, 8, 5, 33, 8, 1, 9, 1, (0, 4, 0, 4), 8),
+    (2, 32, 6, 6, 48, 1, 1, 1, (0, 0, 0, 0), 1),
+    (1, 8, 10, 10, 16, 5, 5, 2, (3, 3, 3, 3), 4),
+])
+def test_int8_conv_small_shapes_bit_exact(ox, geom):
+    N, Cin, H, W, M, kH, kW, s, pads, g = geom
+    say("int8 conv", geom)
+    conv = synth.ConvLayer("q", N, Cin, H, W, M, kH, s, 0, g, "none", kW=kW, pads=pads)
+    layer = synth.Int8Layer("q", "conv", 1, (Cin // g) * kH * kW, M, conv)
+    t = synth.int8_inputs(layer, 4, 50 + H + W)
+    acc, y = int8_ref(layer, t)
+    assert np.array_equal(int8_gpu(ox, layer, t, "i32").astype(np.int64), acc)
+    assert np.array_equal(int8_gpu(ox, layer, t, "i8"), y)
+
+
+def test_int8_gemm_ragged_bit_exact(ox):
+    layer = synth.Int8Layer("g", "gemm", 77, 200, 45)
+    say("int8 gemm ragged")
+    t = synth.int8_inputs(layer, 4, 60)
+    acc, y = int8_ref(layer, t)
+    assert np.array_equal(int8_gpu(ox, layer, t, "i32").astype(np.int64), acc)
+    assert np.array_equal(int8_gpu(ox, layer, t, "i8"), y)
+
+
+def test_int8_requant_ties_on_gpu(ox):
+    # x_s = 2^-4, w_s = 2^-3, y_s = 2^-6: multiplier 1/2, every odd accumulator
+    # a tie; round half to even gives 0, 2, 0, -2 for 1, 3, -1, -3.
+    say("int8 ties")
+    K = 4
+    accs = np.array([1, 3, -1, -3, 5, -5, 254, -258], np.int64)
+    xq = np.zeros((1, K), np.int8)
+    wq = np.zeros((len(accs), K), np.int8)
+    blk = torch.from_numpy(ox.ox_int8_prepare(wq, np.full(len(accs), 2.0 ** -3, np.float32),
+                                              2.0 ** -4, 0, 2.0 ** -6, 0, accs.astype(np.int32))).cuda()
+    Y = ox.ox_gemm_fused(torch.from_numpy(xq).cuda(), torch.from_numpy(wq).cuda(), transB=True,
+                         int8_params=blk, out_dtype=torch.int8)
+    torch.cuda.synchronize()
+    assert Y.cpu().numpy().ravel().tolist() == [0, 2, 0, -2, 2, -2, 127, -128]
