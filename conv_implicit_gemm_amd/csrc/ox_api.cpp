@@ -216,7 +216,12 @@ ConvArgs conv_args(int dt, const ox_conv_desc* d, int64_t Ho, int64_t Wo, const 
   return a;
 }
 
-enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2 };
+enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2, KIND_PATCH = 3 };
+
+const char* kind_name(int k) {
+  static const char* n[] = {"igemm", "1x1", "dw", "patch"};
+  return n[k];
+}
 
 ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, const Force& f,
                       int* kind) {
@@ -234,6 +239,10 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
       *kind = KIND_1X1;
     } else if (!strcmp(f.variant, "igemm")) {
       *kind = KIND_IGEMM;
+    } else if (!strcmp(f.variant, "patch")) {
+      if (!conv_patch_applicable(a))
+        return fail(OX_ERR_UNSUPPORTED, "%s: forced 'patch' needs bf16, a 3x3 kernel, group 1, C %% 32 == 0 and aligned X/W", fn);
+      *kind = KIND_PATCH;
     } else {
       return fail(OX_ERR_INVALID_ARG, "%s: OX_FORCE_KERNEL variant '%s' does not apply to Conv", fn,
                   f.variant);
@@ -242,6 +251,7 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
   }
   if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
   else if (is_1x1) *kind = KIND_1X1;
+  else if (conv_patch_applicable(a)) *kind = KIND_PATCH;
   else *kind = KIND_IGEMM;
   return OX_OK;
 }
@@ -255,21 +265,23 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
   ox_status st = select_conv(fn, d, a, f, &kind);
   if (st) return st;
   int tile = -1;
-  if (kind != KIND_DW) {
+  if (kind == KIND_IGEMM || kind == KIND_1X1) {
     st = pick_tile(fn, f, d->M / d->group, d->N * a.Ho * a.Wo, d->group, &tile);
     if (st) return st;
   } else if (f.tile != -1) {
-    return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to the depthwise kernel", fn);
+    return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to the %s kernel", fn, kind_name(kind));
   }
   if (log_on())
     fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s\n",
             fn, a.dt, a.N, a.C, a.H, a.W, a.M, a.kH, a.kW, a.sh, a.sw, a.group, act_name(a.act),
-            kind == KIND_DW ? "dw" : kind == KIND_1X1 ? "1x1" : "igemm", tile >= 0 ? " tile=" : "",
+            kind_name(kind), tile >= 0 ? " tile=" : "",
             tile >= 0 ? tile_name(tile) : "");
   if (d->N == 0) return ok();
   int rc;
   if (kind == KIND_DW) {
     rc = launch_conv_depthwise(a, stream);
+  } else if (kind == KIND_PATCH) {
+    rc = launch_conv_patch(a, stream);
   } else {
     const int k = kind == KIND_1X1 ? 1 : 0;
     rc = a.dt == DT_F32 ? launch_conv_f32(a, k, tile, stream)
@@ -493,12 +505,12 @@ ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_
   st = select_conv(fn, d, a, f, &kind);
   if (st) return st;
   int tile = -1;
-  if (kind != KIND_DW) {
+  if (kind == KIND_IGEMM || kind == KIND_1X1) {
     st = pick_tile(fn, f, d->M / d->group, d->N * Ho * Wo, d->group, &tile);
     if (st) return st;
   }
   static const char* dtn[] = {"f32", "bf16", "i8"};
-  snprintf(name, cap, "%s/%s%s%s", kind == KIND_DW ? "dw" : kind == KIND_1X1 ? "1x1" : "igemm",
+  snprintf(name, cap, "%s/%s%s%s", kind_name(kind),
            dtn[(int)t], tile >= 0 ? "/" : "", tile >= 0 ? tile_name(tile) : "");
   return ok();
 }

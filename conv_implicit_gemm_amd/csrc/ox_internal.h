@@ -101,6 +101,9 @@ int launch_conv_i8(const ConvArgs& a, int kind, int tile, void* stream);
 int launch_conv_depthwise(const ConvArgs& a, void* stream);
 // whether the depthwise kernel's LDS band fits this geometry (host only)
 bool depthwise_fits(const ConvArgs& a);
+// 3x3 bf16 convolution with an LDS-staged input patch (group 1, C % 32 == 0)
+bool conv_patch_applicable(const ConvArgs& a);
+int launch_conv_patch(const ConvArgs& a, void* stream);
 // Gemm with a single output row (M = 1): memory-bound, no MFMA
 int launch_gemv(const GemmArgs& a, void* stream);
 

@@ -385,3 +385,35 @@ def test_int8_requant_ties_on_gpu(ox):
                          int8_params=blk, out_dtype=torch.int8)
     torch.cuda.synchronize()
     assert Y.cpu().numpy().ravel().tolist() == [0, 2, 0, -2, 2, -2, 127, -128]
+
+
+def test_patch_conv_sweep_bf16(ox, monkeypatch):
+    # the LDS-patch 3x3 kernel over strides, dilations, asymmetric pads,
+    # ragged channel / pixel counts and several images per block
+    monkeypatch.setenv("OX_FORCE_KERNEL", "patch")
+    r = np.random.default_rng(321)
+    ran = 0
+    for ci in range(60):
+        N = int(r.integers(1, 5))
+        Cin = int(r.choice([32, 64, 96]))
+        H, W = int(r.integers(1, 30)), int(r.integers(1, 30))
+        M = int(r.integers(1, 150))
+        s = int(r.choice([1, 2, 3]))
+        d = int(r.choice([1, 2]))
+        pads = tuple(int(v) for v in r.integers(0, 4, 4))
+        if not conv_case_ok(N, Cin, H, W, M, 3, 3, (s, s), pads, (d, d), 1):
+            continue
+        try:
+            ox.ox_conv2d_variant("bf16", N, Cin, H, W, M, 3, 3, (s, s), pads, (d, d), 1)
+        except ox.OxError:
+            continue      # no patch plan for this geometry
+        act = str(r.choice(["none", "relu", "relu6", "gelu"]))
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 3, 3)) / math.sqrt(9 * Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("patch sweep", ci, (N, Cin, H, W, M, s, pads, d, act))
+        Y = run_conv(ox, X, Wt, b, "bf16", (s, s), pads, (d, d), 1, act)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, (s, s), pads, (d, d), 1, act), "bf16",
+                     "patch %d" % ci)
+        ran += 1
+    assert ran >= 30
