@@ -1,7 +1,7 @@
 """Build libox.so, the gfx950 HIP library, in-tree.
 
 Every *.hip unit is compiled with hipcc for gfx950 only (in parallel), the
-host front end ox_api.cpp with g++, and the objects are linked by hipcc into
+host-only units (*.cpp: the C-ABI front end and kernel planners) with g++, and the objects are linked by hipcc into
 conv_implicit_gemm_amd/libox.so.  Packed-fp32 instruction selection is
 disabled for the device code (-target-feature -packed-fp32-ops).
 """
@@ -47,9 +47,10 @@ def build(verbose: bool = False, jobs: int = 0) -> str:
         o = os.path.join(OBJDIR, f[:-4] + ".o")
         objs.append(o)
         cmds.append([HIPCC] + HIP_FLAGS + ["-c", os.path.join(CSRC, f), "-o", o])
-    o = os.path.join(OBJDIR, "ox_api.o")
-    objs.append(o)
-    cmds.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, "ox_api.cpp"), "-o", o])
+    for f in sorted(f for f in os.listdir(CSRC) if f.endswith(".cpp")):
+        o = os.path.join(OBJDIR, f[:-4] + ".o")
+        objs.append(o)
+        cmds.append(["g++"] + CXX_FLAGS + ["-c", os.path.join(CSRC, f), "-o", o])
     jobs = jobs or min(len(cmds), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), cmds))

@@ -1,0 +1,158 @@
+// conv_patch_plan.cpp -- host-side planning of the LDS-patch 3x3 kernel:
+// which configuration (rows per block, wave grid, pixel tiles per wave) and
+// which band of output rows / images each block owns.  Pure host code.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "ox_internal.h"
+
+namespace ox {
+
+
+int launch_patch_64_1_2(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_64_1_4(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_128_2_7(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_128_2_4(const ConvArgs& a, const PatchPlan& p, void* s);
+
+namespace {
+
+constexpr int kCell = 80;
+constexpr int kLdsMax = 160 * 1024;
+constexpr int kCUs = 256;
+
+struct Cfg {
+  int BM, WM, FN, UPT;
+};
+const Cfg kCfgs[] = {{64, 1, 2, 0}, {64, 1, 4, 0}, {128, 2, 4, 0}, {128, 2, 7, 0}};
+
+PatchPlan make(const ConvArgs& a, const Cfg& c, int TR, int IMB) {
+  PatchPlan p;
+  p.BM = c.BM;
+  p.WM = c.WM;
+  p.FN = c.FN;
+  p.TR = TR;
+  p.IMB = IMB;
+  p.PR = (TR - 1) * a.sh + 2 * a.dh + 1;
+  p.PW = (a.Wo - 1) * a.sw + 2 * a.dw + 1;
+  p.PWs = (p.PW + a.sw - 1) / a.sw;
+  p.PWt = p.PWs * a.sw;
+  p.NT = (IMB * TR * a.Wo + 15) / 16;
+  p.nrb = (a.Ho + TR - 1) / TR;
+  p.nib = (a.N + IMB - 1) / IMB;
+  p.npos = IMB * p.PR * p.PWt;
+  const int HW = a.H * a.W;
+  p.VW = (HW % 2 == 0) ? 2 : 1;   // positions per staging unit (P)
+  p.UPT = (c.FN >= 4 ? 4 : 8) / p.VW;   // staging units per thread (kernel's patch_upt)
+  // staging units: images x 4 channel octets x groups of P plane positions
+  // (a band of R rows spans at most R*W + P - 1 positions from a P-aligned start)
+  const int rows = std::min(a.H, p.PR);
+  p.units = IMB * 4 * ((rows * a.W + 2 * p.VW - 2) / p.VW);
+  p.lds = std::max(c.BM * (9 * 64 + 16) + p.npos * kCell,
+                   c.BM * (p.NT * 16 + 8) * 2);   // the epilogue reuses LDS as [channel][pixel]
+  return p;
+}
+
+bool fits(const PatchPlan& p) {
+  const int ntmax = (4 / p.WM) * p.FN;
+  return p.NT <= ntmax && p.lds <= kLdsMax && p.units <= p.UPT * 256 &&
+         (int64_t)p.nrb * p.nib < (1 << 30);
+}
+
+// Rough time model: MFMA cycles per SIMD over the whole grid against the
+// bytes the blocks pull through L2 (every pixel block reads all weights of its
+// channel block; every channel block re-reads the input band with its halo).
+double cost(const ConvArgs& a, const PatchPlan& p) {
+  const int WN = 4 / p.WM;
+  const int FM = p.BM / (16 * p.WM);
+  const double mblocks = (a.M + p.BM - 1) / p.BM;
+  const double pblocks = (double)p.nrb * p.nib;
+  const double blocks = mblocks * pblocks;
+  const int per_cu = std::max(1, std::min(p.BM == 64 ? 2 : 1, kLdsMax / p.lds));
+  const double waves_cycles = (a.C / 32) * 9.0 * FM * ((p.NT + WN - 1) / WN) * 16.0;
+  const double rounds = std::ceil(blocks / (kCUs * per_cu));
+  const double t_mfma = rounds * per_cu * waves_cycles / 2.4e9;
+  const double wbytes = (double)a.M * a.C * 9 * 2;
+  const double xbytes = (double)a.N * a.C * a.H * a.W * 2;
+  const double halo = (double)std::min(a.H, p.PR) / std::max(1.0, (double)p.TR * a.sh);
+  const double traffic = wbytes * pblocks + xbytes * mblocks * std::max(1.0, halo);
+  const double t_mem = traffic / 6e12;
+  // per-chunk fixed cost (two barriers and an exposed load latency), per round
+  const double t_fix = rounds * (a.C / 32) * 0.25e-6;
+  return std::max(t_mfma, t_mem) + t_fix;
+}
+
+}  // namespace
+
+// OX_PATCH_PLAN=BM:FN:TR:IMB pins the plan (for measurements); a pinned plan
+// that does not fit this geometry makes the kernel inapplicable.
+bool pinned_plan(const ConvArgs& a, PatchPlan* out, bool* pinned) {
+  const char* e = getenv("OX_PATCH_PLAN");
+  *pinned = false;
+  if (!e || !*e) return false;
+  int bm, fn, tr, imb;
+  if (sscanf(e, "%d:%d:%d:%d", &bm, &fn, &tr, &imb) != 4) return false;
+  *pinned = true;
+  for (const Cfg& c : kCfgs) {
+    if (c.BM != bm || c.FN != fn) continue;
+    if (tr < 1 || tr > a.Ho || imb < 1 || (imb > 1 && tr != a.Ho)) return false;
+    const PatchPlan p = make(a, c, tr, imb);
+    if (!fits(p)) return false;
+    *out = p;
+    return true;
+  }
+  return false;
+}
+
+bool patch_plan(const ConvArgs& a, PatchPlan* out) {
+  bool pinned;
+  const bool ok = pinned_plan(a, out, &pinned);
+  if (pinned) return ok;
+  bool found = false;
+  double best = 1e30;
+  for (const Cfg& c : kCfgs) {
+    for (int IMB = 1; IMB <= 8; ++IMB) {
+      for (int TR = 1; TR <= a.Ho; ++TR) {
+        if (IMB > 1 && TR != a.Ho) continue;
+        const PatchPlan p = make(a, c, TR, IMB);
+        if (!fits(p)) continue;
+        const double t = cost(a, p);
+        if (t < best * 0.999) {
+          best = t;
+          *out = p;
+          found = true;
+        }
+      }
+    }
+  }
+  return found;
+}
+
+bool conv_patch_applicable(const ConvArgs& a) {
+  if (a.dt != DT_BF16 || a.group != 1 || a.kH != 3 || a.kW != 3 || a.C % 32 != 0) return false;
+  if (a.sh != a.sw || (a.sw != 1 && a.sw != 2)) return false;
+  if (!a.w_vec || (((uintptr_t)a.X) & 15) != 0) return false;
+  PatchPlan p;
+  return patch_plan(a, &p);
+}
+
+int launch_conv_patch(const ConvArgs& a, void* stream) {
+  PatchPlan p;
+  if (!patch_plan(a, &p)) return 1;  // hipErrorInvalidValue
+  if (p.BM == 64) {
+    return p.FN == 2 ? launch_patch_64_1_2(a, p, stream) : launch_patch_64_1_4(a, p, stream);
+  }
+  return p.FN == 4 ? launch_patch_128_2_4(a, p, stream) : launch_patch_128_2_7(a, p, stream);
+}
+
+const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap) {
+  PatchPlan p;
+  if (!patch_plan(a, &p)) return "";
+  snprintf(buf, cap, "BM=%d WM=%d FN=%d TR=%d IMB=%d NT=%d VW=%d blocks=%lld lds=%d", p.BM, p.WM,
+           p.FN, p.TR, p.IMB, p.NT, p.VW, (long long)p.nrb * p.nib * ((a.M + p.BM - 1) / p.BM), p.lds);
+  return buf;
+}
+
+}  // namespace ox

@@ -271,11 +271,13 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
   } else if (f.tile != -1) {
     return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to the %s kernel", fn, kind_name(kind));
   }
-  if (log_on())
-    fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s\n",
+  if (log_on()) {
+    char plan[160] = "";
+    if (kind == KIND_PATCH) conv_patch_describe(a, plan, sizeof(plan));
+    fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s %s\n",
             fn, a.dt, a.N, a.C, a.H, a.W, a.M, a.kH, a.kW, a.sh, a.sw, a.group, act_name(a.act),
-            kind_name(kind), tile >= 0 ? " tile=" : "",
-            tile >= 0 ? tile_name(tile) : "");
+            kind_name(kind), tile >= 0 ? " tile=" : "", tile >= 0 ? tile_name(tile) : "", plan);
+  }
   if (d->N == 0) return ok();
   int rc;
   if (kind == KIND_DW) {

@@ -87,6 +87,25 @@ struct ConvArgs {
   int x_vec;              // (1x1 only) pixel rows allow 16-byte loads
 };
 
+// Plan of the LDS-patch 3x3 kernel (host-chosen, passed to the kernel by
+// value): configuration, block band and patch geometry.
+struct PatchPlan {
+  int BM, WM, FN, UPT;  // rows per block, wave rows, pixel tiles per wave, staging units per thread
+  int TR;               // output rows per block (per image)
+  int IMB;              // images per block (> 1 only when TR == Ho)
+  int PR;               // patch rows per image
+  int PWs;              // patch columns per stride phase
+  int PWt;              // patch row length in cells (stride * PWs)
+  int PW;               // patch columns used
+  int NT;               // 16-pixel tiles per block
+  int nrb;              // row blocks per image
+  int nib;              // image blocks
+  int npos;             // cells in the patch (IMB * PR * PWt)
+  int VW;               // plane positions per staging unit (1 or 2)
+  int units;            // upper bound of staging units per block
+  int lds;              // bytes of LDS
+};
+
 // Launchers (return a hipError_t as int).  `stream` is a hipStream_t.
 // One translation unit per input type keeps the builds parallel.
 int launch_gemm_f32(const GemmArgs& a, int tile, void* stream);
@@ -104,6 +123,7 @@ bool depthwise_fits(const ConvArgs& a);
 // 3x3 bf16 convolution with an LDS-staged input patch (group 1, C % 32 == 0)
 bool conv_patch_applicable(const ConvArgs& a);
 int launch_conv_patch(const ConvArgs& a, void* stream);
+const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap);
 // Gemm with a single output row (M = 1): memory-bound, no MFMA
 int launch_gemv(const GemmArgs& a, void* stream);
 
