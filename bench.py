@@ -75,16 +75,26 @@ def conv_layers(ox, synth, torch, cfg, layers, dtype, stream):
                          (1, 1), l.group)
         code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
         act = ox.ACT[l.act]
-        args = (code, C.byref(d), Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(), act,
-                Yd.data_ptr(), stream)
-        fn = ox.lib.ox_conv2d_fused
         variant = ox.ox_conv2d_variant(dtype, l.N, l.C, l.H, l.W, l.M, l.kh, l.kw,
                                        (l.stride, l.stride), l.onnx_pads, (1, 1), l.group)
+        Wlaunch = Wd
+        fn = ox.lib.ox_conv2d_fused
+        if ox.ox_conv2d_packed_weights_bytes(dtype, l.N, l.C, l.H, l.W, l.M, l.kh, l.kw,
+                                             (l.stride, l.stride), l.onnx_pads, (1, 1), l.group):
+            # offline weight packing (untimed, like the BatchNorm fold)
+            bits = Wd.view(torch.int16).cpu().numpy().view(np.uint16)
+            Wp = ox.ox_conv2d_pack_weights(bits, dtype, l.N, l.C, l.H, l.W, (l.stride, l.stride),
+                                           l.onnx_pads, (1, 1), l.group)
+            Wlaunch = torch.from_numpy(Wp.view(np.int16)).cuda().view(torch.bfloat16)
+            fn = ox.lib.ox_conv2d_fused_packed
+            variant += "+packed"
+        args = (code, C.byref(d), Xd.data_ptr(), Wlaunch.data_ptr(), bd.data_ptr(), act,
+                Yd.data_ptr(), stream)
         # the oracle reads the bits the GPU reads: X as rounded, W' and b' as
         # the device holds them
         Wh = Wd.float().cpu().numpy().astype(np.float64)
         bh = bd.float().cpu().numpy().astype(np.float64)
-        keep = (Xd, Wd, bd, Yd, d)
+        keep = (Xd, Wd, Wlaunch, bd, Yd, d)
 
         def launch(fn=fn, args=args, keep=keep):
             return fn(*args)

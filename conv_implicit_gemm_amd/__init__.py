@@ -24,7 +24,8 @@ STATUS_NAMES = {0: "OX_OK", 1: "OX_ERR_INVALID_ARG", 2: "OX_ERR_SHAPE",
 
 # every symbol include/ox.h declares
 EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_int8",
-           "ox_conv2d_variant", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
+           "ox_conv2d_variant", "ox_conv2d_fused_packed", "ox_conv2d_packed_weights_bytes",
+           "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
            "ox_last_error", "ox_version")
 
 
@@ -56,6 +57,9 @@ def _load():
         "ox_conv2d_fused": (I, [I, P, P, P, P, I, P, P]),
         "ox_conv2d_int8": (I, [P, P, P, P, I, P, P]),
         "ox_conv2d_variant": (I, [I, P, C.c_char_p, C.c_size_t]),
+        "ox_conv2d_fused_packed": (I, [I, P, P, P, P, I, P, P]),
+        "ox_conv2d_packed_weights_bytes": (C.c_size_t, [I, P]),
+        "ox_conv2d_pack_weights": (I, [I, P, P, P]),
         "ox_fold_batchnorm": (I, [I64, I64, P, P, P, P, P, P, F, P, P]),
         "ox_int8_params_bytes": (C.c_size_t, [I64]),
         "ox_int8_prepare": (I, [I64, I64, P, P, F, I32, F, I32, P, P]),
@@ -194,6 +198,45 @@ def ox_conv2d_fused(X, W, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=
     _check(lib.ox_conv2d_fused(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), ACT[act],
                                _ptr(Y), _stream(stream)))
     return Y
+
+
+def ox_conv2d_fused_packed(X, Wp, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
+                           group=1, act="none", Y=None, M=None, kernel=(3, 3), stream=None):
+    """ox_conv2d_fused with weights packed by ox_conv2d_pack_weights (a device
+    tensor of the packed bytes' dtype).  M: output channels; kernel: (kH, kW)."""
+    torch = _torch()
+    for t, n in ((X, "X"), (Wp, "Wp"), (bias, "bias"), (Y, "Y")):
+        _dense(t, n)
+    N, Cin, H, Wd = X.shape
+    kH, kW = kernel
+    if M is None:
+        M = Wp.numel() // (Cin // group * kH * kW)
+    d = conv_desc(N, Cin, H, Wd, M, kH, kW, stride, pads, dilation, group)
+    if Y is None:
+        ho, wo = conv_out_hw(H, Wd, kH, kW, stride, pads, dilation)
+        Y = torch.empty((N, M, max(ho, 0), max(wo, 0)), dtype=X.dtype, device=X.device)
+    _check(lib.ox_conv2d_fused_packed(_dtype_code(X), C.byref(d), _ptr(X), _ptr(Wp), _ptr(bias), ACT[act],
+                                      _ptr(Y), _stream(stream)))
+    return Y
+
+
+def ox_conv2d_packed_weights_bytes(dtype, N, Cin, H, W, M, kH, kW, stride=(1, 1), pads=(0, 0, 0, 0),
+                                   dilation=(1, 1), group=1):
+    d = conv_desc(N, Cin, H, W, M, kH, kW, stride, pads, dilation, group)
+    return int(lib.ox_conv2d_packed_weights_bytes({"f32": OX_F32, "bf16": OX_BF16}[dtype], C.byref(d)))
+
+
+def ox_conv2d_pack_weights(W, dtype, N, Cin, H, Wd, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
+                           group=1):
+    """Pack host weights W [M, C/g, kH, kW] (numpy array of the dtype's storage: float32, or
+    uint16 bf16 bits) for ox_conv2d_fused_packed; returns a numpy array of the same dtype."""
+    W = np.ascontiguousarray(W)
+    M, _, kH, kW = W.shape
+    d = conv_desc(N, Cin, H, Wd, M, kH, kW, stride, pads, dilation, group)
+    code = {"f32": OX_F32, "bf16": OX_BF16}[dtype]
+    out = np.empty_like(W)
+    _check(lib.ox_conv2d_pack_weights(code, C.byref(d), W.ctypes.data, out.ctypes.data))
+    return out
 
 
 def ox_conv2d_int8(Xq, Wq, int8_params, y_type="i8", stride=(1, 1), pads=(0, 0, 0, 0),

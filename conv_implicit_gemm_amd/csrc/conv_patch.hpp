@@ -12,10 +12,11 @@
 //     elements, repacked by position in registers.  Consecutive lanes take
 //     consecutive positions, so the global loads are contiguous across a wave
 //     and the 16-byte cell writes hit distinct LDS banks;
-//   * stages the weights of the chunk tap-major: W[m, c, kh, kw] is read as
-//     it lies in memory (8 channels x 9 taps = 9 aligned 16-byte loads) and
-//     permuted in registers so that each tap holds its 32 channels
-//     contiguously;
+//   * stages the weights of the chunk tap-major.  ONNX-layout weights
+//     W[m, c, kh, kw] are read as they lie in memory (8 channels x 9 taps =
+//     9 aligned 16-byte loads) and permuted in registers so that each tap
+//     holds its 32 channels contiguously; weights packed offline in that
+//     tap-major order (ox_conv2d_pack_weights) are a straight, coalesced copy;
 //   * runs 9 taps x (BM/16) x (tiles of 16 pixels) MFMA 16x16x32 bf16: for tap
 //     (kh, kw) the operand of output pixel p is the cell at p's patch position
 //     plus a tap offset, so both MFMA fragments are single 128-bit LDS reads.
@@ -43,12 +44,14 @@ constexpr int patch_upt(int P, int FN) { return (FN >= 4 ? 4 : 8) / P; }
 constexpr int kKK = 9;
 constexpr int kAROW = kKK * 64 + 16;
 
-template <int BM, int WM, int FN, int P, int S>
+template <int BM, int WM, int FN, int P, int S, bool WPACK>
 __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf16(const ConvArgs a,
                                                                                   const PatchPlan pp) {
   constexpr int WN = 4 / WM;                 // waves along the pixel tiles
   constexpr int FM = BM / (16 * WM);         // 16-row MFMA tiles per wave
-  constexpr int WUNITS = BM * 4 / kThreads;  // weight staging units per thread
+  // weight staging units per thread: ONNX layout, 8 channels x 9 taps each;
+  // packed layout, one 16-byte vector of a channel block's 576-byte row each
+  constexpr int WUNITS = WPACK ? BM * 36 / kThreads : BM * 4 / kThreads;
   constexpr int UPT = patch_upt(P, FN);      // patch staging units per thread (max)
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* As = smem;
@@ -149,23 +152,36 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  u32x4_t wreg[WUNITS][kKK];
+  u32x4_t wreg[WUNITS][WPACK ? 1 : kKK];
   // raw loaded values (one per channel: P bf16 positions), repacked by
   // position only after the barrier so the loads stay in flight meanwhile
   uint32_t xreg[UPT][8];
 
   auto load_chunk = [&](int c0) {
+    if constexpr (WPACK) {
+      // packed: row m of chunk c0/32 is 9 taps x 32 channels, contiguous
 #pragma unroll
-    for (int k = 0; k < WUNITS; ++k) {
-      const int u = tid + k * kThreads;
-      const int m = u >> 2, oct = u & 3;
-      if (m0 + m < M) {
-        const uint16_t* src = Wt + (int64_t)(m0 + m) * K + (c0 + oct * 8) * kKK;
+      for (int k = 0; k < WUNITS; ++k) {
+        const int v = tid + k * kThreads;
+        const int m = v / 36, j = v - (v / 36) * 36;
+        if (m0 + m < M)
+          wreg[k][0] = *(const u32x4_t*)(Wt + ((int64_t)(m0 + m) * (C / 32) + c0 / 32) * 288 + j * 8);
+        else
+          wreg[k][0] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    } else {
 #pragma unroll
-        for (int j = 0; j < kKK; ++j) wreg[k][j] = *(const u32x4_t*)(src + 8 * j);
-      } else {
+      for (int k = 0; k < WUNITS; ++k) {
+        const int u = tid + k * kThreads;
+        const int m = u >> 2, oct = u & 3;
+        if (m0 + m < M) {
+          const uint16_t* src = Wt + (int64_t)(m0 + m) * K + (c0 + oct * 8) * kKK;
 #pragma unroll
-        for (int j = 0; j < kKK; ++j) wreg[k][j] = u32x4_t{0u, 0u, 0u, 0u};
+          for (int j = 0; j < kKK; ++j) wreg[k][j] = *(const u32x4_t*)(src + 8 * j);
+        } else {
+#pragma unroll
+          for (int j = 0; j < kKK; ++j) wreg[k][j] = u32x4_t{0u, 0u, 0u, 0u};
+        }
       }
     }
     const uint16_t* xc = Xblk + (int64_t)c0 * HW;
@@ -183,25 +199,34 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
   };
 
   auto store_chunk = [&]() {
+    if constexpr (WPACK) {
 #pragma unroll
-    for (int k = 0; k < WUNITS; ++k) {
-      const int u = tid + k * kThreads;
-      const int m = u >> 2, oct = u & 3;
-      char* dst = As + m * kAROW + oct * 16;
+      for (int k = 0; k < WUNITS; ++k) {
+        const int v = tid + k * kThreads;
+        const int m = v / 36, j = v - (v / 36) * 36;
+        *(u32x4_t*)(As + m * kAROW + j * 16) = wreg[k][0];
+      }
+    } else {
 #pragma unroll
-      for (int t = 0; t < kKK; ++t) {
-        // tap t of channels oct*8 .. oct*8+7: elements c*9 + t of the 72 loaded
-        uint32_t d[4];
+      for (int k = 0; k < WUNITS; ++k) {
+        const int u = tid + k * kThreads;
+        const int m = u >> 2, oct = u & 3;
+        char* dst = As + m * kAROW + oct * 16;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int e0 = (2 * j) * kKK + t, e1 = (2 * j + 1) * kKK + t;
-          const uint32_t w0 = wreg[k][e0 >> 3][(e0 & 7) >> 1];
-          const uint32_t w1 = wreg[k][e1 >> 3][(e1 & 7) >> 1];
-          const uint32_t lo = (e0 & 1) ? (w0 >> 16) : (w0 & 0xffffu);
-          const uint32_t hi = (e1 & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
-          d[j] = lo | hi;
+        for (int t = 0; t < kKK; ++t) {
+          // tap t of channels oct*8 .. oct*8+7: elements c*9 + t of the 72 loaded
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int e0 = (2 * j) * kKK + t, e1 = (2 * j + 1) * kKK + t;
+            const uint32_t w0 = wreg[k][e0 >> 3][(e0 & 7) >> 1];
+            const uint32_t w1 = wreg[k][e1 >> 3][(e1 & 7) >> 1];
+            const uint32_t lo = (e0 & 1) ? (w0 >> 16) : (w0 & 0xffffu);
+            const uint32_t hi = (e1 & 1) ? (w1 & 0xffff0000u) : (w1 << 16);
+            d[j] = lo | hi;
+          }
+          *(u32x4_t*)(dst + t * 64) = u32x4_t{d[0], d[1], d[2], d[3]};
         }
-        *(u32x4_t*)(dst + t * 64) = u32x4_t{d[0], d[1], d[2], d[3]};
       }
     }
 #pragma unroll
@@ -322,8 +347,15 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
 template <int BM, int WM, int FN>
 int launch_cfg(const ConvArgs& a, const PatchPlan& p, hipStream_t s) {
   dim3 grid(p.nrb * p.nib, (a.M + BM - 1) / BM, 1);
-#define OX_PATCH_LAUNCH(P_, S_) \
-  hipLaunchKernelGGL((conv3x3_patch_bf16<BM, WM, FN, P_, S_>), grid, dim3(kThreads), p.lds, s, a, p)
+#define OX_PATCH_LAUNCH(P_, S_)                                                                   \
+  do {                                                                                            \
+    if (a.w_packed)                                                                               \
+      hipLaunchKernelGGL((conv3x3_patch_bf16<BM, WM, FN, P_, S_, true>), grid, dim3(kThreads),  \
+                         p.lds, s, a, p);                                                         \
+    else                                                                                          \
+      hipLaunchKernelGGL((conv3x3_patch_bf16<BM, WM, FN, P_, S_, false>), grid, dim3(kThreads), \
+                         p.lds, s, a, p);                                                         \
+  } while (0)
   if (a.sw == 1) {
     if (p.VW == 2) OX_PATCH_LAUNCH(2, 1);
     else OX_PATCH_LAUNCH(1, 1);

@@ -225,6 +225,18 @@ const char* kind_name(int k) {
 
 ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, const Force& f,
                       int* kind) {
+  if (a.w_packed) {
+    // packed weights exist only for the LDS-patch kernel
+    if (f.variant && strcmp(f.variant, "patch"))
+      return fail(OX_ERR_UNSUPPORTED, "%s: OX_FORCE_KERNEL variant '%s' does not take packed weights", fn,
+                  f.variant);
+    if (!conv_patch_applicable(a))
+      return fail(OX_ERR_UNSUPPORTED,
+                  "%s: no packed-weight kernel for this geometry or alignment (needs bf16, 3x3, group 1, "
+                  "C %% 32 == 0, stride 1 or 2, 16-byte aligned X and W)", fn);
+    *kind = KIND_PATCH;
+    return OX_OK;
+  }
   const bool is_dw = d->group == d->C && d->group == d->M;
   const bool is_1x1 = d->kH == 1 && d->kW == 1 && d->s_h == 1 && d->s_w == 1 && d->p_t == 0 &&
                       d->p_l == 0 && d->p_b == 0 && d->p_r == 0 && d->group == 1;
@@ -470,6 +482,61 @@ ox_status ox_conv2d_fused(ox_dtype t, const ox_conv_desc* d, const void* X, cons
     if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
   }
   ConvArgs a = conv_args((int)t, d, Ho, Wo, X, W, bias, Y, (int)act);
+  return conv_dispatch(fn, d, a, stream);
+}
+
+size_t ox_conv2d_packed_weights_bytes(ox_dtype t, const ox_conv_desc* d) {
+  int64_t Ho, Wo;
+  if ((t != OX_F32 && t != OX_BF16) || check_conv_desc("ox_conv2d_packed_weights_bytes", d, &Ho, &Wo))
+    return 0;
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, nullptr, nullptr, nullptr, nullptr, ACT_NONE);
+  if (!conv_patch_geometry(a)) return 0;
+  return (size_t)(d->M * d->C * d->kH * d->kW) * esize(t);
+}
+
+ox_status ox_conv2d_pack_weights(ox_dtype t, const ox_conv_desc* d, const void* W_host, void* Wp_host) {
+  const char* fn = "ox_conv2d_pack_weights";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  int64_t Ho, Wo;
+  st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, nullptr, nullptr, nullptr, nullptr, ACT_NONE);
+  if (!conv_patch_geometry(a))
+    return fail(OX_ERR_UNSUPPORTED, "%s: no packed layout for this geometry (needs bf16, 3x3, group 1, "
+                "C %% 32 == 0, stride 1 or 2)", fn);
+  if (!W_host || !Wp_host) return fail(OX_ERR_INVALID_ARG, "%s: W_host or Wp_host is NULL", fn);
+  const int64_t M = d->M, Cc = d->C, KK = d->kH * d->kW, nch = Cc / 32;
+  const int es = esize(t);
+  const char* src = (const char*)W_host;
+  char* dst = (char*)Wp_host;
+  // Wp[m][chunk][tap][c32] = W[m][chunk*32 + c32][tap]
+  for (int64_t m = 0; m < M; ++m)
+    for (int64_t ch = 0; ch < nch; ++ch)
+      for (int64_t tap = 0; tap < KK; ++tap)
+        for (int64_t c = 0; c < 32; ++c)
+          memcpy(dst + (((m * nch + ch) * KK + tap) * 32 + c) * es,
+                 src + ((m * Cc + ch * 32 + c) * KK + tap) * es, es);
+  return ok();
+}
+
+ox_status ox_conv2d_fused_packed(ox_dtype t, const ox_conv_desc* d, const void* X, const void* Wp,
+                                 const void* bias, ox_act act, void* Y, void* stream) {
+  const char* fn = "ox_conv2d_fused_packed";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  st = check_act(fn, act);
+  if (st) return st;
+  int64_t Ho, Wo;
+  st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  if (d->N > 0) {
+    if (!X) return fail(OX_ERR_INVALID_ARG, "%s: X is NULL", fn);
+    if (!Wp) return fail(OX_ERR_INVALID_ARG, "%s: Wp is NULL", fn);
+    if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
+  }
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, X, Wp, bias, Y, (int)act);
+  a.w_packed = 1;
   return conv_dispatch(fn, d, a, stream);
 }
 

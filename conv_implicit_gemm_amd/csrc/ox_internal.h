@@ -85,6 +85,7 @@ struct ConvArgs {
   const void* i8;         // int8 parameter block, channel = m
   int w_vec;              // weight rows allow 16-byte vector loads
   int x_vec;              // (1x1 only) pixel rows allow 16-byte loads
+  int w_packed;           // Wt is in the packed tap-major layout (see ox_conv2d_pack_weights)
 };
 
 // Plan of the LDS-patch 3x3 kernel (host-chosen, passed to the kernel by
@@ -121,7 +122,8 @@ int launch_conv_depthwise(const ConvArgs& a, void* stream);
 // whether the depthwise kernel's LDS band fits this geometry (host only)
 bool depthwise_fits(const ConvArgs& a);
 // 3x3 bf16 convolution with an LDS-staged input patch (group 1, C % 32 == 0)
-bool conv_patch_applicable(const ConvArgs& a);
+bool conv_patch_geometry(const ConvArgs& a);      // dtype/shape conditions only
+bool conv_patch_applicable(const ConvArgs& a);    // plus alignment and a plan that fits
 int launch_conv_patch(const ConvArgs& a, void* stream);
 const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap);
 // Gemm with a single output row (M = 1): memory-bound, no MFMA

@@ -140,7 +140,29 @@ ox_status ox_conv2d_int8(const ox_conv_desc* d, const int8_t* Xq, const int8_t* 
  * 2).  name: HOST buffer of cap bytes (NUL-terminated, truncated to fit). */
 ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_t cap);
 
+/* Convolution with weights packed offline by ox_conv2d_pack_weights.  Same
+ * operation, arguments and errors as ox_conv2d_fused; Wp is the DEVICE copy
+ * of the packed weights.  Only geometries for which
+ * ox_conv2d_packed_weights_bytes() is non-zero have a packed form; those run
+ * the LDS-patch implicit-GEMM kernel, and OX_ERR_UNSUPPORTED is returned when
+ * X or Wp is not 16-byte aligned. */
+ox_status ox_conv2d_fused_packed(ox_dtype t, const ox_conv_desc* d, const void* X, const void* Wp,
+                                 const void* bias, ox_act act, void* Y, void* stream);
+
 /* ------------------------------------------------- offline, host, untimed */
+
+/* Size in bytes of the packed weights of a convolution, or 0 when this
+ * geometry has no packed form (today: bf16, 3x3, group 1, C % 32 == 0,
+ * equal strides of 1 or 2).  The packed size equals the ONNX size. */
+size_t ox_conv2d_packed_weights_bytes(ox_dtype t, const ox_conv_desc* d);
+
+/* Offline weight preparation (the weight half of the "weight/params prep"
+ * step that the BatchNorm fold begins): reorder ONNX weights W[M][C][kH][kW]
+ * into blocks of 32 input channels, tap-major,
+ *   Wp[m][c/32][kh*kW + kw][c%32] = W[m][c][kh][kw],
+ * so that the kernel copies each block's operand tile into LDS as it lies.
+ * W_host, Wp_host: HOST buffers of ox_conv2d_packed_weights_bytes(t, d) bytes. */
+ox_status ox_conv2d_pack_weights(ox_dtype t, const ox_conv_desc* d, const void* W_host, void* Wp_host);
 
 /* BatchNorm fold (tensorforge "ResNet fusion": W' = scale*W, bias = shift;
  * Kyanite "Optimizer": consecutive affine ops merged into one scale + bias,

@@ -214,3 +214,29 @@ def test_int8_prepare_errors(ox):
         ox.ox_int8_prepare(wq, [0.01, 0.01], 0.1, 200, 0.2, 0)    # x_zp out of range
     with pytest.raises(ox.OxError):
         ox.ox_int8_prepare(wq, [0.01, 0.01], float("nan"), 0, 0.2, 0)
+
+
+def test_pack_weights_is_tap_major_channel_blocks(ox):
+    # Wp[m][c/32][tap][c%32] = W[m][c][tap]: checked against a numpy
+    # reshape/transpose of the same array
+    r = np.random.default_rng(4)
+    M, Cin = 5, 64
+    W = r.integers(0, 60000, (M, Cin, 3, 3)).astype(np.uint16)
+    assert ox.ox_conv2d_packed_weights_bytes("bf16", 2, Cin, 9, 9, M, 3, 3, (1, 1), (1, 1, 1, 1)) == W.nbytes
+    Wp = ox.ox_conv2d_pack_weights(W, "bf16", 2, Cin, 9, 9, (1, 1), (1, 1, 1, 1))
+    ref = W.reshape(M, Cin // 32, 32, 9).transpose(0, 1, 3, 2)
+    assert np.array_equal(Wp.reshape(M, Cin // 32, 9, 32), ref)
+
+
+def test_packed_layout_only_where_a_packed_kernel_exists(ox):
+    b = ox.ox_conv2d_packed_weights_bytes
+    assert b("bf16", 1, 48, 9, 9, 8, 3, 3) == 0            # C % 32 != 0
+    assert b("bf16", 1, 64, 9, 9, 8, 5, 5) == 0            # not 3x3
+    assert b("f32", 1, 64, 9, 9, 8, 3, 3) == 0             # bf16 only
+    assert b("bf16", 1, 64, 9, 9, 8, 3, 3, (3, 3)) == 0    # stride 3
+    assert b("bf16", 1, 64, 9, 9, 8, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 2) == 0   # grouped
+    with pytest.raises(ox.OxError):
+        ox.ox_conv2d_pack_weights(np.zeros((8, 48, 3, 3), np.uint16), "bf16", 1, 48, 9, 9)
+    d = desc(ox, Cin=64, M=8)
+    st = raw(ox).ox_conv2d_fused_packed(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None)
+    assert st == 3 and "packed" in ox.ox_last_error()

@@ -417,3 +417,60 @@ def test_patch_conv_sweep_bf16(ox, monkeypatch):
                      "patch %d" % ci)
         ran += 1
     assert ran >= 30
+
+
+def bf16_bits(a64):
+    return synth.f32_to_bf16_bits(a64.astype(np.float32))
+
+
+def run_conv_packed(ox, X, Wt, b, s, pads, d, act):
+    N, Cin, H, W = X.shape
+    M = Wt.shape[0]
+    Wp = ox.ox_conv2d_pack_weights(bf16_bits(Wt), "bf16", N, Cin, H, W, s, pads, d)
+    Wp_dev = torch.from_numpy(Wp.view(np.int16)).cuda().view(torch.bfloat16)
+    ho, wo = ox.conv_out_hw(H, W, 3, 3, s, pads, d)
+    Y = nan_like((N, M, ho, wo), "bf16")
+    ox.ox_conv2d_fused_packed(dev(X, "bf16"), Wp_dev, dev(b, "bf16"), s, pads, d, act=act, Y=Y, M=M)
+    torch.cuda.synchronize()
+    return Y
+
+
+def test_packed_patch_conv_sweep_bf16(ox):
+    r = np.random.default_rng(654)
+    ran = 0
+    for ci in range(50):
+        N = int(r.integers(1, 5))
+        Cin = int(r.choice([32, 64, 96]))
+        H, W = int(r.integers(1, 30)), int(r.integers(1, 30))
+        M = int(r.integers(1, 150))
+        s = int(r.choice([1, 2]))
+        d = int(r.choice([1, 2]))
+        pads = tuple(int(v) for v in r.integers(0, 4, 4))
+        if not conv_case_ok(N, Cin, H, W, M, 3, 3, (s, s), pads, (d, d), 1):
+            continue
+        act = str(r.choice(["none", "relu", "relu6", "gelu"]))
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 3, 3)) / math.sqrt(9 * Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("packed sweep", ci, (N, Cin, H, W, M, s, pads, d, act))
+        Y = run_conv_packed(ox, X, Wt, b, (s, s), pads, (d, d), act)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, (s, s), pads, (d, d), 1, act), "bf16",
+                     "packed %d" % ci)
+        ran += 1
+    assert ran >= 30
+
+
+@pytest.mark.parametrize("N", [1, 32])
+def test_c3_resnet50_3x3_packed(ox, N):
+    for li, layer in enumerate(synth.resnet50_layers(N)):
+        if layer.k != 3:
+            continue
+        say("C3 packed", N, layer.name)
+        X, Wt, b = conv_layer_tensors(layer, 3, li, "bf16")
+        s = (layer.stride, layer.stride)
+        Y = run_conv_packed(ox, X, Wt, b, s, layer.onnx_pads, (1, 1), layer.act)
+        assert not torch.isnan(Y).any().item()
+        got = host64(Y).ravel()
+        idx = sample_indices(got.size, 4096 if N > 1 else got.size, li)
+        ref = oracle.conv2d(X, Wt, b, s, layer.onnx_pads, (1, 1), 1, layer.act, at=idx)
+        assert_close(got[idx], ref, "bf16", layer.name)
