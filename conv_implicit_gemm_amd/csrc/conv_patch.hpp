@@ -3,29 +3,34 @@
 //
 // The generic implicit GEMM gathers every (channel, tap) element of its
 // operand from global memory, i.e. each input value is fetched once per tap.
-// Here a block owns BM output channels and a band of TR output rows (or IMB
-// whole images) and, for each chunk of 32 input channels:
+// Here a block owns BM = 32*WM*FC output channels and a band of TR output
+// rows (or IMB whole images), and for each chunk of 32 input channels:
 //   * stages the input band (with its halo, zero-filled once) in LDS in a
-//     channel-contiguous layout: one 80-byte cell per input position holds the
-//     32 channels (64 bytes) plus 16 bytes of bank padding.  A staging unit
-//     is P (1 or 2) consecutive plane positions x 8 channels: 8 loads of P
-//     elements, repacked by position in registers.  Consecutive lanes take
-//     consecutive positions, so the global loads are contiguous across a wave
-//     and the 16-byte cell writes hit distinct LDS banks;
+//     channel-contiguous layout: one 80-byte cell per input position holds
+//     the 32 channels (64 bytes) plus 16 bytes of bank padding.  A staging
+//     unit is P (1 or 2) consecutive plane positions x 8 channels: 8 loads of
+//     P elements, repacked by position after the barrier.  Consecutive lanes
+//     take consecutive positions, so global loads are contiguous across a
+//     wave and the 16-byte cell writes hit distinct LDS banks;
 //   * stages the weights of the chunk tap-major.  ONNX-layout weights
 //     W[m, c, kh, kw] are read as they lie in memory (8 channels x 9 taps =
 //     9 aligned 16-byte loads) and permuted in registers so that each tap
 //     holds its 32 channels contiguously; weights packed offline in that
 //     tap-major order (ox_conv2d_pack_weights) are a straight, coalesced copy;
-//   * runs 9 taps x (BM/16) x (tiles of 16 pixels) MFMA 16x16x32 bf16: for tap
-//     (kh, kw) the operand of output pixel p is the cell at p's patch position
-//     plus a tap offset, so both MFMA fragments are single 128-bit LDS reads.
+//   * runs 9 taps x 2 (16-channel halves) x FP x FC v_mfma_f32_32x32x16_bf16
+//     per wave.  The pixel operand of output pixel p for tap (kh, kw) is the
+//     cell at p's patch position plus a tap offset, so both MFMA fragments are
+//     single 128-bit LDS reads.
+// Each wave owns a (32*FP pixels) x (32*FC channels) tile: with FP = FC = 2 a
+// 32x32x16 MFMA (full rate with only a few accumulators) consumes 1 KB of
+// fragment reads per 32 cycles, which the LDS sustains for four waves.
 // Columns of the patch are stored de-interleaved by stride phase (S = 2: all
 // even columns, then all odd ones), so consecutive output pixels read
-// consecutive cells for stride 2 as well as stride 1.  Waves form a WM x
-// (4/WM) grid over (output channels) x (pixel tiles).
+// consecutive cells for stride 2 as well as stride 1.
 // The next chunk's global loads are issued before the current chunk's MFMAs
-// and land in registers; one LDS buffer, two barriers per chunk.
+// and land in registers; one LDS buffer, two barriers per chunk.  The
+// epilogue stages the block's bf16 outputs in LDS as [channel][pixel] and
+// writes each channel's run of output pixels with aligned vector stores.
 #pragma once
 
 #include <algorithm>
@@ -34,25 +39,33 @@
 
 namespace ox {
 
-
 namespace patch {
 
 constexpr int kCell = 80;     // bytes per patch cell
-// staging units per thread: 8 registers each, fewer where the accumulators
-// of a wide wave tile need the room
-constexpr int patch_upt(int P, int FN) { return (FN >= 4 ? 4 : 8) / P; }
 constexpr int kKK = 9;
-constexpr int kAROW = kKK * 64 + 16;
+constexpr int kAROW = kKK * 64 + 16;   // bytes per staged weight row
 
-template <int BM, int WM, int FN, int P, int S, bool WPACK>
-__global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf16(const ConvArgs a,
-                                                                                  const PatchPlan pp) {
-  constexpr int WN = 4 / WM;                 // waves along the pixel tiles
-  constexpr int FM = BM / (16 * WM);         // 16-row MFMA tiles per wave
-  // weight staging units per thread: ONNX layout, 8 channels x 9 taps each;
-  // packed layout, one 16-byte vector of a channel block's 576-byte row each
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
+// staging units per thread: 8 registers each, fewer where the weight tile of
+// a 128-channel block needs the room
+constexpr int patch_upt(int P, int BM) { return (BM >= 128 ? 4 : 8) / P; }
+
+__device__ __forceinline__ void mma32(f32x16_t& c, u32x4_t a, u32x4_t b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                              __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+template <int WM, int WN, int FP, int FC, int P, int S, bool WPACK>
+__global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x3_patch_bf16(
+    const ConvArgs a, const PatchPlan pp) {
+  constexpr int BM = 32 * WM * FC;          // output channels per block
+  constexpr int UPT = patch_upt(P, BM);     // patch staging units per thread (max)
+  // weight staging units per thread: packed layout, one 16-byte vector of a
+  // channel row's 576 bytes each; ONNX layout, 8 channels x 9 taps each
   constexpr int WUNITS = WPACK ? BM * 36 / kThreads : BM * 4 / kThreads;
-  constexpr int UPT = patch_upt(P, FN);      // patch staging units per thread (max)
+  static_assert(WM * WN == 4, "four waves");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* As = smem;
   char* Ps = smem + BM * kAROW;
@@ -60,9 +73,13 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int m0 = blockIdx.y * BM;
-  const int bx = blockIdx.x;
+  const int l32 = lane & 31, kg = lane >> 5;
+  // logical tile: channel-block major, so that the blocks of one XCD share
+  // their weight rows
+  const int npb = pp.nrb * pp.nib;
+  const int tile_id = xcd_tile(blockIdx.x, npb * pp.nmb);
+  const int m0 = (tile_id / npb) * BM;
+  const int bx = tile_id - (tile_id / npb) * npb;
   const int img0 = (bx / pp.nrb) * pp.IMB;
   const int oh0 = (bx - (bx / pp.nrb) * pp.nrb) * pp.TR;
   const int rows_here = min(pp.TR, a.Ho - oh0);
@@ -107,7 +124,8 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
         const int f = f0 + e;
         const int pc = iw + a.pl;
         if (f >= flo && f < fhi && pc < pp.PW) {
-          const int cell = (i * pp.PR + ih - ih_base) * pp.PWt + (S == 1 ? pc : (pc & 1) * pp.PWs + (pc >> 1));
+          const int cell =
+              (i * pp.PR + ih - ih_base) * pp.PWt + (S == 1 ? pc : (pc & 1) * pp.PWs + (pc >> 1));
           u_lds[k][e] = cell * kCell + oct * 16;
         }
         if (++iw == W) {
@@ -118,44 +136,41 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
     }
   }
 
-  // this lane's output pixels (one per pixel tile the wave owns)
-  int pbase[FN];
-  bool pvalid[FN], pon[FN];
-  int pimg[FN], prow[FN], pcol[FN];
+  // this lane's pixel (row of the A operand) in each of the wave's FP tiles
+  int pbase[FP];
   const int ppi = pp.TR * a.Wo;
 #pragma unroll
-  for (int f = 0; f < FN; ++f) {
-    const int j = wn + WN * f;
-    const int q = j * 16 + lr;
+  for (int f = 0; f < FP; ++f) {
+    const int q = (wn * FP + f) * 32 + l32;
     const int i = q / ppi;
     const int rem = q - i * ppi;
     const int r = rem / a.Wo;
     const int c = rem - r * a.Wo;
-    pon[f] = j < pp.NT;
-    pvalid[f] = pon[f] && i < imgs_here && r < rows_here;
-    pimg[f] = i;
-    prow[f] = r;
-    pcol[f] = c;
-    pbase[f] = pvalid[f] ? (i * pp.PR + r * S) * pp.PWt + c : 0;
+    const bool valid = q < pp.NT * 32 && i < imgs_here && r < rows_here;
+    pbase[f] = (valid ? (i * pp.PR + r * S) * pp.PWt + c : 0) * kCell + kg * 16;
   }
   int toff[kKK];
 #pragma unroll
   for (int t = 0; t < kKK; ++t) {
     const int kh = t / 3, kw = t % 3;
     const int cw = kw * a.dw;
-    toff[t] = kh * a.dh * pp.PWt + (cw % S) * pp.PWs + cw / S;
+    toff[t] = (kh * a.dh * pp.PWt + (cw % S) * pp.PWs + cw / S) * kCell;
   }
+  // this lane's weight row (column of the B operand) in each of FC tiles
+  int wbase[FC];
+#pragma unroll
+  for (int f = 0; f < FC; ++f) wbase[f] = (wm * FC * 32 + f * 32 + l32) * kAROW + kg * 16;
 
-  f32x4_t acc[FM][FN];
+  f32x16_t acc[FP][FC];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FP; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < FC; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   u32x4_t wreg[WUNITS][WPACK ? 1 : kKK];
-  // raw loaded values (one per channel: P bf16 positions), repacked by
-  // position only after the barrier so the loads stay in flight meanwhile
-  uint32_t xreg[UPT][8];
+  uint32_t xreg[UPT][8];   // raw loaded values: per channel, P bf16 positions
 
   auto load_chunk = [&](int c0) {
     if constexpr (WPACK) {
@@ -255,54 +270,68 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
     store_chunk();
     __syncthreads();
     if (chunk + 1 < nchunks) load_chunk((chunk + 1) * 32);
-    // 9 taps; the fragments of tap t+1 are read while tap t's MFMAs run.
-    // Every wave computes all FN tiles (a tile past NT reads cell 0 and is
-    // discarded), which keeps the loop free of branches.
-    u32x4_t af[2][FM], bf[2][FN];
-    auto read_frags = [&](int t, int buf) {
+    // 18 k-steps (9 taps x 2 halves of 16 channels).  Fragments are read two
+    // steps ahead into a ring of three register sets, and the scheduler is
+    // told to interleave those LDS reads one by one with the MFMAs of the
+    // current step, so that LDS latency hides under matrix-core time.
+    constexpr int NS = 2 * kKK;
+    u32x4_t pf[3][FP], wf[3][FC];
+    auto read_frags = [&](int s, int buf) {
+      const int t = s >> 1, h = (s & 1) * 32;
 #pragma unroll
-      for (int fm = 0; fm < FM; ++fm)
-        af[buf][fm] = *(const u32x4_t*)(As + (wm * FM * 16 + fm * 16 + lr) * kAROW + t * 64 + lg * 16);
+      for (int f = 0; f < FP; ++f) pf[buf][f] = *(const u32x4_t*)(Ps + pbase[f] + toff[t] + h);
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
-        bf[buf][f] = *(const u32x4_t*)(Ps + (pbase[f] + toff[t]) * kCell + lg * 16);
+      for (int f = 0; f < FC; ++f) wf[buf][f] = *(const u32x4_t*)(As + wbase[f] + t * 64 + h);
     };
     read_frags(0, 0);
+    read_frags(1, 1);
 #pragma unroll
-    for (int t = 0; t < kKK; ++t) {
-      if (t + 1 < kKK) read_frags(t + 1, (t + 1) & 1);
+    for (int s = 0; s < NS; ++s) {
+      const bool ahead = s + 2 < NS;
+      if (ahead) read_frags(s + 2, (s + 2) % 3);
 #pragma unroll
-      for (int f = 0; f < FN; ++f)
+      for (int fp = 0; fp < FP; ++fp)
 #pragma unroll
-        for (int fm = 0; fm < FM; ++fm) Mma<DT_BF16>::run(acc[fm][f], bf[t & 1][f], af[t & 1][fm]);
+        for (int fc = 0; fc < FC; ++fc) mma32(acc[fp][fc], pf[s % 3][fp], wf[s % 3][fc]);
+      constexpr int NM = FP * FC, NR = FP + FC;
+#pragma unroll
+      for (int i = 0; i < (NM > NR ? NM : NR); ++i) {
+        if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        if (ahead && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep each step's reads in its own step
     }
   }
 
-  // Epilogue.  With the pixel operand first, lane (lr, lg) holds, for each
-  // tile pair, output channel 16*fm + lr at the 4 consecutive pixel slots
-  // 16*j + 4*lg .. +3.  Bias, activation and bf16 rounding happen here; the
-  // block's tile is then staged in LDS as [channel][pixel slot] so that each
-  // channel's run of output pixels (contiguous in NCHW) is written with the
-  // widest aligned vector stores.
+  // Epilogue.  Lane (l32, kg) holds, for each (fp, fc), output channel
+  // 32*fc + l32 at pixel slots 8*g + 4*kg + (0..3), g = 0..3, of pixel tile
+  // fp.  Bias, activation and bf16 rounding happen here; the block's tile is
+  // then staged in LDS as [channel][pixel slot] so that each channel's run of
+  // output pixels (contiguous in NCHW) is written with aligned vector stores.
   __syncthreads();                       // all waves are done with the patch
-  const int nslot = pp.NT * 16;
+  const int nslot = pp.NT * 32;
   const int erow = nslot + 8;            // elements per staged channel row
   uint16_t* E = (uint16_t*)smem;
   const uint16_t* bias = (const uint16_t*)a.bias;
 #pragma unroll
-  for (int fm = 0; fm < FM; ++fm) {
-    const int ml = wm * FM * 16 + fm * 16 + lr;
+  for (int fc = 0; fc < FC; ++fc) {
+    const int ml = wm * FC * 32 + fc * 32 + l32;
     const float bv = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
 #pragma unroll
-    for (int f = 0; f < FN; ++f) {
-      const int slot = (wn + WN * f) * 16 + lg * 4;
-      if (slot < nslot) {
-        uint32_t lo = (uint32_t)f32_to_bf16(apply_act(a.act, acc[fm][f][0] + bv)) |
-                      ((uint32_t)f32_to_bf16(apply_act(a.act, acc[fm][f][1] + bv)) << 16);
-        uint32_t hi = (uint32_t)f32_to_bf16(apply_act(a.act, acc[fm][f][2] + bv)) |
-                      ((uint32_t)f32_to_bf16(apply_act(a.act, acc[fm][f][3] + bv)) << 16);
-        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-        *(u32x2_t*)(E + ml * erow + slot) = u32x2_t{lo, hi};
+    for (int fp = 0; fp < FP; ++fp) {
+      const int tile = wn * FP + fp;
+      if (tile < pp.NT) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int slot = tile * 32 + 8 * g + 4 * kg;
+          const uint32_t lo =
+              (uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 0] + bv)) |
+              ((uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 1] + bv)) << 16);
+          const uint32_t hi =
+              (uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 2] + bv)) |
+              ((uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 3] + bv)) << 16);
+          *(u32x2_t*)(E + ml * erow + slot) = u32x2_t{lo, hi};
+        }
       }
     }
   }
@@ -330,11 +359,9 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
     const uint16_t* src = E + m * erow + i * ppi + e;
     uint16_t* dst = Y + ((int64_t)(img0 + i) * M + m0 + m) * HoWo + g0 + e;
     if (V == 8) {
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
       const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
       *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
     } else if (V == 4) {
-      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
       *(u32x2_t*)dst = *(const u32x2_t*)src;
     } else if (V == 2) {
       *(uint32_t*)dst = *(const uint32_t*)src;
@@ -344,17 +371,19 @@ __global__ __launch_bounds__(kThreads, (BM == 64 ? 2 : 1)) void conv3x3_patch_bf
   }
 }
 
-template <int BM, int WM, int FN>
+template <int WM, int WN, int FP>
 int launch_cfg(const ConvArgs& a, const PatchPlan& p, hipStream_t s) {
-  dim3 grid(p.nrb * p.nib, (a.M + BM - 1) / BM, 1);
-#define OX_PATCH_LAUNCH(P_, S_)                                                                   \
-  do {                                                                                            \
-    if (a.w_packed)                                                                               \
-      hipLaunchKernelGGL((conv3x3_patch_bf16<BM, WM, FN, P_, S_, true>), grid, dim3(kThreads),  \
-                         p.lds, s, a, p);                                                         \
-    else                                                                                          \
-      hipLaunchKernelGGL((conv3x3_patch_bf16<BM, WM, FN, P_, S_, false>), grid, dim3(kThreads), \
-                         p.lds, s, a, p);                                                         \
+  constexpr int FC = 2;
+  constexpr int BM = 32 * WM * FC;
+  dim3 grid(p.nrb * p.nib * p.nmb, 1, 1);
+#define OX_PATCH_LAUNCH(P_, S_)                                                                  \
+  do {                                                                                           \
+    if (a.w_packed)                                                                              \
+      hipLaunchKernelGGL((conv3x3_patch_bf16<WM, WN, FP, FC, P_, S_, true>), grid,               \
+                         dim3(kThreads), p.lds, s, a, p);                                        \
+    else                                                                                         \
+      hipLaunchKernelGGL((conv3x3_patch_bf16<WM, WN, FP, FC, P_, S_, false>), grid,              \
+                         dim3(kThreads), p.lds, s, a, p);                                        \
   } while (0)
   if (a.sw == 1) {
     if (p.VW == 2) OX_PATCH_LAUNCH(2, 1);
@@ -369,10 +398,11 @@ int launch_cfg(const ConvArgs& a, const PatchPlan& p, hipStream_t s) {
 
 }  // namespace patch
 
-// kernel configurations (one translation unit each)
-int launch_patch_64_1_2(const ConvArgs& a, const PatchPlan& p, void* s);
-int launch_patch_64_1_4(const ConvArgs& a, const PatchPlan& p, void* s);
-int launch_patch_128_2_7(const ConvArgs& a, const PatchPlan& p, void* s);
-int launch_patch_128_2_4(const ConvArgs& a, const PatchPlan& p, void* s);
+// kernel configurations, one translation unit each: launch_patch_<WM>_<WN>_<FP>
+// runs blocks of 64*WM output channels x 32*WN*FP pixel slots
+int launch_patch_1_4_2(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_1_4_1(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_2_2_2(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_2_2_1(const ConvArgs& a, const PatchPlan& p, void* s);
 
 }  // namespace ox

@@ -1,6 +1,6 @@
 // conv_patch_plan.cpp -- host-side planning of the LDS-patch 3x3 kernel:
-// which configuration (rows per block, wave grid, pixel tiles per wave) and
-// which band of output rows / images each block owns.  Pure host code.
+// which configuration (wave grid, pixel tiles per wave) and which band of
+// output rows / images each block owns.  Pure host code.
 #include <algorithm>
 #include <cmath>
 #include <cstdint>
@@ -11,11 +11,10 @@
 
 namespace ox {
 
-
-int launch_patch_64_1_2(const ConvArgs& a, const PatchPlan& p, void* s);
-int launch_patch_64_1_4(const ConvArgs& a, const PatchPlan& p, void* s);
-int launch_patch_128_2_7(const ConvArgs& a, const PatchPlan& p, void* s);
-int launch_patch_128_2_4(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_1_4_2(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_1_4_1(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_2_2_2(const ConvArgs& a, const PatchPlan& p, void* s);
+int launch_patch_2_2_1(const ConvArgs& a, const PatchPlan& p, void* s);
 
 namespace {
 
@@ -23,55 +22,59 @@ constexpr int kCell = 80;
 constexpr int kLdsMax = 160 * 1024;
 constexpr int kCUs = 256;
 
+// wave grid WM x (4/WM), FP 32-pixel tiles per wave, two 32-channel tiles
+// per wave: a block covers 64*WM channels and 32*(4/WM)*FP pixel slots
 struct Cfg {
-  int BM, WM, FN, UPT;
+  int WM, FP;
 };
-const Cfg kCfgs[] = {{64, 1, 2, 0}, {64, 1, 4, 0}, {128, 2, 4, 0}, {128, 2, 7, 0}};
+const Cfg kCfgs[] = {{1, 2}, {1, 1}, {2, 2}, {2, 1}};
+
+int slots_of(const Cfg& c) { return 32 * (4 / c.WM) * c.FP; }
 
 PatchPlan make(const ConvArgs& a, const Cfg& c, int TR, int IMB) {
   PatchPlan p;
-  p.BM = c.BM;
+  p.BM = 64 * c.WM;
   p.WM = c.WM;
-  p.FN = c.FN;
+  p.FN = c.FP;
   p.TR = TR;
   p.IMB = IMB;
   p.PR = (TR - 1) * a.sh + 2 * a.dh + 1;
   p.PW = (a.Wo - 1) * a.sw + 2 * a.dw + 1;
   p.PWs = (p.PW + a.sw - 1) / a.sw;
   p.PWt = p.PWs * a.sw;
-  p.NT = (IMB * TR * a.Wo + 15) / 16;
+  p.NT = (IMB * TR * a.Wo + 31) / 32;
   p.nrb = (a.Ho + TR - 1) / TR;
   p.nib = (a.N + IMB - 1) / IMB;
+  p.nmb = (a.M + p.BM - 1) / p.BM;
   p.npos = IMB * p.PR * p.PWt;
   const int HW = a.H * a.W;
-  p.VW = (HW % 2 == 0) ? 2 : 1;   // positions per staging unit (P)
-  p.UPT = (c.FN >= 4 ? 4 : 8) / p.VW;   // staging units per thread (kernel's patch_upt)
+  p.VW = (HW % 2 == 0) ? 2 : 1;               // positions per staging unit (P)
+  p.UPT = (p.BM >= 128 ? 4 : 8) / p.VW;       // staging units per thread (kernel's patch_upt)
   // staging units: images x 4 channel octets x groups of P plane positions
   // (a band of R rows spans at most R*W + P - 1 positions from a P-aligned start)
   const int rows = std::min(a.H, p.PR);
   p.units = IMB * 4 * ((rows * a.W + 2 * p.VW - 2) / p.VW);
-  p.lds = std::max(c.BM * (9 * 64 + 16) + p.npos * kCell,
-                   c.BM * (p.NT * 16 + 8) * 2);   // the epilogue reuses LDS as [channel][pixel]
+  p.lds = std::max(p.BM * (9 * 64 + 16) + p.npos * kCell,
+                   p.BM * (p.NT * 32 + 8) * 2);   // the epilogue reuses LDS as [channel][pixel]
   return p;
 }
 
 bool fits(const PatchPlan& p) {
   const int ntmax = (4 / p.WM) * p.FN;
   return p.NT <= ntmax && p.lds <= kLdsMax && p.units <= p.UPT * 256 &&
-         (int64_t)p.nrb * p.nib < (1 << 30);
+         (int64_t)p.nrb * p.nib * p.nmb < (1 << 30);
 }
 
 // Rough time model: MFMA cycles per SIMD over the whole grid against the
 // bytes the blocks pull through L2 (every pixel block reads all weights of its
 // channel block; every channel block re-reads the input band with its halo).
 double cost(const ConvArgs& a, const PatchPlan& p) {
-  const int WN = 4 / p.WM;
-  const int FM = p.BM / (16 * p.WM);
   const double mblocks = (a.M + p.BM - 1) / p.BM;
   const double pblocks = (double)p.nrb * p.nib;
   const double blocks = mblocks * pblocks;
   const int per_cu = std::max(1, std::min(p.BM == 64 ? 2 : 1, kLdsMax / p.lds));
-  const double waves_cycles = (a.C / 32) * 9.0 * FM * ((p.NT + WN - 1) / WN) * 16.0;
+  // per wave and chunk: 18 k-steps x FP x 2 MFMAs of 32 cycles
+  const double waves_cycles = (a.C / 32) * 18.0 * p.FN * 2 * 32.0;
   const double rounds = std::ceil(blocks / (kCUs * per_cu));
   const double t_mfma = rounds * per_cu * waves_cycles / 2.4e9;
   const double wbytes = (double)a.M * a.C * 9 * 2;
@@ -84,19 +87,27 @@ double cost(const ConvArgs& a, const PatchPlan& p) {
   return std::max(t_mfma, t_mem) + t_fix;
 }
 
+// the tallest band of at most `slots` pixels, evened out over the image so
+// that the last band is not a sliver
+int band_rows(const ConvArgs& a, int slots) {
+  const int trmax = std::max(1, std::min(a.Ho, slots / std::max(1, a.Wo)));
+  const int nrb = (a.Ho + trmax - 1) / trmax;
+  return (a.Ho + nrb - 1) / nrb;
+}
+
 }  // namespace
 
-// OX_PATCH_PLAN=BM:FN:TR:IMB pins the plan (for measurements); a pinned plan
+// OX_PATCH_PLAN=WM:FP:TR:IMB pins the plan (for measurements); a pinned plan
 // that does not fit this geometry makes the kernel inapplicable.
 bool pinned_plan(const ConvArgs& a, PatchPlan* out, bool* pinned) {
   const char* e = getenv("OX_PATCH_PLAN");
   *pinned = false;
   if (!e || !*e) return false;
-  int bm, fn, tr, imb;
-  if (sscanf(e, "%d:%d:%d:%d", &bm, &fn, &tr, &imb) != 4) return false;
+  int wm, fp, tr, imb;
+  if (sscanf(e, "%d:%d:%d:%d", &wm, &fp, &tr, &imb) != 4) return false;
   *pinned = true;
   for (const Cfg& c : kCfgs) {
-    if (c.BM != bm || c.FN != fn) continue;
+    if (c.WM != wm || c.FP != fp) continue;
     if (tr < 1 || tr > a.Ho || imb < 1 || (imb > 1 && tr != a.Ho)) return false;
     const PatchPlan p = make(a, c, tr, imb);
     if (!fits(p)) return false;
@@ -110,26 +121,29 @@ bool patch_plan(const ConvArgs& a, PatchPlan* out) {
   bool pinned;
   const bool ok = pinned_plan(a, out, &pinned);
   if (pinned) return ok;
-  // Selection rule, from a sweep of every configuration / band height on the
-  // ResNet-50 3x3 layers at batch 32 (MI355X): 64 output channels per block
-  // with 2 pixel tiles per wave (up to 128 output pixels in one image) was
-  // fastest on all seven shapes; take the tallest band within that limit
-  // that fits LDS and the staging registers.
-  const Cfg& c = kCfgs[0];   // {64, 1, 2}
-  const int tr0 = std::max(1, std::min(a.Ho, 128 / std::max(1, a.Wo)));
-  for (int TR = tr0; TR >= 1; --TR) {
-    const PatchPlan p = make(a, c, TR, 1);
-    if (fits(p)) {
-      *out = p;
-      return true;
+  // Selection rule, from a sweep of every configuration and band height on
+  // the ResNet-50 3x3 layers at batch 32 (MI355X): 64 output channels per
+  // block won on every shape; 128-pixel blocks (one pixel tile per wave) won
+  // wherever such a block holds at least three output rows, 256-pixel blocks
+  // on the wide 56-column layer.  The band is the tallest that fits the
+  // block, evened out over the image.
+  {
+    const int wo = std::max(1, a.Wo);
+    const Cfg& c = (128 / wo >= 3 || a.Ho <= 128 / wo) ? kCfgs[1] : kCfgs[0];
+    for (int TR = band_rows(a, slots_of(c)); TR >= 1; --TR) {
+      const PatchPlan p = make(a, c, TR, 1);
+      if (fits(p)) {
+        *out = p;
+        return true;
+      }
     }
   }
-  // wide rows (Wo > 128): fall back to the cost model over every configuration
   bool found = false;
   double best = 1e30;
-  for (const Cfg& cc : kCfgs) {
+  // rows wider than a block: every configuration and band height
+  for (const Cfg& c : kCfgs) {
     for (int TR = 1; TR <= a.Ho; ++TR) {
-      const PatchPlan p = make(a, cc, TR, 1);
+      const PatchPlan p = make(a, c, TR, 1);
       if (!fits(p)) continue;
       const double t = cost(a, p);
       if (t < best * 0.999) {
@@ -157,17 +171,17 @@ bool conv_patch_applicable(const ConvArgs& a) {
 int launch_conv_patch(const ConvArgs& a, void* stream) {
   PatchPlan p;
   if (!patch_plan(a, &p)) return 1;  // hipErrorInvalidValue
-  if (p.BM == 64) {
-    return p.FN == 2 ? launch_patch_64_1_2(a, p, stream) : launch_patch_64_1_4(a, p, stream);
+  if (p.WM == 1) {
+    return p.FN == 2 ? launch_patch_1_4_2(a, p, stream) : launch_patch_1_4_1(a, p, stream);
   }
-  return p.FN == 4 ? launch_patch_128_2_4(a, p, stream) : launch_patch_128_2_7(a, p, stream);
+  return p.FN == 2 ? launch_patch_2_2_2(a, p, stream) : launch_patch_2_2_1(a, p, stream);
 }
 
 const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap) {
   PatchPlan p;
   if (!patch_plan(a, &p)) return "";
-  snprintf(buf, cap, "BM=%d WM=%d FN=%d TR=%d IMB=%d NT=%d VW=%d blocks=%lld lds=%d", p.BM, p.WM,
-           p.FN, p.TR, p.IMB, p.NT, p.VW, (long long)p.nrb * p.nib * ((a.M + p.BM - 1) / p.BM), p.lds);
+  snprintf(buf, cap, "BM=%d WM=%d FP=%d TR=%d IMB=%d NT=%d VW=%d blocks=%lld lds=%d", p.BM, p.WM,
+           p.FN, p.TR, p.IMB, p.NT, p.VW, (long long)p.nrb * p.nib * p.nmb, p.lds);
   return buf;
 }
 

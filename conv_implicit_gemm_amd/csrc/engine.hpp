@@ -40,6 +40,18 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 256;
 
+// The chip's 256 CUs sit in 8 XCDs, each with its own L2; consecutive block
+// ids are dispatched round-robin over the XCDs.  xcd_tile maps a block id to
+// a logical tile so that each XCD runs one contiguous range of the logical
+// order: blocks that share an operand tile (same weight rows) then hit the
+// same L2.  A bijection on [0, total) for any total.
+constexpr int kXcds = 8;
+__device__ __forceinline__ int xcd_tile(int b, int total) {
+  const int q = total / kXcds, r = total - q * kXcds;
+  const int x = b % kXcds, local = b / kXcds;
+  return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
 template <int DT> struct Traits;
 template <> struct Traits<DT_F32> {
   typedef float T;

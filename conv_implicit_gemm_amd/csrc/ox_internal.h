@@ -91,16 +91,17 @@ struct ConvArgs {
 // Plan of the LDS-patch 3x3 kernel (host-chosen, passed to the kernel by
 // value): configuration, block band and patch geometry.
 struct PatchPlan {
-  int BM, WM, FN, UPT;  // rows per block, wave rows, pixel tiles per wave, staging units per thread
+  int BM, WM, FN, UPT;  // channels per block, wave rows, 32-pixel tiles per wave, staging units per thread
   int TR;               // output rows per block (per image)
   int IMB;              // images per block (> 1 only when TR == Ho)
   int PR;               // patch rows per image
   int PWs;              // patch columns per stride phase
   int PWt;              // patch row length in cells (stride * PWs)
   int PW;               // patch columns used
-  int NT;               // 16-pixel tiles per block
+  int NT;               // 32-pixel tiles per block
   int nrb;              // row blocks per image
   int nib;              // image blocks
+  int nmb;              // output-channel blocks
   int npos;             // cells in the patch (IMB * PR * PWt)
   int VW;               // plane positions per staging unit (1 or 2)
   int units;            // upper bound of staging units per block

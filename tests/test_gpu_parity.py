@@ -460,6 +460,38 @@ def test_packed_patch_conv_sweep_bf16(ox):
     assert ran >= 30
 
 
+@pytest.mark.parametrize("cfg", ["1:2", "1:1", "2:2", "2:1"])
+def test_patch_each_config(ox, cfg, monkeypatch):
+    # every block configuration of the 3x3 kernel (wave grid : pixel tiles
+    # per wave), pinned, over both strides, both staging widths (even and odd
+    # plane sizes), ONNX-layout and packed weights, and partial channel blocks
+    r = np.random.default_rng(77 + int(cfg[0]) * 10 + int(cfg[2]))
+    monkeypatch.setenv("OX_FORCE_KERNEL", "patch")
+    ran = 0
+    for ci, (N, Cin, H, W, M, s, pads) in enumerate([
+            (2, 64, 14, 14, 64, 1, (1, 1, 1, 1)), (3, 32, 9, 7, 96, 1, (1, 1, 1, 1)),
+            (2, 96, 16, 12, 130, 2, (1, 1, 1, 1)), (1, 32, 13, 11, 40, 2, (0, 1, 2, 1))]):
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 3, 3)) / math.sqrt(9 * Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        ho, wo = ox.conv_out_hw(H, W, 3, 3, (s, s), pads, (1, 1))
+        ref = oracle.conv2d(X, Wt, b, (s, s), pads, (1, 1), 1, "relu")
+        for tr in range(ho, 0, -1):
+            monkeypatch.setenv("OX_PATCH_PLAN", "%s:%d:1" % (cfg, tr))
+            try:
+                ox.ox_conv2d_variant("bf16", N, Cin, H, W, M, 3, 3, (s, s), pads, (1, 1), 1)
+            except ox.OxError:
+                continue
+            say("patch config", cfg, "TR", tr, (N, Cin, H, W, M, s, pads))
+            Y = run_conv(ox, X, Wt, b, "bf16", (s, s), pads, (1, 1), 1, "relu")
+            assert_close(host64(Y), ref, "bf16", "config %s case %d" % (cfg, ci))
+            Y = run_conv_packed(ox, X, Wt, b, (s, s), pads, (1, 1), "relu")
+            assert_close(host64(Y), ref, "bf16", "packed config %s case %d" % (cfg, ci))
+            ran += 1
+            break
+    assert ran == 4
+
+
 @pytest.mark.parametrize("N", [1, 32])
 def test_c3_resnet50_3x3_packed(ox, N):
     for li, layer in enumerate(synth.resnet50_layers(N)):
