@@ -45,17 +45,9 @@ constexpr int kCell = 80;     // bytes per patch cell
 constexpr int kKK = 9;
 constexpr int kAROW = kKK * 64 + 16;   // bytes per staged weight row
 
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-
 // staging units per thread: 8 registers each, fewer where the weight tile of
 // a 128-channel block needs the room
 constexpr int patch_upt(int P, int BM) { return (BM >= 128 ? 4 : 8) / P; }
-
-__device__ __forceinline__ void mma32(f32x16_t& c, u32x4_t a, u32x4_t b) {
-  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                              __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-}
 
 template <int WM, int WN, int FP, int FC, int P, int S, bool WPACK>
 __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x3_patch_bf16(
@@ -313,28 +305,35 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   const int erow = nslot + 8;            // elements per staged channel row
   uint16_t* E = (uint16_t*)smem;
   const uint16_t* bias = (const uint16_t*)a.bias;
+  float bv[FC];
 #pragma unroll
   for (int fc = 0; fc < FC; ++fc) {
     const int ml = wm * FC * 32 + fc * 32 + l32;
-    const float bv = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+  }
+  with_act(a.act, [&](auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
-    for (int fp = 0; fp < FP; ++fp) {
-      const int tile = wn * FP + fp;
-      if (tile < pp.NT) {
+    for (int fc = 0; fc < FC; ++fc) {
+      const int ml = wm * FC * 32 + fc * 32 + l32;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int slot = tile * 32 + 8 * g + 4 * kg;
-          const uint32_t lo =
-              (uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 0] + bv)) |
-              ((uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 1] + bv)) << 16);
-          const uint32_t hi =
-              (uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 2] + bv)) |
-              ((uint32_t)f32_to_bf16(apply_act(a.act, acc[fp][fc][4 * g + 3] + bv)) << 16);
-          *(u32x2_t*)(E + ml * erow + slot) = u32x2_t{lo, hi};
+      for (int fp = 0; fp < FP; ++fp) {
+        const int tile = wn * FP + fp;
+        if (tile < pp.NT) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int slot = tile * 32 + 8 * g + 4 * kg;
+            const f32x16_t& c = acc[fp][fc];
+            const uint32_t lo = pack_bf16x2(act_c<ACT>(c[4 * g + 0] + bv[fc]),
+                                            act_c<ACT>(c[4 * g + 1] + bv[fc]));
+            const uint32_t hi = pack_bf16x2(act_c<ACT>(c[4 * g + 2] + bv[fc]),
+                                            act_c<ACT>(c[4 * g + 3] + bv[fc]));
+            *(u32x2_t*)(E + ml * erow + slot) = u32x2_t{lo, hi};
+          }
         }
       }
     }
-  }
+  });
   __syncthreads();
   // runs: for image i of the block and channel m, output pixels
   // [oh0*Wo, (oh0 + rows_here)*Wo) of plane (img0+i, m0+m) come from slots

@@ -1,0 +1,322 @@
+// conv_pw.hpp -- pointwise (1x1, stride 1, unpadded) convolution on NCHW,
+// bf16, as one GEMM over all pixels of the batch (instantiated by
+// k_conv_pw_*.hip).
+//
+// Y[n, m, p] = act(bias[m] + sum_c W[m, c] * X[n, c, p]).  The pixels of the
+// batch are flattened (q = n*HW + p) and a block owns BN consecutive pixels
+// x BM output channels.  For each chunk of KC input channels it
+//   * stages the pixels channel-contiguous in LDS: one (2*KC + 16)-byte row
+//     per pixel (KC channels plus 16 bytes of bank padding).  A staging unit
+//     is P consecutive pixels x 8 channels: 8 loads of P elements, with
+//     consecutive lanes on consecutive pixel groups (coalesced along the
+//     plane), repacked by pixel into 16-byte row pieces;
+//   * stages the weight rows W[m, c0 .. c0+KC) with 16-byte loads (the ONNX
+//     layout already has each row's channels contiguous);
+//   * runs KC/16 k-steps of FP x FC v_mfma_f32_32x32x16_bf16 per wave, both
+//     fragments single 128-bit LDS reads, read two steps ahead and
+//     interleaved with the MFMAs.
+// The next chunk's global loads are in flight (in registers) while the
+// current chunk is multiplied.  The epilogue (bias, activation, bf16
+// rounding) stages the tile in LDS as [channel][pixel] and writes each
+// channel's pixels with aligned vector stores.  Consecutive block ids walk
+// the channel blocks of one pixel block first, so the blocks that share a
+// pixel tile run on one XCD at about the same time.
+#pragma once
+
+#include "engine.hpp"
+
+namespace ox {
+
+namespace pw {
+
+template <int WM, int WN, int FP, int FC, int KC, int P>
+__global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, const PwPlan pl) {
+  constexpr int BM = 32 * WM * FC;          // output channels per block
+  constexpr int BN = 32 * WN * FP;          // pixels per block
+  constexpr int ROW = KC * 2 + 16;          // bytes per staged row
+  constexpr int NG = BN / P;                // pixel groups per block
+  constexpr int XU = (KC / 8) * NG;         // pixel staging units per chunk
+  constexpr int XUPT = (XU + kThreads - 1) / kThreads;
+  constexpr int WPR = KC / 8;               // 16-byte weight pieces per row
+  constexpr int WU = BM * WPR;
+  constexpr int WUPT = (WU + kThreads - 1) / kThreads;
+  constexpr int NS = KC / 16;               // k-steps per chunk
+  static_assert(WM * WN == 4, "four waves");
+  static_assert(BN % P == 0 && KC % 32 == 0, "tile shape");
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  char* As = smem;                 // weights [BM][ROW]
+  char* Xs = smem + BM * ROW;      // pixels  [BN][ROW]
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int total = pl.npb * pl.nmb;
+  const int HW = a.H * a.W, C = a.C, M = a.M;
+  const int Q = a.N * HW;
+  const uint16_t* Xg = (const uint16_t*)a.X;
+  const uint16_t* Wg = (const uint16_t*)a.Wt;
+  uint16_t* Y = (uint16_t*)a.Y;
+  const uint16_t* bias = (const uint16_t*)a.bias;
+
+  // Persistent blocks: block b runs tiles b, b + G, b + 2G, ... (G = grid
+  // size, a multiple of the XCD count when it is below the tile count), so a
+  // block stays on one XCD and xcd_tile keeps each XCD on one contiguous
+  // range of logical tiles.  The next tile's first chunk is loaded while the
+  // current tile finishes its MFMAs and epilogue.
+  int t = blockIdx.x;
+  if (t >= total) return;
+  int pb, m0;
+  auto decode = [&](int tt) {
+    const int logical = xcd_tile(tt, total);
+    pb = logical / pl.nmb;
+    m0 = (logical - pb * pl.nmb) * BM;
+  };
+
+  // this thread's pixel staging units: element offset of the first value
+  // (-1: none) and LDS offset of its first row piece
+  int x_goff[XUPT], x_lds[XUPT];
+  int w_goff[WUPT], w_lds[WUPT];
+#pragma unroll
+  for (int k = 0; k < XUPT; ++k) {
+    const int u = tid + k * kThreads;
+    x_lds[k] = u < XU ? (u % NG) * P * ROW + (u / NG) * 16 : 0;
+  }
+#pragma unroll
+  for (int k = 0; k < WUPT; ++k) {
+    const int v = tid + k * kThreads;
+    w_lds[k] = (v / WPR) * ROW + (v % WPR) * 16;
+  }
+  auto tile_offsets = [&]() {
+    const int q0 = pb * BN;
+#pragma unroll
+    for (int k = 0; k < XUPT; ++k) {
+      const int u = tid + k * kThreads;
+      x_goff[k] = -1;
+      if (u < XU) {
+        const int oct = u / NG, g = u - (u / NG) * NG;
+        const int q = q0 + g * P;
+        if (q < Q) {
+          const int n = q / HW;
+          x_goff[k] = (n * C + oct * 8) * HW + (q - n * HW);
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < WUPT; ++k) {
+      const int v = tid + k * kThreads;
+      const int m = v / WPR, j = v - (v / WPR) * WPR;
+      w_goff[k] = (v < WU && m0 + m < M) ? (m0 + m) * C + j * 8 : -1;
+    }
+  };
+
+  const int pbase = (wn * FP * 32 + l32) * ROW + kg * 16;   // + f*32*ROW
+  const int wbase = (wm * FC * 32 + l32) * ROW + kg * 16;   // + f*32*ROW
+
+  f32x16_t acc[FP][FC];
+  // P = 1: one bf16 per load; P = 2: one dword; P = 4: two dwords
+  constexpr int XR = P == 4 ? 2 : 1;
+  uint32_t xreg[XUPT][8][XR];
+  u32x4_t wreg[WUPT];
+
+  auto load_chunk = [&](int c0) {
+#pragma unroll
+    for (int k = 0; k < WUPT; ++k) {
+      if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU) {
+        if (w_goff[k] >= 0) wreg[k] = *(const u32x4_t*)(Wg + w_goff[k] + c0);
+        else wreg[k] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < XUPT; ++k) {
+      if (x_goff[k] >= 0) {
+        const uint16_t* src = Xg + x_goff[k] + c0 * HW;
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch) {
+          if constexpr (P == 1) {
+            xreg[k][ch][0] = src[ch * HW];
+          } else if constexpr (P == 2) {
+            xreg[k][ch][0] = *(const uint32_t*)(src + ch * HW);
+          } else {
+            const u32x2_t v = *(const u32x2_t*)(src + ch * HW);
+            xreg[k][ch][0] = v[0];
+            xreg[k][ch][1] = v[1];
+          }
+        }
+      } else {
+#pragma unroll
+        for (int ch = 0; ch < 8; ++ch)
+#pragma unroll
+          for (int r = 0; r < XR; ++r) xreg[k][ch][r] = 0u;
+      }
+    }
+  };
+
+  auto store_chunk = [&]() {
+#pragma unroll
+    for (int k = 0; k < WUPT; ++k)
+      if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU)
+        *(u32x4_t*)(As + w_lds[k]) = wreg[k];
+#pragma unroll
+    for (int k = 0; k < XUPT; ++k) {
+      if (k * kThreads + kThreads <= XU || tid + k * kThreads < XU) {
+#pragma unroll
+        for (int e = 0; e < P; ++e) {
+          // pixel e of the unit: bf16 number e of each channel's loaded P
+          uint32_t d[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t lo = xreg[k][2 * j][e >> 1], hi = xreg[k][2 * j + 1][e >> 1];
+            if constexpr (P == 1) d[j] = (lo & 0xffffu) | (hi << 16);
+            else if ((e & 1) == 0) d[j] = (lo & 0xffffu) | (hi << 16);
+            else d[j] = (lo >> 16) | (hi & 0xffff0000u);
+          }
+          *(u32x4_t*)(Xs + x_lds[k] + e * ROW) = u32x4_t{d[0], d[1], d[2], d[3]};
+        }
+      }
+    }
+  };
+
+  auto epilogue = [&](const int q0, const int m0) {
+    // Epilogue: lane (l32, kg) holds, for each (fp, fc), channel 32*fc + l32
+    // at pixel slots 8*g + 4*kg + (0..3) of pixel tile fp.  Stage the block's
+    // bf16 outputs as E[channel][pixel], then store channel rows.
+    __syncthreads();
+    constexpr int EROW = BN + 8;
+    uint16_t* E = (uint16_t*)smem;
+    float bv[FC];
+#pragma unroll
+    for (int fc = 0; fc < FC; ++fc) {
+      const int ml = wm * FC * 32 + fc * 32 + l32;
+      bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+    }
+    with_act(a.act, [&](auto act_k) {
+      constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+      for (int fc = 0; fc < FC; ++fc) {
+        const int ml = wm * FC * 32 + fc * 32 + l32;
+#pragma unroll
+        for (int fp = 0; fp < FP; ++fp) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int slot = (wn * FP + fp) * 32 + 8 * g + 4 * kg;
+            const f32x16_t& c = acc[fp][fc];
+            const uint32_t lo = pack_bf16x2(act_c<ACT>(c[4 * g + 0] + bv[fc]),
+                                            act_c<ACT>(c[4 * g + 1] + bv[fc]));
+            const uint32_t hi = pack_bf16x2(act_c<ACT>(c[4 * g + 2] + bv[fc]),
+                                            act_c<ACT>(c[4 * g + 3] + bv[fc]));
+            *(u32x2_t*)(E + ml * EROW + slot) = u32x2_t{lo, hi};
+          }
+        }
+      }
+    });
+    __syncthreads();
+    const int mvalid = min(BM, M - m0);
+    const int V = pl.V;                      // HW % V == 0 and Y is 2V-byte aligned
+    const int per_row = BN / V;
+    const int items = mvalid * per_row;
+    for (int it = tid; it < items; it += kThreads) {
+      const int m = it / per_row;
+      const int e = (it - m * per_row) * V;
+      const int q = q0 + e;
+      if (q >= Q) continue;
+      const int n = q / HW;
+      const uint16_t* src = E + m * EROW + e;
+      uint16_t* dst = Y + ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
+      if (V == 8) {
+        const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
+        *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+      } else if (V == 4) {
+        *(u32x2_t*)dst = *(const u32x2_t*)src;
+      } else if (V == 2) {
+        *(uint32_t*)dst = *(const uint32_t*)src;
+      } else {
+        *dst = *src;
+      }
+    }
+  };
+
+  const int nchunks = C / KC;
+  decode(t);
+  tile_offsets();
+  load_chunk(0);
+  for (;;) {
+    const int cur_pb = pb, cur_m0 = m0;
+    const int next = t + (int)gridDim.x;
+#pragma unroll
+    for (int i = 0; i < FP; ++i)
+#pragma unroll
+      for (int j = 0; j < FC; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    for (int chunk = 0; chunk < nchunks; ++chunk) {
+      __syncthreads();               // LDS is free: previous MFMAs and epilogue are done
+      store_chunk();
+      __syncthreads();
+      if (chunk + 1 < nchunks) {
+        load_chunk((chunk + 1) * KC);
+      } else if (next < total) {
+        decode(next);
+        tile_offsets();
+        load_chunk(0);
+      }
+      u32x4_t pf[3][FP], wf[3][FC];
+      auto read_frags = [&](int s, int buf) {
+#pragma unroll
+        for (int f = 0; f < FP; ++f) pf[buf][f] = *(const u32x4_t*)(Xs + pbase + f * 32 * ROW + s * 32);
+#pragma unroll
+        for (int f = 0; f < FC; ++f) wf[buf][f] = *(const u32x4_t*)(As + wbase + f * 32 * ROW + s * 32);
+      };
+      read_frags(0, 0);
+      if (NS > 1) read_frags(1, 1);
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bool ahead = s + 2 < NS;
+        if (ahead) read_frags(s + 2, (s + 2) % 3);
+#pragma unroll
+        for (int fp = 0; fp < FP; ++fp)
+#pragma unroll
+          for (int fc = 0; fc < FC; ++fc) mma32(acc[fp][fc], pf[s % 3][fp], wf[s % 3][fc]);
+        constexpr int NM = FP * FC, NR = FP + FC;
+#pragma unroll
+        for (int i = 0; i < (NM > NR ? NM : NR); ++i) {
+          if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+          if (ahead && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+    epilogue(cur_pb * BN, cur_m0);
+    if (next >= total) break;
+    t = next;
+  }
+}
+template <int WM, int WN, int KC>
+int launch_cfg(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
+  constexpr int FP = 2, FC = 2;
+  dim3 grid(p.grid, 1, 1);
+  switch (p.P) {
+    case 4:
+      hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 4>), grid, dim3(kThreads), p.lds, s, a, p);
+      break;
+    case 2:
+      hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 2>), grid, dim3(kThreads), p.lds, s, a, p);
+      break;
+    default:
+      hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 1>), grid, dim3(kThreads), p.lds, s, a, p);
+      break;
+  }
+  return (int)hipGetLastError();
+}
+
+}  // namespace pw
+
+// launch_pw_<WM>_<KC>: blocks of 64*WM channels x 32*(4/WM)*2 pixels, KC
+// input channels per chunk (wider chunks would not fit the staging
+// registers next to the accumulators)
+int launch_pw_1_32(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pw_1_64(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pw_2_32(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pw_2_64(const ConvArgs& a, const PwPlan& p, void* s);
+
+}  // namespace ox

@@ -1,0 +1,109 @@
+// conv_pw_plan.cpp -- host-side planning of the pointwise (1x1) kernel.
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+
+#include "ox_internal.h"
+
+namespace ox {
+
+int launch_pw_1_32(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pw_1_64(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pw_2_32(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pw_2_64(const ConvArgs& a, const PwPlan& p, void* s);
+
+namespace {
+
+constexpr int kLdsMax = 160 * 1024;
+constexpr int kCUs = 256;        // kCUs is a multiple of the 8 XCDs
+constexpr int kMaxPerCu = 2;
+
+bool geometry(const ConvArgs& a) {
+  return a.dt == DT_BF16 && a.group == 1 && a.kH == 1 && a.kW == 1 && a.sh == 1 && a.sw == 1 &&
+         a.pt == 0 && a.pl == 0 && a.Ho == a.H && a.Wo == a.W && a.C % 32 == 0 && a.C > 0;
+}
+
+PwPlan make(const ConvArgs& a, int WM, int KC) {
+  PwPlan p;
+  p.WM = WM;
+  p.KC = KC;
+  const int HW = a.H * a.W;
+  const uintptr_t xa = (uintptr_t)a.X, ya = (uintptr_t)a.Y;
+  p.P = (HW % 4 == 0 && xa % 8 == 0) ? 4 : (HW % 2 == 0 && xa % 4 == 0) ? 2 : 1;
+  p.V = 8;
+  while (p.V > 1 && (HW % p.V || ya % (2 * p.V))) p.V >>= 1;
+  const int BM = 64 * WM, BN = 32 * (4 / WM) * 2;
+  const int64_t Q = (int64_t)a.N * HW;
+  p.npb = (int)((Q + BN - 1) / BN);
+  p.nmb = (a.M + BM - 1) / BM;
+  const int row = KC * 2 + 16;
+  p.lds = std::max((BM + BN) * row, BM * (BN + 8) * 2);
+  // persistent grid: as many blocks as fit the chip at once (LDS-bound, at
+  // most kMaxPerCu per CU), a multiple of the XCD count when tiles are left over
+  int per_cu = std::max(1, std::min(kMaxPerCu, kLdsMax / p.lds));
+  if (const char* e = getenv("OX_PW_PER_CU")) per_cu = std::max(1, std::min(8, atoi(e)));
+  const int64_t tiles = (int64_t)p.npb * p.nmb;
+  const int64_t cap = (int64_t)kCUs * per_cu;
+  p.grid = (int)std::min(tiles, cap);
+  return p;
+}
+
+bool valid(const ConvArgs& a, const PwPlan& p) {
+  // (a 256-pixel block staging single pixels takes 32-channel chunks: the
+  // registers of 64 would spill)
+  return a.C % p.KC == 0 && p.KC <= 64 && !(p.WM == 1 && p.P == 1 && p.KC > 32) &&
+         p.lds <= kLdsMax &&
+         (int64_t)p.npb * p.nmb < (int64_t)1 << 31;
+}
+
+// OX_PW_PLAN=WM:KC pins the configuration (for measurements); a pinned
+// configuration that does not apply makes the kernel inapplicable.
+bool pw_plan(const ConvArgs& a, PwPlan* out) {
+  if (!geometry(a)) return false;
+  const char* e = getenv("OX_PW_PLAN");
+  int wm, kc;
+  if (e && *e && sscanf(e, "%d:%d", &wm, &kc) == 2) {
+    if ((wm != 1 && wm != 2) || (kc != 32 && kc != 64)) return false;
+    const PwPlan p = make(a, wm, kc);
+    if (!valid(a, p)) return false;
+    *out = p;
+    return true;
+  }
+  // 64-channel blocks when M fits one, else 128 x 128; the widest channel
+  // chunk that divides C (fewer barriers, more bytes in flight per chunk)
+  const int WM = a.M <= 64 ? 1 : 2;
+  for (int kc : {64, 32}) {
+    const PwPlan p = make(a, WM, kc);
+    if (valid(a, p)) {
+      *out = p;
+      return true;
+    }
+  }
+  return false;
+}
+
+}  // namespace
+
+bool conv_pw_applicable(const ConvArgs& a) {
+  if (!a.w_vec || ((uintptr_t)a.X) % 2 != 0) return false;
+  PwPlan p;
+  return pw_plan(a, &p);
+}
+
+int launch_conv_pw(const ConvArgs& a, void* stream) {
+  PwPlan p;
+  if (!pw_plan(a, &p)) return 1;   // hipErrorInvalidValue
+  if (p.WM == 1) return p.KC == 64 ? launch_pw_1_64(a, p, stream) : launch_pw_1_32(a, p, stream);
+  return p.KC == 64 ? launch_pw_2_64(a, p, stream) : launch_pw_2_32(a, p, stream);
+}
+
+const char* conv_pw_describe(const ConvArgs& a, char* buf, int cap) {
+  PwPlan p;
+  if (!pw_plan(a, &p)) return "";
+  snprintf(buf, cap, "BM=%d BN=%d KC=%d P=%d V=%d tiles=%lld grid=%d lds=%d", 64 * p.WM,
+           64 * (4 / p.WM), p.KC, p.P, p.V, (long long)p.npb * p.nmb, p.grid, p.lds);
+  return buf;
+}
+
+}  // namespace ox

@@ -27,6 +27,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 #include <stdint.h>
 
 #include "ox_internal.h"
@@ -37,6 +39,8 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
 
@@ -50,6 +54,15 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
   const int q = total / kXcds, r = total - q * kXcds;
   const int x = b % kXcds, local = b / kXcds;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+// One v_mfma_f32_32x32x16_bf16: c[32x32] += a[32x16] * b[16x32].  Lane l
+// supplies row (a) / column (b) l%32 with k = 8*(l/32) .. 8*(l/32)+7 as 8
+// bf16 in one 128-bit register quad; accumulator element i of lane l is
+// row 8*(i/4) + 4*(l/32) + i%4, column l%32.
+__device__ __forceinline__ void mma32(f32x16_t& c, u32x4_t a, u32x4_t b) {
+  c = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                              __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
 template <int DT> struct Traits;
@@ -81,6 +94,14 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Two fp32 -> packed bf16 pair (low half = lo), round to nearest even, in
+// one gfx950 v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 template <typename T> __device__ __forceinline__ float to_f32(T v);
@@ -129,6 +150,28 @@ __device__ __forceinline__ float apply_act(int act, float v) {
     case ACT_RELU6: return fminf(fmaxf(v, 0.0f), 6.0f);
     case ACT_GELU: return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
     default: return v;
+  }
+}
+
+// The same activations with the choice made at compile time: an epilogue
+// that runs one per element must not carry a switch (and the GELU code) per
+// element.  with_act(act, f) calls f(std::integral_constant<int, ACT>{}) for
+// the runtime act, so the body is compiled once per activation.
+template <int ACT>
+__device__ __forceinline__ float act_c(float v) {
+  if constexpr (ACT == ACT_RELU) return fmaxf(v, 0.0f);
+  else if constexpr (ACT == ACT_RELU6) return fminf(fmaxf(v, 0.0f), 6.0f);
+  else if constexpr (ACT == ACT_GELU) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
+  else return v;
+}
+
+template <typename F>
+__device__ __forceinline__ void with_act(int act, F&& f) {
+  switch (act) {
+    case ACT_RELU: f(std::integral_constant<int, ACT_RELU>{}); break;
+    case ACT_RELU6: f(std::integral_constant<int, ACT_RELU6>{}); break;
+    case ACT_GELU: f(std::integral_constant<int, ACT_GELU>{}); break;
+    default: f(std::integral_constant<int, ACT_NONE>{}); break;
   }
 }
 

@@ -78,13 +78,16 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
   } else {
     T* Y = (T*)a.Y + (int64_t)z * a.sy;
     const T* bias = (const T*)a.bias;
-    for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
-      const int row = row0 + r, col = col0 + c;
-      if (row < a.rows && col < a.cols) {
-        float o = a.alpha * v;
-        if (bias) o += a.beta * to_f32(bias[col]);
-        store_float(Y + (int64_t)row * a.ldy + col, apply_act(a.act, o));
-      }
+    with_act(a.act, [&](auto act_k) {
+      constexpr int ACT = decltype(act_k)::value;
+      for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+        const int row = row0 + r, col = col0 + c;
+        if (row < a.rows && col < a.cols) {
+          float o = a.alpha * v;
+          if (bias) o += a.beta * to_f32(bias[col]);
+          store_float(Y + (int64_t)row * a.ldy + col, act_c<ACT>(o));
+        }
+      });
     });
   }
 }
@@ -209,14 +212,17 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
   } else {
     T* Y = (T*)a.Y;
     const T* bias = (const T*)a.bias;
-    for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
-      const int ml = row0 + r, col = col0 + c;
-      if (ml < Mpg && col < NP) {
-        const int m = g * Mpg + ml;
-        float o = v;
-        if (bias) o += to_f32(bias[m]);
-        store_float(Y + out_index(m, col), apply_act(a.act, o));
-      }
+    with_act(a.act, [&](auto act_k) {
+      constexpr int ACT = decltype(act_k)::value;
+      for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+        const int ml = row0 + r, col = col0 + c;
+        if (ml < Mpg && col < NP) {
+          const int m = g * Mpg + ml;
+          float o = v;
+          if (bias) o += to_f32(bias[m]);
+          store_float(Y + out_index(m, col), act_c<ACT>(o));
+        }
+      });
     });
   }
 }

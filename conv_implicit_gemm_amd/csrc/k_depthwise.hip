@@ -172,20 +172,27 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
 
     const int oh = oh0 + r;
     const int64_t ybase = (plane * Ho + oh) * (int64_t)Wo + ow0;
+    if constexpr (DT == DT_I8) {
 #pragma unroll
-    for (int o = 0; o < kStrip; ++o) {
-      if (ow0 + o < Wo) {
-        if constexpr (DT == DT_I8) {
+      for (int o = 0; o < kStrip; ++o) {
+        if (ow0 + o < Wo) {
           if (a.out_dt == DT_I32) ((int32_t*)a.Y)[ybase + o] = acc[o];
           else ((int8_t*)a.Y)[ybase + o] = requant(acc[o], q.mult[c], q.yzp);
-        } else {
-          float v = acc[o];
-          if (bias) v += to_f32(bias[c]);
-          v = apply_act(a.act, v);
-          if constexpr (DT == DT_BF16) ((uint16_t*)a.Y)[ybase + o] = f32_to_bf16(v);
-          else ((float*)a.Y)[ybase + o] = v;
         }
       }
+    } else {
+      const float bv = bias ? to_f32(bias[c]) : 0.0f;
+      with_act(a.act, [&](auto act_k) {
+        constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+        for (int o = 0; o < kStrip; ++o) {
+          if (ow0 + o < Wo) {
+            const float v = act_c<ACT>(acc[o] + bv);
+            if constexpr (DT == DT_BF16) ((uint16_t*)a.Y)[ybase + o] = f32_to_bf16(v);
+            else ((float*)a.Y)[ybase + o] = v;
+          }
+        }
+      });
     }
   }
 }

@@ -108,6 +108,18 @@ struct PatchPlan {
   int lds;              // bytes of LDS
 };
 
+// Plan of the pointwise (1x1) kernel: block configuration and launch grid.
+struct PwPlan {
+  int WM;     // wave rows: 64*WM output channels, 32*(4/WM)*2 pixels per block
+  int KC;     // input channels per chunk (32 or 64)
+  int P;      // pixels per staging load (1, 2 or 4)
+  int V;      // pixels per output store (1, 2, 4 or 8)
+  int npb;    // pixel blocks
+  int nmb;    // output-channel blocks
+  int lds;    // bytes of LDS
+  int grid;   // persistent blocks (tiles are strided over them)
+};
+
 // Launchers (return a hipError_t as int).  `stream` is a hipStream_t.
 // One translation unit per input type keeps the builds parallel.
 int launch_gemm_f32(const GemmArgs& a, int tile, void* stream);
@@ -124,7 +136,11 @@ int launch_conv_depthwise(const ConvArgs& a, void* stream);
 bool depthwise_fits(const ConvArgs& a);
 // 3x3 bf16 convolution with an LDS-staged input patch (group 1, C % 32 == 0)
 bool conv_patch_geometry(const ConvArgs& a);      // dtype/shape conditions only
-bool conv_patch_applicable(const ConvArgs& a);    // plus alignment and a plan that fits
+bool conv_patch_applicable(const ConvArgs& a);
+// pointwise kernel (bf16, 1x1, stride 1, unpadded, group 1, C % 32 == 0)
+bool conv_pw_applicable(const ConvArgs& a);
+int launch_conv_pw(const ConvArgs& a, void* stream);
+const char* conv_pw_describe(const ConvArgs& a, char* buf, int cap);    // plus alignment and a plan that fits
 int launch_conv_patch(const ConvArgs& a, void* stream);
 const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap);
 // Gemm with a single output row (M = 1): memory-bound, no MFMA

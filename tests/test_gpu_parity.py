@@ -233,6 +233,7 @@ def test_depthwise_variants(ox, force, dtype, geom, monkeypatch):
 @pytest.mark.parametrize("force", [None, "1x1", "igemm"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_pointwise_variants(ox, force, dtype, monkeypatch):
+    # C = 40 is not a multiple of 32: the generic 1x1 engine takes it
     if force:
         monkeypatch.setenv("OX_FORCE_KERNEL", force)
     say("1x1", dtype, force)
@@ -242,6 +243,61 @@ def test_pointwise_variants(ox, force, dtype, monkeypatch):
     b = synth.round_to(r.uniform(-0.5, 0.5, 70), dtype)
     Y = run_conv(ox, X, Wt, b, dtype, (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu")
     assert_close(host64(Y), oracle.conv2d(X, Wt, b, act="relu"), dtype, "1x1")
+
+
+def misaligned(t, elems):
+    """A copy of `t` whose data pointer sits `elems` elements past an aligned one."""
+    flat = torch.empty(t.numel() + elems, dtype=t.dtype, device=t.device)
+    v = flat[elems:].view(t.shape)
+    v.copy_(t)
+    return v
+
+
+def test_pw_conv_sweep_bf16(ox, monkeypatch):
+    # the pointwise kernel over ragged pixel counts (odd, even and multiple-of-4
+    # planes, blocks spanning images), partial channel blocks and every chunk width
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
+    r = np.random.default_rng(909)
+    for ci in range(40):
+        N = int(r.integers(1, 5))
+        Cin = int(r.choice([32, 64, 96, 128, 256, 384]))
+        H, W = int(r.integers(1, 24)), int(r.integers(1, 24))
+        M = int(r.integers(1, 300))
+        act = str(r.choice(["none", "relu", "relu6", "gelu"]))
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("pw sweep", ci, (N, Cin, H, W, M, act))
+        Y = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, act)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, act=act), "bf16", "pw %d" % ci)
+
+
+@pytest.mark.parametrize("plan", ["1:32", "1:64", "2:32", "2:64"])
+def test_pw_each_config(ox, plan, monkeypatch):
+    # every block configuration (wave rows : channel chunk), pinned, with the
+    # staging load width (1, 2, 4 pixels) and the store width (1 .. 8 pixels)
+    # driven by the plane size and by X and Y pointers offset from alignment
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
+    monkeypatch.setenv("OX_PW_PLAN", plan)
+    r = np.random.default_rng(31 + int(plan[0]) * 1000 + int(plan[2:]))
+    for ci, (N, Cin, H, W, M, xoff, yoff) in enumerate([
+            (2, 128, 8, 8, 70, 0, 0), (3, 128, 6, 5, 150, 0, 0), (2, 256, 7, 7, 64, 0, 0),
+            (2, 128, 4, 8, 96, 1, 1), (1, 256, 6, 6, 200, 2, 2), (5, 128, 3, 3, 33, 0, 3)]):
+        HW = H * W
+        P = 4 if HW % 4 == 0 and xoff % 4 == 0 else 2 if HW % 2 == 0 and xoff % 2 == 0 else 1
+        if plan == "1:64" and P == 1:
+            continue      # that plan does not take single-pixel staging
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("pw config", plan, (N, Cin, H, W, M, xoff, yoff))
+        Xd = misaligned(dev(X, "bf16"), xoff)
+        Y = misaligned(nan_like((N, M, H, W), "bf16"), yoff)
+        ox.ox_conv2d_fused(Xd, dev(Wt, "bf16"), dev(b, "bf16"), (1, 1), (0, 0, 0, 0), (1, 1), 1,
+                           "relu", Y=Y)
+        torch.cuda.synchronize()
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, act="relu"), "bf16",
+                     "pw %s case %d" % (plan, ci))
 
 
 def conv_layer_tensors(layer, cfg, li, dtype):
