@@ -69,7 +69,7 @@ const char* act_name(int a) {
 
 // OX_FORCE_KERNEL: comma-separated tokens, e.g. "igemm,tile=64x64".
 struct Force {
-  const char* variant = nullptr;   // "dw", "1x1", "pw", "patch", "igemm", "gemv", "mfma"
+  const char* variant = nullptr;   // "dw", "1x1", "pw", "patch", "smallc", "igemm", "gemv", "mfma"
   int tile = -1;
 };
 
@@ -216,10 +216,10 @@ ConvArgs conv_args(int dt, const ox_conv_desc* d, int64_t Ho, int64_t Wo, const 
   return a;
 }
 
-enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2, KIND_PATCH = 3, KIND_PW = 4 };
+enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2, KIND_PATCH = 3, KIND_PW = 4, KIND_SMALLC = 5 };
 
 const char* kind_name(int k) {
-  static const char* n[] = {"igemm", "1x1", "dw", "patch", "pw"};
+  static const char* n[] = {"igemm", "1x1", "dw", "patch", "pw", "smallc"};
   return n[k];
 }
 
@@ -253,6 +253,10 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
       if (!is_1x1 || !conv_pw_applicable(a))
         return fail(OX_ERR_UNSUPPORTED, "%s: forced 'pw' needs bf16, a 1x1/s1/p0/g1 conv, C %% 32 == 0 and aligned X/W", fn);
       *kind = KIND_PW;
+    } else if (!strcmp(f.variant, "smallc")) {
+      if (!conv_smallc_applicable(a))
+        return fail(OX_ERR_UNSUPPORTED, "%s: forced 'smallc' needs bf16, C <= 4, group 1, stride 1 or 2, no dilation, kW <= 8", fn);
+      *kind = KIND_SMALLC;
     } else if (!strcmp(f.variant, "igemm")) {
       *kind = KIND_IGEMM;
     } else if (!strcmp(f.variant, "patch")) {
@@ -268,6 +272,7 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
   if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
   else if (is_1x1) *kind = conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
   else if (conv_patch_applicable(a)) *kind = KIND_PATCH;
+  else if (conv_smallc_applicable(a)) *kind = KIND_SMALLC;
   else *kind = KIND_IGEMM;
   return OX_OK;
 }
@@ -291,6 +296,7 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
     char plan[160] = "";
     if (kind == KIND_PATCH) conv_patch_describe(a, plan, sizeof(plan));
     if (kind == KIND_PW) conv_pw_describe(a, plan, sizeof(plan));
+    if (kind == KIND_SMALLC) conv_smallc_describe(a, plan, sizeof(plan));
     fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s %s\n",
             fn, a.dt, a.N, a.C, a.H, a.W, a.M, a.kH, a.kW, a.sh, a.sw, a.group, act_name(a.act),
             kind_name(kind), tile >= 0 ? " tile=" : "", tile >= 0 ? tile_name(tile) : "", plan);
@@ -303,6 +309,8 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
     rc = launch_conv_patch(a, stream);
   } else if (kind == KIND_PW) {
     rc = launch_conv_pw(a, stream);
+  } else if (kind == KIND_SMALLC) {
+    rc = launch_conv_smallc(a, stream);
   } else {
     const int k = kind == KIND_1X1 ? 1 : 0;
     rc = a.dt == DT_F32 ? launch_conv_f32(a, k, tile, stream)

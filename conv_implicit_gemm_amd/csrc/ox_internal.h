@@ -120,6 +120,20 @@ struct PwPlan {
   int grid;   // persistent blocks (tiles are strided over them)
 };
 
+// Plan of the few-input-channel kernel (C <= 4, e.g. an RGB stem).
+struct SmallcPlan {
+  int FP;     // 32-pixel tiles per wave (block: 64 channels x 128*FP pixel slots)
+  int NH;     // k-steps per kernel row (taps padded to 4*NH)
+  int P;      // input positions per staging load (1 or 8)
+  int TR;     // output rows per block
+  int PR;     // patch rows
+  int PWc;    // patch columns (cells), even
+  int nrb;    // row blocks per image
+  int nmb;    // output-channel blocks
+  int lds;    // bytes of LDS
+  int w_vec;  // weights 16-byte aligned: staged with vector loads
+};
+
 // Launchers (return a hipError_t as int).  `stream` is a hipStream_t.
 // One translation unit per input type keeps the builds parallel.
 int launch_gemm_f32(const GemmArgs& a, int tile, void* stream);
@@ -137,6 +151,10 @@ bool depthwise_fits(const ConvArgs& a);
 // 3x3 bf16 convolution with an LDS-staged input patch (group 1, C % 32 == 0)
 bool conv_patch_geometry(const ConvArgs& a);      // dtype/shape conditions only
 bool conv_patch_applicable(const ConvArgs& a);
+// few-input-channel kernel (bf16, C <= 4, group 1, stride 1 or 2, no dilation, kW <= 8)
+bool conv_smallc_applicable(const ConvArgs& a);
+int launch_conv_smallc(const ConvArgs& a, void* stream);
+const char* conv_smallc_describe(const ConvArgs& a, char* buf, int cap);
 // pointwise kernel (bf16, 1x1, stride 1, unpadded, group 1, C % 32 == 0)
 bool conv_pw_applicable(const ConvArgs& a);
 int launch_conv_pw(const ConvArgs& a, void* stream);

@@ -300,6 +300,53 @@ def test_pw_each_config(ox, plan, monkeypatch):
                      "pw %s case %d" % (plan, ci))
 
 
+def test_smallc_conv_sweep_bf16(ox, monkeypatch):
+    # the few-input-channel kernel (C <= 4): kernels up to 8 wide, both
+    # strides, asymmetric pads, 16-byte and 2-byte input staging
+    monkeypatch.setenv("OX_FORCE_KERNEL", "smallc")
+    r = np.random.default_rng(4242)
+    ran = 0
+    for ci in range(40):
+        N = int(r.integers(1, 4))
+        Cin = int(r.integers(1, 5))
+        kH, kW = int(r.integers(1, 9)), int(r.integers(1, 9))
+        s = int(r.choice([1, 2]))
+        H = int(r.integers(kH, 40))
+        W = int(r.choice([r.integers(kW, 40), 8 * r.integers(1, 6)]))
+        M = int(r.integers(1, 140))
+        pads = tuple(int(v) for v in r.integers(0, 4, 4))
+        if not conv_case_ok(N, Cin, H, W, M, kH, kW, (s, s), pads, (1, 1), 1):
+            continue
+        act = str(r.choice(["none", "relu", "relu6", "gelu"]))
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, kH, kW)) / math.sqrt(Cin * kH * kW), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("smallc sweep", ci, (N, Cin, H, W, M, kH, kW, s, pads, act))
+        Y = run_conv(ox, X, Wt, b, "bf16", (s, s), pads, (1, 1), 1, act)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, (s, s), pads, (1, 1), 1, act), "bf16",
+                     "smallc %d" % ci)
+        ran += 1
+    assert ran >= 25
+
+
+def test_smallc_stem_misaligned_input(ox, monkeypatch):
+    # an input pointer off 16-byte alignment takes the element-wise staging
+    monkeypatch.setenv("OX_FORCE_KERNEL", "smallc")
+    r = np.random.default_rng(77)
+    X = synth.round_to(r.standard_normal((2, 3, 40, 48)), "bf16")
+    Wt = synth.round_to(r.standard_normal((64, 3, 7, 7)) / math.sqrt(147), "bf16")
+    b = synth.round_to(r.uniform(-0.5, 0.5, 64), "bf16")
+    say("smallc misaligned")
+    ref = oracle.conv2d(X, Wt, b, (2, 2), (3, 3, 3, 3), (1, 1), 1, "relu")
+    for xoff, woff in ((1, 0), (0, 1), (3, 5)):
+        Xd = misaligned(dev(X, "bf16"), xoff)
+        Wd = misaligned(dev(Wt, "bf16"), woff)
+        Y = nan_like((2, 64, 20, 24), "bf16")
+        ox.ox_conv2d_fused(Xd, Wd, dev(b, "bf16"), (2, 2), (3, 3, 3, 3), (1, 1), 1, "relu", Y=Y)
+        torch.cuda.synchronize()
+        assert_close(host64(Y), ref, "bf16", "smallc misaligned %d %d" % (xoff, woff))
+
+
 def conv_layer_tensors(layer, cfg, li, dtype):
     t = synth.conv_inputs(layer, cfg, li)
     Wf, bf = oracle.fold_batchnorm(t["W"], t["gamma"], t["beta"], t["mean"], t["var"], 1e-5)
