@@ -3,8 +3,8 @@
 // k_conv_pw_*.hip).
 //
 // Y[n, m, p] = act(bias[m] + sum_c W[m, c] * X[n, c, p]).  The pixels of the
-// batch are flattened (q = n*HW + p) and a block owns BN consecutive pixels
-// x BM output channels.  For each chunk of KC input channels it
+// batch are flattened (q = n*HW + p) and a tile is BN consecutive pixels x
+// BM output channels.  For each chunk of KC input channels a block
 //   * stages the pixels channel-contiguous in LDS: one (2*KC + 16)-byte row
 //     per pixel (KC channels plus 16 bytes of bank padding).  A staging unit
 //     is P consecutive pixels x 8 channels: 8 loads of P elements, with
@@ -15,12 +15,15 @@
 //   * runs KC/16 k-steps of FP x FC v_mfma_f32_32x32x16_bf16 per wave, both
 //     fragments single 128-bit LDS reads, read two steps ahead and
 //     interleaved with the MFMAs.
-// The next chunk's global loads are in flight (in registers) while the
-// current chunk is multiplied.  The epilogue (bias, activation, bf16
-// rounding) stages the tile in LDS as [channel][pixel] and writes each
-// channel's pixels with aligned vector stores.  Consecutive block ids walk
-// the channel blocks of one pixel block first, so the blocks that share a
-// pixel tile run on one XCD at about the same time.
+// Blocks are persistent: each walks a strided sequence of work units and
+// loads the next unit's first chunk while the current one finishes its
+// MFMAs and epilogue.  A work unit is a tile, or -- when there are too few
+// tiles to occupy the chip -- one of S slices of a tile's channel range
+// (split-K): a slice writes its fp32 partial tile to a workspace and
+// conv1x1_reduce adds the S partials in slice order (deterministic) and runs
+// the epilogue.  The epilogue (bias, activation, bf16 rounding) stages the
+// tile in LDS as [channel][pixel] and writes each channel's pixels with
+// aligned vector stores.
 #pragma once
 
 #include "engine.hpp"
@@ -29,12 +32,90 @@ namespace ox {
 
 namespace pw {
 
+// Bias, activation and bf16 conversion of one tile held in the MFMA
+// accumulators of the block's four waves, staged through LDS and stored as
+// channel runs.  Lane (l32, kg) of wave (wm, wn) holds, for each (fp, fc),
+// channel 32*(wm*FC + fc) + l32 at pixel slots 32*(wn*FP + fp) + 8*g + 4*kg
+// + (0..3).  The caller has synchronised the block: LDS is free.
+template <int WM, int WN, int FP, int FC>
+__device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, char* smem,
+                                           const f32x16_t (&acc)[FP][FC], int q0, int m0) {
+  constexpr int BM = 32 * WM * FC, BN = 32 * WN * FP;
+  constexpr int EROW = BN + 8;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
+  const uint16_t* bias = (const uint16_t*)a.bias;
+  uint16_t* E = (uint16_t*)smem;
+  float bv[FC];
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) {
+    const int ml = wm * FC * 32 + fc * 32 + l32;
+    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+  }
+  with_act(a.act, [&](auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+    for (int fc = 0; fc < FC; ++fc) {
+      const int ml = wm * FC * 32 + fc * 32 + l32;
+#pragma unroll
+      for (int fp = 0; fp < FP; ++fp) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int slot = (wn * FP + fp) * 32 + 8 * g + 4 * kg;
+          const f32x16_t& c = acc[fp][fc];
+          const uint32_t lo = pack_bf16x2(act_c<ACT>(c[4 * g + 0] + bv[fc]),
+                                          act_c<ACT>(c[4 * g + 1] + bv[fc]));
+          const uint32_t hi = pack_bf16x2(act_c<ACT>(c[4 * g + 2] + bv[fc]),
+                                          act_c<ACT>(c[4 * g + 3] + bv[fc]));
+          *(u32x2_t*)(E + ml * EROW + slot) = u32x2_t{lo, hi};
+        }
+      }
+    }
+  });
+  __syncthreads();
+  uint16_t* Y = (uint16_t*)a.Y;
+  const int mvalid = min(BM, M - m0);
+  const int V = pl.V;                      // HW % V == 0 and Y is 2V-byte aligned
+  const int per_row = BN / V;
+  const int items = mvalid * per_row;
+  for (int it = tid; it < items; it += kThreads) {
+    const int m = it / per_row;
+    const int e = (it - m * per_row) * V;
+    const int q = q0 + e;
+    if (q >= Q) continue;
+    const int n = q / HW;
+    const uint16_t* src = E + m * EROW + e;
+    uint16_t* dst = Y + ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
+    if (V == 8) {
+      const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
+      *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+    } else if (V == 4) {
+      *(u32x2_t*)dst = *(const u32x2_t*)src;
+    } else if (V == 2) {
+      *(uint32_t*)dst = *(const uint32_t*)src;
+    } else {
+      *dst = *src;
+    }
+  }
+}
+
+// Workspace layout of split-K partials: unit (tile, slice) owns
+// kThreads * FP*FC*4 float4 values, stored [float4 index][thread] so that
+// both the writer and the reducer access it fully coalesced.
+template <int FP, int FC>
+__device__ __forceinline__ f32x4_t* partial_base(float* ws, int64_t unit) {
+  return (f32x4_t*)ws + unit * (int64_t)(kThreads * FP * FC * 4);
+}
+
 template <int WM, int WN, int FP, int FC, int KC, int P>
 __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, const PwPlan pl) {
-  constexpr int BM = 32 * WM * FC;          // output channels per block
-  constexpr int BN = 32 * WN * FP;          // pixels per block
+  constexpr int BM = 32 * WM * FC;          // output channels per tile
+  constexpr int BN = 32 * WN * FP;          // pixels per tile
   constexpr int ROW = KC * 2 + 16;          // bytes per staged row
-  constexpr int NG = BN / P;                // pixel groups per block
+  constexpr int NG = BN / P;                // pixel groups per tile
   constexpr int XU = (KC / 8) * NG;         // pixel staging units per chunk
   constexpr int XUPT = (XU + kThreads - 1) / kThreads;
   constexpr int WPR = KC / 8;               // 16-byte weight pieces per row
@@ -51,26 +132,30 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
   const int l32 = lane & 31, kg = lane >> 5;
-  const int total = pl.npb * pl.nmb;
+  const int tiles = pl.npb * pl.nmb;
+  const int S = pl.splits, cps = pl.cps;    // slices per tile, chunks per slice
+  const int units = tiles * S;
   const int HW = a.H * a.W, C = a.C, M = a.M;
   const int Q = a.N * HW;
+  const int nchunks = C / KC;
   const uint16_t* Xg = (const uint16_t*)a.X;
   const uint16_t* Wg = (const uint16_t*)a.Wt;
-  uint16_t* Y = (uint16_t*)a.Y;
-  const uint16_t* bias = (const uint16_t*)a.bias;
 
-  // Persistent blocks: block b runs tiles b, b + G, b + 2G, ... (G = grid
-  // size, a multiple of the XCD count when it is below the tile count), so a
-  // block stays on one XCD and xcd_tile keeps each XCD on one contiguous
-  // range of logical tiles.  The next tile's first chunk is loaded while the
-  // current tile finishes its MFMAs and epilogue.
-  int t = blockIdx.x;
-  if (t >= total) return;
-  int pb, m0;
-  auto decode = [&](int tt) {
-    const int logical = xcd_tile(tt, total);
-    pb = logical / pl.nmb;
-    m0 = (logical - pb * pl.nmb) * BM;
+  // Block b runs units b, b + G, b + 2G, ... (G = grid size, a multiple of
+  // the XCD count when below the unit count), so a block stays on one XCD and
+  // xcd_tile keeps each XCD on one contiguous range of logical units (the
+  // slices of a tile adjacent, then the channel blocks of a pixel block).
+  int u = blockIdx.x;
+  if (u >= units) return;
+  int pb, m0, c_lo, c_hi, unit_id;
+  auto decode = [&](int uu) {
+    unit_id = xcd_tile(uu, units);
+    const int tile = unit_id / S;
+    const int slice = unit_id - tile * S;
+    pb = tile / pl.nmb;
+    m0 = (tile - pb * pl.nmb) * BM;
+    c_lo = slice * cps;
+    c_hi = min(nchunks, c_lo + cps);
   };
 
   // this thread's pixel staging units: element offset of the first value
@@ -79,8 +164,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   int w_goff[WUPT], w_lds[WUPT];
 #pragma unroll
   for (int k = 0; k < XUPT; ++k) {
-    const int u = tid + k * kThreads;
-    x_lds[k] = u < XU ? (u % NG) * P * ROW + (u / NG) * 16 : 0;
+    const int v = tid + k * kThreads;
+    x_lds[k] = v < XU ? (v % NG) * P * ROW + (v / NG) * 16 : 0;
   }
 #pragma unroll
   for (int k = 0; k < WUPT; ++k) {
@@ -91,10 +176,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     const int q0 = pb * BN;
 #pragma unroll
     for (int k = 0; k < XUPT; ++k) {
-      const int u = tid + k * kThreads;
+      const int v = tid + k * kThreads;
       x_goff[k] = -1;
-      if (u < XU) {
-        const int oct = u / NG, g = u - (u / NG) * NG;
+      if (v < XU) {
+        const int oct = v / NG, g = v - (v / NG) * NG;
         const int q = q0 + g * P;
         if (q < Q) {
           const int n = q / HW;
@@ -177,88 +262,28 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
   };
 
-  auto epilogue = [&](const int q0, const int m0) {
-    // Epilogue: lane (l32, kg) holds, for each (fp, fc), channel 32*fc + l32
-    // at pixel slots 8*g + 4*kg + (0..3) of pixel tile fp.  Stage the block's
-    // bf16 outputs as E[channel][pixel], then store channel rows.
-    __syncthreads();
-    constexpr int EROW = BN + 8;
-    uint16_t* E = (uint16_t*)smem;
-    float bv[FC];
-#pragma unroll
-    for (int fc = 0; fc < FC; ++fc) {
-      const int ml = wm * FC * 32 + fc * 32 + l32;
-      bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
-    }
-    with_act(a.act, [&](auto act_k) {
-      constexpr int ACT = decltype(act_k)::value;
-#pragma unroll
-      for (int fc = 0; fc < FC; ++fc) {
-        const int ml = wm * FC * 32 + fc * 32 + l32;
-#pragma unroll
-        for (int fp = 0; fp < FP; ++fp) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int slot = (wn * FP + fp) * 32 + 8 * g + 4 * kg;
-            const f32x16_t& c = acc[fp][fc];
-            const uint32_t lo = pack_bf16x2(act_c<ACT>(c[4 * g + 0] + bv[fc]),
-                                            act_c<ACT>(c[4 * g + 1] + bv[fc]));
-            const uint32_t hi = pack_bf16x2(act_c<ACT>(c[4 * g + 2] + bv[fc]),
-                                            act_c<ACT>(c[4 * g + 3] + bv[fc]));
-            *(u32x2_t*)(E + ml * EROW + slot) = u32x2_t{lo, hi};
-          }
-        }
-      }
-    });
-    __syncthreads();
-    const int mvalid = min(BM, M - m0);
-    const int V = pl.V;                      // HW % V == 0 and Y is 2V-byte aligned
-    const int per_row = BN / V;
-    const int items = mvalid * per_row;
-    for (int it = tid; it < items; it += kThreads) {
-      const int m = it / per_row;
-      const int e = (it - m * per_row) * V;
-      const int q = q0 + e;
-      if (q >= Q) continue;
-      const int n = q / HW;
-      const uint16_t* src = E + m * EROW + e;
-      uint16_t* dst = Y + ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
-      if (V == 8) {
-        const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
-        *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
-      } else if (V == 4) {
-        *(u32x2_t*)dst = *(const u32x2_t*)src;
-      } else if (V == 2) {
-        *(uint32_t*)dst = *(const uint32_t*)src;
-      } else {
-        *dst = *src;
-      }
-    }
-  };
-
-  const int nchunks = C / KC;
-  decode(t);
+  decode(u);
   tile_offsets();
-  load_chunk(0);
+  load_chunk(c_lo * KC);
   for (;;) {
-    const int cur_pb = pb, cur_m0 = m0;
-    const int next = t + (int)gridDim.x;
+    const int cur_pb = pb, cur_m0 = m0, cur_lo = c_lo, cur_hi = c_hi, cur_unit = unit_id;
+    const int next = u + (int)gridDim.x;
 #pragma unroll
     for (int i = 0; i < FP; ++i)
 #pragma unroll
       for (int j = 0; j < FC; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    for (int chunk = 0; chunk < nchunks; ++chunk) {
+    for (int chunk = cur_lo; chunk < cur_hi; ++chunk) {
       __syncthreads();               // LDS is free: previous MFMAs and epilogue are done
       store_chunk();
       __syncthreads();
-      if (chunk + 1 < nchunks) {
+      if (chunk + 1 < cur_hi) {
         load_chunk((chunk + 1) * KC);
-      } else if (next < total) {
+      } else if (next < units) {
         decode(next);
         tile_offsets();
-        load_chunk(0);
+        load_chunk(c_lo * KC);
       }
       u32x4_t pf[3][FP], wf[3][FC];
       auto read_frags = [&](int s, int buf) {
@@ -286,11 +311,97 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         __builtin_amdgcn_sched_barrier(0);
       }
     }
-    epilogue(cur_pb * BN, cur_m0);
-    if (next >= total) break;
-    t = next;
+    if (S == 1) {
+      __syncthreads();               // every wave is done reading this tile's operands
+      store_tile<WM, WN, FP, FC>(a, pl, smem, acc, cur_pb * BN, cur_m0);
+    } else {
+      f32x4_t* dst = partial_base<FP, FC>(pl.ws, cur_unit) + tid;
+#pragma unroll
+      for (int fp = 0; fp < FP; ++fp)
+#pragma unroll
+        for (int fc = 0; fc < FC; ++fc)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            dst[((fp * FC + fc) * 4 + g) * kThreads] =
+                f32x4_t{acc[fp][fc][4 * g], acc[fp][fc][4 * g + 1], acc[fp][fc][4 * g + 2],
+                        acc[fp][fc][4 * g + 3]};
+    }
+    if (next >= units) break;
+    u = next;
   }
 }
+
+// Second pass of split-K.  One block per (tile, wave of the first pass):
+// its 256 threads split that wave's 64 x FP*FC*4 float4 partial values four
+// ways (more loads in flight per CU), add the S slices in slice order, apply
+// bias and activation, stage the 32*FC x 32*FP sub-tile in LDS as
+// [channel][pixel] and write the channel runs.
+template <int WM, int WN, int FP, int FC>
+__global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, const PwPlan pl) {
+  constexpr int BN = 32 * WN * FP, BM = 32 * WM * FC;
+  constexpr int SUBM = 32 * FC, SUBN = 32 * FP, EROW = SUBN + 8;
+  constexpr int NV = FP * FC * 4;           // float4 values per lane of the first pass
+  constexpr int PER = NV / 4;               // of those, per thread here
+  static_assert(NV % 4 == 0, "four threads per lane");
+  __shared__ __attribute__((aligned(16))) uint16_t E[SUBM * EROW];
+  const int t = blockIdx.x >> 2, w = blockIdx.x & 3;
+  const int wm = w / WN, wn = w - (w / WN) * WN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, part = tid >> 6;     // first-pass lane, quarter of its values
+  const int l32 = lane & 31, kg = lane >> 5;
+  f32x4_t sum[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) sum[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int s = 0; s < pl.splits; ++s) {
+    const f32x4_t* src = partial_base<FP, FC>(pl.ws, (int64_t)t * pl.splits + s) + w * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) sum[k] += src[(part * PER + k) * kThreads];
+  }
+  const int pb = t / pl.nmb;
+  const int q0 = pb * BN + wn * SUBN, m0 = (t - pb * pl.nmb) * BM + wm * SUBM;
+  const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
+  const uint16_t* bias = (const uint16_t*)a.bias;
+  with_act(a.act, [&](auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = part * PER + k;             // value index (fp*FC + fc)*4 + g
+      const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
+      const int m = m0 + fc * 32 + l32;
+      const float bv = (bias && m < M) ? bf16_to_f32(bias[m]) : 0.0f;
+      const uint32_t lo = pack_bf16x2(act_c<ACT>(sum[k][0] + bv), act_c<ACT>(sum[k][1] + bv));
+      const uint32_t hi = pack_bf16x2(act_c<ACT>(sum[k][2] + bv), act_c<ACT>(sum[k][3] + bv));
+      *(u32x2_t*)(E + (fc * 32 + l32) * EROW + fp * 32 + 8 * g + 4 * kg) = u32x2_t{lo, hi};
+    }
+  });
+  __syncthreads();
+  if (m0 >= M) return;
+  uint16_t* Y = (uint16_t*)a.Y;
+  const int mvalid = min(SUBM, M - m0);
+  const int V = pl.V;
+  const int per_row = SUBN / V;
+  for (int it = tid; it < mvalid * per_row; it += kThreads) {
+    const int m = it / per_row;
+    const int e = (it - m * per_row) * V;
+    const int q = q0 + e;
+    if (q >= Q) continue;
+    const int n = q / HW;
+    const uint16_t* src = E + m * EROW + e;
+    uint16_t* dst = Y + ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
+    if (V == 8) {
+      const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
+      *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+    } else if (V == 4) {
+      *(u32x2_t*)dst = *(const u32x2_t*)src;
+    } else if (V == 2) {
+      *(uint32_t*)dst = *(const uint32_t*)src;
+    } else {
+      *dst = *src;
+    }
+  }
+}
+
 template <int WM, int WN, int KC>
 int launch_cfg(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
   constexpr int FP = 2, FC = 2;
@@ -306,12 +417,14 @@ int launch_cfg(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
       hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 1>), grid, dim3(kThreads), p.lds, s, a, p);
       break;
   }
+  if (p.splits > 1)
+    hipLaunchKernelGGL((conv1x1_reduce<WM, WN, FP, FC>), dim3(p.npb * p.nmb * 4), dim3(kThreads), 0, s, a, p);
   return (int)hipGetLastError();
 }
 
 }  // namespace pw
 
-// launch_pw_<WM>_<KC>: blocks of 64*WM channels x 32*(4/WM)*2 pixels, KC
+// launch_pw_<WM>_<KC>: tiles of 64*WM channels x 32*(4/WM)*2 pixels, KC
 // input channels per chunk (wider chunks would not fit the staging
 // registers next to the accumulators)
 int launch_pw_1_32(const ConvArgs& a, const PwPlan& p, void* s);

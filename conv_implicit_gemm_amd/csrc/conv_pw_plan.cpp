@@ -39,22 +39,36 @@ PwPlan make(const ConvArgs& a, int WM, int KC) {
   p.nmb = (a.M + BM - 1) / BM;
   const int row = KC * 2 + 16;
   p.lds = std::max((BM + BN) * row, BM * (BN + 8) * 2);
-  // persistent grid: as many blocks as fit the chip at once (LDS-bound, at
-  // most kMaxPerCu per CU), a multiple of the XCD count when tiles are left over
-  int per_cu = std::max(1, std::min(kMaxPerCu, kLdsMax / p.lds));
-  if (const char* e = getenv("OX_PW_PER_CU")) per_cu = std::max(1, std::min(8, atoi(e)));
+  // split-K when the tiles alone would leave most CUs idle and the channel
+  // range is long: aim at two work units per CU, at least two chunks each
   const int64_t tiles = (int64_t)p.npb * p.nmb;
+  const int nchunks = std::max(1, a.C / KC);   // (a C that KC does not divide is rejected by valid)
+  int target = 1;
+  if (tiles < 192 && nchunks >= 4)
+    target = (int)std::min<int64_t>((2 * kCUs + tiles - 1) / tiles, nchunks / 2);
+  if (const char* e = getenv("OX_PW_SPLITS")) target = std::max(1, std::min(nchunks, atoi(e)));
+  p.cps = (nchunks + target - 1) / target;
+  p.splits = (nchunks + p.cps - 1) / p.cps;
+  p.ws = nullptr;
+  // persistent grid: as many blocks as fit the chip at once (LDS-bound, at
+  // most kMaxPerCu per CU), a multiple of the XCD count when units are left over
+  const int per_cu = std::max(1, std::min(kMaxPerCu, kLdsMax / p.lds));
+  const int64_t units = tiles * p.splits;
   const int64_t cap = (int64_t)kCUs * per_cu;
-  p.grid = (int)std::min(tiles, cap);
+  p.grid = (int)std::min(units, cap);
   return p;
+}
+
+size_t ws_bytes(const PwPlan& p) {
+  const int BM = 64 * p.WM, BN = 32 * (4 / p.WM) * 2;
+  return p.splits > 1 ? (size_t)p.npb * p.nmb * p.splits * BM * BN * sizeof(float) : 0;
 }
 
 bool valid(const ConvArgs& a, const PwPlan& p) {
   // (a 256-pixel block staging single pixels takes 32-channel chunks: the
   // registers of 64 would spill)
   return a.C % p.KC == 0 && p.KC <= 64 && !(p.WM == 1 && p.P == 1 && p.KC > 32) &&
-         p.lds <= kLdsMax &&
-         (int64_t)p.npb * p.nmb < (int64_t)1 << 31;
+         p.lds <= kLdsMax && (int64_t)p.npb * p.nmb * p.splits < (int64_t)1 << 31;
 }
 
 // OX_PW_PLAN=WM:KC pins the configuration (for measurements); a pinned
@@ -94,6 +108,10 @@ bool conv_pw_applicable(const ConvArgs& a) {
 int launch_conv_pw(const ConvArgs& a, void* stream) {
   PwPlan p;
   if (!pw_plan(a, &p)) return 1;   // hipErrorInvalidValue
+  if (p.splits > 1) {
+    p.ws = (float*)stream_workspace(stream, ws_bytes(p));
+    if (!p.ws) return 2;           // hipErrorOutOfMemory
+  }
   if (p.WM == 1) return p.KC == 64 ? launch_pw_1_64(a, p, stream) : launch_pw_1_32(a, p, stream);
   return p.KC == 64 ? launch_pw_2_64(a, p, stream) : launch_pw_2_32(a, p, stream);
 }
@@ -101,8 +119,8 @@ int launch_conv_pw(const ConvArgs& a, void* stream) {
 const char* conv_pw_describe(const ConvArgs& a, char* buf, int cap) {
   PwPlan p;
   if (!pw_plan(a, &p)) return "";
-  snprintf(buf, cap, "BM=%d BN=%d KC=%d P=%d V=%d tiles=%lld grid=%d lds=%d", 64 * p.WM,
-           64 * (4 / p.WM), p.KC, p.P, p.V, (long long)p.npb * p.nmb, p.grid, p.lds);
+  snprintf(buf, cap, "BM=%d BN=%d KC=%d P=%d V=%d tiles=%lld splits=%d grid=%d lds=%d", 64 * p.WM,
+           64 * (4 / p.WM), p.KC, p.P, p.V, (long long)p.npb * p.nmb, p.splits, p.grid, p.lds);
   return buf;
 }
 

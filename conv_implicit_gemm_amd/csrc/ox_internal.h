@@ -117,8 +117,18 @@ struct PwPlan {
   int npb;    // pixel blocks
   int nmb;    // output-channel blocks
   int lds;    // bytes of LDS
-  int grid;   // persistent blocks (tiles are strided over them)
+  int grid;   // persistent blocks (work units are strided over them)
+  int splits; // slices of the channel range per tile (split-K), 1 = none
+  int cps;    // chunks per slice
+  float* ws;  // split-K partials (splits * tiles * BM * BN floats), else null
 };
+
+// Per-(device, stream) scratch of at least `bytes` bytes, owned by the
+// library and kept until the process ends; grown (after synchronising the
+// stream) when a call needs more.  Calls on one stream run in order, so they
+// may share it; calls on different streams get different buffers.  Returns
+// null if the allocation fails.
+void* stream_workspace(void* stream, size_t bytes);
 
 // Plan of the few-input-channel kernel (C <= 4, e.g. an RGB stem).
 struct SmallcPlan {

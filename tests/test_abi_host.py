@@ -115,6 +115,38 @@ def test_forced_variant_must_apply(ox, monkeypatch):
     assert st == 3 and "M=1" in ox.ox_last_error()
 
 
+def test_variant_selection_sweep(ox, monkeypatch):
+    # host-side planning of every kernel over many geometries (no launches):
+    # each call returns a name and the expected kernels are chosen
+    import numpy as np
+    r = np.random.default_rng(2024)
+    for _ in range(600):
+        dt = str(r.choice(["f32", "bf16", "i8"]))
+        k = int(r.choice([1, 1, 3, 3, 5, 7]))
+        g = 1
+        C = int(r.choice([1, 3, 4, 16, 32, 64, 96, 128, 256, 512, 2048]))
+        M = int(r.choice([1, 5, 64, 130, 256, 2048]))
+        if r.random() < 0.15:
+            g, M = C, C
+        N = int(r.integers(1, 40))
+        H, W = int(r.integers(k, 60)), int(r.integers(k, 60))
+        s = int(r.choice([1, 2]))
+        p = k // 2
+        name = ox.ox_conv2d_variant(dt, N, C, H, W, M, k, k, (s, s), (p, p, p, p), (1, 1), g)
+        assert "/" in name
+        if dt == "bf16" and g == 1 and k == 1 and s == 1 and C % 32 == 0:
+            assert name.startswith("pw/"), (name, C, M)
+        if dt == "bf16" and g == 1 and k == 3 and C % 32 == 0:
+            assert name.startswith("patch/"), (name, C, M, H, W, s)
+        if dt == "bf16" and g == 1 and C <= 4 and k > 1 and not (C == 1 and M == 1):
+            assert name.startswith("smallc/"), (name, C, k, s)
+    # pinned split-K counts, including more slices than chunks
+    for splits in ("1", "2", "7", "64"):
+        monkeypatch.setenv("OX_PW_SPLITS", splits)
+        for C in (32, 64, 96, 2048):
+            assert ox.ox_conv2d_variant("bf16", 2, C, 7, 7, 512, 1, 1).startswith("pw/")
+
+
 def test_gemm_argument_errors(ox):
     L = raw(ox)
     g = L.ox_gemm_fused

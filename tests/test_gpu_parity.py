@@ -300,6 +300,26 @@ def test_pw_each_config(ox, plan, monkeypatch):
                      "pw %s case %d" % (plan, ci))
 
 
+@pytest.mark.parametrize("splits", [2, 3, 5])
+def test_pw_split_k(ox, splits, monkeypatch):
+    # split-K: slices of the channel range write fp32 partials, a second
+    # kernel adds them in slice order -- same result as the oracle, and
+    # bit-identical from run to run
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
+    monkeypatch.setenv("OX_PW_SPLITS", str(splits))
+    r = np.random.default_rng(600 + splits)
+    for ci, (N, Cin, H, W, M) in enumerate([(2, 512, 7, 7, 200), (3, 320, 6, 6, 64), (1, 256, 9, 9, 130)]):
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("pw split", splits, (N, Cin, H, W, M))
+        Y1 = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu6")
+        Y2 = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu6")
+        assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+        assert_close(host64(Y1), oracle.conv2d(X, Wt, b, act="relu6"), "bf16",
+                     "pw split %d case %d" % (splits, ci))
+
+
 def test_smallc_conv_sweep_bf16(ox, monkeypatch):
     # the few-input-channel kernel (C <= 4): kernels up to 8 wide, both
     # strides, asymmetric pads, 16-byte and 2-byte input staging
