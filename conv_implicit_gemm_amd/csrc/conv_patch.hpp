@@ -88,10 +88,6 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   const uint16_t* Wt = (const uint16_t*)a.Wt;
   const uint16_t* Xblk = (const uint16_t*)a.X + (int64_t)img0 * C * HW;
 
-  // zero the whole patch once: halo cells are never written again
-  for (int i = tid; i < pp.npos * (kCell / 16); i += kThreads)
-    *(u32x4_t*)(Ps + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
-
   // staging units of this thread, fixed for every chunk: a unit is P
   // consecutive plane positions x 8 channels.  u_goff: element offset of its
   // first value from the chunk's first plane of image img0 (-1: no unit);
@@ -257,6 +253,17 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
 
   const int nchunks = C / 32;
   load_chunk(0);
+  // while the first chunk is in flight: zero the whole patch once (halo
+  // cells are never written again) and fetch this lane's bias values
+  for (int i = tid; i < pp.npos * (kCell / 16); i += kThreads)
+    *(u32x4_t*)(Ps + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
+  const uint16_t* bias = (const uint16_t*)a.bias;
+  float bv[FC];
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) {
+    const int ml = wm * FC * 32 + fc * 32 + l32;
+    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+  }
   for (int chunk = 0; chunk < nchunks; ++chunk) {
     __syncthreads();                 // the previous chunk's MFMAs are done with LDS
     store_chunk();
@@ -304,13 +311,6 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   const int nslot = pp.NT * 32;
   const int erow = nslot + 8;            // elements per staged channel row
   uint16_t* E = (uint16_t*)smem;
-  const uint16_t* bias = (const uint16_t*)a.bias;
-  float bv[FC];
-#pragma unroll
-  for (int fc = 0; fc < FC; ++fc) {
-    const int ml = wm * FC * 32 + fc * 32 + l32;
-    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
-  }
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll

@@ -39,7 +39,8 @@ namespace pw {
 // + (0..3).  The caller has synchronised the block: LDS is free.
 template <int WM, int WN, int FP, int FC>
 __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, char* smem,
-                                           const f32x16_t (&acc)[FP][FC], int q0, int m0) {
+                                           const f32x16_t (&acc)[FP][FC], const float (&bv)[FC],
+                                           int q0, int m0) {
   constexpr int BM = 32 * WM * FC, BN = 32 * WN * FP;
   constexpr int EROW = BN + 8;
   const int tid = threadIdx.x;
@@ -47,14 +48,7 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
   const int l32 = lane & 31, kg = lane >> 5;
   const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
-  const uint16_t* bias = (const uint16_t*)a.bias;
   uint16_t* E = (uint16_t*)smem;
-  float bv[FC];
-#pragma unroll
-  for (int fc = 0; fc < FC; ++fc) {
-    const int ml = wm * FC * 32 + fc * 32 + l32;
-    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
-  }
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
@@ -99,6 +93,20 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
     } else {
       *dst = *src;
     }
+  }
+}
+
+// This lane's bias values (channels 32*(wm*FC + fc) + l32 of the tile at m0),
+// loaded ahead of the epilogue that needs them.
+template <int WM, int WN, int FC>
+__device__ __forceinline__ void load_bias(const ConvArgs& a, int m0, float (&bv)[FC]) {
+  const int wave = threadIdx.x >> 6, l32 = threadIdx.x & 31;
+  const int wm = wave / WN;
+  const uint16_t* bias = (const uint16_t*)a.bias;
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) {
+    const int m = m0 + wm * FC * 32 + fc * 32 + l32;
+    bv[fc] = (bias && m < a.M) ? bf16_to_f32(bias[m]) : 0.0f;
   }
 }
 
@@ -262,11 +270,15 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
   };
 
+  float bv[FC], next_bv[FC] = {};
   decode(u);
   tile_offsets();
   load_chunk(c_lo * KC);
+  if (S == 1) load_bias<WM, WN, FC>(a, m0, next_bv);
   for (;;) {
     const int cur_pb = pb, cur_m0 = m0, cur_lo = c_lo, cur_hi = c_hi, cur_unit = unit_id;
+#pragma unroll
+    for (int fc = 0; fc < FC; ++fc) bv[fc] = next_bv[fc];
     const int next = u + (int)gridDim.x;
 #pragma unroll
     for (int i = 0; i < FP; ++i)
@@ -284,6 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         decode(next);
         tile_offsets();
         load_chunk(c_lo * KC);
+        if (S == 1) load_bias<WM, WN, FC>(a, m0, next_bv);
       }
       u32x4_t pf[3][FP], wf[3][FC];
       auto read_frags = [&](int s, int buf) {
@@ -313,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
     if (S == 1) {
       __syncthreads();               // every wave is done reading this tile's operands
-      store_tile<WM, WN, FP, FC>(a, pl, smem, acc, cur_pb * BN, cur_m0);
+      store_tile<WM, WN, FP, FC>(a, pl, smem, acc, bv, cur_pb * BN, cur_m0);
     } else {
       f32x4_t* dst = partial_base<FP, FC>(pl.ws, cur_unit) + tid;
 #pragma unroll

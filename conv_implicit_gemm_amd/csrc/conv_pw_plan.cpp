@@ -39,13 +39,16 @@ PwPlan make(const ConvArgs& a, int WM, int KC) {
   p.nmb = (a.M + BM - 1) / BM;
   const int row = KC * 2 + 16;
   p.lds = std::max((BM + BN) * row, BM * (BN + 8) * 2);
-  // split-K when the tiles alone would leave most CUs idle and the channel
-  // range is long: aim at two work units per CU, at least two chunks each
+  // split-K when the tiles alone would leave many CUs idle and the channel
+  // range is long: about 192 work units of at least four chunks (a sweep
+  // of the ResNet-50 1x1 layers at batch 32: two slices for 98 tiles x 16
+  // chunks, four for 52 tiles x 32 chunks; more slices cost more in partial
+  // traffic than they gain)
   const int64_t tiles = (int64_t)p.npb * p.nmb;
   const int nchunks = std::max(1, a.C / KC);   // (a C that KC does not divide is rejected by valid)
   int target = 1;
   if (tiles < 192 && nchunks >= 4)
-    target = (int)std::min<int64_t>((2 * kCUs + tiles - 1) / tiles, nchunks / 2);
+    target = (int)std::min<int64_t>((192 + tiles - 1) / tiles, nchunks / 4);
   if (const char* e = getenv("OX_PW_SPLITS")) target = std::max(1, std::min(nchunks, atoi(e)));
   p.cps = (nchunks + target - 1) / target;
   p.splits = (nchunks + p.cps - 1) / p.cps;

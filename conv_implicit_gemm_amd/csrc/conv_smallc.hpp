@@ -52,6 +52,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_bf16(const ConvArgs a
   const int rows_here = min(pl.TR, a.Ho - oh0);
   const int ih_base = oh0 * S - a.pt;
 
+  const uint16_t* bias = (const uint16_t*)a.bias;
+  float bv[2];
+#pragma unroll
+  for (int fc = 0; fc < 2; ++fc) {
+    const int ml = fc * 32 + l32;
+    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+  }
+
   // zero the patch and the weight tile (padding taps and channels stay 0)
   const int zbytes = BM * wrow + pl.PR * pl.PWc * kCellB;
   for (int i = tid * 16; i < zbytes; i += kThreads * 16) *(u32x4_t*)(smem + i) = u32x4_t{0u, 0u, 0u, 0u};
@@ -178,13 +186,6 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_bf16(const ConvArgs a
   const int nslot = WN * FP * 32;
   const int erow = nslot + 8;
   uint16_t* E = (uint16_t*)smem;
-  const uint16_t* bias = (const uint16_t*)a.bias;
-  float bv[FC];
-#pragma unroll
-  for (int fc = 0; fc < FC; ++fc) {
-    const int ml = fc * 32 + l32;
-    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
-  }
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
