@@ -49,6 +49,66 @@ constexpr int kAROW = kKK * 64 + 16;   // bytes per staged weight row
 // a 128-channel block needs the room
 constexpr int patch_upt(int P, int BM) { return (BM >= 128 ? 4 : 8) / P; }
 
+// Writes staged bf16 outputs to Y.  E[m - mlo][slot - slo] holds channel
+// m0 + m, pixel slot `slot` of the tile (slot = i*ppi + e: image img0 + i,
+// output pixel oh0*Wo + e of its plane) for m in [mlo, mhi) and slots in
+// [slo, shi); each image's run of output pixels is written with the widest
+// aligned vector stores.  Threads tid = 0 .. nthr-1 share the work.
+__device__ __forceinline__ void store_runs(const ConvArgs& a, const PatchPlan& pp, const uint16_t* E,
+                                           int erow, int img0, int imgs_here, int oh0, int rows_here,
+                                           int m0, int mlo, int mhi, int slo, int shi, int tid, int nthr) {
+  uint16_t* Y = (uint16_t*)a.Y;
+  const int HoWo = a.Ho * a.Wo;
+  const int L = rows_here * a.Wo;
+  const int g0 = oh0 * a.Wo;
+  const int ppi = pp.TR * a.Wo;
+  const int M = a.M;
+  int V = 8;
+  while (V > 1 && ((HoWo % V) || (g0 % V) || (ppi % V) || (L % V) || (slo % V) ||
+                   (((uintptr_t)Y) % (2 * V))))
+    V >>= 1;
+  const int mc = mhi - mlo;
+  if (mc <= 0) return;
+  for (int i = 0; i < imgs_here; ++i) {
+    const int a0 = max(slo, i * ppi), a1 = min(shi, i * ppi + L);
+    if (a1 <= a0) continue;
+    const int per_run = (a1 - a0 + V - 1) / V;
+    for (int it = tid; it < mc * per_run; it += nthr) {
+      const int m = it / per_run;
+      const int slot = a0 + (it - m * per_run) * V;
+      const uint16_t* src = E + m * erow + (slot - slo);
+      uint16_t* dst = Y + ((int64_t)(img0 + i) * M + m0 + mlo + m) * HoWo + g0 + (slot - i * ppi);
+      if (V == 8) {
+        const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
+        *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+      } else if (V == 4) {
+        *(u32x2_t*)dst = *(const u32x2_t*)src;
+      } else if (V == 2) {
+        *(uint32_t*)dst = *(const uint32_t*)src;
+      } else {
+        *dst = *src;
+      }
+    }
+  }
+}
+
+// Geometry of logical tile `tile_id`: first output channel, first image,
+// first output row, rows and images actually present.
+struct TileGeo {
+  int m0, img0, oh0, rows_here, imgs_here;
+};
+__device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, const PatchPlan& pp, int tile_id, int BM) {
+  const int npb = pp.nrb * pp.nib;
+  TileGeo t;
+  t.m0 = (tile_id / npb) * BM;
+  const int bx = tile_id - (tile_id / npb) * npb;
+  t.img0 = (bx / pp.nrb) * pp.IMB;
+  t.oh0 = (bx - (bx / pp.nrb) * pp.nrb) * pp.TR;
+  t.rows_here = min(pp.TR, a.Ho - t.oh0);
+  t.imgs_here = min(pp.IMB, a.N - t.img0);
+  return t;
+}
+
 template <int WM, int WN, int FP, int FC, int P, int S, bool WPACK>
 __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x3_patch_bf16(
     const ConvArgs a, const PatchPlan pp) {
@@ -66,16 +126,16 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave - (wave / WN) * WN;
   const int l32 = lane & 31, kg = lane >> 5;
-  // logical tile: channel-block major, so that the blocks of one XCD share
-  // their weight rows
-  const int npb = pp.nrb * pp.nib;
-  const int tile_id = xcd_tile(blockIdx.x, npb * pp.nmb);
-  const int m0 = (tile_id / npb) * BM;
-  const int bx = tile_id - (tile_id / npb) * npb;
-  const int img0 = (bx / pp.nrb) * pp.IMB;
-  const int oh0 = (bx - (bx / pp.nrb) * pp.nrb) * pp.TR;
-  const int rows_here = min(pp.TR, a.Ho - oh0);
-  const int imgs_here = min(pp.IMB, a.N - img0);
+  // logical unit: channel-block major, so that the blocks of one XCD share
+  // their weight rows; with split-K a unit is one slice of a tile's
+  // channel chunks, the slices of a tile adjacent
+  const int tiles = pp.nrb * pp.nib * pp.nmb;
+  const int unit = xcd_tile(blockIdx.x, tiles * pp.splits);
+  const int tile_id = unit / pp.splits;
+  const int slice = unit - tile_id * pp.splits;
+  const TileGeo geo = tile_geo(a, pp, tile_id, BM);
+  const int m0 = geo.m0, img0 = geo.img0, oh0 = geo.oh0;
+  const int rows_here = geo.rows_here, imgs_here = geo.imgs_here;
   const int H = a.H, W = a.W, HW = H * W;
   const int C = a.C, M = a.M;
   const int K = C * kKK;
@@ -252,7 +312,8 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   };
 
   const int nchunks = C / 32;
-  load_chunk(0);
+  const int c_lo = slice * pp.cps, c_hi = min(nchunks, c_lo + pp.cps);
+  load_chunk(c_lo * 32);
   // while the first chunk is in flight: zero the whole patch once (halo
   // cells are never written again) and fetch this lane's bias values
   for (int i = tid; i < pp.npos * (kCell / 16); i += kThreads)
@@ -264,11 +325,11 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
     const int ml = wm * FC * 32 + fc * 32 + l32;
     bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
   }
-  for (int chunk = 0; chunk < nchunks; ++chunk) {
+  for (int chunk = c_lo; chunk < c_hi; ++chunk) {
     __syncthreads();                 // the previous chunk's MFMAs are done with LDS
     store_chunk();
     __syncthreads();
-    if (chunk + 1 < nchunks) load_chunk((chunk + 1) * 32);
+    if (chunk + 1 < c_hi) load_chunk((chunk + 1) * 32);
     // 18 k-steps (9 taps x 2 halves of 16 channels).  Fragments are read two
     // steps ahead into a ring of three register sets, and the scheduler is
     // told to interleave those LDS reads one by one with the MFMAs of the
@@ -300,6 +361,20 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
       }
       __builtin_amdgcn_sched_barrier(0);   // keep each step's reads in its own step
     }
+  }
+
+  if (pp.splits > 1) {
+    // fp32 partial tile, [float4 index][thread] (coalesced for writer and reducer)
+    f32x4_t* dst = (f32x4_t*)pp.ws + (int64_t)unit * (kThreads * FP * FC * 4) + tid;
+#pragma unroll
+    for (int fp = 0; fp < FP; ++fp)
+#pragma unroll
+      for (int fc = 0; fc < FC; ++fc)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          dst[((fp * FC + fc) * 4 + g) * kThreads] =
+              f32x4_t{acc[fp][fc][4 * g], acc[fp][fc][4 * g + 1], acc[fp][fc][4 * g + 2], acc[fp][fc][4 * g + 3]};
+    return;
   }
 
   // Epilogue.  Lane (l32, kg) holds, for each (fp, fc), output channel
@@ -335,46 +410,63 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
     }
   });
   __syncthreads();
-  // runs: for image i of the block and channel m, output pixels
-  // [oh0*Wo, (oh0 + rows_here)*Wo) of plane (img0+i, m0+m) come from slots
-  // [i*ppi, i*ppi + L)
-  uint16_t* Y = (uint16_t*)a.Y;
-  const int HoWo = a.Ho * a.Wo;
-  const int L = rows_here * a.Wo;
-  const int g0 = oh0 * a.Wo;
-  const int mvalid = min(BM, M - m0);
-  // widest vector that keeps every run's global and LDS start aligned
-  int V = 8;
-  while (V > 1 && ((HoWo % V) || (g0 % V) || (ppi % V) || (L % V) ||
-                   (((uintptr_t)Y) % (2 * V))))
-    V >>= 1;
-  const int per_run = L / V;
-  const int items = imgs_here * mvalid * per_run;
-  for (int it = tid; it < items; it += kThreads) {
-    const int run = it / per_run;
-    const int e = (it - run * per_run) * V;
-    const int i = run / mvalid;
-    const int m = run - i * mvalid;
-    const uint16_t* src = E + m * erow + i * ppi + e;
-    uint16_t* dst = Y + ((int64_t)(img0 + i) * M + m0 + m) * HoWo + g0 + e;
-    if (V == 8) {
-      const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
-      *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
-    } else if (V == 4) {
-      *(u32x2_t*)dst = *(const u32x2_t*)src;
-    } else if (V == 2) {
-      *(uint32_t*)dst = *(const uint32_t*)src;
-    } else {
-      *dst = *src;
-    }
+  store_runs(a, pp, E, erow, img0, imgs_here, oh0, rows_here, m0, 0, min(BM, M - m0), 0, nslot, tid,
+             kThreads);
+}
+
+// Second pass of split-K: one block per (tile, wave of the first pass); its
+// 256 threads split that wave's partial values four ways, add the slices in
+// slice order, then bias, activation, bf16, LDS staging and the runs of the
+// wave's 32*FC channels x 32*FP pixel slots.
+template <int WM, int WN, int FP, int FC>
+__global__ __launch_bounds__(kThreads) void conv3x3_reduce(const ConvArgs a, const PatchPlan pp) {
+  constexpr int BM = 32 * WM * FC;
+  constexpr int SUBM = 32 * FC, SUBN = 32 * FP, EROW = SUBN + 8;
+  constexpr int NV = FP * FC * 4, PER = NV / 4;
+  __shared__ __attribute__((aligned(16))) uint16_t E[SUBM * EROW];
+  const int tile_id = blockIdx.x >> 2, w = blockIdx.x & 3;
+  const int wm = w / WN, wn = w - (w / WN) * WN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, part = tid >> 6;
+  const int l32 = lane & 31, kg = lane >> 5;
+  f32x4_t sum[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) sum[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 2
+  for (int s = 0; s < pp.splits; ++s) {
+    const f32x4_t* src =
+        (const f32x4_t*)pp.ws + ((int64_t)tile_id * pp.splits + s) * (kThreads * NV) + w * 64 + lane;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) sum[k] += src[(part * PER + k) * kThreads];
   }
+  const TileGeo geo = tile_geo(a, pp, tile_id, BM);
+  const int M = a.M;
+  const uint16_t* bias = (const uint16_t*)a.bias;
+  with_act(a.act, [&](auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int i = part * PER + k;             // value index (fp*FC + fc)*4 + g
+      const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
+      const int m = geo.m0 + wm * SUBM + fc * 32 + l32;
+      const float bv = (bias && m < M) ? bf16_to_f32(bias[m]) : 0.0f;
+      const uint32_t lo = pack_bf16x2(act_c<ACT>(sum[k][0] + bv), act_c<ACT>(sum[k][1] + bv));
+      const uint32_t hi = pack_bf16x2(act_c<ACT>(sum[k][2] + bv), act_c<ACT>(sum[k][3] + bv));
+      *(u32x2_t*)(E + (fc * 32 + l32) * EROW + fp * 32 + 8 * g + 4 * kg) = u32x2_t{lo, hi};
+    }
+  });
+  __syncthreads();
+  const int mlo = wm * SUBM, mhi = min(mlo + SUBM, M - geo.m0);
+  const int slo = wn * SUBN, shi = min(slo + SUBN, pp.NT * 32);
+  store_runs(a, pp, E, EROW, geo.img0, geo.imgs_here, geo.oh0, geo.rows_here, geo.m0, mlo, mhi, slo,
+             shi, tid, kThreads);
 }
 
 template <int WM, int WN, int FP>
 int launch_cfg(const ConvArgs& a, const PatchPlan& p, hipStream_t s) {
   constexpr int FC = 2;
   constexpr int BM = 32 * WM * FC;
-  dim3 grid(p.nrb * p.nib * p.nmb, 1, 1);
+  dim3 grid(p.nrb * p.nib * p.nmb * p.splits, 1, 1);
 #define OX_PATCH_LAUNCH(P_, S_)                                                                  \
   do {                                                                                           \
     if (a.w_packed)                                                                              \
@@ -392,6 +484,9 @@ int launch_cfg(const ConvArgs& a, const PatchPlan& p, hipStream_t s) {
     else OX_PATCH_LAUNCH(1, 2);
   }
 #undef OX_PATCH_LAUNCH
+  if (p.splits > 1)
+    hipLaunchKernelGGL((conv3x3_reduce<WM, WN, FP, FC>), dim3(p.nrb * p.nib * p.nmb * 4), dim3(kThreads),
+                       0, s, a, p);
   return (int)hipGetLastError();
 }
 

@@ -56,13 +56,29 @@ PatchPlan make(const ConvArgs& a, const Cfg& c, int TR, int IMB) {
   p.units = IMB * 4 * ((rows * a.W + 2 * p.VW - 2) / p.VW);
   p.lds = std::max(p.BM * (9 * 64 + 16) + p.npos * kCell,
                    p.BM * (p.NT * 32 + 8) * 2);   // the epilogue reuses LDS as [channel][pixel]
+  p.splits = 1;
+  p.cps = std::max(1, a.C / 32);
+  p.ws = nullptr;
   return p;
+}
+
+// split the channel chunks of each tile into `splits` slices (at least one chunk each)
+void set_splits(const ConvArgs& a, PatchPlan* p, int splits) {
+  const int nchunks = std::max(1, a.C / 32);
+  splits = std::max(1, std::min(splits, nchunks));
+  p->cps = (nchunks + splits - 1) / splits;
+  p->splits = (nchunks + p->cps - 1) / p->cps;
+}
+
+size_t ws_bytes(const PatchPlan& p) {
+  const int FP = p.FN;
+  return p.splits > 1 ? (size_t)p.nrb * p.nib * p.nmb * p.splits * 8192 * FP * sizeof(float) : 0;
 }
 
 bool fits(const PatchPlan& p) {
   const int ntmax = (4 / p.WM) * p.FN;
   return p.NT <= ntmax && p.lds <= kLdsMax && p.units <= p.UPT * 256 &&
-         (int64_t)p.nrb * p.nib * p.nmb < (1 << 30);
+         (int64_t)p.nrb * p.nib * p.nmb * p.splits < (1 << 30);
 }
 
 // Rough time model: MFMA cycles per SIMD over the whole grid against the
@@ -97,19 +113,21 @@ int band_rows(const ConvArgs& a, int slots) {
 
 }  // namespace
 
-// OX_PATCH_PLAN=WM:FP:TR:IMB pins the plan (for measurements); a pinned plan
-// that does not fit this geometry makes the kernel inapplicable.
+// OX_PATCH_PLAN=WM:FP:TR:IMB[:S] pins the plan (for measurements), S being
+// the split-K slice count; a pinned plan that does not fit this geometry
+// makes the kernel inapplicable.
 bool pinned_plan(const ConvArgs& a, PatchPlan* out, bool* pinned) {
   const char* e = getenv("OX_PATCH_PLAN");
   *pinned = false;
   if (!e || !*e) return false;
-  int wm, fp, tr, imb;
-  if (sscanf(e, "%d:%d:%d:%d", &wm, &fp, &tr, &imb) != 4) return false;
+  int wm, fp, tr, imb, sk = 1;
+  if (sscanf(e, "%d:%d:%d:%d:%d", &wm, &fp, &tr, &imb, &sk) < 4) return false;
   *pinned = true;
   for (const Cfg& c : kCfgs) {
     if (c.WM != wm || c.FP != fp) continue;
     if (tr < 1 || tr > a.Ho || imb < 1 || (imb > 1 && tr != a.Ho)) return false;
-    const PatchPlan p = make(a, c, tr, imb);
+    PatchPlan p = make(a, c, tr, imb);
+    set_splits(a, &p, sk);
     if (!fits(p)) return false;
     *out = p;
     return true;
@@ -121,21 +139,41 @@ bool patch_plan(const ConvArgs& a, PatchPlan* out) {
   bool pinned;
   const bool ok = pinned_plan(a, out, &pinned);
   if (pinned) return ok;
-  // Selection rule, from a sweep of every configuration and band height on
-  // the ResNet-50 3x3 layers at batch 32 (MI355X): 64 output channels per
-  // block won on every shape; 128-pixel blocks (one pixel tile per wave) won
-  // wherever such a block holds at least three output rows, 256-pixel blocks
-  // on the wide 56-column layer.  The band is the tallest that fits the
-  // block, evened out over the image.
+  // Selection rule, from a sweep of every configuration, band height,
+  // images per block and split count on the ResNet-50 3x3 layers at batch
+  // 32 (MI355X): 64 output channels per block won on every shape; 128-pixel
+  // blocks (one pixel tile per wave) won wherever such a block holds at least
+  // three output rows, 256-pixel blocks on the wide 56-column layer.  The
+  // band is the tallest that fits the block, evened out over the image.
+  // Images of at most 64 output pixels go two or more to a block; when the
+  // tiles then number fewer than 200, each tile's channel chunks are split
+  // into slices of at least four chunks, up to ~512 work units (split-K:
+  // two slices per CU-slot won on the 7x7 layers, where 16 chunks per tile
+  // otherwise run back to back on half the CUs).
   {
     const int wo = std::max(1, a.Wo);
     const Cfg& c = (128 / wo >= 3 || a.Ho <= 128 / wo) ? kCfgs[1] : kCfgs[0];
-    for (int TR = band_rows(a, slots_of(c)); TR >= 1; --TR) {
-      const PatchPlan p = make(a, c, TR, 1);
-      if (fits(p)) {
-        *out = p;
-        return true;
+    const int slots = slots_of(c);
+    const int64_t img = (int64_t)a.Ho * a.Wo;
+    bool got = false;
+    PatchPlan p;
+    if (img * 2 <= slots) {
+      p = make(a, c, a.Ho, (int)(slots / img));
+      got = fits(p);
+    }
+    for (int TR = band_rows(a, slots); !got && TR >= 1; --TR) {
+      p = make(a, c, TR, 1);
+      got = fits(p);
+    }
+    if (got) {
+      const int64_t tiles = (int64_t)p.nrb * p.nib * p.nmb;
+      const int nchunks = std::max(1, a.C / 32);
+      if (tiles < 200 && nchunks >= 8) {
+        set_splits(a, &p, (int)std::min<int64_t>((512 + tiles - 1) / tiles, nchunks / 4));
+        if (!fits(p)) set_splits(a, &p, 1);
       }
+      *out = p;
+      return true;
     }
   }
   bool found = false;
@@ -171,6 +209,10 @@ bool conv_patch_applicable(const ConvArgs& a) {
 int launch_conv_patch(const ConvArgs& a, void* stream) {
   PatchPlan p;
   if (!patch_plan(a, &p)) return 1;  // hipErrorInvalidValue
+  if (p.splits > 1) {
+    p.ws = (float*)stream_workspace(stream, ws_bytes(p));
+    if (!p.ws) return 2;             // hipErrorOutOfMemory
+  }
   if (p.WM == 1) {
     return p.FN == 2 ? launch_patch_1_4_2(a, p, stream) : launch_patch_1_4_1(a, p, stream);
   }
@@ -180,8 +222,9 @@ int launch_conv_patch(const ConvArgs& a, void* stream) {
 const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap) {
   PatchPlan p;
   if (!patch_plan(a, &p)) return "";
-  snprintf(buf, cap, "BM=%d WM=%d FP=%d TR=%d IMB=%d NT=%d VW=%d blocks=%lld lds=%d", p.BM, p.WM,
-           p.FN, p.TR, p.IMB, p.NT, p.VW, (long long)p.nrb * p.nib * p.nmb, p.lds);
+  snprintf(buf, cap, "BM=%d WM=%d FP=%d TR=%d IMB=%d NT=%d VW=%d splits=%d blocks=%lld lds=%d", p.BM,
+           p.WM, p.FN, p.TR, p.IMB, p.NT, p.VW, p.splits, (long long)p.nrb * p.nib * p.nmb * p.splits,
+           p.lds);
   return buf;
 }
 

@@ -106,6 +106,9 @@ struct PatchPlan {
   int VW;               // plane positions per staging unit (1 or 2)
   int units;            // upper bound of staging units per block
   int lds;              // bytes of LDS
+  int splits;           // slices of the channel chunks per tile (split-K), 1 = none
+  int cps;              // chunks per slice
+  float* ws;            // split-K partials (splits * tiles * BM * NT*32 floats), else null
 };
 
 // Plan of the pointwise (1x1) kernel: block configuration and launch grid.

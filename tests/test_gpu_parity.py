@@ -615,6 +615,37 @@ def test_patch_each_config(ox, cfg, monkeypatch):
     assert ran == 4
 
 
+@pytest.mark.parametrize("cfg", ["1:2", "1:1", "2:2", "2:1"])
+def test_patch_split_k(ox, cfg, monkeypatch):
+    # split-K on the 3x3 kernel: fp32 partials of channel slices, added in
+    # slice order by a second kernel per wave sub-tile; parity with the
+    # oracle and bit-identical repeats
+    monkeypatch.setenv("OX_FORCE_KERNEL", "patch")
+    r = np.random.default_rng(5150 + int(cfg[0]) * 10 + int(cfg[2]))
+    ran = 0
+    for ci, (N, Cin, H, W, M, s, splits) in enumerate([
+            (3, 128, 7, 7, 96, 1, 2), (2, 160, 10, 9, 70, 2, 3), (4, 96, 5, 6, 130, 1, 3)]):
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 3, 3)) / math.sqrt(9 * Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        pads = (1, 1, 1, 1)
+        ho, wo = ox.conv_out_hw(H, W, 3, 3, (s, s), pads, (1, 1))
+        ref = oracle.conv2d(X, Wt, b, (s, s), pads, (1, 1), 1, "relu")
+        for tr, imb in [(ho, 2), (ho, 1), (max(1, ho // 2), 1)]:
+            monkeypatch.setenv("OX_PATCH_PLAN", "%s:%d:%d:%d" % (cfg, tr, imb, splits))
+            try:
+                ox.ox_conv2d_variant("bf16", N, Cin, H, W, M, 3, 3, (s, s), pads, (1, 1), 1)
+            except ox.OxError:
+                continue
+            say("patch split", cfg, "TR", tr, "IMB", imb, "S", splits, (N, Cin, H, W, M, s))
+            Y1 = run_conv(ox, X, Wt, b, "bf16", (s, s), pads, (1, 1), 1, "relu")
+            Y2 = run_conv_packed(ox, X, Wt, b, (s, s), pads, (1, 1), "relu")
+            assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
+            assert_close(host64(Y1), ref, "bf16", "split %s case %d tr %d" % (cfg, ci, tr))
+            ran += 1
+    assert ran >= 3
+
+
 @pytest.mark.parametrize("N", [1, 32])
 def test_c3_resnet50_3x3_packed(ox, N):
     for li, layer in enumerate(synth.resnet50_layers(N)):
