@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
     p.add_argument("--rows", default=None, help="write per-layer rows as JSON to this file")
+    p.add_argument("--copy-bytes", type=int, default=0,
+                   help="only run 10 plain device copies of this many bytes (the reference "
+                        "reading for HBM byte counters), then exit")
     return p.parse_args()
 
 
@@ -90,11 +93,22 @@ def conv_layers(ox, synth, torch, cfg, layers, dtype, stream):
             variant += "+packed"
         args = (code, C.byref(d), Xd.data_ptr(), Wlaunch.data_ptr(), bd.data_ptr(), act,
                 Yd.data_ptr(), stream)
+        # split-K scratch for layers with few output tiles: allocated once,
+        # outside the timed region, and handed to ox_conv2d_fused_ws
+        wsb = ox.ox_conv2d_workspace_bytes(dtype, l.N, l.C, l.H, l.W, l.M, l.kh, l.kw,
+                                           (l.stride, l.stride), l.onnx_pads, (1, 1), l.group)
+        ws = None
+        if wsb:
+            ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+            args = (code, C.byref(d), Xd.data_ptr(), Wlaunch.data_ptr(),
+                    1 if fn is ox.lib.ox_conv2d_fused_packed else 0, bd.data_ptr(), act,
+                    Yd.data_ptr(), ws.data_ptr(), wsb, stream)
+            fn = ox.lib.ox_conv2d_fused_ws
         # the oracle reads the bits the GPU reads: X as rounded, W' and b' as
         # the device holds them
         Wh = Wd.float().cpu().numpy().astype(np.float64)
         bh = bd.float().cpu().numpy().astype(np.float64)
-        keep = (Xd, Wd, Wlaunch, bd, Yd, d)
+        keep = (Xd, Wd, Wlaunch, bd, Yd, d, ws)
 
         def launch(fn=fn, args=args, keep=keep):
             return fn(*args)
@@ -246,6 +260,42 @@ def cpu_baseline(layers, seconds, int8):
                       % (npts, macs_per_layer, len(layers), dt)}
 
 
+# ------------------------------------------------------- measured traffic --
+
+def _sources_digest(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload, dtype):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE per dispatch, scaled by a plain copy's
+    reading), or None when there is none for this kernel and workload or the
+    kernel's sources changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s_%s.txt" % (workload, dtype))
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            line = line.strip()
+            if line and not line.startswith("#") and "=" in line:
+                k, v = line.split("=", 1)
+                kv.setdefault(k.strip(), []).append(v.strip())
+    for entry in kv.get("kernel", []):
+        name, sources, digest, per_launch = entry.split("|")
+        if name != kernel:
+            continue
+        if _sources_digest(sources.split(",")) != digest:
+            return None
+        return float(per_launch), os.path.relpath(path, ROOT)
+    return None
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -260,6 +310,14 @@ def main():
     import synth
 
     torch.cuda.set_device(0)
+    if args.copy_bytes:
+        src = torch.empty(args.copy_bytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(10):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_bytes, "copies": 10}))
+        return
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     wl = args.workload
@@ -326,29 +384,47 @@ def main():
     ms_per_step = total_ms / K
     value = step_flops / (ms_per_step * 1e-3) / 1e12
 
-    # dominant kernel: the variant with the largest share of the step
+    # per-layer roofline (attainable time t_roof = max(FLOP / MFMA peak,
+    # algorithmic bytes / HBM peak)) and the dominant kernel: the variant
+    # with the largest share of the step
+    pk = PEAK[dtype]
     groups = {}
     for L, t in zip(layers, per_layer_ms):
-        g = groups.setdefault(L.variant, {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0})
+        g = groups.setdefault(L.variant, {"ms": 0.0, "flops": 0.0, "bytes": 0.0, "n": 0,
+                                          "t_flop": 0.0, "t_byte": 0.0, "t_roof": 0.0})
         g["ms"] += t
         g["flops"] += L.flops
         g["bytes"] += L.nbytes
         g["n"] += 1
+        tf, tb = L.flops / (pk * 1e12), L.nbytes / (HBM_PEAK * 1e9)
+        if L.variant.startswith("dw") or L.variant.startswith("gemv"):
+            tf = 0.0          # no MFMA: counted against HBM only
+        g["t_flop"] += tf
+        g["t_byte"] += tb
+        g["t_roof"] += max(tf, tb)
     dom = max(groups, key=lambda k: groups[k]["ms"])
     g = groups[dom]
     avg_us = g["ms"] / g["n"] * 1e3
-    if dom.startswith("dw") or dom.startswith("gemv"):
+    if g["t_byte"] >= g["t_flop"]:
         ach = g["bytes"] / (g["ms"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK, "unit": "GB/s",
                 "frac": ach / HBM_PEAK, "traffic": None}
+        algo_per_launch = g["bytes"] / g["n"]
     else:
         ach = g["flops"] / (g["ms"] * 1e-3) / 1e12
-        pk = PEAK[dtype]
-        roof = {"bound": "mfma", "achieved": ach, "peak": pk, "unit": "TOPS" if dtype == "i8" else "TFLOP/s",
-                "frac": ach / pk, "traffic": None}
+        roof = {"bound": "mfma", "achieved": ach, "peak": pk,
+                "unit": "TOPS" if dtype == "i8" else "TFLOP/s", "frac": ach / pk, "traffic": None}
+        algo_per_launch = g["bytes"] / g["n"]
+    mt = measured_traffic(dom, wl, dtype)
+    roof["algorithmic_bytes_per_launch"] = algo_per_launch
+    if mt:
+        roof["traffic"] = mt[0]
+        roof["traffic_vs_algorithmic"] = mt[0] / max(1.0, algo_per_launch)
+        roof["traffic_source"] = mt[1]
     roof["kernel"] = dom
     roof["launches_per_step"] = g["n"]
     roof["avg_launch_us"] = avg_us
+    roof["roofline_frac"] = g["t_roof"] / (g["ms"] * 1e-3)   # sum t_roof / sum t_meas
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -367,11 +443,17 @@ def main():
     if args.rows:
         rows = []
         for L, t in zip(layers, per_layer_ms):
+            tf, tb = L.flops / (pk * 1e12), L.nbytes / (HBM_PEAK * 1e9)
+            if L.variant.startswith("dw") or L.variant.startswith("gemv"):
+                tf = 0.0
             rows.append({"layer": L.name, "variant": L.variant, "us": t * 1e3, "flop": L.flops,
-                         "bytes": L.nbytes, "tflops": L.flops / (t * 1e-3) / 1e12,
+                         "bytes": L.nbytes, "ai": L.flops / max(1.0, L.nbytes),
+                         "bound": "mfma" if tf > tb else "hbm",
+                         "tflops": L.flops / (t * 1e-3) / 1e12,
                          "gbs": L.nbytes / (t * 1e-3) / 1e9,
                          "mfma_frac": L.flops / (t * 1e-3) / 1e12 / PEAK[dtype],
-                         "hbm_frac": L.nbytes / (t * 1e-3) / 1e9 / HBM_PEAK})
+                         "hbm_frac": L.nbytes / (t * 1e-3) / 1e9 / HBM_PEAK,
+                         "roofline_frac": max(tf, tb) / (t * 1e-3)})
         with open(args.rows, "w") as f:
             json.dump({"workload": wl, "dtype": dtype, "rows": rows}, f, indent=1)
     print(json.dumps(out), flush=True)

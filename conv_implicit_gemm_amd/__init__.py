@@ -26,7 +26,7 @@ STATUS_NAMES = {0: "OX_OK", 1: "OX_ERR_INVALID_ARG", 2: "OX_ERR_SHAPE",
 EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_int8",
            "ox_conv2d_variant", "ox_conv2d_fused_packed", "ox_conv2d_packed_weights_bytes",
            "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
-           "ox_last_error", "ox_version")
+           "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws")
 
 
 class OxError(RuntimeError):
@@ -59,6 +59,8 @@ def _load():
         "ox_conv2d_variant": (I, [I, P, C.c_char_p, C.c_size_t]),
         "ox_conv2d_fused_packed": (I, [I, P, P, P, P, I, P, P]),
         "ox_conv2d_packed_weights_bytes": (C.c_size_t, [I, P]),
+        "ox_conv2d_workspace_bytes": (C.c_size_t, [I, P]),
+        "ox_conv2d_fused_ws": (I, [I, P, P, P, I, P, I, P, P, C.c_size_t, P]),
         "ox_conv2d_pack_weights": (I, [I, P, P, P]),
         "ox_fold_batchnorm": (I, [I64, I64, P, P, P, P, P, P, F, P, P]),
         "ox_int8_params_bytes": (C.c_size_t, [I64]),
@@ -184,8 +186,10 @@ def ox_gemm_fused(A, B, bias=None, alpha=1.0, beta=1.0, transA=False, transB=Fal
 
 
 def ox_conv2d_fused(X, W, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1), group=1,
-                    act="none", Y=None, stream=None):
-    """ONNX Conv + bias + activation (NCHW).  W is [M, C/group, kH, kW]."""
+                    act="none", Y=None, stream=None, workspace=None):
+    """ONNX Conv + bias + activation (NCHW).  W is [M, C/group, kH, kW].
+    workspace: optional device tensor of >= ox_conv2d_workspace_bytes bytes
+    (enables split-K; goes through ox_conv2d_fused_ws)."""
     torch = _torch()
     for t, n in ((X, "X"), (W, "W"), (bias, "bias"), (Y, "Y")):
         _dense(t, n)
@@ -195,13 +199,20 @@ def ox_conv2d_fused(X, W, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=
     if Y is None:
         ho, wo = conv_out_hw(H, Wd, kH, kW, stride, pads, dilation)
         Y = torch.empty((N, M, max(ho, 0), max(wo, 0)), dtype=X.dtype, device=X.device)
-    _check(lib.ox_conv2d_fused(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), ACT[act],
-                               _ptr(Y), _stream(stream)))
+    if workspace is not None:
+        _dense(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(lib.ox_conv2d_fused_ws(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), 0, _ptr(bias),
+                                      ACT[act], _ptr(Y), _ptr(workspace), nbytes, _stream(stream)))
+    else:
+        _check(lib.ox_conv2d_fused(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), ACT[act],
+                                   _ptr(Y), _stream(stream)))
     return Y
 
 
 def ox_conv2d_fused_packed(X, Wp, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
-                           group=1, act="none", Y=None, M=None, kernel=(3, 3), stream=None):
+                           group=1, act="none", Y=None, M=None, kernel=(3, 3), stream=None,
+                           workspace=None):
     """ox_conv2d_fused with weights packed by ox_conv2d_pack_weights (a device
     tensor of the packed bytes' dtype).  M: output channels; kernel: (kH, kW)."""
     torch = _torch()
@@ -215,9 +226,22 @@ def ox_conv2d_fused_packed(X, Wp, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), d
     if Y is None:
         ho, wo = conv_out_hw(H, Wd, kH, kW, stride, pads, dilation)
         Y = torch.empty((N, M, max(ho, 0), max(wo, 0)), dtype=X.dtype, device=X.device)
-    _check(lib.ox_conv2d_fused_packed(_dtype_code(X), C.byref(d), _ptr(X), _ptr(Wp), _ptr(bias), ACT[act],
-                                      _ptr(Y), _stream(stream)))
+    if workspace is not None:
+        _dense(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+        _check(lib.ox_conv2d_fused_ws(_dtype_code(X), C.byref(d), _ptr(X), _ptr(Wp), 1, _ptr(bias),
+                                      ACT[act], _ptr(Y), _ptr(workspace), nbytes, _stream(stream)))
+    else:
+        _check(lib.ox_conv2d_fused_packed(_dtype_code(X), C.byref(d), _ptr(X), _ptr(Wp), _ptr(bias),
+                                          ACT[act], _ptr(Y), _stream(stream)))
     return Y
+
+
+def ox_conv2d_workspace_bytes(dtype, N, Cin, H, W, M, kH, kW, stride=(1, 1), pads=(0, 0, 0, 0),
+                              dilation=(1, 1), group=1):
+    """Scratch bytes ox_conv2d_fused_ws may use for this geometry (0: none)."""
+    d = conv_desc(N, Cin, H, W, M, kH, kW, stride, pads, dilation, group)
+    return int(lib.ox_conv2d_workspace_bytes({"f32": OX_F32, "bf16": OX_BF16}[dtype], C.byref(d)))
 
 
 def ox_conv2d_packed_weights_bytes(dtype, N, Cin, H, W, M, kH, kW, stride=(1, 1), pads=(0, 0, 0, 0),

@@ -93,15 +93,30 @@ __device__ __forceinline__ void store_runs(const ConvArgs& a, const PatchPlan& p
 }
 
 // Geometry of logical tile `tile_id`: first output channel, first image,
-// first output row, rows and images actually present.
+// first output row, rows and images actually present.  The logical order
+// cuts the (pixel block x channel block) grid into ga x gb equal rectangles,
+// one per XCD (xcd_tile hands each XCD one contiguous eighth of the order),
+// each walked channel block fastest: an XCD then re-reads its input bands
+// (for its channel blocks) and its weight rows (for its pixel blocks) from
+// its own L2.  ga = gb = 1: channel-block-major order.
 struct TileGeo {
   int m0, img0, oh0, rows_here, imgs_here;
 };
 __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, const PatchPlan& pp, int tile_id, int BM) {
   const int npb = pp.nrb * pp.nib;
+  int mb, bx;
+  if (pp.ga * pp.gb > 1) {
+    const int rp = npb / pp.ga, rm = pp.nmb / pp.gb;   // exact: the planner checks
+    const int r = tile_id / (rp * rm), w = tile_id - (tile_id / (rp * rm)) * (rp * rm);
+    const int ri = r / pp.gb, rj = r - (r / pp.gb) * pp.gb;
+    bx = ri * rp + w / rm;
+    mb = rj * rm + (w - (w / rm) * rm);
+  } else {
+    mb = tile_id / npb;
+    bx = tile_id - mb * npb;
+  }
   TileGeo t;
-  t.m0 = (tile_id / npb) * BM;
-  const int bx = tile_id - (tile_id / npb) * npb;
+  t.m0 = mb * BM;
   t.img0 = (bx / pp.nrb) * pp.IMB;
   t.oh0 = (bx - (bx / pp.nrb) * pp.nrb) * pp.TR;
   t.rows_here = min(pp.TR, a.Ho - t.oh0);

@@ -59,7 +59,39 @@ PatchPlan make(const ConvArgs& a, const Cfg& c, int TR, int IMB) {
   p.splits = 1;
   p.cps = std::max(1, a.C / 32);
   p.ws = nullptr;
+  p.ga = p.gb = 1;
   return p;
+}
+
+// XCD rectangles (see tile_geo): each of the 8 XCDs takes (pixel blocks /
+// ga) x (channel blocks / gb) tiles, so every input band is fetched into gb
+// L2s and every weight row into ga.  Pick the split of 8 = ga*gb (exact
+// divisions only) with the fewest estimated L2 fill bytes, against the plain
+// channel-block-major order (bands into ~nmb L2s, weights into ~8/nmb).
+void set_groups(const ConvArgs& a, PatchPlan* p) {
+  p->ga = p->gb = 1;
+  const int npb = p->nrb * p->nib;
+  const double xb = (double)a.N * a.C * a.H * a.W * 2, wb = (double)a.M * a.C * 9 * 2;
+  const int nm = p->nmb;
+  double best = xb * std::min(nm, 8) + wb * std::max(1.0, 8.0 / nm);
+  if (const char* e = getenv("OX_PATCH_XCD")) {
+    int ga, gb;
+    if (sscanf(e, "%d:%d", &ga, &gb) == 2 && ga * gb == 8 && npb % ga == 0 && nm % gb == 0) {
+      p->ga = ga;
+      p->gb = gb;
+    }
+    return;
+  }
+  for (int gb = 1; gb <= 8; gb *= 2) {
+    const int ga = 8 / gb;
+    if (npb % ga || nm % gb) continue;
+    const double c = xb * gb + wb * ga;
+    if (c < best * 0.97) {
+      best = c;
+      p->ga = ga;
+      p->gb = gb;
+    }
+  }
 }
 
 // split the channel chunks of each tile into `splits` slices (at least one chunk each)
@@ -114,8 +146,8 @@ int band_rows(const ConvArgs& a, int slots) {
 }  // namespace
 
 // OX_PATCH_PLAN=WM:FP:TR:IMB[:S] pins the plan (for measurements), S being
-// the split-K slice count; a pinned plan that does not fit this geometry
-// makes the kernel inapplicable.
+// the split-K slice count (taken only when the call brings a workspace); a
+// pinned plan that does not fit this geometry makes the kernel inapplicable.
 bool pinned_plan(const ConvArgs& a, PatchPlan* out, bool* pinned) {
   const char* e = getenv("OX_PATCH_PLAN");
   *pinned = false;
@@ -127,8 +159,9 @@ bool pinned_plan(const ConvArgs& a, PatchPlan* out, bool* pinned) {
     if (c.WM != wm || c.FP != fp) continue;
     if (tr < 1 || tr > a.Ho || imb < 1 || (imb > 1 && tr != a.Ho)) return false;
     PatchPlan p = make(a, c, tr, imb);
-    set_splits(a, &p, sk);
+    set_splits(a, &p, a.ws ? sk : 1);
     if (!fits(p)) return false;
+    set_groups(a, &p);
     *out = p;
     return true;
   }
@@ -168,10 +201,11 @@ bool patch_plan(const ConvArgs& a, PatchPlan* out) {
     if (got) {
       const int64_t tiles = (int64_t)p.nrb * p.nib * p.nmb;
       const int nchunks = std::max(1, a.C / 32);
-      if (tiles < 200 && nchunks >= 8) {
+      if (a.ws && tiles < 200 && nchunks >= 8) {
         set_splits(a, &p, (int)std::min<int64_t>((512 + tiles - 1) / tiles, nchunks / 4));
         if (!fits(p)) set_splits(a, &p, 1);
       }
+      set_groups(a, &p);
       *out = p;
       return true;
     }
@@ -210,8 +244,8 @@ int launch_conv_patch(const ConvArgs& a, void* stream) {
   PatchPlan p;
   if (!patch_plan(a, &p)) return 1;  // hipErrorInvalidValue
   if (p.splits > 1) {
-    p.ws = (float*)stream_workspace(stream, ws_bytes(p));
-    if (!p.ws) return 2;             // hipErrorOutOfMemory
+    if (!a.ws || a.ws_bytes < ws_bytes(p)) return 1;   // validated by the entry point
+    p.ws = (float*)a.ws;
   }
   if (p.WM == 1) {
     return p.FN == 2 ? launch_patch_1_4_2(a, p, stream) : launch_patch_1_4_1(a, p, stream);
@@ -219,12 +253,17 @@ int launch_conv_patch(const ConvArgs& a, void* stream) {
   return p.FN == 2 ? launch_patch_2_2_2(a, p, stream) : launch_patch_2_2_1(a, p, stream);
 }
 
+size_t conv_patch_ws_bytes(const ConvArgs& a) {
+  PatchPlan p;
+  return patch_plan(a, &p) ? ws_bytes(p) : 0;
+}
+
 const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap) {
   PatchPlan p;
   if (!patch_plan(a, &p)) return "";
-  snprintf(buf, cap, "BM=%d WM=%d FP=%d TR=%d IMB=%d NT=%d VW=%d splits=%d blocks=%lld lds=%d", p.BM,
-           p.WM, p.FN, p.TR, p.IMB, p.NT, p.VW, p.splits, (long long)p.nrb * p.nib * p.nmb * p.splits,
-           p.lds);
+  snprintf(buf, cap, "BM=%d WM=%d FP=%d TR=%d IMB=%d NT=%d VW=%d splits=%d xcd=%dx%d blocks=%lld lds=%d",
+           p.BM, p.WM, p.FN, p.TR, p.IMB, p.NT, p.VW, p.splits, p.ga, p.gb,
+           (long long)p.nrb * p.nib * p.nmb * p.splits, p.lds);
   return buf;
 }
 

@@ -47,9 +47,10 @@ PwPlan make(const ConvArgs& a, int WM, int KC) {
   const int64_t tiles = (int64_t)p.npb * p.nmb;
   const int nchunks = std::max(1, a.C / KC);   // (a C that KC does not divide is rejected by valid)
   int target = 1;
-  if (tiles < 192 && nchunks >= 4)
+  if (a.ws && tiles < 192 && nchunks >= 4)
     target = (int)std::min<int64_t>((192 + tiles - 1) / tiles, nchunks / 4);
-  if (const char* e = getenv("OX_PW_SPLITS")) target = std::max(1, std::min(nchunks, atoi(e)));
+  if (const char* e = getenv("OX_PW_SPLITS"))
+    if (a.ws) target = std::max(1, std::min(nchunks, atoi(e)));
   p.cps = (nchunks + target - 1) / target;
   p.splits = (nchunks + p.cps - 1) / p.cps;
   p.ws = nullptr;
@@ -112,11 +113,16 @@ int launch_conv_pw(const ConvArgs& a, void* stream) {
   PwPlan p;
   if (!pw_plan(a, &p)) return 1;   // hipErrorInvalidValue
   if (p.splits > 1) {
-    p.ws = (float*)stream_workspace(stream, ws_bytes(p));
-    if (!p.ws) return 2;           // hipErrorOutOfMemory
+    if (!a.ws || a.ws_bytes < ws_bytes(p)) return 1;   // validated by the entry point
+    p.ws = (float*)a.ws;
   }
   if (p.WM == 1) return p.KC == 64 ? launch_pw_1_64(a, p, stream) : launch_pw_1_32(a, p, stream);
   return p.KC == 64 ? launch_pw_2_64(a, p, stream) : launch_pw_2_32(a, p, stream);
+}
+
+size_t conv_pw_ws_bytes(const ConvArgs& a) {
+  PwPlan p;
+  return pw_plan(a, &p) ? ws_bytes(p) : 0;
 }
 
 const char* conv_pw_describe(const ConvArgs& a, char* buf, int cap) {

@@ -292,6 +292,12 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
   } else if (f.tile != -1) {
     return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to the %s kernel", fn, kind_name(kind));
   }
+  if (a.ws) {
+    const size_t need = kind == KIND_PW ? conv_pw_ws_bytes(a) : kind == KIND_PATCH ? conv_patch_ws_bytes(a) : 0;
+    if (need > a.ws_bytes)
+      return fail(OX_ERR_INVALID_ARG, "%s: workspace_bytes=%zu < %zu that this geometry needs", fn,
+                  a.ws_bytes, need);
+  }
   if (log_on()) {
     char plan[160] = "";
     if (kind == KIND_PATCH) conv_patch_describe(a, plan, sizeof(plan));
@@ -552,6 +558,45 @@ ox_status ox_conv2d_fused_packed(ox_dtype t, const ox_conv_desc* d, const void* 
   }
   ConvArgs a = conv_args((int)t, d, Ho, Wo, X, Wp, bias, Y, (int)act);
   a.w_packed = 1;
+  return conv_dispatch(fn, d, a, stream);
+}
+
+size_t ox_conv2d_workspace_bytes(ox_dtype t, const ox_conv_desc* d) {
+  const char* fn = "ox_conv2d_workspace_bytes";
+  int64_t Ho, Wo;
+  if ((t != OX_F32 && t != OX_BF16) || check_conv_desc(fn, d, &Ho, &Wo)) return 0;
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, nullptr, nullptr, nullptr, nullptr, ACT_NONE);
+  a.ws = (void*)(uintptr_t)256;   // "a workspace will be given": plan with split-K allowed
+  a.ws_bytes = SIZE_MAX;
+  const Force f = read_force();
+  int kind;
+  if (select_conv(fn, d, a, f, &kind)) return 0;
+  return kind == KIND_PW ? conv_pw_ws_bytes(a) : kind == KIND_PATCH ? conv_patch_ws_bytes(a) : 0;
+}
+
+ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                             int w_packed, const void* bias, ox_act act, void* Y, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  const char* fn = "ox_conv2d_fused_ws";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  st = check_act(fn, act);
+  if (st) return st;
+  if (w_packed != 0 && w_packed != 1) return fail(OX_ERR_INVALID_ARG, "%s: w_packed=%d is not 0 or 1", fn, w_packed);
+  if (workspace && ((uintptr_t)workspace) % 16)
+    return fail(OX_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  int64_t Ho, Wo;
+  st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  if (d->N > 0) {
+    if (!X) return fail(OX_ERR_INVALID_ARG, "%s: X is NULL", fn);
+    if (!W) return fail(OX_ERR_INVALID_ARG, "%s: W is NULL", fn);
+    if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
+  }
+  ConvArgs a = conv_args((int)t, d, Ho, Wo, X, W, bias, Y, (int)act);
+  a.w_packed = w_packed;
+  a.ws = workspace;
+  a.ws_bytes = workspace ? workspace_bytes : 0;
   return conv_dispatch(fn, d, a, stream);
 }
 

@@ -86,6 +86,8 @@ struct ConvArgs {
   int w_vec;              // weight rows allow 16-byte vector loads
   int x_vec;              // (1x1 only) pixel rows allow 16-byte loads
   int w_packed;           // Wt is in the packed tap-major layout (see ox_conv2d_pack_weights)
+  void* ws;               // caller's scratch for split-K partials, or null (no split-K)
+  size_t ws_bytes;        // its size
 };
 
 // Plan of the LDS-patch 3x3 kernel (host-chosen, passed to the kernel by
@@ -106,6 +108,7 @@ struct PatchPlan {
   int VW;               // plane positions per staging unit (1 or 2)
   int units;            // upper bound of staging units per block
   int lds;              // bytes of LDS
+  int ga, gb;           // XCD rectangles: pixel blocks in ga groups x channel blocks in gb
   int splits;           // slices of the channel chunks per tile (split-K), 1 = none
   int cps;              // chunks per slice
   float* ws;            // split-K partials (splits * tiles * BM * NT*32 floats), else null
@@ -126,12 +129,10 @@ struct PwPlan {
   float* ws;  // split-K partials (splits * tiles * BM * BN floats), else null
 };
 
-// Per-(device, stream) scratch of at least `bytes` bytes, owned by the
-// library and kept until the process ends; grown (after synchronising the
-// stream) when a call needs more.  Calls on one stream run in order, so they
-// may share it; calls on different streams get different buffers.  Returns
-// null if the allocation fails.
-void* stream_workspace(void* stream, size_t bytes);
+// Scratch bytes the plan chosen for `a` needs (0: no split-K).  Split-K is
+// only planned when a.ws is non-null.
+size_t conv_pw_ws_bytes(const ConvArgs& a);
+size_t conv_patch_ws_bytes(const ConvArgs& a);
 
 // Plan of the few-input-channel kernel (C <= 4, e.g. an RGB stem).
 struct SmallcPlan {

@@ -149,6 +149,28 @@ ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_
 ox_status ox_conv2d_fused_packed(ox_dtype t, const ox_conv_desc* d, const void* X, const void* Wp,
                                  const void* bias, ox_act act, void* Y, void* stream);
 
+/* Scratch bytes that ox_conv2d_fused_ws may use for this geometry: the fp32
+ * partial tiles of a channel-split (split-K) plan, which the 1x1 and the
+ * LDS-patch 3x3 kernels choose when a layer has too few output tiles to
+ * occupy the chip (the deep, small-spatial layers of an image network).
+ * 0 when no split is planned.  Host only; honours OX_FORCE_KERNEL. */
+size_t ox_conv2d_workspace_bytes(ox_dtype t, const ox_conv_desc* d);
+
+/* ox_conv2d_fused (w_packed = 0, W in ONNX layout) or ox_conv2d_fused_packed
+ * (w_packed = 1, W packed by ox_conv2d_pack_weights) with a caller-owned
+ * scratch buffer, so that the kernels may split a tile's channel range into
+ * slices that write fp32 partials and a second pass adds them in slice order
+ * (the result does not depend on timing).  The library allocates nothing.
+ * workspace: DEVICE, 16-byte aligned, at least
+ * ox_conv2d_workspace_bytes(t, d) bytes (workspace_bytes says how many), or
+ * NULL for no split (then identical to the calls above).  Its contents on
+ * entry do not matter and are garbage afterwards; calls that share it must
+ * be ordered on one stream.  Errors as ox_conv2d_fused, plus
+ * OX_ERR_INVALID_ARG for a misaligned or too small workspace. */
+ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                             int w_packed, const void* bias, ox_act act, void* Y, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------- offline, host, untimed */
 
 /* Size in bytes of the packed weights of a convolution, or 0 when this

@@ -147,6 +147,26 @@ def test_variant_selection_sweep(ox, monkeypatch):
             assert ox.ox_conv2d_variant("bf16", 2, C, 7, 7, 512, 1, 1).startswith("pw/")
 
 
+def test_workspace_entry_point(ox):
+    # split-K scratch: sized by the library, brought by the caller; the
+    # checks run before anything is enqueued
+    L = raw(ox)
+    assert ox.ox_conv2d_workspace_bytes("bf16", 32, 2048, 7, 7, 512, 1, 1) > 0      # 52 tiles x 32 chunks
+    assert ox.ox_conv2d_workspace_bytes("bf16", 32, 512, 7, 7, 512, 3, 3, (1, 1), (1, 1, 1, 1)) > 0
+    assert ox.ox_conv2d_workspace_bytes("bf16", 32, 64, 56, 56, 256, 1, 1) == 0      # many tiles
+    assert ox.ox_conv2d_workspace_bytes("f32", 32, 2048, 7, 7, 512, 1, 1) == 0
+    d = ox.conv_desc(32, 2048, 7, 7, 512, 1, 1)
+    need = ox.ox_conv2d_workspace_bytes("bf16", 32, 2048, 7, 7, 512, 1, 1)
+    f = L.ox_conv2d_fused_ws
+    assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, 0, None, 0, FAKE, FAKE + 8, need, None) == 1
+    assert "16-byte aligned" in ox.ox_last_error()
+    assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, 0, None, 0, FAKE, FAKE, need - 16, None) == 1
+    assert "workspace_bytes" in ox.ox_last_error()
+    assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, 2, None, 0, FAKE, FAKE, need, None) == 1
+    assert "w_packed" in ox.ox_last_error()
+    assert f(ox.OX_I8, C.byref(d), FAKE, FAKE, 0, None, 0, FAKE, FAKE, need, None) == 3
+
+
 def test_gemm_argument_errors(ox):
     L = raw(ox)
     g = L.ox_gemm_fused

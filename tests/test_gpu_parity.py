@@ -171,11 +171,18 @@ def sweep(n, seed):
     return [c for c in sweep_cases(n, seed) if conv_case_ok(*c[:11])]
 
 
-def run_conv(ox, X, Wt, b, dtype, s, pads, d, g, act):
+def workspace_for(ox, dtype, N, Cin, H, W, M, kH, kW, s, pads, d, g):
+    """A device scratch buffer of the size ox_conv2d_fused_ws asks for (None if 0)."""
+    n = ox.ox_conv2d_workspace_bytes(dtype, N, Cin, H, W, M, kH, kW, s, pads, d, g)
+    return torch.empty(n, dtype=torch.uint8, device="cuda") if n else None
+
+
+def run_conv(ox, X, Wt, b, dtype, s, pads, d, g, act, ws=False):
     ho, wo = ox.conv_out_hw(X.shape[2], X.shape[3], Wt.shape[2], Wt.shape[3], s, pads, d)
     Y = nan_like((X.shape[0], Wt.shape[0], ho, wo), dtype)
+    wsb = workspace_for(ox, dtype, *X.shape, Wt.shape[0], Wt.shape[2], Wt.shape[3], s, pads, d, g) if ws else None
     ox.ox_conv2d_fused(dev(X, dtype), dev(Wt, dtype), None if b is None else dev(b, dtype),
-                       s, pads, d, g, act, Y=Y)
+                       s, pads, d, g, act, Y=Y, workspace=wsb)
     torch.cuda.synchronize()
     return Y
 
@@ -313,8 +320,9 @@ def test_pw_split_k(ox, splits, monkeypatch):
         Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
         b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
         say("pw split", splits, (N, Cin, H, W, M))
-        Y1 = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu6")
-        Y2 = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu6")
+        assert ox.ox_conv2d_workspace_bytes("bf16", N, Cin, H, W, M, 1, 1) > 0
+        Y1 = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu6", ws=True)
+        Y2 = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu6", ws=True)
         assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
         assert_close(host64(Y1), oracle.conv2d(X, Wt, b, act="relu6"), "bf16",
                      "pw split %d case %d" % (splits, ci))
@@ -373,10 +381,10 @@ def conv_layer_tensors(layer, cfg, li, dtype):
     return (synth.round_to(t["X"], dtype), synth.round_to(Wf, dtype), synth.round_to(bf, dtype))
 
 
-def check_layer(ox, layer, cfg, li, dtype, n_sample):
+def check_layer(ox, layer, cfg, li, dtype, n_sample, ws=False):
     X, Wt, b = conv_layer_tensors(layer, cfg, li, dtype)
     s = (layer.stride, layer.stride)
-    Y = run_conv(ox, X, Wt, b, dtype, s, layer.onnx_pads, (1, 1), layer.group, layer.act)
+    Y = run_conv(ox, X, Wt, b, dtype, s, layer.onnx_pads, (1, 1), layer.group, layer.act, ws=ws)
     assert not torch.isnan(Y).any().item(), layer.name
     got = host64(Y).ravel()
     if n_sample is None:
@@ -399,9 +407,10 @@ def test_c2_mobilenetv2_layers(ox, dtype, N):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [1, 32])
 def test_c3_resnet50_layers(ox, dtype, N):
+    # with a workspace, as the benchmark runs them (split-K where planned)
     for li, layer in enumerate(synth.resnet50_layers(N)):
         say("C3", N, dtype, layer.name, layer.key())
-        check_layer(ox, layer, 3, li, dtype, None if N == 1 else 4096)
+        check_layer(ox, layer, 3, li, dtype, None if N == 1 else 4096, ws=True)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -546,14 +555,16 @@ def bf16_bits(a64):
     return synth.f32_to_bf16_bits(a64.astype(np.float32))
 
 
-def run_conv_packed(ox, X, Wt, b, s, pads, d, act):
+def run_conv_packed(ox, X, Wt, b, s, pads, d, act, ws=False):
     N, Cin, H, W = X.shape
     M = Wt.shape[0]
     Wp = ox.ox_conv2d_pack_weights(bf16_bits(Wt), "bf16", N, Cin, H, W, s, pads, d)
     Wp_dev = torch.from_numpy(Wp.view(np.int16)).cuda().view(torch.bfloat16)
     ho, wo = ox.conv_out_hw(H, W, 3, 3, s, pads, d)
     Y = nan_like((N, M, ho, wo), "bf16")
-    ox.ox_conv2d_fused_packed(dev(X, "bf16"), Wp_dev, dev(b, "bf16"), s, pads, d, act=act, Y=Y, M=M)
+    wsb = workspace_for(ox, "bf16", N, Cin, H, W, M, 3, 3, s, pads, d, 1) if ws else None
+    ox.ox_conv2d_fused_packed(dev(X, "bf16"), Wp_dev, dev(b, "bf16"), s, pads, d, act=act, Y=Y, M=M,
+                              workspace=wsb)
     torch.cuda.synchronize()
     return Y
 
@@ -638,12 +649,28 @@ def test_patch_split_k(ox, cfg, monkeypatch):
             except ox.OxError:
                 continue
             say("patch split", cfg, "TR", tr, "IMB", imb, "S", splits, (N, Cin, H, W, M, s))
-            Y1 = run_conv(ox, X, Wt, b, "bf16", (s, s), pads, (1, 1), 1, "relu")
-            Y2 = run_conv_packed(ox, X, Wt, b, (s, s), pads, (1, 1), "relu")
+            assert ox.ox_conv2d_workspace_bytes("bf16", N, Cin, H, W, M, 3, 3, (s, s), pads) > 0
+            Y1 = run_conv(ox, X, Wt, b, "bf16", (s, s), pads, (1, 1), 1, "relu", ws=True)
+            Y2 = run_conv_packed(ox, X, Wt, b, (s, s), pads, (1, 1), "relu", ws=True)
             assert torch.equal(Y1.view(torch.int16), Y2.view(torch.int16))
             assert_close(host64(Y1), ref, "bf16", "split %s case %d tr %d" % (cfg, ci, tr))
             ran += 1
     assert ran >= 3
+
+
+@pytest.mark.parametrize("xcd", ["8:1", "4:2", "2:4", "1:8"])
+def test_patch_xcd_orders(ox, xcd, monkeypatch):
+    # every split of the tile grid into XCD rectangles covers each output once
+    monkeypatch.setenv("OX_PATCH_XCD", xcd)
+    r = np.random.default_rng(8080 + int(xcd[0]))
+    N, Cin, H, W, M = 16, 64, 8, 8, 512
+    X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+    Wt = synth.round_to(r.standard_normal((M, Cin, 3, 3)) / math.sqrt(9 * Cin), "bf16")
+    b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+    say("patch xcd", xcd)
+    Y = run_conv_packed(ox, X, Wt, b, (1, 1), (1, 1, 1, 1), (1, 1), "relu")
+    assert_close(host64(Y), oracle.conv2d(X, Wt, b, (1, 1), (1, 1, 1, 1), (1, 1), 1, "relu"), "bf16",
+                 "xcd %s" % xcd)
 
 
 @pytest.mark.parametrize("N", [1, 32])
@@ -654,7 +681,7 @@ def test_c3_resnet50_3x3_packed(ox, N):
         say("C3 packed", N, layer.name)
         X, Wt, b = conv_layer_tensors(layer, 3, li, "bf16")
         s = (layer.stride, layer.stride)
-        Y = run_conv_packed(ox, X, Wt, b, s, layer.onnx_pads, (1, 1), layer.act)
+        Y = run_conv_packed(ox, X, Wt, b, s, layer.onnx_pads, (1, 1), layer.act, ws=True)
         assert not torch.isnan(Y).any().item()
         got = host64(Y).ravel()
         idx = sample_indices(got.size, 4096 if N > 1 else got.size, li)
