@@ -136,6 +136,9 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* As = smem;
   char* Ps = smem + BM * kAROW;
+  // the tile's fp32 bias, beyond the operand and epilogue areas: fetched with
+  // the first chunk and written to LDS with it, so no wait lands early
+  float* Bs = (float*)(smem + pp.lds - BM * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -334,14 +337,10 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   for (int i = tid; i < pp.npos * (kCell / 16); i += kThreads)
     *(u32x4_t*)(Ps + i * 16) = u32x4_t{0u, 0u, 0u, 0u};
   const uint16_t* bias = (const uint16_t*)a.bias;
-  float bv[FC];
-#pragma unroll
-  for (int fc = 0; fc < FC; ++fc) {
-    const int ml = wm * FC * 32 + fc * 32 + l32;
-    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
-  }
+  const uint32_t braw = (tid < BM && bias && m0 + tid < M) ? (uint32_t)bias[m0 + tid] : 0u;
   for (int chunk = c_lo; chunk < c_hi; ++chunk) {
     __syncthreads();                 // the previous chunk's MFMAs are done with LDS
+    if (chunk == c_lo && tid < BM) Bs[tid] = __uint_as_float(braw << 16);
     store_chunk();
     __syncthreads();
     if (chunk + 1 < c_hi) load_chunk((chunk + 1) * 32);
@@ -401,6 +400,9 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   const int nslot = pp.NT * 32;
   const int erow = nslot + 8;            // elements per staged channel row
   uint16_t* E = (uint16_t*)smem;
+  float bv[FC];
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) bv[fc] = Bs[wm * FC * 32 + fc * 32 + l32];
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll

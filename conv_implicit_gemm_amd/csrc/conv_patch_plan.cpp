@@ -55,7 +55,8 @@ PatchPlan make(const ConvArgs& a, const Cfg& c, int TR, int IMB) {
   const int rows = std::min(a.H, p.PR);
   p.units = IMB * 4 * ((rows * a.W + 2 * p.VW - 2) / p.VW);
   p.lds = std::max(p.BM * (9 * 64 + 16) + p.npos * kCell,
-                   p.BM * (p.NT * 32 + 8) * 2);   // the epilogue reuses LDS as [channel][pixel]
+                   p.BM * (p.NT * 32 + 8) * 2)    // the epilogue reuses LDS as [channel][pixel]
+          + p.BM * 4;                             // + the tile's fp32 bias
   p.splits = 1;
   p.cps = std::max(1, a.C / 32);
   p.ws = nullptr;

@@ -39,8 +39,8 @@ namespace pw {
 // + (0..3).  The caller has synchronised the block: LDS is free.
 template <int WM, int WN, int FP, int FC>
 __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, char* smem,
-                                           const f32x16_t (&acc)[FP][FC], const float (&bv)[FC],
-                                           int q0, int m0) {
+                                           const float* Bs, const f32x16_t (&acc)[FP][FC], int q0,
+                                           int m0) {
   constexpr int BM = 32 * WM * FC, BN = 32 * WN * FP;
   constexpr int EROW = BN + 8;
   const int tid = threadIdx.x;
@@ -49,6 +49,9 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
   const int l32 = lane & 31, kg = lane >> 5;
   const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
   uint16_t* E = (uint16_t*)smem;
+  float bv[FC];
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) bv[fc] = Bs[wm * FC * 32 + fc * 32 + l32];
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
@@ -96,20 +99,6 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
   }
 }
 
-// This lane's bias values (channels 32*(wm*FC + fc) + l32 of the tile at m0),
-// loaded ahead of the epilogue that needs them.
-template <int WM, int WN, int FC>
-__device__ __forceinline__ void load_bias(const ConvArgs& a, int m0, float (&bv)[FC]) {
-  const int wave = threadIdx.x >> 6, l32 = threadIdx.x & 31;
-  const int wm = wave / WN;
-  const uint16_t* bias = (const uint16_t*)a.bias;
-#pragma unroll
-  for (int fc = 0; fc < FC; ++fc) {
-    const int m = m0 + wm * FC * 32 + fc * 32 + l32;
-    bv[fc] = (bias && m < a.M) ? bf16_to_f32(bias[m]) : 0.0f;
-  }
-}
-
 // Workspace layout of split-K partials: unit (tile, slice) owns
 // kThreads * FP*FC*4 float4 values, stored [float4 index][thread] so that
 // both the writer and the reducer access it fully coalesced.
@@ -135,6 +124,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* As = smem;                 // weights [BM][ROW]
   char* Xs = smem + BM * ROW;      // pixels  [BN][ROW]
+  // the tile's bias, fp32, beyond both the operand tiles and the epilogue's
+  // staging area: fetched with the tile's first chunk and written to LDS
+  // with it, so that the epilogue never waits on a global load
+  float* Bs = (float*)(smem + pl.lds - BM * 4);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -166,10 +159,14 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     c_hi = min(nchunks, c_lo + cps);
   };
 
-  // this thread's pixel staging units: element offset of the first value
-  // (-1: none) and LDS offset of its first row piece
+  // this thread's pixel staging units: element offset of the first value and
+  // LDS offset of its first row piece; units and weight pieces that fall
+  // outside the tensors load from offset 0 and store zeros (loads are never
+  // predicated: a register that a load may or may not write would force the
+  // wave to wait on every load in flight before reusing it)
   int x_goff[XUPT], x_lds[XUPT];
   int w_goff[WUPT], w_lds[WUPT];
+  uint32_t x_ok = 0, w_ok = 0;   // bit k: unit / piece k is inside the tensor
 #pragma unroll
   for (int k = 0; k < XUPT; ++k) {
     const int v = tid + k * kThreads;
@@ -182,24 +179,24 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   }
   auto tile_offsets = [&]() {
     const int q0 = pb * BN;
+    x_ok = w_ok = 0;
 #pragma unroll
     for (int k = 0; k < XUPT; ++k) {
       const int v = tid + k * kThreads;
-      x_goff[k] = -1;
-      if (v < XU) {
-        const int oct = v / NG, g = v - (v / NG) * NG;
-        const int q = q0 + g * P;
-        if (q < Q) {
-          const int n = q / HW;
-          x_goff[k] = (n * C + oct * 8) * HW + (q - n * HW);
-        }
-      }
+      const int oct = v / NG, g = v - (v / NG) * NG;
+      const int q = q0 + g * P;
+      const bool ok = v < XU && q < Q;
+      const int n = ok ? q / HW : 0;
+      x_goff[k] = ok ? (n * C + oct * 8) * HW + (q - n * HW) : 0;
+      x_ok |= (ok ? 1u : 0u) << k;
     }
 #pragma unroll
     for (int k = 0; k < WUPT; ++k) {
       const int v = tid + k * kThreads;
       const int m = v / WPR, j = v - (v / WPR) * WPR;
-      w_goff[k] = (v < WU && m0 + m < M) ? (m0 + m) * C + j * 8 : -1;
+      const bool ok = v < WU && m0 + m < M;
+      w_goff[k] = ok ? (m0 + m) * C + j * 8 : 0;
+      w_ok |= (ok ? 1u : 0u) << k;
     }
   };
 
@@ -211,45 +208,42 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   constexpr int XR = P == 4 ? 2 : 1;
   uint32_t xreg[XUPT][8][XR];
   u32x4_t wreg[WUPT];
+  uint32_t breg = 0;               // raw bias bits of channel m0 + tid (tid < BM)
+  bool b_ok = false;
+  const uint16_t* bias = (const uint16_t*)a.bias;
+  auto load_bias = [&]() {
+    const int m = m0 + (tid % BM);
+    b_ok = bias != nullptr && m < M;
+    breg = (b_ok ? bias : Wg)[b_ok ? m : 0];
+  };
 
   auto load_chunk = [&](int c0) {
 #pragma unroll
-    for (int k = 0; k < WUPT; ++k) {
-      if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU) {
-        if (w_goff[k] >= 0) wreg[k] = *(const u32x4_t*)(Wg + w_goff[k] + c0);
-        else wreg[k] = u32x4_t{0u, 0u, 0u, 0u};
-      }
-    }
+    for (int k = 0; k < WUPT; ++k) wreg[k] = *(const u32x4_t*)(Wg + w_goff[k] + c0);
 #pragma unroll
     for (int k = 0; k < XUPT; ++k) {
-      if (x_goff[k] >= 0) {
-        const uint16_t* src = Xg + x_goff[k] + c0 * HW;
+      const uint16_t* src = Xg + x_goff[k] + c0 * HW;
 #pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          if constexpr (P == 1) {
-            xreg[k][ch][0] = src[ch * HW];
-          } else if constexpr (P == 2) {
-            xreg[k][ch][0] = *(const uint32_t*)(src + ch * HW);
-          } else {
-            const u32x2_t v = *(const u32x2_t*)(src + ch * HW);
-            xreg[k][ch][0] = v[0];
-            xreg[k][ch][1] = v[1];
-          }
+      for (int ch = 0; ch < 8; ++ch) {
+        if constexpr (P == 1) {
+          xreg[k][ch][0] = src[ch * HW];
+        } else if constexpr (P == 2) {
+          xreg[k][ch][0] = *(const uint32_t*)(src + ch * HW);
+        } else {
+          const u32x2_t v = *(const u32x2_t*)(src + ch * HW);
+          xreg[k][ch][0] = v[0];
+          xreg[k][ch][1] = v[1];
         }
-      } else {
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch)
-#pragma unroll
-          for (int r = 0; r < XR; ++r) xreg[k][ch][r] = 0u;
       }
     }
   };
 
-  auto store_chunk = [&]() {
+  auto store_chunk = [&](bool with_bias) {
+    if (with_bias && tid < BM) Bs[tid] = b_ok ? __uint_as_float(breg << 16) : 0.0f;
 #pragma unroll
     for (int k = 0; k < WUPT; ++k)
       if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU)
-        *(u32x4_t*)(As + w_lds[k]) = wreg[k];
+        *(u32x4_t*)(As + w_lds[k]) = ((w_ok >> k) & 1) ? wreg[k] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < XUPT; ++k) {
       if (k * kThreads + kThreads <= XU || tid + k * kThreads < XU) {
@@ -257,9 +251,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         for (int e = 0; e < P; ++e) {
           // pixel e of the unit: bf16 number e of each channel's loaded P
           uint32_t d[4];
+          const bool ok = (x_ok >> k) & 1;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = xreg[k][2 * j][e >> 1], hi = xreg[k][2 * j + 1][e >> 1];
+            const uint32_t lo = ok ? xreg[k][2 * j][e >> 1] : 0u, hi = ok ? xreg[k][2 * j + 1][e >> 1] : 0u;
             if constexpr (P == 1) d[j] = (lo & 0xffffu) | (hi << 16);
             else if ((e & 1) == 0) d[j] = (lo & 0xffffu) | (hi << 16);
             else d[j] = (lo >> 16) | (hi & 0xffff0000u);
@@ -270,15 +265,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
   };
 
-  float bv[FC], next_bv[FC] = {};
   decode(u);
   tile_offsets();
   load_chunk(c_lo * KC);
-  if (S == 1) load_bias<WM, WN, FC>(a, m0, next_bv);
+  if (S == 1) load_bias();
   for (;;) {
     const int cur_pb = pb, cur_m0 = m0, cur_lo = c_lo, cur_hi = c_hi, cur_unit = unit_id;
-#pragma unroll
-    for (int fc = 0; fc < FC; ++fc) bv[fc] = next_bv[fc];
     const int next = u + (int)gridDim.x;
 #pragma unroll
     for (int i = 0; i < FP; ++i)
@@ -288,7 +280,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     for (int chunk = cur_lo; chunk < cur_hi; ++chunk) {
       __syncthreads();               // LDS is free: previous MFMAs and epilogue are done
-      store_chunk();
+      store_chunk(S == 1 && chunk == cur_lo);
       __syncthreads();
       if (chunk + 1 < cur_hi) {
         load_chunk((chunk + 1) * KC);
@@ -296,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         decode(next);
         tile_offsets();
         load_chunk(c_lo * KC);
-        if (S == 1) load_bias<WM, WN, FC>(a, m0, next_bv);
+        if (S == 1) load_bias();
       }
       u32x4_t pf[3][FP], wf[3][FC];
       auto read_frags = [&](int s, int buf) {
@@ -326,7 +318,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
     if (S == 1) {
       __syncthreads();               // every wave is done reading this tile's operands
-      store_tile<WM, WN, FP, FC>(a, pl, smem, acc, bv, cur_pb * BN, cur_m0);
+      store_tile<WM, WN, FP, FC>(a, pl, smem, Bs, acc, cur_pb * BN, cur_m0);
     } else {
       f32x4_t* dst = partial_base<FP, FC>(pl.ws, cur_unit) + tid;
 #pragma unroll

@@ -38,7 +38,7 @@ PwPlan make(const ConvArgs& a, int WM, int KC) {
   p.npb = (int)((Q + BN - 1) / BN);
   p.nmb = (a.M + BM - 1) / BM;
   const int row = KC * 2 + 16;
-  p.lds = std::max((BM + BN) * row, BM * (BN + 8) * 2);
+  p.lds = std::max((BM + BN) * row, BM * (BN + 8) * 2) + BM * 4;   // + the tile's fp32 bias
   // split-K when the tiles alone would leave many CUs idle and the channel
   // range is long: about 192 work units of at least four chunks (a sweep
   // of the ResNet-50 1x1 layers at batch 32: two slices for 98 tiles x 16
@@ -56,7 +56,8 @@ PwPlan make(const ConvArgs& a, int WM, int KC) {
   p.ws = nullptr;
   // persistent grid: as many blocks as fit the chip at once (LDS-bound, at
   // most kMaxPerCu per CU), a multiple of the XCD count when units are left over
-  const int per_cu = std::max(1, std::min(kMaxPerCu, kLdsMax / p.lds));
+  int per_cu = std::max(1, std::min(kMaxPerCu, kLdsMax / p.lds));
+  if (const char* e = getenv("OX_PW_PER_CU")) per_cu = std::max(1, std::min(kLdsMax / p.lds, atoi(e)));
   const int64_t units = tiles * p.splits;
   const int64_t cap = (int64_t)kCUs * per_cu;
   p.grid = (int)std::min(units, cap);

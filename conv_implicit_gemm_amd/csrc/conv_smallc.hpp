@@ -53,11 +53,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_bf16(const ConvArgs a
   const int ih_base = oh0 * S - a.pt;
 
   const uint16_t* bias = (const uint16_t*)a.bias;
-  float bv[2];
+  uint32_t braw[2];   // raw bits, converted in the epilogue (see the 3x3 kernel)
 #pragma unroll
   for (int fc = 0; fc < 2; ++fc) {
     const int ml = fc * 32 + l32;
-    bv[fc] = (bias && m0 + ml < M) ? bf16_to_f32(bias[m0 + ml]) : 0.0f;
+    braw[fc] = (bias && m0 + ml < M) ? (uint32_t)bias[m0 + ml] : 0u;
   }
 
   // zero the patch and the weight tile (padding taps and channels stay 0)
@@ -186,6 +186,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_bf16(const ConvArgs a
   const int nslot = WN * FP * 32;
   const int erow = nslot + 8;
   uint16_t* E = (uint16_t*)smem;
+  float bv[FC];
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) bv[fc] = __uint_as_float(braw[fc] << 16);
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
