@@ -56,6 +56,12 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
 }
 
+// n / f.d for 0 <= n < 2^31 (see make_fastdiv)
+__device__ __forceinline__ int fdiv(const FastDiv& f, int n) {
+  const uint64_t hi = __umulhi((uint32_t)n, f.mul);
+  return (int)((hi + (uint32_t)n) >> f.shr);
+}
+
 // One v_mfma_f32_32x32x16_bf16: c[32x32] += a[32x16] * b[16x32].  Lane l
 // supplies row (a) / column (b) l%32 with k = 8*(l/32) .. 8*(l/32)+7 as 8
 // bf16 in one 128-bit register quad; accumulator element i of lane l is

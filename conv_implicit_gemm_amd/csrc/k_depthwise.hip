@@ -39,6 +39,10 @@ struct DwPlan {
   int RIN;    // input rows staged per plane
   int WP;     // staged row width (input columns incl. left/right halo)
   int OWT;    // outputs per thread strip (4)
+  FastDiv fd_w;       // input row length W
+  FastDiv fd_plane;   // H*W: span of one input plane (blocks of several planes)
+  FastDiv fd_nstrip;  // output strips per row
+  FastDiv fd_pstrips; // strips per plane of a several-plane block (Ho * strips per row)
 };
 
 constexpr int kStrip = 4;
@@ -93,35 +97,68 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
     }
   }
 
-  // interior: rows [r_lo, r_hi) of each plane are one contiguous span of X
+  // interior: the block's input is one contiguous span of X -- rows [r_lo,
+  // r_hi) of one plane, or all rows of its np planes -- read as a flat array
+  // with 16-byte loads (an unaligned head and the tail element-wise) and
+  // scattered to (plane, row, column) of the LDS tile, every load of the
+  // block in flight at once.
   const int r_lo = max(0, -ih_start), r_hi = min(rin, H - ih_start);
   const int wcopy = min(W, pl.WP - a.pl);                  // input columns used
   if (r_hi > r_lo && wcopy > 0) {
     const T* X = (const T*)a.X;
     constexpr int EPC = 16 / sizeof(T);
-    const bool vec = (W % EPC == 0) && wcopy == W;
-    for (int pp = 0; pp < np; ++pp) {
-      const int64_t plane = pl0 + pp;
-      const T* src = X + (plane * H + (ih_start + r_lo)) * (int64_t)W;
-      A* dst = tile + (pp * pl.RIN + r_lo) * pl.WP + a.pl;
-      const int nrow = r_hi - r_lo;
-      if (vec && (((uintptr_t)src) & 15) == 0) {
-        const int vpr = W / EPC;                           // vectors per row
-        for (int v = threadIdx.x; v < nrow * vpr; v += kThreads) {
-          const int r = v / vpr, cc = (v - r * vpr) * EPC;
-          const u32x4_t raw = *(const u32x4_t*)(src + (int64_t)r * W + cc);
-          T e[EPC];
-          __builtin_memcpy(e, &raw, 16);
-          A* d = dst + r * pl.WP + cc;
+    const int nrow = r_hi - r_lo;
+    const T* src0 = X + ((int64_t)pl0 * H + (ih_start + r_lo)) * (int64_t)W;
+    A* dst0 = tile + r_lo * pl.WP + a.pl;
+    // np > 1 (whole images, TH == Ho): the span is all H rows of each plane,
+    // of which the first nrow are staged (a strided kernel may not reach the
+    // last rows); np == 1: the span is the nrow staged rows
+    const int span = np == 1 ? nrow * W : np * H * W;
+    // element f of the span -> LDS cell (or -1 when its row or column is not needed)
+    auto cell = [&](int f) {
+      int pp = 0, rem = f;
+      if (np > 1) {
+        pp = fdiv(pl.fd_plane, f);
+        rem = f - pp * H * W;
+      }
+      const int r = fdiv(pl.fd_w, rem);
+      const int cc = rem - r * W;
+      return (cc < wcopy && r < nrow) ? (pp * pl.RIN + r) * pl.WP + cc : -1;
+    };
+    const int head = min(span, (int)(((16 - (((uintptr_t)src0) & 15)) & 15) / sizeof(T)));
+    const int nvec = (span - head) / EPC;
+    for (int v = threadIdx.x; v < nvec; v += kThreads) {
+      const int f0 = head + v * EPC;
+      const u32x4_t raw = *(const u32x4_t*)(src0 + f0);
+      T e[EPC];
+      __builtin_memcpy(e, &raw, 16);
+      // walk (plane, row, column) from the first element
+      int pp = 0, rem = f0;
+      if (np > 1) {
+        pp = fdiv(pl.fd_plane, f0);
+        rem = f0 - pp * H * W;
+      }
+      int r = fdiv(pl.fd_w, rem);
+      int cc = rem - r * W;
 #pragma unroll
-          for (int j = 0; j < EPC; ++j) d[j] = widen<T, A>(e[j]);
-        }
-      } else {
-        for (int i = threadIdx.x; i < nrow * wcopy; i += kThreads) {
-          const int r = i / wcopy, cc = i - r * wcopy;
-          dst[r * pl.WP + cc] = widen<T, A>(src[(int64_t)r * W + cc]);
+      for (int j = 0; j < EPC; ++j) {
+        if (cc < wcopy && r < nrow) dst0[(pp * pl.RIN + r) * pl.WP + cc] = widen<T, A>(e[j]);
+        if (++cc == W) {
+          cc = 0;
+          if (++r == H) {            // next plane (np > 1 only: a one-plane span ends first)
+            r = 0;
+            ++pp;
+          }
         }
       }
+    }
+    for (int f = threadIdx.x; f < head; f += kThreads) {
+      const int d = cell(f);
+      if (d >= 0) dst0[d] = widen<T, A>(src0[f]);
+    }
+    for (int f = head + nvec * EPC + threadIdx.x; f < span; f += kThreads) {
+      const int d = cell(f);
+      if (d >= 0) dst0[d] = widen<T, A>(src0[f]);
     }
   }
   __syncthreads();
@@ -131,9 +168,9 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   const int per_plane = th * nstrip;
   const T* bias = (const T*)a.bias;
   for (int t = threadIdx.x; t < np * per_plane; t += kThreads) {
-    const int pp = t / per_plane;
+    const int pp = np > 1 ? fdiv(pl.fd_pstrips, t) : 0;   // (np > 1: th == Ho)
     const int rem = t - pp * per_plane;
-    const int r = rem / nstrip;
+    const int r = fdiv(pl.fd_nstrip, rem);
     const int ow0 = (rem - r * nstrip) * kStrip;
     const int64_t plane = pl0 + pp;
     const int c = (int)(plane % C);
@@ -205,6 +242,11 @@ int lds_bytes(const DwPlan& p, int KK) {
 
 DwPlan make_plan(const ConvArgs& a) {
   DwPlan p;
+  const int nstrip = (a.Wo + kStrip - 1) / kStrip;
+  p.fd_w = make_fastdiv((uint32_t)std::max(1, a.W));
+  p.fd_plane = make_fastdiv((uint32_t)std::max(1, a.H * a.W));
+  p.fd_nstrip = make_fastdiv((uint32_t)std::max(1, nstrip));
+  p.fd_pstrips = make_fastdiv((uint32_t)std::max(1, a.Ho * nstrip));
   p.OWT = kStrip;
   p.WP = (a.Wo - 1) * a.sw + (a.kW - 1) * a.dw + 1 + kStrip * a.sw;   // + strip overrun
   const int KK = a.kH * a.kW;

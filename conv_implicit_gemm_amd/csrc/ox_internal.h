@@ -90,6 +90,22 @@ struct ConvArgs {
   size_t ws_bytes;        // its size
 };
 
+// Division by a divisor fixed for a launch (0 <= n < 2^31, 1 <= d < 2^31):
+// q = (umulhi(n, mul) + n) >> shr with a 33-bit magic multiplier whose top
+// bit is implicit.  Set on the host, used in kernels where a runtime
+// division per element would cost more than the element's arithmetic.
+struct FastDiv {
+  uint32_t d, mul, shr;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+  FastDiv f;
+  f.d = d;
+  f.shr = 0;
+  while ((1ull << f.shr) < d) ++f.shr;
+  f.mul = (uint32_t)(((1ull << 32) * ((1ull << f.shr) - d)) / d + 1);
+  return f;
+}
+
 // Plan of the LDS-patch 3x3 kernel (host-chosen, passed to the kernel by
 // value): configuration, block band and patch geometry.
 struct PatchPlan {
