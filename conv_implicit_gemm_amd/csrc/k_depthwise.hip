@@ -16,6 +16,7 @@
 // dilation 1) are compiled with fixed loop bounds; any other geometry runs a
 // generic variant of the same scheme.
 #include <algorithm>
+#include <cstdlib>
 
 #include "engine.hpp"
 
@@ -252,7 +253,11 @@ DwPlan make_plan(const ConvArgs& a) {
   const int KK = a.kH * a.kW;
   const int per_plane = a.Ho * a.Wo;
   auto rin = [&](int th) { return (th - 1) * a.sh + (a.kH - 1) * a.dh + 1; };
-  const int target = 4096;       // outputs per block
+  // Outputs per block: sized so that a block stages about 4096 input pixels
+  // (2048 for planes under 512 pixels, where more blocks hide the latency
+  // better); a strided kernel reads sh*sw input pixels per output.
+  int target = (a.H * a.W >= 512 ? 4096 : 2048) / std::max(1, a.sh * a.sw);
+  if (const char* e = getenv("OX_DW_TARGET")) target = std::max(64, std::min(65536, atoi(e)));  // tuning override
   if (per_plane >= target / 2) {
     p.P = 1;
     p.TH = std::max(1, std::min(a.Ho, target / std::max(1, a.Wo)));
