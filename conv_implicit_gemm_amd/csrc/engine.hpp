@@ -57,8 +57,9 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
 }
 
 // n / f.d for 0 <= n < 2^31 (see make_fastdiv)
+// (umulhi(n, mul) < n, so the sum stays below 2n < 2^32: 32-bit arithmetic)
 __device__ __forceinline__ int fdiv(const FastDiv& f, int n) {
-  const uint64_t hi = __umulhi((uint32_t)n, f.mul);
+  const uint32_t hi = __umulhi((uint32_t)n, f.mul);
   return (int)((hi + (uint32_t)n) >> f.shr);
 }
 

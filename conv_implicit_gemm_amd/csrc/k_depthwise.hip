@@ -24,15 +24,20 @@ namespace ox {
 
 namespace {
 
+// T: element in HBM; A: accumulator; L: element of the LDS tile (widened
+// once, as it is staged, so the inner loop reads ready operands)
 template <int DT> struct Dw;
-template <> struct Dw<DT_F32> { typedef float T; typedef float A; };
-template <> struct Dw<DT_BF16> { typedef uint16_t T; typedef float A; };
-template <> struct Dw<DT_I8> { typedef int8_t T; typedef int A; };
+template <> struct Dw<DT_F32> { typedef float T; typedef float A; typedef float L; };
+template <> struct Dw<DT_BF16> { typedef uint16_t T; typedef float A; typedef float L; };
+template <> struct Dw<DT_I8> { typedef int8_t T; typedef int A; typedef int L; };
+constexpr int lds_elem_size(int) { return 4; }
 
 template <typename T, typename A> __device__ __forceinline__ A widen(T v);
 template <> __device__ __forceinline__ float widen<float, float>(float v) { return v; }
 template <> __device__ __forceinline__ float widen<uint16_t, float>(uint16_t v) { return bf16_to_f32(v); }
 template <> __device__ __forceinline__ int widen<int8_t, int>(int8_t v) { return (int)v; }
+template <> __device__ __forceinline__ uint16_t widen<uint16_t, uint16_t>(uint16_t v) { return v; }
+template <> __device__ __forceinline__ int widen<int, int>(int v) { return v; }
 
 struct DwPlan {
   int TH;     // output rows per block
@@ -46,16 +51,26 @@ struct DwPlan {
   FastDiv fd_pstrips; // strips per plane of a several-plane block (Ho * strips per row)
 };
 
-constexpr int kStrip = 4;
+// 16-byte loads per thread issued at once in the staging phase (about 96, 64
+// and 48 bytes); a plan sizes its blocks to stay within them.
+template <int DT> struct DwLoads;
+template <> struct DwLoads<DT_F32> { static constexpr int V = 6; };
+template <> struct DwLoads<DT_BF16> { static constexpr int V = 4; };
+template <> struct DwLoads<DT_I8> { static constexpr int V = 3; };
+
+constexpr int kStrip = 4;   // the vector stores below write exactly 4 outputs
 
 template <int DT, int KH, int KW, int S>
 __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const DwPlan pl) {
   typedef typename Dw<DT>::T T;
   typedef typename Dw<DT>::A A;
   extern __shared__ __attribute__((aligned(16))) char dw_smem[];
-  A* tile = (A*)dw_smem;                                   // [P][RIN][WP] (+ slack)
-  const int tile_elems = pl.P * pl.RIN * pl.WP + 64;
-  A* wts = tile + tile_elems;                              // [P][kH*kW]
+  typedef typename Dw<DT>::L L;
+  L* tile = (L*)dw_smem;                                   // [P][RIN][WP] (+ slack)
+  const int tile_bytes = ((pl.P * pl.RIN * pl.WP + 64) * (int)sizeof(L) + 15) & ~15;
+  A* wts = (A*)(dw_smem + tile_bytes);                     // [P][kH*kW]
+  A* pbias = wts + pl.P * (KH ? KH * KW : a.kH * a.kW);    // [P] per-plane bias (fp32 / int32)
+  double* pmult = (double*)(((uintptr_t)(pbias + pl.P) + 7) & ~(uintptr_t)7);  // [P] int8 multipliers
 
   const int kH = KH ? KH : a.kH, kW = KW ? KW : a.kW;
   const int sh = S ? S : a.sh, sw = S ? S : a.sw;
@@ -71,25 +86,71 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   const int rin = (th - 1) * sh + (kH - 1) * dh + 1;       // rows this block needs
 
   I8View q;
-  A padv = (A)0;
+  L padv = (L)0;
   if constexpr (DT == DT_I8) {
     q.init(a.i8);
-    padv = (A)q.xzp;
+    padv = (L)q.xzp;
   }
 
-  // weights of the block's channels
+  // Every global load of the staging phase is issued before the first wait:
+  // the interior as 16-byte vectors into registers (at most kLoads per
+  // thread; a plan keeps the span within that, and a loop after the first
+  // wave of loads takes any remainder), the span's unaligned head and tail
+  // elements, and up to two weights per thread.  The halo is filled while the
+  // loads are in flight, then everything is written to LDS.
+  const int r_lo = max(0, -ih_start), r_hi = min(rin, H - ih_start);
+  const bool any = r_hi > r_lo;
+  const int nrow = any ? r_hi - r_lo : 0;
+  const T* src0 = (const T*)a.X + ((int64_t)pl0 * H + (ih_start + r_lo)) * (int64_t)W;
+  L* dst0 = tile + r_lo * pl.WP + a.pl;
+  constexpr int EPC = 16 / sizeof(T);
+  constexpr int NV = DwLoads<DT>::V;
+  // the block's input is one contiguous span of X: rows [r_lo, r_hi) of one
+  // plane, or all H rows of each of its np planes (whole images, TH == Ho),
+  // of which the first nrow are staged (a strided kernel may not reach the
+  // last rows)
+  const int span = !any ? 0 : (np == 1 ? nrow * W : np * H * W);
+  const int head = min(span, (int)(((16 - (((uintptr_t)src0) & 15)) & 15) / sizeof(T)));
+  const int nvec = (span - head) / EPC;
+  const int tail0 = head + nvec * EPC;
+  const int tid = threadIdx.x;
   const T* Wt = (const T*)a.Wt;
-  for (int i = threadIdx.x; i < np * KK; i += kThreads) {
+  const int nw = np * KK;
+  auto widx = [&](int i) {                                 // weight i of the block -> index in Wt
     const int pp = i / KK;
-    const int c = (pl0 + pp) % C;
-    wts[i] = widen<T, A>(Wt[c * KK + (i - pp * KK)]);
+    return ((pl0 + pp) % C) * KK + (i - pp * KK);
+  };
+  const int wi0 = widx(min(tid, nw - 1)), wi1 = widx(min(tid + kThreads, nw - 1));
+  const int cb = (pl0 + min(tid, np - 1)) % C;             // channel of this thread's plane value
+  // (every thread issues all NV vector loads, lanes past the end re-reading
+  // the last vector, so that no load is predicated)
+  const int ntail = span - tail0;
+  u32x4_t buf[NV];
+  if (nvec > 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      buf[i] = *(const u32x4_t*)(src0 + head + min(tid + i * kThreads, nvec - 1) * EPC);
+  }
+  // head and tail elements (a block with an empty span reads a weight instead)
+  const T he = span > 0 ? src0[min(tid, span - 1)] : Wt[wi0];
+  const T te = span > 0 ? src0[min(tail0 + tid, span - 1)] : Wt[wi0];
+  const T w0 = Wt[wi0], w1 = Wt[wi1];
+  // the bias of plane tid (and its int8 multiplier)
+  A b0 = (A)0;
+  double m0 = 0.0;
+  const T* bias = (const T*)a.bias;
+  if constexpr (DT == DT_I8) {
+    b0 = q.bias[cb];
+    m0 = q.mult[cb];
+  } else {
+    if (bias) b0 = widen<T, A>(bias[cb]);
   }
 
   // halo cells: rows outside the image, and columns left/right of it
-  for (int i = threadIdx.x; i < np * rin; i += kThreads) {
+  for (int i = tid; i < np * rin; i += kThreads) {
     const int pp = i / rin, r = i - (i / rin) * rin;
     const int ih = ih_start + r;
-    A* row = tile + (pp * pl.RIN + r) * pl.WP;
+    L* row = tile + (pp * pl.RIN + r) * pl.WP;
     if ((unsigned)ih >= (unsigned)H) {
       for (int j = 0; j < pl.WP; ++j) row[j] = padv;
     } else {
@@ -98,87 +159,97 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
     }
   }
 
-  // interior: the block's input is one contiguous span of X -- rows [r_lo,
-  // r_hi) of one plane, or all rows of its np planes -- read as a flat array
-  // with 16-byte loads (an unaligned head and the tail element-wise) and
-  // scattered to (plane, row, column) of the LDS tile, every load of the
-  // block in flight at once.
-  const int r_lo = max(0, -ih_start), r_hi = min(rin, H - ih_start);
-  const int wcopy = min(W, pl.WP - a.pl);                  // input columns used
-  if (r_hi > r_lo && wcopy > 0) {
-    const T* X = (const T*)a.X;
-    constexpr int EPC = 16 / sizeof(T);
-    const int nrow = r_hi - r_lo;
-    const T* src0 = X + ((int64_t)pl0 * H + (ih_start + r_lo)) * (int64_t)W;
-    A* dst0 = tile + r_lo * pl.WP + a.pl;
-    // np > 1 (whole images, TH == Ho): the span is all H rows of each plane,
-    // of which the first nrow are staged (a strided kernel may not reach the
-    // last rows); np == 1: the span is the nrow staged rows
-    const int span = np == 1 ? nrow * W : np * H * W;
-    // element f of the span -> LDS cell (or -1 when its row or column is not needed)
-    auto cell = [&](int f) {
-      int pp = 0, rem = f;
-      if (np > 1) {
-        pp = fdiv(pl.fd_plane, f);
-        rem = f - pp * H * W;
+  if (tid < nw) wts[tid] = widen<T, A>(w0);
+  if (tid + kThreads < nw) wts[tid + kThreads] = widen<T, A>(w1);
+  for (int i = tid + 2 * kThreads; i < nw; i += kThreads) wts[i] = widen<T, A>(Wt[widx(i)]);
+  auto plane_vals = [&](int i, A bv, double mv) {
+    pbias[i] = bv;
+    if constexpr (DT == DT_I8) pmult[i] = mv;
+  };
+  if (tid < np) plane_vals(tid, b0, m0);
+  for (int i = tid + kThreads; i < np; i += kThreads) {
+    const int c = (pl0 + i) % C;
+    if constexpr (DT == DT_I8) plane_vals(i, q.bias[c], q.mult[c]);
+    else plane_vals(i, bias ? widen<T, A>(bias[c]) : (A)0, 0.0);
+  }
+
+  // element f of the span -> LDS cell (or -1 when its row or column is not needed)
+  auto cell = [&](int f) {
+    int pp = 0, rem = f;
+    if (np > 1) {
+      pp = fdiv(pl.fd_plane, f);
+      rem = f - pp * H * W;
+    }
+    const int r = fdiv(pl.fd_w, rem);
+    const int cc = rem - r * W;
+    return (pp * pl.RIN + r) * pl.WP + cc;
+  };
+  // the EPC elements of vector v.  Every element of the span has a cell (the
+  // plan makes rows at least pl + W wide and, for several-plane blocks, keeps
+  // all H rows of each plane), so nothing is predicated: a vector that stays
+  // in one row goes to consecutive cells; one that reaches the end of its row
+  // (W >= EPC: at most once) continues at column 0 of the next row, which may
+  // be the first row of the next plane; narrower rows walk element by element.
+  auto scatter = [&](int v, const u32x4_t& raw) {
+    const int f0 = head + v * EPC;
+    T e[EPC];
+    __builtin_memcpy(e, &raw, 16);
+    int pp = 0, rem = f0;
+    if (np > 1) {
+      pp = fdiv(pl.fd_plane, f0);
+      rem = f0 - pp * H * W;
+    }
+    int r = fdiv(pl.fd_w, rem);
+    int cc = rem - r * W;
+    L* d = dst0 + (pp * pl.RIN + r) * pl.WP + cc;
+    if (W >= EPC) {
+      const int k = W - cc;                                // cells left in this row
+      if (k >= EPC) {
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) d[j] = widen<T, L>(e[j]);
+      } else {
+        const int gap = (pl.WP - W) + (r + 1 == H ? (pl.RIN - H) * pl.WP : 0);
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) d[j + (j >= k ? gap : 0)] = widen<T, L>(e[j]);
       }
-      const int r = fdiv(pl.fd_w, rem);
-      const int cc = rem - r * W;
-      return (cc < wcopy && r < nrow) ? (pp * pl.RIN + r) * pl.WP + cc : -1;
-    };
-    const int head = min(span, (int)(((16 - (((uintptr_t)src0) & 15)) & 15) / sizeof(T)));
-    const int nvec = (span - head) / EPC;
-    for (int v = threadIdx.x; v < nvec; v += kThreads) {
-      const int f0 = head + v * EPC;
-      const u32x4_t raw = *(const u32x4_t*)(src0 + f0);
-      T e[EPC];
-      __builtin_memcpy(e, &raw, 16);
-      // walk (plane, row, column) from the first element
-      int pp = 0, rem = f0;
-      if (np > 1) {
-        pp = fdiv(pl.fd_plane, f0);
-        rem = f0 - pp * H * W;
-      }
-      int r = fdiv(pl.fd_w, rem);
-      int cc = rem - r * W;
+    } else {
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
-        if (cc < wcopy && r < nrow) dst0[(pp * pl.RIN + r) * pl.WP + cc] = widen<T, A>(e[j]);
+        dst0[(pp * pl.RIN + r) * pl.WP + cc] = widen<T, L>(e[j]);
         if (++cc == W) {
           cc = 0;
-          if (++r == H) {            // next plane (np > 1 only: a one-plane span ends first)
+          if (++r == H) {          // next plane (np > 1 only: a one-plane span ends first)
             r = 0;
             ++pp;
           }
         }
       }
     }
-    for (int f = threadIdx.x; f < head; f += kThreads) {
-      const int d = cell(f);
-      if (d >= 0) dst0[d] = widen<T, A>(src0[f]);
-    }
-    for (int f = head + nvec * EPC + threadIdx.x; f < span; f += kThreads) {
-      const int d = cell(f);
-      if (d >= 0) dst0[d] = widen<T, A>(src0[f]);
-    }
+  };
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = tid + i * kThreads;
+    if (v < nvec) scatter(v, buf[i]);
   }
+  for (int v = tid + NV * kThreads; v < nvec; v += kThreads)
+    scatter(v, *(const u32x4_t*)(src0 + head + v * EPC));
+  if (tid < head) dst0[cell(tid)] = widen<T, L>(he);
+  if (tid < ntail) dst0[cell(tail0 + tid)] = widen<T, L>(te);
   __syncthreads();
 
   // compute: strips of kStrip outputs along a row
   const int nstrip = (Wo + kStrip - 1) / kStrip;
   const int per_plane = th * nstrip;
-  const T* bias = (const T*)a.bias;
   for (int t = threadIdx.x; t < np * per_plane; t += kThreads) {
     const int pp = np > 1 ? fdiv(pl.fd_pstrips, t) : 0;   // (np > 1: th == Ho)
     const int rem = t - pp * per_plane;
     const int r = fdiv(pl.fd_nstrip, rem);
     const int ow0 = (rem - r * nstrip) * kStrip;
     const int64_t plane = pl0 + pp;
-    const int c = (int)(plane % C);
     const A* wk = wts + pp * KK;
     A acc[kStrip];
     A init = (A)0;
-    if constexpr (DT == DT_I8) init = q.bias[c];
+    if constexpr (DT == DT_I8) init = pbias[pp];
 #pragma unroll
     for (int o = 0; o < kStrip; ++o) acc[o] = init;
 
@@ -186,10 +257,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
       constexpr int WIN = (kStrip - 1) * S + KW;
 #pragma unroll
       for (int kh = 0; kh < KH; ++kh) {
-        const A* rp = tile + (pp * pl.RIN + r * S + kh) * pl.WP + ow0 * S;
+        const L* rp = tile + (pp * pl.RIN + r * S + kh) * pl.WP + ow0 * S;
         A win[WIN];
 #pragma unroll
-        for (int j = 0; j < WIN; ++j) win[j] = rp[j];
+        for (int j = 0; j < WIN; ++j) win[j] = widen<L, A>(rp[j]);
 #pragma unroll
         for (int kw = 0; kw < KW; ++kw) {
           const A wv = wk[kh * KW + kw];
@@ -199,35 +270,70 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
       }
     } else {
       for (int kh = 0; kh < kH; ++kh) {
-        const A* rp = tile + (pp * pl.RIN + r * sh + kh * dh) * pl.WP + ow0 * sw;
+        const L* rp = tile + (pp * pl.RIN + r * sh + kh * dh) * pl.WP + ow0 * sw;
         for (int kw = 0; kw < kW; ++kw) {
           const A wv = wk[kh * kW + kw];
 #pragma unroll
-          for (int o = 0; o < kStrip; ++o) acc[o] += rp[o * sw + kw * dw] * wv;
+          for (int o = 0; o < kStrip; ++o) acc[o] += widen<L, A>(rp[o * sw + kw * dw]) * wv;
         }
       }
     }
 
+    // a full strip whose first output is aligned is written with one 4x-wide
+    // store (whole cache lines per wave instead of partial lines)
     const int oh = oh0 + r;
     const int64_t ybase = (plane * Ho + oh) * (int64_t)Wo + ow0;
+    const bool full = ow0 + kStrip <= Wo;
     if constexpr (DT == DT_I8) {
+      if (a.out_dt == DT_I32) {
+        int32_t* yp = (int32_t*)a.Y + ybase;
+        if (full && ((uintptr_t)yp & 15) == 0) {
+          *(i32x4_t*)yp = i32x4_t{acc[0], acc[1], acc[2], acc[3]};
+        } else {
 #pragma unroll
-      for (int o = 0; o < kStrip; ++o) {
-        if (ow0 + o < Wo) {
-          if (a.out_dt == DT_I32) ((int32_t*)a.Y)[ybase + o] = acc[o];
-          else ((int8_t*)a.Y)[ybase + o] = requant(acc[o], q.mult[c], q.yzp);
+          for (int o = 0; o < kStrip; ++o)
+            if (ow0 + o < Wo) yp[o] = acc[o];
+        }
+      } else {
+        int8_t* yp = (int8_t*)a.Y + ybase;
+        int8_t v[kStrip];
+        const double mv = pmult[pp];
+#pragma unroll
+        for (int o = 0; o < kStrip; ++o) v[o] = requant(acc[o], mv, q.yzp);
+        if (full && ((uintptr_t)yp & 3) == 0) {
+          uint32_t w;
+          __builtin_memcpy(&w, v, 4);
+          *(uint32_t*)yp = w;
+        } else {
+#pragma unroll
+          for (int o = 0; o < kStrip; ++o)
+            if (ow0 + o < Wo) yp[o] = v[o];
         }
       }
     } else {
-      const float bv = bias ? to_f32(bias[c]) : 0.0f;
+      const float bv = pbias[pp];
       with_act(a.act, [&](auto act_k) {
         constexpr int ACT = decltype(act_k)::value;
+        float v[kStrip];
 #pragma unroll
-        for (int o = 0; o < kStrip; ++o) {
-          if (ow0 + o < Wo) {
-            const float v = act_c<ACT>(acc[o] + bv);
-            if constexpr (DT == DT_BF16) ((uint16_t*)a.Y)[ybase + o] = f32_to_bf16(v);
-            else ((float*)a.Y)[ybase + o] = v;
+        for (int o = 0; o < kStrip; ++o) v[o] = act_c<ACT>(acc[o] + bv);
+        if constexpr (DT == DT_BF16) {
+          uint16_t* yp = (uint16_t*)a.Y + ybase;
+          if (full && ((uintptr_t)yp & 7) == 0) {
+            *(u32x2_t*)yp = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else {
+#pragma unroll
+            for (int o = 0; o < kStrip; ++o)
+              if (ow0 + o < Wo) yp[o] = f32_to_bf16(v[o]);
+          }
+        } else {
+          float* yp = (float*)a.Y + ybase;
+          if (full && ((uintptr_t)yp & 15) == 0) {
+            *(f32x4_t*)yp = f32x4_t{v[0], v[1], v[2], v[3]};
+          } else {
+#pragma unroll
+            for (int o = 0; o < kStrip; ++o)
+              if (ow0 + o < Wo) yp[o] = v[o];
           }
         }
       });
@@ -237,8 +343,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
 
 constexpr int kLdsCap = 64 * 1024;
 
-int lds_bytes(const DwPlan& p, int KK) {
-  return (p.P * p.RIN * p.WP + 64 + p.P * KK) * 4;
+// the tile (elements of lsize bytes, 16-byte rounded), the fp32/int32
+// weights, the per-plane bias and (int8) the per-plane fp64 multipliers
+int lds_bytes(const DwPlan& p, int KK, int lsize) {
+  return (((p.P * p.RIN * p.WP + 64) * lsize + 15) & ~15) + p.P * KK * 4 + p.P * 4 + 8 + p.P * 8;
 }
 
 DwPlan make_plan(const ConvArgs& a) {
@@ -249,28 +357,43 @@ DwPlan make_plan(const ConvArgs& a) {
   p.fd_nstrip = make_fastdiv((uint32_t)std::max(1, nstrip));
   p.fd_pstrips = make_fastdiv((uint32_t)std::max(1, a.Ho * nstrip));
   p.OWT = kStrip;
-  p.WP = (a.Wo - 1) * a.sw + (a.kW - 1) * a.dw + 1 + kStrip * a.sw;   // + strip overrun
+  // staged row: left halo, every input column (a strided kernel may not read
+  // the last ones, but the staging copies whole rows), right halo and the
+  // overrun of the last strip
+  p.WP = std::max((a.Wo - 1) * a.sw + (a.kW - 1) * a.dw + 1 + kStrip * a.sw, a.pl + a.W);
   const int KK = a.kH * a.kW;
   const int per_plane = a.Ho * a.Wo;
   auto rin = [&](int th) { return (th - 1) * a.sh + (a.kH - 1) * a.dh + 1; };
-  // Outputs per block: sized so that a block stages about 4096 input pixels
-  // (2048 for planes under 512 pixels, where more blocks hide the latency
-  // better); a strided kernel reads sh*sw input pixels per output.
-  int target = (a.H * a.W >= 512 ? 4096 : 2048) / std::max(1, a.sh * a.sw);
+  // Outputs per block: sized so that a block stages about 16 KB of LDS tile
+  // (4096 fp32 or 8192 raw bf16 input pixels; half that for planes under 512
+  // pixels, where more blocks hide the latency better); a strided kernel
+  // reads sh*sw input pixels per output.  The bytes one block has in flight
+  // while it stages are what bound the kernel's bandwidth.
+  const int lsize = lds_elem_size(a.dt);
+  int target = (a.H * a.W >= 512 ? 4096 : 2048) * (4 / lsize) / std::max(1, a.sh * a.sw);
   if (const char* e = getenv("OX_DW_TARGET")) target = std::max(64, std::min(65536, atoi(e)));  // tuning override
+  // input elements the staging phase's first wave of loads covers
+  const int esize = a.dt == DT_F32 ? 4 : a.dt == DT_BF16 ? 2 : 1;
+  const int64_t cap = (int64_t)(a.dt == DT_F32 ? DwLoads<DT_F32>::V
+                                : a.dt == DT_BF16 ? DwLoads<DT_BF16>::V : DwLoads<DT_I8>::V) *
+                      kThreads * (16 / esize);
   if (per_plane >= target / 2) {
     p.P = 1;
     p.TH = std::max(1, std::min(a.Ho, target / std::max(1, a.Wo)));
     p.RIN = rin(p.TH);
-    while (p.TH > 1 && lds_bytes(p, KK) > kLdsCap) {
+    while (p.TH > 1 && (lds_bytes(p, KK, lsize) > kLdsCap || (int64_t)p.RIN * a.W > cap)) {
       --p.TH;
       p.RIN = rin(p.TH);
     }
+    // equal bands: the fewest bands of at most TH rows, with their rows spread evenly
+    const int nb = (a.Ho + p.TH - 1) / p.TH;
+    p.TH = (a.Ho + nb - 1) / nb;
+    p.RIN = rin(p.TH);
   } else {
     p.TH = a.Ho;
-    p.RIN = rin(p.TH);
+    p.RIN = std::max(rin(p.TH), a.pt + a.H);               // whole planes are staged
     p.P = std::max(1, target / per_plane);
-    while (p.P > 1 && lds_bytes(p, KK) > kLdsCap) --p.P;
+    while (p.P > 1 && (lds_bytes(p, KK, lsize) > kLdsCap || (int64_t)p.P * a.H * a.W > cap)) --p.P;
   }
   return p;
 }
@@ -279,7 +402,7 @@ template <int DT>
 int launch_dt(const ConvArgs& a, hipStream_t s) {
   const DwPlan p = make_plan(a);
   const int KK = a.kH * a.kW;
-  const int bytes = lds_bytes(p, KK);
+  const int bytes = lds_bytes(p, KK, lds_elem_size(DT));
   if (bytes > kLdsCap) return (int)hipErrorInvalidConfiguration;
   const int64_t nplanes = (int64_t)a.N * a.C;
   dim3 grid((unsigned)((nplanes + p.P - 1) / p.P), (a.Ho + p.TH - 1) / p.TH, 1);
@@ -299,7 +422,7 @@ int launch_dt(const ConvArgs& a, hipStream_t s) {
 
 bool depthwise_fits(const ConvArgs& a) {
   const DwPlan p = make_plan(a);
-  return lds_bytes(p, a.kH * a.kW) <= kLdsCap && (a.Ho + p.TH - 1) / p.TH <= 65535;
+  return lds_bytes(p, a.kH * a.kW, lds_elem_size(a.dt)) <= kLdsCap && (a.Ho + p.TH - 1) / p.TH <= 65535;
 }
 
 int launch_conv_depthwise(const ConvArgs& a, void* stream) {

@@ -237,6 +237,29 @@ def test_depthwise_variants(ox, force, dtype, geom, monkeypatch):
     assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, pads, d, Cc, "relu6"), dtype, "dw")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("geom", [
+    (2, 20, 14, 14, (1, 1), 1),     # Wo = 14: rows alternate between aligned and unaligned strips
+    (3, 12, 7, 7, (1, 1), 0),       # Wo = 7: one full strip and a tail per row
+    (2, 16, 28, 28, (2, 2), 3),     # output pointer 3 elements past an aligned one
+    (1, 8, 9, 16, (1, 1), 2),
+])
+def test_depthwise_output_alignment(ox, dtype, geom):
+    # strips of 4 outputs go out as one wide store only where they are full
+    # and aligned; every other strip element by element
+    N, Cc, H, W, s, yoff = geom
+    say("depthwise alignment", geom, dtype)
+    r = np.random.default_rng(H * 31 + yoff)
+    X = synth.round_to(r.standard_normal((N, Cc, H, W)), dtype)
+    Wt = synth.round_to(r.standard_normal((Cc, 1, 3, 3)) / 3.0, dtype)
+    b = synth.round_to(r.uniform(-0.5, 0.5, Cc), dtype)
+    ho, wo = ox.conv_out_hw(H, W, 3, 3, s, (1, 1, 1, 1), (1, 1))
+    Y = misaligned(nan_like((N, Cc, ho, wo), dtype), yoff)
+    ox.ox_conv2d_fused(dev(X, dtype), dev(Wt, dtype), dev(b, dtype), s, (1, 1, 1, 1), (1, 1), Cc, "relu6", Y=Y)
+    torch.cuda.synchronize()
+    assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, (1, 1, 1, 1), (1, 1), Cc, "relu6"), dtype, "dw align")
+
+
 @pytest.mark.parametrize("force", [None, "1x1", "igemm"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_pointwise_variants(ox, force, dtype, monkeypatch):
