@@ -167,7 +167,7 @@ __device__ __forceinline__ float apply_act(int act, float v) {
 template <int ACT>
 __device__ __forceinline__ float act_c(float v) {
   if constexpr (ACT == ACT_RELU) return fmaxf(v, 0.0f);
-  else if constexpr (ACT == ACT_RELU6) return fminf(fmaxf(v, 0.0f), 6.0f);
+  else if constexpr (ACT == ACT_RELU6) return __builtin_amdgcn_fmed3f(v, 0.0f, 6.0f);  // one v_med3_f32
   else if constexpr (ACT == ACT_GELU) return 0.5f * v * (1.0f + erff(v * 0.70710678118654752f));
   else return v;
 }

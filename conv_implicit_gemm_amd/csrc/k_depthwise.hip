@@ -17,6 +17,7 @@
 // generic variant of the same scheme.
 #include <algorithm>
 #include <cstdlib>
+#include <type_traits>
 
 #include "engine.hpp"
 
@@ -24,13 +25,12 @@ namespace ox {
 
 namespace {
 
-// T: element in HBM; A: accumulator; L: element of the LDS tile (widened
-// once, as it is staged, so the inner loop reads ready operands)
+// T: element in HBM; A: accumulator; L: element of the LDS tile, four bytes
+// (widened once, as it is staged, so the inner loop reads ready operands)
 template <int DT> struct Dw;
 template <> struct Dw<DT_F32> { typedef float T; typedef float A; typedef float L; };
 template <> struct Dw<DT_BF16> { typedef uint16_t T; typedef float A; typedef float L; };
 template <> struct Dw<DT_I8> { typedef int8_t T; typedef int A; typedef int L; };
-constexpr int lds_elem_size(int) { return 4; }
 
 template <typename T, typename A> __device__ __forceinline__ A widen(T v);
 template <> __device__ __forceinline__ float widen<float, float>(float v) { return v; }
@@ -48,7 +48,9 @@ struct DwPlan {
   FastDiv fd_w;       // input row length W
   FastDiv fd_plane;   // H*W: span of one input plane (blocks of several planes)
   FastDiv fd_nstrip;  // output strips per row
-  FastDiv fd_pstrips; // strips per plane of a several-plane block (Ho * strips per row)
+  FastDiv fd_ho;      // output rows Ho (rows of a several-plane block, plane-major)
+  FastDiv fd_c;       // channels C (plane -> channel)
+  FastDiv fd_kk;      // taps kH*kW
 };
 
 // 16-byte loads per thread issued at once in the staging phase (about 96, 64
@@ -58,10 +60,14 @@ template <> struct DwLoads<DT_F32> { static constexpr int V = 6; };
 template <> struct DwLoads<DT_BF16> { static constexpr int V = 4; };
 template <> struct DwLoads<DT_I8> { static constexpr int V = 3; };
 
-constexpr int kStrip = 4;   // the vector stores below write exactly 4 outputs
+// Outputs per thread strip: 4, or 8 where the row length wastes no more
+// outputs that way (halving the per-strip index and store bookkeeping).  A
+// strip is written in chunks of 4 (one 4-wide store where full and aligned).
+constexpr int kChunk = 4;
 
-template <int DT, int KH, int KW, int S>
+template <int DT, int KH, int KW, int S, int ST>
 __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const DwPlan pl) {
+  static_assert(ST % kChunk == 0, "strips are whole store chunks");
   typedef typename Dw<DT>::T T;
   typedef typename Dw<DT>::A A;
   extern __shared__ __attribute__((aligned(16))) char dw_smem[];
@@ -116,12 +122,13 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   const int tid = threadIdx.x;
   const T* Wt = (const T*)a.Wt;
   const int nw = np * KK;
+  auto chan = [&](int plane) { return plane - fdiv(pl.fd_c, plane) * C; };
   auto widx = [&](int i) {                                 // weight i of the block -> index in Wt
-    const int pp = i / KK;
-    return ((pl0 + pp) % C) * KK + (i - pp * KK);
+    const int pp = KH ? i / KK : fdiv(pl.fd_kk, i);
+    return chan(pl0 + pp) * KK + (i - pp * KK);
   };
   const int wi0 = widx(min(tid, nw - 1)), wi1 = widx(min(tid + kThreads, nw - 1));
-  const int cb = (pl0 + min(tid, np - 1)) % C;             // channel of this thread's plane value
+  const int cb = chan(pl0 + min(tid, np - 1));             // channel of this thread's plane value
   // (every thread issues all NV vector loads, lanes past the end re-reading
   // the last vector, so that no load is predicated)
   const int ntail = span - tail0;
@@ -168,7 +175,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   };
   if (tid < np) plane_vals(tid, b0, m0);
   for (int i = tid + kThreads; i < np; i += kThreads) {
-    const int c = (pl0 + i) % C;
+    const int c = chan(pl0 + i);
     if constexpr (DT == DT_I8) plane_vals(i, q.bias[c], q.mult[c]);
     else plane_vals(i, bias ? widen<T, A>(bias[c]) : (A)0, 0.0);
   }
@@ -237,24 +244,22 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   if (tid < ntail) dst0[cell(tail0 + tid)] = widen<T, L>(te);
   __syncthreads();
 
-  // compute: strips of kStrip outputs along a row
-  const int nstrip = (Wo + kStrip - 1) / kStrip;
-  const int per_plane = th * nstrip;
-  for (int t = threadIdx.x; t < np * per_plane; t += kThreads) {
-    const int pp = np > 1 ? fdiv(pl.fd_pstrips, t) : 0;   // (np > 1: th == Ho)
-    const int rem = t - pp * per_plane;
-    const int r = fdiv(pl.fd_nstrip, rem);
-    const int ow0 = (rem - r * nstrip) * kStrip;
-    const int64_t plane = pl0 + pp;
+  // compute: strips of ST outputs along a row.  The block's output rows are
+  // numbered plane-major (q = pp * th + r); a thread keeps one strip column
+  // and steps down rows, so its per-strip index work is a few adds.
+  const int nstrip = (Wo + ST - 1) / ST;
+  const int nq = np * th;
+  const int64_t yblock = ((int64_t)pl0 * Ho + oh0) * Wo;  // output offset of (plane pl0, row oh0)
+  auto strip = [&](int pp, int r, int ow0, auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
     const A* wk = wts + pp * KK;
-    A acc[kStrip];
-    A init = (A)0;
-    if constexpr (DT == DT_I8) init = pbias[pp];
+    A acc[ST];
+    const A init = pbias[pp];                              // the bias seeds the accumulators
 #pragma unroll
-    for (int o = 0; o < kStrip; ++o) acc[o] = init;
+    for (int o = 0; o < ST; ++o) acc[o] = init;
 
     if constexpr (KH > 0) {
-      constexpr int WIN = (kStrip - 1) * S + KW;
+      constexpr int WIN = (ST - 1) * S + KW;
 #pragma unroll
       for (int kh = 0; kh < KH; ++kh) {
         const L* rp = tile + (pp * pl.RIN + r * S + kh) * pl.WP + ow0 * S;
@@ -265,7 +270,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
         for (int kw = 0; kw < KW; ++kw) {
           const A wv = wk[kh * KW + kw];
 #pragma unroll
-          for (int o = 0; o < kStrip; ++o) acc[o] += win[o * S + kw] * wv;
+          for (int o = 0; o < ST; ++o) acc[o] += win[o * S + kw] * wv;
         }
       }
     } else {
@@ -274,103 +279,148 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
         for (int kw = 0; kw < kW; ++kw) {
           const A wv = wk[kh * kW + kw];
 #pragma unroll
-          for (int o = 0; o < kStrip; ++o) acc[o] += widen<L, A>(rp[o * sw + kw * dw]) * wv;
+          for (int o = 0; o < ST; ++o) acc[o] += widen<L, A>(rp[o * sw + kw * dw]) * wv;
         }
       }
     }
 
-    // a full strip whose first output is aligned is written with one 4x-wide
-    // store (whole cache lines per wave instead of partial lines)
-    const int oh = oh0 + r;
-    const int64_t ybase = (plane * Ho + oh) * (int64_t)Wo + ow0;
-    const bool full = ow0 + kStrip <= Wo;
-    if constexpr (DT == DT_I8) {
-      if (a.out_dt == DT_I32) {
-        int32_t* yp = (int32_t*)a.Y + ybase;
-        if (full && ((uintptr_t)yp & 15) == 0) {
-          *(i32x4_t*)yp = i32x4_t{acc[0], acc[1], acc[2], acc[3]};
-        } else {
+    // each chunk of 4 outputs that is full and aligned is written with one
+    // 4x-wide store (whole cache lines per wave instead of partial lines)
+    const int yoff = (pp * Ho + r) * Wo + ow0;             // within the block's output span
+    double mv = 0.0;
+    if constexpr (DT == DT_I8) mv = pmult[pp];
 #pragma unroll
-          for (int o = 0; o < kStrip; ++o)
-            if (ow0 + o < Wo) yp[o] = acc[o];
+    for (int c4 = 0; c4 < ST; c4 += kChunk) {
+      const A* ac = acc + c4;
+      const int o0 = ow0 + c4;
+      const bool full = o0 + kChunk <= Wo;
+      if constexpr (DT == DT_I8) {
+        if (a.out_dt == DT_I32) {
+          int32_t* yp = (int32_t*)a.Y + yblock + yoff + c4;
+          if (full && ((uintptr_t)yp & 15) == 0) {
+            *(i32x4_t*)yp = i32x4_t{ac[0], ac[1], ac[2], ac[3]};
+          } else {
+#pragma unroll
+            for (int o = 0; o < kChunk; ++o)
+              if (o0 + o < Wo) yp[o] = ac[o];
+          }
+        } else {
+          int8_t* yp = (int8_t*)a.Y + yblock + yoff + c4;
+          int8_t v[kChunk];
+#pragma unroll
+          for (int o = 0; o < kChunk; ++o) v[o] = requant(ac[o], mv, q.yzp);
+          if (full && ((uintptr_t)yp & 3) == 0) {
+            uint32_t w;
+            __builtin_memcpy(&w, v, 4);
+            *(uint32_t*)yp = w;
+          } else {
+#pragma unroll
+            for (int o = 0; o < kChunk; ++o)
+              if (o0 + o < Wo) yp[o] = v[o];
+          }
         }
       } else {
-        int8_t* yp = (int8_t*)a.Y + ybase;
-        int8_t v[kStrip];
-        const double mv = pmult[pp];
+        float v[kChunk];
 #pragma unroll
-        for (int o = 0; o < kStrip; ++o) v[o] = requant(acc[o], mv, q.yzp);
-        if (full && ((uintptr_t)yp & 3) == 0) {
-          uint32_t w;
-          __builtin_memcpy(&w, v, 4);
-          *(uint32_t*)yp = w;
-        } else {
-#pragma unroll
-          for (int o = 0; o < kStrip; ++o)
-            if (ow0 + o < Wo) yp[o] = v[o];
-        }
-      }
-    } else {
-      const float bv = pbias[pp];
-      with_act(a.act, [&](auto act_k) {
-        constexpr int ACT = decltype(act_k)::value;
-        float v[kStrip];
-#pragma unroll
-        for (int o = 0; o < kStrip; ++o) v[o] = act_c<ACT>(acc[o] + bv);
+        for (int o = 0; o < kChunk; ++o) v[o] = act_c<ACT>(ac[o]);
         if constexpr (DT == DT_BF16) {
-          uint16_t* yp = (uint16_t*)a.Y + ybase;
+          uint16_t* yp = (uint16_t*)a.Y + yblock + yoff + c4;
           if (full && ((uintptr_t)yp & 7) == 0) {
             *(u32x2_t*)yp = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
           } else {
 #pragma unroll
-            for (int o = 0; o < kStrip; ++o)
-              if (ow0 + o < Wo) yp[o] = f32_to_bf16(v[o]);
+            for (int o = 0; o < kChunk; ++o)
+              if (o0 + o < Wo) yp[o] = f32_to_bf16(v[o]);
           }
         } else {
-          float* yp = (float*)a.Y + ybase;
+          float* yp = (float*)a.Y + yblock + yoff + c4;
           if (full && ((uintptr_t)yp & 15) == 0) {
             *(f32x4_t*)yp = f32x4_t{v[0], v[1], v[2], v[3]};
           } else {
 #pragma unroll
-            for (int o = 0; o < kStrip; ++o)
-              if (ow0 + o < Wo) yp[o] = v[o];
+            for (int o = 0; o < kChunk; ++o)
+              if (o0 + o < Wo) yp[o] = v[o];
           }
         }
-      });
+      }
     }
-  }
+  };
+  // row q of the block -> (plane, row); several planes only with th == Ho
+  auto row_of = [&](int qq, int& pp, int& r) {
+    pp = np > 1 ? fdiv(pl.fd_ho, qq) : 0;
+    r = qq - pp * Ho;
+  };
+  auto run = [&](auto act_k) {
+    if (nstrip <= kThreads) {
+      const int rpp = kThreads / nstrip;                   // rows per pass
+      const int q0 = fdiv(pl.fd_nstrip, tid);
+      const int ow0 = (tid - q0 * nstrip) * ST;
+      if (q0 < rpp) {
+        for (int qq = q0; qq < nq; qq += rpp) {
+          int pp, r;
+          row_of(qq, pp, r);
+          strip(pp, r, ow0, act_k);
+        }
+      }
+    } else {
+      for (int t = tid; t < nq * nstrip; t += kThreads) {
+        const int qq = fdiv(pl.fd_nstrip, t);
+        int pp, r;
+        row_of(qq, pp, r);
+        strip(pp, r, (t - qq * nstrip) * ST, act_k);
+      }
+    }
+  };
+  if constexpr (DT == DT_I8) run(std::integral_constant<int, ACT_NONE>{});
+  else with_act(a.act, run);
 }
 
 constexpr int kLdsCap = 64 * 1024;
 
-// the tile (elements of lsize bytes, 16-byte rounded), the fp32/int32
-// weights, the per-plane bias and (int8) the per-plane fp64 multipliers
-int lds_bytes(const DwPlan& p, int KK, int lsize) {
-  return (((p.P * p.RIN * p.WP + 64) * lsize + 15) & ~15) + p.P * KK * 4 + p.P * 4 + 8 + p.P * 8;
+// the tile (4-byte elements, 16-byte rounded), the fp32/int32 weights, the
+// per-plane bias and (int8) the per-plane fp64 multipliers
+int lds_bytes(const DwPlan& p, int KK) {
+  return (((p.P * p.RIN * p.WP + 64) * 4 + 15) & ~15) + p.P * KK * 4 + p.P * 4 + 8 + p.P * 8;
+}
+
+// the fixed-shape kernels (3x3 stride 1 or 2, 1x9; dilation 1)
+bool fixed_shape(const ConvArgs& a) {
+  const bool d1 = a.dh == 1 && a.dw == 1;
+  return d1 && ((a.kH == 3 && a.kW == 3 && a.sh == a.sw && (a.sh == 1 || a.sh == 2)) ||
+                (a.kH == 1 && a.kW == 9 && a.sh == 1 && a.sw == 1));
+}
+
+int strip_width(const ConvArgs& a) {
+  // (a stride-2 strip of 8 needs a 17-wide window; on short rows the
+  // block's few strips would spread unevenly over its threads)
+  if (!fixed_shape(a) || a.sh != 1 || a.Wo < 32) return 4;
+  const int w4 = (a.Wo + 3) / 4 * 4, w8 = (a.Wo + 7) / 8 * 8;
+  return w8 <= w4 ? 8 : 4;
 }
 
 DwPlan make_plan(const ConvArgs& a) {
   DwPlan p;
-  const int nstrip = (a.Wo + kStrip - 1) / kStrip;
+  p.OWT = strip_width(a);
+  const int nstrip = (a.Wo + p.OWT - 1) / p.OWT;
   p.fd_w = make_fastdiv((uint32_t)std::max(1, a.W));
   p.fd_plane = make_fastdiv((uint32_t)std::max(1, a.H * a.W));
   p.fd_nstrip = make_fastdiv((uint32_t)std::max(1, nstrip));
-  p.fd_pstrips = make_fastdiv((uint32_t)std::max(1, a.Ho * nstrip));
-  p.OWT = kStrip;
+  p.fd_ho = make_fastdiv((uint32_t)std::max(1, a.Ho));
+  p.fd_c = make_fastdiv((uint32_t)std::max(1, a.C));
+  p.fd_kk = make_fastdiv((uint32_t)std::max(1, a.kH * a.kW));
   // staged row: left halo, every input column (a strided kernel may not read
   // the last ones, but the staging copies whole rows), right halo and the
   // overrun of the last strip
-  p.WP = std::max((a.Wo - 1) * a.sw + (a.kW - 1) * a.dw + 1 + kStrip * a.sw, a.pl + a.W);
+  p.WP = std::max((a.Wo - 1) * a.sw + (a.kW - 1) * a.dw + 1 + p.OWT * a.sw, a.pl + a.W);
   const int KK = a.kH * a.kW;
   const int per_plane = a.Ho * a.Wo;
   auto rin = [&](int th) { return (th - 1) * a.sh + (a.kH - 1) * a.dh + 1; };
-  // Outputs per block: sized so that a block stages about 16 KB of LDS tile
-  // (4096 fp32 or 8192 raw bf16 input pixels; half that for planes under 512
-  // pixels, where more blocks hide the latency better); a strided kernel
-  // reads sh*sw input pixels per output.  The bytes one block has in flight
-  // while it stages are what bound the kernel's bandwidth.
-  const int lsize = lds_elem_size(a.dt);
-  int target = (a.H * a.W >= 512 ? 4096 : 2048) * (4 / lsize) / std::max(1, a.sh * a.sw);
+  // Outputs per block: a block stages about 4096 input pixels (2048 on
+  // planes under 512 pixels, where more, smaller blocks balance better); a
+  // strided kernel reads sh*sw input pixels per output, but on large planes
+  // (2048+ pixels) a strided block does best with twice that share.
+  const int sa = std::max(1, a.sh * a.sw);
+  int target = (a.H * a.W >= 512 ? 4096 : 2048) / (sa > 1 && a.H * a.W >= 2048 ? std::max(1, sa / 2) : sa);
   if (const char* e = getenv("OX_DW_TARGET")) target = std::max(64, std::min(65536, atoi(e)));  // tuning override
   // input elements the staging phase's first wave of loads covers
   const int esize = a.dt == DT_F32 ? 4 : a.dt == DT_BF16 ? 2 : 1;
@@ -381,7 +431,7 @@ DwPlan make_plan(const ConvArgs& a) {
     p.P = 1;
     p.TH = std::max(1, std::min(a.Ho, target / std::max(1, a.Wo)));
     p.RIN = rin(p.TH);
-    while (p.TH > 1 && (lds_bytes(p, KK, lsize) > kLdsCap || (int64_t)p.RIN * a.W > cap)) {
+    while (p.TH > 1 && (lds_bytes(p, KK) > kLdsCap || (int64_t)p.RIN * a.W > cap)) {
       --p.TH;
       p.RIN = rin(p.TH);
     }
@@ -393,7 +443,7 @@ DwPlan make_plan(const ConvArgs& a) {
     p.TH = a.Ho;
     p.RIN = std::max(rin(p.TH), a.pt + a.H);               // whole planes are staged
     p.P = std::max(1, target / per_plane);
-    while (p.P > 1 && (lds_bytes(p, KK, lsize) > kLdsCap || (int64_t)p.P * a.H * a.W > cap)) --p.P;
+    while (p.P > 1 && (lds_bytes(p, KK) > kLdsCap || (int64_t)p.P * a.H * a.W > cap)) --p.P;
   }
   return p;
 }
@@ -402,19 +452,20 @@ template <int DT>
 int launch_dt(const ConvArgs& a, hipStream_t s) {
   const DwPlan p = make_plan(a);
   const int KK = a.kH * a.kW;
-  const int bytes = lds_bytes(p, KK, lds_elem_size(DT));
+  const int bytes = lds_bytes(p, KK);
   if (bytes > kLdsCap) return (int)hipErrorInvalidConfiguration;
   const int64_t nplanes = (int64_t)a.N * a.C;
   dim3 grid((unsigned)((nplanes + p.P - 1) / p.P), (a.Ho + p.TH - 1) / p.TH, 1);
-  const bool d1 = a.dh == 1 && a.dw == 1;
-  if (d1 && a.kH == 3 && a.kW == 3 && a.sh == 1 && a.sw == 1)
-    hipLaunchKernelGGL((dw_kernel<DT, 3, 3, 1>), grid, dim3(kThreads), bytes, s, a, p);
-  else if (d1 && a.kH == 3 && a.kW == 3 && a.sh == 2 && a.sw == 2)
-    hipLaunchKernelGGL((dw_kernel<DT, 3, 3, 2>), grid, dim3(kThreads), bytes, s, a, p);
-  else if (d1 && a.kH == 1 && a.kW == 9 && a.sh == 1 && a.sw == 1)
-    hipLaunchKernelGGL((dw_kernel<DT, 1, 9, 1>), grid, dim3(kThreads), bytes, s, a, p);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, grid, dim3(kThreads), bytes, s, a, p); };
+  const bool w8 = p.OWT == 8;
+  if (!fixed_shape(a))
+    go(dw_kernel<DT, 0, 0, 0, 4>);
+  else if (a.kH == 1)
+    w8 ? go(dw_kernel<DT, 1, 9, 1, 8>) : go(dw_kernel<DT, 1, 9, 1, 4>);
+  else if (a.sh == 1)
+    w8 ? go(dw_kernel<DT, 3, 3, 1, 8>) : go(dw_kernel<DT, 3, 3, 1, 4>);
   else
-    hipLaunchKernelGGL((dw_kernel<DT, 0, 0, 0>), grid, dim3(kThreads), bytes, s, a, p);
+    w8 ? go(dw_kernel<DT, 3, 3, 2, 8>) : go(dw_kernel<DT, 3, 3, 2, 4>);
   return (int)hipGetLastError();
 }
 
@@ -422,7 +473,7 @@ int launch_dt(const ConvArgs& a, hipStream_t s) {
 
 bool depthwise_fits(const ConvArgs& a) {
   const DwPlan p = make_plan(a);
-  return lds_bytes(p, a.kH * a.kW, lds_elem_size(a.dt)) <= kLdsCap && (a.Ho + p.TH - 1) / p.TH <= 65535;
+  return lds_bytes(p, a.kH * a.kW) <= kLdsCap && (a.Ho + p.TH - 1) / p.TH <= 65535;
 }
 
 int launch_conv_depthwise(const ConvArgs& a, void* stream) {
