@@ -407,9 +407,9 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
   }
 }
 
-template <int WM, int WN, int KC>
-int launch_cfg(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
-  constexpr int FP = 2, FC = 2;
+template <int WM, int WN, int FP, int KC>
+int launch_fp(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
+  constexpr int FC = 2;
   dim3 grid(p.grid, 1, 1);
   switch (p.P) {
     case 4:
@@ -427,9 +427,14 @@ int launch_cfg(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
+template <int WM, int WN, int KC>
+int launch_cfg(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
+  return p.FP == 1 ? launch_fp<WM, WN, 1, KC>(a, p, s) : launch_fp<WM, WN, 2, KC>(a, p, s);
+}
+
 }  // namespace pw
 
-// launch_pw_<WM>_<KC>: tiles of 64*WM channels x 32*(4/WM)*2 pixels, KC
+// launch_pw_<WM>_<KC>: tiles of 64*WM channels x 32*(4/WM)*FP pixels, KC
 // input channels per chunk (wider chunks would not fit the staging
 // registers next to the accumulators)
 int launch_pw_1_32(const ConvArgs& a, const PwPlan& p, void* s);

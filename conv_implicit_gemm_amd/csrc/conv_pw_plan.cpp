@@ -24,16 +24,17 @@ bool geometry(const ConvArgs& a) {
          a.pt == 0 && a.pl == 0 && a.Ho == a.H && a.Wo == a.W && a.C % 32 == 0 && a.C > 0;
 }
 
-PwPlan make(const ConvArgs& a, int WM, int KC) {
+PwPlan make(const ConvArgs& a, int WM, int KC, int FP) {
   PwPlan p;
   p.WM = WM;
+  p.FP = FP;
   p.KC = KC;
   const int HW = a.H * a.W;
   const uintptr_t xa = (uintptr_t)a.X, ya = (uintptr_t)a.Y;
   p.P = (HW % 4 == 0 && xa % 8 == 0) ? 4 : (HW % 2 == 0 && xa % 4 == 0) ? 2 : 1;
   p.V = 8;
   while (p.V > 1 && (HW % p.V || ya % (2 * p.V))) p.V >>= 1;
-  const int BM = 64 * WM, BN = 32 * (4 / WM) * 2;
+  const int BM = 64 * WM, BN = 32 * (4 / WM) * FP;
   const int64_t Q = (int64_t)a.N * HW;
   p.npb = (int)((Q + BN - 1) / BN);
   p.nmb = (a.M + BM - 1) / BM;
@@ -65,15 +66,29 @@ PwPlan make(const ConvArgs& a, int WM, int KC) {
 }
 
 size_t ws_bytes(const PwPlan& p) {
-  const int BM = 64 * p.WM, BN = 32 * (4 / p.WM) * 2;
+  const int BM = 64 * p.WM, BN = 32 * (4 / p.WM) * p.FP;
   return p.splits > 1 ? (size_t)p.npb * p.nmb * p.splits * BM * BN * sizeof(float) : 0;
 }
 
 bool valid(const ConvArgs& a, const PwPlan& p) {
   // (a 256-pixel block staging single pixels takes 32-channel chunks: the
   // registers of 64 would spill)
-  return a.C % p.KC == 0 && p.KC <= 64 && !(p.WM == 1 && p.P == 1 && p.KC > 32) &&
+  return a.C % p.KC == 0 && p.KC <= 64 && !(p.WM == 1 && p.FP == 2 && p.P == 1 && p.KC > 32) &&
          p.lds <= kLdsMax && (int64_t)p.npb * p.nmb * p.splits < (int64_t)1 << 31;
+}
+
+// Pixel fragments per wave: two (128 x 128 or 64 x 256 tiles), or one where
+// tiles of that size would leave CUs without a block -- half-width tiles
+// double the block count, so that blocks share CUs and overlap one's staging
+// with another's MFMAs (a sweep of the ResNet-50 1x1 layers at batch 32:
+// -28% at 208 tiles, -12% at 98, -3% at 196, but +8..+26% at 392).
+// OX_PW_FP pins it.
+int fp_choice(const ConvArgs& a, int WM) {
+  if (const char* e = getenv("OX_PW_FP")) return atoi(e) == 1 ? 1 : 2;
+  const int64_t Q = (int64_t)a.N * a.H * a.W;
+  const int BM = 64 * WM, BN = 32 * (4 / WM) * 2;
+  const int64_t tiles = ((Q + BN - 1) / BN) * ((a.M + BM - 1) / BM);
+  return tiles < kCUs ? 1 : 2;
 }
 
 // OX_PW_PLAN=WM:KC pins the configuration (for measurements); a pinned
@@ -84,7 +99,7 @@ bool pw_plan(const ConvArgs& a, PwPlan* out) {
   int wm, kc;
   if (e && *e && sscanf(e, "%d:%d", &wm, &kc) == 2) {
     if ((wm != 1 && wm != 2) || (kc != 32 && kc != 64)) return false;
-    const PwPlan p = make(a, wm, kc);
+    const PwPlan p = make(a, wm, kc, fp_choice(a, wm));
     if (!valid(a, p)) return false;
     *out = p;
     return true;
@@ -93,7 +108,7 @@ bool pw_plan(const ConvArgs& a, PwPlan* out) {
   // chunk that divides C (fewer barriers, more bytes in flight per chunk)
   const int WM = a.M <= 64 ? 1 : 2;
   for (int kc : {64, 32}) {
-    const PwPlan p = make(a, WM, kc);
+    const PwPlan p = make(a, WM, kc, fp_choice(a, WM));
     if (valid(a, p)) {
       *out = p;
       return true;
@@ -130,7 +145,7 @@ const char* conv_pw_describe(const ConvArgs& a, char* buf, int cap) {
   PwPlan p;
   if (!pw_plan(a, &p)) return "";
   snprintf(buf, cap, "BM=%d BN=%d KC=%d P=%d V=%d tiles=%lld splits=%d grid=%d lds=%d", 64 * p.WM,
-           64 * (4 / p.WM), p.KC, p.P, p.V, (long long)p.npb * p.nmb, p.splits, p.grid, p.lds);
+           32 * (4 / p.WM) * p.FP, p.KC, p.P, p.V, (long long)p.npb * p.nmb, p.splits, p.grid, p.lds);
   return buf;
 }
 

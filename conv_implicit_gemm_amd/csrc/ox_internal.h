@@ -132,7 +132,8 @@ struct PatchPlan {
 
 // Plan of the pointwise (1x1) kernel: block configuration and launch grid.
 struct PwPlan {
-  int WM;     // wave rows: 64*WM output channels, 32*(4/WM)*2 pixels per block
+  int WM;     // wave rows: 64*WM output channels, 32*(4/WM)*FP pixels per block
+  int FP;     // 32-pixel fragments per wave (1 or 2)
   int KC;     // input channels per chunk (32 or 64)
   int P;      // pixels per staging load (1, 2 or 4)
   int V;      // pixels per output store (1, 2, 4 or 8)

@@ -302,20 +302,22 @@ def test_pw_conv_sweep_bf16(ox, monkeypatch):
         assert_close(host64(Y), oracle.conv2d(X, Wt, b, act=act), "bf16", "pw %d" % ci)
 
 
+@pytest.mark.parametrize("fp", ["1", "2"])
 @pytest.mark.parametrize("plan", ["1:32", "1:64", "2:32", "2:64"])
-def test_pw_each_config(ox, plan, monkeypatch):
+def test_pw_each_config(ox, plan, fp, monkeypatch):
     # every block configuration (wave rows : channel chunk), pinned, with the
     # staging load width (1, 2, 4 pixels) and the store width (1 .. 8 pixels)
     # driven by the plane size and by X and Y pointers offset from alignment
     monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
     monkeypatch.setenv("OX_PW_PLAN", plan)
+    monkeypatch.setenv("OX_PW_FP", fp)      # 32-pixel fragments per wave
     r = np.random.default_rng(31 + int(plan[0]) * 1000 + int(plan[2:]))
     for ci, (N, Cin, H, W, M, xoff, yoff) in enumerate([
             (2, 128, 8, 8, 70, 0, 0), (3, 128, 6, 5, 150, 0, 0), (2, 256, 7, 7, 64, 0, 0),
             (2, 128, 4, 8, 96, 1, 1), (1, 256, 6, 6, 200, 2, 2), (5, 128, 3, 3, 33, 0, 3)]):
         HW = H * W
         P = 4 if HW % 4 == 0 and xoff % 4 == 0 else 2 if HW % 2 == 0 and xoff % 2 == 0 else 1
-        if plan == "1:64" and P == 1:
+        if plan == "1:64" and P == 1 and fp == "2":
             continue      # that plan does not take single-pixel staging
         X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
         Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
@@ -330,13 +332,15 @@ def test_pw_each_config(ox, plan, monkeypatch):
                      "pw %s case %d" % (plan, ci))
 
 
+@pytest.mark.parametrize("fp", ["1", "2"])
 @pytest.mark.parametrize("splits", [2, 3, 5])
-def test_pw_split_k(ox, splits, monkeypatch):
+def test_pw_split_k(ox, splits, fp, monkeypatch):
     # split-K: slices of the channel range write fp32 partials, a second
     # kernel adds them in slice order -- same result as the oracle, and
     # bit-identical from run to run
     monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
     monkeypatch.setenv("OX_PW_SPLITS", str(splits))
+    monkeypatch.setenv("OX_PW_FP", fp)
     r = np.random.default_rng(600 + splits)
     for ci, (N, Cin, H, W, M) in enumerate([(2, 512, 7, 7, 200), (3, 320, 6, 6, 64), (1, 256, 9, 9, 130)]):
         X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
