@@ -122,8 +122,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   static_assert(WM * WN == 4, "four waves");
   static_assert(BN % P == 0 && KC % 32 == 0, "tile shape");
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  char* As = smem;                 // weights [BM][ROW]
-  char* Xs = smem + BM * ROW;      // pixels  [BN][ROW]
+  // two operand buffers: chunk k+1 is staged into one while chunk k's MFMAs
+  // read the other
+  constexpr int BUF = (BM + BN) * ROW;
+  auto As = [&](int b) { return smem + b * BUF; };             // weights [BM][ROW]
+  auto Xs = [&](int b) { return smem + b * BUF + BM * ROW; };  // pixels  [BN][ROW]
   // the tile's bias, fp32, beyond both the operand tiles and the epilogue's
   // staging area: fetched with the tile's first chunk and written to LDS
   // with it, so that the epilogue never waits on a global load
@@ -238,12 +241,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
   };
 
-  auto store_chunk = [&](bool with_bias) {
+  auto store_chunk = [&](int buf, bool with_bias) {
     if (with_bias && tid < BM) Bs[tid] = b_ok ? __uint_as_float(breg << 16) : 0.0f;
 #pragma unroll
     for (int k = 0; k < WUPT; ++k)
       if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU)
-        *(u32x4_t*)(As + w_lds[k]) = ((w_ok >> k) & 1) ? wreg[k] : u32x4_t{0u, 0u, 0u, 0u};
+        *(u32x4_t*)(As(buf) + w_lds[k]) = ((w_ok >> k) & 1) ? wreg[k] : u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
     for (int k = 0; k < XUPT; ++k) {
       if (k * kThreads + kThreads <= XU || tid + k * kThreads < XU) {
@@ -259,7 +262,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
             else if ((e & 1) == 0) d[j] = (lo & 0xffffu) | (hi << 16);
             else d[j] = (lo >> 16) | (hi & 0xffff0000u);
           }
-          *(u32x4_t*)(Xs + x_lds[k] + e * ROW) = u32x4_t{d[0], d[1], d[2], d[3]};
+          *(u32x4_t*)(Xs(buf) + x_lds[k] + e * ROW) = u32x4_t{d[0], d[1], d[2], d[3]};
         }
       }
     }
@@ -278,24 +281,33 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
       for (int j = 0; j < FC; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    for (int chunk = cur_lo; chunk < cur_hi; ++chunk) {
-      __syncthreads();               // LDS is free: previous MFMAs and epilogue are done
-      store_chunk(S == 1 && chunk == cur_lo);
-      __syncthreads();
-      if (chunk + 1 < cur_hi) {
-        load_chunk((chunk + 1) * KC);
+    // the registers hold chunk cur_lo; after a chunk is stored they are
+    // refilled with the next chunk of this unit or, after its last, with the
+    // next unit's first chunk (and bias)
+    auto load_after = [&](int c) {
+      if (c < cur_hi) {
+        load_chunk(c * KC);
       } else if (next < units) {
         decode(next);
         tile_offsets();
         load_chunk(c_lo * KC);
         if (S == 1) load_bias();
       }
+    };
+    __syncthreads();                 // LDS is free: previous MFMAs and epilogue are done
+    store_chunk(0, S == 1);
+    load_after(cur_lo + 1);
+    __syncthreads();
+    for (int chunk = cur_lo; chunk < cur_hi; ++chunk) {
+      const int buf = (chunk - cur_lo) & 1;
+      const char* Xb = Xs(buf);
+      const char* Ab = As(buf);
       u32x4_t pf[3][FP], wf[3][FC];
-      auto read_frags = [&](int s, int buf) {
+      auto read_frags = [&](int s, int fb) {
 #pragma unroll
-        for (int f = 0; f < FP; ++f) pf[buf][f] = *(const u32x4_t*)(Xs + pbase + f * 32 * ROW + s * 32);
+        for (int f = 0; f < FP; ++f) pf[fb][f] = *(const u32x4_t*)(Xb + pbase + f * 32 * ROW + s * 32);
 #pragma unroll
-        for (int f = 0; f < FC; ++f) wf[buf][f] = *(const u32x4_t*)(As + wbase + f * 32 * ROW + s * 32);
+        for (int f = 0; f < FC; ++f) wf[fb][f] = *(const u32x4_t*)(Ab + wbase + f * 32 * ROW + s * 32);
       };
       read_frags(0, 0);
       if (NS > 1) read_frags(1, 1);
@@ -315,9 +327,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (chunk + 1 < cur_hi) {
+        store_chunk(buf ^ 1, false); // the other buffer: its last reader finished before the previous barrier
+        load_after(chunk + 2);
+      }
+      __syncthreads();
     }
     if (S == 1) {
-      __syncthreads();               // every wave is done reading this tile's operands
       store_tile<WM, WN, FP, FC>(a, pl, smem, Bs, acc, cur_pb * BN, cur_m0);
     } else {
       f32x4_t* dst = partial_base<FP, FC>(pl.ws, cur_unit) + tid;
