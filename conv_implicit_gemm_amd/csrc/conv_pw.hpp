@@ -39,7 +39,7 @@ namespace pw {
 // + (0..3).  The caller has synchronised the block: LDS is free.
 template <int WM, int WN, int FP, int FC>
 __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, char* smem,
-                                           const float* Bs, const f32x16_t (&acc)[FP][FC], int q0,
+                                           const uint16_t* Bv, const f32x16_t (&acc)[FP][FC], int q0,
                                            int m0) {
   constexpr int BM = 32 * WM * FC, BN = 32 * WN * FP;
   constexpr int EROW = BN + 8;
@@ -51,7 +51,10 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
   uint16_t* E = (uint16_t*)smem;
   float bv[FC];
 #pragma unroll
-  for (int fc = 0; fc < FC; ++fc) bv[fc] = Bs[wm * FC * 32 + fc * 32 + l32];
+  for (int fc = 0; fc < FC; ++fc) {
+    const int m = m0 + wm * FC * 32 + fc * 32 + l32;
+    bv[fc] = (Bv && m < M) ? bf16_to_f32(Bv[m]) : 0.0f;
+  }
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
@@ -127,10 +130,11 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   constexpr int BUF = (BM + BN) * ROW;
   auto As = [&](int b) { return smem + b * BUF; };             // weights [BM][ROW]
   auto Xs = [&](int b) { return smem + b * BUF + BM * ROW; };  // pixels  [BN][ROW]
-  // the tile's bias, fp32, beyond both the operand tiles and the epilogue's
-  // staging area: fetched with the tile's first chunk and written to LDS
-  // with it, so that the epilogue never waits on a global load
-  float* Bs = (float*)(smem + pl.lds - BM * 4);
+  // the bias vector, raw bf16, beyond both the operand buffers and the
+  // epilogue's staging area: staged once per block with the first chunk (as
+  // the 32-bit words that hold it, from its aligned-down address), so that
+  // no epilogue waits on a global load and no load is carried across units
+  uint32_t* Bw = (uint32_t*)(smem + pl.lds - pl.bias_lds);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -211,13 +215,23 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   constexpr int XR = P == 4 ? 2 : 1;
   uint32_t xreg[XUPT][8][XR];
   u32x4_t wreg[WUPT];
-  uint32_t breg = 0;               // raw bias bits of channel m0 + tid (tid < BM)
-  bool b_ok = false;
+  constexpr int BWPT = 4;          // bias words per thread in the first round
   const uint16_t* bias = (const uint16_t*)a.bias;
-  auto load_bias = [&]() {
-    const int m = m0 + (tid % BM);
-    b_ok = bias != nullptr && m < M;
-    breg = (b_ok ? bias : Wg)[b_ok ? m : 0];
+  const uintptr_t baddr = (uintptr_t)bias;
+  const int boff = (int)(baddr & 3);                       // byte offset of bias[0] in its word
+  const uint32_t* bwords = (const uint32_t*)(baddr & ~(uintptr_t)3);
+  const int nbw = (bias && S == 1) ? (boff + 2 * M + 3) / 4 : 0;
+  const uint16_t* Bv = nbw ? (const uint16_t*)((const char*)Bw + boff) : nullptr;
+  uint32_t bwv[BWPT];
+  if (nbw > 0) {
+#pragma unroll
+    for (int k = 0; k < BWPT; ++k) bwv[k] = bwords[min(tid + k * kThreads, nbw - 1)];
+  }
+  auto store_bias = [&]() {
+#pragma unroll
+    for (int k = 0; k < BWPT; ++k)
+      if (tid + k * kThreads < nbw) Bw[tid + k * kThreads] = bwv[k];
+    for (int i = tid + BWPT * kThreads; i < nbw; i += kThreads) Bw[i] = bwords[i];
   };
 
   auto load_chunk = [&](int c0) {
@@ -241,8 +255,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     }
   };
 
-  auto store_chunk = [&](int buf, bool with_bias) {
-    if (with_bias && tid < BM) Bs[tid] = b_ok ? __uint_as_float(breg << 16) : 0.0f;
+  auto store_chunk = [&](int buf) {
 #pragma unroll
     for (int k = 0; k < WUPT; ++k)
       if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU)
@@ -271,7 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   decode(u);
   tile_offsets();
   load_chunk(c_lo * KC);
-  if (S == 1) load_bias();
+  bool first_unit = true;
   for (;;) {
     const int cur_pb = pb, cur_m0 = m0, cur_lo = c_lo, cur_hi = c_hi, cur_unit = unit_id;
     const int next = u + (int)gridDim.x;
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
     // the registers hold chunk cur_lo; after a chunk is stored they are
     // refilled with the next chunk of this unit or, after its last, with the
-    // next unit's first chunk (and bias)
+    // next unit's first chunk
     auto load_after = [&](int c) {
       if (c < cur_hi) {
         load_chunk(c * KC);
@@ -291,11 +304,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         decode(next);
         tile_offsets();
         load_chunk(c_lo * KC);
-        if (S == 1) load_bias();
       }
     };
     __syncthreads();                 // LDS is free: previous MFMAs and epilogue are done
-    store_chunk(0, S == 1);
+    if (first_unit) store_bias();
+    first_unit = false;
+    store_chunk(0);
     load_after(cur_lo + 1);
     __syncthreads();
     for (int chunk = cur_lo; chunk < cur_hi; ++chunk) {
@@ -328,13 +342,13 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
         __builtin_amdgcn_sched_barrier(0);
       }
       if (chunk + 1 < cur_hi) {
-        store_chunk(buf ^ 1, false); // the other buffer: its last reader finished before the previous barrier
+        store_chunk(buf ^ 1);        // the other buffer: its last reader finished before the previous barrier
         load_after(chunk + 2);
       }
       __syncthreads();
     }
     if (S == 1) {
-      store_tile<WM, WN, FP, FC>(a, pl, smem, Bs, acc, cur_pb * BN, cur_m0);
+      store_tile<WM, WN, FP, FC>(a, pl, smem, Bv, acc, cur_pb * BN, cur_m0);
     } else {
       f32x4_t* dst = partial_base<FP, FC>(pl.ws, cur_unit) + tid;
 #pragma unroll

@@ -39,8 +39,10 @@ PwPlan make(const ConvArgs& a, int WM, int KC, int FP) {
   p.npb = (int)((Q + BN - 1) / BN);
   p.nmb = (a.M + BM - 1) / BM;
   const int row = KC * 2 + 16;
-  // two operand buffers (or the epilogue's staging tile) + the tile's fp32 bias
-  p.lds = std::max(2 * (BM + BN) * row, BM * (BN + 8) * 2) + BM * 4;
+  // two operand buffers (or the epilogue's staging tile) + the bias vector
+  // (raw bf16 words from its aligned-down address)
+  p.bias_lds = ((2 * a.M + 3 + 3) / 4 * 4 + 15) / 16 * 16;
+  p.lds = std::max(2 * (BM + BN) * row, BM * (BN + 8) * 2) + p.bias_lds;
   // split-K when the tiles alone would leave many CUs idle and the channel
   // range is long: about 192 work units of at least four chunks (a sweep
   // of the ResNet-50 1x1 layers at batch 32: two slices for 98 tiles x 16

@@ -140,6 +140,7 @@ struct PwPlan {
   int npb;    // pixel blocks
   int nmb;    // output-channel blocks
   int lds;    // bytes of LDS
+  int bias_lds;  // of which the staged bias vector (its tail)
   int grid;   // persistent blocks (work units are strided over them)
   int splits; // slices of the channel range per tile (split-K), 1 = none
   int cps;    // chunks per slice
