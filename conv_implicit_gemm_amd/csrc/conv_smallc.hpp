@@ -52,6 +52,43 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_bf16(const ConvArgs a
   const int rows_here = min(pl.TR, a.Ho - oh0);
   const int ih_base = oh0 * S - a.pt;
 
+  // Staging issues every global load before its first wait: the block's
+  // weight rows (one contiguous range of mvalid*K values, 16-byte vectors
+  // where W is aligned: WV per thread, a loop takes any rest), the input
+  // band's 8-position groups (XV per thread; a group's rows outside the
+  // image load row 0 or H-1 and are not stored).  The LDS tile is zeroed
+  // while they are in flight.
+  constexpr int WV = 6, XV = 2;
+  const uint16_t* Wg = (const uint16_t*)a.Wt + (int64_t)m0 * K;
+  const int wcount = min(BM, M - m0) * K;
+  const int nvec = pl.w_vec ? wcount / 8 : 0;
+  u32x4_t wv[WV];
+  if (nvec > 0) {
+#pragma unroll
+    for (int k = 0; k < WV; ++k) wv[k] = *(const u32x4_t*)(Wg + min(tid + k * kThreads, nvec - 1) * 8);
+  }
+  const uint16_t* Xn = (const uint16_t*)a.X + (int64_t)n * C * H * W;
+  const int ngrp = W / 8;
+  const int nunits = P == 8 ? pl.PR * ngrp : 0;
+  u32x4_t xv[XV][4];
+  auto unit_src = [&](int u, int c) {        // channel c (clamped to C-1) of band group u
+    const int pr = u / ngrp, j = u - (u / ngrp) * ngrp;
+    const int ih = min(max(ih_base + pr, 0), H - 1);
+    return Xn + ((int64_t)min(c, C - 1) * H + ih) * W + j * 8;
+  };
+  if (nunits > 0) {
+#pragma unroll
+    for (int k = 0; k < XV; ++k) {
+      const int u = min(tid + k * kThreads, nunits - 1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) xv[k][c] = *(const u32x4_t*)unit_src(u, c);
+    }
+  }
+  // zero the patch and the weight tile (padding taps and channels stay 0)
+  const int zbytes = BM * wrow + pl.PR * pl.PWc * kCellB;
+  for (int i = tid * 16; i < zbytes; i += kThreads * 16) *(u32x4_t*)(smem + i) = u32x4_t{0u, 0u, 0u, 0u};
+  __syncthreads();
+  // (the bias after the zeroing: its loads are waited for with the staging data)
   const uint16_t* bias = (const uint16_t*)a.bias;
   uint32_t braw[2];   // raw bits, converted in the epilogue (see the 3x3 kernel)
 #pragma unroll
@@ -60,44 +97,42 @@ __global__ __launch_bounds__(kThreads, 2) void conv_smallc_bf16(const ConvArgs a
     braw[fc] = (bias && m0 + ml < M) ? (uint32_t)bias[m0 + ml] : 0u;
   }
 
-  // zero the patch and the weight tile (padding taps and channels stay 0)
-  const int zbytes = BM * wrow + pl.PR * pl.PWc * kCellB;
-  for (int i = tid * 16; i < zbytes; i += kThreads * 16) *(u32x4_t*)(smem + i) = u32x4_t{0u, 0u, 0u, 0u};
-  __syncthreads();
-
-  // weights: the block's rows W[m0 .. m0+mvalid) are one contiguous range of
-  // mvalid*K values; copy it as stored (16-byte loads where W is aligned),
-  // then rearrange into (kh, tap, channel) order below
-  const uint16_t* Wg = (const uint16_t*)a.Wt + (int64_t)m0 * K;
-  const int wcount = min(BM, M - m0) * K;
+  // weights, as stored, to Wraw (rearranged into (kh, tap, channel) order below)
   if (pl.w_vec) {
-    const int nvec = wcount / 8;
-    for (int v = tid; v < nvec; v += kThreads) *(u32x4_t*)(Wraw + v * 8) = *(const u32x4_t*)(Wg + v * 8);
+#pragma unroll
+    for (int k = 0; k < WV; ++k)
+      if (tid + k * kThreads < nvec) *(u32x4_t*)(Wraw + (tid + k * kThreads) * 8) = wv[k];
+    for (int v = tid + WV * kThreads; v < nvec; v += kThreads)
+      *(u32x4_t*)(Wraw + v * 8) = *(const u32x4_t*)(Wg + v * 8);
     for (int e = nvec * 8 + tid; e < wcount; e += kThreads) Wraw[e] = Wg[e];
   } else {
     for (int e = tid; e < wcount; e += kThreads) Wraw[e] = Wg[e];
   }
   // input band: patch cell (pr, pc) = input (ih_base + pr, pc - pl), channels 0..C-1
-  const uint16_t* Xn = (const uint16_t*)a.X + (int64_t)n * C * H * W;
   if constexpr (P == 8) {
-    const int ngrp = W / 8;
-    for (int u = tid; u < pl.PR * ngrp; u += kThreads) {
+    auto put = [&](int u, const u32x4_t (&v)[4]) {
       const int pr = u / ngrp, j = u - (u / ngrp) * ngrp;
       const int ih = ih_base + pr;
-      if (ih < 0 || ih >= H) continue;
-      u32x4_t v[4];
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        v[c] = c < C ? *(const u32x4_t*)(Xn + ((int64_t)c * H + ih) * W + j * 8) : u32x4_t{0u, 0u, 0u, 0u};
+      if (ih < 0 || ih >= H) return;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int pc = j * 8 + e + a.pl;
         if (pc >= pl.PWc) break;
         const int sh = (e & 1) * 16, w = e >> 1;
-        const uint32_t c0 = (v[0][w] >> sh) & 0xffffu, c1 = (v[1][w] >> sh) & 0xffffu;
-        const uint32_t c2 = (v[2][w] >> sh) & 0xffffu, c3 = (v[3][w] >> sh) & 0xffffu;
-        *(u32x2_t*)(Ps + (pr * pl.PWc + pc) * kCellB) = u32x2_t{c0 | (c1 << 16), c2 | (c3 << 16)};
+        uint32_t cw[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) cw[c] = c < C ? (v[c][w] >> sh) & 0xffffu : 0u;
+        *(u32x2_t*)(Ps + (pr * pl.PWc + pc) * kCellB) = u32x2_t{cw[0] | (cw[1] << 16), cw[2] | (cw[3] << 16)};
       }
+    };
+#pragma unroll
+    for (int k = 0; k < XV; ++k)
+      if (tid + k * kThreads < nunits) put(tid + k * kThreads, xv[k]);
+    for (int u = tid + XV * kThreads; u < nunits; u += kThreads) {
+      u32x4_t v[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = *(const u32x4_t*)unit_src(u, c);
+      put(u, v);
     }
   } else {
     for (int u = tid; u < pl.PR * W; u += kThreads) {

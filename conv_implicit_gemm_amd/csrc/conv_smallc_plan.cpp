@@ -1,5 +1,6 @@
 // conv_smallc_plan.cpp -- host-side planning of the few-input-channel kernel.
 #include <algorithm>
+#include <cstdlib>
 #include <cstdint>
 #include <cstdio>
 
@@ -46,6 +47,10 @@ bool make(const ConvArgs& a, int FP, SmallcPlan* out) {
 // still has two blocks per CU; else 256-pixel blocks
 bool plan(const ConvArgs& a, SmallcPlan* out) {
   if (!geometry(a)) return false;
+  if (const char* e = getenv("OX_SMALLC_FP")) {   // pins the tiles per wave (measurements)
+    const int fp = atoi(e) == 2 ? 2 : 4;
+    return make(a, fp, out);
+  }
   SmallcPlan p4;
   if (make(a, 4, &p4) && (int64_t)p4.nrb * a.N * p4.nmb >= 512) {
     *out = p4;
