@@ -301,7 +301,7 @@ def measured_traffic(kernel, workload, dtype):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py: this build runs on one GPU only; --gpus %d is not supported "
+        print("bench.py: the library runs on one GPU; --gpus %d is not supported "
               "(the per-GPU path is the same kernel at one GPU's share)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
