@@ -110,8 +110,16 @@ __device__ __forceinline__ f32x4_t* partial_base(float* ws, int64_t unit) {
   return (f32x4_t*)ws + unit * (int64_t)(kThreads * FP * FC * 4);
 }
 
+// Raw buffer resource over [p, p + bytes): a load whose offset lies beyond
+// the range returns zeros, which stands in for the zero padding of partial
+// tiles (rows past M, pixels past the batch) with no per-load predicate.
+constexpr uint32_t kOutside = 0x80000000u;    // an offset past any tensor the kernel takes
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
 template <int WM, int WN, int FP, int FC, int KC, int P>
-__global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, const PwPlan pl) {
+__global__ __launch_bounds__(kThreads, KC == 32 ? 3 : 2) void conv1x1_bf16(const ConvArgs a, const PwPlan pl) {
   constexpr int BM = 32 * WM * FC;          // output channels per tile
   constexpr int BN = 32 * WN * FP;          // pixels per tile
   constexpr int ROW = KC * 2 + 16;          // bytes per staged row
@@ -122,6 +130,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   constexpr int WU = BM * WPR;
   constexpr int WUPT = (WU + kThreads - 1) / kThreads;
   constexpr int NS = KC / 16;               // k-steps per chunk
+  // register sets of loaded chunks: two for 64-channel chunks; one for
+  // 32-channel chunks, whose blocks are small enough to run three per CU
+  // (a second set would cost that occupancy)
+  constexpr int NSET = KC == 64 ? 2 : 1;
   static_assert(WM * WN == 4, "four waves");
   static_assert(BN % P == 0 && KC % 32 == 0, "tile shape");
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -146,34 +158,43 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   const int HW = a.H * a.W, C = a.C, M = a.M;
   const int Q = a.N * HW;
   const int nchunks = C / KC;
-  const uint16_t* Xg = (const uint16_t*)a.X;
-  const uint16_t* Wg = (const uint16_t*)a.Wt;
+  // (the plan keeps both tensors below 2^30 bytes, so that no offset of a
+  // unit past the tensor's end wraps around 2^32)
+  const __amdgpu_buffer_rsrc_t xr = buffer_rsrc(a.X, (uint32_t)Q * (uint32_t)C * 2u);
+  const __amdgpu_buffer_rsrc_t wr = buffer_rsrc(a.Wt, (uint32_t)M * (uint32_t)C * 2u);
 
   // Block b runs units b, b + G, b + 2G, ... (G = grid size, a multiple of
   // the XCD count when below the unit count), so a block stays on one XCD and
   // xcd_tile keeps each XCD on one contiguous range of logical units (the
   // slices of a tile adjacent, then the channel blocks of a pixel block).
-  int u = blockIdx.x;
-  if (u >= units) return;
-  int pb, m0, c_lo, c_hi, unit_id;
+  if ((int)blockIdx.x >= units) return;
+  struct Unit {
+    int id, pb, m0, lo, hi;   // logical unit, pixel block, first channel, chunk range
+  };
   auto decode = [&](int uu) {
-    unit_id = xcd_tile(uu, units);
-    const int tile = unit_id / S;
-    const int slice = unit_id - tile * S;
-    pb = tile / pl.nmb;
-    m0 = (tile - pb * pl.nmb) * BM;
-    c_lo = slice * cps;
-    c_hi = min(nchunks, c_lo + cps);
+    Unit d;
+    d.id = xcd_tile(uu, units);
+    const int tile = d.id / S;
+    const int slice = d.id - tile * S;
+    d.pb = tile / pl.nmb;
+    d.m0 = (tile - d.pb * pl.nmb) * BM;
+    d.lo = slice * cps;
+    d.hi = min(nchunks, d.lo + cps);
+    return d;
   };
 
-  // this thread's pixel staging units: element offset of the first value and
-  // LDS offset of its first row piece; units and weight pieces that fall
-  // outside the tensors load from offset 0 and store zeros (loads are never
-  // predicated: a register that a load may or may not write would force the
-  // wave to wait on every load in flight before reusing it)
-  int x_goff[XUPT], x_lds[XUPT];
-  int w_goff[WUPT], w_lds[WUPT];
-  uint32_t x_ok = 0, w_ok = 0;   // bit k: unit / piece k is inside the tensor
+  // The block's chunks form one stream (unit after unit).  Stream position j
+  // is loaded into register set j % NSET, NSET positions ahead of its use:
+  // while chunk j's MFMAs run, chunk j+1 is staged from its registers into
+  // the other LDS buffer and (two sets) the loads of chunk j+2 are in
+  // flight.  The load cursor runs ahead of the compute cursor and crosses
+  // into the next unit on its own.
+  //
+  // Staging units of this thread: byte offset of the first value in X (or in
+  // W) at chunk 0 and LDS offset of its first row piece.  Units past the
+  // tile's pixels or channels read beyond the tensor and get zeros.
+  uint32_t x_off[XUPT], w_off[WUPT];
+  int x_lds[XUPT], w_lds[WUPT];
 #pragma unroll
   for (int k = 0; k < XUPT; ++k) {
     const int v = tid + k * kThreads;
@@ -184,26 +205,22 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     const int v = tid + k * kThreads;
     w_lds[k] = (v / WPR) * ROW + (v % WPR) * 16;
   }
-  auto tile_offsets = [&]() {
+  auto tile_offsets = [&](int pb, int m0) {
     const int q0 = pb * BN;
-    x_ok = w_ok = 0;
 #pragma unroll
     for (int k = 0; k < XUPT; ++k) {
       const int v = tid + k * kThreads;
       const int oct = v / NG, g = v - (v / NG) * NG;
       const int q = q0 + g * P;
-      const bool ok = v < XU && q < Q;
-      const int n = ok ? q / HW : 0;
-      x_goff[k] = ok ? (n * C + oct * 8) * HW + (q - n * HW) : 0;
-      x_ok |= (ok ? 1u : 0u) << k;
+      const int n = q / HW;                 // n >= N past the batch: beyond X
+      x_off[k] = v < XU ? ((uint32_t)(n * C + oct * 8) * (uint32_t)HW + (uint32_t)(q - n * HW)) * 2u : kOutside;
     }
 #pragma unroll
     for (int k = 0; k < WUPT; ++k) {
       const int v = tid + k * kThreads;
       const int m = v / WPR, j = v - (v / WPR) * WPR;
-      const bool ok = v < WU && m0 + m < M;
-      w_goff[k] = ok ? (m0 + m) * C + j * 8 : 0;
-      w_ok |= (ok ? 1u : 0u) << k;
+      // rows m0 + m >= M lie beyond W
+      w_off[k] = v < WU ? ((uint32_t)(m0 + m) * (uint32_t)C + (uint32_t)(j * 8)) * 2u : kOutside;
     }
   };
 
@@ -213,8 +230,8 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
   f32x16_t acc[FP][FC];
   // P = 1: one bf16 per load; P = 2: one dword; P = 4: two dwords
   constexpr int XR = P == 4 ? 2 : 1;
-  uint32_t xreg[XUPT][8][XR];
-  u32x4_t wreg[WUPT];
+  uint32_t xreg[NSET][XUPT][8][XR];
+  u32x4_t wreg[NSET][WUPT];
   constexpr int BWPT = 4;          // bias words per thread in the first round
   const uint16_t* bias = (const uint16_t*)a.bias;
   const uintptr_t baddr = (uintptr_t)bias;
@@ -234,123 +251,190 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
     for (int i = tid + BWPT * kThreads; i < nbw; i += kThreads) Bw[i] = bwords[i];
   };
 
-  auto load_chunk = [&](int c0) {
+  // global loads of chunk c0 of the load cursor's unit into register set R
+  auto load_chunk = [&](auto Rc, int c0) {
+    constexpr int R = decltype(Rc)::value % NSET;
+    const uint32_t wc = (uint32_t)c0 * 2u;
 #pragma unroll
-    for (int k = 0; k < WUPT; ++k) wreg[k] = *(const u32x4_t*)(Wg + w_goff[k] + c0);
+    for (int k = 0; k < WUPT; ++k) wreg[R][k] = __builtin_amdgcn_raw_buffer_load_b128(wr, w_off[k] + wc, 0, 0);
 #pragma unroll
-    for (int k = 0; k < XUPT; ++k) {
-      const uint16_t* src = Xg + x_goff[k] + c0 * HW;
+    for (int ch = 0; ch < 8; ++ch) {
+      const uint32_t xc = (uint32_t)(c0 + ch) * (uint32_t)HW * 2u;
 #pragma unroll
-      for (int ch = 0; ch < 8; ++ch) {
+      for (int k = 0; k < XUPT; ++k) {
         if constexpr (P == 1) {
-          xreg[k][ch][0] = src[ch * HW];
+          xreg[R][k][ch][0] = __builtin_amdgcn_raw_buffer_load_b16(xr, x_off[k] + xc, 0, 0);
         } else if constexpr (P == 2) {
-          xreg[k][ch][0] = *(const uint32_t*)(src + ch * HW);
+          xreg[R][k][ch][0] = __builtin_amdgcn_raw_buffer_load_b32(xr, x_off[k] + xc, 0, 0);
         } else {
-          const u32x2_t v = *(const u32x2_t*)(src + ch * HW);
-          xreg[k][ch][0] = v[0];
-          xreg[k][ch][1] = v[1];
+          const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, x_off[k] + xc, 0, 0);
+          xreg[R][k][ch][0] = v[0];
+          xreg[R][k][ch][1] = v[1];
         }
       }
     }
   };
 
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int k = 0; k < WUPT; ++k)
+  // LDS stores of register set R into operand buffer B: piece i of NPC
+  // (weight pieces first, then one piece per pixel of each staging unit)
+  constexpr int NPC = WUPT + XUPT * P;
+  auto store_piece = [&](auto Rc, auto Bc, auto Ic) {
+    constexpr int R = decltype(Rc)::value % NSET, B = decltype(Bc)::value, I = decltype(Ic)::value;
+    if constexpr (I < WUPT) {
+      constexpr int k = I;
       if (k * kThreads + kThreads <= WU || tid + k * kThreads < WU)
-        *(u32x4_t*)(As(buf) + w_lds[k]) = ((w_ok >> k) & 1) ? wreg[k] : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int k = 0; k < XUPT; ++k) {
+        *(u32x4_t*)(As(B) + w_lds[k]) = wreg[R][k];
+    } else {
+      constexpr int k = (I - WUPT) / P, e = (I - WUPT) % P;
       if (k * kThreads + kThreads <= XU || tid + k * kThreads < XU) {
+        // pixel e of the unit: bf16 number e of each channel's loaded P
+        uint32_t d[4];
 #pragma unroll
-        for (int e = 0; e < P; ++e) {
-          // pixel e of the unit: bf16 number e of each channel's loaded P
-          uint32_t d[4];
-          const bool ok = (x_ok >> k) & 1;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = ok ? xreg[k][2 * j][e >> 1] : 0u, hi = ok ? xreg[k][2 * j + 1][e >> 1] : 0u;
-            if constexpr (P == 1) d[j] = (lo & 0xffffu) | (hi << 16);
-            else if ((e & 1) == 0) d[j] = (lo & 0xffffu) | (hi << 16);
-            else d[j] = (lo >> 16) | (hi & 0xffff0000u);
-          }
-          *(u32x4_t*)(Xs(buf) + x_lds[k] + e * ROW) = u32x4_t{d[0], d[1], d[2], d[3]};
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t lo = xreg[R][k][2 * j][e >> 1], hi = xreg[R][k][2 * j + 1][e >> 1];
+          d[j] = __builtin_amdgcn_perm(hi, lo, (P == 1 || (e & 1) == 0) ? 0x05040100u : 0x07060302u);
         }
+        *(u32x4_t*)(Xs(B) + x_lds[k] + e * ROW) = u32x4_t{d[0], d[1], d[2], d[3]};
       }
     }
   };
+  auto store_chunk = [&](auto Rc, auto Bc) {
+    static_for<NPC>([&](auto Ic) { store_piece(Rc, Bc, Ic); });
+  };
 
-  decode(u);
-  tile_offsets();
-  load_chunk(c_lo * KC);
+  // the load cursor: block-loop index of its unit, next chunk, end of the unit
+  int lu = blockIdx.x;
+  Unit cu = decode(lu);                     // the compute cursor's unit
+  int lc = cu.lo, lhi = cu.hi;
+  tile_offsets(cu.pb, cu.m0);
+  // Issue the next stream position into register set R.  With two sets a
+  // unit's first chunk always goes to set 0: when the stream would put it in
+  // set 1 (the previous unit had an odd chunk count) that position is a
+  // bubble and the unit start fills set 1 itself.  A position with nothing to load (a
+  // bubble, or past the block's last chunk) reloads the cursor's previous
+  // chunk into the free set, so that every position issues the same loads
+  // and each wait covers exactly one register set.
+  bool bubble = false;
+  auto issue = [&](auto Rc) {
+    constexpr int R = decltype(Rc)::value % NSET;
+    bool fresh = true;
+    if (lc >= lhi) {
+      const int nu = lu + (int)gridDim.x;
+      if (R == 0 && nu < units) {
+        lu = nu;
+        const Unit d = decode(nu);
+        lc = d.lo;
+        lhi = d.hi;
+        tile_offsets(d.pb, d.m0);
+      } else {
+        fresh = false;
+        if (nu < units) bubble = true;
+      }
+    }
+    load_chunk(Rc, (fresh ? lc : lc - 1) * KC);
+    if (fresh) ++lc;
+  };
+
+  // The k-steps of the chunk in LDS buffer B; with ST, register set B^1 is
+  // staged into buffer B^1 at the same time, its LDS stores spread over the
+  // k-steps and interleaved with the MFMAs (the matrix core runs while the
+  // staging instructions issue).
+  auto mfma_chunk = [&](auto Bc, auto STc) {
+    constexpr int B = decltype(Bc)::value;
+    constexpr bool ST = decltype(STc)::value;
+    std::integral_constant<int, B ^ 1> other;
+    const char* Xb = Xs(B);
+    const char* Ab = As(B);
+    u32x4_t pf[3][FP], wf[3][FC];
+    auto read_frags = [&](int s, int fb) {
+#pragma unroll
+      for (int f = 0; f < FP; ++f) pf[fb][f] = *(const u32x4_t*)(Xb + pbase + f * 32 * ROW + s * 32);
+#pragma unroll
+      for (int f = 0; f < FC; ++f) wf[fb][f] = *(const u32x4_t*)(Ab + wbase + f * 32 * ROW + s * 32);
+    };
+    read_frags(0, 0);
+    if (NS > 1) read_frags(1, 1);
+    static_for<NS>([&](auto Sc) {
+      constexpr int s = decltype(Sc)::value;
+      constexpr bool ahead = s + 2 < NS;
+      if constexpr (ahead) read_frags(s + 2, (s + 2) % 3);
+      // this step's share of the staging pieces
+      constexpr int p0 = ST ? s * NPC / NS : 0, p1 = ST ? (s + 1) * NPC / NS : 0;
+      static_for<p1 - p0>([&](auto Jc) {
+        store_piece(other, other, std::integral_constant<int, p0 + decltype(Jc)::value>{});
+      });
+#pragma unroll
+      for (int fp = 0; fp < FP; ++fp)
+#pragma unroll
+        for (int fc = 0; fc < FC; ++fc) mma32(acc[fp][fc], pf[s % 3][fp], wf[s % 3][fc]);
+      constexpr int NM = FP * FC, NR = ahead ? FP + FC : 0, NW = p1 - p0;
+      constexpr int NMAX = NM > NR ? (NM > NW ? NM : NW) : (NR > NW ? NR : NW);
+#pragma unroll
+      for (int i = 0; i < NMAX; ++i) {
+        if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
+        if (i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        if (i < NW) {
+          __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);             // a piece's VALU packing
+          __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);             // its LDS write
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  };
+
+  std::integral_constant<int, 0> s0, b0;
+  std::integral_constant<int, 1> s1, b1;
+  std::true_type stage;
+  std::false_type no_stage;
+  issue(s0);
+  if constexpr (NSET == 2) issue(s1);
   bool first_unit = true;
+  int u = blockIdx.x;
   for (;;) {
-    const int cur_pb = pb, cur_m0 = m0, cur_lo = c_lo, cur_hi = c_hi, cur_unit = unit_id;
-    const int next = u + (int)gridDim.x;
 #pragma unroll
     for (int i = 0; i < FP; ++i)
 #pragma unroll
       for (int j = 0; j < FC; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-    // the registers hold chunk cur_lo; after a chunk is stored they are
-    // refilled with the next chunk of this unit or, after its last, with the
-    // next unit's first chunk
-    auto load_after = [&](int c) {
-      if (c < cur_hi) {
-        load_chunk(c * KC);
-      } else if (next < units) {
-        decode(next);
-        tile_offsets();
-        load_chunk(c_lo * KC);
-      }
-    };
+    const int n = cu.hi - cu.lo;
+    // chunk i of the unit is in register set i % NSET and is read from LDS
+    // buffer i & 1; the loop is unrolled by two so that both are known at
+    // compile time
     __syncthreads();                 // LDS is free: previous MFMAs and epilogue are done
     if (first_unit) store_bias();
     first_unit = false;
-    store_chunk(0);
-    load_after(cur_lo + 1);
+    if (bubble) {                    // chunk 1 was not prefetched
+      bubble = false;
+      issue(s1);
+    }
+    store_chunk(s0, b0);
+    issue(s0);
     __syncthreads();
-    for (int chunk = cur_lo; chunk < cur_hi; ++chunk) {
-      const int buf = (chunk - cur_lo) & 1;
-      const char* Xb = Xs(buf);
-      const char* Ab = As(buf);
-      u32x4_t pf[3][FP], wf[3][FC];
-      auto read_frags = [&](int s, int fb) {
-#pragma unroll
-        for (int f = 0; f < FP; ++f) pf[fb][f] = *(const u32x4_t*)(Xb + pbase + f * 32 * ROW + s * 32);
-#pragma unroll
-        for (int f = 0; f < FC; ++f) wf[fb][f] = *(const u32x4_t*)(Ab + wbase + f * 32 * ROW + s * 32);
-      };
-      read_frags(0, 0);
-      if (NS > 1) read_frags(1, 1);
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bool ahead = s + 2 < NS;
-        if (ahead) read_frags(s + 2, (s + 2) % 3);
-#pragma unroll
-        for (int fp = 0; fp < FP; ++fp)
-#pragma unroll
-          for (int fc = 0; fc < FC; ++fc) mma32(acc[fp][fc], pf[s % 3][fp], wf[s % 3][fc]);
-        constexpr int NM = FP * FC, NR = FP + FC;
-#pragma unroll
-        for (int i = 0; i < (NM > NR ? NM : NR); ++i) {
-          if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
-          if (ahead && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if (chunk + 1 < cur_hi) {
-        store_chunk(buf ^ 1);        // the other buffer: its last reader finished before the previous barrier
-        load_after(chunk + 2);
-      }
+    // full iterations only reach the back edge, so that the loads in flight
+    // there are always set 1 then set 0 (a partial iteration on the back
+    // edge would make the compiler wait for both sets at every store)
+    int i = 0;
+    for (; i + 2 < n; i += 2) {
+      mfma_chunk(b0, stage);         // + chunk i+1: set 1 -> buffer 1 (its last reader passed the previous barrier)
+      issue(s1);
+      __syncthreads();
+      mfma_chunk(b1, stage);         // + chunk i+2: set 0 -> buffer 0
+      issue(s0);
       __syncthreads();
     }
+    mfma_chunk(b0, no_stage);        // the last one or two chunks
+    if (i + 1 < n) {
+      store_chunk(s1, b1);
+      issue(s1);
+      __syncthreads();
+      mfma_chunk(b1, no_stage);
+    }
+    __syncthreads();
     if (S == 1) {
-      store_tile<WM, WN, FP, FC>(a, pl, smem, Bv, acc, cur_pb * BN, cur_m0);
+      store_tile<WM, WN, FP, FC>(a, pl, smem, Bv, acc, cu.pb * BN, cu.m0);
     } else {
-      f32x4_t* dst = partial_base<FP, FC>(pl.ws, cur_unit) + tid;
+      f32x4_t* dst = partial_base<FP, FC>(pl.ws, cu.id) + tid;
 #pragma unroll
       for (int fp = 0; fp < FP; ++fp)
 #pragma unroll
@@ -361,8 +445,9 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_bf16(const ConvArgs a, co
                 f32x4_t{acc[fp][fc][4 * g], acc[fp][fc][4 * g + 1], acc[fp][fc][4 * g + 2],
                         acc[fp][fc][4 * g + 3]};
     }
-    if (next >= units) break;
-    u = next;
+    u += (int)gridDim.x;
+    if (u >= units) break;
+    cu = decode(u);
   }
 }
 

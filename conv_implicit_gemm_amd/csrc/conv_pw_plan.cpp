@@ -65,6 +65,9 @@ PwPlan make(const ConvArgs& a, int WM, int KC, int FP) {
   const int64_t units = tiles * p.splits;
   const int64_t cap = (int64_t)kCUs * per_cu;
   p.grid = (int)std::min(units, cap);
+  // OX_PW_GRID=n pins the persistent grid (blocks then run several units
+  // each: the path that crosses from one unit into the next)
+  if (const char* e = getenv("OX_PW_GRID")) p.grid = (int)std::max<int64_t>(1, std::min<int64_t>(units, atoi(e)));
   return p;
 }
 
@@ -74,10 +77,12 @@ size_t ws_bytes(const PwPlan& p) {
 }
 
 bool valid(const ConvArgs& a, const PwPlan& p) {
-  // (a 256-pixel block staging single pixels takes 32-channel chunks: the
-  // registers of 64 would spill)
-  return a.C % p.KC == 0 && p.KC <= 64 && !(p.WM == 1 && p.FP == 2 && p.P == 1 && p.KC > 32) &&
-         p.lds <= kLdsMax && (int64_t)p.npb * p.nmb * p.splits < (int64_t)1 << 31;
+  // (a block of two pixel fragments per wave staging single pixels takes
+  // 32-channel chunks: the two register sets of 64 would spill)
+  return a.C % p.KC == 0 && p.KC <= 64 && !(p.FP == 2 && p.P == 1 && p.KC > 32) &&
+         p.lds <= kLdsMax && (int64_t)p.npb * p.nmb * p.splits < (int64_t)1 << 31 &&
+         // byte offsets of the kernel's buffer loads are 32-bit
+         (int64_t)a.N * a.C * a.H * a.W * 2 < (int64_t)1 << 30 && (int64_t)a.M * a.C * 2 < (int64_t)1 << 30;
 }
 
 // Pixel fragments per wave: two (128 x 128 or 64 x 256 tiles), or one where

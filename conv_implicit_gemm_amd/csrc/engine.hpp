@@ -29,6 +29,7 @@
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
+#include <utility>
 #include <stdint.h>
 
 #include "ox_internal.h"
@@ -54,6 +55,18 @@ __device__ __forceinline__ int xcd_tile(int b, int total) {
   const int q = total / kXcds, r = total - q * kXcds;
   const int x = b % kXcds, local = b / kXcds;
   return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + local;
+}
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}):
+// a loop unrolled at compile time whose index can select registers and
+// template arguments.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // n / f.d for 0 <= n < 2^31 (see make_fastdiv)

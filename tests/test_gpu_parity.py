@@ -317,8 +317,8 @@ def test_pw_each_config(ox, plan, fp, monkeypatch):
             (2, 128, 4, 8, 96, 1, 1), (1, 256, 6, 6, 200, 2, 2), (5, 128, 3, 3, 33, 0, 3)]):
         HW = H * W
         P = 4 if HW % 4 == 0 and xoff % 4 == 0 else 2 if HW % 2 == 0 and xoff % 2 == 0 else 1
-        if plan == "1:64" and P == 1 and fp == "2":
-            continue      # that plan does not take single-pixel staging
+        if plan.endswith(":64") and P == 1 and fp == "2":
+            continue      # those plans do not take single-pixel staging
         X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
         Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
         b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
@@ -330,6 +330,34 @@ def test_pw_each_config(ox, plan, fp, monkeypatch):
         torch.cuda.synchronize()
         assert_close(host64(Y), oracle.conv2d(X, Wt, b, act="relu"), "bf16",
                      "pw %s case %d" % (plan, ci))
+
+
+@pytest.mark.parametrize("grid", ["1", "3", "8"])
+def test_pw_persistent_blocks(ox, grid, monkeypatch):
+    # a small persistent grid: every block runs many work units in a row, so
+    # the loads of a unit's first chunks are issued while the previous unit
+    # computes -- with odd and even chunk counts per unit, split-K slices and
+    # partial tiles at the end of the pixel range
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
+    monkeypatch.setenv("OX_PW_GRID", grid)
+    r = np.random.default_rng(700 + int(grid))
+    for ci, (N, Cin, H, W, M, plan, splits) in enumerate([
+            (3, 96, 9, 11, 200, "2:32", None), (2, 320, 8, 8, 70, "1:64", None),
+            (4, 128, 6, 6, 260, "2:64", None), (2, 192, 7, 7, 130, "2:64", None),
+            (2, 224, 5, 9, 96, "2:32", "3"), (3, 64, 12, 12, 300, "1:32", None)]):
+        monkeypatch.setenv("OX_PW_PLAN", plan)
+        if splits:
+            monkeypatch.setenv("OX_PW_SPLITS", splits)
+        else:
+            monkeypatch.delenv("OX_PW_SPLITS", raising=False)
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("pw persistent", grid, (N, Cin, H, W, M, plan, splits))
+        Y = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu",
+                     ws=bool(splits))
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, act="relu"), "bf16",
+                     "pw persistent grid %s case %d" % (grid, ci))
 
 
 @pytest.mark.parametrize("fp", ["1", "2"])
