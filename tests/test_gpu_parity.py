@@ -237,6 +237,41 @@ def test_depthwise_variants(ox, force, dtype, geom, monkeypatch):
     assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, pads, d, Cc, "relu6"), dtype, "dw")
 
 
+@pytest.mark.parametrize("geom", [
+    # N, C, H, W, kH, kW, stride, pads, Y offset (elements), OX_DW_TARGET
+    (1, 3, 900, 4, 3, 3, 1, (1, 1, 1, 1), 0, 4096),     # runs of 4 rows, every strip full
+    (2, 2, 600, 10, 3, 3, 1, (1, 1, 1, 1), 0, 4096),    # runs of 4 rows, partial last strips
+    (1, 2, 64, 512, 3, 3, 2, (1, 1, 1, 1), 0, 2048),    # stride 2, runs of 2 rows
+    (1, 2, 40, 256, 3, 3, 1, (1, 1, 1, 1), 0, 8192),    # strips of 8, runs of 3 rows
+    (1, 2, 40, 256, 3, 3, 1, (1, 1, 1, 1), 1, 8192),    # the same, Y one element past alignment
+    (2, 2, 40, 64, 1, 9, 1, (0, 4, 0, 4), 0, 2048),     # 1-D kernel, one window row
+    (2, 5, 21, 40, 3, 3, 1, (1, 1, 1, 1), 0, 64),       # bands of one row
+])
+def test_depthwise_sliding_strips(ox, geom, monkeypatch):
+    # one plane per block (block sizes pinned with OX_DW_TARGET): the
+    # sliding-window strips over runs of rows (the window's rows rotating
+    # through their register slots), runs that start inside a band, and the
+    # store paths with and without the all-aligned fast path; bf16 and int8
+    N, Cc, H, W, kH, kW, s, pads, yoff, target = geom
+    monkeypatch.setenv("OX_DW_TARGET", str(target))
+    say("depthwise sliding", geom)
+    r = np.random.default_rng(H * 7 + W + target)
+    X = synth.round_to(r.standard_normal((N, Cc, H, W)), "bf16")
+    Wt = synth.round_to(r.standard_normal((Cc, 1, kH, kW)) / 3.0, "bf16")
+    b = synth.round_to(r.uniform(-0.5, 0.5, Cc), "bf16")
+    ho, wo = ox.conv_out_hw(H, W, kH, kW, (s, s), pads, (1, 1))
+    Y = misaligned(nan_like((N, Cc, ho, wo), "bf16"), yoff)
+    ox.ox_conv2d_fused(dev(X, "bf16"), dev(Wt, "bf16"), dev(b, "bf16"), (s, s), pads, (1, 1), Cc, "relu6", Y=Y)
+    torch.cuda.synchronize()
+    assert_close(host64(Y), oracle.conv2d(X, Wt, b, (s, s), pads, (1, 1), Cc, "relu6"), "bf16", "dw slide")
+    conv = synth.ConvLayer("q", N, Cc, H, W, Cc, kH, s, 0, Cc, "none", kW=kW, pads=pads)
+    layer = synth.Int8Layer("q", "conv", 1, kH * kW, Cc, conv)
+    t = synth.int8_inputs(layer, 4, 80 + H + W)
+    acc, y = int8_ref(layer, t)
+    assert np.array_equal(int8_gpu(ox, layer, t, "i32").astype(np.int64), acc)
+    assert np.array_equal(int8_gpu(ox, layer, t, "i8"), y)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("geom", [
     (2, 20, 14, 14, (1, 1), 1),     # Wo = 14: rows alternate between aligned and unaligned strips
