@@ -60,6 +60,8 @@ def lib():
             "oxref_conv_out_dims": (C.c_int, [P, P, P]),
             "oxref_conv2d": (C.c_int, [P, P, P, P, C.c_int, P]),
             "oxref_conv2d_at": (C.c_int, [P, P, P, P, C.c_int, I64, P, P]),
+            "oxref_conv2d_res": (C.c_int, [P, P, P, P, P, C.c_int, P]),
+            "oxref_conv2d_res_at": (C.c_int, [P, P, P, P, P, C.c_int, I64, P, P]),
             "oxref_batchnorm": (C.c_int, [I64, I64, I64, P, P, P, P, P, D]),
             "oxref_fold_batchnorm": (C.c_int, [I64, I64, P, P, P, P, P, P, D, P, P]),
             "oxref_conv2d_int8": (C.c_int, [P, P, P, P, I32, F, P, F, I32, P, P]),
@@ -166,9 +168,11 @@ def conv_out_dims(d):
 
 
 def conv2d(X, Wt, b=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
-           group=1, act="none", at=None):
-    """ONNX Conv (direct summation) + bias + activation.  X [N,C,H,W],
-    Wt [M,C/g,kH,kW].  With ``at`` only those flat output indices."""
+           group=1, act="none", at=None, residual=None):
+    """ONNX Conv (direct summation) + bias (+ residual) + activation.
+    X [N,C,H,W], Wt [M,C/g,kH,kW]; residual, if given, has the output's
+    shape [N,M,Ho,Wo] and is added after the bias, before the activation.
+    With ``at`` only those flat output indices."""
     X = _f64(X)
     Wt = _f64(Wt)
     b = _f64(b)
@@ -178,15 +182,18 @@ def conv2d(X, Wt, b=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
     d = conv_desc(N, Cin, H, W, M, kH, kW, stride, pads, dilation, group)
     rc, Ho, Wo = conv_out_dims(d)
     _check(rc, "conv_out_dims")
+    R = _f64(residual)
+    if R is not None:
+        assert R.shape == (N, M, Ho, Wo), "residual must have the output's shape"
     L = lib()
     if at is None:
         Y = np.empty((N, M, Ho, Wo), dtype=np.float64)
-        _check(L.oxref_conv2d(C.byref(d), _p(X), _p(Wt), _p(b), ACT[act], _p(Y)), "conv2d")
+        _check(L.oxref_conv2d_res(C.byref(d), _p(X), _p(Wt), _p(b), _p(R), ACT[act], _p(Y)), "conv2d")
         return Y
     idx = np.ascontiguousarray(np.asarray(at, dtype=np.int64))
     out = np.empty(idx.size, dtype=np.float64)
-    _check(L.oxref_conv2d_at(C.byref(d), _p(X), _p(Wt), _p(b), ACT[act], idx.size, _p(idx),
-                             _p(out)), "conv2d_at")
+    _check(L.oxref_conv2d_res_at(C.byref(d), _p(X), _p(Wt), _p(b), _p(R), ACT[act], idx.size,
+                                 _p(idx), _p(out)), "conv2d_at")
     return out
 
 

@@ -181,8 +181,8 @@ static int conv_inputs(const oxref_conv* d, const double* X, const double* Wt) {
   return OXREF_OK;
 }
 
-int oxref_conv2d(const oxref_conv* d, const double* X, const double* Wt,
-                 const double* b, int act, double* Y) {
+int oxref_conv2d_res(const oxref_conv* d, const double* X, const double* Wt,
+                     const double* b, const double* R, int act, double* Y) {
   int rc = conv_inputs(d, X, Wt);
   if (rc) return rc;
   if (!act_ok(act)) return OXREF_EARG;
@@ -197,14 +197,20 @@ int oxref_conv2d(const oxref_conv* d, const double* X, const double* Wt,
             n = o / (Wo * Ho * d->M);
     double v = conv_sum(d, X, Wt, n, m, oh, ow);
     if (b) v = b[m] + v;
+    if (R) v = v + R[o];
     Y[o] = oxref_act1(act, v);
   }
   return OXREF_OK;
 }
 
-int oxref_conv2d_at(const oxref_conv* d, const double* X, const double* Wt,
-                    const double* b, int act, int64_t npts, const int64_t* idx,
-                    double* out) {
+int oxref_conv2d(const oxref_conv* d, const double* X, const double* Wt,
+                 const double* b, int act, double* Y) {
+  return oxref_conv2d_res(d, X, Wt, b, NULL, act, Y);
+}
+
+int oxref_conv2d_res_at(const oxref_conv* d, const double* X, const double* Wt,
+                        const double* b, const double* R, int act, int64_t npts,
+                        const int64_t* idx, double* out) {
   int rc = conv_inputs(d, X, Wt);
   if (rc) return rc;
   if (!act_ok(act) || npts < 0 || (npts > 0 && (!idx || !out))) return OXREF_EARG;
@@ -220,9 +226,16 @@ int oxref_conv2d_at(const oxref_conv* d, const double* X, const double* Wt,
             n = o / (Wo * Ho * d->M);
     double v = conv_sum(d, X, Wt, n, m, oh, ow);
     if (b) v = b[m] + v;
+    if (R) v = v + R[o];
     out[p] = oxref_act1(act, v);
   }
   return OXREF_OK;
+}
+
+int oxref_conv2d_at(const oxref_conv* d, const double* X, const double* Wt,
+                    const double* b, int act, int64_t npts, const int64_t* idx,
+                    double* out) {
+  return oxref_conv2d_res_at(d, X, Wt, b, NULL, act, npts, idx, out);
 }
 
 /* ------------------------------------------------------------- BatchNorm -- */

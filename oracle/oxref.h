@@ -106,6 +106,18 @@ int oxref_conv2d_at(const oxref_conv* d, const double* X, const double* Wt,
                     const double* b, int act, int64_t npts, const int64_t* idx,
                     double* out);
 
+/* The same with a residual input R of the output's shape [N, M, Ho, Wo] (or
+ * NULL), added after the bias and before the activation:
+ *   Y[o] = act((b[m] + conv sum) + R[o])
+ * -- the fused "convolution + residual + bias + relu" operation that the
+ * Kyanite README ("Cuda Executor", operator fusion) plans for cuDNN, with any
+ * of the activations here. */
+int oxref_conv2d_res(const oxref_conv* d, const double* X, const double* Wt,
+                     const double* b, const double* R, int act, double* Y);
+int oxref_conv2d_res_at(const oxref_conv* d, const double* X, const double* Wt,
+                        const double* b, const double* R, int act, int64_t npts,
+                        const int64_t* idx, double* out);
+
 /* ONNX BatchNormalization (inference), in place on Y [N, M, HW]:
  *   z = (y - mean[m]) / sqrt(var[m] + eps) * gamma[m] + beta[m]. */
 int oxref_batchnorm(int64_t N, int64_t M, int64_t HW, double* Y,

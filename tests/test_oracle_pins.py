@@ -220,6 +220,49 @@ def test_conv_sweep_against_torch_float64():
     assert ran > 300 and shaped > 10
 
 
+def test_conv_residual_against_torch_float64():
+    # the fused residual (Kyanite README, "Cuda Executor": a single
+    # convolution + residual + bias + relu operation): act(conv + b + R),
+    # against torch's float64 convolution plus the residual
+    ran = 0
+    for ci, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act) in enumerate(sweep_cases(300, 77077)):
+        desc = oracle.conv_desc(N, Cin, H, W, M, kH, kW, s, pads, d, g)
+        rc, Ho, Wo = oracle.conv_out_dims(desc)
+        if Ho < 1 or Wo < 1:
+            continue
+        r = np.random.default_rng(5000 + ci)
+        X = r.standard_normal((N, Cin, H, W))
+        Wt = r.standard_normal((M, Cin // g, kH, kW))
+        b = r.standard_normal(M)
+        R = r.standard_normal((N, M, Ho, Wo))
+        Y = oracle.conv2d(X, Wt, b, s, pads, d, g, act, residual=R)
+        ref = oracle.act(act, torch_conv(X, Wt, b, s, pads, d, g).reshape(Y.shape) + R)
+        np.testing.assert_allclose(Y, ref, rtol=1e-12, atol=1e-12,
+                                   err_msg=str((N, Cin, H, W, M, kH, kW, s, pads, d, g, act)))
+        ran += 1
+    assert ran > 150
+
+
+def test_conv_residual_special_cases():
+    # a zero residual is the plain convolution, bit for bit; zero weights give
+    # act(b + R) exactly; the sampled-point form agrees with the full one
+    r = np.random.default_rng(88)
+    X = r.standard_normal((2, 6, 7, 9))
+    Wt = r.standard_normal((5, 6, 3, 3))
+    b = r.standard_normal(5)
+    R = r.standard_normal((2, 5, 7, 9))
+    for act in ("none", "relu", "relu6", "gelu"):
+        plain = oracle.conv2d(X, Wt, b, (1, 1), (1, 1, 1, 1), act=act)
+        zero = oracle.conv2d(X, Wt, b, (1, 1), (1, 1, 1, 1), act=act, residual=np.zeros_like(R))
+        assert np.array_equal(plain, zero)
+        z = oracle.conv2d(X, np.zeros_like(Wt), b, (1, 1), (1, 1, 1, 1), act=act, residual=R)
+        assert np.array_equal(z, oracle.act(act, b[None, :, None, None] + R))
+        full = oracle.conv2d(X, Wt, b, (1, 1), (1, 1, 1, 1), act=act, residual=R)
+        idx = r.integers(0, full.size, 50)
+        at = oracle.conv2d(X, Wt, b, (1, 1), (1, 1, 1, 1), act=act, residual=R, at=idx)
+        assert np.array_equal(at, full.ravel()[idx])
+
+
 @pytest.mark.parametrize("k", [3, 7])
 def test_conv_centre_tap_is_identity(k):
     r = np.random.default_rng(k)
