@@ -26,7 +26,8 @@ STATUS_NAMES = {0: "OX_OK", 1: "OX_ERR_INVALID_ARG", 2: "OX_ERR_SHAPE",
 EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_int8",
            "ox_conv2d_variant", "ox_conv2d_fused_packed", "ox_conv2d_packed_weights_bytes",
            "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
-           "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws")
+           "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
+           "ox_conv2d_fused_res")
 
 
 class OxError(RuntimeError):
@@ -61,6 +62,7 @@ def _load():
         "ox_conv2d_packed_weights_bytes": (C.c_size_t, [I, P]),
         "ox_conv2d_workspace_bytes": (C.c_size_t, [I, P]),
         "ox_conv2d_fused_ws": (I, [I, P, P, P, I, P, I, P, P, C.c_size_t, P]),
+        "ox_conv2d_fused_res": (I, [I, P, P, P, P, P, I, P, P, C.c_size_t, P]),
         "ox_conv2d_pack_weights": (I, [I, P, P, P]),
         "ox_fold_batchnorm": (I, [I64, I64, P, P, P, P, P, P, F, P, P]),
         "ox_int8_params_bytes": (C.c_size_t, [I64]),
@@ -207,6 +209,28 @@ def ox_conv2d_fused(X, W, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=
     else:
         _check(lib.ox_conv2d_fused(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), ACT[act],
                                    _ptr(Y), _stream(stream)))
+    return Y
+
+
+def ox_conv2d_fused_res(X, W, R, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
+                        group=1, act="none", Y=None, stream=None, workspace=None):
+    """ONNX Conv + bias + residual R (the output's shape) + activation, fused:
+    Y = act(conv(X, W) + bias + R).  Y may be R itself (in place)."""
+    torch = _torch()
+    for t, n in ((X, "X"), (W, "W"), (R, "R"), (bias, "bias"), (Y, "Y")):
+        _dense(t, n)
+    N, Cin, H, Wd = X.shape
+    M, _, kH, kW = W.shape
+    d = conv_desc(N, Cin, H, Wd, M, kH, kW, stride, pads, dilation, group)
+    if Y is None:
+        ho, wo = conv_out_hw(H, Wd, kH, kW, stride, pads, dilation)
+        Y = torch.empty((N, M, max(ho, 0), max(wo, 0)), dtype=X.dtype, device=X.device)
+    nbytes = 0
+    if workspace is not None:
+        _dense(workspace, "workspace")
+        nbytes = workspace.numel() * workspace.element_size()
+    _check(lib.ox_conv2d_fused_res(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), _ptr(R),
+                                   ACT[act], _ptr(Y), _ptr(workspace), nbytes, _stream(stream)))
     return Y
 
 

@@ -32,6 +32,81 @@ namespace ox {
 
 namespace pw {
 
+// The epilogue with a residual input R (Y's shape and type): the tile's fp32
+// values acc + bias are staged in LDS as [channel][pixel], then each
+// channel's run of V pixels is read back, R's matching run added (one vector
+// load, coalesced along the plane), the activation applied and the result
+// stored: Y = act((acc + bias) + R).  R may be Y itself (each element is
+// read before it is written, by the same thread).  The caller has
+// synchronised the block: LDS is free.
+template <int WM, int WN, int FP, int FC>
+__device__ __forceinline__ void store_tile_res(const ConvArgs& a, const PwPlan& pl, char* smem,
+                                               const float (&bv)[FC], const f32x16_t (&acc)[FP][FC],
+                                               int q0, int m0) {
+  constexpr int BM = 32 * WM * FC, BN = 32 * WN * FP;
+  constexpr int EROW = BN + 4;             // floats per staged channel row
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+  const int l32 = lane & 31, kg = lane >> 5;
+  const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
+  float* E = (float*)smem;
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) {
+    const int ml = wm * FC * 32 + fc * 32 + l32;
+#pragma unroll
+    for (int fp = 0; fp < FP; ++fp) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int slot = (wn * FP + fp) * 32 + 8 * g + 4 * kg;
+        const f32x16_t& c = acc[fp][fc];
+        *(f32x4_t*)(E + ml * EROW + slot) =
+            f32x4_t{c[4 * g] + bv[fc], c[4 * g + 1] + bv[fc], c[4 * g + 2] + bv[fc], c[4 * g + 3] + bv[fc]};
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* Y = (uint16_t*)a.Y;
+  const uint16_t* R = (const uint16_t*)a.res;
+  const int mvalid = min(BM, M - m0);
+  const int V = pl.V;                      // HW % V == 0, Y and R 2V-byte aligned
+  const int per_row = BN / V;
+  const int items = mvalid * per_row;
+  with_act(a.act, [&](auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
+    for (int it = tid; it < items; it += kThreads) {
+      const int m = it / per_row;
+      const int e = (it - m * per_row) * V;
+      const int q = q0 + e;
+      if (q >= Q) continue;
+      const int n = q / HW;
+      const int64_t off = ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
+      const float* src = E + m * EROW + e;
+      // two residual values per 32-bit word: low half first
+      auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
+      auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
+      auto out2 = [&](float x0, float x1, uint32_t r) {
+        return pack_bf16x2(act_c<ACT>(x0 + lo(r)), act_c<ACT>(x1 + hi(r)));
+      };
+      if (V == 8) {
+        const u32x4_t r = *(const u32x4_t*)(R + off);
+        const f32x4_t s0 = *(const f32x4_t*)src, s1 = *(const f32x4_t*)(src + 4);
+        *(u32x4_t*)(Y + off) = u32x4_t{out2(s0[0], s0[1], r[0]), out2(s0[2], s0[3], r[1]),
+                                       out2(s1[0], s1[1], r[2]), out2(s1[2], s1[3], r[3])};
+      } else if (V == 4) {
+        const u32x2_t r = *(const u32x2_t*)(R + off);
+        const f32x4_t s0 = *(const f32x4_t*)src;
+        *(u32x2_t*)(Y + off) = u32x2_t{out2(s0[0], s0[1], r[0]), out2(s0[2], s0[3], r[1])};
+      } else if (V == 2) {
+        const uint32_t r = *(const uint32_t*)(R + off);
+        *(uint32_t*)(Y + off) = out2(src[0], src[1], r);
+      } else {
+        Y[off] = f32_to_bf16(act_c<ACT>(src[0] + bf16_to_f32(R[off])));
+      }
+    }
+  });
+}
+
 // Bias, activation and bf16 conversion of one tile held in the MFMA
 // accumulators of the block's four waves, staged through LDS and stored as
 // channel runs.  Lane (l32, kg) of wave (wm, wn) holds, for each (fp, fc),
@@ -54,6 +129,10 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
   for (int fc = 0; fc < FC; ++fc) {
     const int m = m0 + wm * FC * 32 + fc * 32 + l32;
     bv[fc] = (Bv && m < M) ? bf16_to_f32(Bv[m]) : 0.0f;
+  }
+  if (a.res) {
+    store_tile_res<WM, WN, FP, FC>(a, pl, smem, bv, acc, q0, m0);
+    return;
   }
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
@@ -482,6 +561,7 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
   const int q0 = pb * BN + wn * SUBN, m0 = (t - pb * pl.nmb) * BM + wm * SUBM;
   const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
   const uint16_t* bias = (const uint16_t*)a.bias;
+  const uint16_t* R = (const uint16_t*)a.res;   // residual, added after the bias
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
@@ -490,8 +570,19 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
       const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
       const int m = m0 + fc * 32 + l32;
       const float bv = (bias && m < M) ? bf16_to_f32(bias[m]) : 0.0f;
-      const uint32_t lo = pack_bf16x2(act_c<ACT>(sum[k][0] + bv), act_c<ACT>(sum[k][1] + bv));
-      const uint32_t hi = pack_bf16x2(act_c<ACT>(sum[k][2] + bv), act_c<ACT>(sum[k][3] + bv));
+      float v[4] = {sum[k][0] + bv, sum[k][1] + bv, sum[k][2] + bv, sum[k][3] + bv};
+      if (R && m < M) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = q0 + fp * 32 + 8 * g + 4 * kg + j;
+          if (q < Q) {
+            const int n = q / HW;
+            v[j] += bf16_to_f32(R[((int64_t)n * M + m) * HW + (q - n * HW)]);
+          }
+        }
+      }
+      const uint32_t lo = pack_bf16x2(act_c<ACT>(v[0]), act_c<ACT>(v[1]));
+      const uint32_t hi = pack_bf16x2(act_c<ACT>(v[2]), act_c<ACT>(v[3]));
       *(u32x2_t*)(E + (fc * 32 + l32) * EROW + fp * 32 + 8 * g + 4 * kg) = u32x2_t{lo, hi};
     }
   });

@@ -32,8 +32,9 @@ PwPlan make(const ConvArgs& a, int WM, int KC, int FP) {
   const int HW = a.H * a.W;
   const uintptr_t xa = (uintptr_t)a.X, ya = (uintptr_t)a.Y;
   p.P = (HW % 4 == 0 && xa % 8 == 0) ? 4 : (HW % 2 == 0 && xa % 4 == 0) ? 2 : 1;
+  const uintptr_t ra = (uintptr_t)a.res;     // residual (0: none), read in runs like Y
   p.V = 8;
-  while (p.V > 1 && (HW % p.V || ya % (2 * p.V))) p.V >>= 1;
+  while (p.V > 1 && (HW % p.V || ya % (2 * p.V) || ra % (2 * p.V))) p.V >>= 1;
   const int BM = 64 * WM, BN = 32 * (4 / WM) * FP;
   const int64_t Q = (int64_t)a.N * HW;
   p.npb = (int)((Q + BN - 1) / BN);
@@ -43,6 +44,7 @@ PwPlan make(const ConvArgs& a, int WM, int KC, int FP) {
   // (raw bf16 words from its aligned-down address)
   p.bias_lds = ((2 * a.M + 3 + 3) / 4 * 4 + 15) / 16 * 16;
   p.lds = std::max(2 * (BM + BN) * row, BM * (BN + 8) * 2) + p.bias_lds;
+  if (a.res) p.lds = std::max(p.lds, BM * (BN + 4) * 4 + p.bias_lds);   // fp32 staging of the residual epilogue
   // split-K when the tiles alone would leave many CUs idle and the channel
   // range is long: about 192 work units of at least four chunks (a sweep
   // of the ResNet-50 1x1 layers at batch 32: two slices for 98 tiles x 16

@@ -212,15 +212,18 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
   } else {
     T* Y = (T*)a.Y;
     const T* bias = (const T*)a.bias;
+    const T* R = (const T*)a.res;     // residual, added after the bias (may be Y itself)
     with_act(a.act, [&](auto act_k) {
       constexpr int ACT = decltype(act_k)::value;
       for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
         const int ml = row0 + r, col = col0 + c;
         if (ml < Mpg && col < NP) {
           const int m = g * Mpg + ml;
+          const int64_t o_idx = out_index(m, col);
           float o = v;
           if (bias) o += to_f32(bias[m]);
-          store_float(Y + out_index(m, col), act_c<ACT>(o));
+          if (R) o += to_f32(R[o_idx]);
+          store_float(Y + o_idx, act_c<ACT>(o));
         }
       });
     });

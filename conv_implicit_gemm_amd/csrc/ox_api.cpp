@@ -226,7 +226,9 @@ const char* kind_name(int k) {
 ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, const Force& f,
                       int* kind) {
   if (a.w_packed) {
-    // packed weights exist only for the LDS-patch kernel
+    // packed weights exist only for the LDS-patch kernel (which takes no residual)
+    if (a.res)
+      return fail(OX_ERR_UNSUPPORTED, "%s: packed weights do not take a residual input", fn);
     if (f.variant && strcmp(f.variant, "patch"))
       return fail(OX_ERR_UNSUPPORTED, "%s: OX_FORCE_KERNEL variant '%s' does not take packed weights", fn,
                   f.variant);
@@ -267,6 +269,15 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
       return fail(OX_ERR_INVALID_ARG, "%s: OX_FORCE_KERNEL variant '%s' does not apply to Conv", fn,
                   f.variant);
     }
+    if (a.res && *kind != KIND_PW && *kind != KIND_1X1 && *kind != KIND_IGEMM)
+      return fail(OX_ERR_UNSUPPORTED, "%s: forced '%s' does not take a residual input", fn, f.variant);
+    return OX_OK;
+  }
+  if (a.res) {
+    // a residual input: the kernels whose epilogue reads it are the
+    // pointwise kernel and the tile engine (any geometry)
+    if (is_1x1) *kind = conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
+    else *kind = KIND_IGEMM;
     return OX_OK;
   }
   if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
@@ -574,10 +585,10 @@ size_t ox_conv2d_workspace_bytes(ox_dtype t, const ox_conv_desc* d) {
   return kind == KIND_PW ? conv_pw_ws_bytes(a) : kind == KIND_PATCH ? conv_patch_ws_bytes(a) : 0;
 }
 
-ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
-                             int w_packed, const void* bias, ox_act act, void* Y, void* workspace,
-                             size_t workspace_bytes, void* stream) {
-  const char* fn = "ox_conv2d_fused_ws";
+static ox_status conv_fused_ws_res(const char* fn, ox_dtype t, const ox_conv_desc* d, const void* X,
+                                   const void* W, int w_packed, const void* bias, const void* R,
+                                   ox_act act, void* Y, void* workspace, size_t workspace_bytes,
+                                   void* stream) {
   ox_status st = check_float_dt(fn, t);
   if (st) return st;
   st = check_act(fn, act);
@@ -585,6 +596,8 @@ ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, c
   if (w_packed != 0 && w_packed != 1) return fail(OX_ERR_INVALID_ARG, "%s: w_packed=%d is not 0 or 1", fn, w_packed);
   if (workspace && ((uintptr_t)workspace) % 16)
     return fail(OX_ERR_INVALID_ARG, "%s: workspace is not 16-byte aligned", fn);
+  if (R && ((uintptr_t)R) % (t == OX_F32 ? 4 : 2))
+    return fail(OX_ERR_INVALID_ARG, "%s: R is not aligned to its element size", fn);
   int64_t Ho, Wo;
   st = check_conv_desc(fn, d, &Ho, &Wo);
   if (st) return st;
@@ -597,7 +610,22 @@ ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, c
   a.w_packed = w_packed;
   a.ws = workspace;
   a.ws_bytes = workspace ? workspace_bytes : 0;
+  a.res = R;
   return conv_dispatch(fn, d, a, stream);
+}
+
+ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                             int w_packed, const void* bias, ox_act act, void* Y, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return conv_fused_ws_res("ox_conv2d_fused_ws", t, d, X, W, w_packed, bias, nullptr, act, Y, workspace,
+                           workspace_bytes, stream);
+}
+
+ox_status ox_conv2d_fused_res(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                              const void* bias, const void* R, ox_act act, void* Y, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  return conv_fused_ws_res("ox_conv2d_fused_res", t, d, X, W, 0, bias, R, act, Y, workspace,
+                           workspace_bytes, stream);
 }
 
 ox_status ox_conv2d_int8(const ox_conv_desc* d, const int8_t* Xq, const int8_t* Wq,

@@ -88,6 +88,7 @@ struct ConvArgs {
   int w_packed;           // Wt is in the packed tap-major layout (see ox_conv2d_pack_weights)
   void* ws;               // caller's scratch for split-K partials, or null (no split-K)
   size_t ws_bytes;        // its size
+  const void* res;        // residual [N, M, Ho, Wo] of Y's type, added before the activation, or null
 };
 
 // Division by a divisor fixed for a launch (0 <= n < 2^31, 1 <= d < 2^31):

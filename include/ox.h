@@ -171,6 +171,29 @@ ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, c
                              int w_packed, const void* bias, ox_act act, void* Y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* Conv + bias + residual + activation, fused:
+ *   Y[n,m,oh,ow] = act((conv(X, W)[n,m,oh,ow] + bias[m]) + R[n,m,oh,ow])
+ * the single "convolution + residual + bias + relu" operation that the
+ * Kyanite README (section "Cuda Executor", operator fusion) plans for a
+ * residual block, here with any activation: an ONNX Conv whose output feeds
+ * an Add with a tensor of its own shape, then the activation.  With BatchNorm
+ * folded into W and bias this is the end of a ResNet bottleneck (conv, BN,
+ * + shortcut, ReLU) or of a MobileNetV2 stride-1 block (act = OX_ACT_NONE).
+ * t: OX_F32 or OX_BF16; X, W (ONNX layout), bias, R and Y all of type t.
+ * R: DEVICE, dense [N, M, Ho, Wo] like Y, aligned to its element size; it may
+ * be Y itself (the residual is then replaced by the result); any other
+ * overlap of R or Y with the inputs is undefined.  R = NULL is
+ * ox_conv2d_fused_ws.  The 1x1 convolutions run on the pointwise kernel, all
+ * other geometries on the implicit-GEMM tile engine (the LDS-patch,
+ * depthwise and few-channel kernels take no residual).  workspace: as for
+ * ox_conv2d_fused_ws (ox_conv2d_workspace_bytes(t, d) bytes suffice).
+ * Errors as ox_conv2d_fused_ws, plus OX_ERR_INVALID_ARG for a misaligned R
+ * and OX_ERR_UNSUPPORTED when OX_FORCE_KERNEL names a kernel without a
+ * residual epilogue. */
+ox_status ox_conv2d_fused_res(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                              const void* bias, const void* R, ox_act act, void* Y, void* workspace,
+                              size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------- offline, host, untimed */
 
 /* Size in bytes of the packed weights of a convolution, or 0 when this

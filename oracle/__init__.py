@@ -135,6 +135,8 @@ def gemm(A, B, bias=None, alpha=1.0, beta=1.0, transA=False, transB=False,
     M = A.shape[1] if transA else A.shape[0]
     K = A.shape[0] if transA else A.shape[1]
     N = B.shape[0] if transB else B.shape[1]
+    assert (B.shape[1] if transB else B.shape[0]) == K, "A and B disagree on K"
+    assert bias is None or bias.shape == (N,), "bias must have N elements"
     L = lib()
     if at is None:
         Y = np.empty((M, N), dtype=np.float64)

@@ -167,6 +167,25 @@ def test_workspace_entry_point(ox):
     assert f(ox.OX_I8, C.byref(d), FAKE, FAKE, 0, None, 0, FAKE, FAKE, need, None) == 3
 
 
+def test_residual_entry_point_errors(ox, monkeypatch):
+    # the fused residual call validates before anything is enqueued: dtype,
+    # the residual's alignment, forced kernels without a residual epilogue
+    L = raw(ox)
+    f = L.ox_conv2d_fused_res
+    d = ox.conv_desc(2, 64, 8, 8, 64, 3, 3, (1, 1), (1, 1, 1, 1))
+    assert f(ox.OX_I8, C.byref(d), FAKE, FAKE, None, FAKE, 0, FAKE, None, 0, None) == 3
+    assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, None, FAKE + 1, 0, FAKE, None, 0, None) == 1
+    assert "R is not aligned" in ox.ox_last_error()
+    assert f(ox.OX_F32, C.byref(d), FAKE, FAKE, None, FAKE + 2, 0, FAKE, None, 0, None) == 1
+    assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, None, FAKE, 7, FAKE, None, 0, None) == 1
+    assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, None, FAKE, 0, None, None, 0, None) == 1
+    assert "Y is NULL" in ox.ox_last_error()
+    for v in ("patch", "dw", "smallc"):
+        monkeypatch.setenv("OX_FORCE_KERNEL", v)
+        assert f(ox.OX_BF16, C.byref(d), FAKE, FAKE, None, FAKE, 0, FAKE, None, 0, None) == 3
+    monkeypatch.delenv("OX_FORCE_KERNEL")
+
+
 def test_gemm_argument_errors(ox):
     L = raw(ox)
     g = L.ox_gemm_fused

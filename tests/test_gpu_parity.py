@@ -777,3 +777,84 @@ def test_c3_resnet50_3x3_packed(ox, N):
         idx = sample_indices(got.size, 4096 if N > 1 else got.size, li)
         ref = oracle.conv2d(X, Wt, b, s, layer.onnx_pads, (1, 1), 1, layer.act, at=idx)
         assert_close(got[idx], ref, "bf16", layer.name)
+
+
+# ------------------------------------------------------------- residual --
+
+def run_conv_res(ox, X, Wt, b, Rr, dtype, s, pads, d, g, act, ws=False, in_place=False, roff=0):
+    """ox_conv2d_fused_res on device copies; Rr is the residual (float64 of
+    values exact in dtype).  in_place: Y is the residual tensor itself;
+    roff: R (and Y) sit roff elements past an aligned pointer."""
+    Rd = misaligned(dev(Rr, dtype), roff) if roff else dev(Rr, dtype)
+    Y = Rd if in_place else misaligned(nan_like(Rr.shape, dtype), roff)
+    wsb = workspace_for(ox, dtype, *X.shape, Wt.shape[0], Wt.shape[2], Wt.shape[3], s, pads, d, g) if ws else None
+    ox.ox_conv2d_fused_res(dev(X, dtype), dev(Wt, dtype), Rd, None if b is None else dev(b, dtype),
+                           s, pads, d, g, act, Y=Y, workspace=wsb)
+    torch.cuda.synchronize()
+    return Y
+
+
+@pytest.mark.parametrize("grid", [None, "3"])
+def test_residual_pointwise(ox, grid, monkeypatch):
+    # the pointwise kernel's residual epilogue (fp32 staging, R read in runs
+    # of V pixels): every activation, ragged tiles, split-K (the residual is
+    # added in the second pass), a persistent grid, R one element off
+    # alignment (V = 1), and R = Y in place
+    if grid:
+        monkeypatch.setenv("OX_PW_GRID", grid)
+    r = np.random.default_rng(4040 + (3 if grid else 0))
+    cases = [(2, 64, 8, 8, 96, "relu", False, 0, False), (3, 128, 7, 7, 130, "relu6", False, 0, False),
+             (1, 256, 6, 10, 64, "gelu", True, 0, False), (2, 96, 9, 9, 70, "none", False, 1, False),
+             (2, 128, 8, 8, 128, "relu", False, 0, True), (1, 512, 7, 7, 200, "relu", True, 0, True)]
+    for ci, (N, Cin, H, W, M, act, ws, roff, in_place) in enumerate(cases):
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        Rr = synth.round_to(r.standard_normal((N, M, H, W)), "bf16")
+        assert ox.ox_conv2d_variant("bf16", N, Cin, H, W, M, 1, 1).startswith("pw")
+        say("residual pw", grid, (N, Cin, H, W, M, act, ws, roff, in_place))
+        Y = run_conv_res(ox, X, Wt, b, Rr, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, act, ws=ws,
+                         in_place=in_place, roff=roff)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, act=act, residual=Rr), "bf16",
+                     "residual pw case %d" % ci)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_residual_tile_engine(ox, dtype):
+    # every other geometry takes the tile engine's epilogue: 3x3, strided,
+    # dilated, grouped, depthwise, a C that is not a multiple of 32, fp32 1x1
+    r = np.random.default_rng(5151)
+    cases = [(2, 32, 9, 11, 40, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1, "relu"),
+             (1, 24, 13, 13, 24, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 24, "relu6"),
+             (2, 16, 10, 8, 32, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2), 4, "gelu"),
+             (3, 40, 6, 7, 70, 1, 1, (1, 1), (0, 0, 0, 0), (1, 1), 1, "none"),
+             (1, 3, 20, 20, 16, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1), 1, "relu")]
+    for ci, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act) in enumerate(cases):
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), dtype)
+        Wt = synth.round_to(r.standard_normal((M, Cin // g, kH, kW)) / math.sqrt(kH * kW * Cin // g), dtype)
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), dtype)
+        ho, wo = ox.conv_out_hw(H, W, kH, kW, s, pads, d)
+        Rr = synth.round_to(r.standard_normal((N, M, ho, wo)), dtype)
+        say("residual engine", dtype, (N, Cin, H, W, M, kH, kW, s, pads, d, g, act))
+        Y = run_conv_res(ox, X, Wt, b, Rr, dtype, s, pads, d, g, act, in_place=(ci == 1))
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, pads, d, g, act, residual=Rr), dtype,
+                     "residual engine case %d" % ci)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_c3_resnet50_bottleneck_residual(ox, dtype):
+    # the bottleneck's last 1x1 (C/4 -> C) with the block input as residual
+    # and ReLU, at batch 32 (sampled comparison)
+    for li, layer in enumerate(synth.resnet50_layers(32)):
+        if not layer.name.endswith("1x1b"):
+            continue
+        X, Wt, b = conv_layer_tensors(layer, 3, li, dtype)
+        Rr = synth.round_to(np.random.default_rng([7, li]).standard_normal((layer.N, layer.M, layer.H, layer.W)),
+                            dtype)
+        say("C3 residual", dtype, layer.name)
+        Y = run_conv_res(ox, X, Wt, b, Rr, dtype, (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu", ws=True)
+        assert not torch.isnan(Y).any().item(), layer.name
+        got = host64(Y).ravel()
+        idx = sample_indices(got.size, 4096, li)
+        ref = oracle.conv2d(X, Wt, b, act="relu", residual=Rr, at=idx)
+        assert_close(got[idx], ref, dtype, layer.name)
