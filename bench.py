@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
     p.add_argument("--rows", default=None, help="write per-layer rows as JSON to this file")
+    p.add_argument("--residual", action="store_true",
+                   help="resnet50 / mobilenetv2: the block-closing convolutions add a residual "
+                        "input before their activation (ox_conv2d_fused_res)")
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run 10 plain device copies of this many bytes (the reference "
                         "reading for HBM byte counters), then exit")
@@ -58,7 +61,9 @@ class Layer:
         self.nout, self.kred = nout, kred
 
 
-def conv_layers(ox, synth, torch, cfg, layers, dtype, stream):
+def conv_layers(ox, synth, torch, cfg, layers, dtype, stream, residual=()):
+    """residual: names of layers that add a residual input (the tensor of the
+    output's shape) before their activation, through ox_conv2d_fused_res."""
     import oracle
     tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
     out = []
@@ -104,20 +109,34 @@ def conv_layers(ox, synth, torch, cfg, layers, dtype, stream):
                     1 if fn is ox.lib.ox_conv2d_fused_packed else 0, bd.data_ptr(), act,
                     Yd.data_ptr(), ws.data_ptr(), wsb, stream)
             fn = ox.lib.ox_conv2d_fused_ws
+        nbytes = l.nbytes(ESIZE[dtype])
+        R64, Rd = None, None
+        if l.name in residual:
+            # a residual of the output's shape (seeded; the shortcut of a
+            # bottleneck), read once more from HBM
+            R64 = synth.round_to(synth.rng(cfg, li, 9).standard_normal((l.N, l.M, ho, wo)), dtype)
+            Rd = torch.from_numpy(R64.astype(np.float32)).cuda().to(tdt)
+            variant = ox.ox_conv2d_variant(dtype, l.N, l.C, l.H, l.W, l.M, l.kh, l.kw,
+                                           (l.stride, l.stride), l.onnx_pads, (1, 1), l.group) + "+res"
+            args = (code, C.byref(d), Xd.data_ptr(), Wd.data_ptr(), bd.data_ptr(), Rd.data_ptr(), act,
+                    Yd.data_ptr(), ws.data_ptr() if ws is not None else None, wsb if ws is not None else 0,
+                    stream)
+            fn = ox.lib.ox_conv2d_fused_res
+            nbytes += Rd.numel() * Rd.element_size()
         # the oracle reads the bits the GPU reads: X as rounded, W' and b' as
         # the device holds them
         Wh = Wd.float().cpu().numpy().astype(np.float64)
         bh = bd.float().cpu().numpy().astype(np.float64)
-        keep = (Xd, Wd, Wlaunch, bd, Yd, d, ws)
+        keep = (Xd, Wd, Wlaunch, bd, Yd, d, ws, Rd)
 
         def launch(fn=fn, args=args, keep=keep):
             return fn(*args)
 
-        def oracle_at(idx, X64=X64, Wh=Wh, bh=bh, l=l):
+        def oracle_at(idx, X64=X64, Wh=Wh, bh=bh, l=l, R64=R64):
             return oracle.conv2d(X64, Wh, bh, (l.stride, l.stride), l.onnx_pads, (1, 1), l.group,
-                                 l.act, at=idx)
+                                 l.act, at=idx, residual=R64)
         kred = (l.C // l.group) * l.kh * l.kw
-        out.append(Layer(l.name, l.flops(), l.nbytes(ESIZE[dtype]), variant, launch, oracle_at,
+        out.append(Layer(l.name, l.flops(), nbytes, variant, launch, oracle_at,
                          l.N * l.M * ho * wo, kred))
     return out
 
@@ -324,15 +343,25 @@ def main():
     if wl == "resnet50":
         dtype = args.dtype or "bf16"
         batch = args.batch or 32
-        layers = conv_layers(ox, synth, torch, 3, synth.resnet50_layers(batch), dtype, sp)
+        res = [l.name for l in synth.resnet50_layers(batch) if l.name.endswith("1x1b")] if args.residual else []
+        layers = conv_layers(ox, synth, torch, 3, synth.resnet50_layers(batch), dtype, sp, res)
         cfg = {"workload": "resnet50-v2 convolutions (16 layers), NCHW", "batch": batch,
                "input": "3x224x224", "epilogue": "folded BN bias + ReLU"}
+        if res:
+            cfg["residual"] = "the last 1x1 of each stage adds a residual before its ReLU"
     elif wl == "mobilenetv2":
         dtype = args.dtype or "f32"
         batch = args.batch or 64
-        layers = conv_layers(ox, synth, torch, 2, synth.mobilenetv2_layers(batch), dtype, sp)
+        mb = synth.mobilenetv2_layers(batch)
+        # the stride-1 blocks whose input and output widths agree close with
+        # a residual add after their (linear) projection
+        res = [mb[i].name for i in range(len(mb)) if args.residual and mb[i].name.endswith("project")
+               and not mb[i].name.endswith(".0.project")] if args.residual else []
+        layers = conv_layers(ox, synth, torch, 2, mb, dtype, sp, res)
         cfg = {"workload": "mobilenetv2 convolutions (51 layers), NCHW", "batch": batch,
                "input": "3x224x224", "epilogue": "folded BN bias + ReLU6 / linear"}
+        if res:
+            cfg["residual"] = "the projection of each repeated block adds a residual"
     elif wl == "mlp":
         dtype = args.dtype or "bf16"
         layers = gemm_layers(ox, synth, torch, synth.mlp_rows(), dtype, sp)

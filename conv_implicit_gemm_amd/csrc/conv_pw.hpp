@@ -69,40 +69,70 @@ __device__ __forceinline__ void store_tile_res(const ConvArgs& a, const PwPlan& 
   uint16_t* Y = (uint16_t*)a.Y;
   const uint16_t* R = (const uint16_t*)a.res;
   const int mvalid = min(BM, M - m0);
-  const int V = pl.V;                      // HW % V == 0, Y and R 2V-byte aligned
-  const int per_row = BN / V;
-  const int items = mvalid * per_row;
-  with_act(a.act, [&](auto act_k) {
-    constexpr int ACT = decltype(act_k)::value;
-    for (int it = tid; it < items; it += kThreads) {
-      const int m = it / per_row;
-      const int e = (it - m * per_row) * V;
-      const int q = q0 + e;
-      if (q >= Q) continue;
-      const int n = q / HW;
-      const int64_t off = ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
-      const float* src = E + m * EROW + e;
-      // two residual values per 32-bit word: low half first
-      auto lo = [](uint32_t w) { return __uint_as_float(w << 16); };
-      auto hi = [](uint32_t w) { return __uint_as_float(w & 0xffff0000u); };
-      auto out2 = [&](float x0, float x1, uint32_t r) {
-        return pack_bf16x2(act_c<ACT>(x0 + lo(r)), act_c<ACT>(x1 + hi(r)));
-      };
-      if (V == 8) {
-        const u32x4_t r = *(const u32x4_t*)(R + off);
-        const f32x4_t s0 = *(const f32x4_t*)src, s1 = *(const f32x4_t*)(src + 4);
-        *(u32x4_t*)(Y + off) = u32x4_t{out2(s0[0], s0[1], r[0]), out2(s0[2], s0[3], r[1]),
-                                       out2(s1[0], s1[1], r[2]), out2(s1[2], s1[3], r[3])};
-      } else if (V == 4) {
-        const u32x2_t r = *(const u32x2_t*)(R + off);
-        const f32x4_t s0 = *(const f32x4_t*)src;
-        *(u32x2_t*)(Y + off) = u32x2_t{out2(s0[0], s0[1], r[0]), out2(s0[2], s0[3], r[1])};
-      } else if (V == 2) {
-        const uint32_t r = *(const uint32_t*)(R + off);
-        *(uint32_t*)(Y + off) = out2(src[0], src[1], r);
-      } else {
-        Y[off] = f32_to_bf16(act_c<ACT>(src[0] + bf16_to_f32(R[off])));
+  const int per_row_v = BN / pl.V;
+  const int items = mvalid * per_row_v;
+  // Runs are handled 4 per thread at a time: the 4 residual loads are all
+  // issued before the first store (R may be Y itself, so the compiler could
+  // not move a load above an earlier store on its own).
+  auto run = [&](auto Vc, auto act_k) {
+    constexpr int V = decltype(Vc)::value, ACT = decltype(act_k)::value;
+    constexpr int NW = V >= 2 ? V / 2 : 1;          // 32-bit residual words per run
+    constexpr int G = 4;
+    const int per_row = BN / V;
+    for (int base = tid; base < items; base += G * kThreads) {
+      uint32_t rw[G][NW];
+      int off[G];                                   // (the plan keeps Y below 2^31 elements)
+      int srcv[G];
+      bool ok[G];
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        const int it = base + u * kThreads;
+        const int m = it / per_row;
+        const int e = (it - m * per_row) * V;
+        const int q = q0 + e;
+        ok[u] = it < items && q < Q;
+        const int n = ok[u] ? q / HW : 0;
+        off[u] = ok[u] ? (n * M + m0 + m) * HW + (q - n * HW) : 0;
+        srcv[u] = m * EROW + e;
+        if constexpr (V == 8) {
+          const u32x4_t r = ok[u] ? *(const u32x4_t*)(R + off[u]) : u32x4_t{0u, 0u, 0u, 0u};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) rw[u][j] = r[j];
+        } else if constexpr (V == 4) {
+          const u32x2_t r = ok[u] ? *(const u32x2_t*)(R + off[u]) : u32x2_t{0u, 0u};
+          rw[u][0] = r[0];
+          rw[u][1] = r[1];
+        } else if constexpr (V == 2) {
+          rw[u][0] = ok[u] ? *(const uint32_t*)(R + off[u]) : 0u;
+        } else {
+          rw[u][0] = ok[u] ? (uint32_t)R[off[u]] : 0u;
+        }
       }
+#pragma unroll
+      for (int u = 0; u < G; ++u) {
+        if (!ok[u]) continue;
+        const float* src = E + srcv[u];
+        if constexpr (V == 1) {
+          Y[off[u]] = f32_to_bf16(act_c<ACT>(src[0] + __uint_as_float(rw[u][0] << 16)));
+        } else {
+          uint32_t o[NW];
+#pragma unroll
+          for (int j = 0; j < NW; ++j)
+            o[j] = pack_bf16x2(act_c<ACT>(src[2 * j] + __uint_as_float(rw[u][j] << 16)),
+                               act_c<ACT>(src[2 * j + 1] + __uint_as_float(rw[u][j] & 0xffff0000u)));
+          if constexpr (V == 8) *(u32x4_t*)(Y + off[u]) = u32x4_t{o[0], o[1], o[2], o[3]};
+          else if constexpr (V == 4) *(u32x2_t*)(Y + off[u]) = u32x2_t{o[0], o[1]};
+          else *(uint32_t*)(Y + off[u]) = o[0];
+        }
+      }
+    }
+  };
+  with_act(a.act, [&](auto act_k) {
+    switch (pl.V) {                        // HW % V == 0, Y and R 2V-byte aligned
+      case 8: run(std::integral_constant<int, 8>{}, act_k); break;
+      case 4: run(std::integral_constant<int, 4>{}, act_k); break;
+      case 2: run(std::integral_constant<int, 2>{}, act_k); break;
+      default: run(std::integral_constant<int, 1>{}, act_k); break;
     }
   });
 }
@@ -112,7 +142,7 @@ __device__ __forceinline__ void store_tile_res(const ConvArgs& a, const PwPlan& 
 // channel runs.  Lane (l32, kg) of wave (wm, wn) holds, for each (fp, fc),
 // channel 32*(wm*FC + fc) + l32 at pixel slots 32*(wn*FP + fp) + 8*g + 4*kg
 // + (0..3).  The caller has synchronised the block: LDS is free.
-template <int WM, int WN, int FP, int FC>
+template <int WM, int WN, int FP, int FC, bool RES>
 __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, char* smem,
                                            const uint16_t* Bv, const f32x16_t (&acc)[FP][FC], int q0,
                                            int m0) {
@@ -130,7 +160,7 @@ __device__ __forceinline__ void store_tile(const ConvArgs& a, const PwPlan& pl, 
     const int m = m0 + wm * FC * 32 + fc * 32 + l32;
     bv[fc] = (Bv && m < M) ? bf16_to_f32(Bv[m]) : 0.0f;
   }
-  if (a.res) {
+  if constexpr (RES) {
     store_tile_res<WM, WN, FP, FC>(a, pl, smem, bv, acc, q0, m0);
     return;
   }
@@ -197,8 +227,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* p, uin
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
-template <int WM, int WN, int FP, int FC, int KC, int P>
-__global__ __launch_bounds__(kThreads, KC == 32 ? 3 : 2) void conv1x1_bf16(const ConvArgs a, const PwPlan pl) {
+template <int WM, int WN, int FP, int FC, int KC, int P, bool RES>
+__global__ __launch_bounds__(kThreads, (KC == 32 && !RES) ? 3 : 2) void conv1x1_bf16(const ConvArgs a, const PwPlan pl) {
   constexpr int BM = 32 * WM * FC;          // output channels per tile
   constexpr int BN = 32 * WN * FP;          // pixels per tile
   constexpr int ROW = KC * 2 + 16;          // bytes per staged row
@@ -211,8 +241,10 @@ __global__ __launch_bounds__(kThreads, KC == 32 ? 3 : 2) void conv1x1_bf16(const
   constexpr int NS = KC / 16;               // k-steps per chunk
   // register sets of loaded chunks: two for 64-channel chunks; one for
   // 32-channel chunks, whose blocks are small enough to run three per CU
-  // (a second set would cost that occupancy)
-  constexpr int NSET = KC == 64 ? 2 : 1;
+  // (a second set would cost that occupancy).  The residual epilogue's
+  // fp32 staging leaves room for two blocks per CU whatever the chunk, and
+  // its registers take the place of the second set.
+  constexpr int NSET = (KC == 64 && !RES) ? 2 : 1;
   static_assert(WM * WN == 4, "four waves");
   static_assert(BN % P == 0 && KC % 32 == 0, "tile shape");
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -511,7 +543,7 @@ __global__ __launch_bounds__(kThreads, KC == 32 ? 3 : 2) void conv1x1_bf16(const
     }
     __syncthreads();
     if (S == 1) {
-      store_tile<WM, WN, FP, FC>(a, pl, smem, Bv, acc, cu.pb * BN, cu.m0);
+      store_tile<WM, WN, FP, FC, RES>(a, pl, smem, Bv, acc, cu.pb * BN, cu.m0);
     } else {
       f32x4_t* dst = partial_base<FP, FC>(pl.ws, cu.id) + tid;
 #pragma unroll
@@ -617,17 +649,22 @@ template <int WM, int WN, int FP, int KC>
 int launch_fp(const ConvArgs& a, const PwPlan& p, hipStream_t s) {
   constexpr int FC = 2;
   dim3 grid(p.grid, 1, 1);
-  switch (p.P) {
-    case 4:
-      hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 4>), grid, dim3(kThreads), p.lds, s, a, p);
-      break;
-    case 2:
-      hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 2>), grid, dim3(kThreads), p.lds, s, a, p);
-      break;
-    default:
-      hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, 1>), grid, dim3(kThreads), p.lds, s, a, p);
-      break;
-  }
+  // the residual epilogue is a separate instantiation, so that the plain
+  // kernels keep their registers
+  auto go = [&](auto Pc, auto Rc) {
+    constexpr int P = decltype(Pc)::value;
+    constexpr bool R = decltype(Rc)::value;
+    hipLaunchKernelGGL((conv1x1_bf16<WM, WN, FP, FC, KC, P, R>), grid, dim3(kThreads), p.lds, s, a, p);
+  };
+  auto by_p = [&](auto Rc) {
+    switch (p.P) {
+      case 4: go(std::integral_constant<int, 4>{}, Rc); break;
+      case 2: go(std::integral_constant<int, 2>{}, Rc); break;
+      default: go(std::integral_constant<int, 1>{}, Rc); break;
+    }
+  };
+  if (a.res) by_p(std::true_type{});
+  else by_p(std::false_type{});
   if (p.splits > 1)
     hipLaunchKernelGGL((conv1x1_reduce<WM, WN, FP, FC>), dim3(p.npb * p.nmb * 4), dim3(kThreads), 0, s, a, p);
   return (int)hipGetLastError();

@@ -84,7 +84,8 @@ bool valid(const ConvArgs& a, const PwPlan& p) {
   return a.C % p.KC == 0 && p.KC <= 64 && !(p.FP == 2 && p.P == 1 && p.KC > 32) &&
          p.lds <= kLdsMax && (int64_t)p.npb * p.nmb * p.splits < (int64_t)1 << 31 &&
          // byte offsets of the kernel's buffer loads are 32-bit
-         (int64_t)a.N * a.C * a.H * a.W * 2 < (int64_t)1 << 30 && (int64_t)a.M * a.C * 2 < (int64_t)1 << 30;
+         (int64_t)a.N * a.C * a.H * a.W * 2 < (int64_t)1 << 30 && (int64_t)a.M * a.C * 2 < (int64_t)1 << 30 &&
+         (int64_t)a.N * a.M * a.H * a.W < (int64_t)1 << 31;   // 32-bit element offsets into Y (and R)
 }
 
 // Pixel fragments per wave: two (128 x 128 or 64 x 256 tiles), or one where
