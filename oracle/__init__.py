@@ -63,6 +63,8 @@ def lib():
             "oxref_conv2d_res": (C.c_int, [P, P, P, P, P, C.c_int, P]),
             "oxref_conv2d_res_at": (C.c_int, [P, P, P, P, P, C.c_int, I64, P, P]),
             "oxref_batchnorm": (C.c_int, [I64, I64, I64, P, P, P, P, P, D]),
+            "oxref_maxpool2d": (C.c_int, [P, P, P]),
+            "oxref_global_avgpool": (C.c_int, [I64, I64, I64, P, P]),
             "oxref_fold_batchnorm": (C.c_int, [I64, I64, P, P, P, P, P, P, D, P, P]),
             "oxref_conv2d_int8": (C.c_int, [P, P, P, P, I32, F, P, F, I32, P, P]),
             "oxref_gemm_int8": (C.c_int, [I64, I64, I64, P, P, P, I32, F, P, F, I32, P, P]),
@@ -197,6 +199,33 @@ def conv2d(X, Wt, b=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1),
     _check(L.oxref_conv2d_res_at(C.byref(d), _p(X), _p(Wt), _p(b), _p(R), ACT[act], idx.size,
                                  _p(idx), _p(out)), "conv2d_at")
     return out
+
+
+def maxpool2d(X, kernel, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1)):
+    """ONNX MaxPool (ceil_mode 0) on X [N,C,H,W]; pads (top, left, bottom, right)."""
+    X = _f64(X)
+    N, Cc, H, W = X.shape
+    d = conv_desc(N, Cc, H, W, Cc, kernel[0], kernel[1], stride, pads, dilation, 1)
+    rc, Ho, Wo = conv_out_dims(d)
+    _check(rc, "conv_out_dims")
+    Y = np.empty((N, Cc, Ho, Wo), dtype=np.float64)
+    _check(lib().oxref_maxpool2d(C.byref(d), _p(X), _p(Y)), "maxpool2d")
+    return Y
+
+
+def global_avgpool(X):
+    """ONNX GlobalAveragePool: X [N,C,H,W] -> [N,C,1,1]."""
+    X = _f64(X)
+    N, Cc = X.shape[:2]
+    HW = int(np.prod(X.shape[2:]))
+    Y = np.empty((N, Cc, 1, 1), dtype=np.float64)
+    _check(lib().oxref_global_avgpool(N, Cc, HW, _p(X), _p(Y)), "global_avgpool")
+    return Y
+
+
+def batchnorm_act(X, gamma, beta, mean, var, eps=1e-5, act="none"):
+    """Unfused inference BatchNormalization followed by an activation."""
+    return globals()["act"](act, batchnorm(X, gamma, beta, mean, var, eps))
 
 
 def batchnorm(Y, gamma, beta, mean, var, eps=1e-5):

@@ -255,6 +255,49 @@ int oxref_batchnorm(int64_t N, int64_t M, int64_t HW, double* Y,
   return OXREF_OK;
 }
 
+/* --------------------------------------------------------------- Pooling -- */
+
+int oxref_maxpool2d(const oxref_conv* d, const double* X, double* Y) {
+  int64_t Ho, Wo;
+  int rc = oxref_conv_out_dims(d, &Ho, &Wo);
+  if (rc) return rc;
+  if (d->N < 0 || d->C < 0) return OXREF_EARG;
+  int64_t total = d->N * d->C * Ho * Wo;
+  if (total == 0) return OXREF_OK;
+  if (!X || !Y) return OXREF_EARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t o = 0; o < total; ++o) {
+    int64_t ow = o % Wo, oh = (o / Wo) % Ho, nc = o / (Wo * Ho);
+    const double* plane = X + nc * d->H * d->W;
+    double best = -INFINITY;            /* padding never wins: it is -inf */
+    for (int64_t kh = 0; kh < d->kH; ++kh) {
+      int64_t ih = oh * d->s_h - d->p_t + kh * d->d_h;
+      if (ih < 0 || ih >= d->H) continue;
+      for (int64_t kw = 0; kw < d->kW; ++kw) {
+        int64_t iw = ow * d->s_w - d->p_l + kw * d->d_w;
+        if (iw < 0 || iw >= d->W) continue;
+        double v = plane[ih * d->W + iw];
+        if (v > best) best = v;
+      }
+    }
+    Y[o] = best;
+  }
+  return OXREF_OK;
+}
+
+int oxref_global_avgpool(int64_t N, int64_t C, int64_t HW, const double* X, double* Y) {
+  if (N < 0 || C < 0 || HW < 1) return OXREF_EARG;
+  if (N * C == 0) return OXREF_OK;
+  if (!X || !Y) return OXREF_EARG;
+#pragma omp parallel for schedule(static)
+  for (int64_t nc = 0; nc < N * C; ++nc) {
+    double acc = 0.0;
+    for (int64_t i = 0; i < HW; ++i) acc += X[nc * HW + i];
+    Y[nc] = acc / (double)HW;
+  }
+  return OXREF_OK;
+}
+
 int oxref_fold_batchnorm(int64_t M, int64_t Kper, const double* W, const double* b0,
                          const double* gamma, const double* beta,
                          const double* mean, const double* var, double eps,

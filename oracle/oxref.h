@@ -124,6 +124,16 @@ int oxref_batchnorm(int64_t N, int64_t M, int64_t HW, double* Y,
                     const double* gamma, const double* beta, const double* mean,
                     const double* var, double eps);
 
+/* ONNX MaxPool (NCHW, ceil_mode 0): the window of ONNX Conv's geometry in
+ * d (kH, kW, strides, pads, dilations; C planes, d->M and d->group unused),
+ * each output the largest input under it; padding cells never win (-inf).
+ * ONNX GlobalAveragePool: Y[n,c] = (1/HW) * sum over the plane, summed in
+ * order.  Both are the classifier-head / stem steps next to the convolutions
+ * in the ResNet pipelines of tensorforge ("ResNet fusion") and onnx-vulkan-rs
+ * (the CNN operator list). */
+int oxref_maxpool2d(const oxref_conv* d, const double* X, double* Y);
+int oxref_global_avgpool(int64_t N, int64_t C, int64_t HW, const double* X, double* Y);
+
 /* Offline BatchNorm fold, in double:
  *   scale = gamma / sqrt(var + eps), shift = beta - mean * scale
  *   W'[m,:] = scale[m] * W[m,:],  b'[m] = scale[m] * b0[m] + shift[m]

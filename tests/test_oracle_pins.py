@@ -345,6 +345,50 @@ def test_conv_sampled_points_match_full():
 
 # --------------------------------------------------------------- BatchNorm --
 
+def test_maxpool_against_torch_float64():
+    # ONNX MaxPool: torch's max_pool2d on the input padded with -inf (ONNX
+    # pads may be asymmetric), float64
+    r = np.random.default_rng(606)
+    ran = 0
+    for ci in range(400):
+        N, Cc = int(r.integers(1, 3)), int(r.integers(1, 5))
+        H, W = int(r.integers(1, 12)), int(r.integers(1, 12))
+        kH, kW = int(r.integers(1, 5)), int(r.integers(1, 5))
+        s = (int(r.integers(1, 4)), int(r.integers(1, 4)))
+        d = (int(r.integers(1, 3)), int(r.integers(1, 3)))
+        pads = tuple(int(v) for v in r.integers(0, 3, 4))
+        if pads[0] >= kH * d[0] or pads[2] >= kH * d[0] or pads[1] >= kW * d[1] or pads[3] >= kW * d[1]:
+            continue                    # a window entirely in the padding: not a valid ONNX MaxPool
+        desc = oracle.conv_desc(N, Cc, H, W, Cc, kH, kW, s, pads, d, 1)
+        rc, Ho, Wo = oracle.conv_out_dims(desc)
+        if Ho < 1 or Wo < 1:
+            continue
+        X = r.standard_normal((N, Cc, H, W))
+        t, lft, b, rt = pads
+        xp = F.pad(torch.from_numpy(X), (lft, rt, t, b), value=float("-inf"))
+        ref = F.max_pool2d(xp, (kH, kW), stride=s, dilation=d).numpy()
+        got = oracle.maxpool2d(X, (kH, kW), s, pads, d)
+        assert got.shape == ref.shape and np.array_equal(got, ref), (ci, N, Cc, H, W, kH, kW, s, pads, d)
+        ran += 1
+    assert ran > 120
+    # closed forms: a 1x1 window is the identity; a constant plane stays constant
+    X = r.standard_normal((2, 3, 5, 6))
+    assert np.array_equal(oracle.maxpool2d(X, (1, 1)), X)
+    assert np.all(oracle.maxpool2d(np.full((1, 2, 7, 7), 2.5), (3, 3), (2, 2), (1, 1, 1, 1)) == 2.5)
+
+
+def test_global_avgpool_against_torch_and_closed_forms():
+    r = np.random.default_rng(707)
+    X = r.standard_normal((3, 5, 7, 9))
+    np.testing.assert_allclose(oracle.global_avgpool(X),
+                               torch.from_numpy(X).mean(dim=(2, 3), keepdim=True).numpy(),
+                               rtol=1e-14, atol=1e-14)
+    assert np.all(oracle.global_avgpool(np.ones((2, 4, 7, 7))) == 1.0)
+    # integer planes whose sums are exact: the mean is the exact quotient
+    Xi = r.integers(-50, 50, (2, 3, 4, 4)).astype(np.float64)
+    assert np.array_equal(oracle.global_avgpool(Xi)[..., 0, 0], Xi.sum(axis=(2, 3)) / 16.0)
+
+
 def test_batchnorm_against_torch():
     r = np.random.default_rng(8)
     Y = r.standard_normal((2, 5, 4, 3))
