@@ -27,7 +27,7 @@ EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_i
            "ox_conv2d_variant", "ox_conv2d_fused_packed", "ox_conv2d_packed_weights_bytes",
            "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
            "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
-           "ox_conv2d_fused_res")
+           "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool")
 
 
 class OxError(RuntimeError):
@@ -63,6 +63,9 @@ def _load():
         "ox_conv2d_workspace_bytes": (C.c_size_t, [I, P]),
         "ox_conv2d_fused_ws": (I, [I, P, P, P, I, P, I, P, P, C.c_size_t, P]),
         "ox_conv2d_fused_res": (I, [I, P, P, P, P, P, I, P, P, C.c_size_t, P]),
+        "ox_batchnorm_act": (I, [I, I64, I64, I64, P, P, P, P, P, F, I, P, P]),
+        "ox_maxpool2d": (I, [I, P, P, P, P]),
+        "ox_global_avgpool": (I, [I, I64, I64, I64, P, P, P]),
         "ox_conv2d_pack_weights": (I, [I, P, P, P]),
         "ox_fold_batchnorm": (I, [I64, I64, P, P, P, P, P, P, F, P, P]),
         "ox_int8_params_bytes": (C.c_size_t, [I64]),
@@ -231,6 +234,48 @@ def ox_conv2d_fused_res(X, W, R, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), di
         nbytes = workspace.numel() * workspace.element_size()
     _check(lib.ox_conv2d_fused_res(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), _ptr(R),
                                    ACT[act], _ptr(Y), _ptr(workspace), nbytes, _stream(stream)))
+    return Y
+
+
+def ox_batchnorm_act(X, gamma, beta, mean, var, eps=1e-5, act="none", Y=None, stream=None):
+    """ONNX BatchNormalization (inference) + activation on NCHW X; the four
+    parameters are fp32 device tensors [C].  Y may be X (in place)."""
+    torch = _torch()
+    for t, n in ((X, "X"), (gamma, "gamma"), (beta, "beta"), (mean, "mean"), (var, "var"), (Y, "Y")):
+        _dense(t, n)
+    N, Cc = X.shape[:2]
+    HW = X.numel() // max(1, N * Cc)
+    if Y is None:
+        Y = torch.empty_like(X)
+    _check(lib.ox_batchnorm_act(_dtype_code(X), N, Cc, HW, _ptr(X), _ptr(gamma), _ptr(beta), _ptr(mean),
+                                _ptr(var), float(eps), ACT[act], _ptr(Y), _stream(stream)))
+    return Y
+
+
+def ox_maxpool2d(X, kernel, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1), Y=None, stream=None):
+    """ONNX MaxPool (NCHW, ceil_mode 0); pads (top, left, bottom, right)."""
+    torch = _torch()
+    _dense(X, "X")
+    _dense(Y, "Y")
+    N, Cc, H, W = X.shape
+    d = conv_desc(N, Cc, H, W, Cc, kernel[0], kernel[1], stride, pads, dilation, 1)
+    if Y is None:
+        ho, wo = conv_out_hw(H, W, kernel[0], kernel[1], stride, pads, dilation)
+        Y = torch.empty((N, Cc, max(ho, 0), max(wo, 0)), dtype=X.dtype, device=X.device)
+    _check(lib.ox_maxpool2d(_dtype_code(X), C.byref(d), _ptr(X), _ptr(Y), _stream(stream)))
+    return Y
+
+
+def ox_global_avgpool(X, Y=None, stream=None):
+    """ONNX GlobalAveragePool: [N, C, H, W] -> [N, C, 1, 1]."""
+    torch = _torch()
+    _dense(X, "X")
+    _dense(Y, "Y")
+    N, Cc = X.shape[:2]
+    HW = X.numel() // max(1, N * Cc)
+    if Y is None:
+        Y = torch.empty((N, Cc, 1, 1), dtype=X.dtype, device=X.device)
+    _check(lib.ox_global_avgpool(_dtype_code(X), N, Cc, HW, _ptr(X), _ptr(Y), _stream(stream)))
     return Y
 
 

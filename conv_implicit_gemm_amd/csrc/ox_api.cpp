@@ -19,6 +19,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
+#include <cmath>
 #include <string>
 
 #include "../../include/ox.h"
@@ -646,6 +648,113 @@ ox_status ox_conv2d_int8(const ox_conv_desc* d, const int8_t* Xq, const int8_t* 
   a.out_dt = (int)y_type;
   a.i8 = int8_params;
   return conv_dispatch(fn, d, a, stream);
+}
+
+ox_status ox_batchnorm_act(ox_dtype t, int64_t N, int64_t C, int64_t HW, const void* X,
+                           const float* gamma, const float* beta, const float* mean, const float* var,
+                           float eps, ox_act act, void* Y, void* stream) {
+  const char* fn = "ox_batchnorm_act";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  st = check_act(fn, act);
+  if (st) return st;
+  if (N < 0 || C < 0 || HW < 0) return fail(OX_ERR_SHAPE, "%s: negative size (N=%lld C=%lld HW=%lld)", fn,
+                                            (long long)N, (long long)C, (long long)HW);
+  if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(OX_ERR_INVALID_ARG, "%s: eps=%g is not a positive finite value", fn, (double)eps);
+  const int64_t total = N * C * HW;
+  if (C > INT32_MAX || HW > INT32_MAX || (HW > 0 && C > 0 && N > INT64_MAX / C / HW))
+    return fail(OX_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  if (total > 0) {
+    if (!X || !Y) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is NULL", fn);
+    if (!gamma || !beta || !mean || !var) return fail(OX_ERR_INVALID_ARG, "%s: a BatchNorm parameter is NULL", fn);
+    const size_t es = t == OX_F32 ? 4 : 2;
+    if ((uintptr_t)X % es || (uintptr_t)Y % es) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is misaligned", fn);
+  }
+  if (total == 0) return ok();
+  PoolArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dt = (int)t;
+  a.total = total;
+  a.planes = N * C;
+  a.C = (int)C;
+  a.HW = (int)HW;
+  a.X = X;
+  a.Y = Y;
+  a.gamma = gamma;
+  a.beta = beta;
+  a.mean = mean;
+  a.var = var;
+  a.eps = eps;
+  a.act = (int)act;
+  return hip_result(fn, launch_bn_act(a, stream));
+}
+
+ox_status ox_maxpool2d(ox_dtype t, const ox_conv_desc* d, const void* X, void* Y, void* stream) {
+  const char* fn = "ox_maxpool2d";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  if (!d) return fail(OX_ERR_INVALID_ARG, "%s: d is NULL", fn);
+  if (d->M != d->C || d->group != 1)
+    return fail(OX_ERR_INVALID_ARG, "%s: a pooling descriptor needs M == C and group == 1", fn);
+  int64_t Ho, Wo;
+  st = check_conv_desc(fn, d, &Ho, &Wo);
+  if (st) return st;
+  // every window must reach the image (ONNX: pads smaller than the kernel extent)
+  const int64_t eh = (d->kH - 1) * d->d_h + 1, ew = (d->kW - 1) * d->d_w + 1;
+  if (d->p_t >= eh || d->p_b >= eh || d->p_l >= ew || d->p_r >= ew)
+    return fail(OX_ERR_INVALID_ARG, "%s: a pad reaches the kernel extent (a window of padding only)", fn);
+  const int64_t outs = d->N * d->C * Ho * Wo;
+  if (outs > 0) {
+    if (!X || !Y) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is NULL", fn);
+    const size_t es = t == OX_F32 ? 4 : 2;
+    if ((uintptr_t)X % es || (uintptr_t)Y % es) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is misaligned", fn);
+  } else {
+    return ok();
+  }
+  PoolArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dt = (int)t;
+  a.planes = d->N * d->C;
+  a.H = (int)d->H;
+  a.W = (int)d->W;
+  a.Ho = (int)Ho;
+  a.Wo = (int)Wo;
+  a.kH = (int)d->kH;
+  a.kW = (int)d->kW;
+  a.sh = (int)d->s_h;
+  a.sw = (int)d->s_w;
+  a.pt = (int)d->p_t;
+  a.pl = (int)d->p_l;
+  a.dh = (int)d->d_h;
+  a.dw = (int)d->d_w;
+  a.X = X;
+  a.Y = Y;
+  return hip_result(fn, launch_maxpool(a, stream));
+}
+
+ox_status ox_global_avgpool(ox_dtype t, int64_t N, int64_t C, int64_t HW, const void* X, void* Y,
+                            void* stream) {
+  const char* fn = "ox_global_avgpool";
+  ox_status st = check_float_dt(fn, t);
+  if (st) return st;
+  if (N < 0 || C < 0 || HW < 1)
+    return fail(OX_ERR_SHAPE, "%s: N=%lld C=%lld HW=%lld (HW must be at least 1)", fn, (long long)N,
+                (long long)C, (long long)HW);
+  if (HW > INT32_MAX || (C > 0 && N > INT64_MAX / C / HW))
+    return fail(OX_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  if (N * C == 0) return ok();
+  if (!X || !Y) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is NULL", fn);
+  const size_t es = t == OX_F32 ? 4 : 2;
+  if ((uintptr_t)X % es || (uintptr_t)Y % es) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is misaligned", fn);
+  PoolArgs a;
+  memset(&a, 0, sizeof(a));
+  a.dt = (int)t;
+  a.planes = N * C;
+  a.C = (int)std::min<int64_t>(C, INT32_MAX);
+  a.HW = (int)HW;
+  a.X = X;
+  a.Y = Y;
+  return hip_result(fn, launch_global_avgpool(a, stream));
 }
 
 ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_t cap) {

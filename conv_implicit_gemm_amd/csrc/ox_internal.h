@@ -197,4 +197,24 @@ const char* conv_patch_describe(const ConvArgs& a, char* buf, int cap);
 // Gemm with a single output row (M = 1): memory-bound, no MFMA
 int launch_gemv(const GemmArgs& a, void* stream);
 
+// The memory-bound steps beside the convolutions (NCHW).
+struct PoolArgs {
+  int dt;                 // DT_F32 or DT_BF16
+  int64_t total;          // elements of X (BatchNorm)
+  int64_t planes;         // N * C
+  int C, HW;              // channels; plane length H * W (BatchNorm, GlobalAveragePool)
+  int H, W, Ho, Wo, kH, kW, sh, sw, pt, pl, dh, dw;   // MaxPool window geometry
+  const void* X;
+  void* Y;
+  const float* gamma;     // BatchNorm parameters, fp32, [C]
+  const float* beta;
+  const float* mean;
+  const float* var;
+  float eps;
+  int act;
+};
+int launch_bn_act(const PoolArgs& a, void* stream);
+int launch_maxpool(const PoolArgs& a, void* stream);
+int launch_global_avgpool(const PoolArgs& a, void* stream);
+
 }  // namespace ox

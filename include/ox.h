@@ -194,6 +194,40 @@ ox_status ox_conv2d_fused_res(ox_dtype t, const ox_conv_desc* d, const void* X, 
                               const void* bias, const void* R, ox_act act, void* Y, void* workspace,
                               size_t workspace_bytes, void* stream);
 
+/* ---------------------------------- memory-bound steps beside the convs */
+
+/* ONNX BatchNormalization (inference) + activation, for a BatchNorm that
+ * cannot be folded into a convolution (the pre-activation BN -> ReLU of a
+ * ResNet-v2 block; tensorforge's "ResNet fusion" folds only the BN that
+ * follows a conv):
+ *   Y[n,c,i] = act((X[n,c,i] - mean[c]) * gamma[c] / sqrt(var[c] + eps) + beta[c])
+ * computed in fp32 (the scale and shift per channel, then one multiply-add
+ * per element).  X, Y: DEVICE, dense NCHW [N, C, HW] of type t (OX_F32 or
+ * OX_BF16), may be the same buffer (in place).  gamma, beta, mean, var:
+ * DEVICE fp32 [C].  eps > 0.  One kernel, no allocation.  Errors:
+ * OX_ERR_UNSUPPORTED for another t, OX_ERR_SHAPE for negative sizes,
+ * OX_ERR_INVALID_ARG for NULL or misaligned pointers, a bad act or eps. */
+ox_status ox_batchnorm_act(ox_dtype t, int64_t N, int64_t C, int64_t HW, const void* X,
+                           const float* gamma, const float* beta, const float* mean, const float* var,
+                           float eps, ox_act act, void* Y, void* stream);
+
+/* ONNX MaxPool (NCHW, ceil_mode 0, storage_order 0): the window geometry is
+ * an ox_conv_desc with M == C and group == 1 (kH, kW, strides, pads
+ * [t,l,b,r], dilations; output size as for Conv); each output is the largest
+ * input under its window, padding cells never taken.  X [N, C, H, W], Y
+ * [N, C, Ho, Wo], DEVICE, type t (OX_F32 or OX_BF16; bf16 maxima are exact).
+ * Errors as ox_conv2d_fused, plus OX_ERR_INVALID_ARG when a pad reaches the
+ * kernel extent (a window of padding only). */
+ox_status ox_maxpool2d(ox_dtype t, const ox_conv_desc* d, const void* X, void* Y, void* stream);
+
+/* ONNX GlobalAveragePool: Y[n,c] = (1/HW) * sum_i X[n,c,i], summed in fp32
+ * in a fixed order (the same bits every run) and rounded to t once.
+ * X [N, C, HW], Y [N, C] (i.e. [N, C, 1, 1]), DEVICE, type t (OX_F32 or
+ * OX_BF16).  HW >= 1.  Errors: OX_ERR_SHAPE for HW < 1 or negative sizes,
+ * OX_ERR_INVALID_ARG for NULL or misaligned pointers. */
+ox_status ox_global_avgpool(ox_dtype t, int64_t N, int64_t C, int64_t HW, const void* X, void* Y,
+                            void* stream);
+
 /* ------------------------------------------------- offline, host, untimed */
 
 /* Size in bytes of the packed weights of a convolution, or 0 when this

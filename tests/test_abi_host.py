@@ -186,6 +186,32 @@ def test_residual_entry_point_errors(ox, monkeypatch):
     monkeypatch.delenv("OX_FORCE_KERNEL")
 
 
+def test_pool_and_batchnorm_argument_errors(ox):
+    L = raw(ox)
+    bn = L.ox_batchnorm_act
+    assert bn(ox.OX_I8, 1, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-5, 0, FAKE, None) == 3
+    assert bn(ox.OX_F32, -1, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-5, 0, FAKE, None) == 2
+    assert bn(ox.OX_F32, 1, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 0.0, 0, FAKE, None) == 1
+    assert "eps" in ox.ox_last_error()
+    assert bn(ox.OX_F32, 1, 2, 4, FAKE, None, FAKE, FAKE, FAKE, 1e-5, 0, FAKE, None) == 1
+    assert bn(ox.OX_BF16, 1, 2, 4, FAKE + 1, FAKE, FAKE, FAKE, FAKE, 1e-5, 0, FAKE, None) == 1
+    assert bn(ox.OX_F32, 1, 2, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1e-5, 9, FAKE, None) == 1
+    assert bn(ox.OX_F32, 0, 2, 4, None, None, None, None, None, 1e-5, 0, None, None) == 0   # empty: nothing to do
+    mp = L.ox_maxpool2d
+    d_bad = ox.conv_desc(1, 4, 8, 8, 5, 3, 3, (2, 2), (1, 1, 1, 1))
+    assert mp(ox.OX_F32, C.byref(d_bad), FAKE, FAKE, None) == 1
+    assert "M == C" in ox.ox_last_error()
+    d_pad = ox.conv_desc(1, 4, 8, 8, 4, 2, 2, (1, 1), (2, 0, 0, 0))
+    assert mp(ox.OX_F32, C.byref(d_pad), FAKE, FAKE, None) == 1
+    assert "pad reaches" in ox.ox_last_error()
+    d_small = ox.conv_desc(1, 4, 2, 2, 4, 5, 5)
+    assert mp(ox.OX_F32, C.byref(d_small), FAKE, FAKE, None) == 2
+    gap = L.ox_global_avgpool
+    assert gap(ox.OX_F32, 1, 2, 0, FAKE, FAKE, None) == 2
+    assert gap(ox.OX_I8, 1, 2, 4, FAKE, FAKE, None) == 3
+    assert gap(ox.OX_F32, 1, 2, 4, None, FAKE, None) == 1
+
+
 def test_gemm_argument_errors(ox):
     L = raw(ox)
     g = L.ox_gemm_fused

@@ -858,3 +858,103 @@ def test_c3_resnet50_bottleneck_residual(ox, dtype):
         idx = sample_indices(got.size, 4096, li)
         ref = oracle.conv2d(X, Wt, b, act="relu", residual=Rr, at=idx)
         assert_close(got[idx], ref, dtype, layer.name)
+
+
+# --------------------------------------- BatchNorm + act, MaxPool, GAP --
+
+def bn_params(r, Cc):
+    g = r.uniform(0.5, 1.5, Cc).astype(np.float32)
+    be = (r.standard_normal(Cc) * 0.3).astype(np.float32)
+    mu = (r.standard_normal(Cc) * 0.3).astype(np.float32)
+    var = r.uniform(0.5, 1.5, Cc).astype(np.float32)
+    return g, be, mu, var
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_batchnorm_act(ox, dtype):
+    # vector path (plane length a multiple of the vector), element path (odd
+    # planes, a misaligned X), in place, every activation
+    r = np.random.default_rng(8080)
+    for ci, (N, Cc, H, W, act, xoff, in_place) in enumerate([
+            (3, 16, 8, 8, "relu", 0, False), (2, 7, 5, 9, "relu6", 0, False), (1, 33, 7, 7, "gelu", 1, False),
+            (2, 64, 28, 28, "none", 0, True), (4, 5, 1, 1, "relu", 0, False)]):
+        X = synth.round_to(r.standard_normal((N, Cc, H, W)) * 2, dtype)
+        g, be, mu, var = bn_params(r, Cc)
+        say("bn act", dtype, (N, Cc, H, W, act, xoff, in_place))
+        Xd = misaligned(dev(X, dtype), xoff) if xoff else dev(X, dtype)
+        prm = [torch.from_numpy(v).cuda() for v in (g, be, mu, var)]
+        Y = ox.ox_batchnorm_act(Xd, *prm, eps=1e-5, act=act, Y=Xd if in_place else None)
+        torch.cuda.synchronize()
+        ref = oracle.batchnorm_act(X, g, be, mu, var, 1e-5, act)
+        assert_close(host64(Y), ref, dtype, "bn case %d" % ci)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_maxpool(ox, dtype):
+    # a maximum of values exact in the dtype is one of them: bit-exact
+    r = np.random.default_rng(9090)
+    ran = 0
+    while ran < 40:
+        N, Cc = int(r.integers(1, 3)), int(r.integers(1, 6))
+        H, W = int(r.integers(1, 15)), int(r.integers(1, 15))
+        kH, kW = int(r.integers(1, 4)), int(r.integers(1, 4))
+        s = (int(r.integers(1, 3)), int(r.integers(1, 3)))
+        d = (int(r.integers(1, 3)), int(r.integers(1, 3)))
+        pads = tuple(int(v) for v in r.integers(0, 2, 4))
+        if pads[0] >= (kH - 1) * d[0] + 1 or pads[2] >= (kH - 1) * d[0] + 1 or \
+           pads[1] >= (kW - 1) * d[1] + 1 or pads[3] >= (kW - 1) * d[1] + 1:
+            continue
+        ho, wo = ox.conv_out_hw(H, W, kH, kW, s, pads, d)
+        if ho < 1 or wo < 1:
+            continue
+        X = synth.round_to(r.standard_normal((N, Cc, H, W)), dtype)
+        say("maxpool", dtype, (N, Cc, H, W, kH, kW, s, pads, d))
+        Y = ox.ox_maxpool2d(dev(X, dtype), (kH, kW), s, pads, d, Y=nan_like((N, Cc, ho, wo), dtype))
+        torch.cuda.synchronize()
+        assert np.array_equal(host64(Y), oracle.maxpool2d(X, (kH, kW), s, pads, d)), ran
+        ran += 1
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_global_avgpool(ox, dtype):
+    r = np.random.default_rng(1010)
+    for N, Cc, H, W in [(2, 7, 7, 7), (1, 5, 1, 1), (3, 4, 15, 20), (2, 3, 9, 1)]:
+        X = synth.round_to(r.standard_normal((N, Cc, H, W)), dtype)
+        say("gap", dtype, (N, Cc, H, W))
+        Y = ox.ox_global_avgpool(dev(X, dtype), Y=nan_like((N, Cc, 1, 1), dtype))
+        torch.cuda.synchronize()
+        assert_close(host64(Y), oracle.global_avgpool(X), dtype, "gap")
+        Y2 = ox.ox_global_avgpool(dev(X, dtype))
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(-1), Y2.view(-1))     # fixed summation order
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_resnet50_pool_and_bn_full_size(ox, dtype):
+    # the ResNet-50 stem MaxPool (3x3 s2 p1, 64 x 112^2 -> 56^2), a
+    # pre-activation BN + ReLU at stage 1 and the head's GlobalAveragePool,
+    # batch 32 (sampled comparisons after a NaN scan)
+    r = np.random.default_rng(2020)
+    X = synth.round_to(r.standard_normal((32, 64, 112, 112)), dtype)
+    Y = ox.ox_maxpool2d(dev(X, dtype), (3, 3), (2, 2), (1, 1, 1, 1))
+    torch.cuda.synchronize()
+    assert not torch.isnan(Y).any().item()
+    got = host64(Y)
+    ref = oracle.maxpool2d(X, (3, 3), (2, 2), (1, 1, 1, 1))
+    assert np.array_equal(got, ref)
+    X = synth.round_to(r.standard_normal((32, 256, 56, 56)), dtype)
+    g, be, mu, var = bn_params(r, 256)
+    Y = ox.ox_batchnorm_act(dev(X, dtype), *[torch.from_numpy(v).cuda() for v in (g, be, mu, var)],
+                            act="relu")
+    torch.cuda.synchronize()
+    got = host64(Y).ravel()
+    idx = sample_indices(got.size, 4096, 3)
+    Xs = X.reshape(-1)[idx]
+    c = (idx // (56 * 56)) % 256
+    refs = oracle.act("relu", (Xs - mu[c].astype(np.float64)) / np.sqrt(var[c].astype(np.float64) + 1e-5)
+                      * g[c].astype(np.float64) + be[c].astype(np.float64))
+    assert_close(got[idx], refs, dtype, "bn full size")
+    X = synth.round_to(r.standard_normal((32, 2048, 7, 7)), dtype)
+    Y = ox.ox_global_avgpool(dev(X, dtype))
+    torch.cuda.synchronize()
+    assert_close(host64(Y), oracle.global_avgpool(X), dtype, "gap full size")
