@@ -34,7 +34,7 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="resnet50",
-                   choices=["resnet50", "mobilenetv2", "mlp", "matmul", "int8"])
+                   choices=["resnet50", "mobilenetv2", "mlp", "matmul", "int8", "resnet50-aux"])
     p.add_argument("--dtype", default=None, help="bf16 or f32 (float workloads)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -138,6 +138,43 @@ def conv_layers(ox, synth, torch, cfg, layers, dtype, stream, residual=()):
         kred = (l.C // l.group) * l.kh * l.kw
         out.append(Layer(l.name, l.flops(), nbytes, variant, launch, oracle_at,
                          l.N * l.M * ho * wo, kred))
+    return out
+
+
+def aux_layers(ox, torch, dtype, batch, stream):
+    """The memory-bound steps around ResNet-50's convolutions at the same
+    batch: the stem MaxPool (3x3 s2 p1, 64 x 112^2), an unfoldable
+    (pre-activation) BatchNorm + ReLU at each stage's input width and the
+    head's GlobalAveragePool.  Seeded synthetic tensors."""
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    es = ESIZE[dtype]
+    code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1234)
+    out = []
+
+    def rnd(*shape):
+        return torch.randn(*shape, generator=g, device="cuda", dtype=torch.float32).to(tdt)
+
+    X = rnd(batch, 64, 112, 112)
+    Y = torch.empty((batch, 64, 56, 56), dtype=tdt, device="cuda")
+    d = ox.conv_desc(batch, 64, 112, 112, 64, 3, 3, (2, 2), (1, 1, 1, 1))
+    args = (code, C.byref(d), X.data_ptr(), Y.data_ptr(), stream)
+    out.append(Layer("stem.maxpool3x3s2", 0.0, (X.numel() + Y.numel()) * es, "maxpool/" + dtype,
+                     lambda a=args, k=(X, Y, d): ox.lib.ox_maxpool2d(*a), None, Y.numel(), 9))
+    for cc, hw in ((256, 56), (512, 28), (1024, 14), (2048, 7)):
+        X = rnd(batch, cc, hw, hw)
+        Y = torch.empty_like(X)
+        prm = [torch.rand(cc, generator=g, device="cuda") + 0.5 for _ in range(4)]
+        args = (code, batch, cc, hw * hw, X.data_ptr(), prm[0].data_ptr(), prm[1].data_ptr(),
+                prm[2].data_ptr(), prm[3].data_ptr(), 1e-5, ox.ACT["relu"], Y.data_ptr(), stream)
+        out.append(Layer("bn_relu.%dx%d^2" % (cc, hw), 0.0, 2 * X.numel() * es + 16 * cc, "bn_act/" + dtype,
+                         lambda a=args, k=(X, Y, prm): ox.lib.ox_batchnorm_act(*a), None, X.numel(), 1))
+    X = rnd(batch, 2048, 7, 7)
+    Y = torch.empty((batch, 2048, 1, 1), dtype=tdt, device="cuda")
+    args = (code, batch, 2048, 49, X.data_ptr(), Y.data_ptr(), stream)
+    out.append(Layer("head.gap", 0.0, (X.numel() + Y.numel()) * es, "gap/" + dtype,
+                     lambda a=args, k=(X, Y): ox.lib.ox_global_avgpool(*a), None, Y.numel(), 49))
     return out
 
 
@@ -349,6 +386,12 @@ def main():
                "input": "3x224x224", "epilogue": "folded BN bias + ReLU"}
         if res:
             cfg["residual"] = "the last 1x1 of each stage adds a residual before its ReLU"
+    elif wl == "resnet50-aux":
+        dtype = args.dtype or "bf16"
+        batch = args.batch or 32
+        layers = aux_layers(ox, torch, dtype, batch, sp)
+        cfg = {"workload": "resnet50 memory-bound steps: stem MaxPool, pre-activation BatchNorm + "
+                           "ReLU at each stage width, head GlobalAveragePool", "batch": batch}
     elif wl == "mobilenetv2":
         dtype = args.dtype or "f32"
         batch = args.batch or 64
@@ -422,6 +465,8 @@ def main():
     step_flops = sum(L.flops for L in layers)
     ms_per_step = total_ms / K
     value = step_flops / (ms_per_step * 1e-3) / 1e12
+    if step_flops == 0:      # a workload of memory-bound steps only: report its bandwidth
+        value = sum(L.nbytes for L in layers) / (ms_per_step * 1e-3) / 1e9
 
     # per-layer roofline (attainable time t_roof = max(FLOP / MFMA peak,
     # algorithmic bytes / HBM peak)) and the dominant kernel: the variant
@@ -466,10 +511,12 @@ def main():
     roof["roofline_frac"] = g["t_roof"] / (g["ms"] * 1e-3)   # sum t_roof / sum t_meas
 
     cpu = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and step_flops > 0:
         cpu = cpu_baseline(layers, args.cpu_seconds, dtype == "i8")
 
     unit = "TOPS" if dtype == "i8" else "TFLOP/s"
+    if step_flops == 0:
+        unit = "GB/s"
     out = {
         "metric": "TFLOP/s (TOPS int8) per fused GEMM/conv shape + % of MFMA or HBM roofline",
         "value": value, "unit": unit, "n_gpus": 1, "steps": K, "warmup": args.warmup,

@@ -15,19 +15,28 @@ namespace {
 // ---------------------------------------------------- BatchNorm + act ----
 // Y = act((X - mean[c]) * (gamma[c] / sqrt(var[c] + eps)) + beta[c]).  The
 // flat NCHW range is walked in vectors of V elements (16 bytes when the
-// pointers and the plane length allow, so that a vector never leaves its
-// plane), grid-stride, two vectors per thread and step in flight.
+// pointers allow and a plane holds at least V elements, so that a vector
+// crosses at most one plane boundary: its elements take the channel of
+// their own plane), grid-stride, two vectors per thread and step in flight;
+// the last total % V elements go element by element.
 template <typename T, int V, int ACT>
 __global__ __launch_bounds__(kThreads) void bn_act_kernel(const PoolArgs a) {
   const T* X = (const T*)a.X;
   T* Y = (T*)a.Y;
   const int64_t nvec = a.total / V;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
+  auto params = [&](int c, float& sc, float& sh) {
+    sc = a.gamma[c] / sqrtf(a.var[c] + a.eps);
+    sh = a.beta[c] - a.mean[c] * sc;
+  };
   auto one = [&](int64_t v) {
     const int64_t e0 = v * V;
-    const int c = (int)((e0 / a.HW) % a.C);
-    const float sc = a.gamma[c] / sqrtf(a.var[c] + a.eps);
-    const float sh = a.beta[c] - a.mean[c] * sc;
+    const int64_t p0 = e0 / a.HW;
+    const int left = (int)(a.HW - (e0 - p0 * a.HW));      // elements of this vector in plane p0 (>= 1)
+    const int c0 = (int)(p0 % a.C);
+    float sc0, sh0, sc1 = 0.f, sh1 = 0.f;
+    params(c0, sc0, sh0);
+    if (left < V) params(c0 + 1 == a.C ? 0 : c0 + 1, sc1, sh1);
     T in[V], out[V];
     if constexpr (V * sizeof(T) == 16) {
       const u32x4_t raw = *(const u32x4_t*)(X + e0);
@@ -38,7 +47,8 @@ __global__ __launch_bounds__(kThreads) void bn_act_kernel(const PoolArgs a) {
     }
 #pragma unroll
     for (int j = 0; j < V; ++j) {
-      const float y = act_c<ACT>(fmaf(to_f32(in[j]), sc, sh));
+      const bool first = j < left;
+      const float y = act_c<ACT>(fmaf(to_f32(in[j]), first ? sc0 : sc1, first ? sh0 : sh1));
       if constexpr (sizeof(T) == 2) out[j] = f32_to_bf16(y);
       else out[j] = y;
     }
@@ -57,6 +67,16 @@ __global__ __launch_bounds__(kThreads) void bn_act_kernel(const PoolArgs a) {
     one(v + stride);
   }
   if (v < nvec) one(v);
+  if (blockIdx.x == 0) {
+    for (int64_t e = nvec * V + threadIdx.x; e < a.total; e += kThreads) {
+      const int c = (int)((e / a.HW) % a.C);
+      float sc, sh;
+      params(c, sc, sh);
+      const float y = act_c<ACT>(fmaf(to_f32(X[e]), sc, sh));
+      if constexpr (sizeof(T) == 2) Y[e] = f32_to_bf16(y);
+      else Y[e] = y;
+    }
+  }
 }
 
 // ------------------------------------------------------------- MaxPool ----
@@ -130,7 +150,7 @@ int blocks_for(int64_t items) {
 template <typename T>
 int launch_bn(const PoolArgs& a, hipStream_t s) {
   constexpr int V16 = 16 / sizeof(T);
-  const bool vec = ((uintptr_t)a.X % 16 == 0) && ((uintptr_t)a.Y % 16 == 0) && a.HW % V16 == 0;
+  const bool vec = ((uintptr_t)a.X % 16 == 0) && ((uintptr_t)a.Y % 16 == 0) && a.HW >= V16;
   const int64_t nvec = vec ? a.total / V16 : a.total;
   dim3 grid(blocks_for((nvec + 1) / 2));
   with_act_host(a.act, [&](auto act_k) {
