@@ -19,6 +19,7 @@
 // and its window of input rows sliding down (one or two new rows per step,
 // read as 16-byte vectors).
 #include <algorithm>
+#include <cmath>
 #include <cstdlib>
 #include <type_traits>
 
@@ -69,7 +70,7 @@ template <> struct DwLoads<DT_I8> { static constexpr int V = 3; };
 // strip is written in chunks of 4 (one 4-wide store where full and aligned).
 constexpr int kChunk = 4;
 
-template <int DT, int KH, int KW, int S, int ST, bool SLIDE>
+template <int DT, int KH, int KW, int S, int ST, bool SLIDE, bool MAXP = false>
 __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const DwPlan pl) {
   static_assert(ST % kChunk == 0, "strips are whole store chunks");
   typedef typename Dw<DT>::T T;
@@ -101,6 +102,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
     q.init(a.i8);
     padv = (L)q.xzp;
   }
+  if constexpr (MAXP) padv = (L)-INFINITY;      // MaxPool: padding never wins
 
   // Every global load of the staging phase is issued before the first wait:
   // the interior as 16-byte vectors into registers (at most kLoads per
@@ -143,9 +145,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
       buf[i] = *(const u32x4_t*)(src0 + head + min(tid + i * kThreads, nvec - 1) * EPC);
   }
   // head and tail elements (a block with an empty span reads a weight instead)
-  const T he = span > 0 ? src0[min(tid, span - 1)] : Wt[wi0];
-  const T te = span > 0 ? src0[min(tail0 + tid, span - 1)] : Wt[wi0];
-  const T w0 = Wt[wi0], w1 = Wt[wi1];
+  // (MaxPool has no weights: nothing is read in their place)
+  const T he = span > 0 ? src0[min(tid, span - 1)] : (MAXP ? (T)0 : Wt[wi0]);
+  const T te = span > 0 ? src0[min(tail0 + tid, span - 1)] : (MAXP ? (T)0 : Wt[wi0]);
+  const T w0 = MAXP ? (T)0 : Wt[wi0], w1 = MAXP ? (T)0 : Wt[wi1];
   // the bias of plane tid (and its int8 multiplier)
   A b0 = (A)0;
   double m0 = 0.0;
@@ -172,7 +175,8 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
 
   if (tid < nw) wts[tid] = widen<T, A>(w0);
   if (tid + kThreads < nw) wts[tid + kThreads] = widen<T, A>(w1);
-  for (int i = tid + 2 * kThreads; i < nw; i += kThreads) wts[i] = widen<T, A>(Wt[widx(i)]);
+  if constexpr (!MAXP)
+    for (int i = tid + 2 * kThreads; i < nw; i += kThreads) wts[i] = widen<T, A>(Wt[widx(i)]);
   auto plane_vals = [&](int i, A bv, double mv) {
     pbias[i] = bv;
     if constexpr (DT == DT_I8) pmult[i] = mv;
@@ -327,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   auto strip = [&](int pp, int r, int ow0, auto act_k) {
     const A* wk = wts + pp * KK;
     A acc[ST];
-    const A init = pbias[pp];                              // the bias seeds the accumulators
+    const A init = MAXP ? (A)-INFINITY : pbias[pp];       // the bias seeds the accumulators
 #pragma unroll
     for (int o = 0; o < ST; ++o) acc[o] = init;
     for (int kh = 0; kh < kH; ++kh) {
@@ -335,7 +339,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
       for (int kw = 0; kw < kW; ++kw) {
         const A wv = wk[kh * kW + kw];
 #pragma unroll
-        for (int o = 0; o < ST; ++o) acc[o] += widen<L, A>(rp[o * sw + kw * dw]) * wv;
+        for (int o = 0; o < ST; ++o) {
+          if constexpr (MAXP) acc[o] = fmaxf(acc[o], widen<L, A>(rp[o * sw + kw * dw]));
+          else acc[o] += widen<L, A>(rp[o * sw + kw * dw]) * wv;
+        }
       }
     }
     store_strip(pp, r, ow0, acc, act_k);
@@ -387,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
       if (refill) {
 #pragma unroll
         for (int k = 0; k < KK; ++k) wv[k] = wts[pp * KK + k];
-        init = pbias[pp];
+        init = MAXP ? (A)-INFINITY : pbias[pp];
         static_for<KH>([&](auto KHc) {
           constexpr int kh = decltype(KHc)::value;
           read_row(win[(kh + S * PH) % NSL], r * S + kh);
@@ -407,7 +414,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
 #pragma unroll
         for (int kw = 0; kw < KW; ++kw)
 #pragma unroll
-          for (int o = 0; o < ST; ++o) acc[o] += widen<L, A>(w[o * S + kw]) * wv[kh * KW + kw];
+          for (int o = 0; o < ST; ++o) {
+            if constexpr (MAXP) acc[o] = fmaxf(acc[o], widen<L, A>(w[o * S + kw]));
+            else acc[o] += widen<L, A>(w[o * S + kw]) * wv[kh * KW + kw];
+          }
       });
       store_strip(pp, r, ow0, acc, act_k);
       if (++r == Ho) {                                     // next plane (several-plane blocks)
@@ -535,7 +545,7 @@ DwPlan make_plan(const ConvArgs& a) {
   return p;
 }
 
-template <int DT>
+template <int DT, bool MAXP = false>
 int launch_dt(const ConvArgs& a, hipStream_t s) {
   const DwPlan p = make_plan(a);
   const int KK = a.kH * a.kW;
@@ -547,16 +557,16 @@ int launch_dt(const ConvArgs& a, hipStream_t s) {
   const bool w8 = p.OWT == 8;
   auto go2 = [&](auto slide_k, auto plain_k) { p.slide ? go(slide_k) : go(plain_k); };
   if (!fixed_shape(a))
-    go(dw_kernel<DT, 0, 0, 0, 4, false>);
+    go(dw_kernel<DT, 0, 0, 0, 4, false, MAXP>);
   else if (a.kH == 1)
-    w8 ? go2(dw_kernel<DT, 1, 9, 1, 8, true>, dw_kernel<DT, 1, 9, 1, 8, false>)
-       : go2(dw_kernel<DT, 1, 9, 1, 4, true>, dw_kernel<DT, 1, 9, 1, 4, false>);
+    w8 ? go2(dw_kernel<DT, 1, 9, 1, 8, true, MAXP>, dw_kernel<DT, 1, 9, 1, 8, false, MAXP>)
+       : go2(dw_kernel<DT, 1, 9, 1, 4, true, MAXP>, dw_kernel<DT, 1, 9, 1, 4, false, MAXP>);
   else if (a.sh == 1)
-    w8 ? go2(dw_kernel<DT, 3, 3, 1, 8, true>, dw_kernel<DT, 3, 3, 1, 8, false>)
-       : go2(dw_kernel<DT, 3, 3, 1, 4, true>, dw_kernel<DT, 3, 3, 1, 4, false>);
+    w8 ? go2(dw_kernel<DT, 3, 3, 1, 8, true, MAXP>, dw_kernel<DT, 3, 3, 1, 8, false, MAXP>)
+       : go2(dw_kernel<DT, 3, 3, 1, 4, true, MAXP>, dw_kernel<DT, 3, 3, 1, 4, false, MAXP>);
   else
-    w8 ? go2(dw_kernel<DT, 3, 3, 2, 8, true>, dw_kernel<DT, 3, 3, 2, 8, false>)
-       : go2(dw_kernel<DT, 3, 3, 2, 4, true>, dw_kernel<DT, 3, 3, 2, 4, false>);
+    w8 ? go2(dw_kernel<DT, 3, 3, 2, 8, true, MAXP>, dw_kernel<DT, 3, 3, 2, 8, false, MAXP>)
+       : go2(dw_kernel<DT, 3, 3, 2, 4, true, MAXP>, dw_kernel<DT, 3, 3, 2, 4, false, MAXP>);
   return (int)hipGetLastError();
 }
 
@@ -565,6 +575,18 @@ int launch_dt(const ConvArgs& a, hipStream_t s) {
 bool depthwise_fits(const ConvArgs& a) {
   const DwPlan p = make_plan(a);
   return lds_bytes(p, a.kH * a.kW) <= kLdsCap && (a.Ho + p.TH - 1) / p.TH <= 65535;
+}
+
+// MaxPool through the same staged-band kernel: the window is the depthwise
+// window, -inf fills the halo and the taps are combined with max (no
+// weights, no bias, no activation)
+int launch_maxpool_dw(const ConvArgs& a, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  switch (a.dt) {
+    case DT_F32: return launch_dt<DT_F32, true>(a, s);
+    case DT_BF16: return launch_dt<DT_BF16, true>(a, s);
+    default: return (int)hipErrorInvalidValue;
+  }
 }
 
 int launch_conv_depthwise(const ConvArgs& a, void* stream) {

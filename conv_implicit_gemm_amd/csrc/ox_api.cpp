@@ -711,6 +711,15 @@ ox_status ox_maxpool2d(ox_dtype t, const ox_conv_desc* d, const void* X, void* Y
   } else {
     return ok();
   }
+  // the depthwise kernel's staged band, where its LDS band fits; else one
+  // thread per output (OX_POOL_SIMPLE=1 forces the latter, for tests)
+  const char* simple = getenv("OX_POOL_SIMPLE");
+  if (!(simple && simple[0] == '1')) {
+    ox_conv_desc dd = *d;
+    dd.group = d->C;
+    ConvArgs ca = conv_args((int)t, &dd, Ho, Wo, X, nullptr, nullptr, Y, ACT_NONE);
+    if (depthwise_fits(ca)) return hip_result(fn, launch_maxpool_dw(ca, stream));
+  }
   PoolArgs a;
   memset(&a, 0, sizeof(a));
   a.dt = (int)t;

@@ -214,6 +214,8 @@ struct PoolArgs {
   int act;
 };
 int launch_bn_act(const PoolArgs& a, void* stream);
+// MaxPool on the depthwise kernel's staged band (group == C == M, f32 / bf16)
+int launch_maxpool_dw(const ConvArgs& a, void* stream);
 int launch_maxpool(const PoolArgs& a, void* stream);
 int launch_global_avgpool(const PoolArgs& a, void* stream);
 

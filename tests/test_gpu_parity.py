@@ -889,9 +889,13 @@ def test_batchnorm_act(ox, dtype):
         assert_close(host64(Y), ref, dtype, "bn case %d" % ci)
 
 
+@pytest.mark.parametrize("simple", [False, True])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_maxpool(ox, dtype):
-    # a maximum of values exact in the dtype is one of them: bit-exact
+def test_maxpool(ox, dtype, simple, monkeypatch):
+    # a maximum of values exact in the dtype is one of them: bit-exact; the
+    # staged-band (depthwise) kernel and the one-thread-per-output kernel
+    if simple:
+        monkeypatch.setenv("OX_POOL_SIMPLE", "1")
     r = np.random.default_rng(9090)
     ran = 0
     while ran < 40:
