@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="target CPU time of the oracle baseline sample (0 = skip)")
     p.add_argument("--rows", default=None, help="write per-layer rows as JSON to this file")
+    p.add_argument("--graph", action="store_true",
+                   help="capture one step's launches in a HIP graph (torch.cuda.CUDAGraph) and time "
+                        "K replays of it instead of K eager steps")
     p.add_argument("--residual", action="store_true",
                    help="resnet50 / mobilenetv2: the block-closing convolutions add a residual "
                         "input before their activation (ox_conv2d_fused_res)")
@@ -375,6 +378,10 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "copies": 10}))
         return
     stream = torch.cuda.current_stream()
+    if args.graph:
+        # capture needs a stream of its own (default priority)
+        stream = torch.cuda.Stream()
+        torch.cuda.set_stream(stream)
     sp = stream.cuda_stream
     wl = args.workload
     if wl == "resnet50":
@@ -429,6 +436,17 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+    run_step = step
+    if args.graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            step()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        run_step = graph.replay
+        cfg = dict(cfg, graph="one step captured in a HIP graph, replayed")
 
     # timed region: K steps back to back, one event pair around all of them
     # (same stream).  An event between two kernels is a stream marker that
@@ -441,7 +459,7 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(K):
-        step()
+        run_step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
