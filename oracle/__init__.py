@@ -69,6 +69,8 @@ def lib():
             "oxref_conv2d_int8": (C.c_int, [P, P, P, P, I32, F, P, F, I32, P, P]),
             "oxref_gemm_int8": (C.c_int, [I64, I64, I64, P, P, P, I32, F, P, F, I32, P, P]),
             "oxref_requant1": (I32, [I64, F, F, F, I32]),
+            "oxref_qconv2d": (C.c_int, [P, P, P, P, I32, P, F, P, F, I32, I32, I32, P, P]),
+            "oxref_qgemm": (C.c_int, [I64, I64, I64, P, P, P, I32, P, F, P, F, I32, I32, I32, P, P]),
         }
         for name, (res, args) in sig.items():
             fn = getattr(L, name)
@@ -290,6 +292,57 @@ def gemm_int8(Xq, Wq, bias_q, x_zp, x_s, w_s, y_s, y_zp):
     _check(lib().oxref_gemm_int8(M, N, K, _p(Xq), _p(Wq), _p(bq), int(x_zp),
                                  float(np.float32(x_s)), _p(ws), float(np.float32(y_s)),
                                  int(y_zp), _p(acc), _p(y)), "gemm_int8")
+    return acc, y
+
+
+def _i32(a):
+    return np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+
+
+def _yrange(y_unsigned):
+    return (0, 255) if y_unsigned else (-128, 127)
+
+
+def qconv2d(X, Wq, bias_q, x_zp, w_zp, x_s, w_s, y_s, y_zp, y_unsigned=False, stride=(1, 1),
+            pads=(0, 0, 0, 0), dilation=(1, 1), group=1):
+    """Quantised conv with activation and per-channel weight zero points
+    (int8 or uint8 stored integers): returns (acc int64, y int32 holding int8
+    or uint8 values), both [N,M,Ho,Wo]."""
+    X = _i32(X)
+    Wq = _i32(Wq)
+    N, Cin, H, W = X.shape
+    M, _, kH, kW = Wq.shape
+    d = conv_desc(N, Cin, H, W, M, kH, kW, stride, pads, dilation, group)
+    rc, Ho, Wo = conv_out_dims(d)
+    _check(rc, "conv_out_dims")
+    bq = None if bias_q is None else _i32(bias_q)
+    wz = None if w_zp is None else _i32(w_zp)
+    ws = np.ascontiguousarray(np.asarray(w_s, dtype=np.float32))
+    lo, hi = _yrange(y_unsigned)
+    acc = np.empty((N, M, Ho, Wo), dtype=np.int64)
+    y = np.empty((N, M, Ho, Wo), dtype=np.int32)
+    _check(lib().oxref_qconv2d(C.byref(d), _p(X), _p(Wq), _p(bq), int(x_zp), _p(wz),
+                               float(np.float32(x_s)), _p(ws), float(np.float32(y_s)), int(y_zp),
+                               lo, hi, _p(acc), _p(y)), "qconv2d")
+    return acc, y
+
+
+def qgemm(X, Wq, bias_q, x_zp, w_zp, x_s, w_s, y_s, y_zp, y_unsigned=False):
+    """Quantised Gemm X [M,K] x W [N,K] with both zero points: returns
+    (acc int64 [M,N], y int32 [M,N] holding int8 or uint8 values)."""
+    X = _i32(X)
+    Wq = _i32(Wq)
+    M, K = X.shape
+    N = Wq.shape[0]
+    bq = None if bias_q is None else _i32(bias_q)
+    wz = None if w_zp is None else _i32(w_zp)
+    ws = np.ascontiguousarray(np.asarray(w_s, dtype=np.float32))
+    lo, hi = _yrange(y_unsigned)
+    acc = np.empty((M, N), dtype=np.int64)
+    y = np.empty((M, N), dtype=np.int32)
+    _check(lib().oxref_qgemm(M, N, K, _p(X), _p(Wq), _p(bq), int(x_zp), _p(wz),
+                             float(np.float32(x_s)), _p(ws), float(np.float32(y_s)), int(y_zp),
+                             lo, hi, _p(acc), _p(y)), "qgemm")
     return acc, y
 
 

@@ -395,3 +395,84 @@ int oxref_gemm_int8(int64_t M, int64_t N, int64_t K, const int8_t* xq,
   }
   return bad ? OXREF_ERANGE : OXREF_OK;
 }
+
+/* requantisation into [lo, hi] (int8 or uint8 output) */
+static int32_t requant_range(int64_t acc, float x_s, float w_s, float y_s, int32_t y_zp,
+                             int32_t lo, int32_t hi) {
+  double mult = ((double)x_s * (double)w_s) / (double)y_s;
+  double y = rint((double)acc * mult) + (double)y_zp;
+  if (y > (double)hi) y = (double)hi;
+  if (y < (double)lo) y = (double)lo;
+  return (int32_t)y;
+}
+
+static int q_range_ok(int32_t y_zp, int32_t y_lo, int32_t y_hi) {
+  if (!((y_lo == -128 && y_hi == 127) || (y_lo == 0 && y_hi == 255))) return 0;
+  return y_zp >= y_lo && y_zp <= y_hi;
+}
+
+int oxref_qconv2d(const oxref_conv* d, const int32_t* x, const int32_t* w,
+                  const int32_t* bias_q, int32_t x_zp, const int32_t* w_zp, float x_s,
+                  const float* w_s, float y_s, int32_t y_zp, int32_t y_lo, int32_t y_hi,
+                  int64_t* acc_out, int32_t* y_out) {
+  int64_t Ho, Wo;
+  int rc = oxref_conv_out_dims(d, &Ho, &Wo);
+  if (rc) return rc;
+  if (!q_range_ok(y_zp, y_lo, y_hi)) return OXREF_EARG;
+  int64_t total = d->N * d->M * Ho * Wo;
+  if (total == 0) return OXREF_OK;
+  if (!x || !w) return OXREF_EARG;
+  if (y_out && !w_s) return OXREF_EARG;
+  int64_t cpg = d->C / d->group;
+  int bad = 0;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t o = 0; o < total; ++o) {
+    int64_t ow = o % Wo, oh = (o / Wo) % Ho, m = (o / (Wo * Ho)) % d->M,
+            n = o / (Wo * Ho * d->M);
+    int64_t gm = m / (d->M / d->group);
+    int64_t wz = w_zp ? (int64_t)w_zp[m] : 0;
+    int64_t acc = bias_q ? (int64_t)bias_q[m] : 0;
+    for (int64_t c = 0; c < cpg; ++c) {
+      const int32_t* xplane = x + ((n * d->C) + gm * cpg + c) * d->H * d->W;
+      const int32_t* wk = w + ((m * cpg) + c) * d->kH * d->kW;
+      for (int64_t kh = 0; kh < d->kH; ++kh) {
+        int64_t ih = oh * d->s_h - d->p_t + kh * d->d_h;
+        if (ih < 0 || ih >= d->H) continue;
+        for (int64_t kw = 0; kw < d->kW; ++kw) {
+          int64_t iw = ow * d->s_w - d->p_l + kw * d->d_w;
+          if (iw < 0 || iw >= d->W) continue;
+          acc += ((int64_t)xplane[ih * d->W + iw] - x_zp) * ((int64_t)wk[kh * d->kW + kw] - wz);
+        }
+      }
+    }
+    if (acc >= INT32_LIMIT || acc < -INT32_LIMIT) bad = 1;
+    if (acc_out) acc_out[o] = acc;
+    if (y_out) y_out[o] = requant_range(acc, x_s, w_s[m], y_s, y_zp, y_lo, y_hi);
+  }
+  return bad ? OXREF_ERANGE : OXREF_OK;
+}
+
+int oxref_qgemm(int64_t M, int64_t N, int64_t K, const int32_t* x, const int32_t* w,
+                const int32_t* bias_q, int32_t x_zp, const int32_t* w_zp, float x_s,
+                const float* w_s, float y_s, int32_t y_zp, int32_t y_lo, int32_t y_hi,
+                int64_t* acc_out, int32_t* y_out) {
+  if (M < 0 || N < 0 || K < 0) return OXREF_EARG;
+  if (!q_range_ok(y_zp, y_lo, y_hi)) return OXREF_EARG;
+  if (M * N == 0) return OXREF_OK;
+  if (K > 0 && (!x || !w)) return OXREF_EARG;
+  if (y_out && !w_s) return OXREF_EARG;
+  int bad = 0;
+  int64_t total = M * N;
+#pragma omp parallel for schedule(static) reduction(| : bad)
+  for (int64_t o = 0; o < total; ++o) {
+    int64_t i = o / N, j = o % N;
+    int64_t wz = w_zp ? (int64_t)w_zp[j] : 0;
+    int64_t acc = bias_q ? (int64_t)bias_q[j] : 0;
+    for (int64_t k = 0; k < K; ++k)
+      acc += ((int64_t)x[i * K + k] - x_zp) * ((int64_t)w[j * K + k] - wz);
+    if (acc >= INT32_LIMIT || acc < -INT32_LIMIT) bad = 1;
+    if (acc_out) acc_out[o] = acc;
+    if (y_out) y_out[o] = requant_range(acc, x_s, w_s[j], y_s, y_zp, y_lo, y_hi);
+  }
+  return bad ? OXREF_ERANGE : OXREF_OK;
+}

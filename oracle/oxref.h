@@ -25,7 +25,9 @@
  *     (the Gelu composite of the Onyxia README, read as the exact erf form).
  *   - Static int8 (QLinearConv / QLinearMatMul with int32 bias) as listed in
  *     the onnx-vulkan-rs feature list, with int64 accumulation and a fixed
- *     fp64 requantisation with round-half-to-even.
+ *     fp64 requantisation with round-half-to-even; and the same with uint8
+ *     activations or outputs and per-channel weight zero points (the full
+ *     zero-point correction of the onnx-vulkan-rs design notes).
  *
  * Floating point: every input arrives as double (fp32 and bf16 values widen
  * exactly); sums run in double in a fixed loop order (channel, then kernel
@@ -163,6 +165,29 @@ int oxref_gemm_int8(int64_t M, int64_t N, int64_t K, const int8_t* xq,
                     const int8_t* wq, const int32_t* bias_q, int32_t x_zp,
                     float x_s, const float* w_s, float y_s, int32_t y_zp,
                     int64_t* acc_out, int8_t* y_out);
+
+/* Quantised convolution with both zero points (QLinearConv / ConvInteger as
+ * the onnx-vulkan-rs design notes write the zero-point correction: every
+ * product is (x - x_zp) * (w - w_zp)).  Activations and weights arrive as
+ * int32 holding their stored integers (int8 or uint8 values); the weight
+ * zero point is per output channel (w_zp [M], NULL = all 0):
+ *   acc[n,m,oh,ow] = bias_q[m] + sum over in-bounds taps (x - x_zp) * (w - w_zp[m])
+ * (a tap in the padding holds the value x_zp and contributes nothing), in
+ * int64 (OXREF_ERANGE if any |acc| >= 2^31), then
+ *   y = clamp(rint((double)acc * mult[m]) + y_zp, y_lo, y_hi)
+ * with mult[m] as above and [y_lo, y_hi] = [-128, 127] (int8 output) or
+ * [0, 255] (uint8 output).  acc_out / y_out may be NULL. */
+int oxref_qconv2d(const oxref_conv* d, const int32_t* x, const int32_t* w,
+                  const int32_t* bias_q, int32_t x_zp, const int32_t* w_zp, float x_s,
+                  const float* w_s, float y_s, int32_t y_zp, int32_t y_lo, int32_t y_hi,
+                  int64_t* acc_out, int32_t* y_out);
+
+/* The same for a Gemm / MatMulInteger, X [M,K], W stored [N,K], channel j:
+ *   acc[i,j] = bias_q[j] + sum_k (x[i,k] - x_zp) * (w[j,k] - w_zp[j]) */
+int oxref_qgemm(int64_t M, int64_t N, int64_t K, const int32_t* x, const int32_t* w,
+                const int32_t* bias_q, int32_t x_zp, const int32_t* w_zp, float x_s,
+                const float* w_s, float y_s, int32_t y_zp, int32_t y_lo, int32_t y_hi,
+                int64_t* acc_out, int32_t* y_out);
 
 /* The requantisation step alone, for one accumulator (used by the tie and
  * saturation checks). */

@@ -493,6 +493,80 @@ def test_int8_accumulator_range_is_asserted():
     assert e.value.code == oracle.ERANGE
 
 
+# ---------------------------- uint8 activations, asymmetric weight zero points --
+
+def test_qconv_acc_equals_float64_conv_of_both_shifted_operands():
+    # uint8 activations, per-channel weight zero points: every product is
+    # (x - x_zp)(w - w_zp[m]); the padding holds x_zp, i.e. zero after the shift
+    r = np.random.default_rng(31)
+    x = r.integers(0, 256, (2, 4, 6, 7))
+    w = r.integers(-128, 128, (6, 2, 3, 3))
+    wz = r.integers(-128, 128, 6)
+    bias = r.integers(-1000, 1000, 6).astype(np.int32)
+    zx = 141
+    acc, _ = oracle.qconv2d(x, w, bias, zx, wz, 0.05, np.full(6, 0.004, np.float32), 0.3, 3,
+                            False, (1, 2), (1, 2, 0, 1), (2, 1), 2)
+    ref = torch_conv(x.astype(np.float64) - zx, w.astype(np.float64) - wz[:, None, None, None],
+                     bias.astype(np.float64), (1, 2), (1, 2, 0, 1), (2, 1), 2)
+    assert np.array_equal(acc.astype(np.float64), ref)
+
+
+def test_qgemm_four_term_identity():
+    # onnx-vulkan-rs design notes, the zero-point correction in full:
+    # sum (a-az)(b-bz) = sum ab - az*sum b - bz*sum a + K*az*bz, with a
+    # per-channel bz over a Gemm on uint8 activations
+    r = np.random.default_rng(32)
+    K = 72
+    x = r.integers(0, 256, (11, K))
+    w = r.integers(-128, 128, (7, K))
+    wz = r.integers(-128, 128, 7)
+    zx = 200
+    acc, _ = oracle.qgemm(x, w, None, zx, wz, 0.1, np.full(7, 0.01, np.float32), 1.0, 0)
+    x64, w64 = x.astype(np.int64), w.astype(np.int64)
+    four = (x64 @ w64.T - zx * w64.sum(1)[None, :] - wz[None, :] * x64.sum(1)[:, None]
+            + K * zx * wz[None, :])
+    assert np.array_equal(acc, four)
+
+
+def test_qconv_reduces_to_the_symmetric_int8_conv():
+    # int8 activations with every weight zero point 0 is the symmetric case
+    r = np.random.default_rng(33)
+    x = r.integers(-128, 128, (1, 6, 5, 8)).astype(np.int8)
+    w = r.integers(-127, 128, (4, 6, 3, 3)).astype(np.int8)
+    bias = r.integers(-500, 500, 4).astype(np.int32)
+    ws = np.full(4, 0.003, np.float32)
+    acc0, y0 = oracle.conv2d_int8(x, w, bias, -9, 0.04, ws, 0.2, -3, (2, 1), (1, 1, 1, 1))
+    acc1, y1 = oracle.qconv2d(x, w, bias, -9, np.zeros(4, np.int32), 0.04, ws, 0.2, -3, False,
+                              (2, 1), (1, 1, 1, 1))
+    assert np.array_equal(acc0, acc1) and np.array_equal(y0.astype(np.int32), y1)
+
+
+def test_qconv_uint8_shift_by_128_is_exact():
+    # u - zu = (u - 128) - (zu - 128): uint8 activations equal int8 ones
+    # offset by 128, zero point included (the identity the GPU path uses)
+    r = np.random.default_rng(34)
+    u = r.integers(0, 256, (2, 3, 7, 7))
+    w = r.integers(-128, 128, (5, 3, 3, 3))
+    wz = r.integers(-128, 128, 5)
+    ws = np.full(5, 0.002, np.float32)
+    a0, _ = oracle.qconv2d(u, w, None, 77, wz, 0.05, ws, 0.5, 0, False, (1, 1), (2, 0, 1, 1))
+    a1, _ = oracle.qconv2d(u - 128, w, None, 77 - 128, wz, 0.05, ws, 0.5, 0, False, (1, 1), (2, 0, 1, 1))
+    assert np.array_equal(a0, a1)
+
+
+def test_q_uint8_output_range_and_rounding():
+    # multiplier 1/2: ties round half to even, then + y_zp, clamp to [0, 255]
+    xs, ws, ys = 2.0 ** -4, 2.0 ** -3, 2.0 ** -6
+    x = np.array([[1], [3], [5], [-1], [-3], [400], [-400]])
+    w = np.array([[1]])
+    _, y = oracle.qgemm(x, w, None, 0, None, xs, np.array([ws], np.float32), ys, 128, True)
+    assert y[:, 0].tolist() == [128, 130, 130, 128, 126, 255, 0]
+    _, y = oracle.qgemm(x, w, None, 0, None, xs, np.array([ws], np.float32), ys, 0, True)
+    assert y[:, 0].tolist() == [0, 2, 2, 0, 0, 200, 0]
+    with pytest.raises(oracle.OracleError):
+        oracle.qgemm(x, w, None, 0, None, xs, np.array([ws], np.float32), ys, 256, True)
+
+
 # ------------------------------------------------------------- determinism --
 
 def test_bit_identical_for_any_thread_count():
