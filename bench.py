@@ -43,6 +43,9 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="capture one step's launches in a HIP graph (torch.cuda.CUDAGraph) and time "
                         "K replays of it instead of K eager steps")
+    p.add_argument("--quant", default="s8", choices=["s8", "u8", "s8-wzp", "u8-wzp"],
+                   help="int8 workload: int8 ('s8') or uint8 ('u8') activations and outputs, "
+                        "with ('-wzp') or without per-channel weight zero points")
     p.add_argument("--residual", action="store_true",
                    help="resnet50 / mobilenetv2: the block-closing convolutions add a residual "
                         "input before their activation (ox_conv2d_fused_res)")
@@ -226,27 +229,40 @@ def matmul_layers(ox, synth, torch, stream):
                   oracle_at, 16 * 64 * 64, 128)]
 
 
-def int8_layers(ox, synth, torch, stream):
+def int8_layers(ox, synth, torch, stream, quant="s8"):
+    """quant 's8': int8 activations and outputs, symmetric weights; 'u8':
+    uint8 activations and outputs (the same values shifted by 128, zero
+    points too); '-wzp': per-channel weight zero points in [-8, 8]."""
     import oracle
     out = []
+    u8 = quant.startswith("u8")
+    wz = quant.endswith("-wzp")
     for li, l in enumerate(synth.conformer_int8_layers()):
         t = synth.int8_inputs(l, 4, li)
+        wzp = None
+        if u8:
+            t = dict(t, xq=(t["xq"].astype(np.int16) + 128).astype(np.uint8), x_zp=t["x_zp"] + 128,
+                     y_zp=t["y_zp"] + 128)
+        if wz:
+            wzp = np.random.default_rng(900 + li).integers(-8, 9, t["wq"].shape[0]).astype(np.int32)
         blk = torch.from_numpy(ox.ox_int8_prepare(t["wq"], t["w_s"], t["x_s"], t["x_zp"], t["y_s"],
-                                                  t["y_zp"], t["bias_q"])).cuda()
+                                                  t["y_zp"], t["bias_q"], w_zp=wzp, x_unsigned=u8,
+                                                  y_unsigned=u8)).cuda()
         xq, wq = torch.from_numpy(t["xq"]).cuda(), torch.from_numpy(t["wq"]).cuda()
+        ydt = torch.uint8 if u8 else torch.int8
         if l.kind == "gemm":
-            Y = torch.empty((l.M, l.N), dtype=torch.int8, device="cuda")
+            Y = torch.empty((l.M, l.N), dtype=ydt, device="cuda")
             args = (ox.OX_I8, l.M, l.N, l.K, 0, 1, 1.0, xq.data_ptr(), wq.data_ptr(), 1.0, None, 0,
                     Y.data_ptr(), blk.data_ptr(), stream)
             fn = ox.lib.ox_gemm_fused
             flops = 2.0 * l.M * l.N * l.K
             nout = l.M * l.N
             variant = "mfma/i8"
-            nbytes = l.M * l.K + l.N * l.K + l.M * l.N + 12 * l.N
+            nbytes = l.M * l.K + l.N * l.K + l.M * l.N + 16 * l.N
         else:
             c = l.conv
             ho, wo = c.out_hw()
-            Y = torch.empty((c.N, c.M, ho, wo), dtype=torch.int8, device="cuda")
+            Y = torch.empty((c.N, c.M, ho, wo), dtype=ydt, device="cuda")
             d = ox.conv_desc(c.N, c.C, c.H, c.W, c.M, c.kh, c.kw, (c.stride, c.stride), c.onnx_pads,
                              (1, 1), c.group)
             args = (C.byref(d), xq.data_ptr(), wq.data_ptr(), blk.data_ptr(), ox.OX_I8,
@@ -256,13 +272,23 @@ def int8_layers(ox, synth, torch, stream):
             nout = c.N * c.M * ho * wo
             variant = ox.ox_conv2d_variant("i8", c.N, c.C, c.H, c.W, c.M, c.kh, c.kw,
                                            (c.stride, c.stride), c.onnx_pads, (1, 1), c.group)
-            nbytes = c.nbytes(1) - c.M + 12 * c.M
+            nbytes = c.nbytes(1) - c.M + 16 * c.M
         keep = (blk, xq, wq, Y, args)
 
         def launch(fn=fn, args=args, keep=keep):
             return fn(*args)
 
-        def oracle_at(idx, l=l, t=t):
+        def oracle_at(idx, l=l, t=t, wzp=wzp):
+            if u8 or wz:
+                if l.kind == "gemm":
+                    _, y = oracle.qgemm(t["xq"], t["wq"], t["bias_q"], t["x_zp"], wzp, t["x_s"],
+                                        t["w_s"], t["y_s"], t["y_zp"], u8)
+                else:
+                    c = l.conv
+                    _, y = oracle.qconv2d(t["xq"], t["wq"], t["bias_q"], t["x_zp"], wzp, t["x_s"],
+                                          t["w_s"], t["y_s"], t["y_zp"], u8, (c.stride, c.stride),
+                                          c.onnx_pads, (1, 1), c.group)
+                return y.ravel()[idx]
             if l.kind == "gemm":
                 acc, y = oracle.gemm_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"],
                                           t["w_s"], t["y_s"], t["y_zp"])
@@ -423,9 +449,14 @@ def main():
         cfg = {"workload": "batched MatMul [16,64,128] x [16,128,64]"}
     else:
         dtype = "i8"
-        layers = int8_layers(ox, synth, torch, sp)
+        layers = int8_layers(ox, synth, torch, sp, args.quant)
         cfg = {"workload": "static int8 conformer block, T=1000, d_model=1024 "
                            "(FFN, QKV, depthwise 1-D k9, pointwise)"}
+        if args.quant != "s8":
+            cfg["quant"] = {"u8": "uint8 activations and outputs",
+                            "s8-wzp": "per-channel weight zero points",
+                            "u8-wzp": "uint8 activations and outputs, per-channel weight zero "
+                                      "points"}[args.quant]
 
     def step():
         for L in layers:

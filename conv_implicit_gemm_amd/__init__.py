@@ -27,7 +27,8 @@ EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_i
            "ox_conv2d_variant", "ox_conv2d_fused_packed", "ox_conv2d_packed_weights_bytes",
            "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
            "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
-           "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool")
+           "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool",
+           "ox_int8_prepare_ex")
 
 
 class OxError(RuntimeError):
@@ -70,6 +71,7 @@ def _load():
         "ox_fold_batchnorm": (I, [I64, I64, P, P, P, P, P, P, F, P, P]),
         "ox_int8_params_bytes": (C.c_size_t, [I64]),
         "ox_int8_prepare": (I, [I64, I64, P, P, F, I32, F, I32, P, P]),
+        "ox_int8_prepare_ex": (I, [I64, I64, P, P, P, F, I32, I, F, I32, I, P, P]),
         "ox_last_error": (C.c_char_p, []),
         "ox_version": (C.c_char_p, []),
     }
@@ -105,7 +107,10 @@ def _torch():
 
 def _dtype_code(t):
     torch = _torch()
-    m = {torch.float32: OX_F32, torch.bfloat16: OX_BF16, torch.int8: OX_I8, torch.int32: OX_I32}
+    # uint8 tensors travel as bytes through the int8 calls: the parameter
+    # block (ox_int8_prepare(..., x_unsigned / y_unsigned)) says how to read them
+    m = {torch.float32: OX_F32, torch.bfloat16: OX_BF16, torch.int8: OX_I8, torch.uint8: OX_I8,
+         torch.int32: OX_I32}
     if t.dtype not in m:
         raise TypeError("unsupported tensor dtype %s" % t.dtype)
     return m[t.dtype]
@@ -334,7 +339,9 @@ def ox_conv2d_pack_weights(W, dtype, N, Cin, H, Wd, stride=(1, 1), pads=(0, 0, 0
 
 def ox_conv2d_int8(Xq, Wq, int8_params, y_type="i8", stride=(1, 1), pads=(0, 0, 0, 0),
                    dilation=(1, 1), group=1, Y=None, stream=None):
-    """Static int8 Conv: Xq int8 [N,C,H,W], Wq int8 [M,C/g,kH,kW]; y_type 'i8' or 'i32'."""
+    """Static int8 Conv: Xq int8 (or uint8, as the parameter block says) [N,C,H,W],
+    Wq int8 [M,C/g,kH,kW]; y_type 'i8', 'u8' (uint8 outputs, as the block
+    says) or 'i32'."""
     torch = _torch()
     for t, n in ((Xq, "Xq"), (Wq, "Wq"), (Y, "Y")):
         _dense(t, n)
@@ -345,7 +352,8 @@ def ox_conv2d_int8(Xq, Wq, int8_params, y_type="i8", stride=(1, 1), pads=(0, 0, 
     if Y is None:
         ho, wo = conv_out_hw(H, Wd, kH, kW, stride, pads, dilation)
         Y = torch.empty((N, M, max(ho, 0), max(wo, 0)),
-                        dtype=torch.int32 if yt == OX_I32 else torch.int8, device=Xq.device)
+                        dtype=torch.int32 if yt == OX_I32 else
+                        (torch.uint8 if y_type == "u8" else torch.int8), device=Xq.device)
     _check(lib.ox_conv2d_int8(C.byref(d), _ptr(Xq), _ptr(Wq), _ptr(int8_params), yt, _ptr(Y),
                               _stream(stream)))
     return Y
@@ -388,9 +396,30 @@ def ox_int8_params_bytes(M):
     return int(lib.ox_int8_params_bytes(int(M)))
 
 
-def ox_int8_prepare(Wq, w_scale, x_scale, x_zp, y_scale, y_zp, bias_q=None):
+def ox_int8_prepare(Wq, w_scale, x_scale, x_zp, y_scale, y_zp, bias_q=None, w_zp=None,
+                    x_unsigned=False, y_unsigned=False):
     """Build the int8 parameter block on the host; returns it as a uint8 numpy array
-    (copy it to the device, e.g. torch.from_numpy(block).cuda())."""
+    (copy it to the device, e.g. torch.from_numpy(block).cuda()).
+    w_zp: per-channel weight zero points (or None); x_unsigned / y_unsigned:
+    activations / requantised outputs are uint8.  Wq is int8 (uint8 weights:
+    convert them with ox_int8_weights_from_uint8 first, and give the
+    converted weights to the calls as well)."""
+    if np.asarray(Wq).dtype != np.int8:
+        raise TypeError("Wq must be int8 (convert uint8 weights with ox_int8_weights_from_uint8)")
+    if w_zp is not None or x_unsigned or y_unsigned:
+        Wq = _np(Wq, np.int8)
+        M = Wq.shape[0]
+        kper = int(Wq.size // M) if M else 0
+        ws = _np(w_scale, np.float32)
+        bq = None if bias_q is None else _np(bias_q, np.int32)
+        wz = None if w_zp is None else _np(np.broadcast_to(np.asarray(w_zp, np.int32), (M,)), np.int32)
+        out = np.zeros(ox_int8_params_bytes(M), np.uint8)
+        _check(lib.ox_int8_prepare_ex(M, kper, Wq.ctypes.data, None if wz is None else wz.ctypes.data,
+                                      ws.ctypes.data, float(np.float32(x_scale)), int(x_zp),
+                                      int(bool(x_unsigned)), float(np.float32(y_scale)), int(y_zp),
+                                      int(bool(y_unsigned)), None if bq is None else bq.ctypes.data,
+                                      out.ctypes.data))
+        return out
     Wq = _np(Wq, np.int8)
     M = Wq.shape[0]
     kper = int(Wq.size // M) if M else 0
@@ -401,3 +430,17 @@ def ox_int8_prepare(Wq, w_scale, x_scale, x_zp, y_scale, y_zp, bias_q=None):
                                int(x_zp), float(np.float32(y_scale)), int(y_zp),
                                None if bq is None else bq.ctypes.data, out.ctypes.data))
     return out
+
+
+def ox_int8_weights_from_uint8(Wq_u8, w_zp_u8):
+    """uint8 weights with (per-channel or scalar) uint8 zero points -> the
+    int8 weights w - 128 and int32 zero points w_zp - 128 the int8 calls take;
+    every product (w - w_zp) is unchanged."""
+    Wq_u8 = np.asarray(Wq_u8)
+    if Wq_u8.dtype != np.uint8:
+        raise TypeError("Wq_u8 must be uint8")
+    M = Wq_u8.shape[0]
+    zp = np.broadcast_to(np.asarray(w_zp_u8, np.int32), (M,))
+    if zp.min(initial=0) < 0 or zp.max(initial=0) > 255:
+        raise ValueError("uint8 weight zero points must lie in [0, 255]")
+    return (Wq_u8.astype(np.int16) - 128).astype(np.int8), (zp - 128).astype(np.int32)

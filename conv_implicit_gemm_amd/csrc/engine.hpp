@@ -206,15 +206,46 @@ __device__ __forceinline__ int8_t requant(int acc, double mult, int yzp) {
 struct I8View {
   const double* mult;
   const int32_t* bias;
-  int xzp, yzp;
+  const int32_t* wzp;   // per-channel weight zero points
+  int xzp, yzp;         // zero points of the int8 view (a uint8 one minus 128)
+  uint32_t xm;          // 0x80808080 for uint8 activations (their int8 view), else 0
+  int ym;               // 0x80 for uint8 outputs, else 0
+  bool wz;              // some weight zero point is nonzero
   __device__ __forceinline__ void init(const void* p) {
     const Int8Header* h = (const Int8Header*)p;
     xzp = h->x_zp;
     yzp = h->y_zp;
+    const int f = h->flags;
+    xm = (f & kI8XUnsigned) ? 0x80808080u : 0u;
+    ym = (f & kI8YUnsigned) ? 0x80 : 0;
+    wz = (f & kI8WZp) != 0;
     mult = (const double*)((const char*)p + sizeof(Int8Header));
     bias = (const int32_t*)((const char*)p + sizeof(Int8Header) + 8 * h->M);
+    wzp = bias + h->M;
+  }
+  // requantised output byte (a uint8 output is its int8 view with the top bit flipped)
+  __device__ __forceinline__ int8_t out(int acc, int ch) const {
+    return (int8_t)(requant(acc, mult[ch], yzp) ^ ym);
   }
 };
+
+// FLIP (int8 only): a uint8 operand is written to LDS in its int8 view, u -
+// 128 (the top bit of every byte flipped).  The flip is applied as a chunk is
+// stored, not as it is loaded, so the loads stay in flight across the MMAs;
+// zeros a loader supplied past K become -128 (they meet zero weights).
+template <int DT, bool FLIP>
+__device__ __forceinline__ u32x4_t flip_chunk(const u32x4_t& v) {
+  if constexpr (DT == DT_I8 && FLIP) return v ^ 0x80808080u;
+  else return v;
+}
+
+// sum of the sixteen int8 values of a 16-byte fragment, added to s
+__device__ __forceinline__ int sum16_i8(const u32x4_t& v, int s) {
+  s = __builtin_amdgcn_sdot4((int)v[0], 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4((int)v[1], 0x01010101, s, false);
+  s = __builtin_amdgcn_sdot4((int)v[2], 0x01010101, s, false);
+  return __builtin_amdgcn_sdot4((int)v[3], 0x01010101, s, false);
+}
 
 // ---------------------------------------------------------------- loaders --
 //
@@ -228,7 +259,7 @@ template <int BKU> struct Lds {
 };
 
 // Operand stored K-contiguous: [rows, K] with row stride ld.
-template <int DT, int BROWS, int BKU>
+template <int DT, int BROWS, int BKU, bool FLIP = false>
 struct LoadRowK {
   typedef typename Traits<DT>::T T;
   enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
@@ -272,7 +303,7 @@ struct LoadRowK {
     for (int i = 0; i < NCH; ++i) {
       const int q = threadIdx.x + i * kThreads;
       if (TOTAL % kThreads == 0 || q < TOTAL)
-        *(u32x4_t*)(lds + (q / CPR) * ROWB + (q % CPR) * 16) = r[i];
+        *(u32x4_t*)(lds + (q / CPR) * ROWB + (q % CPR) * 16) = flip_chunk<DT, FLIP>(r[i]);
     }
   }
 };
@@ -280,7 +311,7 @@ struct LoadRowK {
 // Operand stored K-strided: element k of this thread's column at
 // colbase[k*ld].  The thread keeps one column (tid % BCOLS) for the whole
 // kernel and gathers whole chunks of K for it.
-template <int DT, int BCOLS, int BKU>
+template <int DT, int BCOLS, int BKU, bool FLIP = false>
 struct LoadColK {
   typedef typename Traits<DT>::T T;
   enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
@@ -317,7 +348,7 @@ struct LoadColK {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = ch0 + i * STEP;
-      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = r[i];
+      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = flip_chunk<DT, FLIP>(r[i]);
     }
   }
 };
@@ -326,7 +357,7 @@ struct LoadColK {
 // (img, oh, ow), k = (c, kh, kw) in the weight's own order, element =
 // X[img, c, oh*sh - pt + kh*dh, ow*sw - pl + kw*dw], or `pad` outside the
 // image (0 for floats; x_zp for int8, whose zero-point fold expects it).
-template <int DT, int BCOLS, int BKU>
+template <int DT, int BCOLS, int BKU, bool FLIP = false>
 struct LoadIm2col {
   typedef typename Traits<DT>::T T;
   enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
@@ -335,8 +366,9 @@ struct LoadIm2col {
   int ih0, iw0;
   bool valid;
   int H, W, HW, kH, kW, KK, dh, dw, K;
-  T pad;
+  T pad;                // as stored in X (flipped with the rest under FLIP)
   u32x4_t r[NCH];
+
 
   __device__ __forceinline__ void load(int k0) {
     const int ch0 = threadIdx.x / BCOLS;
@@ -378,7 +410,7 @@ struct LoadIm2col {
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = ch0 + i * STEP;
-      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = r[i];
+      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = flip_chunk<DT, FLIP>(r[i]);
     }
   }
 };
@@ -391,9 +423,13 @@ template <int DT, int BM, int BN> struct WaveTile {
 };
 
 // The K loop shared by every problem: accumulates into acc[FM][FN].
-template <int DT, int BM, int BN, int BKU, class LA, class LB>
+// SUMS (int8 only): 1 also sums the int8 values of every A row this lane
+// reads into ks[fm], 2 of every B column into ks[fn]: the per-row /
+// per-column activation sums of the weight zero-point term.
+template <int DT, int BM, int BN, int BKU, int SUMS = 0, class LA, class LB>
 __device__ __forceinline__ void engine_mainloop(LA& la, LB& lb, int K, char* smem,
-                                                typename Traits<DT>::Acc (&acc)[BM / 32][BN / 32]) {
+                                                typename Traits<DT>::Acc (&acc)[BM / 32][BN / 32],
+                                                int* ks = nullptr) {
   typedef WaveTile<DT, BM, BN> WT;
   enum { ROWB = Lds<BKU>::ROWB, A_BYTES = BM * ROWB, B_BYTES = BN * ROWB,
          KSTEP = BKU * 4 * Traits<DT>::EPC };
@@ -429,6 +465,13 @@ __device__ __forceinline__ void engine_mainloop(LA& la, LB& lb, int K, char* sme
       for (int fm = 0; fm < WT::FM; ++fm)
 #pragma unroll
         for (int fn = 0; fn < WT::FN; ++fn) Mma<DT>::run(acc[fm][fn], a[fm], b[fn]);
+      if constexpr (SUMS == 1) {
+#pragma unroll
+        for (int fm = 0; fm < WT::FM; ++fm) ks[fm] = sum16_i8(a[fm], ks[fm]);
+      } else if constexpr (SUMS == 2) {
+#pragma unroll
+        for (int fn = 0; fn < WT::FN; ++fn) ks[fn] = sum16_i8(b[fn], ks[fn]);
+      }
     }
     if (more) {
       char* An = smem + ((s + 1) & 1) * (A_BYTES + B_BYTES);
@@ -436,6 +479,31 @@ __device__ __forceinline__ void engine_mainloop(LA& la, LB& lb, int K, char* sme
       lb.store(An + A_BYTES);
     }
     __syncthreads();
+  }
+}
+
+// Completes the sums of engine_mainloop<SUMS> (each lane holds a quarter of
+// the k range of one row or column) and writes them to S[row_in_tile]
+// (SUMS 1) or S[col_in_tile] (SUMS 2) in LDS; the caller synchronises.
+template <int DT, int BM, int BN, int SUMS>
+__device__ __forceinline__ void ksums_to_lds(int* ks, int* S) {
+  typedef WaveTile<DT, BM, BN> WT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lg = lane >> 4;
+  constexpr int NF = SUMS == 1 ? WT::FM : WT::FN;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    int v = ks[f];
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    if (lg == 0) {
+      if constexpr (SUMS == 1) {
+        if (wn == 0) S[wm * WT::TM + f * 16 + lr] = v;
+      } else {
+        if (wm == 0) S[wn * WT::TN + f * 16 + lr] = v;
+      }
+    }
   }
 }
 

@@ -24,18 +24,19 @@ template <> __device__ __forceinline__ void store_float<uint16_t>(uint16_t* y, f
 // L = A' (rows = i), R = B' (cols = j).  LK: A stored [M,K]; !LK: [K,M].
 // RK: B stored [N,K] (transB); !RK: [K,N].  z = batch index.
 
-template <int DT, int BM, int BN, int BKU, bool LK, bool RK>
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
+// One block's tile.  int8: rows are activations (x_q [M,K]), columns weight
+// channels; FLIP reads uint8 activations in their int8 view, WZ adds the
+// weight zero-point term (both chosen per launch from the parameter block).
+template <int DT, int BM, int BN, int BKU, bool LK, bool RK, bool FLIP, bool WZ>
+__device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, const I8View& q) {
   typedef typename Traits<DT>::T T;
   typedef typename Traits<DT>::Acc Acc;
-  enum { ROWB = Lds<BKU>::ROWB };
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
 
   const int z = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
   const T* L = (const T*)a.L + (int64_t)z * a.sl;
   const T* R = (const T*)a.R + (int64_t)z * a.sr;
 
-  typename std::conditional<LK, LoadRowK<DT, BM, BKU>, LoadColK<DT, BM, BKU>>::type la;
+  typename std::conditional<LK, LoadRowK<DT, BM, BKU, FLIP>, LoadColK<DT, BM, BKU, FLIP>>::type la;
   typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
   if constexpr (LK) {
     la.init(L, a.ldl, row0, a.rows, a.K, a.l_vec);
@@ -56,23 +57,37 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
 #pragma unroll
     for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-  engine_mainloop<DT, BM, BN, BKU>(la, lb, a.K, smem, acc);
+  int ks[WaveTile<DT, BM, BN>::FM] = {};
+  engine_mainloop<DT, BM, BN, BKU, WZ ? 1 : 0>(la, lb, a.K, smem, acc, ks);
 
   if constexpr (DT == DT_I8) {
-    I8View q;
-    q.init(a.i8);
+    // weight zero points: acc -= w_zp[ch] * sum_k (x - x_zp) over the row,
+    // the row sums completed in LDS (all in wrapping 32-bit arithmetic)
+    int* S = (int*)smem;
+    if constexpr (WZ) {
+      ksums_to_lds<DT, BM, BN, 1>(ks, S);
+      __syncthreads();
+    }
+    // sum_k (x - x_zp) = S - K*x_zp; under FLIP the loader's zeros past K
+    // were summed as -128 each
+    constexpr int KSTEP = BKU * 4 * Traits<DT>::EPC;
+    const int kzx = a.K * q.xzp - (FLIP ? 128 * ((a.K + KSTEP - 1) / KSTEP * KSTEP - a.K) : 0);
+    auto full = [&](int v, int r, int ch) -> int {
+      uint32_t u = (uint32_t)v + (uint32_t)q.bias[ch];
+      if constexpr (WZ) u -= (uint32_t)q.wzp[ch] * (uint32_t)(S[r] - kzx);
+      return (int)u;
+    };
     if (a.out_dt == DT_I32) {
       int32_t* Y = (int32_t*)a.Y + (int64_t)z * a.sy;
       for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
         const int row = row0 + r, col = col0 + c;
-        if (row < a.rows && col < a.cols) Y[(int64_t)row * a.ldy + col] = v + q.bias[col];
+        if (row < a.rows && col < a.cols) Y[(int64_t)row * a.ldy + col] = full(v, r, col);
       });
     } else {
       int8_t* Y = (int8_t*)a.Y + (int64_t)z * a.sy;
       for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
         const int row = row0 + r, col = col0 + c;
-        if (row < a.rows && col < a.cols)
-          Y[(int64_t)row * a.ldy + col] = requant(v + q.bias[col], q.mult[col], q.yzp);
+        if (row < a.rows && col < a.cols) Y[(int64_t)row * a.ldy + col] = q.out(full(v, r, col), col);
       });
     }
   } else {
@@ -89,6 +104,25 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
         }
       });
     });
+  }
+}
+
+template <int DT, int BM, int BN, int BKU, bool LK, bool RK>
+__global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * Lds<BKU>::ROWB];
+  I8View q;
+  if constexpr (DT == DT_I8) {
+    q.init(a.i8);
+    // uniform per launch: one of four instantiations runs
+    if (q.xm) {
+      if (q.wz) gemm_tile<DT, BM, BN, BKU, LK, RK, true, true>(a, smem, q);
+      else gemm_tile<DT, BM, BN, BKU, LK, RK, true, false>(a, smem, q);
+    } else {
+      if (q.wz) gemm_tile<DT, BM, BN, BKU, LK, RK, false, true>(a, smem, q);
+      else gemm_tile<DT, BM, BN, BKU, LK, RK, false, false>(a, smem, q);
+    }
+  } else {
+    gemm_tile<DT, BM, BN, BKU, LK, RK, false, false>(a, smem, q);
   }
 }
 
@@ -131,20 +165,15 @@ int launch_gemm_dt(const GemmArgs& a, int tile, void* stream) {
 // KIND 0: implicit GEMM (im2col gathered on the fly); KIND 1: 1x1, stride 1,
 // no pad, where column n of image img is X[img, c, p] with p = n % (H*W).
 
-template <int DT, int BM, int BN, int BKU, int KIND>
-__global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
+template <int DT, int BM, int BN, int BKU, int KIND, bool FLIP, bool WZ>
+__device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I8View& q) {
   typedef typename Traits<DT>::T T;
   typedef typename Traits<DT>::Acc Acc;
-  enum { ROWB = Lds<BKU>::ROWB };
-  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * ROWB];
 
   const int g = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
   const int Mpg = a.M / a.group, cpg = a.C / a.group;
   const int KK = a.kH * a.kW, K = cpg * KK;
   const int HoWo = a.Ho * a.Wo, HW = a.H * a.W, NP = a.N * HoWo;
-
-  I8View q;
-  if constexpr (DT == DT_I8) q.init(a.i8);
 
   LoadRowK<DT, BM, BKU> la;
   la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K, a.w_vec);
@@ -155,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
   const int p = nvalid ? n - img * HoWo : 0;
   const T* xg = (const T*)a.X + ((int64_t)img * a.C + (int64_t)g * cpg) * HW;
 
-  typename std::conditional<KIND == 1, LoadColK<DT, BN, BKU>, LoadIm2col<DT, BN, BKU>>::type lb;
+  typename std::conditional<KIND == 1, LoadColK<DT, BN, BKU, FLIP>, LoadIm2col<DT, BN, BKU, FLIP>>::type lb;
   if constexpr (KIND == 1) {
     lb.init_col(xg + p, nvalid, HW, K);
   } else {
@@ -173,7 +202,9 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
     lb.dh = a.dh;
     lb.dw = a.dw;
     lb.K = K;
-    if constexpr (DT == DT_I8) lb.pad = (T)q.xzp;
+    // (int8: the padding holds x_zp in the int8 view; under FLIP it is
+    // stored as the uint8 byte, flipped with the loaded data)
+    if constexpr (DT == DT_I8) lb.pad = (T)(int8_t)(FLIP ? (q.xzp ^ 0x80) : q.xzp);
     else lb.pad = (T)0;
   }
 
@@ -183,20 +214,38 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
 #pragma unroll
     for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
 
-  engine_mainloop<DT, BM, BN, BKU>(la, lb, K, smem, acc);
+  int ks[WaveTile<DT, BM, BN>::FN] = {};
+  engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0>(la, lb, K, smem, acc, ks);
 
   auto out_index = [&](int m, int col) -> int64_t {
     const int im = col / HoWo;
     return ((int64_t)im * a.M + m) * HoWo + (col - im * HoWo);
   };
   if constexpr (DT == DT_I8) {
+    // weight zero points: acc -= w_zp[m] * sum over the pixel's taps of
+    // (x - x_zp) (padding taps hold x_zp: zero), the column sums completed in
+    // LDS (all in wrapping 32-bit arithmetic)
+    int* S = (int*)smem;
+    if constexpr (WZ) {
+      ksums_to_lds<DT, BM, BN, 2>(ks, S);
+      __syncthreads();
+    }
+    // sum over taps of (x - x_zp) = S - K*x_zp (padding taps hold x_zp);
+    // under FLIP the loader's zeros past K were summed as -128 each
+    constexpr int KSTEP = BKU * 4 * Traits<DT>::EPC;
+    const int kzx = K * q.xzp - (FLIP ? 128 * ((K + KSTEP - 1) / KSTEP * KSTEP - K) : 0);
+    auto full = [&](int v, int c, int m) -> int {
+      uint32_t u = (uint32_t)v + (uint32_t)q.bias[m];
+      if constexpr (WZ) u -= (uint32_t)q.wzp[m] * (uint32_t)(S[c] - kzx);
+      return (int)u;
+    };
     if (a.out_dt == DT_I32) {
       int32_t* Y = (int32_t*)a.Y;
       for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
         const int ml = row0 + r, col = col0 + c;
         if (ml < Mpg && col < NP) {
           const int m = g * Mpg + ml;
-          Y[out_index(m, col)] = v + q.bias[m];
+          Y[out_index(m, col)] = full(v, c, m);
         }
       });
     } else {
@@ -205,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
         const int ml = row0 + r, col = col0 + c;
         if (ml < Mpg && col < NP) {
           const int m = g * Mpg + ml;
-          Y[out_index(m, col)] = requant(v + q.bias[m], q.mult[m], q.yzp);
+          Y[out_index(m, col)] = q.out(full(v, c, m), m);
         }
       });
     }
@@ -227,6 +276,25 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
         }
       });
     });
+  }
+}
+
+template <int DT, int BM, int BN, int BKU, int KIND>
+__global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * Lds<BKU>::ROWB];
+  I8View q;
+  if constexpr (DT == DT_I8) {
+    q.init(a.i8);
+    // uniform per launch: one of four instantiations runs
+    if (q.xm) {
+      if (q.wz) conv_tile<DT, BM, BN, BKU, KIND, true, true>(a, smem, q);
+      else conv_tile<DT, BM, BN, BKU, KIND, true, false>(a, smem, q);
+    } else {
+      if (q.wz) conv_tile<DT, BM, BN, BKU, KIND, false, true>(a, smem, q);
+      else conv_tile<DT, BM, BN, BKU, KIND, false, false>(a, smem, q);
+    }
+  } else {
+    conv_tile<DT, BM, BN, BKU, KIND, false, false>(a, smem, q);
   }
 }
 

@@ -102,6 +102,17 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
     q.init(a.i8);
     padv = (L)q.xzp;
   }
+  // an input element as staged: int8 in its int8 view (a uint8 byte with the
+  // top bit flipped, u - 128), the float types widened
+  auto wx = [&](T v) -> L {
+    if constexpr (DT == DT_I8) return (L)(int8_t)((uint8_t)v ^ (uint8_t)q.xm);
+    else return widen<T, L>(v);
+  };
+  // a weight as used: int8 minus its channel's zero point (Wt index i)
+  auto ww = [&](T v, int i) -> A {
+    if constexpr (DT == DT_I8) return (A)v - (q.wz ? q.wzp[i / KK] : 0);
+    else return widen<T, A>(v);
+  };
   if constexpr (MAXP) padv = (L)-INFINITY;      // MaxPool: padding never wins
 
   // Every global load of the staging phase is issued before the first wait:
@@ -153,8 +164,10 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   A b0 = (A)0;
   double m0 = 0.0;
   const T* bias = (const T*)a.bias;
+  // (int8 with weight zero points: the weights are used as w - w_zp, so the
+  // folded bias, bias - x_zp * sum w, gains x_zp * kH*kW * w_zp)
   if constexpr (DT == DT_I8) {
-    b0 = q.bias[cb];
+    b0 = q.bias[cb] + (q.wz ? q.xzp * KK * q.wzp[cb] : 0);
     m0 = q.mult[cb];
   } else {
     if (bias) b0 = widen<T, A>(bias[cb]);
@@ -173,10 +186,13 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
     }
   }
 
-  if (tid < nw) wts[tid] = widen<T, A>(w0);
-  if (tid + kThreads < nw) wts[tid + kThreads] = widen<T, A>(w1);
+  if (tid < nw) wts[tid] = ww(w0, wi0);
+  if (tid + kThreads < nw) wts[tid + kThreads] = ww(w1, wi1);
   if constexpr (!MAXP)
-    for (int i = tid + 2 * kThreads; i < nw; i += kThreads) wts[i] = widen<T, A>(Wt[widx(i)]);
+    for (int i = tid + 2 * kThreads; i < nw; i += kThreads) {
+      const int wi = widx(i);
+      wts[i] = ww(Wt[wi], wi);
+    }
   auto plane_vals = [&](int i, A bv, double mv) {
     pbias[i] = bv;
     if constexpr (DT == DT_I8) pmult[i] = mv;
@@ -184,7 +200,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   if (tid < np) plane_vals(tid, b0, m0);
   for (int i = tid + kThreads; i < np; i += kThreads) {
     const int c = chan(pl0 + i);
-    if constexpr (DT == DT_I8) plane_vals(i, q.bias[c], q.mult[c]);
+    if constexpr (DT == DT_I8) plane_vals(i, q.bias[c] + (q.wz ? q.xzp * KK * q.wzp[c] : 0), q.mult[c]);
     else plane_vals(i, bias ? widen<T, A>(bias[c]) : (A)0, 0.0);
   }
 
@@ -221,16 +237,16 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
       const int k = W - cc;                                // cells left in this row
       if (k >= EPC) {
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) d[j] = widen<T, L>(e[j]);
+        for (int j = 0; j < EPC; ++j) d[j] = wx(e[j]);
       } else {
         const int gap = (pl.WP - W) + (r + 1 == H ? (pl.RIN - H) * pl.WP : 0);
 #pragma unroll
-        for (int j = 0; j < EPC; ++j) d[j + (j >= k ? gap : 0)] = widen<T, L>(e[j]);
+        for (int j = 0; j < EPC; ++j) d[j + (j >= k ? gap : 0)] = wx(e[j]);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < EPC; ++j) {
-        dst0[(pp * pl.RIN + r) * pl.WP + cc] = widen<T, L>(e[j]);
+        dst0[(pp * pl.RIN + r) * pl.WP + cc] = wx(e[j]);
         if (++cc == W) {
           cc = 0;
           if (++r == H) {          // next plane (np > 1 only: a one-plane span ends first)
@@ -248,8 +264,8 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
   }
   for (int v = tid + NV * kThreads; v < nvec; v += kThreads)
     scatter(v, *(const u32x4_t*)(src0 + head + v * EPC));
-  if (tid < head) dst0[cell(tid)] = widen<T, L>(he);
-  if (tid < ntail) dst0[cell(tail0 + tid)] = widen<T, L>(te);
+  if (tid < head) dst0[cell(tid)] = wx(he);
+  if (tid < ntail) dst0[cell(tail0 + tid)] = wx(te);
   __syncthreads();
 
   // compute: strips of ST outputs along a row.  The block's output rows are
@@ -289,7 +305,7 @@ __global__ __launch_bounds__(kThreads) void dw_kernel(const ConvArgs a, const Dw
           int8_t* yp = (int8_t*)a.Y + yblock + yoff + c4;
           int8_t v[kChunk];
 #pragma unroll
-          for (int o = 0; o < kChunk; ++o) v[o] = requant(ac[o], mv, q.yzp);
+          for (int o = 0; o < kChunk; ++o) v[o] = (int8_t)(requant(ac[o], mv, q.yzp) ^ q.ym);
           if (fast || (full && ((uintptr_t)yp & 3) == 0)) {
             uint32_t w;
             __builtin_memcpy(&w, v, 4);

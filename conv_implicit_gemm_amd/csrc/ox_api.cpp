@@ -816,50 +816,77 @@ ox_status ox_fold_batchnorm(int64_t M, int64_t Kper, const float* W, const float
 
 size_t ox_int8_params_bytes(int64_t M) {
   if (M < 0) return 0;
-  return sizeof(Int8Header) + (size_t)M * (sizeof(double) + sizeof(int32_t));
+  return sizeof(Int8Header) + (size_t)M * (sizeof(double) + 2 * sizeof(int32_t));
 }
 
-ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const float* w_scale,
-                          float x_scale, int32_t x_zp, float y_scale, int32_t y_zp,
-                          const int32_t* bias_q, void* params_host_out) {
+ox_status ox_int8_prepare_ex(int64_t M, int64_t Kper, const int8_t* Wq_host, const int32_t* w_zp,
+                             const float* w_scale, float x_scale, int32_t x_zp, int x_unsigned,
+                             float y_scale, int32_t y_zp, int y_unsigned, const int32_t* bias_q,
+                             void* params_host_out) {
   const char* fn = "ox_int8_prepare";
   if (M < 0 || Kper < 0) return fail(OX_ERR_INVALID_ARG, "%s: negative size", fn);
   if (!params_host_out) return fail(OX_ERR_INVALID_ARG, "%s: params_host_out is NULL", fn);
   if (M > 0 && !w_scale) return fail(OX_ERR_INVALID_ARG, "%s: w_scale is NULL", fn);
   if (M > 0 && Kper > 0 && !Wq_host) return fail(OX_ERR_INVALID_ARG, "%s: Wq_host is NULL", fn);
-  if (x_zp < -128 || x_zp > 127) return fail(OX_ERR_INVALID_ARG, "%s: x_zp=%d outside [-128,127]", fn, x_zp);
-  if (y_zp < -128 || y_zp > 127) return fail(OX_ERR_INVALID_ARG, "%s: y_zp=%d outside [-128,127]", fn, y_zp);
+  const int32_t xlo = x_unsigned ? 0 : -128, ylo = y_unsigned ? 0 : -128;
+  if (x_zp < xlo || x_zp > xlo + 255)
+    return fail(OX_ERR_INVALID_ARG, "%s: x_zp=%d outside [%d,%d]", fn, x_zp, xlo, xlo + 255);
+  if (y_zp < ylo || y_zp > ylo + 255)
+    return fail(OX_ERR_INVALID_ARG, "%s: y_zp=%d outside [%d,%d]", fn, y_zp, ylo, ylo + 255);
   if (!(x_scale > 0.0f) || !isfinite(x_scale)) return fail(OX_ERR_INVALID_ARG, "%s: x_scale must be finite and > 0", fn);
   if (!(y_scale > 0.0f) || !isfinite(y_scale)) return fail(OX_ERR_INVALID_ARG, "%s: y_scale must be finite and > 0", fn);
-  for (int64_t m = 0; m < M; ++m)
+  bool any_wzp = false;
+  for (int64_t m = 0; m < M; ++m) {
     if (!(w_scale[m] > 0.0f) || !isfinite(w_scale[m]))
       return fail(OX_ERR_INVALID_ARG, "%s: w_scale[%lld] must be finite and > 0", fn, (long long)m);
-  if (Kper > 66000)
-    return fail(OX_ERR_UNSUPPORTED, "%s: Kper=%lld > 66000 could overflow the int32 accumulator", fn,
-                (long long)Kper);
+    if (w_zp && (w_zp[m] < -128 || w_zp[m] > 127))
+      return fail(OX_ERR_INVALID_ARG, "%s: w_zp[%lld]=%d outside [-128,127]", fn, (long long)m, w_zp[m]);
+    if (w_zp && w_zp[m] != 0) any_wzp = true;
+  }
+  // |x - x_zp| <= 255 and |w| <= 128 (|w - w_zp| <= 255 with weight zero
+  // points): the largest K whose sum stays inside int32
+  const int64_t kmax = any_wzp ? 33000 : 66000;
+  if (Kper > kmax)
+    return fail(OX_ERR_UNSUPPORTED, "%s: Kper=%lld > %lld could overflow the int32 accumulator", fn,
+                (long long)Kper, (long long)kmax);
+  // the kernels read a uint8 tensor as int8 with the top bit flipped (u - 128)
+  const int32_t xz = x_unsigned ? x_zp - 128 : x_zp;
+  const int32_t yz = y_unsigned ? y_zp - 128 : y_zp;
   char* out = (char*)params_host_out;
   Int8Header h;
   memset(&h, 0, sizeof(h));
   h.magic = kInt8Magic;
-  h.version = 1;
+  h.version = 2;
   h.M = M;
-  h.x_zp = x_zp;
-  h.y_zp = y_zp;
+  h.x_zp = xz;
+  h.y_zp = yz;
+  h.flags = (x_unsigned ? kI8XUnsigned : 0) | (y_unsigned ? kI8YUnsigned : 0) | (any_wzp ? kI8WZp : 0);
   memcpy(out, &h, sizeof(h));
   double* mult = (double*)(out + sizeof(Int8Header));
   int32_t* bfold = (int32_t*)(out + sizeof(Int8Header) + 8 * M);
+  int32_t* wz = bfold + M;
   for (int64_t m = 0; m < M; ++m) {
     int64_t wsum = 0;
     for (int64_t k = 0; k < Kper; ++k) wsum += Wq_host[m * Kper + k];
-    const int64_t bf = (bias_q ? (int64_t)bias_q[m] : 0) - (int64_t)x_zp * wsum;
+    // sum (x - x_zp) w = sum x w - x_zp sum w, in the int8 view
+    const int64_t bf = (bias_q ? (int64_t)bias_q[m] : 0) - (int64_t)xz * wsum;
     if (bf >= ((int64_t)1 << 31) || bf < -((int64_t)1 << 31))
       return fail(OX_ERR_UNSUPPORTED, "%s: folded bias of channel %lld overflows int32", fn, (long long)m);
     const double mm = ((double)x_scale * (double)w_scale[m]) / (double)y_scale;
     memcpy(mult + m, &mm, sizeof(double));
     const int32_t b32 = (int32_t)bf;
     memcpy(bfold + m, &b32, sizeof(int32_t));
+    const int32_t z32 = w_zp ? w_zp[m] : 0;
+    memcpy(wz + m, &z32, sizeof(int32_t));
   }
   return ok();
+}
+
+ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const float* w_scale,
+                          float x_scale, int32_t x_zp, float y_scale, int32_t y_zp,
+                          const int32_t* bias_q, void* params_host_out) {
+  return ox_int8_prepare_ex(M, Kper, Wq_host, nullptr, w_scale, x_scale, x_zp, 0, y_scale, y_zp, 0,
+                            bias_q, params_host_out);
 }
 
 }  // extern "C"

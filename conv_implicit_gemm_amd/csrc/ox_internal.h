@@ -39,17 +39,24 @@ inline const char* tile_name(int t) {
 }
 
 // Layout of the int8 parameter block (device copy of ox_int8_prepare's
-// output): a 32-byte header, then mult[M] (fp64), then bias_fold[M] (int32).
+// output): a 32-byte header, then mult[M] (fp64), bias_fold[M] (int32) and
+// w_zp[M] (int32).  x_zp and y_zp are the zero points as the kernels use
+// them: a uint8 tensor is read as int8 after flipping its top bit (u - 128),
+// so its zero point is stored minus 128.
 struct Int8Header {
   int32_t magic;       // 'OXI8'
-  int32_t version;     // 1
+  int32_t version;     // 2
   int64_t M;
   int32_t x_zp;
   int32_t y_zp;
-  int64_t reserved;
+  int32_t flags;       // kI8XUnsigned | kI8YUnsigned | kI8WZp
+  int32_t reserved;
 };
 static_assert(sizeof(Int8Header) == 32, "int8 header is 32 bytes");
 constexpr int32_t kInt8Magic = 0x3849584F;  // "OXI8" little-endian
+constexpr int32_t kI8XUnsigned = 1;         // activations are uint8
+constexpr int32_t kI8YUnsigned = 2;         // requantised outputs are uint8
+constexpr int32_t kI8WZp = 4;               // some weight zero point is nonzero
 
 // A GEMM on the tile engine: rows x cols output, reduction K, batch in z.
 //   out[z][r][c] = epi( sum_k L[z][r][k] * R[z][k][c] )

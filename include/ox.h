@@ -256,8 +256,8 @@ ox_status ox_fold_batchnorm(int64_t M, int64_t Kper, const float* W, const float
                             const float* var, float eps, float* W_out, float* b_out);
 
 /* Size in bytes of the int8 parameter block for M output channels
- * (a 32-byte header, then 8 B fp64 multiplier + 4 B folded int32 bias per
- * channel). */
+ * (a 32-byte header, then 8 B fp64 multiplier + 4 B folded int32 bias + 4 B
+ * weight zero point per channel). */
 size_t ox_int8_params_bytes(int64_t M);
 
 /* Prepare the int8 parameter block on the host, once per layer.  Host fp64:
@@ -272,6 +272,29 @@ size_t ox_int8_params_bytes(int64_t M);
 ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const float* w_scale,
                           float x_scale, int32_t x_zp, float y_scale, int32_t y_zp,
                           const int32_t* bias_q, void* params_host_out);
+
+/* The parameter block for the other quantisation variants (QLinearConv /
+ * QLinearMatMul with uint8 activations or outputs and per-channel weight
+ * zero points; ConvInteger / MatMulInteger through OX_I32 outputs), with
+ * the full zero-point correction of the onnx-vulkan-rs design notes:
+ *   acc = bias_q[m] + sum over in-bounds taps (x - x_zp) * (w - w_zp[m])
+ *   y   = clamp(rint(acc * mult[m]) + y_zp, lo, hi)
+ * with [lo, hi] = [0, 255] when y_unsigned, else [-128, 127].  The padding
+ * of a convolution holds x_zp (the quantised real zero).
+ * x_unsigned: the activations given to the int8 calls are uint8 and
+ * x_zp is in [0, 255] (else int8, x_zp in [-128, 127]); y_unsigned: the
+ * requantised outputs are written as uint8 and y_zp is in [0, 255].
+ * Wq_host: HOST int8 [M, Kper] (uint8 weights: pass w - 128 with
+ * w_zp - 128, which leaves every product unchanged); w_zp: HOST int32 [M] in
+ * [-128, 127] or NULL (all 0).  With a nonzero w_zp, Kper is at most 33000.
+ * The block records the signedness: the same int8 calls (ox_gemm_fused with
+ * OX_I8 / OX_I32, ox_conv2d_int8) then read and write uint8 tensors through
+ * their int8_t pointers.  ox_int8_prepare(...) is this call with w_zp = NULL
+ * and both flags 0. */
+ox_status ox_int8_prepare_ex(int64_t M, int64_t Kper, const int8_t* Wq_host, const int32_t* w_zp,
+                             const float* w_scale, float x_scale, int32_t x_zp, int x_unsigned,
+                             float y_scale, int32_t y_zp, int y_unsigned, const int32_t* bias_q,
+                             void* params_host_out);
 
 /* The message of the last failing call on this thread ("" if none). */
 const char* ox_last_error(void);

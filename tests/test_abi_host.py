@@ -287,9 +287,10 @@ def test_int8_params_block_layout(ox):
     bq = r.integers(-5000, 5000, M).astype(np.int32)
     xs, ys, xzp, yzp = np.float32(0.05), np.float32(0.7), -9, 4
     blk = ox.ox_int8_prepare(wq, ws, xs, xzp, ys, yzp, bq)
-    assert blk.size == ox.ox_int8_params_bytes(M) == 32 + 12 * M
-    magic, ver, m, xz, yz = struct.unpack_from("<iiqii", blk.tobytes(), 0)
-    assert (magic, ver, m, xz, yz) == (0x3849584F, 1, M, xzp, yzp)
+    assert blk.size == ox.ox_int8_params_bytes(M) == 32 + 16 * M
+    magic, ver, m, xz, yz, flags = struct.unpack_from("<iiqiii", blk.tobytes(), 0)
+    assert (magic, ver, m, xz, yz, flags) == (0x3849584F, 2, M, xzp, yzp, 0)
+    assert not np.frombuffer(blk.tobytes(), np.int32, M, 32 + 12 * M).any()    # w_zp all 0
     mult = np.frombuffer(blk.tobytes(), np.float64, M, 32)
     bfold = np.frombuffer(blk.tobytes(), np.int32, M, 32 + 8 * M)
     # multiplier: ((double)x_s * (double)w_s) / (double)y_s, as the oracle defines it
@@ -311,6 +312,56 @@ def test_int8_prepare_errors(ox):
         ox.ox_int8_prepare(wq, [0.01, 0.01], 0.1, 200, 0.2, 0)    # x_zp out of range
     with pytest.raises(ox.OxError):
         ox.ox_int8_prepare(wq, [0.01, 0.01], float("nan"), 0, 0.2, 0)
+
+
+def test_int8_params_block_unsigned_and_weight_zero_points(ox):
+    # uint8 activations / outputs are read as int8 with the top bit flipped:
+    # the block stores their zero points minus 128, folds with that x_zp, and
+    # records the weight zero points and the flags
+    r = np.random.default_rng(2)
+    M, K = 5, 29
+    wq = r.integers(-128, 128, (M, K)).astype(np.int8)
+    ws = r.uniform(1e-3, 1e-2, M).astype(np.float32)
+    bq = r.integers(-5000, 5000, M).astype(np.int32)
+    wz = np.array([3, 0, -128, 127, -1], np.int32)
+    xs, ys, xzp, yzp = np.float32(0.05), np.float32(0.7), 201, 17
+    blk = ox.ox_int8_prepare(wq, ws, xs, xzp, ys, yzp, bq, w_zp=wz, x_unsigned=True, y_unsigned=True)
+    magic, ver, m, xz, yz, flags = struct.unpack_from("<iiqiii", blk.tobytes(), 0)
+    assert (ver, m, xz, yz, flags) == (2, M, xzp - 128, yzp - 128, 7)
+    bfold = np.frombuffer(blk.tobytes(), np.int32, M, 32 + 8 * M)
+    assert np.array_equal(np.frombuffer(blk.tobytes(), np.int32, M, 32 + 12 * M), wz)
+    # the int8 view reproduces the oracle's uint8 accumulator with the
+    # weight zero-point term: x' = u - 128, fold with x_zp - 128, then
+    # - w_zp * sum (x' - x_zp')
+    u = r.integers(0, 256, (4, K))
+    acc, _ = oracle.qgemm(u, wq, bq, xzp, wz, xs, ws, ys, yzp, True)
+    xv = u.astype(np.int64) - 128
+    got = xv @ wq.astype(np.int64).T + bfold[None, :] - wz[None, :] * (xv - (xzp - 128)).sum(1)[:, None]
+    assert np.array_equal(acc, got)
+    # only x unsigned: flags 1; only weight zero points: flags 4
+    b1 = ox.ox_int8_prepare(wq, ws, xs, 0, ys, 0, x_unsigned=True)
+    assert struct.unpack_from("<iiqiii", b1.tobytes(), 0)[3:] == (-128, 0, 1)
+    b4 = ox.ox_int8_prepare(wq, ws, xs, 0, ys, 0, w_zp=wz)
+    assert struct.unpack_from("<iiqiii", b4.tobytes(), 0)[5] == 4
+
+
+def test_int8_prepare_ex_errors(ox):
+    wq = np.zeros((2, 3), np.int8)
+    ws = [0.01, 0.01]
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(wq, ws, 0.1, -1, 0.2, 0, x_unsigned=True)        # uint8 x_zp < 0
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(wq, ws, 0.1, 0, 0.2, 256, y_unsigned=True)       # uint8 y_zp > 255
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(wq, ws, 0.1, 0, 0.2, 0, w_zp=[0, 128])           # w_zp > 127
+    big = np.zeros((1, 40000), np.int8)
+    ox.ox_int8_prepare(big, [0.01], 0.1, 0, 0.2, 0)                         # symmetric: fine
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(big, [0.01], 0.1, 0, 0.2, 0, w_zp=[1])           # K > 33000 with w_zp
+    with pytest.raises(TypeError):
+        ox.ox_int8_prepare(wq.astype(np.uint8), ws, 0.1, 0, 0.2, 0)         # uint8 weights unconverted
+    w8, z8 = ox.ox_int8_weights_from_uint8(np.array([[0, 255, 128]], np.uint8), 130)
+    assert w8.tolist() == [[-128, 127, 0]] and z8.tolist() == [2]
 
 
 def test_pack_weights_is_tap_major_channel_blocks(ox):

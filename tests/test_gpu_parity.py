@@ -609,6 +609,95 @@ def test_int8_requant_ties_on_gpu(ox):
     assert Y.cpu().numpy().ravel().tolist() == [0, 2, 0, -2, 2, -2, 127, -128]
 
 
+# ---------------------- uint8 activations / outputs, weight zero points --
+
+# (x uint8, y uint8, per-channel weight zero points)
+QVARIANTS = [(False, False, False), (True, False, False), (False, False, True),
+             (False, True, False), (True, True, True)]
+
+
+def q_inputs(r, xu, wz, xshape, wshape):
+    x = r.integers(0, 256, xshape) if xu else r.integers(-128, 128, xshape)
+    w = r.integers(-128, 128, wshape).astype(np.int8)
+    M = wshape[0]
+    wzp = r.integers(-128, 128, M).astype(np.int32) if wz else None
+    xzp = int(r.integers(0, 256)) if xu else int(r.integers(-128, 128))
+    bq = r.integers(-20000, 20000, M).astype(np.int32)
+    w_s = r.uniform(1e-3, 1e-2, M).astype(np.float32)
+    return x, w, wzp, xzp, bq, np.float32(0.05), w_s
+
+
+def q_out_scale(acc, x_s, w_s):
+    # an output scale that spreads the requantised values over the 8-bit range
+    spread = float(np.std(acc)) if acc.size > 1 else float(abs(acc).max() + 1)
+    return np.float32(x_s * float(np.median(w_s)) * max(spread, 1.0) / 40.0)
+
+
+def q_run(ox, blk, x, xu, w, yu, call):
+    xd = torch.from_numpy(x.astype(np.uint8 if xu else np.int8)).cuda()
+    wd = torch.from_numpy(w).cuda()
+    bd = torch.from_numpy(blk).cuda()
+    y32 = call(xd, wd, bd, "i32")
+    y8 = call(xd, wd, bd, "u8" if yu else "i8")
+    torch.cuda.synchronize()
+    return y32.cpu().numpy().astype(np.int64), y8.cpu().numpy().astype(np.int32)
+
+
+@pytest.mark.parametrize("xu,yu,wz", QVARIANTS)
+def test_qgemm_variants_bit_exact(ox, xu, yu, wz):
+    # QLinearMatMul / MatMulInteger with uint8 activations or outputs and
+    # per-channel weight zero points, over ragged tiles and one row
+    r = np.random.default_rng(700 + 4 * xu + 2 * yu + wz)
+    for (M, K, N) in [(77, 200, 45), (130, 72, 33), (1, 64, 16), (64, 1000, 96)]:
+        say("qgemm", (xu, yu, wz), (M, K, N))
+        x, w, wzp, xzp, bq, x_s, w_s = q_inputs(r, xu, wz, (M, K), (N, K))
+        acc0, _ = oracle.qgemm(x, w, bq, xzp, wzp, x_s, w_s, 1.0, 0)
+        y_s = q_out_scale(acc0, x_s, w_s)
+        yzp = int(r.integers(0, 256)) if yu else int(r.integers(-128, 128))
+        acc, y = oracle.qgemm(x, w, bq, xzp, wzp, x_s, w_s, y_s, yzp, yu)
+        blk = ox.ox_int8_prepare(w, w_s, x_s, xzp, y_s, yzp, bq, w_zp=wzp, x_unsigned=xu, y_unsigned=yu)
+
+        def call(xd, wd, bd, yt):
+            od = {"i32": torch.int32, "u8": torch.uint8, "i8": torch.int8}[yt]
+            return ox.ox_gemm_fused(xd, wd, transB=True, int8_params=bd, out_dtype=od)
+        g32, g8 = q_run(ox, blk, x, xu, w, yu, call)
+        assert np.array_equal(g32, acc), (M, K, N)
+        assert np.array_equal(g8, y), (M, K, N)
+        assert len(np.unique(y)) > 8          # the outputs are spread, not saturated
+
+
+@pytest.mark.parametrize("xu,yu,wz", QVARIANTS)
+def test_qconv_variants_bit_exact(ox, xu, yu, wz):
+    # QLinearConv / ConvInteger variants on every int8 conv kernel: the
+    # implicit GEMM (padding at x_zp, strides, dilation, groups), the 1x1
+    # kernel, and the depthwise kernel (2-D and the conformer's 1-D shape)
+    r = np.random.default_rng(800 + 4 * xu + 2 * yu + wz)
+    for (N, Cin, H, W, M, kH, kW, s, pads, d, g) in [
+            (2, 16, 9, 11, 24, 3, 3, 1, (1, 1, 1, 1), 1, 1),
+            (1, 12, 13, 10, 20, 3, 3, 2, (2, 1, 0, 1), 1, 2),
+            (2, 8, 12, 12, 8, 3, 3, 1, (2, 2, 2, 2), 2, 1),
+            (2, 64, 14, 14, 96, 3, 3, 1, (1, 1, 1, 1), 1, 1),
+            (2, 48, 7, 9, 40, 1, 1, 1, (0, 0, 0, 0), 1, 1),
+            (2, 24, 10, 13, 24, 3, 3, 1, (1, 1, 1, 1), 1, 24),
+            (1, 16, 1, 50, 16, 1, 9, 1, (0, 4, 0, 4), 1, 16)]:
+        geom = (N, Cin, H, W, M, kH, kW, s, pads, d, g)
+        say("qconv", (xu, yu, wz), geom,
+            ox.ox_conv2d_variant("i8", N, Cin, H, W, M, kH, kW, (s, s), pads, (d, d), g))
+        x, w, wzp, xzp, bq, x_s, w_s = q_inputs(r, xu, wz, (N, Cin, H, W), (M, Cin // g, kH, kW))
+        args = ((s, s), pads, (d, d), g)
+        acc0, _ = oracle.qconv2d(x, w, bq, xzp, wzp, x_s, w_s, 1.0, 0, False, *args)
+        y_s = q_out_scale(acc0, x_s, w_s)
+        yzp = int(r.integers(0, 256)) if yu else int(r.integers(-128, 128))
+        acc, y = oracle.qconv2d(x, w, bq, xzp, wzp, x_s, w_s, y_s, yzp, yu, *args)
+        blk = ox.ox_int8_prepare(w, w_s, x_s, xzp, y_s, yzp, bq, w_zp=wzp, x_unsigned=xu, y_unsigned=yu)
+
+        def call(xd, wd, bd, yt):
+            return ox.ox_conv2d_int8(xd, wd, bd, yt, *args)
+        g32, g8 = q_run(ox, blk, x, xu, w, yu, call)
+        assert np.array_equal(g32, acc), geom
+        assert np.array_equal(g8, y), geom
+
+
 def test_patch_conv_sweep_bf16(ox, monkeypatch):
     # the LDS-patch 3x3 kernel over strides, dilations, asymmetric pads,
     # ragged channel / pixel counts and several images per block
