@@ -9,7 +9,8 @@ int8), the roofline object of the dominant kernel (measured with HIP events
 on the launch stream inside the timed region) and the CPU oracle timed on a
 bounded sample of the same workload.
 
-    python bench.py [--steps K] [--warmup W] [--workload resnet50|mobilenetv2|mlp|matmul|int8]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload resnet50|mobilenetv2|mlp|matmul|int8|resnet50-aux|dynq]
 """
 import argparse
 import ctypes as C
@@ -34,7 +35,8 @@ def parse():
     p.add_argument("--steps", type=int, default=20)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="resnet50",
-                   choices=["resnet50", "mobilenetv2", "mlp", "matmul", "int8", "resnet50-aux"])
+                   choices=["resnet50", "mobilenetv2", "mlp", "matmul", "int8", "resnet50-aux",
+                            "dynq"])
     p.add_argument("--dtype", default=None, help="bf16 or f32 (float workloads)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -181,6 +183,28 @@ def aux_layers(ox, torch, dtype, batch, stream):
     args = (code, batch, 2048, 49, X.data_ptr(), Y.data_ptr(), stream)
     out.append(Layer("head.gap", 0.0, (X.numel() + Y.numel()) * es, "gap/" + dtype,
                      lambda a=args, k=(X, Y): ox.lib.ox_global_avgpool(*a), None, Y.numel(), 49))
+    return out
+
+
+def dynq_layers(ox, torch, stream):
+    """DynamicQuantizeLinear of the conformer block's fp32 activations
+    (T = 1000 frames: the 1024-wide block input and the 4096-wide FFN hidden
+    activation).  Algorithmic bytes: x read once (4 B) and y written (1 B)
+    per element; the kernels read x twice (range, then quantise)."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4321)
+    ws = torch.empty(int(ox.lib.ox_dynamic_quantize_workspace_bytes()), dtype=torch.uint8, device="cuda")
+    out = []
+    for width in (1024, 4096):
+        X = torch.randn(1000, width, generator=g, device="cuda") * 1.7 + 0.2
+        Y = torch.empty((1000, width), dtype=torch.uint8, device="cuda")
+        sc = torch.empty(1, dtype=torch.float32, device="cuda")
+        zp = torch.empty(1, dtype=torch.uint8, device="cuda")
+        args = (X.numel(), X.data_ptr(), Y.data_ptr(), sc.data_ptr(), zp.data_ptr(), ws.data_ptr(),
+                ws.numel(), stream)
+        out.append(Layer("dynq.1000x%d" % width, 0.0, 5 * X.numel(), "dynq/f32",
+                         lambda a=args, k=(X, Y, sc, zp, ws): ox.lib.ox_dynamic_quantize_linear(*a),
+                         None, X.numel(), 1))
     return out
 
 
@@ -443,6 +467,11 @@ def main():
         layers = gemm_layers(ox, synth, torch, synth.mlp_rows(), dtype, sp)
         cfg = {"workload": "MLP Gemm rows M in {1,64,256} x (1024->4096 GELU, 4096->1024, "
                            "1024->1024 ReLU)"}
+    elif wl == "dynq":
+        dtype = "f32"
+        layers = dynq_layers(ox, torch, sp)
+        cfg = {"workload": "DynamicQuantizeLinear fp32 -> uint8 of [1000,1024] and [1000,4096] "
+                           "activations"}
     elif wl == "matmul":
         dtype = "f32"
         layers = matmul_layers(ox, synth, torch, sp)

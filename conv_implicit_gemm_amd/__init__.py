@@ -28,7 +28,7 @@ EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_i
            "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
            "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
            "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool",
-           "ox_int8_prepare_ex")
+           "ox_int8_prepare_ex", "ox_dynamic_quantize_workspace_bytes", "ox_dynamic_quantize_linear")
 
 
 class OxError(RuntimeError):
@@ -72,6 +72,8 @@ def _load():
         "ox_int8_params_bytes": (C.c_size_t, [I64]),
         "ox_int8_prepare": (I, [I64, I64, P, P, F, I32, F, I32, P, P]),
         "ox_int8_prepare_ex": (I, [I64, I64, P, P, P, F, I32, I, F, I32, I, P, P]),
+        "ox_dynamic_quantize_workspace_bytes": (C.c_size_t, []),
+        "ox_dynamic_quantize_linear": (I, [I64, P, P, P, P, P, C.c_size_t, P]),
         "ox_last_error": (C.c_char_p, []),
         "ox_version": (C.c_char_p, []),
     }
@@ -240,6 +242,27 @@ def ox_conv2d_fused_res(X, W, R, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), di
     _check(lib.ox_conv2d_fused_res(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), _ptr(R),
                                    ACT[act], _ptr(Y), _ptr(workspace), nbytes, _stream(stream)))
     return Y
+
+
+def ox_dynamic_quantize_linear(X, Y=None, y_scale=None, y_zp=None, workspace=None, stream=None):
+    """ONNX DynamicQuantizeLinear of a dense fp32 device tensor: returns
+    (Y uint8 of X's shape, y_scale fp32 [1], y_zp uint8 [1]), all on the device."""
+    torch = _torch()
+    _dense(X, "X")
+    if X.dtype != torch.float32:
+        raise TypeError("X must be float32")
+    if Y is None:
+        Y = torch.empty(X.shape, dtype=torch.uint8, device=X.device)
+    if y_scale is None:
+        y_scale = torch.empty(1, dtype=torch.float32, device=X.device)
+    if y_zp is None:
+        y_zp = torch.empty(1, dtype=torch.uint8, device=X.device)
+    if workspace is None:
+        workspace = torch.empty(int(lib.ox_dynamic_quantize_workspace_bytes()), dtype=torch.uint8,
+                                device=X.device)
+    _check(lib.ox_dynamic_quantize_linear(X.numel(), _ptr(X), _ptr(Y), _ptr(y_scale), _ptr(y_zp),
+                                          _ptr(workspace), workspace.numel(), _stream(stream)))
+    return Y, y_scale, y_zp
 
 
 def ox_batchnorm_act(X, gamma, beta, mean, var, eps=1e-5, act="none", Y=None, stream=None):

@@ -766,6 +766,23 @@ ox_status ox_global_avgpool(ox_dtype t, int64_t N, int64_t C, int64_t HW, const 
   return hip_result(fn, launch_global_avgpool(a, stream));
 }
 
+size_t ox_dynamic_quantize_workspace_bytes(void) { return dynq_workspace_bytes(); }
+
+ox_status ox_dynamic_quantize_linear(int64_t n, const float* X, uint8_t* Y, float* y_scale,
+                                     uint8_t* y_zp, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  const char* fn = "ox_dynamic_quantize_linear";
+  if (n < 0) return fail(OX_ERR_SHAPE, "%s: n=%lld is negative", fn, (long long)n);
+  if (!y_scale || !y_zp) return fail(OX_ERR_INVALID_ARG, "%s: y_scale or y_zp is NULL", fn);
+  if (n > 0 && (!X || !Y)) return fail(OX_ERR_INVALID_ARG, "%s: X or Y is NULL", fn);
+  if ((uintptr_t)X % 4 || (uintptr_t)y_scale % 4)
+    return fail(OX_ERR_INVALID_ARG, "%s: X or y_scale is not 4-byte aligned", fn);
+  if (!workspace || workspace_bytes < dynq_workspace_bytes() || (uintptr_t)workspace % 16)
+    return fail(OX_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned and hold %zu bytes", fn,
+                dynq_workspace_bytes());
+  return hip_result(fn, launch_dynamic_quantize(n, X, Y, y_scale, y_zp, workspace, stream));
+}
+
 ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_t cap) {
   const char* fn = "ox_conv2d_variant";
   if (t != OX_F32 && t != OX_BF16 && t != OX_I8)

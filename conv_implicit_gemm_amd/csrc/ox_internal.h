@@ -222,6 +222,9 @@ struct PoolArgs {
 };
 int launch_bn_act(const PoolArgs& a, void* stream);
 // MaxPool on the depthwise kernel's staged band (group == C == M, f32 / bf16)
+size_t dynq_workspace_bytes();
+int launch_dynamic_quantize(int64_t n, const float* X, uint8_t* Y, float* y_scale, uint8_t* y_zp,
+                            void* ws, void* stream);
 int launch_maxpool_dw(const ConvArgs& a, void* stream);
 int launch_maxpool(const PoolArgs& a, void* stream);
 int launch_global_avgpool(const PoolArgs& a, void* stream);

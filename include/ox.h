@@ -296,6 +296,26 @@ ox_status ox_int8_prepare_ex(int64_t M, int64_t Kper, const int8_t* Wq_host, con
                              float y_scale, int32_t y_zp, int y_unsigned, const int32_t* bias_q,
                              void* params_host_out);
 
+/* Dynamic per-tensor quantisation of fp32 activations to uint8 (ONNX
+ * DynamicQuantizeLinear; the onnx-vulkan-rs notes name dynamically
+ * quantised graphs, whose scale follows the tensor's extremes):
+ *   lo = min(0, min X), hi = max(0, max X), y_scale = (hi - lo) / 255,
+ *   y_zp = rint(clamp(-lo / y_scale, 0, 255)),
+ *   Y = clamp(rint(X / y_scale) + y_zp, 0, 255)
+ * in fp32 (correctly rounded division, round half to even).  An all-zero X
+ * (or n = 0) gives y_scale = 0, y_zp = 0, Y = 0.  NaN inputs are not
+ * supported (min / max skip them; their Y is 0).
+ * X: DEVICE fp32 [n] (4-byte aligned; 16-byte aligned X with 4-byte aligned
+ * Y takes the vector path); Y: DEVICE uint8 [n]; y_scale: DEVICE fp32 [1];
+ * y_zp: DEVICE uint8 [1]; workspace: DEVICE, 16-byte aligned, at least
+ * ox_dynamic_quantize_workspace_bytes() bytes, owned by the caller (two
+ * launches on `stream`; calls that share a workspace must not overlap).
+ * y_scale / y_zp then feed ox_int8_prepare_ex-style consumers (x_unsigned). */
+size_t ox_dynamic_quantize_workspace_bytes(void);
+ox_status ox_dynamic_quantize_linear(int64_t n, const float* X, uint8_t* Y, float* y_scale,
+                                     uint8_t* y_zp, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
 /* The message of the last failing call on this thread ("" if none). */
 const char* ox_last_error(void);
 

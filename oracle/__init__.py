@@ -346,6 +346,27 @@ def qgemm(X, Wq, bias_q, x_zp, w_zp, x_s, w_s, y_s, y_zp, y_unsigned=False):
     return acc, y
 
 
+def dynamic_quantize_linear(x):
+    """ONNX DynamicQuantizeLinear (the dynamically quantised graphs of the
+    onnx-vulkan-rs notes), step by step in float32 as the operator defines it:
+    the range [min(0, min x), max(0, max x)], y_scale = range / 255, the zero
+    point -x_min / y_scale clamped to [0, 255] and rounded half to even, then
+    y = clamp(rint(x / y_scale) + y_zp, 0, 255).  Reading: an all-zero (or
+    empty) x gives y_scale = 0, y_zp = 0 and y = 0.  Returns (y uint8,
+    y_scale float32, y_zp int)."""
+    x = np.asarray(x, dtype=np.float32)
+    f = np.float32
+    x_min = f(min(f(0), x.min())) if x.size else f(0)
+    x_max = f(max(f(0), x.max())) if x.size else f(0)
+    y_scale = f(f(x_max - x_min) / f(255))
+    if y_scale == 0:
+        return np.zeros(x.shape, np.uint8), y_scale, 0
+    zp = f(np.rint(np.clip(f(f(0) - f(x_min / y_scale)), f(0), f(255))))
+    q = np.rint((x / y_scale).astype(np.float32)).astype(np.float32) + zp
+    y = np.clip(q, f(0), f(255)).astype(np.uint8)
+    return y, y_scale, int(zp)
+
+
 def requant1(acc, x_s, w_s, y_s, y_zp):
     """The oracle's requantisation of a single accumulator."""
     return lib().oxref_requant1(int(acc), float(np.float32(x_s)), float(np.float32(w_s)),

@@ -186,6 +186,21 @@ def test_residual_entry_point_errors(ox, monkeypatch):
     monkeypatch.delenv("OX_FORCE_KERNEL")
 
 
+def test_dynamic_quantize_argument_errors(ox):
+    L = raw(ox)
+    need = L.ox_dynamic_quantize_workspace_bytes()
+    assert need >= 16
+    dq = L.ox_dynamic_quantize_linear
+    assert dq(-1, FAKE, FAKE, FAKE, FAKE, FAKE, need, None) == 2
+    assert dq(8, FAKE, FAKE, None, FAKE, FAKE, need, None) == 1                 # y_scale NULL
+    assert dq(8, None, FAKE, FAKE, FAKE, FAKE, need, None) == 1                 # X NULL
+    assert dq(8, FAKE + 2, FAKE, FAKE, FAKE, FAKE, need, None) == 1             # X misaligned
+    assert dq(8, FAKE, FAKE, FAKE, FAKE, FAKE, need - 4, None) == 1             # workspace too small
+    assert "workspace" in ox.ox_last_error()
+    assert dq(8, FAKE, FAKE, FAKE, FAKE, FAKE + 8, need, None) == 1             # workspace misaligned
+    assert dq(8, FAKE, FAKE, FAKE, FAKE, None, need, None) == 1
+
+
 def test_pool_and_batchnorm_argument_errors(ox):
     L = raw(ox)
     bn = L.ox_batchnorm_act

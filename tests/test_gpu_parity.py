@@ -698,6 +698,63 @@ def test_qconv_variants_bit_exact(ox, xu, yu, wz):
         assert np.array_equal(g8, y), geom
 
 
+# ------------------------------------------------- DynamicQuantizeLinear --
+
+def dq_check(ox, x, offset=0):
+    n = x.size
+    buf = torch.zeros(n + offset, dtype=torch.float32, device="cuda")
+    Xd = buf[offset:]
+    Xd.copy_(torch.from_numpy(np.ascontiguousarray(x.ravel())))
+    Y = torch.full((n,), 77, dtype=torch.uint8, device="cuda")
+    Yg, sc, zp = ox.ox_dynamic_quantize_linear(Xd, Y=Y)
+    torch.cuda.synchronize()
+    y_ref, sc_ref, zp_ref = oracle.dynamic_quantize_linear(x.ravel())
+    assert sc.cpu().numpy()[0] == sc_ref and int(zp.cpu()[0]) == zp_ref
+    assert np.array_equal(Yg.cpu().numpy(), y_ref)
+    return y_ref, sc_ref, zp_ref
+
+
+@pytest.mark.parametrize("n", [0, 1, 3, 17, 4096, 70001])
+@pytest.mark.parametrize("offset", [0, 1])
+def test_dynamic_quantize_bit_exact(ox, n, offset):
+    # the vector path (aligned) and the element path (X one element off), a
+    # ragged tail, several blocks; fp32 scale, zero point and bytes exact
+    r = np.random.default_rng(n + 13 * offset)
+    x = (r.standard_normal(n) * 2.5 + 0.3).astype(np.float32)
+    say("dynq", n, offset)
+    dq_check(ox, x, offset)
+
+
+def test_dynamic_quantize_special_ranges(ox):
+    say("dynq special")
+    for x in [np.zeros(100, np.float32), np.linspace(0.5, 9.0, 333).astype(np.float32),
+              -np.linspace(0.1, 4.0, 260).astype(np.float32), np.arange(256, dtype=np.float32),
+              np.array([-1.0, 0.0, 1.0], np.float32), (np.ones(64) * 1e30).astype(np.float32)]:
+        dq_check(ox, x)
+
+
+def test_dynamic_quantize_then_matmul_integer(ox):
+    # a dynamically quantised MatMulInteger: the conformer FFN's hidden
+    # activation [1000, 4096] fp32 quantised on the device, then the int8
+    # Gemm with int32 outputs against the oracle's acc on the oracle's bytes
+    r = np.random.default_rng(77)
+    x = (r.standard_normal((1000, 4096)) * 1.7).astype(np.float32)
+    say("dynq + matmul integer")
+    y_ref, sc, zp = dq_check(ox, x)
+    w = r.integers(-128, 128, (256, 4096)).astype(np.int8)
+    wz = r.integers(-5, 6, 256).astype(np.int32)
+    w_s = np.full(256, 0.01, np.float32)
+    blk = torch.from_numpy(ox.ox_int8_prepare(w, w_s, sc, zp, 1.0, 0, w_zp=wz, x_unsigned=True)).cuda()
+    Xd = torch.from_numpy(x).cuda()
+    Yq, _, _ = ox.ox_dynamic_quantize_linear(Xd)
+    acc = ox.ox_gemm_fused(Yq.view(1000, 4096), torch.from_numpy(w).cuda(), transB=True,
+                           int8_params=blk, out_dtype=torch.int32)
+    torch.cuda.synchronize()
+    rows = np.arange(0, 1000, 37)
+    ref, _ = oracle.qgemm(y_ref.reshape(1000, 4096)[rows], w, None, zp, wz, sc, w_s, 1.0, 0)
+    assert np.array_equal(acc.cpu().numpy()[rows].astype(np.int64), ref)
+
+
 def test_patch_conv_sweep_bf16(ox, monkeypatch):
     # the LDS-patch 3x3 kernel over strides, dilations, asymmetric pads,
     # ragged channel / pixel counts and several images per block

@@ -567,6 +567,43 @@ def test_q_uint8_output_range_and_rounding():
         oracle.qgemm(x, w, None, 0, None, xs, np.array([ws], np.float32), ys, 256, True)
 
 
+# ------------------------------------------------- DynamicQuantizeLinear --
+
+def test_dynamic_quantize_closed_forms():
+    # [0, 255]: scale 1, zero point 0, y = x
+    y, sc, zp = oracle.dynamic_quantize_linear(np.arange(256, dtype=np.float32))
+    assert sc == np.float32(1) and zp == 0 and np.array_equal(y, np.arange(256))
+    # all positive: the range is widened to 0, so zp = 0 and the maximum maps to 255
+    y, sc, zp = oracle.dynamic_quantize_linear(np.array([2.0, 4.0, 5.1], np.float32))
+    assert zp == 0 and y[-1] == 255 and sc == np.float32(np.float32(5.1) / np.float32(255))
+    # all negative: zp = 255, the minimum maps to 0
+    y, sc, zp = oracle.dynamic_quantize_linear(np.array([-3.0, -1.0], np.float32))
+    assert zp == 255 and y[0] == 0
+    # symmetric [-1, 1]: in exact arithmetic -lo/scale = 127.5; in fp32 the
+    # scale 2/255 rounds up (0.0078431377...), so 1/scale is just below 127.5:
+    # zp = 127, x = 1 -> 127 + 127 = 254, x = -1 -> -127 + 127 = 0 (a
+    # computation in double would give 128 and 255 here)
+    y, sc, zp = oracle.dynamic_quantize_linear(np.array([-1.0, 0.0, 1.0], np.float32))
+    assert float(sc) > 2 / 255
+    assert zp == 127 and y.tolist() == [0, 127, 254]
+    # all zero (and empty): scale 0, zero point 0, y = 0
+    y, sc, zp = oracle.dynamic_quantize_linear(np.zeros(5, np.float32))
+    assert sc == 0 and zp == 0 and not y.any()
+    assert oracle.dynamic_quantize_linear(np.zeros(0, np.float32))[1] == 0
+
+
+def test_dynamic_quantize_round_trip_error_is_half_a_step():
+    # dequantising gives x back within scale/2 (all values lie in the range)
+    r = np.random.default_rng(41)
+    x = (r.standard_normal(5000) * 3 + 0.7).astype(np.float32)
+    y, sc, zp = oracle.dynamic_quantize_linear(x)
+    back = (y.astype(np.float64) - zp) * np.float64(sc)
+    assert np.max(np.abs(back - x)) <= np.float64(sc) * 0.5 * (1 + 1e-5)
+    assert y.min() == 0 or y.max() == 255
+    # the extremes map to the ends of the range (up to the zero point's rounding)
+    assert y[np.argmax(x)] >= 254 and y[np.argmin(x)] <= 1
+
+
 # ------------------------------------------------------------- determinism --
 
 def test_bit_identical_for_any_thread_count():
