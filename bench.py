@@ -10,7 +10,7 @@ on the launch stream inside the timed region) and the CPU oracle timed on a
 bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W]
-                    [--workload resnet50|mobilenetv2|mlp|matmul|int8|resnet50-aux|dynq]
+                    [--workload resnet50|mobilenetv2|mlp|matmul|int8|resnet50-aux|dynq|nbits]
 """
 import argparse
 import ctypes as C
@@ -36,7 +36,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="resnet50",
                    choices=["resnet50", "mobilenetv2", "mlp", "matmul", "int8", "resnet50-aux",
-                            "dynq"])
+                            "dynq", "nbits"])
     p.add_argument("--dtype", default=None, help="bf16 or f32 (float workloads)")
     p.add_argument("--batch", type=int, default=None)
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -183,6 +183,37 @@ def aux_layers(ox, torch, dtype, batch, stream):
     args = (code, batch, 2048, 49, X.data_ptr(), Y.data_ptr(), stream)
     out.append(Layer("head.gap", 0.0, (X.numel() + Y.numel()) * es, "gap/" + dtype,
                      lambda a=args, k=(X, Y): ox.lib.ox_global_avgpool(*a), None, Y.numel(), 49))
+    return out
+
+
+def nbits_layers(ox, synth, torch, stream):
+    """MatMulNBits (4-bit weights in blocks of 32, zero points, bf16
+    activations) on a 4096 x 4096 projection: decode (1 row) and prefill
+    (64 rows, 256 rows).  Algorithmic bytes: A, packed B, scales, zero
+    points and Y once each."""
+    import oracle
+    out = []
+    N = K = 4096
+    for M in (1, 64, 256):
+        t = synth.nbits_inputs(M, N, K, 700 + M, pow2_scales=False, with_bias=False)
+        A = torch.from_numpy(t["A"].astype(np.float32)).cuda().to(torch.bfloat16)
+        B = torch.from_numpy(t["B"]).cuda()
+        sc = torch.from_numpy(t["scales"]).cuda()
+        zp = torch.from_numpy(t["zero_points"]).cuda()
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        args = (ox.OX_BF16, M, N, K, 4, 32, A.data_ptr(), B.data_ptr(), sc.data_ptr(), zp.data_ptr(),
+                None, Y.data_ptr(), stream)
+        nbytes = A.numel() * 2 + B.numel() + sc.numel() * 4 + zp.numel() + Y.numel() * 2
+
+        def oracle_at(idx, t=t, M=M):
+            rows = np.unique(np.asarray(idx) // N)
+            full = oracle.matmul_nbits(t["A"][rows], t["B"], t["scales"], K, t["zero_points"])
+            pos = {r: i for i, r in enumerate(rows)}
+            return np.array([full[pos[i // N], i % N] for i in np.asarray(idx)])
+        out.append(Layer("nbits.%dx%dx%d" % (M, N, K), 2.0 * M * N * K, nbytes,
+                         "nbits/bf16" if M > 1 else "gemv-nbits/bf16",
+                         lambda a=args, k=(A, B, sc, zp, Y): ox.lib.ox_matmul_nbits(*a),
+                         oracle_at, M * N, K))
     return out
 
 
@@ -467,6 +498,11 @@ def main():
         layers = gemm_layers(ox, synth, torch, synth.mlp_rows(), dtype, sp)
         cfg = {"workload": "MLP Gemm rows M in {1,64,256} x (1024->4096 GELU, 4096->1024, "
                            "1024->1024 ReLU)"}
+    elif wl == "nbits":
+        dtype = "bf16"
+        layers = nbits_layers(ox, synth, torch, sp)
+        cfg = {"workload": "MatMulNBits 4-bit blocks of 32 with zero points, [M,4096] x "
+                           "[4096->4096], M in {1, 64, 256}"}
     elif wl == "dynq":
         dtype = "f32"
         layers = dynq_layers(ox, torch, sp)

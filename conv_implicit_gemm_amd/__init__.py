@@ -28,7 +28,8 @@ EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_i
            "ox_conv2d_pack_weights", "ox_fold_batchnorm", "ox_int8_params_bytes", "ox_int8_prepare",
            "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
            "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool",
-           "ox_int8_prepare_ex", "ox_dynamic_quantize_workspace_bytes", "ox_dynamic_quantize_linear")
+           "ox_int8_prepare_ex", "ox_dynamic_quantize_workspace_bytes", "ox_dynamic_quantize_linear",
+           "ox_matmul_nbits")
 
 
 class OxError(RuntimeError):
@@ -73,6 +74,7 @@ def _load():
         "ox_int8_prepare": (I, [I64, I64, P, P, F, I32, F, I32, P, P]),
         "ox_int8_prepare_ex": (I, [I64, I64, P, P, P, F, I32, I, F, I32, I, P, P]),
         "ox_dynamic_quantize_workspace_bytes": (C.c_size_t, []),
+        "ox_matmul_nbits": (I, [I, I64, I64, I64, I, I, P, P, P, P, P, P, P]),
         "ox_dynamic_quantize_linear": (I, [I64, P, P, P, P, P, C.c_size_t, P]),
         "ox_last_error": (C.c_char_p, []),
         "ox_version": (C.c_char_p, []),
@@ -241,6 +243,23 @@ def ox_conv2d_fused_res(X, W, R, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), di
         nbytes = workspace.numel() * workspace.element_size()
     _check(lib.ox_conv2d_fused_res(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), _ptr(bias), _ptr(R),
                                    ACT[act], _ptr(Y), _ptr(workspace), nbytes, _stream(stream)))
+    return Y
+
+
+def ox_matmul_nbits(A, B, scales, K, zero_points=None, bias=None, Y=None, stream=None):
+    """MatMulNBits (4 bits, blocks of 32): A bf16 [M,K] x dequant(B)^T -> Y bf16 [M,N].
+    B uint8 [N, ceil(K/32), 16], scales fp32 [N, ceil(K/32)], zero_points
+    uint8 [N, ceil(ceil(K/32)/2)] or None (8)."""
+    torch = _torch()
+    for t, n in ((A, "A"), (B, "B"), (scales, "scales"), (zero_points, "zero_points"),
+                 (bias, "bias"), (Y, "Y")):
+        _dense(t, n)
+    M = A.shape[0]
+    N = B.shape[0]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=torch.bfloat16, device=A.device)
+    _check(lib.ox_matmul_nbits(OX_BF16, M, N, K, 4, 32, _ptr(A), _ptr(B), _ptr(scales),
+                               _ptr(zero_points), _ptr(bias), _ptr(Y), _stream(stream)))
     return Y
 
 

@@ -766,6 +766,43 @@ ox_status ox_global_avgpool(ox_dtype t, int64_t N, int64_t C, int64_t HW, const 
   return hip_result(fn, launch_global_avgpool(a, stream));
 }
 
+ox_status ox_matmul_nbits(ox_dtype t, int64_t M, int64_t N, int64_t K, int bits, int block_size,
+                          const void* A, const uint8_t* B, const float* scales,
+                          const uint8_t* zero_points, const void* bias, void* Y, void* stream) {
+  const char* fn = "ox_matmul_nbits";
+  if (t != OX_BF16) return fail(OX_ERR_UNSUPPORTED, "%s: dtype %d is not OX_BF16", fn, (int)t);
+  if (bits != 4 || block_size != 32)
+    return fail(OX_ERR_UNSUPPORTED, "%s: bits=%d block_size=%d (only 4-bit blocks of 32)", fn, bits,
+                block_size);
+  if (M < 0 || N < 0 || K < 0)
+    return fail(OX_ERR_SHAPE, "%s: negative size M=%lld N=%lld K=%lld", fn, (long long)M,
+                (long long)N, (long long)K);
+  if (M > INT32_MAX || N > INT32_MAX || K > INT32_MAX - 64)
+    return fail(OX_ERR_UNSUPPORTED, "%s: sizes too large", fn);
+  if (M * N == 0) return ok();
+  if (!Y) return fail(OX_ERR_INVALID_ARG, "%s: Y is NULL", fn);
+  if (K > 0 && (!A || !B || !scales)) return fail(OX_ERR_INVALID_ARG, "%s: A, B or scales is NULL", fn);
+  if ((uintptr_t)A % 2 || (uintptr_t)Y % 2 || (uintptr_t)bias % 2 || (uintptr_t)B % 4 ||
+      (uintptr_t)scales % 4)
+    return fail(OX_ERR_INVALID_ARG, "%s: A / Y / bias must be 2-byte and B / scales 4-byte aligned", fn);
+  NBitsArgs a;
+  memset(&a, 0, sizeof(a));
+  a.M = (int)M;
+  a.N = (int)N;
+  a.K = (int)K;
+  a.nblk = (int)((K + 31) / 32);
+  a.A = A;
+  a.lda = K;
+  a.a_vec = ((uintptr_t)A % 16) == 0 && K % 8 == 0;
+  a.B = B;
+  a.scales = scales;
+  a.zp = zero_points;
+  a.bias = bias;
+  a.Y = Y;
+  a.ldy = N;
+  return hip_result(fn, launch_matmul_nbits(a, stream));
+}
+
 size_t ox_dynamic_quantize_workspace_bytes(void) { return dynq_workspace_bytes(); }
 
 ox_status ox_dynamic_quantize_linear(int64_t n, const float* X, uint8_t* Y, float* y_scale,

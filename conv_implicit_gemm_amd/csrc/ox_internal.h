@@ -222,6 +222,21 @@ struct PoolArgs {
 };
 int launch_bn_act(const PoolArgs& a, void* stream);
 // MaxPool on the depthwise kernel's staged band (group == C == M, f32 / bf16)
+// Weight-only int4 MatMul (MatMulNBits, 4 bits, blocks of 32 along K).
+struct NBitsArgs {
+  int M, N, K, nblk;      // nblk = ceil(K / 32)
+  const void* A;          // bf16 [M, K], row stride lda
+  int64_t lda;
+  bool a_vec;             // A 16-byte aligned with lda % 8 == 0
+  const uint8_t* B;       // [N][nblk][16] packed nibbles
+  const float* scales;    // [N][nblk]
+  const uint8_t* zp;      // [N][(nblk + 1) / 2] packed nibbles, or null (8)
+  const void* bias;       // bf16 [N] or null
+  void* Y;                // bf16 [M, N], row stride ldy
+  int64_t ldy;
+};
+int launch_matmul_nbits(const NBitsArgs& a, void* stream);
+
 size_t dynq_workspace_bytes();
 int launch_dynamic_quantize(int64_t n, const float* X, uint8_t* Y, float* y_scale, uint8_t* y_zp,
                             void* ws, void* stream);

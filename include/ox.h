@@ -296,6 +296,28 @@ ox_status ox_int8_prepare_ex(int64_t M, int64_t Kper, const int8_t* Wq_host, con
                              float y_scale, int32_t y_zp, int y_unsigned, const int32_t* bias_q,
                              void* params_host_out);
 
+/* Weight-only int4 MatMul (ONNX MatMulNBits with 4-bit weights in blocks of
+ * 32 along K; the Onyxia README runs 4-bit LLM weights that stay packed on
+ * the device, its prefill matmul dequantising each weight tile into shared
+ * memory on load):
+ *   Y[m,n] = sum_k A[m,k] * w[n,k] (+ bias[n]),
+ *   w[n,k] = (q[n,k] - zp[n,k/32]) * scales[n,k/32]
+ * t = OX_BF16: A [M,K], bias [N] (or NULL) and Y [M,N] bf16, row-major and
+ * dense; fp32 accumulation.  Up to 4 rows (decode) run a fused
+ * matrix-vector kernel that keeps the dequantised weights in fp32; more rows
+ * run the MFMA tile engine, which rounds each dequantised weight to bf16.
+ * A 16-byte aligned B is needed for the decode kernel (else the tile engine
+ * runs those rows too).
+ * B: DEVICE uint8 [N][ceil(K/32)][16]: element k of block b of row n in byte
+ * (k%32)/2 of that block, the low nibble for even k (4-byte aligned).
+ * scales: DEVICE fp32 [N][ceil(K/32)].  zero_points: DEVICE uint8
+ * [N][ceil(ceil(K/32)/2)], block b's zero point in byte b/2, the low nibble
+ * for even b; NULL means 8 for every block.  bits must be 4 and block_size
+ * 32 (OX_ERR_UNSUPPORTED otherwise). */
+ox_status ox_matmul_nbits(ox_dtype t, int64_t M, int64_t N, int64_t K, int bits, int block_size,
+                          const void* A, const uint8_t* B, const float* scales,
+                          const uint8_t* zero_points, const void* bias, void* Y, void* stream);
+
 /* Dynamic per-tensor quantisation of fp32 activations to uint8 (ONNX
  * DynamicQuantizeLinear; the onnx-vulkan-rs notes name dynamically
  * quantised graphs, whose scale follows the tensor's extremes):

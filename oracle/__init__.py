@@ -346,6 +346,35 @@ def qgemm(X, Wq, bias_q, x_zp, w_zp, x_s, w_s, y_s, y_zp, y_unsigned=False):
     return acc, y
 
 
+def matmul_nbits(A, B, scales, K, zero_points=None, bias=None):
+    """Weight-only 4-bit MatMul (ONNX MatMulNBits, blocks of 32 along K; the
+    Onyxia README's q4 weights): Y = A x W^T (+ bias) in float64 with
+    W[n,k] = (q[n,k] - zp[n,k//32]) * scales[n,k//32], where q[n,k] is the low
+    nibble of byte (k%32)//2 of block k//32 of row n for even k and the high
+    nibble for odd k, and zp is block b's nibble of zero_points[n, b//2] (low
+    for even b), or 8 when zero_points is None.  A: [M,K]; B: uint8
+    [N, ceil(K/32), 16]; scales: [N, ceil(K/32)]."""
+    A = np.asarray(A, dtype=np.float64)
+    B = np.asarray(B, dtype=np.uint8)
+    sc = np.asarray(scales, dtype=np.float64)
+    N = B.shape[0]
+    W = np.empty((N, K), dtype=np.float64)
+    for k in range(K):
+        b = k // 32
+        byte = B[:, b, (k % 32) // 2].astype(np.int64)
+        q = (byte & 15) if k % 2 == 0 else (byte >> 4)
+        if zero_points is None:
+            zp = 8
+        else:
+            zb = np.asarray(zero_points, dtype=np.uint8)[:, b // 2].astype(np.int64)
+            zp = (zb & 15) if b % 2 == 0 else (zb >> 4)
+        W[:, k] = (q - zp) * sc[:, b]
+    Y = A @ W.T
+    if bias is not None:
+        Y = Y + np.asarray(bias, dtype=np.float64)[None, :]
+    return Y
+
+
 def dynamic_quantize_linear(x):
     """ONNX DynamicQuantizeLinear (the dynamically quantised graphs of the
     onnx-vulkan-rs notes), step by step in float32 as the operator defines it:

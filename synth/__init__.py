@@ -271,3 +271,38 @@ def int8_inputs(layer: Int8Layer, cfg: int = 4, li: int = 0):
                      * np.sqrt(kred) * 73.9 * 73.6 / 127.0)
     y_zp = int(rng(cfg, li, T_YZP).integers(-20, 21))
     return dict(xq=xq, wq=wq, x_s=x_s, x_zp=x_zp, w_s=w_s, bias_q=bias_q, y_s=y_s, y_zp=y_zp)
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """[rows, n] values in 0..15 -> [rows, ceil(n/2)] bytes, value 2i in the
+    low nibble of byte i and value 2i+1 in its high nibble (the MatMulNBits
+    storage order)."""
+    q = np.asarray(q, dtype=np.uint8)
+    if q.shape[1] % 2:
+        q = np.concatenate([q, np.zeros((q.shape[0], 1), np.uint8)], axis=1)
+    return (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+
+
+def nbits_inputs(M: int, N: int, K: int, seed: int, with_zp: bool = True, pow2_scales: bool = True,
+                 with_bias: bool = True):
+    """Seeded MatMulNBits operands (4 bits, blocks of 32): A ~ N(0,1) in bf16,
+    q ~ U{0..15}, zero points ~ U{0..15} (or the default 8), scales per block
+    either powers of two around 1/(4*sqrt(K)) (every dequantised weight exact
+    in bf16) or U[0.5,1.5]/(4*sqrt(K)); bias ~ N(0, 0.1) in bf16.  Returns a
+    dict with the unpacked values (q, zp, scales) and the packed device forms
+    (B [N, nblk, 16], zero_points [N, ceil(nblk/2)])."""
+    r = np.random.default_rng(seed)
+    nblk = (K + 31) // 32
+    A = round_to(r.standard_normal((M, K)), "bf16")
+    q = r.integers(0, 16, (N, nblk * 32)).astype(np.uint8)
+    zp = r.integers(0, 16, (N, nblk)).astype(np.uint8) if with_zp else np.full((N, nblk), 8, np.uint8)
+    base = 1.0 / (4.0 * np.sqrt(max(K, 1)))
+    if pow2_scales:
+        scales = (2.0 ** np.round(np.log2(base) + r.integers(-1, 2, (N, nblk)))).astype(np.float32)
+    else:
+        scales = (r.uniform(0.5, 1.5, (N, nblk)) * base).astype(np.float32)
+    B = pack_nibbles(q).reshape(N, nblk, 16)
+    zpk = pack_nibbles(zp) if with_zp else None
+    bias = round_to(r.standard_normal(N) * 0.1, "bf16") if with_bias else None
+    return {"A": A, "q": q[:, :K], "zp": zp, "scales": scales, "B": B, "zero_points": zpk,
+            "bias": bias, "K": K}

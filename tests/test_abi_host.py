@@ -186,6 +186,19 @@ def test_residual_entry_point_errors(ox, monkeypatch):
     monkeypatch.delenv("OX_FORCE_KERNEL")
 
 
+def test_matmul_nbits_argument_errors(ox):
+    L = raw(ox)
+    nb = L.ox_matmul_nbits
+    assert nb(ox.OX_F32, 2, 4, 64, 4, 32, FAKE, FAKE, FAKE, None, None, FAKE, None) == 3   # dtype
+    assert nb(ox.OX_BF16, 2, 4, 64, 8, 32, FAKE, FAKE, FAKE, None, None, FAKE, None) == 3  # bits
+    assert nb(ox.OX_BF16, 2, 4, 64, 4, 64, FAKE, FAKE, FAKE, None, None, FAKE, None) == 3  # block size
+    assert nb(ox.OX_BF16, -2, 4, 64, 4, 32, FAKE, FAKE, FAKE, None, None, FAKE, None) == 2
+    assert nb(ox.OX_BF16, 2, 4, 64, 4, 32, FAKE, None, FAKE, None, None, FAKE, None) == 1  # B NULL
+    assert nb(ox.OX_BF16, 2, 4, 64, 4, 32, FAKE, FAKE + 2, FAKE, None, None, FAKE, None) == 1
+    assert nb(ox.OX_BF16, 2, 4, 64, 4, 32, FAKE + 1, FAKE, FAKE, None, None, FAKE, None) == 1
+    assert nb(ox.OX_BF16, 0, 4, 64, 4, 32, None, None, None, None, None, None, None) == 0  # empty
+
+
 def test_dynamic_quantize_argument_errors(ox):
     L = raw(ox)
     need = L.ox_dynamic_quantize_workspace_bytes()

@@ -698,6 +698,49 @@ def test_qconv_variants_bit_exact(ox, xu, yu, wz):
         assert np.array_equal(g8, y), geom
 
 
+# ----------------------------------------------------------- MatMulNBits --
+
+def nbits_run(ox, t, a_offset=0):
+    M, K = t["A"].shape
+    buf = torch.zeros(M * K + a_offset, dtype=torch.bfloat16, device="cuda")
+    Ad = buf[a_offset:].view(M, K)
+    Ad.copy_(dev(t["A"], "bf16"))
+    B = torch.from_numpy(t["B"]).cuda()
+    sc = torch.from_numpy(t["scales"]).cuda()
+    zp = None if t["zero_points"] is None else torch.from_numpy(t["zero_points"]).cuda()
+    bias = None if t["bias"] is None else dev(t["bias"], "bf16")
+    Y = nan_like((M, B.shape[0]), "bf16")
+    ox.ox_matmul_nbits(Ad, B, sc, K, zp, bias, Y)
+    torch.cuda.synchronize()
+    return host64(Y)
+
+
+@pytest.mark.parametrize("shape", [(1, 64, 64), (5, 45, 200), (33, 77, 512), (130, 96, 96),
+                                   (64, 256, 4096), (1, 4096, 4096)])
+@pytest.mark.parametrize("zp", [True, False])
+def test_matmul_nbits_parity(ox, shape, zp):
+    # decode (one row) and prefill rows, ragged N and K (a partial last
+    # block), with and without zero points and bias; scales that are powers
+    # of two keep every dequantised weight exact in bf16
+    M, N, K = shape
+    say("nbits", shape, zp)
+    t = synth.nbits_inputs(M, N, K, 300 + M + N + K, with_zp=zp, with_bias=(M % 2 == 1))
+    got = nbits_run(ox, t)
+    ref = oracle.matmul_nbits(t["A"], t["B"], t["scales"], K, t["zero_points"], t["bias"])
+    assert_close(got, ref, "bf16", "nbits %s" % (shape,))
+
+
+def test_matmul_nbits_general_scales_and_unaligned_rows(ox):
+    # arbitrary fp32 scales (each dequantised weight rounded to bf16 once)
+    # and A one element off 16-byte alignment (the element-wise A loads)
+    for (M, N, K, off) in [(7, 100, 320, 0), (3, 64, 96, 1), (40, 33, 72, 1)]:
+        say("nbits general", (M, N, K, off))
+        t = synth.nbits_inputs(M, N, K, 500 + K, pow2_scales=False)
+        got = nbits_run(ox, t, off)
+        ref = oracle.matmul_nbits(t["A"], t["B"], t["scales"], K, t["zero_points"], t["bias"])
+        assert_close(got, ref, "bf16", "nbits general")
+
+
 # ------------------------------------------------- DynamicQuantizeLinear --
 
 def dq_check(ox, x, offset=0):

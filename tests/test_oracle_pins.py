@@ -567,6 +567,41 @@ def test_q_uint8_output_range_and_rounding():
         oracle.qgemm(x, w, None, 0, None, xs, np.array([ws], np.float32), ys, 256, True)
 
 
+# ----------------------------------------------------------- MatMulNBits --
+
+def test_matmul_nbits_against_unpacked_weights():
+    # the oracle unpacks B itself; here W is built from the unpacked q, zero
+    # points and scales the generator drew, and multiplied with numpy
+    for (M, N, K, zp) in [(3, 5, 64, True), (2, 7, 200, False), (1, 4, 31, True)]:
+        t = synth.nbits_inputs(M, N, K, 100 + K, with_zp=zp, pow2_scales=False)
+        got = oracle.matmul_nbits(t["A"], t["B"], t["scales"], K, t["zero_points"], t["bias"])
+        blk = np.arange(K) // 32
+        W = (t["q"].astype(np.float64) - t["zp"][:, blk]) * t["scales"].astype(np.float64)[:, blk]
+        ref = t["A"] @ W.T + t["bias"][None, :]
+        assert np.allclose(got, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_matmul_nbits_nibble_order_and_zero_point_cases():
+    # one weight at k = 1 (the high nibble of byte 0) and one at k = 34
+    # (block 1, byte 1, low nibble); A picks them out
+    N, K = 1, 64
+    B = np.zeros((N, 2, 16), np.uint8)
+    B[0, 0, 0] = 0x5 | (0xC << 4)          # k=0 -> 5, k=1 -> 12
+    B[0, 1, 1] = 0x3                       # k=34 -> 3
+    scales = np.array([[0.5, 2.0]], np.float32)
+    zps = np.array([[0x8 | (0x1 << 4)]], np.uint8)     # block 0: 8, block 1: 1
+    A = np.zeros((3, K))
+    A[0, 1] = 1.0
+    A[1, 34] = 1.0
+    A[2, 0] = 1.0
+    Y = oracle.matmul_nbits(A, B, scales, K, zps)
+    assert Y[:, 0].tolist() == [(12 - 8) * 0.5, (3 - 1) * 2.0, (5 - 8) * 0.5]
+    # default zero point 8: an all-8 B contributes nothing, leaving the bias
+    B8 = np.full((2, 1, 16), 0x88, np.uint8)
+    Y = oracle.matmul_nbits(np.ones((4, 32)), B8, np.ones((2, 1), np.float32), 32, None, [1.5, -2.0])
+    assert np.array_equal(Y, np.tile([1.5, -2.0], (4, 1)))
+
+
 # ------------------------------------------------- DynamicQuantizeLinear --
 
 def test_dynamic_quantize_closed_forms():
