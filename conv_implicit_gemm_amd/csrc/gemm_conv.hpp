@@ -126,9 +126,8 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
   }
 }
 
-template <int DT, int BM, int BN>
-int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
-  constexpr int BKU = 1;
+template <int DT, int BM, int BN, int BKU>
+int launch_gemm_tile_k(const GemmArgs& a, hipStream_t s) {
   dim3 grid((a.cols + BN - 1) / BN, (a.rows + BM - 1) / BM, a.batch);
   if constexpr (DT == DT_I8) {
     hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, true>), grid, dim3(kThreads), 0, s, a);
@@ -143,6 +142,28 @@ int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
       hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, false, false>), grid, dim3(kThreads), 0, s, a);
   }
   return (int)hipGetLastError();
+}
+
+// With few output tiles (at most two blocks per CU) one block runs the whole
+// K loop and every K stage costs about one global-load latency: a long K (16
+// stages or more of 64 bytes per row) then takes four 64-byte units per
+// stage, a quarter of the stages (small tiles only: the LDS of the deeper
+// stages would cost a larger grid its occupancy).
+template <int DT, int BM, int BN>
+constexpr bool deep_k_tile() { return BM <= 64 && BN <= 64; }
+template <int DT>
+bool deep_k(int64_t K, int64_t blocks) {
+  constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
+  return blocks <= 512 && (K + KSTEP1 - 1) / KSTEP1 >= 16;
+}
+
+template <int DT, int BM, int BN>
+int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
+  if constexpr (deep_k_tile<DT, BM, BN>()) {
+    const int64_t blocks = (int64_t)((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) * a.batch;
+    if (deep_k<DT>(a.K, blocks)) return launch_gemm_tile_k<DT, BM, BN, 4>(a, s);
+  }
+  return launch_gemm_tile_k<DT, BM, BN, 1>(a, s);
 }
 
 template <int DT>
@@ -298,9 +319,8 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
   }
 }
 
-template <int DT, int BM, int BN>
-int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
-  constexpr int BKU = 1;
+template <int DT, int BM, int BN, int BKU>
+int launch_conv_tile_k(const ConvArgs& a, int kind, hipStream_t s) {
   const int Mpg = a.M / a.group;
   const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
   dim3 grid((unsigned)((NP + BN - 1) / BN), (Mpg + BM - 1) / BM, a.group);
@@ -309,6 +329,17 @@ int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
   else
     hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 0>), grid, dim3(kThreads), 0, s, a);
   return (int)hipGetLastError();
+}
+
+template <int DT, int BM, int BN>
+int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
+  if constexpr (deep_k_tile<DT, BM, BN>()) {
+    const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
+    const int64_t blocks = ((NP + BN - 1) / BN) * ((a.M / a.group + BM - 1) / BM) * a.group;
+    if (deep_k<DT>((int64_t)(a.C / a.group) * a.kH * a.kW, blocks))
+      return launch_conv_tile_k<DT, BM, BN, 4>(a, kind, s);
+  }
+  return launch_conv_tile_k<DT, BM, BN, 1>(a, kind, s);
 }
 
 template <int DT>

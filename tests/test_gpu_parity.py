@@ -116,6 +116,24 @@ def test_gemm_layouts_and_scalars(ox, dtype, ta, tb, act):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_long_k_few_tiles(ox, dtype, ta, tb):
+    # few output tiles and a long, ragged K: the small tiles with four K
+    # units per stage, in every operand layout
+    M, N, K = 64, 200, 1500
+    say("gemm long K", dtype, ta, tb)
+    r = np.random.default_rng(150 + 2 * ta + tb)
+    A = synth.round_to(r.standard_normal((K, M) if ta else (M, K)), dtype)
+    B = synth.round_to(r.standard_normal((N, K) if tb else (K, N)) / math.sqrt(K), dtype)
+    bias = synth.round_to(r.uniform(-1, 1, N), dtype)
+    Y = nan_like((M, N), dtype)
+    ox.ox_gemm_fused(dev(A, dtype), dev(B, dtype), dev(bias, dtype), transA=bool(ta),
+                     transB=bool(tb), act="gelu", Y=Y)
+    torch.cuda.synchronize()
+    assert_close(host64(Y), oracle.gemm(A, B, bias, 1.0, 1.0, ta, tb, "gelu"), dtype, "gemm long K")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("tb", [0, 1])
 @pytest.mark.parametrize("force", [None, "mfma"])
 def test_gemm_single_row(ox, dtype, tb, force, monkeypatch):
@@ -648,7 +666,7 @@ def test_qgemm_variants_bit_exact(ox, xu, yu, wz):
     # QLinearMatMul / MatMulInteger with uint8 activations or outputs and
     # per-channel weight zero points, over ragged tiles and one row
     r = np.random.default_rng(700 + 4 * xu + 2 * yu + wz)
-    for (M, K, N) in [(77, 200, 45), (130, 72, 33), (1, 64, 16), (64, 1000, 96)]:
+    for (M, K, N) in [(77, 200, 45), (130, 72, 33), (1, 64, 16), (64, 1000, 96), (40, 2500, 70)]:
         say("qgemm", (xu, yu, wz), (M, K, N))
         x, w, wzp, xzp, bq, x_s, w_s = q_inputs(r, xu, wz, (M, K), (N, K))
         acc0, _ = oracle.qgemm(x, w, bq, xzp, wzp, x_s, w_s, 1.0, 0)
@@ -679,7 +697,9 @@ def test_qconv_variants_bit_exact(ox, xu, yu, wz):
             (2, 64, 14, 14, 96, 3, 3, 1, (1, 1, 1, 1), 1, 1),
             (2, 48, 7, 9, 40, 1, 1, 1, (0, 0, 0, 0), 1, 1),
             (2, 24, 10, 13, 24, 3, 3, 1, (1, 1, 1, 1), 1, 24),
-            (1, 16, 1, 50, 16, 1, 9, 1, (0, 4, 0, 4), 1, 16)]:
+            (1, 16, 1, 50, 16, 1, 9, 1, (0, 4, 0, 4), 1, 16),
+            (1, 128, 9, 9, 64, 3, 3, 1, (1, 1, 1, 1), 1, 1),      # long K: four K units per stage
+            (1, 1024, 1, 50, 72, 1, 1, 1, (0, 0, 0, 0), 1, 1)]:
         geom = (N, Cin, H, W, M, kH, kW, s, pads, d, g)
         say("qconv", (xu, yu, wz), geom,
             ox.ox_conv2d_variant("i8", N, Cin, H, W, M, kH, kW, (s, s), pads, (d, d), g))
