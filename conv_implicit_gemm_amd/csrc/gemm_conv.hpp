@@ -146,15 +146,18 @@ int launch_gemm_tile_k(const GemmArgs& a, hipStream_t s) {
 
 // With few output tiles (at most two blocks per CU) one block runs the whole
 // K loop and every K stage costs about one global-load latency: a long K (16
-// stages or more of 64 bytes per row) then takes four 64-byte units per
-// stage, a quarter of the stages (small tiles only: the LDS of the deeper
-// stages would cost a larger grid its occupancy).
+// stages or more of 64 bytes per row; 4 or more when the grid has at most 64
+// blocks) then takes four 64-byte units per stage, a quarter of the stages
+// (small tiles only: the LDS of the deeper stages would cost a larger grid
+// its occupancy).
 template <int DT, int BM, int BN>
 constexpr bool deep_k_tile() { return BM <= 64 && BN <= 64; }
 template <int DT>
 bool deep_k(int64_t K, int64_t blocks) {
   constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
-  return blocks <= 512 && (K + KSTEP1 - 1) / KSTEP1 >= 16;
+  const int64_t stages = (K + KSTEP1 - 1) / KSTEP1;
+  // (a grid of at most 64 blocks leaves most CUs idle: there even 4 stages)
+  return (blocks <= 512 && stages >= 16) || (blocks <= 64 && stages >= 4);
 }
 
 template <int DT, int BM, int BN>
