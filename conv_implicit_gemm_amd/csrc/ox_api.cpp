@@ -107,7 +107,9 @@ bool log_on() {
 }
 
 // Tile choice: the largest tile that still gives two blocks per CU (the 256
-// CUs of an MI355X), never a tile taller than the problem.
+// CUs of an MI355X), never a tile taller than the problem; a problem too
+// small for that takes the smallest tile (the most blocks: each block's K
+// loop, not the MMA rate, sets the time there).
 int choose_tile(int64_t rows, int64_t cols, int64_t z) {
   static const int order[] = {TILE_128x128, TILE_64x128, TILE_128x64, TILE_64x64, TILE_32x64};
   for (int t : order) {
@@ -117,8 +119,7 @@ int choose_tile(int64_t rows, int64_t cols, int64_t z) {
     const int64_t blocks = ((rows + bm - 1) / bm) * ((cols + bn - 1) / bn) * z;
     if (blocks >= 512) return t;
   }
-  if (rows <= 32) return TILE_32x64;
-  return TILE_64x64;
+  return TILE_32x64;
 }
 
 ox_status pick_tile(const char* fn, const Force& f, int64_t rows, int64_t cols, int64_t z,
