@@ -248,13 +248,16 @@ def gemm_layers(ox, synth, torch, rows, dtype, stream):
         Xd, Wd, bd = (torch.from_numpy(a.astype(np.float32)).cuda().to(tdt) for a in (X, W, b))
         Yd = torch.empty((r.M, r.N), dtype=tdt, device="cuda")
         code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
+        # the split-K workspace where one is planned (allocated once, untimed)
+        nws = ox.ox_gemm_workspace_bytes(dtype, r.M, r.N, r.K)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
         args = (code, r.M, r.N, r.K, 0, 1, 1.0, Xd.data_ptr(), Wd.data_ptr(), 1.0, bd.data_ptr(),
-                ox.ACT[r.act], Yd.data_ptr(), None, stream)
-        keep = (Xd, Wd, bd, Yd)
+                ox.ACT[r.act], Yd.data_ptr(), ws.data_ptr() if nws else None, nws, stream)
+        keep = (Xd, Wd, bd, Yd, ws)
         variant = ("gemv/%s" % dtype) if r.M == 1 else ("mfma/%s" % dtype)
 
         def launch(args=args, keep=keep):
-            return ox.lib.ox_gemm_fused(*args)
+            return ox.lib.ox_gemm_fused_ws(*args)
 
         def oracle_at(idx, X=X, W=W, b=b, r=r):
             return oracle.gemm(X, W, b, transB=True, act=r.act, at=idx)

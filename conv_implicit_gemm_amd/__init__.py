@@ -29,7 +29,7 @@ EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_i
            "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
            "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool",
            "ox_int8_prepare_ex", "ox_dynamic_quantize_workspace_bytes", "ox_dynamic_quantize_linear",
-           "ox_matmul_nbits")
+           "ox_matmul_nbits", "ox_gemm_workspace_bytes", "ox_gemm_fused_ws")
 
 
 class OxError(RuntimeError):
@@ -75,6 +75,8 @@ def _load():
         "ox_int8_prepare_ex": (I, [I64, I64, P, P, P, F, I32, I, F, I32, I, P, P]),
         "ox_dynamic_quantize_workspace_bytes": (C.c_size_t, []),
         "ox_matmul_nbits": (I, [I, I64, I64, I64, I, I, P, P, P, P, P, P, P]),
+        "ox_gemm_workspace_bytes": (C.c_size_t, [I, I64, I64, I64]),
+        "ox_gemm_fused_ws": (I, [I, I64, I64, I64, I, I, F, P, P, F, P, I, P, P, C.c_size_t, P]),
         "ox_dynamic_quantize_linear": (I, [I64, P, P, P, P, P, C.c_size_t, P]),
         "ox_last_error": (C.c_char_p, []),
         "ox_version": (C.c_char_p, []),
@@ -196,6 +198,29 @@ def ox_gemm_fused(A, B, bias=None, alpha=1.0, beta=1.0, transA=False, transB=Fal
     _check(lib.ox_gemm_fused(code, M, N, K, int(transA), int(transB), float(alpha), _ptr(A), _ptr(B),
                              float(beta), _ptr(bias), ACT[act], _ptr(Y), _ptr(int8_params),
                              _stream(stream)))
+    return Y
+
+
+def ox_gemm_workspace_bytes(dtype, M, N, K):
+    code = {"f32": OX_F32, "bf16": OX_BF16}[dtype]
+    return int(lib.ox_gemm_workspace_bytes(code, M, N, K))
+
+
+def ox_gemm_fused_ws(A, B, workspace, bias=None, alpha=1.0, beta=1.0, transA=False, transB=False,
+                     act="none", Y=None, stream=None):
+    """Float Gemm + activation with a split-K workspace (see ox_gemm_workspace_bytes)."""
+    torch = _torch()
+    for t, n in ((A, "A"), (B, "B"), (bias, "bias"), (Y, "Y"), (workspace, "workspace")):
+        _dense(t, n)
+    M = A.shape[1] if transA else A.shape[0]
+    K = A.shape[0] if transA else A.shape[1]
+    N = B.shape[0] if transB else B.shape[1]
+    if Y is None:
+        Y = torch.empty((M, N), dtype=A.dtype, device=A.device)
+    nb = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.ox_gemm_fused_ws(_dtype_code(A), M, N, K, int(transA), int(transB), float(alpha),
+                                _ptr(A), _ptr(B), float(beta), _ptr(bias), ACT[act], _ptr(Y),
+                                _ptr(workspace), nb, _stream(stream)))
     return Y
 
 

@@ -3,6 +3,7 @@
 // Each *.hip unit instantiates these for one input type.
 #pragma once
 
+#include <algorithm>
 #include <type_traits>
 
 #include "engine.hpp"
@@ -167,6 +168,103 @@ int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
     if (deep_k<DT>(a.K, blocks)) return launch_gemm_tile_k<DT, BM, BN, 4>(a, s);
   }
   return launch_gemm_tile_k<DT, BM, BN, 1>(a, s);
+}
+
+// ---------------------------------------------------- split-K float Gemm --
+//
+// A Gemm with too few output tiles to fill the chip and a long K: slice z of
+// the grid takes K range [z*kslice, (z+1)*kslice) (a multiple of the deep
+// stage, so vector alignment is kept) and writes its fp32 partial tile to
+// ws[z][rows][cols]; a second kernel adds the slices in order and applies
+// alpha, beta*bias and the activation.  32x64 tiles (the tile a problem
+// this small is given), four K units per stage.
+
+template <int DT, bool LK, bool RK>
+__global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(const GemmArgs a, int kslice,
+                                                               float* ws) {
+  typedef typename Traits<DT>::T T;
+  constexpr int BM = 32, BN = 64, BKU = 4;
+  __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * Lds<BKU>::ROWB];
+  const int z = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
+  const int k0 = z * kslice;
+  const int Kz = min(kslice, a.K - k0);          // >= 1: the host makes every slice non-empty
+  const T* L = (const T*)a.L + (LK ? (int64_t)k0 : (int64_t)k0 * a.ldl);
+  const T* R = (const T*)a.R + (RK ? (int64_t)k0 : (int64_t)k0 * a.ldr);
+  typename std::conditional<LK, LoadRowK<DT, BM, BKU>, LoadColK<DT, BM, BKU>>::type la;
+  typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
+  if constexpr (LK) {
+    la.init(L, a.ldl, row0, a.rows, Kz, a.l_vec);
+  } else {
+    const int r = row0 + threadIdx.x % BM;
+    la.init_col(L + r, r < a.rows, a.ldl, Kz);
+  }
+  if constexpr (RK) {
+    lb.init(R, a.ldr, col0, a.cols, Kz, a.r_vec);
+  } else {
+    const int c = col0 + threadIdx.x % BN;
+    lb.init_col(R + c, c < a.cols, a.ldr, Kz);
+  }
+  f32x4_t acc[BM / 32][BN / 32];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 32; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  engine_mainloop<DT, BM, BN, BKU>(la, lb, Kz, smem, acc);
+  float* P = ws + (int64_t)z * a.rows * a.cols;
+  for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+    const int row = row0 + r, col = col0 + c;
+    if (row < a.rows && col < a.cols) P[(int64_t)row * a.cols + col] = v;
+  });
+}
+
+template <int DT, int ACT>
+__global__ __launch_bounds__(kThreads) void gemm_splitk_reduce(const GemmArgs a, int S,
+                                                               const float* ws) {
+  typedef typename Traits<DT>::T T;
+  const int64_t total = (int64_t)a.rows * a.cols;
+  const T* bias = (const T*)a.bias;
+  T* Y = (T*)a.Y;
+  for (int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * kThreads) {
+    float v = 0.0f;
+    for (int z = 0; z < S; ++z) v += ws[(int64_t)z * total + i];
+    const int row = (int)(i / a.cols), col = (int)(i - (int64_t)row * a.cols);
+    float o = a.alpha * v;
+    if (bias) o += a.beta * to_f32(bias[col]);
+    store_float(Y + (int64_t)row * a.ldy + col, act_c<ACT>(o));
+  }
+}
+
+template <int DT>
+int launch_gemm_splitk_dt(const GemmArgs& a, int S, int kslice, float* ws, void* stream) {
+  hipStream_t s = (hipStream_t)stream;
+  dim3 grid((a.cols + 63) / 64, (a.rows + 31) / 32, S);
+  if (a.l_kmajor && a.r_kmajor)
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+  else if (a.l_kmajor)
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+  else if (a.r_kmajor)
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+  else
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+  const int64_t total = (int64_t)a.rows * a.cols;
+  const int nb = (int)std::min<int64_t>(2048, (total + kThreads - 1) / kThreads);
+  const float* wsc = ws;
+  switch (a.act) {
+    case ACT_RELU:
+      hipLaunchKernelGGL((gemm_splitk_reduce<DT, ACT_RELU>), dim3(nb), dim3(kThreads), 0, s, a, S, wsc);
+      break;
+    case ACT_RELU6:
+      hipLaunchKernelGGL((gemm_splitk_reduce<DT, ACT_RELU6>), dim3(nb), dim3(kThreads), 0, s, a, S, wsc);
+      break;
+    case ACT_GELU:
+      hipLaunchKernelGGL((gemm_splitk_reduce<DT, ACT_GELU>), dim3(nb), dim3(kThreads), 0, s, a, S, wsc);
+      break;
+    default:
+      hipLaunchKernelGGL((gemm_splitk_reduce<DT, ACT_NONE>), dim3(nb), dim3(kThreads), 0, s, a, S, wsc);
+      break;
+  }
+  return (int)hipGetLastError();
 }
 
 template <int DT>

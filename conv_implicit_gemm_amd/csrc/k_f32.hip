@@ -12,4 +12,8 @@ int launch_conv_f32(const ConvArgs& a, int kind, int tile, void* stream) {
   return launch_conv_dt<DT_F32>(a, kind, tile, stream);
 }
 
+int launch_gemm_splitk_f32(const GemmArgs& a, int S, int kslice, float* ws, void* stream) {
+  return launch_gemm_splitk_dt<DT_F32>(a, S, kslice, ws, stream);
+}
+
 }  // namespace ox

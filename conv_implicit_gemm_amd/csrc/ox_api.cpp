@@ -408,10 +408,42 @@ ox_status ox_matmul_batched(ox_dtype t, int64_t batch, int64_t M, int64_t N, int
   return hip_result(fn, rc);
 }
 
-ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA, int transB,
-                        float alpha, const void* A, const void* B, float beta, const void* bias,
-                        ox_act act, void* Y, const void* int8_params, void* stream) {
-  const char* fn = "ox_gemm_fused";
+// Split-K plan of a float Gemm: 0 when none.  Only problems that no tile
+// fills the chip with (they take 32x64 tiles, here fewer than 256 of them)
+// and whose K gives every slice at least four deep stages; at most 8 slices
+// and about one block per CU.
+struct GemmSplit {
+  int S, kslice;
+};
+static GemmSplit gemm_split_plan(ox_dtype t, int64_t M, int64_t N, int64_t K) {
+  GemmSplit g = {0, 0};
+  if (t != OX_F32 && t != OX_BF16) return g;
+  if (M <= 1 || N <= 0 || K <= 0) return g;
+  if (choose_tile(M, N, 1) != TILE_32x64) return g;
+  const int64_t blocks = ((M + 31) / 32) * ((N + 63) / 64);
+  if (blocks >= 256) return g;
+  const int64_t kstep = t == OX_F32 ? 64 : 128;   // four 64-byte units per stage
+  const int64_t stages = (K + kstep - 1) / kstep;
+  int64_t S = std::min<int64_t>({8, 256 / blocks, stages / 4});
+  if (S < 2) return g;
+  const int64_t kslice = (stages + S - 1) / S * kstep;
+  S = (K + kslice - 1) / kslice;
+  if (S < 2) return g;
+  g.S = (int)S;
+  g.kslice = (int)kslice;
+  return g;
+}
+
+size_t ox_gemm_workspace_bytes(ox_dtype t, int64_t M, int64_t N, int64_t K) {
+  const GemmSplit g = gemm_split_plan(t, M, N, K);
+  return g.S ? (size_t)g.S * (size_t)M * (size_t)N * sizeof(float) : 0;
+}
+
+static ox_status gemm_fused_impl(const char* fn, ox_dtype t, int64_t M, int64_t N, int64_t K,
+                                 int transA, int transB, float alpha, const void* A, const void* B,
+                                 float beta, const void* bias, ox_act act, void* Y,
+                                 const void* int8_params, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
   const bool i8 = t == OX_I8 || t == OX_I32;
   if (!i8) {
     ox_status st = check_float_dt(fn, t);
@@ -488,6 +520,21 @@ ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA,
               (long long)N, (long long)K, transB, act_name(act));
     return hip_result(fn, launch_gemv(a, stream));
   }
+  if (workspace && !i8 && f.tile == -1) {
+    const GemmSplit g = gemm_split_plan(t, M, N, K);
+    if (g.S) {
+      const size_t need = (size_t)g.S * (size_t)M * (size_t)N * sizeof(float);
+      if (workspace_bytes < need || (uintptr_t)workspace % 16)
+        return fail(OX_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned and hold %zu bytes", fn,
+                    need);
+      if (log_on())
+        fprintf(stderr, "[ox] %s dt=%d M=%lld N=%lld K=%lld -> mfma split-K S=%d kslice=%d\n", fn,
+                (int)t, (long long)M, (long long)N, (long long)K, g.S, g.kslice);
+      const int rc = t == OX_F32 ? launch_gemm_splitk_f32(a, g.S, g.kslice, (float*)workspace, stream)
+                                 : launch_gemm_splitk_bf16(a, g.S, g.kslice, (float*)workspace, stream);
+      return hip_result(fn, rc);
+    }
+  }
   int tile;
   st = pick_tile(fn, f, M, N, 1, &tile);
   if (st) return st;
@@ -499,6 +546,23 @@ ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA,
                : t == OX_F32 ? launch_gemm_f32(a, tile, stream)
                              : launch_gemm_bf16(a, tile, stream);
   return hip_result(fn, rc);
+}
+
+ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA, int transB,
+                        float alpha, const void* A, const void* B, float beta, const void* bias,
+                        ox_act act, void* Y, const void* int8_params, void* stream) {
+  return gemm_fused_impl("ox_gemm_fused", t, M, N, K, transA, transB, alpha, A, B, beta, bias, act,
+                         Y, int8_params, nullptr, 0, stream);
+}
+
+ox_status ox_gemm_fused_ws(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA, int transB,
+                           float alpha, const void* A, const void* B, float beta, const void* bias,
+                           ox_act act, void* Y, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  if (t != OX_F32 && t != OX_BF16)
+    return fail(OX_ERR_UNSUPPORTED, "ox_gemm_fused_ws: dtype %d is not OX_F32 or OX_BF16", (int)t);
+  return gemm_fused_impl("ox_gemm_fused_ws", t, M, N, K, transA, transB, alpha, A, B, beta, bias,
+                         act, Y, nullptr, workspace, workspace_bytes, stream);
 }
 
 ox_status ox_conv2d_fused(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,

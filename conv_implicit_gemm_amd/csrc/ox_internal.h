@@ -179,6 +179,10 @@ struct SmallcPlan {
 int launch_gemm_f32(const GemmArgs& a, int tile, void* stream);
 int launch_gemm_bf16(const GemmArgs& a, int tile, void* stream);
 int launch_gemm_i8(const GemmArgs& a, int tile, void* stream);
+// split-K float Gemm (32x64 tiles): S slices of kslice along K, fp32
+// partials in ws [S][rows][cols], then the reduction with the epilogue
+int launch_gemm_splitk_f32(const GemmArgs& a, int S, int kslice, float* ws, void* stream);
+int launch_gemm_splitk_bf16(const GemmArgs& a, int S, int kslice, float* ws, void* stream);
 // kind: 0 = implicit GEMM (any kernel / stride / pad / dilation / group),
 //       1 = 1x1 stride-1 unpadded convolution (a per-image GEMM on NCHW).
 int launch_conv_f32(const ConvArgs& a, int kind, int tile, void* stream);

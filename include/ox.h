@@ -105,6 +105,21 @@ ox_status ox_gemm_fused(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA,
                         const void* bias, ox_act act, void* Y, const void* int8_params,
                         void* stream);
 
+/* The same float Gemm (t = OX_F32 / OX_BF16) with a caller-owned workspace
+ * that lets a problem too small to fill the GPU split its reduction: K is
+ * cut into slices whose fp32 partial products go to the workspace
+ * ([slices][M][N]) and a second kernel adds them in slice order before
+ * alpha, beta * bias and the activation (so the sum order differs from
+ * ox_gemm_fused's; the tolerance of a float Gemm covers it).  workspace:
+ * DEVICE, 16-byte aligned, at least ox_gemm_workspace_bytes(t, M, N, K)
+ * bytes (0 = no split planned: the call is then ox_gemm_fused; workspace
+ * may be NULL); calls sharing a workspace must not overlap. */
+size_t ox_gemm_workspace_bytes(ox_dtype t, int64_t M, int64_t N, int64_t K);
+ox_status ox_gemm_fused_ws(ox_dtype t, int64_t M, int64_t N, int64_t K, int transA, int transB,
+                           float alpha, const void* A, const void* B, float beta,
+                           const void* bias, ox_act act, void* Y, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* ONNX Conv + bias + activation, float path (Conv -> BatchNorm -> Relu folded
  * into one fused convolution, tensorforge "ResNet fusion"; per-shape choice
  * of an implicit-GEMM, a 1x1 and a depthwise kernel, "OxiONNX 0.1.7

@@ -186,6 +186,21 @@ def test_residual_entry_point_errors(ox, monkeypatch):
     monkeypatch.delenv("OX_FORCE_KERNEL")
 
 
+def test_gemm_workspace_plan_and_errors(ox):
+    # split-K is planned only for float Gemms too small to fill the GPU with a long K
+    assert ox.ox_gemm_workspace_bytes("bf16", 64, 1024, 4096) == 8 * 64 * 1024 * 4
+    assert ox.ox_gemm_workspace_bytes("bf16", 1000, 4096, 1024) == 0      # fills the chip
+    assert ox.ox_gemm_workspace_bytes("f32", 16, 64, 128) == 0            # K too short
+    assert ox.ox_gemm_workspace_bytes("bf16", 1, 4096, 4096) == 0         # one row: GEMV
+    L = raw(ox)
+    g = L.ox_gemm_fused_ws
+    assert g(ox.OX_I8, 64, 1024, 4096, 0, 1, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, FAKE, 1 << 30, None) == 3
+    need = ox.ox_gemm_workspace_bytes("bf16", 64, 1024, 4096)
+    assert g(ox.OX_BF16, 64, 1024, 4096, 0, 1, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, FAKE, need - 4, None) == 1
+    assert "workspace" in ox.ox_last_error()
+    assert g(ox.OX_BF16, 64, 1024, 4096, 0, 1, 1.0, FAKE, FAKE, 1.0, None, 0, FAKE, FAKE + 8, need, None) == 1
+
+
 def test_matmul_nbits_argument_errors(ox):
     L = raw(ox)
     nb = L.ox_matmul_nbits

@@ -134,6 +134,29 @@ def test_gemm_long_k_few_tiles(ox, dtype, ta, tb):
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (0, 1), (1, 0), (1, 1)])
+def test_gemm_split_k_workspace(ox, dtype, ta, tb):
+    # few output tiles, long K: K slices with fp32 partials in the caller's
+    # workspace, then the ordered sum with alpha, beta*bias and GELU; ragged K
+    # (a short last slice) and the MLP's 4096-deep row shape
+    for (M, N, K) in [(64, 200, 1500), (64, 1024, 4096), (37, 70, 1777)]:
+        say("gemm split-K", dtype, ta, tb, (M, N, K))
+        r = np.random.default_rng(170 + 2 * ta + tb + K)
+        A = synth.round_to(r.standard_normal((K, M) if ta else (M, K)), dtype)
+        B = synth.round_to(r.standard_normal((N, K) if tb else (K, N)) / math.sqrt(K), dtype)
+        bias = synth.round_to(r.uniform(-1, 1, N), dtype)
+        nb = ox.ox_gemm_workspace_bytes(dtype, M, N, K)
+        assert nb > 0
+        ws = torch.full((nb // 4,), float("nan"), dtype=torch.float32, device="cuda")
+        Y = nan_like((M, N), dtype)
+        ox.ox_gemm_fused_ws(dev(A, dtype), dev(B, dtype), ws, dev(bias, dtype), alpha=0.75, beta=-1.5,
+                            transA=bool(ta), transB=bool(tb), act="gelu", Y=Y)
+        torch.cuda.synchronize()
+        ref = oracle.gemm(A, B, bias, 0.75, -1.5, ta, tb, "gelu")
+        assert_close(host64(Y), ref, dtype, "gemm split-K")
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("tb", [0, 1])
 @pytest.mark.parametrize("force", [None, "mfma"])
 def test_gemm_single_row(ox, dtype, tb, force, monkeypatch):
