@@ -4,10 +4,10 @@ Every entry point launches kernels only (no allocation, no memset, no host
 synchronisation), so a caller may record a whole layer chain into one HIP
 graph and replay it.  The test captures such a chain (a split-K 3x3 conv with
 its workspace, a depthwise conv, a residual pointwise conv, MaxPool,
-BatchNorm + ReLU, GlobalAveragePool, a Gemm + GELU, a batched f32 MatMul and an
-int8 Gemm), then replays it several times with new inputs; between replays
-the outputs are refilled with NaN and the same chain runs eagerly on the same
-buffers.  Each replay must equal the eager results bit for bit (the same
+BatchNorm + ReLU, GlobalAveragePool, a Gemm + GELU, a batched f32 MatMul, an
+int8 Gemm and a split-K Gemm with its workspace), then replays it several
+times with new inputs; between replays the outputs are refilled with NaN and
+the same chain runs eagerly on the same buffers.  Each replay must equal the eager results bit for bit (the same
 kernels with the same launch shapes and a fixed summation order), and the
 MatMul is also checked against the oracle."""
 import sys
@@ -62,6 +62,12 @@ def test_captured_chain_replays_match_eager():
     qblk = torch.from_numpy(ox.ox_int8_prepare(qt["wq"], qt["w_s"], qt["x_s"], qt["x_zp"], qt["y_s"],
                                                qt["y_zp"], qt["bias_q"])).cuda()
     wq = torch.from_numpy(qt["wq"]).cuda()
+    # a split-K Gemm with its workspace (64 rows, K = 2048)
+    Ag = wt(64, 2048, scale=1.0)
+    Bs = wt(256, 2048, scale=0.02)
+    gws_bytes = ox.ox_gemm_workspace_bytes("bf16", 64, 256, 2048)
+    assert gws_bytes > 0
+    gws = torch.empty(gws_bytes // 4, dtype=torch.float32, device="cuda")
 
     # inputs (refilled before every run) and outputs (fixed addresses)
     X0 = torch.empty((N, C, H, H), dtype=bf, device="cuda")
@@ -74,7 +80,8 @@ def test_captured_chain_replays_match_eager():
     Y7 = torch.empty((N, 300), dtype=bf, device="cuda")
     Cm = torch.empty((4, 37, 29), dtype=torch.float32, device="cuda")
     Yq = torch.empty((77, 45), dtype=torch.int8, device="cuda")
-    outs = [Y1, Y2, Y3, Y4, Y5, Y6, Y7, Cm]
+    Ys = torch.empty((64, 256), dtype=bf, device="cuda")
+    outs = [Y1, Y2, Y3, Y4, Y5, Y6, Y7, Cm, Ys]
 
     s = torch.cuda.Stream()
 
@@ -88,6 +95,7 @@ def test_captured_chain_replays_match_eager():
         ox.ox_gemm_fused(Y6.view(N, M), Bg, bg, act="gelu", Y=Y7, stream=s)
         ox.ox_matmul_batched(A, B, Cm, stream=s)
         ox.ox_gemm_fused(xq, wq, transB=True, int8_params=qblk, out_dtype=torch.int8, Y=Yq, stream=s)
+        ox.ox_gemm_fused_ws(Ag, Bs, gws, transB=True, act="relu", Y=Ys, stream=s)
 
     def refill(rep):
         rr = np.random.default_rng(5000 + rep)
