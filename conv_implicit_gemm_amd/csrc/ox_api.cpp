@@ -962,14 +962,36 @@ ox_status ox_int8_prepare_ex(int64_t M, int64_t Kper, const int8_t* Wq_host, con
       return fail(OX_ERR_INVALID_ARG, "%s: w_zp[%lld]=%d outside [-128,127]", fn, (long long)m, w_zp[m]);
     if (w_zp && w_zp[m] != 0) any_wzp = true;
   }
-  // |x - x_zp| <= 255 and |w| <= 128 (|w - w_zp| <= 255 with weight zero
-  // points): the largest K whose sum stays inside int32
-  const int64_t kmax = any_wzp ? 33000 : 66000;
-  if (Kper > kmax)
-    return fail(OX_ERR_UNSUPPORTED, "%s: Kper=%lld > %lld could overflow the int32 accumulator", fn,
-                (long long)Kper, (long long)kmax);
   // the kernels read a uint8 tensor as int8 with the top bit flipped (u - 128)
   const int32_t xz = x_unsigned ? x_zp - 128 : x_zp;
+  // Exact int32 range check, per output channel, over every activation the
+  // type allows (int8 view x in [-128, 127], so x - x_zp in [-lo, hi]):
+  //  * the true accumulator sum (x - x_zp)(w - w_zp[m]) + bias_q[m] lies in
+  //    [bias - (lo*P + hi*Q), bias + (hi*P + lo*Q)], with P and Q the sums of
+  //    the positive parts and of the magnitudes of the negative parts of
+  //    w - w_zp[m];
+  //  * the kernels' raw int8 x int8 sums (sum x*w, before the folded bias)
+  //    lie in [-(128*Pw + 127*Qw), 127*Pw + 128*Qw] for the raw weights.
+  // A channel whose range leaves int32 for some input is refused.
+  {
+    const int64_t lo = (int64_t)xz + 128, hi = 127 - (int64_t)xz;
+    const int64_t imax = INT32_MAX, imin = INT32_MIN;
+    for (int64_t m = 0; m < M; ++m) {
+      const int64_t z = w_zp ? w_zp[m] : 0;
+      int64_t P = 0, Q = 0, Pw = 0, Qw = 0;
+      for (int64_t k = 0; k < Kper; ++k) {
+        const int64_t w = Wq_host[m * Kper + k], d = w - z;
+        if (d > 0) P += d; else Q -= d;
+        if (w > 0) Pw += w; else Qw -= w;
+      }
+      const int64_t b = bias_q ? (int64_t)bias_q[m] : 0;
+      if (b + hi * P + lo * Q > imax || b - (lo * P + hi * Q) < imin ||
+          127 * Pw + 128 * Qw > imax || -(128 * Pw + 127 * Qw) < imin)
+        return fail(OX_ERR_UNSUPPORTED,
+                    "%s: channel %lld (Kper=%lld) could overflow the int32 accumulator for some input",
+                    fn, (long long)m, (long long)Kper);
+    }
+  }
   const int32_t yz = y_unsigned ? y_zp - 128 : y_zp;
   char* out = (char*)params_host_out;
   Int8Header h;

@@ -283,7 +283,13 @@ size_t ox_int8_params_bytes(int64_t M);
  * Wq_host: HOST int8 [M, Kper]; w_scale: HOST [M] (> 0); bias_q: HOST [M] or
  * NULL; x_zp, y_zp in [-128, 127]; scales finite and > 0.
  * params_host_out: HOST, ox_int8_params_bytes(M) bytes; the caller copies it
- * to the device and passes that copy to the int8 calls. */
+ * to the device and passes that copy to the int8 calls.
+ * Range: the accumulators are int32.  A channel m is refused
+ * (OX_ERR_UNSUPPORTED, naming m) when some input could take it outside
+ * int32: bias_q[m] + sum_k (x - x_zp) * w[m,k] over every x the activation
+ * type allows, or the kernels' raw sum_k x * w[m,k] before the folded bias.
+ * The bound is exact per channel (computed from the weights), so e.g.
+ * Kper = 65793 weights of -128 with x_zp = -128 pass and 65794 do not. */
 ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const float* w_scale,
                           float x_scale, int32_t x_zp, float y_scale, int32_t y_zp,
                           const int32_t* bias_q, void* params_host_out);
@@ -301,7 +307,7 @@ ox_status ox_int8_prepare(int64_t M, int64_t Kper, const int8_t* Wq_host, const 
  * requantised outputs are written as uint8 and y_zp is in [0, 255].
  * Wq_host: HOST int8 [M, Kper] (uint8 weights: pass w - 128 with
  * w_zp - 128, which leaves every product unchanged); w_zp: HOST int32 [M] in
- * [-128, 127] or NULL (all 0).  With a nonzero w_zp, Kper is at most 33000.
+ * [-128, 127] or NULL (all 0).
  * The block records the signedness: the same int8 calls (ox_gemm_fused with
  * OX_I8 / OX_I32, ox_conv2d_int8) then read and write uint8 tensors through
  * their int8_t pointers.  ox_int8_prepare(...) is this call with w_zp = NULL

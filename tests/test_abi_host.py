@@ -397,14 +397,50 @@ def test_int8_prepare_ex_errors(ox):
         ox.ox_int8_prepare(wq, ws, 0.1, 0, 0.2, 256, y_unsigned=True)       # uint8 y_zp > 255
     with pytest.raises(ox.OxError):
         ox.ox_int8_prepare(wq, ws, 0.1, 0, 0.2, 0, w_zp=[0, 128])           # w_zp > 127
-    big = np.zeros((1, 40000), np.int8)
-    ox.ox_int8_prepare(big, [0.01], 0.1, 0, 0.2, 0)                         # symmetric: fine
-    with pytest.raises(ox.OxError):
-        ox.ox_int8_prepare(big, [0.01], 0.1, 0, 0.2, 0, w_zp=[1])           # K > 33000 with w_zp
     with pytest.raises(TypeError):
         ox.ox_int8_prepare(wq.astype(np.uint8), ws, 0.1, 0, 0.2, 0)         # uint8 weights unconverted
     w8, z8 = ox.ox_int8_weights_from_uint8(np.array([[0, 255, 128]], np.uint8), 130)
     assert w8.tolist() == [[-128, 127, 0]] and z8.tolist() == [2]
+
+
+def test_int8_prepare_refuses_exactly_the_channels_that_could_overflow(ox):
+    # The int32 accumulator bound, exact per channel.  With x_zp = -128 an
+    # activation byte can sit 255 above the zero point; K weights of -128
+    # then reach -255*128*K, which fits int32 for K = 65793 and not for
+    # K = 65794 (2^31 = 65793.1 * 32640).
+    ok = np.full((1, 65793), -128, np.int8)
+    bad = np.full((1, 65794), -128, np.int8)
+    ox.ox_int8_prepare(ok, [0.01], 0.1, -128, 0.2, 0)
+    with pytest.raises(ox.OxError) as e:
+        ox.ox_int8_prepare(bad, [0.01], 0.1, -128, 0.2, 0)
+    assert "channel 0" in str(e.value)
+    # the K = 66000 case of a fixed K limit: refused at x_zp = -128 ...
+    k66 = np.full((1, 66000), -128, np.int8)
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(k66, [0.01], 0.1, -128, 0.2, 0)
+    # ... and accepted at x_zp = 0, where |x - x_zp| <= 128 (128*128*66000 fits)
+    ox.ox_int8_prepare(k66, [0.01], 0.1, 0, 0.2, 0)
+    # the bias counts: -255*128*65793 = -2147483520, so bias_q = -128 reaches
+    # INT32_MIN exactly (accepted) and -129 goes past it (refused)
+    ox.ox_int8_prepare(ok, [0.01], 0.1, -128, 0.2, 0, bias_q=[-128])
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(ok, [0.01], 0.1, -128, 0.2, 0, bias_q=[-129])
+    # only the offending channel matters: a second channel of zeros is fine,
+    # and the refusal names channel 1 when the long row is second
+    two = np.zeros((2, 65794), np.int8)
+    two[1, :] = -128
+    with pytest.raises(ox.OxError) as e:
+        ox.ox_int8_prepare(two, [0.01, 0.01], 0.1, -128, 0.2, 0)
+    assert "channel 1" in str(e.value)
+    # weight zero points: w - w_zp = -127 for w = 0, w_zp = 127; the bound is
+    # 255*127*K, which fits for K = 66311 and not for K = 66312
+    # (2^31 = 66311.06 * 32385)
+    z = np.zeros((1, 66311), np.int8)
+    ox.ox_int8_prepare(z, [0.01], 0.1, -128, 0.2, 0, w_zp=[127])
+    with pytest.raises(ox.OxError):
+        ox.ox_int8_prepare(np.zeros((1, 66312), np.int8), [0.01], 0.1, -128, 0.2, 0, w_zp=[127])
+    # ... and a zero-point-free row of zeros of that length is fine
+    ox.ox_int8_prepare(np.zeros((1, 66312), np.int8), [0.01], 0.1, -128, 0.2, 0)
 
 
 def test_pack_weights_is_tap_major_channel_blocks(ox):

@@ -6,10 +6,12 @@ graph and replay it.  The test captures such a chain (a split-K 3x3 conv with
 its workspace, a depthwise conv, a residual pointwise conv, MaxPool,
 BatchNorm + ReLU, GlobalAveragePool, a Gemm + GELU, a batched f32 MatMul, an
 int8 Gemm and a split-K Gemm with its workspace), then replays it several
-times with new inputs; between replays the outputs are refilled with NaN and
-the same chain runs eagerly on the same buffers.  Each replay must equal the eager results bit for bit (the same
-kernels with the same launch shapes and a fixed summation order), and the
-MatMul is also checked against the oracle."""
+times with new inputs.  Each call reads its own input buffers, refilled with
+new seeded values before every replay, so every replayed output is compared
+with the oracle on those values; between replays the outputs are refilled
+with NaN and the same chain runs eagerly on the same buffers, and each replay
+must also equal the eager results bit for bit (the same kernels with the same
+launch shapes and a fixed summation order)."""
 import sys
 
 import numpy as np
@@ -34,7 +36,7 @@ def to_dev(a, dt):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda().to(dt)
 
 
-def test_captured_chain_replays_match_eager():
+def test_captured_chain_replays_match_eager_and_oracle():
     import conv_implicit_gemm_amd as ox
     bf = torch.bfloat16
     r = np.random.default_rng(4242)
@@ -43,17 +45,20 @@ def test_captured_chain_replays_match_eager():
     Hp = 4                         # MaxPool 3x3 s2 p1 of 7x7
 
     def wt(*shape, scale):
-        return to_dev(synth.round_to(r.standard_normal(shape) * scale, "bf16"), bf)
+        h = synth.round_to(r.standard_normal(shape) * scale, "bf16")
+        return h, to_dev(h, bf)
 
-    # weights and parameters (fixed across replays)
-    W1, b1 = wt(M, C, 3, 3, scale=0.05), wt(M, scale=0.1)
-    Wd, bd = wt(M, 1, 3, 3, scale=0.3), wt(M, scale=0.1)
-    Wp, bp = wt(M, M, 1, 1, scale=0.08), wt(M, scale=0.1)
-    gam = torch.from_numpy(r.uniform(0.5, 1.5, M).astype(np.float32)).cuda()
-    bet = torch.from_numpy((r.standard_normal(M) * 0.3).astype(np.float32)).cuda()
-    mu = torch.from_numpy((r.standard_normal(M) * 0.3).astype(np.float32)).cuda()
-    var = torch.from_numpy(r.uniform(0.5, 1.5, M).astype(np.float32)).cuda()
-    Bg, bg = wt(M, 300, scale=0.1), wt(300, scale=0.1)
+    # weights and parameters (fixed across replays): host float64 copies of
+    # the exact bf16 values, and the device tensors
+    (W1h, W1), (b1h, b1) = wt(M, C, 3, 3, scale=0.05), wt(M, scale=0.1)
+    (Wdh, Wd), (bdh, bd) = wt(M, 1, 3, 3, scale=0.3), wt(M, scale=0.1)
+    (Wph, Wp), (bph, bp) = wt(M, M, 1, 1, scale=0.08), wt(M, scale=0.1)
+    gh = r.uniform(0.5, 1.5, M).astype(np.float32)
+    beh = (r.standard_normal(M) * 0.3).astype(np.float32)
+    muh = (r.standard_normal(M) * 0.3).astype(np.float32)
+    varh = r.uniform(0.5, 1.5, M).astype(np.float32)
+    gam, bet, mu, var = (torch.from_numpy(v).cuda() for v in (gh, beh, muh, varh))
+    (Bgh, Bg), (bgh, bg) = wt(M, 300, scale=0.1), wt(300, scale=0.1)
     ws_bytes = ox.ox_conv2d_workspace_bytes("bf16", N, C, H, H, M, 3, 3, (1, 1), (1, 1, 1, 1))
     assert ws_bytes > 0
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
@@ -63,14 +68,17 @@ def test_captured_chain_replays_match_eager():
                                                qt["y_zp"], qt["bias_q"])).cuda()
     wq = torch.from_numpy(qt["wq"]).cuda()
     # a split-K Gemm with its workspace (64 rows, K = 2048)
-    Ag = wt(64, 2048, scale=1.0)
-    Bs = wt(256, 2048, scale=0.02)
+    Bsh, Bs = wt(256, 2048, scale=0.02)
     gws_bytes = ox.ox_gemm_workspace_bytes("bf16", 64, 256, 2048)
     assert gws_bytes > 0
     gws = torch.empty(gws_bytes // 4, dtype=torch.float32, device="cuda")
 
-    # inputs (refilled before every run) and outputs (fixed addresses)
-    X0 = torch.empty((N, C, H, H), dtype=bf, device="cuda")
+    # inputs (refilled before every run, one buffer per call) and outputs
+    # (fixed addresses)
+    shapes_in = {"X0": (N, C, H, H), "X1": (N, M, H, H), "X2": (N, M, H, H), "R2": (N, M, H, H),
+                 "X3": (N, M, H, H), "X4": (N, M, Hp, Hp), "X5": (N, M, Hp, Hp), "X6": (N, M),
+                 "Ag": (64, 2048)}
+    ins = {k: torch.empty(v, dtype=bf, device="cuda") for k, v in shapes_in.items()}
     A = torch.empty((4, 37, 53), dtype=torch.float32, device="cuda")
     B = torch.empty((4, 53, 29), dtype=torch.float32, device="cuda")
     xq = torch.empty((77, 200), dtype=torch.int8, device="cuda")
@@ -86,30 +94,54 @@ def test_captured_chain_replays_match_eager():
     s = torch.cuda.Stream()
 
     def chain():
-        ox.ox_conv2d_fused(X0, W1, b1, (1, 1), (1, 1, 1, 1), act="relu", Y=Y1, stream=s, workspace=ws)
-        ox.ox_conv2d_fused(Y1, Wd, bd, (1, 1), (1, 1, 1, 1), group=M, act="relu6", Y=Y2, stream=s)
-        ox.ox_conv2d_fused_res(Y2, Wp, Y1, bp, act="relu", Y=Y3, stream=s)
-        ox.ox_maxpool2d(Y3, (3, 3), (2, 2), (1, 1, 1, 1), Y=Y4, stream=s)
-        ox.ox_batchnorm_act(Y4, gam, bet, mu, var, 1e-5, "relu", Y=Y5, stream=s)
-        ox.ox_global_avgpool(Y5, Y=Y6, stream=s)
-        ox.ox_gemm_fused(Y6.view(N, M), Bg, bg, act="gelu", Y=Y7, stream=s)
+        i = ins
+        ox.ox_conv2d_fused(i["X0"], W1, b1, (1, 1), (1, 1, 1, 1), act="relu", Y=Y1, stream=s, workspace=ws)
+        ox.ox_conv2d_fused(i["X1"], Wd, bd, (1, 1), (1, 1, 1, 1), group=M, act="relu6", Y=Y2, stream=s)
+        ox.ox_conv2d_fused_res(i["X2"], Wp, i["R2"], bp, act="relu", Y=Y3, stream=s)
+        ox.ox_maxpool2d(i["X3"], (3, 3), (2, 2), (1, 1, 1, 1), Y=Y4, stream=s)
+        ox.ox_batchnorm_act(i["X4"], gam, bet, mu, var, 1e-5, "relu", Y=Y5, stream=s)
+        ox.ox_global_avgpool(i["X5"], Y=Y6, stream=s)
+        ox.ox_gemm_fused(i["X6"], Bg, bg, act="gelu", Y=Y7, stream=s)
         ox.ox_matmul_batched(A, B, Cm, stream=s)
         ox.ox_gemm_fused(xq, wq, transB=True, int8_params=qblk, out_dtype=torch.int8, Y=Yq, stream=s)
-        ox.ox_gemm_fused_ws(Ag, Bs, gws, transB=True, act="relu", Y=Ys, stream=s)
+        ox.ox_gemm_fused_ws(i["Ag"], Bs, gws, transB=True, act="relu", Y=Ys, stream=s)
 
     def refill(rep):
+        # new seeded inputs for every call; returns their host values
         rr = np.random.default_rng(5000 + rep)
-        X0.copy_(to_dev(synth.round_to(rr.standard_normal((N, C, H, H)), "bf16"), bf))
-        a64 = rr.standard_normal((4, 37, 53))
-        b64 = rr.standard_normal((4, 53, 29))
-        A.copy_(torch.from_numpy(a64.astype(np.float32)))
-        B.copy_(torch.from_numpy(b64.astype(np.float32)))
-        xq.copy_(torch.from_numpy(rr.integers(-128, 128, (77, 200)).astype(np.int8)))
+        h = {}
+        for k, shp in shapes_in.items():
+            h[k] = synth.round_to(rr.standard_normal(shp), "bf16")
+            ins[k].copy_(to_dev(h[k], bf))
+        h["A"] = rr.standard_normal((4, 37, 53)).astype(np.float32).astype(np.float64)
+        h["B"] = rr.standard_normal((4, 53, 29)).astype(np.float32).astype(np.float64)
+        A.copy_(torch.from_numpy(h["A"].astype(np.float32)))
+        B.copy_(torch.from_numpy(h["B"].astype(np.float32)))
+        h["xq"] = rr.integers(-128, 128, (77, 200)).astype(np.int8)
+        xq.copy_(torch.from_numpy(h["xq"]))
         for t in outs:
             t.fill_(float("nan"))
         Yq.fill_(0)
         torch.cuda.synchronize()
-        return a64.astype(np.float32).astype(np.float64), b64.astype(np.float32).astype(np.float64)
+        return h
+
+    def oracle_refs(h):
+        # what each call computes, from the same inputs, by the oracle
+        _, yq = oracle.gemm_int8(h["xq"], qt["wq"], qt["bias_q"], qt["x_zp"], qt["x_s"], qt["w_s"],
+                                 qt["y_s"], qt["y_zp"])
+        return [
+            ("conv3x3", oracle.conv2d(h["X0"], W1h, b1h, (1, 1), (1, 1, 1, 1), act="relu"), "bf16"),
+            ("depthwise", oracle.conv2d(h["X1"], Wdh, bdh, (1, 1), (1, 1, 1, 1), group=M, act="relu6"),
+             "bf16"),
+            ("1x1+residual", oracle.conv2d(h["X2"], Wph, bph, act="relu", residual=h["R2"]), "bf16"),
+            ("maxpool", oracle.maxpool2d(h["X3"], (3, 3), (2, 2), (1, 1, 1, 1)), "bf16"),
+            ("bn+relu", oracle.batchnorm_act(h["X4"], gh, beh, muh, varh, 1e-5, "relu"), "bf16"),
+            ("gap", oracle.global_avgpool(h["X5"]), "bf16"),
+            ("gemm+gelu", oracle.gemm(h["X6"], Bgh, bgh, act="gelu"), "bf16"),
+            ("matmul", oracle.matmul(h["A"], h["B"]), "f32"),
+            ("split-K gemm", oracle.gemm(h["Ag"], Bsh, None, transB=True, act="relu"), "bf16"),
+            ("int8 gemm", yq, None),
+        ]
 
     say("graph chain: warm-up and capture")
     refill(0)
@@ -124,11 +156,17 @@ def test_captured_chain_replays_match_eager():
 
     for rep in range(1, 5):
         say("graph chain replay", rep)
-        a64, b64 = refill(rep)
+        h = refill(rep)
         g.replay()
         torch.cuda.synchronize()
         got = [t.clone() for t in outs + [Yq]]
-        assert_close(Cm.double().cpu().numpy(), oracle.matmul(a64, b64), "f32", "replay matmul")
+        for (name, ref, dt), x in zip(oracle_refs(h), got):
+            if dt is None:
+                assert np.array_equal(x.cpu().numpy(), ref), "replay %d %s" % (rep, name)
+            else:
+                xh = x.double().cpu().numpy()
+                assert not np.isnan(xh).any(), name
+                assert_close(xh, ref.reshape(xh.shape), dt, "replay %d %s" % (rep, name))
         refill(rep)
         with torch.cuda.stream(s):
             chain()

@@ -20,16 +20,36 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
 # ------------------------------------------------------------------ MatMul --
 
+def read_golden(name):
+    """key = value lines of a golden file (comments start with #)."""
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = (t.strip() for t in line.split("=", 1))
+                vals[k] = float(v) if "." in v else int(v)
+    return vals
+
+
 def test_all_ones_64_cube_gives_64():
     # The closed-form case of the OxiONNX 0.1.7 two-stream race report
-    # ("Why OxiONNX 0.1.7 is a game changer"): a 64x64x64 all-ones MatMul,
-    # where every correct element is 64.
-    A = np.ones((1, 64, 64))
-    C = oracle.matmul(A, A)
-    assert C.shape == (1, 64, 64)
-    assert np.all(C == 64.0)
-    Y = oracle.gemm(A[0], A[0], transB=True)
-    assert np.all(Y == 64.0)
+    # ("Why OxiONNX 0.1.7 is a game changer"): an all-ones MatMul of the
+    # sizes the golden file records, where every correct element equals K.
+    g = read_golden("all_ones_64.txt")
+    M, N, K = g["M"], g["N"], g["K"]
+    assert M * N == g["elements"] and g["value"] == K
+    A = np.ones((1, M, K))
+    B = np.ones((1, K, N))
+    C = oracle.matmul(A, B)
+    assert C.shape == (1, M, N)
+    assert np.all(C == g["value"])
+    Y = oracle.gemm(A[0], B[0].T.copy(), transB=True)
+    assert np.all(Y == g["value"])
+    # the race's reported result (3456 elements reading 0.0) fails this pin
+    bad = C.copy().ravel()
+    bad[:g["race_wrong"]] = g["race_wrong_value"]
+    assert np.count_nonzero(bad != g["value"]) == g["race_wrong"]
 
 
 def test_matmul_integer_inputs_exact_against_int64():
@@ -491,6 +511,90 @@ def test_int8_accumulator_range_is_asserted():
     with pytest.raises(oracle.OracleError) as e:
         oracle.gemm_int8(xq, wq, None, 127, 0.1, np.ones(1, np.float32), 1.0, 0)
     assert e.value.code == oracle.ERANGE
+
+
+
+def _np_requant(acc, x_s, w_s, y_s, y_zp, axis, lo=-128, hi=127):
+    # The requantisation written out with numpy, independent of the oracle's C
+    # code: multiplier (x_s * w_s[m]) / y_s in float64 in that order, the
+    # accumulator times it, numpy's rint (half to even), + y_zp, saturate.
+    mult = (np.float64(np.float32(x_s)) * np.asarray(w_s, np.float32).astype(np.float64)) \
+        / np.float64(np.float32(y_s))
+    shape = [1] * acc.ndim
+    shape[axis] = -1
+    v = acc.astype(np.float64) * mult.reshape(shape)
+    return np.clip(np.rint(v) + y_zp, lo, hi).astype(np.int64)
+
+
+def _distinct_scales(n, seed):
+    # per-channel weight scales that differ from channel to channel, drawn as
+    # the int8 workloads draw them (U[1e-3, 1e-2]), widened so that no two are
+    # close: a requantisation that takes another channel's scale changes
+    # many outputs
+    ws = np.random.default_rng(seed).permutation(np.linspace(1e-3, 1e-2, n))
+    return ws.astype(np.float32)
+
+
+def test_int8_conv_requant_uses_each_output_channels_scale():
+    # the requantised y of conv2d_int8, element by element, against the
+    # numpy requantisation with w_s[m] of its own channel m (stride, pads and
+    # a ragged channel count)
+    layer = synth.Int8Layer("t", "conv", 1, 27, 11,
+                            synth.ConvLayer("t", 2, 3, 9, 7, 11, 3, 2, 1, 1, "none"))
+    t = synth.int8_inputs(layer, 4, 98)
+    ws = _distinct_scales(11, 5)
+    acc, y = oracle.conv2d_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"], ws,
+                                t["y_s"], t["y_zp"], (2, 2), (1, 1, 1, 1))
+    ref = _np_requant(acc, t["x_s"], ws, t["y_s"], t["y_zp"], axis=1)
+    assert np.array_equal(y.astype(np.int64), ref)
+    # the channels' outputs really differ in scale: the same accumulator
+    # requantised with a neighbour's scale gives other bytes somewhere
+    assert not np.array_equal(ref, _np_requant(acc, t["x_s"], np.roll(ws, 1), t["y_s"],
+                                               t["y_zp"], axis=1))
+
+
+def test_qconv_requant_uses_each_output_channels_scale():
+    # qconv2d with uint8 activations and outputs, per-channel weight zero
+    # points and per-channel scales, in groups (each group's channels carry
+    # their own scale)
+    r = np.random.default_rng(36)
+    x = r.integers(0, 256, (2, 4, 6, 7))
+    w = r.integers(-128, 128, (6, 2, 3, 3))
+    wz = r.integers(-128, 128, 6)
+    bias = r.integers(-3000, 3000, 6).astype(np.int32)
+    ws = _distinct_scales(6, 6)
+    for unsigned, y_zp in ((False, -7), (True, 131)):
+        acc, y = oracle.qconv2d(x, w, bias, 141, wz, 0.05, ws, 1.9, y_zp, unsigned,
+                                (1, 2), (1, 2, 0, 1), (2, 1), 2)
+        lo, hi = (0, 255) if unsigned else (-128, 127)
+        ref = _np_requant(acc, 0.05, ws, 1.9, y_zp, axis=1, lo=lo, hi=hi)
+        assert np.array_equal(y.astype(np.int64), ref)
+
+
+def test_qgemm_requant_uses_each_output_columns_scale():
+    # qgemm: column j of Y takes w_s[j]; int8 and uint8 outputs
+    r = np.random.default_rng(37)
+    x = r.integers(-128, 128, (13, 40))
+    w = r.integers(-127, 128, (9, 40))
+    wz = r.integers(-128, 128, 9)
+    bias = r.integers(-2000, 2000, 9).astype(np.int32)
+    ws = _distinct_scales(9, 7)
+    for unsigned, y_zp in ((False, 3), (True, 120)):
+        acc, y = oracle.qgemm(x, w, bias, -11, wz, 0.04, ws, 2.3, y_zp, unsigned)
+        lo, hi = (0, 255) if unsigned else (-128, 127)
+        ref = _np_requant(acc, 0.04, ws, 2.3, y_zp, axis=1, lo=lo, hi=hi)
+        assert np.array_equal(y.astype(np.int64), ref)
+
+
+def test_int8_gemm_requant_all_outputs_against_numpy():
+    # every output of gemm_int8 (not only sampled ones) against the numpy
+    # requantisation with its column's scale
+    layer = synth.Int8Layer("t", "gemm", 37, 96, 24)
+    t = synth.int8_inputs(layer, 4, 99)
+    acc, y = oracle.gemm_int8(t["xq"], t["wq"], t["bias_q"], t["x_zp"], t["x_s"], t["w_s"],
+                              t["y_s"], t["y_zp"])
+    ref = _np_requant(acc, t["x_s"], t["w_s"], t["y_s"], t["y_zp"], axis=1)
+    assert np.array_equal(y.astype(np.int64), ref)
 
 
 # ---------------------------- uint8 activations, asymmetric weight zero points --
