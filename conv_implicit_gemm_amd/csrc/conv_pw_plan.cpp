@@ -12,6 +12,12 @@ int launch_pw_1_32(const ConvArgs& a, const PwPlan& p, void* s);
 int launch_pw_1_64(const ConvArgs& a, const PwPlan& p, void* s);
 int launch_pw_2_32(const ConvArgs& a, const PwPlan& p, void* s);
 int launch_pw_2_64(const ConvArgs& a, const PwPlan& p, void* s);
+int launch_pwd_128_64_64(const ConvArgs& a, const PwdPlan& p, void* s);
+int launch_pwd_128_64_32(const ConvArgs& a, const PwdPlan& p, void* s);
+int launch_pwd_64_128_64(const ConvArgs& a, const PwdPlan& p, void* s);
+int launch_pwd_64_128_32(const ConvArgs& a, const PwdPlan& p, void* s);
+int launch_pwd_64_256_64(const ConvArgs& a, const PwdPlan& p, void* s);
+int launch_pwd_64_256_32(const ConvArgs& a, const PwdPlan& p, void* s);
 
 namespace {
 
@@ -140,7 +146,114 @@ bool pw_plan(const ConvArgs& a, PwPlan* out) {
   return false;
 }
 
+// ---------------------------------------------------- DMA-staged kernel --
+//
+// Configurations (BP pixels x BC channels, KC channels per stage, S stages,
+// WP waves along the pixels) -- each one instantiation in k_conv_pwd.hip:
+struct PwdCfg {
+  int BP, BC, KC, S, WP;
+  int (*launch)(const ConvArgs&, const PwdPlan&, void*);
+};
+const PwdCfg kPwdCfgs[] = {
+    {128, 64, 64, 3, 4, launch_pwd_128_64_64}, {128, 64, 32, 4, 4, launch_pwd_128_64_32},
+    {64, 128, 64, 3, 2, launch_pwd_64_128_64}, {64, 128, 32, 4, 2, launch_pwd_64_128_32},
+    {64, 256, 64, 2, 1, launch_pwd_64_256_64}, {64, 256, 32, 3, 1, launch_pwd_64_256_32},
+};
+
+int pwd_lds(const PwdCfg& c, bool res) {
+  const int slot = c.KC * c.BP * 2 + c.BC * c.KC * 2, stage = c.BC * (c.BP * 2 + 8);
+  return c.S * slot + (res || stage <= slot ? 0 : stage);
+}
+
+bool aligned16p(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// The configuration for a shape: output channels per block from M (the
+// whole of M up to 256, so that X is read once per pixel block where it
+// can be), 64-channel stages where C allows, 128-pixel tiles for 64-channel
+// blocks.  OX_PWD_CFG=BP:BC:KC pins one (an entry of the table above).
+bool pwd_plan(const ConvArgs& a, PwdPlan* out) {
+  if (!geometry(a)) return false;
+  const int64_t HW = (int64_t)a.H * a.W;
+  const int64_t Q = (int64_t)a.N * HW;
+  if (HW % 8 != 0 || Q == 0) return false;
+  if (!aligned16p(a.X) || !aligned16p(a.Y) || !aligned16p(a.Wt) || (a.res && !aligned16p(a.res)))
+    return false;
+  if ((int64_t)a.N * a.C * HW * 2 >= ((int64_t)1 << 30) || (int64_t)a.M * a.C * 2 >= ((int64_t)1 << 30) ||
+      (int64_t)a.N * a.M * HW >= ((int64_t)1 << 31))
+    return false;
+  int BP, BC, KC;
+  const char* e = getenv("OX_PWD_CFG");
+  if (e && *e) {
+    if (sscanf(e, "%d:%d:%d", &BP, &BC, &KC) != 3) return false;
+  } else {
+    BC = a.M <= 64 ? 64 : a.M <= 128 ? 128 : 256;
+    KC = a.C % 64 == 0 ? 64 : 32;
+    BP = BC == 64 ? 128 : 64;
+  }
+  const PwdCfg* cfg = nullptr;
+  for (const PwdCfg& c : kPwdCfgs)
+    if (c.BP == BP && c.BC == BC && c.KC == KC) cfg = &c;
+  if (!cfg || a.C % cfg->KC != 0) return false;
+  PwdPlan p;
+  p.BP = cfg->BP;
+  p.BC = cfg->BC;
+  p.KC = cfg->KC;
+  p.S = cfg->S;
+  p.WP = cfg->WP;
+  p.nmb = (a.M + p.BC - 1) / p.BC;
+  p.Q = (int)Q;
+  p.lds = pwd_lds(*cfg, a.res != nullptr);
+  if (p.lds > kLdsMax) return false;
+  // persistent grid of at most as many blocks as fit the chip at once
+  // (LDS-bound, at most two per CU).  Pixel ranges are k whole units of 128
+  // pixels -- 64 where 128 would leave fewer than 256 blocks -- with k the
+  // least that fits the grid, so that every block gets the same work.
+  // OX_PWD_GRID caps the block count (a test of ranges with several tiles).
+  const int per_cu = std::max(1, std::min(2, kLdsMax / p.lds));
+  int64_t cap = (int64_t)kCUs * per_cu;
+  if (const char* g = getenv("OX_PWD_GRID")) cap = std::max(1, atoi(g));
+  const int64_t units128 = (Q + 127) / 128;
+  const int unit = units128 * p.nmb >= kCUs || cap < kCUs ? 128 : 64;
+  const int64_t units = (Q + unit - 1) / unit;
+  const int64_t per_range_cap = std::max<int64_t>(1, cap / p.nmb);
+  const int64_t k = (units + per_range_cap - 1) / per_range_cap;
+  p.span = (int)std::min<int64_t>(k * unit, (int64_t)1 << 30);
+  p.nranges = (int)((units + k - 1) / k);
+  if ((int64_t)p.nranges * p.nmb >= ((int64_t)1 << 31)) return false;
+  p.grid = p.nranges * p.nmb;
+  p.hw = make_fastdiv((uint32_t)HW);
+  p.x_bytes = (uint32_t)((int64_t)a.N * a.C * HW * 2);
+  p.w_bytes = (uint32_t)((int64_t)a.M * a.C * 2);
+  *out = p;
+  return true;
+}
+
+const PwdCfg* pwd_cfg(const PwdPlan& p) {
+  for (const PwdCfg& c : kPwdCfgs)
+    if (c.BP == p.BP && c.BC == p.BC && c.KC == p.KC) return &c;
+  return nullptr;
+}
+
 }  // namespace
+
+bool conv_pwd_applicable(const ConvArgs& a) {
+  PwdPlan p;
+  return pwd_plan(a, &p);
+}
+
+int launch_conv_pwd(const ConvArgs& a, void* stream) {
+  PwdPlan p;
+  if (!pwd_plan(a, &p)) return 1;   // hipErrorInvalidValue
+  return pwd_cfg(p)->launch(a, p, stream);
+}
+
+const char* conv_pwd_describe(const ConvArgs& a, char* buf, int cap) {
+  PwdPlan p;
+  if (!pwd_plan(a, &p)) return "";
+  snprintf(buf, cap, "BP=%d BC=%d KC=%d S=%d WP=%d ranges=%d grid=%d lds=%d", p.BP, p.BC, p.KC, p.S, p.WP,
+           p.nranges, p.grid, p.lds);
+  return buf;
+}
 
 bool conv_pw_applicable(const ConvArgs& a) {
   if (!a.w_vec || ((uintptr_t)a.X) % 2 != 0) return false;

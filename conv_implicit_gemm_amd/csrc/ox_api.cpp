@@ -219,10 +219,11 @@ ConvArgs conv_args(int dt, const ox_conv_desc* d, int64_t Ho, int64_t Wo, const 
   return a;
 }
 
-enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2, KIND_PATCH = 3, KIND_PW = 4, KIND_SMALLC = 5 };
+enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2, KIND_PATCH = 3, KIND_PW = 4, KIND_SMALLC = 5,
+                KIND_PWD = 6 };
 
 const char* kind_name(int k) {
-  static const char* n[] = {"igemm", "1x1", "dw", "patch", "pw", "smallc"};
+  static const char* n[] = {"igemm", "1x1", "dw", "patch", "pw", "smallc", "pwd"};
   return n[k];
 }
 
@@ -258,6 +259,11 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
       if (!is_1x1 || !conv_pw_applicable(a))
         return fail(OX_ERR_UNSUPPORTED, "%s: forced 'pw' needs bf16, a 1x1/s1/p0/g1 conv, C %% 32 == 0 and aligned X/W", fn);
       *kind = KIND_PW;
+    } else if (!strcmp(f.variant, "pwd")) {
+      if (!is_1x1 || !conv_pwd_applicable(a))
+        return fail(OX_ERR_UNSUPPORTED, "%s: forced 'pwd' needs bf16, a 1x1/s1/p0/g1 conv, C %% 32 == 0, "
+                    "H*W %% 8 == 0 and 16-byte aligned X/W/Y", fn);
+      *kind = KIND_PWD;
     } else if (!strcmp(f.variant, "smallc")) {
       if (!conv_smallc_applicable(a))
         return fail(OX_ERR_UNSUPPORTED, "%s: forced 'smallc' needs bf16, C <= 4, group 1, stride 1 or 2, no dilation, kW <= 8", fn);
@@ -272,19 +278,19 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
       return fail(OX_ERR_INVALID_ARG, "%s: OX_FORCE_KERNEL variant '%s' does not apply to Conv", fn,
                   f.variant);
     }
-    if (a.res && *kind != KIND_PW && *kind != KIND_1X1 && *kind != KIND_IGEMM)
+    if (a.res && *kind != KIND_PW && *kind != KIND_PWD && *kind != KIND_1X1 && *kind != KIND_IGEMM)
       return fail(OX_ERR_UNSUPPORTED, "%s: forced '%s' does not take a residual input", fn, f.variant);
     return OX_OK;
   }
   if (a.res) {
     // a residual input: the kernels whose epilogue reads it are the
     // pointwise kernel and the tile engine (any geometry)
-    if (is_1x1) *kind = conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
+    if (is_1x1) *kind = conv_pwd_applicable(a) ? KIND_PWD : conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
     else *kind = KIND_IGEMM;
     return OX_OK;
   }
   if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
-  else if (is_1x1) *kind = conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
+  else if (is_1x1) *kind = conv_pwd_applicable(a) ? KIND_PWD : conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
   else if (conv_patch_applicable(a)) *kind = KIND_PATCH;
   else if (conv_smallc_applicable(a)) *kind = KIND_SMALLC;
   else *kind = KIND_IGEMM;
@@ -316,6 +322,7 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
     char plan[160] = "";
     if (kind == KIND_PATCH) conv_patch_describe(a, plan, sizeof(plan));
     if (kind == KIND_PW) conv_pw_describe(a, plan, sizeof(plan));
+    if (kind == KIND_PWD) conv_pwd_describe(a, plan, sizeof(plan));
     if (kind == KIND_SMALLC) conv_smallc_describe(a, plan, sizeof(plan));
     fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s %s\n",
             fn, a.dt, a.N, a.C, a.H, a.W, a.M, a.kH, a.kW, a.sh, a.sw, a.group, act_name(a.act),
@@ -329,6 +336,8 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
     rc = launch_conv_patch(a, stream);
   } else if (kind == KIND_PW) {
     rc = launch_conv_pw(a, stream);
+  } else if (kind == KIND_PWD) {
+    rc = launch_conv_pwd(a, stream);
   } else if (kind == KIND_SMALLC) {
     rc = launch_conv_smallc(a, stream);
   } else {

@@ -155,6 +155,24 @@ struct PwPlan {
   float* ws;  // split-K partials (splits * tiles * BM * BN floats), else null
 };
 
+// Plan of the DMA-staged pointwise kernel (bf16 1x1 with H*W % 8 == 0):
+// tile BP pixels x BC output channels, KC input channels per stage, S ring
+// stages, WP waves along the pixels (4/WP along the channels).  The grid is
+// persistent: nranges x nmb blocks, block (r, mb) computes channel block mb
+// over pixel range r = [r*span, min((r+1)*span, Q)), span = kunits * unit
+// pixels with unit = 64 or 128 -- in tiles of BP pixels.
+struct PwdPlan {
+  int BP, BC, KC, S, WP;
+  int nmb;                // channel blocks
+  int nranges;            // pixel ranges
+  int grid;               // nranges * nmb blocks
+  int span;               // pixels per range (a multiple of 64)
+  int Q;                  // pixels of the batch (N * H * W)
+  FastDiv hw;             // division by H * W
+  uint32_t x_bytes, w_bytes;   // buffer ranges of X and W
+  int lds;                // bytes of LDS
+};
+
 // Scratch bytes the plan chosen for `a` needs (0: no split-K).  Split-K is
 // only planned when a.ws is non-null.
 size_t conv_pw_ws_bytes(const ConvArgs& a);
@@ -199,6 +217,11 @@ bool conv_patch_applicable(const ConvArgs& a);
 bool conv_smallc_applicable(const ConvArgs& a);
 int launch_conv_smallc(const ConvArgs& a, void* stream);
 const char* conv_smallc_describe(const ConvArgs& a, char* buf, int cap);
+// DMA-staged pointwise kernel (bf16, 1x1, stride 1, unpadded, group 1,
+// C % 32 == 0, H*W % 8 == 0, 16-byte aligned X, W, Y and residual)
+bool conv_pwd_applicable(const ConvArgs& a);
+int launch_conv_pwd(const ConvArgs& a, void* stream);
+const char* conv_pwd_describe(const ConvArgs& a, char* buf, int cap);
 // pointwise kernel (bf16, 1x1, stride 1, unpadded, group 1, C % 32 == 0)
 bool conv_pw_applicable(const ConvArgs& a);
 int launch_conv_pw(const ConvArgs& a, void* stream);

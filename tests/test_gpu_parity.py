@@ -388,6 +388,124 @@ def test_pw_conv_sweep_bf16(ox, monkeypatch):
         assert_close(host64(Y), oracle.conv2d(X, Wt, b, act=act), "bf16", "pw %d" % ci)
 
 
+PWD_CFGS = ["128:64:64", "128:64:32", "64:128:64", "64:128:32", "64:256:64", "64:256:32"]
+
+
+@pytest.mark.parametrize("cfg", PWD_CFGS)
+def test_pwd_each_config_integer_exact(ox, cfg, monkeypatch):
+    # the DMA-staged pointwise kernel, each configuration pinned, on inputs
+    # in {-1, 0, 1}: every sum is an integer of magnitude <= C <= 256, exact
+    # in bf16, so a wrong swizzle, fragment row or pixel offset shows as a
+    # mismatch.  Ragged pixel tails (N*H*W not a multiple of the tile),
+    # partial channel blocks, tiles spanning images, every activation.
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pwd")
+    monkeypatch.setenv("OX_PWD_CFG", cfg)
+    kc = int(cfg.split(":")[2])
+    r = np.random.default_rng(4100 + PWD_CFGS.index(cfg))
+    cases = [(2, 128, 8, 8, 70), (3, 64, 4, 6, 150), (1, 256, 16, 16, 200), (5, 192, 2, 4, 33),
+             (2, 96, 6, 12, 256), (1, 32, 8, 1, 300)]
+    ran = 0
+    for ci, (N, Cin, H, W, M) in enumerate(cases):
+        if Cin % kc:
+            continue
+        act = ["none", "relu", "relu6", "gelu"][ci % 4]
+        X = r.integers(-1, 2, (N, Cin, H, W)).astype(np.float64)
+        Wt = r.integers(-1, 2, (M, Cin, 1, 1)).astype(np.float64)
+        b = r.integers(-3, 4, M).astype(np.float64)
+        say("pwd config", cfg, (N, Cin, H, W, M, act))
+        Y = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, act)
+        ref = oracle.conv2d(X, Wt, b, act=act)
+        if act == "gelu":
+            assert_close(host64(Y), ref, "bf16", "pwd %s case %d" % (cfg, ci))
+        else:
+            assert np.array_equal(host64(Y), ref), "pwd %s case %d" % (cfg, ci)
+        ran += 1
+    assert ran >= 3
+
+
+@pytest.mark.parametrize("grid", ["1", "5", "37"])
+def test_pwd_persistent_ranges(ox, grid, monkeypatch):
+    # a small persistent grid: each block walks a pixel range of many tiles,
+    # its ring running on from one tile into the next, and the ranges end
+    # inside tiles; integer-valued inputs, compared exactly
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pwd")
+    monkeypatch.setenv("OX_PWD_GRID", grid)
+    r = np.random.default_rng(4150 + int(grid))
+    for ci, (N, Cin, H, W, M) in enumerate([(3, 128, 12, 16, 64), (2, 64, 10, 24, 200),
+                                            (4, 96, 8, 8, 130), (1, 256, 20, 8, 520)]):
+        X = r.integers(-1, 2, (N, Cin, H, W)).astype(np.float64)
+        Wt = r.integers(-1, 2, (M, Cin, 1, 1)).astype(np.float64)
+        b = r.integers(-3, 4, M).astype(np.float64)
+        say("pwd persistent", grid, (N, Cin, H, W, M))
+        Y = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu")
+        assert np.array_equal(host64(Y), oracle.conv2d(X, Wt, b, act="relu")), \
+            "pwd grid %s case %d" % (grid, ci)
+
+
+def test_pwd_sweep_bf16(ox, monkeypatch):
+    # default configuration choice over random shapes the DMA kernel takes
+    # (H*W % 8 == 0, C % 32 == 0), random values
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pwd")
+    r = np.random.default_rng(4200)
+    for ci in range(30):
+        N = int(r.integers(1, 5))
+        Cin = int(r.choice([32, 64, 96, 128, 256, 384, 512]))
+        H, W = int(r.integers(1, 20)), 8 * int(r.integers(1, 4))
+        M = int(r.integers(1, 600))
+        act = str(r.choice(["none", "relu", "relu6", "gelu"]))
+        X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+        Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+        b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+        say("pwd sweep", ci, (N, Cin, H, W, M, act))
+        Y = run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, act)
+        assert_close(host64(Y), oracle.conv2d(X, Wt, b, act=act), "bf16", "pwd sweep %d" % ci)
+
+
+def test_pwd_not_taken_for_unaligned_or_odd_planes(ox, monkeypatch):
+    # the DMA kernel needs 16-byte aligned tensors and H*W % 8 == 0: other
+    # cases select another kernel (and a forced 'pwd' is refused), with the
+    # same results
+    r = np.random.default_rng(4300)
+    X = synth.round_to(r.standard_normal((2, 64, 7, 7)), "bf16")
+    Wt = synth.round_to(r.standard_normal((96, 64, 1, 1)) / 8.0, "bf16")
+    b = synth.round_to(r.uniform(-0.5, 0.5, 96), "bf16")
+    assert not ox.ox_conv2d_variant("bf16", 2, 64, 7, 7, 96, 1, 1).startswith("pwd/")
+    assert ox.ox_conv2d_variant("bf16", 2, 64, 8, 8, 96, 1, 1).startswith("pwd/")
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pwd")
+    with pytest.raises(ox.OxError):
+        run_conv(ox, X, Wt, b, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu")
+    monkeypatch.delenv("OX_FORCE_KERNEL")
+    X8 = synth.round_to(r.standard_normal((2, 64, 8, 8)), "bf16")
+    ref = oracle.conv2d(X8, Wt, b, act="relu")
+    for xoff, yoff in ((1, 0), (0, 4), (8, 8)):
+        say("pwd alignment", xoff, yoff)
+        Xd = misaligned(dev(X8, "bf16"), xoff)
+        Y = misaligned(nan_like((2, 96, 8, 8), "bf16"), yoff)
+        ox.ox_conv2d_fused(Xd, dev(Wt, "bf16"), dev(b, "bf16"), act="relu", Y=Y)
+        torch.cuda.synchronize()
+        assert_close(host64(Y), ref, "bf16", "pwd alignment %d %d" % (xoff, yoff))
+
+
+@pytest.mark.parametrize("cfg", PWD_CFGS)
+def test_pwd_residual_each_config(ox, cfg, monkeypatch):
+    # Y = act(conv + b + R) on the DMA kernel: separate R, and R = Y in place
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pwd")
+    monkeypatch.setenv("OX_PWD_CFG", cfg)
+    kc = int(cfg.split(":")[2])
+    r = np.random.default_rng(4400 + PWD_CFGS.index(cfg))
+    N, Cin, H, W, M = 3, 64 if kc == 64 else 96, 6, 8, 140
+    X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+    Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
+    b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+    Rr = synth.round_to(r.standard_normal((N, M, H, W)), "bf16")
+    ref = oracle.conv2d(X, Wt, b, act="relu", residual=Rr)
+    for in_place in (False, True):
+        say("pwd residual", cfg, in_place)
+        Y = run_conv_res(ox, X, Wt, b, Rr, "bf16", (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu",
+                         in_place=in_place)
+        assert_close(host64(Y), ref, "bf16", "pwd residual %s %s" % (cfg, in_place))
+
+
 @pytest.mark.parametrize("fp", ["1", "2"])
 @pytest.mark.parametrize("plan", ["1:32", "1:64", "2:32", "2:64"])
 def test_pw_each_config(ox, plan, fp, monkeypatch):
