@@ -29,7 +29,8 @@ EXPORTS = ("ox_matmul_batched", "ox_gemm_fused", "ox_conv2d_fused", "ox_conv2d_i
            "ox_last_error", "ox_version", "ox_conv2d_workspace_bytes", "ox_conv2d_fused_ws",
            "ox_conv2d_fused_res", "ox_batchnorm_act", "ox_maxpool2d", "ox_global_avgpool",
            "ox_int8_prepare_ex", "ox_dynamic_quantize_workspace_bytes", "ox_dynamic_quantize_linear",
-           "ox_matmul_nbits", "ox_gemm_workspace_bytes", "ox_gemm_fused_ws")
+           "ox_matmul_nbits", "ox_gemm_workspace_bytes", "ox_gemm_fused_ws",
+           "ox_static_scratch_bytes", "ox_conv2d_fused_static")
 
 
 class OxError(RuntimeError):
@@ -64,6 +65,8 @@ def _load():
         "ox_conv2d_packed_weights_bytes": (C.c_size_t, [I, P]),
         "ox_conv2d_workspace_bytes": (C.c_size_t, [I, P]),
         "ox_conv2d_fused_ws": (I, [I, P, P, P, I, P, I, P, P, C.c_size_t, P]),
+        "ox_conv2d_fused_static": (I, [I, P, P, P, I, P, I, P, P]),
+        "ox_static_scratch_bytes": (C.c_size_t, []),
         "ox_conv2d_fused_res": (I, [I, P, P, P, P, P, I, P, P, C.c_size_t, P]),
         "ox_batchnorm_act": (I, [I, I64, I64, I64, P, P, P, P, P, F, I, P, P]),
         "ox_maxpool2d": (I, [I, P, P, P, P]),
@@ -376,6 +379,32 @@ def ox_conv2d_fused_packed(X, Wp, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), d
         _check(lib.ox_conv2d_fused_packed(_dtype_code(X), C.byref(d), _ptr(X), _ptr(Wp), _ptr(bias),
                                           ACT[act], _ptr(Y), _stream(stream)))
     return Y
+
+
+def ox_conv2d_fused_static(X, W, bias=None, stride=(1, 1), pads=(0, 0, 0, 0), dilation=(1, 1), group=1,
+                           act="none", Y=None, stream=None, packed=False, M=None):
+    """ox_conv2d_fused_ws with the library's static scratch array in place of a
+    workspace (allocates nothing itself; Y must be given).  packed: W is
+    packed by ox_conv2d_pack_weights (then M names the output channels)."""
+    for t, n in ((X, "X"), (W, "W"), (bias, "bias"), (Y, "Y")):
+        _dense(t, n)
+    if Y is None:
+        raise ValueError("ox_conv2d_fused_static: Y must be given")
+    N, Cin, H, Wd = X.shape
+    if packed:
+        M = Y.shape[1] if M is None else M
+        kH = kW = 3
+    else:
+        M, _, kH, kW = W.shape
+    d = conv_desc(N, Cin, H, Wd, M, kH, kW, stride, pads, dilation, group)
+    _check(lib.ox_conv2d_fused_static(_dtype_code(X), C.byref(d), _ptr(X), _ptr(W), int(bool(packed)),
+                                      _ptr(bias), ACT[act], _ptr(Y), _stream(stream)))
+    return Y
+
+
+def ox_static_scratch_bytes():
+    """Bytes of the static scratch array behind ox_conv2d_fused_static."""
+    return int(lib.ox_static_scratch_bytes())
 
 
 def ox_conv2d_workspace_bytes(dtype, N, Cin, H, W, M, kH, kW, stride=(1, 1), pads=(0, 0, 0, 0),

@@ -299,8 +299,11 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
 
 }  // namespace
 
-// The stream-aware body of both convolution entry points.
-static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& a, void* stream) {
+// The stream-aware body of the convolution entry points.  static_ws: the
+// workspace is the library's static scratch array (a plan needing more is
+// refused as unsupported, not as a caller error).
+static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& a, void* stream,
+                               bool static_ws = false) {
   const Force f = read_force();
   int kind;
   ox_status st = select_conv(fn, d, a, f, &kind);
@@ -314,6 +317,9 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
   }
   if (a.ws) {
     const size_t need = kind == KIND_PW ? conv_pw_ws_bytes(a) : kind == KIND_PATCH ? conv_patch_ws_bytes(a) : 0;
+    if (need > a.ws_bytes && static_ws)
+      return fail(OX_ERR_UNSUPPORTED, "%s: this geometry's split-K plan needs %zu bytes of scratch, more than "
+                  "the %zu of the static scratch array", fn, need, a.ws_bytes);
     if (need > a.ws_bytes)
       return fail(OX_ERR_INVALID_ARG, "%s: workspace_bytes=%zu < %zu that this geometry needs", fn,
                   a.ws_bytes, need);
@@ -664,7 +670,7 @@ size_t ox_conv2d_workspace_bytes(ox_dtype t, const ox_conv_desc* d) {
 static ox_status conv_fused_ws_res(const char* fn, ox_dtype t, const ox_conv_desc* d, const void* X,
                                    const void* W, int w_packed, const void* bias, const void* R,
                                    ox_act act, void* Y, void* workspace, size_t workspace_bytes,
-                                   void* stream) {
+                                   void* stream, bool static_ws = false) {
   ox_status st = check_float_dt(fn, t);
   if (st) return st;
   st = check_act(fn, act);
@@ -687,7 +693,33 @@ static ox_status conv_fused_ws_res(const char* fn, ox_dtype t, const ox_conv_des
   a.ws = workspace;
   a.ws_bytes = workspace ? workspace_bytes : 0;
   a.res = R;
-  return conv_dispatch(fn, d, a, stream);
+  if (static_ws) {
+    // the static array's address on this device, only now that every
+    // argument has passed (a refused call makes no HIP call at all)
+    const Force f = read_force();
+    int kind;
+    st = select_conv(fn, d, a, f, &kind);
+    if (st) return st;
+    const size_t need = kind == KIND_PW ? conv_pw_ws_bytes(a) : kind == KIND_PATCH ? conv_patch_ws_bytes(a) : 0;
+    if (need > workspace_bytes)
+      return fail(OX_ERR_UNSUPPORTED, "%s: this geometry's split-K plan needs %zu bytes of scratch, more "
+                  "than the %zu of the static scratch array", fn, need, workspace_bytes);
+    void* p = nullptr;
+    const int rc = static_scratch(&p);
+    if (rc) return fail(OX_ERR_HIP, "%s: looking up the static scratch array failed (hip error %d)", fn, rc);
+    a.ws = p;
+  }
+  return conv_dispatch(fn, d, a, stream, static_ws);
+}
+
+size_t ox_static_scratch_bytes(void) { return static_scratch_bytes(); }
+
+ox_status ox_conv2d_fused_static(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                                 int w_packed, const void* bias, ox_act act, void* Y, void* stream) {
+  // a non-null stand-in until the arguments are checked; replaced by the
+  // device address of the static array before anything is enqueued
+  return conv_fused_ws_res("ox_conv2d_fused_static", t, d, X, W, w_packed, bias, nullptr, act, Y,
+                           (void*)(uintptr_t)256, static_scratch_bytes(), stream, true);
 }
 
 ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,

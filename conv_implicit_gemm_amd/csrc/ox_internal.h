@@ -173,6 +173,12 @@ struct PwdPlan {
   int lds;                // bytes of LDS
 };
 
+// The static device scratch array (k_static_scratch.hip): its size, and its
+// address on the current device (looked up once per device; returns a
+// hipError_t, 0 on success).
+size_t static_scratch_bytes();
+int static_scratch(void** ptr);
+
 // Scratch bytes the plan chosen for `a` needs (0: no split-K).  Split-K is
 // only planned when a.ws is non-null.
 size_t conv_pw_ws_bytes(const ConvArgs& a);

@@ -186,6 +186,24 @@ ox_status ox_conv2d_fused_ws(ox_dtype t, const ox_conv_desc* d, const void* X, c
                              int w_packed, const void* bias, ox_act act, void* Y, void* workspace,
                              size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * ox_conv2d_fused_ws with the scratch taken from a device array inside the
+ * library instead of a caller workspace.  Same operation, arguments (minus
+ * the workspace) and errors as ox_conv2d_fused_ws; no hipMalloc, hipFree or
+ * other allocation, here or in the kernels.
+ * The array holds ox_static_scratch_bytes() bytes (32 MiB) on every GPU the
+ * library runs on, for the life of the process; its address on a device is
+ * looked up on the first call made with that device current.  A geometry
+ * whose split-K plan needs more scratch than that is refused with
+ * OX_ERR_UNSUPPORTED before anything is enqueued (ox_conv2d_workspace_bytes
+ * gives the need).  All calls on one GPU share its array, which keeps the last
+ * call's partials: calls that overlap on one GPU (several streams or host
+ * threads) race on it and must be ordered by the caller. */
+size_t ox_static_scratch_bytes(void);
+ox_status ox_conv2d_fused_static(ox_dtype t, const ox_conv_desc* d, const void* X, const void* W,
+                                 int w_packed, const void* bias, ox_act act, void* Y, void* stream);
+
 /* Conv + bias + residual + activation, fused:
  *   Y[n,m,oh,ow] = act((conv(X, W)[n,m,oh,ow] + bias[m]) + R[n,m,oh,ow])
  * the single "convolution + residual + bias + relu" operation that the

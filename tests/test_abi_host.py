@@ -470,3 +470,22 @@ def test_packed_layout_only_where_a_packed_kernel_exists(ox):
     d = desc(ox, Cin=64, M=8)
     st = raw(ox).ox_conv2d_fused_packed(ox.OX_F32, C.byref(d), FAKE, FAKE, None, 0, FAKE, None)
     assert st == 3 and "packed" in ox.ox_last_error()
+
+
+def test_static_scratch_entry_point_refuses_oversized_plans(ox, monkeypatch):
+    # ox_conv2d_fused_static: a split-K plan needing more scratch than the
+    # static array is refused as unsupported before any HIP call (forced
+    # here with many slices on a long-K 1x1), and argument errors come first
+    L = raw(ox)
+    assert ox.ox_static_scratch_bytes() == 32 << 20
+    monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
+    monkeypatch.setenv("OX_PW_SPLITS", "64")
+    need = ox.ox_conv2d_workspace_bytes("bf16", 32, 2048, 7, 7, 512, 1, 1)
+    assert need > ox.ox_static_scratch_bytes()
+    d = ox.conv_desc(32, 2048, 7, 7, 512, 1, 1)
+    st = L.ox_conv2d_fused_static(ox.OX_BF16, C.byref(d), FAKE, FAKE, 0, None, 0, FAKE, None)
+    assert st == 3 and "static scratch" in ox.ox_last_error() and str(need) in ox.ox_last_error()
+    st = L.ox_conv2d_fused_static(ox.OX_BF16, C.byref(d), None, FAKE, 0, None, 0, FAKE, None)
+    assert st == 1 and "X is NULL" in ox.ox_last_error()
+    st = L.ox_conv2d_fused_static(ox.OX_BF16, C.byref(d), FAKE, FAKE, 2, None, 0, FAKE, None)
+    assert st == 1 and "w_packed" in ox.ox_last_error()
