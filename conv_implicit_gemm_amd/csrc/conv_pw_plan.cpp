@@ -14,6 +14,7 @@ int launch_pw_2_32(const ConvArgs& a, const PwPlan& p, void* s);
 int launch_pw_2_64(const ConvArgs& a, const PwPlan& p, void* s);
 int launch_pwd_128_64_64(const ConvArgs& a, const PwdPlan& p, void* s);
 int launch_pwd_128_64_32(const ConvArgs& a, const PwdPlan& p, void* s);
+int launch_pwd_64_64_64(const ConvArgs& a, const PwdPlan& p, void* s);
 int launch_pwd_64_128_64(const ConvArgs& a, const PwdPlan& p, void* s);
 int launch_pwd_64_128_32(const ConvArgs& a, const PwdPlan& p, void* s);
 int launch_pwd_64_256_64(const ConvArgs& a, const PwdPlan& p, void* s);
@@ -156,6 +157,7 @@ struct PwdCfg {
 };
 const PwdCfg kPwdCfgs[] = {
     {128, 64, 64, 3, 4, launch_pwd_128_64_64}, {128, 64, 32, 4, 4, launch_pwd_128_64_32},
+    {64, 64, 64, 4, 2, launch_pwd_64_64_64},
     {64, 128, 64, 3, 2, launch_pwd_64_128_64}, {64, 128, 32, 4, 2, launch_pwd_64_128_32},
     {64, 256, 64, 2, 1, launch_pwd_64_256_64}, {64, 256, 32, 3, 1, launch_pwd_64_256_32},
 };
@@ -165,34 +167,80 @@ int pwd_lds(const PwdCfg& c, bool res) {
   return c.S * slot + (res || stage <= slot ? 0 : stage);
 }
 
-bool aligned16p(const void* p) { return ((uintptr_t)p & 15) == 0; }
+bool aligned_to(const void* p, uintptr_t n) { return ((uintptr_t)p % n) == 0; }
 
-// The configuration for a shape: output channels per block from M (the
-// whole of M up to 256, so that X is read once per pixel block where it
-// can be), 64-channel stages where C allows, 128-pixel tiles for 64-channel
-// blocks.  OX_PWD_CFG=BP:BC:KC pins one (an entry of the table above).
+const PwdCfg* find_cfg(int BP, int BC, int KC) {
+  for (const PwdCfg& c : kPwdCfgs)
+    if (c.BP == BP && c.BC == BC && c.KC == KC) return &c;
+  return nullptr;
+}
+
+// Blocks of the persistent grid for a configuration (ranges of 64 or 128
+// pixels x channel blocks), and the range split: pixel ranges are k whole
+// units of 128 pixels -- 64 where 128 would leave fewer than 256 blocks --
+// with k the least that fits the grid (at most as many blocks as fit the
+// chip at once), so that every block gets the same work.  OX_PWD_GRID caps
+// the block count (a test of ranges with several tiles).
+void split_ranges(const ConvArgs& a, int64_t Q, PwdPlan* p) {
+  const int per_cu = std::max(1, std::min(2, kLdsMax / p->lds));
+  int64_t cap = (int64_t)kCUs * per_cu;
+  if (const char* g = getenv("OX_PWD_GRID")) cap = std::max(1, atoi(g));
+  const int64_t units128 = (Q + 127) / 128;
+  const int unit = units128 * p->nmb >= kCUs || cap < kCUs ? 128 : 64;
+  const int64_t units = (Q + unit - 1) / unit;
+  const int64_t per_range_cap = std::max<int64_t>(1, cap / p->nmb);
+  const int64_t k = (units + per_range_cap - 1) / per_range_cap;
+  p->span = (int)std::min<int64_t>(k * unit, (int64_t)1 << 30);
+  p->nranges = (int)((units + k - 1) / k);
+  p->grid = p->nranges * p->nmb;
+  (void)a;
+}
+
+// The configuration for a shape.  Output channels per block: the largest of
+// 256 / 128 / 64 (not beyond what M needs) that still gives 256 blocks --
+// a wide block reads each pixel once, a narrow one gives small layers
+// enough blocks without splitting K.  64-channel stages where C allows;
+// 128-pixel tiles for 64-channel blocks when the pixels give 256 of them.
+// Pixel pieces of 16 bytes when H*W % 8 == 0 (and X is 16-byte aligned),
+// else 4 bytes when H*W is even.  OX_PWD_CFG=BP:BC:KC pins a configuration.
 bool pwd_plan(const ConvArgs& a, PwdPlan* out) {
   if (!geometry(a)) return false;
   const int64_t HW = (int64_t)a.H * a.W;
   const int64_t Q = (int64_t)a.N * HW;
-  if (HW % 8 != 0 || Q == 0) return false;
-  if (!aligned16p(a.X) || !aligned16p(a.Y) || !aligned16p(a.Wt) || (a.res && !aligned16p(a.res)))
-    return false;
+  if (Q == 0 || !aligned_to(a.Wt, 16)) return false;
+  int PB;
+  if (HW % 8 == 0 && aligned_to(a.X, 16)) PB = 16;
+  else if (HW % 2 == 0 && aligned_to(a.X, 4)) PB = 4;
+  else return false;
+  if (a.res && (PB != 16 || !aligned_to(a.Y, 16) || !aligned_to(a.res, 16))) return false;
   if ((int64_t)a.N * a.C * HW * 2 >= ((int64_t)1 << 30) || (int64_t)a.M * a.C * 2 >= ((int64_t)1 << 30) ||
       (int64_t)a.N * a.M * HW >= ((int64_t)1 << 31))
     return false;
-  int BP, BC, KC;
-  const char* e = getenv("OX_PWD_CFG");
-  if (e && *e) {
-    if (sscanf(e, "%d:%d:%d", &BP, &BC, &KC) != 3) return false;
-  } else {
-    BC = a.M <= 64 ? 64 : a.M <= 128 ? 128 : 256;
-    KC = a.C % 64 == 0 ? 64 : 32;
-    BP = BC == 64 ? 128 : 64;
-  }
+  int V = 8;
+  while (V > 1 && (HW % V || !aligned_to(a.Y, 2 * V))) V >>= 1;
+  const int KC = a.C % 64 == 0 ? 64 : 32;
   const PwdCfg* cfg = nullptr;
-  for (const PwdCfg& c : kPwdCfgs)
-    if (c.BP == BP && c.BC == BC && c.KC == KC) cfg = &c;
+  const char* e = getenv("OX_PWD_CFG");
+  int BP = 0, BC = 0, KCp = 0;
+  if (e && *e) {
+    if (sscanf(e, "%d:%d:%d", &BP, &BC, &KCp) != 3) return false;
+    cfg = find_cfg(BP, BC, KCp);
+  } else {
+    const int mcap = a.M <= 64 ? 64 : a.M <= 128 ? 128 : 256;
+    for (int bc = mcap; bc >= 64 && !cfg; bc /= 2) {
+      const PwdCfg* c = nullptr;
+      if (bc == 64) {
+        const bool wide = (Q + 127) / 128 * ((a.M + 63) / 64) >= kCUs;
+        c = find_cfg(wide ? 128 : 64, 64, KC);
+        if (!c) c = find_cfg(128, 64, KC);
+      } else {
+        c = find_cfg(64, bc, KC);
+      }
+      if (!c) continue;
+      const int64_t nmb = (a.M + bc - 1) / bc;
+      if ((Q + 63) / 64 * nmb >= kCUs || bc == 64) cfg = c;
+    }
+  }
   if (!cfg || a.C % cfg->KC != 0) return false;
   PwdPlan p;
   p.BP = cfg->BP;
@@ -200,27 +248,14 @@ bool pwd_plan(const ConvArgs& a, PwdPlan* out) {
   p.KC = cfg->KC;
   p.S = cfg->S;
   p.WP = cfg->WP;
+  p.PB = PB;
+  p.V = V;
   p.nmb = (a.M + p.BC - 1) / p.BC;
   p.Q = (int)Q;
   p.lds = pwd_lds(*cfg, a.res != nullptr);
   if (p.lds > kLdsMax) return false;
-  // persistent grid of at most as many blocks as fit the chip at once
-  // (LDS-bound, at most two per CU).  Pixel ranges are k whole units of 128
-  // pixels -- 64 where 128 would leave fewer than 256 blocks -- with k the
-  // least that fits the grid, so that every block gets the same work.
-  // OX_PWD_GRID caps the block count (a test of ranges with several tiles).
-  const int per_cu = std::max(1, std::min(2, kLdsMax / p.lds));
-  int64_t cap = (int64_t)kCUs * per_cu;
-  if (const char* g = getenv("OX_PWD_GRID")) cap = std::max(1, atoi(g));
-  const int64_t units128 = (Q + 127) / 128;
-  const int unit = units128 * p.nmb >= kCUs || cap < kCUs ? 128 : 64;
-  const int64_t units = (Q + unit - 1) / unit;
-  const int64_t per_range_cap = std::max<int64_t>(1, cap / p.nmb);
-  const int64_t k = (units + per_range_cap - 1) / per_range_cap;
-  p.span = (int)std::min<int64_t>(k * unit, (int64_t)1 << 30);
-  p.nranges = (int)((units + k - 1) / k);
+  split_ranges(a, Q, &p);
   if ((int64_t)p.nranges * p.nmb >= ((int64_t)1 << 31)) return false;
-  p.grid = p.nranges * p.nmb;
   p.hw = make_fastdiv((uint32_t)HW);
   p.x_bytes = (uint32_t)((int64_t)a.N * a.C * HW * 2);
   p.w_bytes = (uint32_t)((int64_t)a.M * a.C * 2);
@@ -250,8 +285,8 @@ int launch_conv_pwd(const ConvArgs& a, void* stream) {
 const char* conv_pwd_describe(const ConvArgs& a, char* buf, int cap) {
   PwdPlan p;
   if (!pwd_plan(a, &p)) return "";
-  snprintf(buf, cap, "BP=%d BC=%d KC=%d S=%d WP=%d ranges=%d grid=%d lds=%d", p.BP, p.BC, p.KC, p.S, p.WP,
-           p.nranges, p.grid, p.lds);
+  snprintf(buf, cap, "BP=%d BC=%d KC=%d S=%d WP=%d PB=%d V=%d ranges=%d span=%d grid=%d lds=%d", p.BP, p.BC,
+           p.KC, p.S, p.WP, p.PB, p.V, p.nranges, p.span, p.grid, p.lds);
   return buf;
 }
 

@@ -3,8 +3,10 @@
 //
 // Y[n, m, p] = act(bias[m] + sum_c W[m, c] * X[n, c, p] (+ R[n, m, p])) is a
 // GEMM over the flattened pixels of the batch, q = n*HW + p (the 1x1 fast
-// path: a GEMM straight on the input, with no im2col).  HW % 8 == 0, so an
-// 8-pixel piece never straddles two images and a tile may span images.
+// path: a GEMM straight on the input, with no im2col).  The pixel tile is
+// gathered in pieces of PB bytes (PB = 16: 8 pixels, when HW % 8 == 0; PB =
+// 4: 2 pixels, when HW is even), each lane fetching its own piece, so that a
+// piece never straddles two images and a tile may span images.
 //
 // Work split.  The grid is persistent: block (r, mb) owns output channels
 // [mb*BC, mb*BC + BC) over pixel range r, one of nranges equal contiguous
@@ -74,7 +76,7 @@ __device__ __forceinline__ void swap_halves(uint32_t& a, uint32_t& b) {
   b = r[1];
 }
 
-template <int BP, int BC, int KC, int S, int WP, bool RES>
+template <int BP, int BC, int KC, int S, int WP, int PB, bool RES>
 __global__ __launch_bounds__(kThreads, 2) void conv1x1_dma(const ConvArgs a, const PwdPlan pl) {
   constexpr int WC = 4 / WP;
   constexpr int TP = BP / WP, TC = BC / WC;   // wave tile: pixels x channels
@@ -84,12 +86,16 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_dma(const ConvArgs a, con
   constexpr int WROW = KC * 2;                // bytes per staged weight row
   constexpr int WB = BC * WROW;               // weight tile bytes per stage
   constexpr int SB = XB + WB;                 // stage bytes
-  constexpr int IX = XB / 4096, IW = WB / 4096;   // DMA instructions per wave per stage
+  constexpr int XI = 64 * PB;                 // bytes of one pixel DMA instruction
+  constexpr int IX = XB / (4 * XI), IW = WB / 4096;   // DMA instructions per wave per stage
   constexpr int D = IX + IW;
   constexpr int XPR = BP / 8, WPR = KC / 8;   // 16-byte pieces per row
+  constexpr int SUB = 16 / PB;                // DMA pieces per 16-byte piece
   constexpr int NS = KC / 16;                 // k-steps per stage
   static_assert(WP * WC == 4 && FP >= 1 && FC >= 1, "four waves");
-  static_assert(XB % 4096 == 0 && WB % 4096 == 0, "whole DMA instructions per wave");
+  static_assert(XB % (4 * XI) == 0 && WB % 4096 == 0, "whole DMA instructions per wave");
+  static_assert(PB == 16 || PB == 4, "pixel DMA piece");
+  static_assert(!RES || PB == 16, "the residual epilogue takes 8-pixel runs");
   static_assert(BP == 64 || BP == 128, "pixel tile");
   static_assert(KC == 32 || KC == 64, "channel stage");
   static_assert(S >= 2 && S <= 4, "ring depth");
@@ -129,9 +135,12 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_dma(const ConvArgs a, con
     const int q0 = qb + t * BP, q1 = min(q0 + BP, qe);
 #pragma unroll
     for (int i = 0; i < IX; ++i) {
+      // LDS position e (in DMA pieces) of this lane: channel row r, 16-byte
+      // piece jp / SUB, part jp % SUB; it holds logical piece
+      // (jp / SUB) ^ swizzle of the row
       const int e = (wave * IX + i) * 64 + lane;
-      const int r = e / XPR, jp = e % XPR;
-      const int q = q0 + 8 * (jp ^ swz_x<BP>(r));
+      const int r = e / (XPR * SUB), jp = e % (XPR * SUB);
+      const int q = q0 + 8 * ((jp / SUB) ^ swz_x<BP>(r)) + (jp % SUB) * (PB / 2);
       if (q < q1) {
         const int n = fdiv(pl.hw, q);
         xo[i] = ((uint32_t)(n * C + r) * (uint32_t)HW + (uint32_t)(q - n * HW)) * 2u;
@@ -164,8 +173,10 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_dma(const ConvArgs a, con
   auto issue_next = [&]() {
     const uint32_t base = lds0 + (uint32_t)(is * SB);
 #pragma unroll
-    for (int i = 0; i < IX; ++i)
-      dma16(base + (uint32_t)((wave * IX + i) * 1024), xo[i] + (uint32_t)ik * xstep, xr);
+    for (int i = 0; i < IX; ++i) {
+      if constexpr (PB == 16) dma16(base + (uint32_t)((wave * IX + i) * XI), xo[i] + (uint32_t)ik * xstep, xr);
+      else dma4(base + (uint32_t)((wave * IX + i) * XI), xo[i] + (uint32_t)ik * xstep, xr);
+    }
 #pragma unroll
     for (int i = 0; i < IW; ++i)
       dma16(base + (uint32_t)(XB + (wave * IW + i) * 1024), wo[i] + (uint32_t)ik * wstep, wr);
@@ -336,17 +347,37 @@ __global__ __launch_bounds__(kThreads, 2) void conv1x1_dma(const ConvArgs a, con
       }
     });
     lds_barrier();
-    constexpr int ITEMS = BC * XPR;
+    // runs of V pixels of one channel row (HW % V == 0: a run never
+    // straddles two images), consecutive lanes on consecutive runs
+    auto store_runs = [&](auto Vc) {
+      constexpr int V = decltype(Vc)::value, RPR = BP / V;
+      constexpr int ITEMS = BC * RPR;
 #pragma unroll 2
-    for (int it = tid; it < ITEMS; it += kThreads) {
-      const int row = it / XPR, pc = it - (it / XPR) * XPR;
-      const int m = m0 + row, q = q0 + 8 * pc;
-      if (m < M && q < q1) {
-        const int n = fdiv(pl.hw, q);
-        const char* src = E + row * EP + pc * 16;
-        const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 8);
-        *(u32x4_t*)(Y + ((int64_t)n * M + m) * HW + (q - n * HW)) = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+      for (int it = tid; it < ITEMS; it += kThreads) {
+        const int row = it / RPR, pc = it - (it / RPR) * RPR;
+        const int m = m0 + row, q = q0 + V * pc;
+        if (m < M && q < q1) {
+          const int n = fdiv(pl.hw, q);
+          const char* src = E + row * EP + pc * V * 2;
+          uint16_t* dst = Y + ((int64_t)n * M + m) * HW + (q - n * HW);
+          if constexpr (V == 8) {
+            const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 8);
+            *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
+          } else if constexpr (V == 4) {
+            *(u32x2_t*)dst = *(const u32x2_t*)src;
+          } else if constexpr (V == 2) {
+            *(uint32_t*)dst = *(const uint32_t*)src;
+          } else {
+            *dst = *(const uint16_t*)src;
+          }
+        }
       }
+    };
+    switch (pl.V) {
+      case 8: store_runs(std::integral_constant<int, 8>{}); break;
+      case 4: store_runs(std::integral_constant<int, 4>{}); break;
+      case 2: store_runs(std::integral_constant<int, 2>{}); break;
+      default: store_runs(std::integral_constant<int, 1>{}); break;
     }
     // (the next stage's wait includes lgkmcnt(0) before its barrier: the
     // staging reads are done before any DMA reuses the slot)
@@ -389,13 +420,13 @@ constexpr int lds_bytes() {
 template <int BP, int BC, int KC, int S, int WP>
 int launch(const ConvArgs& a, const PwdPlan& p, hipStream_t s) {
   dim3 grid(p.grid, 1, 1);
-  if (a.res) {
-    constexpr int L = lds_bytes<BP, BC, KC, S, true>();
-    hipLaunchKernelGGL((conv1x1_dma<BP, BC, KC, S, WP, true>), grid, dim3(kThreads), L, s, a, p);
-  } else {
-    constexpr int L = lds_bytes<BP, BC, KC, S, false>();
-    hipLaunchKernelGGL((conv1x1_dma<BP, BC, KC, S, WP, false>), grid, dim3(kThreads), L, s, a, p);
-  }
+  constexpr int LR = lds_bytes<BP, BC, KC, S, true>(), L = lds_bytes<BP, BC, KC, S, false>();
+  if (p.PB == 4)   // (the planner gives a residual only 16-byte pieces)
+    hipLaunchKernelGGL((conv1x1_dma<BP, BC, KC, S, WP, 4, false>), grid, dim3(kThreads), L, s, a, p);
+  else if (a.res)
+    hipLaunchKernelGGL((conv1x1_dma<BP, BC, KC, S, WP, 16, true>), grid, dim3(kThreads), LR, s, a, p);
+  else
+    hipLaunchKernelGGL((conv1x1_dma<BP, BC, KC, S, WP, 16, false>), grid, dim3(kThreads), L, s, a, p);
   return (int)hipGetLastError();
 }
 

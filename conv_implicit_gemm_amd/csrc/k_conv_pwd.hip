@@ -11,6 +11,9 @@ int launch_pwd_128_64_64(const ConvArgs& a, const PwdPlan& p, void* s) {
 int launch_pwd_128_64_32(const ConvArgs& a, const PwdPlan& p, void* s) {
   return pwd::launch<128, 64, 32, 4, 4>(a, p, (hipStream_t)s);
 }
+int launch_pwd_64_64_64(const ConvArgs& a, const PwdPlan& p, void* s) {
+  return pwd::launch<64, 64, 64, 4, 2>(a, p, (hipStream_t)s);
+}
 int launch_pwd_64_128_64(const ConvArgs& a, const PwdPlan& p, void* s) {
   return pwd::launch<64, 128, 64, 3, 2>(a, p, (hipStream_t)s);
 }

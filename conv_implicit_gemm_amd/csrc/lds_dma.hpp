@@ -65,6 +65,18 @@ __device__ __forceinline__ void dma16(uint32_t lds, uint32_t voff, u32x4_t rsrc)
       : "memory");
 }
 
+// 4 bytes per lane: global [rsrc + voff] -> LDS [lds + 4*lane] (packed:
+// one wave instruction fills 256 contiguous bytes).  The 2-byte form does not
+// pack (each lane still fills a dword), so no narrower form is offered.
+__device__ __forceinline__ void dma4(uint32_t lds, uint32_t voff, u32x4_t rsrc) {
+  asm volatile(
+      "s_nop 0\n\t"
+      "buffer_load_dword %0, %1, 0 offen lds"
+      :
+      : "v"(voff), "s"(rsrc), "{m0}"(lds)
+      : "memory");
+}
+
 // Wait until at most N of this wave's vector-memory instructions are
 // outstanding and all its LDS reads have returned, then the workgroup
 // barrier: every wave's DMA of the stage is then in LDS and no wave still

@@ -155,7 +155,7 @@ struct PwPlan {
   float* ws;  // split-K partials (splits * tiles * BM * BN floats), else null
 };
 
-// Plan of the DMA-staged pointwise kernel (bf16 1x1 with H*W % 8 == 0):
+// Plan of the DMA-staged pointwise kernel (bf16 1x1 with H*W even):
 // tile BP pixels x BC output channels, KC input channels per stage, S ring
 // stages, WP waves along the pixels (4/WP along the channels).  The grid is
 // persistent: nranges x nmb blocks, block (r, mb) computes channel block mb
@@ -163,6 +163,8 @@ struct PwPlan {
 // pixels with unit = 64 or 128 -- in tiles of BP pixels.
 struct PwdPlan {
   int BP, BC, KC, S, WP;
+  int PB;                 // bytes per pixel DMA piece: 16 (H*W % 8 == 0) or 4 (H*W even)
+  int V;                  // pixels per output store (8, 4, 2 or 1; H*W % V == 0)
   int nmb;                // channel blocks
   int nranges;            // pixel ranges
   int grid;               // nranges * nmb blocks
@@ -224,7 +226,8 @@ bool conv_smallc_applicable(const ConvArgs& a);
 int launch_conv_smallc(const ConvArgs& a, void* stream);
 const char* conv_smallc_describe(const ConvArgs& a, char* buf, int cap);
 // DMA-staged pointwise kernel (bf16, 1x1, stride 1, unpadded, group 1,
-// C % 32 == 0, H*W % 8 == 0, 16-byte aligned X, W, Y and residual)
+// C % 32 == 0, H*W even; X aligned to its DMA piece, W 16-byte aligned; a
+// residual needs H*W % 8 == 0 and 16-byte aligned X, Y and R)
 bool conv_pwd_applicable(const ConvArgs& a);
 int launch_conv_pwd(const ConvArgs& a, void* stream);
 const char* conv_pwd_describe(const ConvArgs& a, char* buf, int cap);

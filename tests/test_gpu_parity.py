@@ -388,7 +388,7 @@ def test_pw_conv_sweep_bf16(ox, monkeypatch):
         assert_close(host64(Y), oracle.conv2d(X, Wt, b, act=act), "bf16", "pw %d" % ci)
 
 
-PWD_CFGS = ["128:64:64", "128:64:32", "64:128:64", "64:128:32", "64:256:64", "64:256:32"]
+PWD_CFGS = ["128:64:64", "128:64:32", "64:64:64", "64:128:64", "64:128:32", "64:256:64", "64:256:32"]
 
 
 @pytest.mark.parametrize("cfg", PWD_CFGS)
@@ -402,8 +402,11 @@ def test_pwd_each_config_integer_exact(ox, cfg, monkeypatch):
     monkeypatch.setenv("OX_PWD_CFG", cfg)
     kc = int(cfg.split(":")[2])
     r = np.random.default_rng(4100 + PWD_CFGS.index(cfg))
+    # planes that are multiples of 8 pixels (16-byte pixel pieces) and even
+    # planes that are not (4-byte pieces: 14x14, 6x7, 5x2, 3x6)
     cases = [(2, 128, 8, 8, 70), (3, 64, 4, 6, 150), (1, 256, 16, 16, 200), (5, 192, 2, 4, 33),
-             (2, 96, 6, 12, 256), (1, 32, 8, 1, 300)]
+             (2, 96, 6, 12, 256), (1, 32, 8, 1, 300), (2, 128, 14, 14, 90), (3, 64, 6, 7, 130),
+             (4, 192, 5, 2, 64), (2, 96, 3, 6, 200)]
     ran = 0
     for ci, (N, Cin, H, W, M) in enumerate(cases):
         if Cin % kc:
@@ -420,7 +423,7 @@ def test_pwd_each_config_integer_exact(ox, cfg, monkeypatch):
         else:
             assert np.array_equal(host64(Y), ref), "pwd %s case %d" % (cfg, ci)
         ran += 1
-    assert ran >= 3
+    assert ran >= 5
 
 
 @pytest.mark.parametrize("grid", ["1", "5", "37"])
@@ -450,7 +453,8 @@ def test_pwd_sweep_bf16(ox, monkeypatch):
     for ci in range(30):
         N = int(r.integers(1, 5))
         Cin = int(r.choice([32, 64, 96, 128, 256, 384, 512]))
-        H, W = int(r.integers(1, 20)), 8 * int(r.integers(1, 4))
+        H = int(r.integers(1, 20))
+        W = 8 * int(r.integers(1, 4)) if ci % 2 else 2 * int(r.integers(1, 12))   # 16- or 4-byte pieces
         M = int(r.integers(1, 600))
         act = str(r.choice(["none", "relu", "relu6", "gelu"]))
         X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
@@ -477,7 +481,9 @@ def test_pwd_not_taken_for_unaligned_or_odd_planes(ox, monkeypatch):
     monkeypatch.delenv("OX_FORCE_KERNEL")
     X8 = synth.round_to(r.standard_normal((2, 64, 8, 8)), "bf16")
     ref = oracle.conv2d(X8, Wt, b, act="relu")
-    for xoff, yoff in ((1, 0), (0, 4), (8, 8)):
+    # X one element off (no DMA piece fits: another kernel), two elements off
+    # (4-byte pieces), Y off alignment (narrower stores), both 16-byte aligned
+    for xoff, yoff in ((1, 0), (2, 0), (0, 4), (0, 1), (8, 8)):
         say("pwd alignment", xoff, yoff)
         Xd = misaligned(dev(X8, "bf16"), xoff)
         Y = misaligned(nan_like((2, 96, 8, 8), "bf16"), yoff)
