@@ -220,10 +220,10 @@ ConvArgs conv_args(int dt, const ox_conv_desc* d, int64_t Ho, int64_t Wo, const 
 }
 
 enum ConvKind { KIND_IGEMM = 0, KIND_1X1 = 1, KIND_DW = 2, KIND_PATCH = 3, KIND_PW = 4, KIND_SMALLC = 5,
-                KIND_PWD = 6 };
+                KIND_PWD = 6, KIND_DWR = 7 };
 
 const char* kind_name(int k) {
-  static const char* n[] = {"igemm", "1x1", "dw", "patch", "pw", "smallc", "pwd"};
+  static const char* n[] = {"igemm", "1x1", "dw", "patch", "pw", "smallc", "pwd", "dwr"};
   return n[k];
 }
 
@@ -247,7 +247,12 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
   const bool is_1x1 = d->kH == 1 && d->kW == 1 && d->s_h == 1 && d->s_w == 1 && d->p_t == 0 &&
                       d->p_l == 0 && d->p_b == 0 && d->p_r == 0 && d->group == 1;
   if (f.variant) {
-    if (!strcmp(f.variant, "dw")) {
+    if (!strcmp(f.variant, "dwr")) {
+      if (!is_dw || !depthwise_rows_applicable(a))
+        return fail(OX_ERR_UNSUPPORTED, "%s: forced 'dwr' needs a 3x3 depthwise conv with pads 1, stride 1 or 2, "
+                    "fp32 or bf16, an even W (bf16 or stride 2), Wo <= 512 and 4-byte aligned X", fn);
+      *kind = KIND_DWR;
+    } else if (!strcmp(f.variant, "dw")) {
       if (!is_dw) return fail(OX_ERR_UNSUPPORTED, "%s: forced 'dw' but group != C or C != M", fn);
       if (!depthwise_fits(a))
         return fail(OX_ERR_UNSUPPORTED, "%s: forced 'dw' but the row band does not fit LDS", fn);
@@ -289,7 +294,8 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
     else *kind = KIND_IGEMM;
     return OX_OK;
   }
-  if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
+  if (is_dw && depthwise_rows_applicable(a)) *kind = KIND_DWR;
+  else if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
   else if (is_1x1) *kind = conv_pwd_applicable(a) ? KIND_PWD : conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
   else if (conv_patch_applicable(a)) *kind = KIND_PATCH;
   else if (conv_smallc_applicable(a)) *kind = KIND_SMALLC;
@@ -329,6 +335,7 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
     if (kind == KIND_PATCH) conv_patch_describe(a, plan, sizeof(plan));
     if (kind == KIND_PW) conv_pw_describe(a, plan, sizeof(plan));
     if (kind == KIND_PWD) conv_pwd_describe(a, plan, sizeof(plan));
+    if (kind == KIND_DWR) conv_depthwise_rows_describe(a, plan, sizeof(plan));
     if (kind == KIND_SMALLC) conv_smallc_describe(a, plan, sizeof(plan));
     fprintf(stderr, "[ox] %s dt=%d N=%d C=%d %dx%d M=%d k=%dx%d s=%d,%d g=%d act=%s -> %s%s%s %s\n",
             fn, a.dt, a.N, a.C, a.H, a.W, a.M, a.kH, a.kW, a.sh, a.sw, a.group, act_name(a.act),
@@ -338,6 +345,8 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
   int rc;
   if (kind == KIND_DW) {
     rc = launch_conv_depthwise(a, stream);
+  } else if (kind == KIND_DWR) {
+    rc = launch_conv_depthwise_rows(a, stream);
   } else if (kind == KIND_PATCH) {
     rc = launch_conv_patch(a, stream);
   } else if (kind == KIND_PW) {

@@ -218,6 +218,10 @@ int launch_conv_i8(const ConvArgs& a, int kind, int tile, void* stream);
 int launch_conv_depthwise(const ConvArgs& a, void* stream);
 // whether the depthwise kernel's LDS band fits this geometry (host only)
 bool depthwise_fits(const ConvArgs& a);
+// depthwise 3x3 with one row segment per lane (pads 1, stride 1 or 2, fp32 / bf16)
+bool depthwise_rows_applicable(const ConvArgs& a);
+int launch_conv_depthwise_rows(const ConvArgs& a, void* stream);
+const char* conv_depthwise_rows_describe(const ConvArgs& a, char* buf, int cap);
 // 3x3 bf16 convolution with an LDS-staged input patch (group 1, C % 32 == 0)
 bool conv_patch_geometry(const ConvArgs& a);      // dtype/shape conditions only
 bool conv_patch_applicable(const ConvArgs& a);

@@ -13,6 +13,7 @@ import pytest
 
 import oracle
 import synth
+from kernel_rules import dwr_applies
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -143,6 +144,9 @@ def test_variant_selection_sweep(ox, monkeypatch):
             assert name.startswith("patch/"), (name, C, M, H, W, s)
         if dt == "bf16" and g == 1 and C <= 4 and k > 1 and not (C == 1 and M == 1):
             assert name.startswith("smallc/"), (name, C, k, s)
+        if g == C and M == C and k == 3 and dt != "i8":
+            # depthwise 3x3, pads 1: the row-segment kernel where it applies
+            assert name.startswith("dwr/") == dwr_applies(dt, W, s), (name, dt, H, W, s)
     # pinned split-K counts, including more slices than chunks
     for splits in ("1", "2", "7", "64"):
         monkeypatch.setenv("OX_PW_SPLITS", splits)

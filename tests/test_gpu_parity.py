@@ -12,6 +12,7 @@ import pytest
 
 import oracle
 import synth
+from kernel_rules import dwr_applies
 from parity import assert_close
 
 torch = pytest.importorskip("torch")
@@ -312,8 +313,10 @@ def test_depthwise_sliding_strips(ox, geom, monkeypatch):
     b = synth.round_to(r.uniform(-0.5, 0.5, Cc), "bf16")
     ho, wo = ox.conv_out_hw(H, W, kH, kW, (s, s), pads, (1, 1))
     Y = misaligned(nan_like((N, Cc, ho, wo), "bf16"), yoff)
+    monkeypatch.setenv("OX_FORCE_KERNEL", "dw")
     ox.ox_conv2d_fused(dev(X, "bf16"), dev(Wt, "bf16"), dev(b, "bf16"), (s, s), pads, (1, 1), Cc, "relu6", Y=Y)
     torch.cuda.synchronize()
+    monkeypatch.delenv("OX_FORCE_KERNEL")
     assert_close(host64(Y), oracle.conv2d(X, Wt, b, (s, s), pads, (1, 1), Cc, "relu6"), "bf16", "dw slide")
     conv = synth.ConvLayer("q", N, Cc, H, W, Cc, kH, s, 0, Cc, "none", kW=kW, pads=pads)
     layer = synth.Int8Layer("q", "conv", 1, kH * kW, Cc, conv)
@@ -323,6 +326,7 @@ def test_depthwise_sliding_strips(ox, geom, monkeypatch):
     assert np.array_equal(int8_gpu(ox, layer, t, "i8"), y)
 
 
+@pytest.mark.parametrize("force", [None, "dw"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("geom", [
     (2, 20, 14, 14, (1, 1), 1),     # Wo = 14: rows alternate between aligned and unaligned strips
@@ -330,9 +334,13 @@ def test_depthwise_sliding_strips(ox, geom, monkeypatch):
     (2, 16, 28, 28, (2, 2), 3),     # output pointer 3 elements past an aligned one
     (1, 8, 9, 16, (1, 1), 2),
 ])
-def test_depthwise_output_alignment(ox, dtype, geom):
-    # strips of 4 outputs go out as one wide store only where they are full
-    # and aligned; every other strip element by element
+def test_depthwise_output_alignment(ox, force, dtype, geom, monkeypatch):
+    # the staged-band kernel (forced) stores strips of 4 outputs as one wide
+    # store only where they are full and aligned, every other strip element
+    # by element; the row kernel (chosen where it applies) stores a lane's
+    # segment whole only where Y is aligned to it
+    if force:
+        monkeypatch.setenv("OX_FORCE_KERNEL", force)
     N, Cc, H, W, s, yoff = geom
     say("depthwise alignment", geom, dtype)
     r = np.random.default_rng(H * 31 + yoff)
@@ -344,6 +352,84 @@ def test_depthwise_output_alignment(ox, dtype, geom):
     ox.ox_conv2d_fused(dev(X, dtype), dev(Wt, dtype), dev(b, dtype), s, (1, 1, 1, 1), (1, 1), Cc, "relu6", Y=Y)
     torch.cuda.synchronize()
     assert_close(host64(Y), oracle.conv2d(X, Wt, b, s, (1, 1, 1, 1), (1, 1), Cc, "relu6"), dtype, "dw align")
+
+
+DWR_CASES = [
+    # N, C, H, W, stride: one to nine bands per wave, ragged last bands (odd
+    # heights), rows of 1 to 64 lanes, odd output widths (stride 2), tiny
+    # planes, one band per wave at 64 lanes a row
+    (2, 8, 112, 112, 1), (1, 6, 112, 112, 2), (3, 16, 56, 56, 1), (2, 24, 56, 56, 2),
+    (4, 32, 28, 28, 1), (2, 48, 14, 14, 1), (3, 40, 14, 14, 2), (2, 64, 7, 8, 1),
+    (1, 5, 9, 10, 1), (2, 3, 13, 6, 2), (1, 2, 1, 2, 1), (2, 7, 3, 2, 2), (1, 300, 4, 4, 1),
+    (1, 2, 6, 512, 1), (1, 3, 900, 4, 1), (2, 5, 21, 40, 1),
+]
+# fp32 only: odd widths at stride 1 (lanes of one output each)
+DWR_F32_ODD = [(2, 12, 7, 7, 1), (1, 3, 5, 9, 1), (2, 5, 11, 23, 1)]
+
+
+@pytest.mark.parametrize("tr,vmax", [(None, None), ("4", None), ("8", None), ("8", "2"), ("4", "1")])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_dwr_cases(ox, dtype, tr, vmax, monkeypatch):
+    # the row-segment depthwise kernel, forced, with each band height and
+    # narrower segments; fp32 on integer values is exact, bf16 on random
+    # values within tolerance; every activation.  Where no segment width
+    # applies, the forced call is refused.
+    monkeypatch.setenv("OX_FORCE_KERNEL", "dwr")
+    if tr:
+        monkeypatch.setenv("OX_DWR_TR", tr)
+    if vmax:
+        monkeypatch.setenv("OX_DWR_V", vmax)
+    cases = DWR_CASES + (DWR_F32_ODD if dtype == "f32" else [])
+    for ci, (N, Cc, H, W, st) in enumerate(cases):
+        act = ["relu6", "none", "relu", "gelu"][ci % 4]
+        r = np.random.default_rng(5100 + ci)
+        if dtype == "f32":
+            X = r.integers(-4, 5, (N, Cc, H, W)).astype(np.float64)
+            Wt = r.integers(-3, 4, (Cc, 1, 3, 3)).astype(np.float64)
+            b = r.integers(-5, 6, Cc).astype(np.float64)
+            act = "relu" if act == "gelu" else act
+        else:
+            X = synth.round_to(r.standard_normal((N, Cc, H, W)), "bf16")
+            Wt = synth.round_to(r.standard_normal((Cc, 1, 3, 3)) / 3.0, "bf16")
+            b = synth.round_to(r.uniform(-0.5, 0.5, Cc), "bf16")
+        bias = None if ci == 3 else b
+        say("dwr", dtype, tr, vmax, (N, Cc, H, W, st, act))
+        if not dwr_applies(dtype, W, st, int(vmax or 8)):
+            with pytest.raises(ox.OxError):
+                run_conv(ox, X, Wt, bias, dtype, (st, st), (1, 1, 1, 1), (1, 1), Cc, act)
+            continue
+        Y = run_conv(ox, X, Wt, bias, dtype, (st, st), (1, 1, 1, 1), (1, 1), Cc, act)
+        ref = oracle.conv2d(X, Wt, bias, (st, st), (1, 1, 1, 1), (1, 1), Cc, act)
+        if dtype == "f32":
+            assert np.array_equal(host64(Y), ref), ("dwr", ci)
+        else:
+            assert_close(host64(Y), ref, dtype, "dwr %d" % ci)
+
+
+def test_dwr_selection_and_misalignment(ox, monkeypatch):
+    # the row kernel is chosen for 3x3 pads-1 depthwise convs it applies to;
+    # bf16 with an odd width, other pads, or an X whose alignment admits no
+    # segment load take the staged-band kernel; a Y off its store width is
+    # written element by element
+    assert ox.ox_conv2d_variant("bf16", 2, 32, 56, 56, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
+    assert ox.ox_conv2d_variant("f32", 2, 32, 56, 56, 32, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
+    assert ox.ox_conv2d_variant("f32", 2, 32, 7, 7, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
+    assert ox.ox_conv2d_variant("bf16", 2, 32, 7, 7, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dw/")
+    assert ox.ox_conv2d_variant("bf16", 2, 32, 8, 8, 32, 3, 3, (1, 1), (0, 0, 0, 0), (1, 1), 32).startswith("dw/")
+    assert ox.ox_conv2d_variant("bf16", 1, 4, 8, 1040, 4, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 4).startswith("dw/")
+    r = np.random.default_rng(5300)
+    X = synth.round_to(r.standard_normal((2, 16, 20, 20)), "bf16")
+    Wt = synth.round_to(r.standard_normal((16, 1, 3, 3)) / 3.0, "bf16")
+    b = synth.round_to(r.uniform(-0.5, 0.5, 16), "bf16")
+    ref = oracle.conv2d(X, Wt, b, (1, 1), (1, 1, 1, 1), (1, 1), 16, "relu6")
+    for xoff, yoff in ((0, 1), (0, 2), (0, 4), (0, 8), (1, 0), (2, 3), (4, 0)):
+        say("dwr misaligned X/Y", xoff, yoff)
+        Xd = misaligned(dev(X, "bf16"), xoff) if xoff else dev(X, "bf16")
+        Y = misaligned(nan_like((2, 16, 20, 20), "bf16"), yoff)
+        ox.ox_conv2d_fused(Xd, dev(Wt, "bf16"), dev(b, "bf16"), (1, 1), (1, 1, 1, 1), (1, 1), 16,
+                           "relu6", Y=Y)
+        torch.cuda.synchronize()
+        assert_close(host64(Y), ref, "bf16", "dwr xoff %d yoff %d" % (xoff, yoff))
 
 
 @pytest.mark.parametrize("force", [None, "1x1", "igemm"])
