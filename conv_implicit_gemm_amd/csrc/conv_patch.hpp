@@ -8,10 +8,12 @@
 //   * stages the input band (with its halo, zero-filled once) in LDS in a
 //     channel-contiguous layout: one 80-byte cell per input position holds
 //     the 32 channels (64 bytes) plus 16 bytes of bank padding.  A staging
-//     unit is P (1 or 2) consecutive plane positions x 8 channels: 8 loads of
-//     P elements, repacked by position after the barrier.  Consecutive lanes
-//     take consecutive positions, so global loads are contiguous across a
-//     wave and the 16-byte cell writes hit distinct LDS banks;
+//     unit is P (1, 2, 4 or 8: the widest that keeps every plane's start
+//     aligned) consecutive plane positions x 8 channels: 8 loads of P
+//     elements, transposed by position (byte permutes) after the barrier.
+//     Consecutive lanes take consecutive position groups, so global loads are
+//     contiguous across a wave and the 16-byte cell writes hit distinct LDS
+//     banks;
 //   * stages the weights of the chunk tap-major.  ONNX-layout weights
 //     W[m, c, kh, kw] are read as they lie in memory (8 channels x 9 taps =
 //     9 aligned 16-byte loads) and permuted in registers so that each tap
@@ -27,10 +29,11 @@
 // Columns of the patch are stored de-interleaved by stride phase (S = 2: all
 // even columns, then all odd ones), so consecutive output pixels read
 // consecutive cells for stride 2 as well as stride 1.
-// The next chunk's global loads are issued before the current chunk's MFMAs
-// and land in registers; one LDS buffer, two barriers per chunk.  The
-// epilogue stages the block's bf16 outputs in LDS as [channel][pixel] and
-// writes each channel's run of output pixels with aligned vector stores.
+// The next chunk's global loads (raw-buffer loads, 2P bytes per channel
+// and unit, branch-free) are interleaved with the first half of the current
+// chunk's MFMAs and land in registers; one LDS buffer, two barriers per
+// chunk.  The epilogue stores straight from the accumulators: each lane
+// holds four consecutive output pixels of one channel.
 #pragma once
 
 #include <algorithm>
@@ -45,9 +48,16 @@ constexpr int kCell = 80;     // bytes per patch cell
 constexpr int kKK = 9;
 constexpr int kAROW = kKK * 64 + 16;   // bytes per staged weight row
 
-// staging units per thread: 8 registers each, fewer where the weight tile of
-// a 128-channel block needs the room
-constexpr int patch_upt(int P, int BM) { return (BM >= 128 ? 4 : 8) / P; }
+// staging registers of a unit (8 channels x P positions): one dword per
+// channel up to P = 2, P/2 dwords per channel beyond
+constexpr int patch_unit_dwords(int P) { return P <= 2 ? 8 : 4 * P; }
+// staging units per thread: 64 (P = 1) or 32 staging registers, half that
+// where the weight tile of a 128-channel block needs the room, at least one unit
+constexpr int patch_upt(int P, int BM) {
+  return (P == 1 ? 64 : 32) / (BM >= 128 ? 2 : 1) / patch_unit_dwords(P) > 0
+             ? (P == 1 ? 64 : 32) / (BM >= 128 ? 2 : 1) / patch_unit_dwords(P)
+             : 1;
+}
 
 // Writes staged bf16 outputs to Y.  E[m - mlo][slot - slo] holds channel
 // m0 + m, pixel slot `slot` of the tile (slot = i*ppi + e: image img0 + i,
@@ -73,9 +83,14 @@ __device__ __forceinline__ void store_runs(const ConvArgs& a, const PatchPlan& p
     const int a0 = max(slo, i * ppi), a1 = min(shi, i * ppi + L);
     if (a1 <= a0) continue;
     const int per_run = (a1 - a0 + V - 1) / V;
-    for (int it = tid; it < mc * per_run; it += nthr) {
-      const int m = it / per_run;
-      const int slot = a0 + (it - m * per_run) * V;
+    // a power-of-two group of threads per channel row, the rows of a pass
+    // side by side (nthr is a power of two): no division per store
+    int lg = 0;
+    while ((1 << lg) < per_run && (1 << lg) < nthr) ++lg;
+    const int tpr = 1 << lg, rpp = nthr >> lg;
+    for (int m = tid >> lg; m < mc; m += rpp)
+    for (int c = tid & (tpr - 1); c < per_run; c += tpr) {
+      const int slot = a0 + c * V;
       const uint16_t* src = E + m * erow + (slot - slo);
       uint16_t* dst = Y + ((int64_t)(img0 + i) * M + m0 + mlo + m) * HoWo + g0 + (slot - i * ppi);
       if (V == 8) {
@@ -107,21 +122,85 @@ __device__ __forceinline__ TileGeo tile_geo(const ConvArgs& a, const PatchPlan& 
   int mb, bx;
   if (pp.ga * pp.gb > 1) {
     const int rp = npb / pp.ga, rm = pp.nmb / pp.gb;   // exact: the planner checks
-    const int r = tile_id / (rp * rm), w = tile_id - (tile_id / (rp * rm)) * (rp * rm);
-    const int ri = r / pp.gb, rj = r - (r / pp.gb) * pp.gb;
-    bx = ri * rp + w / rm;
-    mb = rj * rm + (w - (w / rm) * rm);
+    const int r = div_small(tile_id, rp * rm), w = tile_id - r * (rp * rm);
+    const int ri = div_small(r, pp.gb), rj = r - ri * pp.gb;
+    const int wq = div_small(w, rm);
+    bx = ri * rp + wq;
+    mb = rj * rm + (w - wq * rm);
   } else {
-    mb = tile_id / npb;
+    mb = div_small(tile_id, npb);
     bx = tile_id - mb * npb;
   }
   TileGeo t;
+  const int ib = div_small(bx, pp.nrb);
   t.m0 = mb * BM;
-  t.img0 = (bx / pp.nrb) * pp.IMB;
-  t.oh0 = (bx - (bx / pp.nrb) * pp.nrb) * pp.TR;
+  t.img0 = ib * pp.IMB;
+  t.oh0 = (bx - ib * pp.nrb) * pp.TR;
   t.rows_here = min(pp.TR, a.Ho - t.oh0);
   t.imgs_here = min(pp.IMB, a.N - t.img0);
   return t;
+}
+
+// The direct-store epilogue: bias (fp32, from LDS),
+// activation, bf16 rounding and stores of a wave's (32*FP pixel) x (32*FC
+// channel) tile.
+template <int FP, int FC>
+__device__ __forceinline__ void store_acc(const ConvArgs& a, const PatchPlan& pp, const f32x16_t (&acc)[FP][FC],
+                                          const float* Bs, int wm, int wn, int l32, int kg, int m0, int img0,
+                                          int oh0, int rows_here, int imgs_here) {
+  const int M = a.M;
+  const int ppi = pp.TR * a.Wo;
+  // Straight from the accumulators.  Lane (l32, kg) holds, for
+  // each (fp, fc), output channel 32*fc + l32 at pixel slots 8*g + 4*kg +
+  // (0..3), g = 0..3, of pixel tile fp: four consecutive slots of one
+  // channel, which are four consecutive output pixels of one NCHW plane
+  // whenever they lie in one image's band.  Bias, activation and bf16
+  // rounding happen here; four such pixels at an 8-byte aligned address go
+  // out as one store, any other slot element by element.  (The bias reads
+  // LDS, published by the chunk loop's barriers.)
+  uint16_t* Y = (uint16_t*)a.Y;
+  const int HoWo = a.Ho * a.Wo;
+  const int Lb = rows_here * a.Wo;             // output pixels of each image's band
+  const int g0 = oh0 * a.Wo;                   // first of them in its plane
+  float bv[FC];
+#pragma unroll
+  for (int fc = 0; fc < FC; ++fc) bv[fc] = Bs[wm * FC * 32 + fc * 32 + l32];
+  with_act(a.act, [&](auto act_k) {
+    constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+    for (int fp = 0; fp < FP; ++fp) {
+      const int tile = wn * FP + fp;
+      if (tile >= pp.NT) continue;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int slot = tile * 32 + 8 * g + 4 * kg;
+        const int i = div_small(slot, ppi);
+        const int e = slot - i * ppi;           // position in image i's band
+#pragma unroll
+        for (int fc = 0; fc < FC; ++fc) {
+          const int m = m0 + wm * FC * 32 + fc * 32 + l32;
+          if (m >= M) continue;
+          const f32x16_t& c = acc[fp][fc];
+          float v[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) v[j] = act_c<ACT>(c[4 * g + j] + bv[fc]);
+          const int64_t off = ((int64_t)(img0 + i) * M + m) * HoWo + g0 + e;
+          if (i < imgs_here && e + 3 < Lb && (off & 3) == 0) {
+            *(u32x2_t*)(Y + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              // (with several images per block the slots may reach further images)
+              const int ij = div_small(slot + j, ppi), ej = slot + j - ij * ppi;
+              if (ij < imgs_here && ej < Lb)
+                Y[((int64_t)(img0 + ij) * M + m) * HoWo + g0 + ej] =
+                    (uint16_t)(pack_bf16x2(v[j], 0.f) & 0xffffu);
+            }
+          }
+        }
+      }
+    }
+  });
 }
 
 template <int WM, int WN, int FP, int FC, int P, int S, bool WPACK>
@@ -129,10 +208,14 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
     const ConvArgs a, const PatchPlan pp) {
   constexpr int BM = 32 * WM * FC;          // output channels per block
   constexpr int UPT = patch_upt(P, BM);     // patch staging units per thread (max)
+  constexpr int XC = patch_unit_dwords(P) / 8;   // staging dwords per channel of a unit
   // weight staging units per thread: packed layout, one 16-byte vector of a
   // channel row's 576 bytes each; ONNX layout, 8 channels x 9 taps each
   constexpr int WUNITS = WPACK ? BM * 36 / kThreads : BM * 4 / kThreads;
+  constexpr int NLW = WUNITS * (WPACK ? 1 : kKK);   // weight loads per thread and chunk
+  constexpr int NL = NLW + UPT * 8;                  // all loads per thread and chunk
   static_assert(WM * WN == 4, "four waves");
+  static_assert(P == 1 || P == 2 || P == 4 || P == 8, "staging width");
   extern __shared__ __attribute__((aligned(16))) char smem[];
   char* As = smem;
   char* Ps = smem + BM * kAROW;
@@ -149,7 +232,7 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   // channel chunks, the slices of a tile adjacent
   const int tiles = pp.nrb * pp.nib * pp.nmb;
   const int unit = xcd_tile(blockIdx.x, tiles * pp.splits);
-  const int tile_id = unit / pp.splits;
+  const int tile_id = div_small(unit, pp.splits);
   const int slice = unit - tile_id * pp.splits;
   const TileGeo geo = tile_geo(a, pp, tile_id, BM);
   const int m0 = geo.m0, img0 = geo.img0, oh0 = geo.oh0;
@@ -163,28 +246,37 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
   const int fs = (flo / P) * P;
   const int ngrp = fhi > flo ? (fhi - fs + P - 1) / P : 0;
   const int units = imgs_here * 4 * ngrp;
-  const uint16_t* Wt = (const uint16_t*)a.Wt;
-  const uint16_t* Xblk = (const uint16_t*)a.X + (int64_t)img0 * C * HW;
+
+  // Operands are read through raw buffers: a load whose offset lies past the
+  // tensor returns zeros, so absent staging units, weight rows past M and the
+  // loads after a slice's last chunk (offset with bit 31 set: every operand
+  // is below 2^31 bytes) need no branch.
+  constexpr uint32_t kPast = 0x80000000u;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.X), (short)0, (int)((uint32_t)a.N * (uint32_t)C * (uint32_t)HW * 2u), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.Wt), (short)0, (int)((uint32_t)M * (uint32_t)K * 2u), 0x00020000);
 
   // staging units of this thread, fixed for every chunk: a unit is P
-  // consecutive plane positions x 8 channels.  u_goff: element offset of its
-  // first value from the chunk's first plane of image img0 (-1: no unit);
+  // consecutive plane positions x 8 channels.  u_voff: byte offset of its
+  // first value in the block's first chunk of channels (kPast: no unit);
   // u_lds: LDS byte offset of the cell of each position (-1: not needed).
-  int u_goff[UPT], u_lds[UPT][P];
+  uint32_t u_voff[UPT];
+  int u_lds[UPT][P];
 #pragma unroll
   for (int k = 0; k < UPT; ++k) {
     const int u = tid + k * kThreads;
-    u_goff[k] = -1;
+    u_voff[k] = kPast;
 #pragma unroll
     for (int e = 0; e < P; ++e) u_lds[k][e] = -1;
     if (u < units) {
-      const int i = u / (4 * ngrp);
+      const int i = div_small(u, 4 * ngrp);
       const int rem = u - i * 4 * ngrp;
-      const int oct = rem / ngrp;
+      const int oct = div_small(rem, ngrp);
       const int g = rem - oct * ngrp;
       const int f0 = fs + g * P;
-      u_goff[k] = (i * C + oct * 8) * HW + f0;
-      int ih = f0 / W, iw = f0 - (f0 / W) * W;
+      u_voff[k] = (uint32_t)((((img0 + i) * C + oct * 8) * HW + f0) * 2);
+      int ih = div_small(f0, W), iw = f0 - ih * W;
 #pragma unroll
       for (int e = 0; e < P; ++e) {
         const int f = f0 + e;
@@ -201,6 +293,21 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
       }
     }
   }
+  // weight loads of this thread: byte offset of each in the block's first
+  // chunk (kPast: row past M).  Packed: 16-byte vector j of row m's 576
+  // bytes per chunk; ONNX layout: taps 0..8 of channel octet oct of row m.
+  uint32_t w_voff[WUNITS];
+#pragma unroll
+  for (int k = 0; k < WUNITS; ++k) {
+    const int v = tid + k * kThreads;
+    if constexpr (WPACK) {
+      const int m = v / 36, j = v - (v / 36) * 36;
+      w_voff[k] = m0 + m < M ? (uint32_t)((m0 + m) * C * 18 + j * 16) : kPast;
+    } else {
+      const int m = v >> 2, oct = v & 3;
+      w_voff[k] = m0 + m < M ? (uint32_t)((m0 + m) * K * 2 + oct * 144) : kPast;
+    }
+  }
 
   // this lane's pixel (row of the A operand) in each of the wave's FP tiles
   int pbase[FP];
@@ -208,9 +315,9 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
 #pragma unroll
   for (int f = 0; f < FP; ++f) {
     const int q = (wn * FP + f) * 32 + l32;
-    const int i = q / ppi;
+    const int i = div_small(q, ppi);
     const int rem = q - i * ppi;
-    const int r = rem / a.Wo;
+    const int r = div_small(rem, a.Wo);
     const int c = rem - r * a.Wo;
     const bool valid = q < pp.NT * 32 && i < imgs_here && r < rows_here;
     pbase[f] = (valid ? (i * pp.PR + r * S) * pp.PWt + c : 0) * kCell + kg * 16;
@@ -236,45 +343,32 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
   u32x4_t wreg[WUNITS][WPACK ? 1 : kKK];
-  uint32_t xreg[UPT][8];   // raw loaded values: per channel, P bf16 positions
+  uint32_t xv[UPT][8][XC];   // raw loaded values: per channel, P bf16 positions
 
-  auto load_chunk = [&](int c0) {
-    if constexpr (WPACK) {
-      // packed: row m of chunk c0/32 is 9 taps x 32 channels, contiguous
-#pragma unroll
-      for (int k = 0; k < WUNITS; ++k) {
-        const int v = tid + k * kThreads;
-        const int m = v / 36, j = v - (v / 36) * 36;
-        if (m0 + m < M)
-          wreg[k][0] = *(const u32x4_t*)(Wt + ((int64_t)(m0 + m) * (C / 32) + c0 / 32) * 288 + j * 8);
-        else
-          wreg[k][0] = u32x4_t{0u, 0u, 0u, 0u};
-      }
+  // load i (0 <= i < NL) of the chunk starting at channel c0; kill = kPast
+  // sends it past the tensors (the slice has no further chunk)
+  auto issue = [&](int i, int c0, uint32_t kill) {
+    if (i < NLW) {
+      const int k = WPACK ? i : i / kKK, j = WPACK ? 0 : i - (i / kKK) * kKK;
+      wreg[k][j] = __builtin_amdgcn_raw_buffer_load_b128(wr, (w_voff[k] | kill) + j * 16, c0 * 18, 0);
     } else {
-#pragma unroll
-      for (int k = 0; k < WUNITS; ++k) {
-        const int u = tid + k * kThreads;
-        const int m = u >> 2, oct = u & 3;
-        if (m0 + m < M) {
-          const uint16_t* src = Wt + (int64_t)(m0 + m) * K + (c0 + oct * 8) * kKK;
-#pragma unroll
-          for (int j = 0; j < kKK; ++j) wreg[k][j] = *(const u32x4_t*)(src + 8 * j);
-        } else {
-#pragma unroll
-          for (int j = 0; j < kKK; ++j) wreg[k][j] = u32x4_t{0u, 0u, 0u, 0u};
-        }
-      }
-    }
-    const uint16_t* xc = Xblk + (int64_t)c0 * HW;
-#pragma unroll
-    for (int k = 0; k < UPT; ++k) {
-      if (u_goff[k] >= 0) {
-        const uint16_t* src = xc + u_goff[k];
-#pragma unroll
-        for (int ch = 0; ch < 8; ++ch) {
-          if constexpr (P == 1) xreg[k][ch] = src[ch * HW];
-          else xreg[k][ch] = *(const uint32_t*)(src + ch * HW);
-        }
+      const int k = (i - NLW) >> 3, ch = (i - NLW) & 7;
+      const uint32_t vo = u_voff[k] | kill;
+      const int so = (c0 + ch) * HW * 2;
+      if constexpr (P == 1) {
+        xv[k][ch][0] = __builtin_amdgcn_raw_buffer_load_b16(xr, vo, so, 0);
+      } else if constexpr (P == 2) {
+        xv[k][ch][0] = __builtin_amdgcn_raw_buffer_load_b32(xr, vo, so, 0);
+      } else if constexpr (P == 4) {
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(xr, vo, so, 0);
+        xv[k][ch][0] = v[0];
+        xv[k][ch][1] = v[1];
+      } else {
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(xr, vo, so, 0);
+        xv[k][ch][0] = v[0];
+        xv[k][ch][1] = v[1];
+        xv[k][ch][2] = v[2];
+        xv[k][ch][3] = v[3];
       }
     }
   };
@@ -315,13 +409,16 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
 #pragma unroll
       for (int e = 0; e < P; ++e) {
         if (u_lds[k][e] >= 0) {
+          // the cell of position e: channels (2j, 2j+1) in dword j
           uint32_t d[4];
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const uint32_t lo = xreg[k][2 * j], hi = xreg[k][2 * j + 1];
-            if constexpr (P == 1) d[j] = lo | (hi << 16);
-            else if (e == 0) d[j] = (lo & 0xffffu) | (hi << 16);
-            else d[j] = (lo >> 16) | (hi & 0xffff0000u);
+            if constexpr (P == 1) {
+              d[j] = (xv[k][2 * j][0] & 0xffffu) | (xv[k][2 * j + 1][0] << 16);
+            } else {
+              const uint32_t lo = xv[k][2 * j][e >> 1], hi = xv[k][2 * j + 1][e >> 1];
+              d[j] = __builtin_amdgcn_perm(hi, lo, (e & 1) ? 0x07060302u : 0x05040100u);
+            }
           }
           *(u32x4_t*)(Ps + u_lds[k][e]) = u32x4_t{d[0], d[1], d[2], d[3]};
         }
@@ -331,7 +428,8 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
 
   const int nchunks = C / 32;
   const int c_lo = slice * pp.cps, c_hi = min(nchunks, c_lo + pp.cps);
-  load_chunk(c_lo * 32);
+#pragma unroll
+  for (int i = 0; i < NL; ++i) issue(i, c_lo * 32, 0u);
   // while the first chunk is in flight: zero the whole patch once (halo
   // cells are never written again) and fetch this lane's bias values
   for (int i = tid; i < pp.npos * (kCell / 16); i += kThreads)
@@ -343,11 +441,17 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
     if (chunk == c_lo && tid < BM) Bs[tid] = __uint_as_float(braw << 16);
     store_chunk();
     __syncthreads();
-    if (chunk + 1 < c_hi) load_chunk((chunk + 1) * 32);
+    // The next chunk's loads are spread over the first half of this chunk's
+    // k-steps, so that issuing them hides under matrix-core time (after the
+    // slice's last chunk they are sent past the tensors: uniform code, no
+    // branch).
+    const int cn = (chunk + 1) * 32;
+    const uint32_t kill = chunk + 1 < c_hi ? 0u : kPast;
     // 18 k-steps (9 taps x 2 halves of 16 channels).  Fragments are read two
     // steps ahead into a ring of three register sets, and the scheduler is
-    // told to interleave those LDS reads one by one with the MFMAs of the
-    // current step, so that LDS latency hides under matrix-core time.
+    // told to interleave those LDS reads and the loads one by one with the
+    // MFMAs of the current step, so that their latency hides under
+    // matrix-core time.
     constexpr int NS = 2 * kKK;
     u32x4_t pf[3][FP], wf[3][FC];
     auto read_frags = [&](int s, int buf) {
@@ -363,15 +467,22 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
     for (int s = 0; s < NS; ++s) {
       const bool ahead = s + 2 < NS;
       if (ahead) read_frags(s + 2, (s + 2) % 3);
+      // (over the first half of the steps, which leaves the second half's
+      // matrix-core time for their latency)
+      const int l0 = s < NS / 2 ? s * NL / (NS / 2) : NL, l1 = s < NS / 2 ? (s + 1) * NL / (NS / 2) : NL;
+#pragma unroll
+      for (int i = l0; i < l1; ++i) issue(i, cn, kill);
 #pragma unroll
       for (int fp = 0; fp < FP; ++fp)
 #pragma unroll
         for (int fc = 0; fc < FC; ++fc) mma32(acc[fp][fc], pf[s % 3][fp], wf[s % 3][fc]);
       constexpr int NM = FP * FC, NR = FP + FC;
+      const int NV = l1 - l0;
 #pragma unroll
-      for (int i = 0; i < (NM > NR ? NM : NR); ++i) {
+      for (int i = 0; i < NM + NR + 8; ++i) {
         if (i < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // one MFMA
         if (ahead && i < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // one LDS read
+        if (i < NV) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // one global load
       }
       __builtin_amdgcn_sched_barrier(0);   // keep each step's reads in its own step
     }
@@ -391,44 +502,7 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
     return;
   }
 
-  // Epilogue.  Lane (l32, kg) holds, for each (fp, fc), output channel
-  // 32*fc + l32 at pixel slots 8*g + 4*kg + (0..3), g = 0..3, of pixel tile
-  // fp.  Bias, activation and bf16 rounding happen here; the block's tile is
-  // then staged in LDS as [channel][pixel slot] so that each channel's run of
-  // output pixels (contiguous in NCHW) is written with aligned vector stores.
-  __syncthreads();                       // all waves are done with the patch
-  const int nslot = pp.NT * 32;
-  const int erow = nslot + 8;            // elements per staged channel row
-  uint16_t* E = (uint16_t*)smem;
-  float bv[FC];
-#pragma unroll
-  for (int fc = 0; fc < FC; ++fc) bv[fc] = Bs[wm * FC * 32 + fc * 32 + l32];
-  with_act(a.act, [&](auto act_k) {
-    constexpr int ACT = decltype(act_k)::value;
-#pragma unroll
-    for (int fc = 0; fc < FC; ++fc) {
-      const int ml = wm * FC * 32 + fc * 32 + l32;
-#pragma unroll
-      for (int fp = 0; fp < FP; ++fp) {
-        const int tile = wn * FP + fp;
-        if (tile < pp.NT) {
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int slot = tile * 32 + 8 * g + 4 * kg;
-            const f32x16_t& c = acc[fp][fc];
-            const uint32_t lo = pack_bf16x2(act_c<ACT>(c[4 * g + 0] + bv[fc]),
-                                            act_c<ACT>(c[4 * g + 1] + bv[fc]));
-            const uint32_t hi = pack_bf16x2(act_c<ACT>(c[4 * g + 2] + bv[fc]),
-                                            act_c<ACT>(c[4 * g + 3] + bv[fc]));
-            *(u32x2_t*)(E + ml * erow + slot) = u32x2_t{lo, hi};
-          }
-        }
-      }
-    }
-  });
-  __syncthreads();
-  store_runs(a, pp, E, erow, img0, imgs_here, oh0, rows_here, m0, 0, min(BM, M - m0), 0, nslot, tid,
-             kThreads);
+  store_acc<FP, FC>(a, pp, acc, Bs, wm, wn, l32, kg, m0, img0, oh0, rows_here, imgs_here);
 }
 
 // Second pass of split-K: one block per (tile, wave of the first pass); its
@@ -494,10 +568,14 @@ int launch_cfg(const ConvArgs& a, const PatchPlan& p, hipStream_t s) {
                          dim3(kThreads), p.lds, s, a, p);                                        \
   } while (0)
   if (a.sw == 1) {
-    if (p.VW == 2) OX_PATCH_LAUNCH(2, 1);
+    if (p.VW == 8) OX_PATCH_LAUNCH(8, 1);
+    else if (p.VW == 4) OX_PATCH_LAUNCH(4, 1);
+    else if (p.VW == 2) OX_PATCH_LAUNCH(2, 1);
     else OX_PATCH_LAUNCH(1, 1);
   } else {
-    if (p.VW == 2) OX_PATCH_LAUNCH(2, 2);
+    if (p.VW == 8) OX_PATCH_LAUNCH(8, 2);
+    else if (p.VW == 4) OX_PATCH_LAUNCH(4, 2);
+    else if (p.VW == 2) OX_PATCH_LAUNCH(2, 2);
     else OX_PATCH_LAUNCH(1, 2);
   }
 #undef OX_PATCH_LAUNCH

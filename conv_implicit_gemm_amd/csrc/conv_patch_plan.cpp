@@ -48,14 +48,21 @@ PatchPlan make(const ConvArgs& a, const Cfg& c, int TR, int IMB) {
   p.nmb = (a.M + p.BM - 1) / p.BM;
   p.npos = IMB * p.PR * p.PWt;
   const int HW = a.H * a.W;
-  p.VW = (HW % 2 == 0) ? 2 : 1;               // positions per staging unit (P)
-  p.UPT = (p.BM >= 128 ? 4 : 8) / p.VW;       // staging units per thread (kernel's patch_upt)
+  // positions per staging unit (P): the widest load (P bf16) that every
+  // plane's start keeps aligned
+  p.VW = (HW % 8 == 0) ? 8 : (HW % 4 == 0) ? 4 : (HW % 2 == 0) ? 2 : 1;
+  {
+    // staging units per thread (the kernel's patch_upt): 64 (P = 1) or 32
+    // staging registers, halved for 128-channel blocks, at least one unit
+    const int dwords = p.VW <= 2 ? 8 : 4 * p.VW;
+    const int upt = (p.VW == 1 ? 64 : 32) / (p.BM >= 128 ? 2 : 1) / dwords;
+    p.UPT = upt > 0 ? upt : 1;
+  }
   // staging units: images x 4 channel octets x groups of P plane positions
   // (a band of R rows spans at most R*W + P - 1 positions from a P-aligned start)
   const int rows = std::min(a.H, p.PR);
   p.units = IMB * 4 * ((rows * a.W + 2 * p.VW - 2) / p.VW);
-  p.lds = std::max(p.BM * (9 * 64 + 16) + p.npos * kCell,
-                   p.BM * (p.NT * 32 + 8) * 2)    // the epilogue reuses LDS as [channel][pixel]
+  p.lds = p.BM * (9 * 64 + 16) + p.npos * kCell   // weight rows and patch cells
           + p.BM * 4;                             // + the tile's fp32 bias
   p.splits = 1;
   p.cps = std::max(1, a.C / 32);
@@ -111,7 +118,7 @@ size_t ws_bytes(const PatchPlan& p) {
 bool fits(const PatchPlan& p) {
   const int ntmax = (4 / p.WM) * p.FN;
   return p.NT <= ntmax && p.lds <= kLdsMax && p.units <= p.UPT * 256 &&
-         (int64_t)p.nrb * p.nib * p.nmb * p.splits < (1 << 30);
+         (int64_t)p.nrb * p.nib * p.nmb * p.splits < (1 << 22);
 }
 
 // Rough time model: MFMA cycles per SIMD over the whole grid against the
@@ -137,11 +144,18 @@ double cost(const ConvArgs& a, const PatchPlan& p) {
 }
 
 // the tallest band of at most `slots` pixels, evened out over the image so
-// that the last band is not a sliver
+// that the last band is not a sliver -- or, among the heights that give the
+// same number of bands, one whose bands start at a multiple of four output
+// pixels (8-byte aligned bf16 rows: the epilogue stores four pixels at once
+// only there; 14x14 layers, 8-row bands instead of 7: ~10% faster)
 int band_rows(const ConvArgs& a, int slots) {
   const int trmax = std::max(1, std::min(a.Ho, slots / std::max(1, a.Wo)));
   const int nrb = (a.Ho + trmax - 1) / trmax;
-  return (a.Ho + nrb - 1) / nrb;
+  const int even = (a.Ho + nrb - 1) / nrb;
+  if ((even * a.Wo) % 4 == 0 || nrb == 1) return even;
+  for (int tr = trmax; tr > even; --tr)
+    if ((tr * a.Wo) % 4 == 0 && (a.Ho + tr - 1) / tr == nrb) return tr;
+  return even;
 }
 
 }  // namespace
@@ -230,8 +244,12 @@ bool patch_plan(const ConvArgs& a, PatchPlan* out) {
 }
 
 bool conv_patch_geometry(const ConvArgs& a) {
+  // operands are addressed with 32-bit buffer offsets (below 2^31 bytes);
+  // the kernel's setup divisions need index ranges below 2^22
   return a.dt == DT_BF16 && a.group == 1 && a.kH == 3 && a.kW == 3 && a.C % 32 == 0 &&
-         a.sh == a.sw && (a.sw == 1 || a.sw == 2);
+         a.sh == a.sw && (a.sw == 1 || a.sw == 2) &&
+         (int64_t)a.N * a.C * a.H * a.W * 2 < ((int64_t)1 << 31) &&
+         (int64_t)a.M * a.C * 9 * 2 < ((int64_t)1 << 31) && (int64_t)a.H * a.W < (1 << 22);
 }
 
 bool conv_patch_applicable(const ConvArgs& a) {

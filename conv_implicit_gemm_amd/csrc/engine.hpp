@@ -76,6 +76,19 @@ __device__ __forceinline__ int fdiv(const FastDiv& f, int n) {
   return (int)((hi + (uint32_t)n) >> f.shr);
 }
 
+// n / d for 0 <= n < 2^22, 1 <= d < 2^22, d not fixed for the launch: the
+// single-precision product n * rcp(d) (v_rcp_f32 within 1 ulp, one more
+// rounding) is within 1.5 * 2^-23 * n/d < 0.75 of n / d, so its truncation
+// is off by at most one either way, which one remainder test each way
+// corrects (a handful of instructions instead of the generic 32-bit
+// division sequence; q * d stays below n + d, no overflow).
+__device__ __forceinline__ int div_small(int n, int d) {
+  int q = (int)((float)n * __builtin_amdgcn_rcpf((float)d));
+  const int r = n - q * d;
+  q += (r >= d) - (r < 0);
+  return q;
+}
+
 // One v_mfma_f32_32x32x16_bf16: c[32x32] += a[32x16] * b[16x32].  Lane l
 // supplies row (a) / column (b) l%32 with k = 8*(l/32) .. 8*(l/32)+7 as 8
 // bf16 in one 128-bit register quad; accumulator element i of lane l is

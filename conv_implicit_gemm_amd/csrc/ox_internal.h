@@ -129,7 +129,7 @@ struct PatchPlan {
   int nib;              // image blocks
   int nmb;              // output-channel blocks
   int npos;             // cells in the patch (IMB * PR * PWt)
-  int VW;               // plane positions per staging unit (1 or 2)
+  int VW;               // plane positions per staging unit (1, 2, 4 or 8)
   int units;            // upper bound of staging units per block
   int lds;              // bytes of LDS
   int ga, gb;           // XCD rectangles: pixel blocks in ga groups x channel blocks in gb
