@@ -54,6 +54,13 @@ def parse():
     p.add_argument("--copy-bytes", type=int, default=0,
                    help="only run 10 plain device copies of this many bytes (the reference "
                         "reading for HBM byte counters), then exit")
+    p.add_argument("--rotate-mb", type=float, default=512.0,
+                   help="working set of the timed steps: identical copies of every layer's "
+                        "tensors are cycled step by step until their total reaches this many MB, "
+                        "so inputs come from HBM rather than the 256 MB last-level cache")
+    p.add_argument("--summarize-trace", default=None,
+                   help="only print per-kernel medians of a rocprofv3 kernel-trace CSV as a "
+                        "markdown table, then exit")
     return p.parse_args()
 
 
@@ -439,6 +446,84 @@ def measured_traffic(kernel, workload, dtype):
     return None
 
 
+# --------------------------------------------------------- machine facts --
+
+def gpu_clocks():
+    """Current shader and memory clock levels as rocm-smi reports them (a
+    child process reading the driver's tables), or None."""
+    import subprocess
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        d = json.loads(r.stdout)
+    except Exception:
+        return None
+    card = next(iter(d.values())) if isinstance(d, dict) and d else {}
+    keep = {}
+    for k, v in card.items():
+        kl = k.lower()
+        if "sclk" in kl or "mclk" in kl or "fclk" in kl:
+            keep[k] = v
+    return keep or None
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def copy_ceiling(torch, stream, mb=64, sets=16, reps=48):
+    """Plain device-to-device copies (torch's copy kernel) of `mb` MB each,
+    cycling `sets` source/destination pairs (2 * sets * mb MB, far above the
+    last-level cache): the HBM rate a streaming kernel can expect here."""
+    n = int(mb * 1e6)
+    pairs = [(torch.empty(n, dtype=torch.uint8, device="cuda"), torch.empty(n, dtype=torch.uint8, device="cuda"))
+             for _ in range(sets)]
+    for a, b in pairs:
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        a, b = pairs[r % sets]
+        b.copy_(a)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    del pairs
+    return {"GB/s": 2 * n / (us * 1e-6) / 1e9, "bytes_moved_per_copy": 2 * n, "us_per_copy": us,
+            "working_set_MB": 2 * sets * mb, "kernel": "torch copy_ (device to device)"}
+
+
+def summarize_trace(path):
+    """Per-kernel median / min / mean duration (us) of a rocprofv3
+    kernel-trace CSV, grouped by kernel name and grid size, in order of first
+    dispatch (the library's kernels)."""
+    import csv
+    groups = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            if "ox::" not in name:      # the library's kernels only (not set-up copies)
+                continue
+            grid = row.get("Grid_Size", row.get("Grid_Size_X", ""))
+            dur = (int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3
+            groups.setdefault((name, grid), []).append(dur)
+    print("| kernel | grid (threads) | dispatches | median us | min us | mean us |")
+    print("|---|---:|---:|---:|---:|---:|")
+    for (name, grid), d in groups.items():
+        d = sorted(d)
+        short = name.split("(")[0]
+        print("| `%s` | %s | %d | %.2f | %.2f | %.2f |" % (short, grid, len(d), d[len(d) // 2], d[0],
+                                                          sum(d) / len(d)))
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -448,6 +533,9 @@ def main():
               "(the per-GPU path is the same kernel at one GPU's share)" % args.gpus,
               file=sys.stderr)
         sys.exit(2)
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
     import torch
     import conv_implicit_gemm_amd as ox
     import synth
@@ -472,7 +560,7 @@ def main():
         dtype = args.dtype or "bf16"
         batch = args.batch or 32
         res = [l.name for l in synth.resnet50_layers(batch) if l.name.endswith("1x1b")] if args.residual else []
-        layers = conv_layers(ox, synth, torch, 3, synth.resnet50_layers(batch), dtype, sp, res)
+        builder = lambda: conv_layers(ox, synth, torch, 3, synth.resnet50_layers(batch), dtype, sp, res)
         cfg = {"workload": "resnet50-v2 convolutions (16 layers), NCHW", "batch": batch,
                "input": "3x224x224", "epilogue": "folded BN bias + ReLU"}
         if res:
@@ -480,7 +568,7 @@ def main():
     elif wl == "resnet50-aux":
         dtype = args.dtype or "bf16"
         batch = args.batch or 32
-        layers = aux_layers(ox, torch, dtype, batch, sp)
+        builder = lambda: aux_layers(ox, torch, dtype, batch, sp)
         cfg = {"workload": "resnet50 memory-bound steps: stem MaxPool, pre-activation BatchNorm + "
                            "ReLU at each stage width, head GlobalAveragePool", "batch": batch}
     elif wl == "mobilenetv2":
@@ -491,33 +579,33 @@ def main():
         # a residual add after their (linear) projection
         res = [mb[i].name for i in range(len(mb)) if args.residual and mb[i].name.endswith("project")
                and not mb[i].name.endswith(".0.project")] if args.residual else []
-        layers = conv_layers(ox, synth, torch, 2, mb, dtype, sp, res)
+        builder = lambda: conv_layers(ox, synth, torch, 2, mb, dtype, sp, res)
         cfg = {"workload": "mobilenetv2 convolutions (51 layers), NCHW", "batch": batch,
                "input": "3x224x224", "epilogue": "folded BN bias + ReLU6 / linear"}
         if res:
             cfg["residual"] = "the projection of each repeated block adds a residual"
     elif wl == "mlp":
         dtype = args.dtype or "bf16"
-        layers = gemm_layers(ox, synth, torch, synth.mlp_rows(), dtype, sp)
+        builder = lambda: gemm_layers(ox, synth, torch, synth.mlp_rows(), dtype, sp)
         cfg = {"workload": "MLP Gemm rows M in {1,64,256} x (1024->4096 GELU, 4096->1024, "
                            "1024->1024 ReLU)"}
     elif wl == "nbits":
         dtype = "bf16"
-        layers = nbits_layers(ox, synth, torch, sp)
+        builder = lambda: nbits_layers(ox, synth, torch, sp)
         cfg = {"workload": "MatMulNBits 4-bit blocks of 32 with zero points, [M,4096] x "
                            "[4096->4096], M in {1, 64, 256}"}
     elif wl == "dynq":
         dtype = "f32"
-        layers = dynq_layers(ox, torch, sp)
+        builder = lambda: dynq_layers(ox, torch, sp)
         cfg = {"workload": "DynamicQuantizeLinear fp32 -> uint8 of [1000,1024] and [1000,4096] "
                            "activations"}
     elif wl == "matmul":
         dtype = "f32"
-        layers = matmul_layers(ox, synth, torch, sp)
+        builder = lambda: matmul_layers(ox, synth, torch, sp)
         cfg = {"workload": "batched MatMul [16,64,128] x [16,128,64]"}
     else:
         dtype = "i8"
-        layers = int8_layers(ox, synth, torch, sp, args.quant)
+        builder = lambda: int8_layers(ox, synth, torch, sp, args.quant)
         cfg = {"workload": "static int8 conformer block, T=1000, d_model=1024 "
                            "(FFN, QKV, depthwise 1-D k9, pointwise)"}
         if args.quant != "s8":
@@ -526,27 +614,39 @@ def main():
                             "u8-wzp": "uint8 activations and outputs, per-channel weight zero "
                                       "points"}[args.quant]
 
-    def step():
-        for L in layers:
+    # Rotation: identical copies of every layer's tensors (same seeds), one
+    # set per step in turn, until the sets hold --rotate-mb: each step then
+    # finds its inputs in HBM, not in the 256 MB last-level cache.
+    layers = builder()
+    step_bytes = sum(L.nbytes for L in layers)
+    nsets = int(min(64, max(1, np.ceil(args.rotate_mb * 1e6 / max(1.0, step_bytes)))))
+    sets = [layers] + [builder() for _ in range(nsets - 1)]
+
+    def step(s):
+        for L in sets[s % nsets]:
             st = L.launch()
             if st != 0:
                 raise RuntimeError("%s: %s" % (L.name, ox.ox_last_error()))
 
-    for _ in range(args.warmup):
-        step()
+    for w in range(max(args.warmup, nsets)):
+        step(w)
     torch.cuda.synchronize()
     run_step = step
     if args.graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph, stream=stream):
-            step()
+        graphs = []
+        for k in range(nsets):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                step(k)
+            graphs.append(g)
         torch.cuda.synchronize()
-        for _ in range(args.warmup):
-            graph.replay()
+        for w in range(max(args.warmup, nsets)):
+            graphs[w % nsets].replay()
         torch.cuda.synchronize()
-        run_step = graph.replay
-        cfg = dict(cfg, graph="one step captured in a HIP graph, replayed")
+        run_step = lambda s: graphs[s % nsets].replay()
+        cfg = dict(cfg, graph="one step per tensor set captured in a HIP graph, replayed in turn")
 
+    clocks_before = gpu_clocks()
     # timed region: K steps back to back, one event pair around all of them
     # (same stream).  An event between two kernels is a stream marker that
     # itself costs a few microseconds of idle GPU, so the per-kernel events
@@ -558,26 +658,41 @@ def main():
     wall0 = time.perf_counter()
     t_start.record(stream)
     for s in range(K):
-        run_step()
+        run_step(s)
     t_end.record(stream)
+    host_s = time.perf_counter() - wall0
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
+    clocks_after = gpu_clocks()
 
-    # per-kernel pass: K more steps, an event pair around every launch
+    # per-kernel pass: K more steps, an event pair around every launch;
+    # the per-layer figure is the median over the K steps
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in layers] for _ in range(K)]
     torch.cuda.synchronize()
     for s in range(K):
-        for i, L in enumerate(layers):
+        for i, L in enumerate(sets[s % nsets]):
             ev[s][i][0].record(stream)
             st = L.launch()
             ev[s][i][1].record(stream)
             if st != 0:
                 raise RuntimeError("%s: %s" % (L.name, ox.ox_last_error()))
     torch.cuda.synchronize()
-    per_layer_ms = [float(np.mean([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)]))
+    per_layer_ms = [float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)]))
                     for i in range(len(layers))]
+
+    # host cost of one C-ABI call (argument marshalling and the launch), on
+    # the first set, without waiting for the GPU
+    torch.cuda.synchronize()
+    ncall = 0
+    h0 = time.perf_counter()
+    while ncall < 2000 and time.perf_counter() - h0 < 0.2:
+        for L in layers:
+            L.launch()
+            ncall += 1
+    t_call_us = (time.perf_counter() - h0) / max(1, ncall) * 1e6
+    torch.cuda.synchronize()
 
     step_flops = sum(L.flops for L in layers)
     ms_per_step = total_ms / K
@@ -627,9 +742,23 @@ def main():
     roof["avg_launch_us"] = avg_us
     roof["roofline_frac"] = g["t_roof"] / (g["ms"] * 1e-3)   # sum t_roof / sum t_meas
 
+    # every variant family of the step (the dominant one is `roofline`)
+    families = {}
+    for name, gr in groups.items():
+        mfma = gr["t_flop"] > gr["t_byte"]
+        sec = gr["ms"] * 1e-3
+        families[name] = {"launches_per_step": gr["n"], "us_per_step": gr["ms"] * 1e3,
+                          "bound": "mfma" if mfma else "hbm",
+                          "tflops": gr["flops"] / sec / 1e12, "gbs": gr["bytes"] / sec / 1e9,
+                          "mfma_frac": gr["flops"] / sec / 1e12 / pk if gr["t_flop"] > 0 else None,
+                          "hbm_frac": gr["bytes"] / sec / 1e9 / HBM_PEAK,
+                          "roofline_frac": gr["t_roof"] / sec}
+
     cpu = None
     if args.cpu_seconds > 0 and step_flops > 0:
         cpu = cpu_baseline(layers, args.cpu_seconds, dtype == "i8")
+        cpu["cpu_model"] = cpu_model()
+    ceiling = copy_ceiling(torch, stream)
 
     unit = "TOPS" if dtype == "i8" else "TFLOP/s"
     if step_flops == 0:
@@ -641,7 +770,15 @@ def main():
         "vs_baseline": None, "dtype": dtype if dtype != "i8" else "int8",
         "data": "synthetic (seeded; shapes and value distributions of the workload)",
         "config": cfg, "roofline": roof, "cpu_baseline": cpu,
-        "host_wall_s": wall,
+        "families": families,
+        "rotation": {"tensor_sets": nsets, "working_set_MB": nsets * step_bytes / 1e6,
+                     "step_algorithmic_MB": step_bytes / 1e6},
+        "timing": {"per_layer": "median over the K steps of an event pair around each launch "
+                                "(a second pass; the step time has no events between kernels)",
+                   "host_wall_s": wall, "host_enqueue_s_per_step": host_s / K,
+                   "t_call_us": t_call_us},
+        "machine": {"gpu_clocks_before": clocks_before, "gpu_clocks_after": clocks_after,
+                    "cpu_model": cpu_model(), "copy_ceiling": ceiling},
     }
     if args.rows:
         rows = []
