@@ -519,7 +519,7 @@ def summarize_trace(path):
     print("|---|---:|---:|---:|---:|---:|")
     for (name, grid), d in groups.items():
         d = sorted(d)
-        short = name.split("(")[0]
+        short = name.replace("(anonymous namespace)::", "").split("(")[0]
         print("| `%s` | %s | %d | %.2f | %.2f | %.2f |" % (short, grid, len(d), d[len(d) // 2], d[0],
                                                           sum(d) / len(d)))
 

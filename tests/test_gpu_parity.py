@@ -175,6 +175,24 @@ def test_gemm_single_row(ox, dtype, tb, force, monkeypatch):
     assert_close(host64(Y), oracle.gemm(A, B, bias, transB=tb, act="gelu"), dtype, "gemv")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gemv_rows_per_block(ox, dtype):
+    # the M = 1 kernel over [N, K] weights: 1, 2, 4 and 8 rows per block
+    # (N = 1000, 1024, 2048, 4097: a partial last block), 16-byte rows whose
+    # chunk count is or is not a multiple of the four K quarters, rows that
+    # are not 16-byte aligned (element path), K below one chunk per lane
+    r = np.random.default_rng(31)
+    for N, K in ((1000, 1000), (1024, 4096), (2048, 1032), (4097, 1024), (1024, 1001), (64, 24), (3, 4100)):
+        say("gemv", dtype, N, K)
+        A = synth.round_to(r.standard_normal((1, K)), dtype)
+        B = synth.round_to(r.standard_normal((N, K)) / math.sqrt(K), dtype)
+        bias = synth.round_to(r.uniform(-0.1, 0.1, N), dtype)
+        Y = nan_like((1, N), dtype)
+        ox.ox_gemm_fused(dev(A, dtype), dev(B, dtype), dev(bias, dtype), transB=True, act="relu", Y=Y)
+        torch.cuda.synchronize()
+        assert_close(host64(Y), oracle.gemm(A, B, bias, transB=True, act="relu"), dtype, "gemv %d x %d" % (N, K))
+
+
 def test_gemm_empty_reduction_writes_activation_of_bias(ox):
     say("gemm K=0")
     bias = np.array([-1.0, 0.5, 7.0], np.float64)
