@@ -58,6 +58,10 @@ def parse():
                    help="working set of the timed steps: identical copies of every layer's "
                         "tensors are cycled step by step until their total reaches this many MB, "
                         "so inputs come from HBM rather than the 256 MB last-level cache")
+    p.add_argument("--ab", action="store_true",
+                   help="only time every applicable kernel of each layer of the workload (forced "
+                        "through OX_FORCE_KERNEL, on rotated tensors) next to the one the library "
+                        "selects, print a markdown table, then exit")
     p.add_argument("--summarize-trace", default=None,
                    help="only print per-kernel medians of a rocprofv3 kernel-trace CSV as a "
                         "markdown table, then exit")
@@ -524,6 +528,145 @@ def summarize_trace(path):
                                                           sum(d) / len(d)))
 
 
+# ------------------------------------------------------------- selection --
+
+def _time_calls(torch, stream, calls, reps=None):
+    """Per-call time (us) of `calls` (a list of closures, one per rotated
+    tensor set) launched back to back, one event pair around them all."""
+    reps = reps or max(24, 3 * len(calls))
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for r in range(reps):
+        calls[r % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def ab_conv(ox, synth, torch, layers, dtype, stream, rotate_mb):
+    """Every applicable conv kernel of each layer, timed on identical tensor
+    sets cycled until they hold `rotate_mb` MB."""
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    cands = ["dwr", "dw", "pwd", "pw", "1x1", "patch", "patch+packed", "smallc", "igemm"]
+    rows = []
+    for l in layers:
+        ho, wo = l.out_hw()
+        st, pads = (l.stride, l.stride), l.onnx_pads
+        geo = (l.N, l.C, l.H, l.W, l.M, l.kh, l.kw, st, pads, (1, 1), l.group)
+        nb = l.nbytes(ESIZE[dtype])
+        nsets = int(min(32, max(2, np.ceil(rotate_mb * 1e6 / nb))))
+        K = (l.C // l.group) * l.kh * l.kw
+        sets = []
+        for k in range(nsets):
+            X = torch.randn(l.N, l.C, l.H, l.W, device="cuda").to(tdt)
+            W = (torch.randn(l.M, l.C // l.group, l.kh, l.kw) / np.sqrt(K)).to(tdt)
+            b = (torch.randn(l.M, device="cuda") * 0.1).to(tdt)
+            Y = torch.empty(l.N, l.M, ho, wo, device="cuda", dtype=tdt)
+            Wp = None
+            if dtype == "bf16" and ox.ox_conv2d_packed_weights_bytes(dtype, *geo):
+                bits = W.view(torch.int16).numpy().view(np.uint16)
+                Wp = torch.from_numpy(ox.ox_conv2d_pack_weights(bits, dtype, l.N, l.C, l.H, l.W, st, pads,
+                                                                (1, 1), l.group).view(np.int16)).cuda().view(torch.bfloat16)
+            sets.append((X, W.cuda(), b, Y, Wp))
+        selected = ox.ox_conv2d_variant(dtype, *geo)
+        times = {}
+        for v in ["default"] + cands:
+            packed = v.endswith("+packed") or (v == "default" and sets[0][4] is not None)
+            if v == "default":
+                os.environ.pop("OX_FORCE_KERNEL", None)
+            else:
+                os.environ["OX_FORCE_KERNEL"] = v.split("+")[0]
+            try:
+                if packed and sets[0][4] is None:
+                    raise ox.OxError(3, "no packed weights")
+                wsb = ox.ox_conv2d_workspace_bytes(dtype, *geo)
+                ws = torch.empty(wsb, dtype=torch.uint8, device="cuda") if wsb else None
+                d = ox.conv_desc(*geo)
+                code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
+                sp = stream.cuda_stream
+                calls = []
+                for (X, W, b, Y, Wp) in sets:
+                    wt = Wp if packed else W
+                    # the raw C-ABI call, as the benchmark step makes it
+                    calls.append(lambda X=X, wt=wt, b=b, Y=Y: ox.lib.ox_conv2d_fused_ws(
+                        code, C.byref(d), X.data_ptr(), wt.data_ptr(), 1 if packed else 0, b.data_ptr(),
+                        ox.ACT[l.act], Y.data_ptr(), ws.data_ptr() if ws is not None else None, wsb, sp))
+                if calls[0]() != 0:
+                    raise ox.OxError(3, ox.ox_last_error())
+                times[v] = _time_calls(torch, stream, calls)
+            except ox.OxError:
+                pass
+        os.environ.pop("OX_FORCE_KERNEL", None)
+        flops = l.flops()
+        rows.append((l.name, "%d->%d %dx%d k%d s%d g%d" % (l.C, l.M, l.H, l.W, l.kh, l.stride, l.group),
+                     flops / nb, selected, times))
+    return rows
+
+
+def ab_gemm(ox, synth, torch, grows, dtype, stream, rotate_mb):
+    """GEMV against the tile engine at M = 1, split-K against a single pass
+    where a split is planned."""
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    code = ox.OX_BF16 if dtype == "bf16" else ox.OX_F32
+    rows = []
+    for r in grows:
+        nb = (r.M * r.K + r.N * r.K + r.N + r.M * r.N) * ESIZE[dtype]
+        nsets = int(min(64, max(2, np.ceil(rotate_mb * 1e6 / nb))))
+        sets = [(torch.randn(r.M, r.K, device="cuda").to(tdt), (torch.randn(r.N, r.K, device="cuda") / np.sqrt(r.K)).to(tdt),
+                 (torch.randn(r.N, device="cuda") * 0.1).to(tdt), torch.empty(r.M, r.N, device="cuda", dtype=tdt))
+                for _ in range(nsets)]
+        nws = ox.ox_gemm_workspace_bytes(dtype, r.M, r.N, r.K)
+        ws = torch.empty(max(nws, 16), dtype=torch.uint8, device="cuda")
+        sp = stream.cuda_stream
+        times = {}
+        variants = [("default", None, nws)]
+        if r.M == 1:
+            variants += [("gemv", "gemv", 0), ("mfma", "mfma", 0)]
+        if nws:
+            variants += [("mfma split-K", "mfma", nws), ("mfma single pass", "mfma", 0)]
+        for name, force, wsb in variants:
+            if force:
+                os.environ["OX_FORCE_KERNEL"] = force
+            else:
+                os.environ.pop("OX_FORCE_KERNEL", None)
+            calls = [lambda X=X, W=W, b=b, Y=Y, wsb=wsb: ox.lib.ox_gemm_fused_ws(
+                code, r.M, r.N, r.K, 0, 1, 1.0, X.data_ptr(), W.data_ptr(), 1.0, b.data_ptr(), ox.ACT[r.act],
+                Y.data_ptr(), ws.data_ptr() if wsb else None, wsb, sp) for (X, W, b, Y) in sets]
+            if calls[0]() == 0:
+                times[name] = _time_calls(torch, stream, calls)
+        os.environ.pop("OX_FORCE_KERNEL", None)
+        m, n, k = r.M, r.N, r.K
+        ai = 2.0 * m * n * k / ((m * k + k * n + m * n) * ESIZE[dtype])
+        rows.append((r.name, "M%d N%d K%d" % (m, n, k), ai, "gemv" if m == 1 else
+                     ("mfma split-K" if nws else "mfma"), times))
+    return rows
+
+
+def print_ab(rows, title):
+    print("# %s" % title)
+    print()
+    print("| layer | shape | intensity (flop/B) | selected | fastest | selected / fastest | times (us per call) |")
+    print("|---|---|---:|---|---|---:|---|")
+    for name, shape, ai, sel, times in rows:
+        if not times:
+            continue
+        # the selected kernel's time: its forced run where there is one (the
+        # default run is the same kernel; the better of the two is kept, so
+        # that run-to-run noise is not read as a wrong choice)
+        key = sel.split("/")[0]
+        if key == "patch" and "patch+packed" in times:
+            key = "patch+packed"
+        selt = min(t for k, t in times.items() if k in ("default", key))
+        forced = {k: t for k, t in times.items() if k != "default"}
+        best = min(forced, key=forced.get) if forced else "default"
+        ratio = selt / min(selt, forced.get(best, selt))
+        print("| %s | %s | %.0f | `%s` | `%s` | %.2f | %s |" % (
+            name, shape, ai, sel, best, ratio, ", ".join("%s %.1f" % (k, v) for k, v in times.items())))
+
+
 # -------------------------------------------------------------------- main --
 
 def main():
@@ -550,6 +693,21 @@ def main():
         print(json.dumps({"copy_bytes": args.copy_bytes, "copies": 10}))
         return
     stream = torch.cuda.current_stream()
+    if args.ab:
+        wl = args.workload
+        dtype = args.dtype or ("f32" if wl == "mobilenetv2" else "bf16")
+        if wl == "resnet50":
+            rows = ab_conv(ox, synth, torch, synth.resnet50_layers(args.batch or 32), dtype, stream, args.rotate_mb)
+        elif wl == "mobilenetv2":
+            rows = ab_conv(ox, synth, torch, synth.mobilenetv2_layers(args.batch or 64), dtype, stream, args.rotate_mb)
+        elif wl == "mlp":
+            rows = ab_gemm(ox, synth, torch, synth.mlp_rows(), dtype, stream, args.rotate_mb)
+        else:
+            print("bench.py --ab: resnet50, mobilenetv2 or mlp", file=sys.stderr)
+            sys.exit(2)
+        print_ab(rows, "%s, %s%s: every applicable kernel per layer" % (
+            wl, dtype, "" if wl == "mlp" else ", batch %d" % (args.batch or (32 if wl == "resnet50" else 64))))
+        return
     if args.graph:
         # capture needs a stream of its own (default priority)
         stream = torch.cuda.Stream()
@@ -628,6 +786,19 @@ def main():
             if st != 0:
                 raise RuntimeError("%s: %s" % (L.name, ox.ox_last_error()))
 
+    # host cost of one C-ABI call (argument marshalling and the launch), on
+    # the first set, without waiting for the GPU (whole steps, before the
+    # warm-up: a profiler's last pass stays the per-kernel pass below)
+    torch.cuda.synchronize()
+    ncall = 0
+    h0 = time.perf_counter()
+    while ncall < 2000 and time.perf_counter() - h0 < 0.2:
+        for L in layers:
+            L.launch()
+            ncall += 1
+    t_call_us = (time.perf_counter() - h0) / max(1, ncall) * 1e6
+    torch.cuda.synchronize()
+
     for w in range(max(args.warmup, nsets)):
         step(w)
     torch.cuda.synchronize()
@@ -681,18 +852,6 @@ def main():
     torch.cuda.synchronize()
     per_layer_ms = [float(np.median([ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(K)]))
                     for i in range(len(layers))]
-
-    # host cost of one C-ABI call (argument marshalling and the launch), on
-    # the first set, without waiting for the GPU
-    torch.cuda.synchronize()
-    ncall = 0
-    h0 = time.perf_counter()
-    while ncall < 2000 and time.perf_counter() - h0 < 0.2:
-        for L in layers:
-            L.launch()
-            ncall += 1
-    t_call_us = (time.perf_counter() - h0) / max(1, ncall) * 1e6
-    torch.cuda.synchronize()
 
     step_flops = sum(L.flops for L in layers)
     ms_per_step = total_ms / K

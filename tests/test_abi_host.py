@@ -137,8 +137,9 @@ def test_variant_selection_sweep(ox, monkeypatch):
         assert "/" in name
         if dt == "bf16" and g == 1 and k == 1 and s == 1 and C % 32 == 0:
             # the DMA-staged kernel where the plane has an even pixel count
-            # (the fake pointers are aligned), else the register-staged one
-            want = "pwd/" if (H * W) % 2 == 0 else "pw/"
+            # (the fake pointers are aligned) and C is a multiple of 64 or the
+            # layer has at least 65536 pixels, else the register-staged one
+            want = "pwd/" if (H * W) % 2 == 0 and (C % 64 == 0 or N * H * W >= 65536) else "pw/"
             assert name.startswith(want), (name, C, M, H, W)
         if dt == "bf16" and g == 1 and k == 3 and C % 32 == 0:
             assert name.startswith("patch/"), (name, C, M, H, W, s)
