@@ -366,6 +366,109 @@ struct LoadColK {
   }
 };
 
+// Branch-free loaders for the pipelined K loop.  They read through raw
+// buffers, where an offset with bit 31 set (kPastK) returns zeros: rows or
+// columns past the operand and k past K cost no branch, so the loads of
+// several stages can stay in flight behind one another.  Callers guarantee
+// that every byte offset they form from the block's base stays below 2^31.
+constexpr uint32_t kPastK = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void* p) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+
+// [rows, K] operand, row stride ld, K a multiple of EPC and rows 16-byte
+// aligned (a chunk is all inside K or all past it).
+template <int DT, int BROWS, int BKU, bool FLIP = false>
+struct LoadRowKB {
+  typedef typename Traits<DT>::T T;
+  enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         TOTAL = BROWS * CPR, NCH = (TOTAL + kThreads - 1) / kThreads };
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo[NCH];     // chunk i's byte offset in stage 0, or kPastK
+  int K;
+  u32x4_t r[NCH];
+
+  __device__ __forceinline__ void init(const T* p, int64_t ld, int row0, int rows, int K_) {
+    rs = operand_rsrc(p + (int64_t)row0 * ld);
+    K = K_;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      const int row = q / CPR, ch = q % CPR;
+      const bool ok = (TOTAL % kThreads == 0 || q < TOTAL) && row < rows - row0;
+      vo[i] = ok ? (uint32_t)(row * ld * (int64_t)sizeof(T)) + ch * 16 : kPastK;
+    }
+  }
+  __device__ __forceinline__ void load(int k0) {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = (threadIdx.x + i * kThreads) % CPR;
+      const uint32_t off = k0 + ch * EPC < K ? vo[i] : kPastK;
+      r[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              rs, off, k0 * (int)sizeof(T), 0));
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int q = threadIdx.x + i * kThreads;
+      if (TOTAL % kThreads == 0 || q < TOTAL)
+        *(u32x4_t*)(lds + (q / CPR) * ROWB + (q % CPR) * 16) = flip_chunk<DT, FLIP>(r[i]);
+    }
+  }
+};
+
+// [K, cols] fp32 operand, row stride ld: the thread keeps column tid % BCOLS
+// and gathers the 4 consecutive k of a chunk with one load each.  (Narrower
+// elements would need widening in registers whose loads are still in
+// flight, which forces early waits: those take LoadColK.)
+template <int DT, int BCOLS, int BKU, bool FLIP = false>
+struct LoadColKB {
+  typedef typename Traits<DT>::T T;
+  static_assert(sizeof(T) == 4, "fp32 columns only");
+  enum { EPC = Traits<DT>::EPC, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         STEP = kThreads / BCOLS, NCH = (CPR + STEP - 1) / STEP };
+  static_assert(kThreads % BCOLS == 0, "columns must divide the block");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo;          // this column's byte offset at k = 0
+  uint32_t ldb;         // row stride in bytes
+  int K;
+  bool valid;
+  u32x4_t r[NCH];
+
+  __device__ __forceinline__ void init(const T* p, int64_t ld, int col0, int cols, int K_) {
+    rs = operand_rsrc(p + col0);
+    const int col = threadIdx.x % BCOLS;
+    valid = col < cols - col0;
+    vo = (uint32_t)col * 4u;
+    ldb = (uint32_t)(ld * 4);
+    K = K_;
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int ch0 = threadIdx.x / BCOLS;
+    const int soff = k0 * (int)ldb;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int kk = ch * 4 + j;
+        const bool ok = valid && (CPR % STEP == 0 || ch < CPR) && k0 + kk < K;
+        r[i][j] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? vo + kk * ldb : kPastK, soff, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int col = threadIdx.x % BCOLS, ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = r[i];
+    }
+  }
+};
+
 // The implicit-GEMM operand of a convolution: column = one output pixel
 // (img, oh, ow), k = (c, kh, kw) in the weight's own order, element =
 // X[img, c, oh*sh - pt + kh*dh, ow*sw - pl + kw*dw], or `pad` outside the
@@ -435,63 +538,139 @@ template <int DT, int BM, int BN> struct WaveTile {
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 16x16 block");
 };
 
+// One stage's MMAs: the BKU units of the LDS stage at As / Bs.
+template <int DT, int BM, int BN, int BKU, int SUMS>
+__device__ __forceinline__ void engine_stage(const char* As, const char* Bs,
+                                             typename Traits<DT>::Acc (&acc)[BM / 32][BN / 32],
+                                             int* ks) {
+  typedef WaveTile<DT, BM, BN> WT;
+  enum { ROWB = Lds<BKU>::ROWB };
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int u = 0; u < BKU; ++u) {
+    u32x4_t a[WT::FM], b[WT::FN];
+#pragma unroll
+    for (int fm = 0; fm < WT::FM; ++fm)
+      a[fm] = *(const u32x4_t*)(As + (wm * WT::TM + fm * 16 + lr) * ROWB + u * 64 + lg * 16);
+#pragma unroll
+    for (int fn = 0; fn < WT::FN; ++fn)
+      b[fn] = *(const u32x4_t*)(Bs + (wn * WT::TN + fn * 16 + lr) * ROWB + u * 64 + lg * 16);
+#pragma unroll
+    for (int fm = 0; fm < WT::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < WT::FN; ++fn) Mma<DT>::run(acc[fm][fn], a[fm], b[fn]);
+    if constexpr (SUMS == 1) {
+#pragma unroll
+      for (int fm = 0; fm < WT::FM; ++fm) ks[fm] = sum16_i8(a[fm], ks[fm]);
+    } else if constexpr (SUMS == 2) {
+#pragma unroll
+      for (int fn = 0; fn < WT::FN; ++fn) ks[fn] = sum16_i8(b[fn], ks[fn]);
+    }
+  }
+}
+
 // The K loop shared by every problem: accumulates into acc[FM][FN].
 // SUMS (int8 only): 1 also sums the int8 values of every A row this lane
 // reads into ks[fm], 2 of every B column into ks[fn]: the per-row /
 // per-column activation sums of the weight zero-point term.
-template <int DT, int BM, int BN, int BKU, int SUMS = 0, class LA, class LB>
+//
+// Two LDS stages alternate.  D = 1: the next stage's global loads are issued
+// before this stage's MMAs and written to LDS after them, so every stage
+// waits out one global-load latency.  D = 2 or 4: D register copies of each
+// loader keep the loads of stages s+1 .. s+D in flight while stage s is
+// multiplied (stage t lives in copy t % D), which divides that wait by D
+// for D times the loader registers.  The loop body is unrolled D times so
+// that every copy index is a constant; the last 2D stages issue no loads
+// past the end of K.
+template <int DT, int BM, int BN, int BKU, int SUMS = 0, int D = 1, class LA, class LB>
 __device__ __forceinline__ void engine_mainloop(LA& la, LB& lb, int K, char* smem,
                                                 typename Traits<DT>::Acc (&acc)[BM / 32][BN / 32],
                                                 int* ks = nullptr) {
-  typedef WaveTile<DT, BM, BN> WT;
-  enum { ROWB = Lds<BKU>::ROWB, A_BYTES = BM * ROWB, B_BYTES = BN * ROWB,
+  static_assert(D == 1 || D == 2 || D == 4, "1, 2 or 4 stages in flight");
+  enum { ROWB = Lds<BKU>::ROWB, A_BYTES = BM * ROWB, STAGE = (BM + BN) * ROWB,
          KSTEP = BKU * 4 * Traits<DT>::EPC };
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int lr = lane & 15, lg = lane >> 4;
   const int nk = (K + KSTEP - 1) / KSTEP;
   if (nk == 0) return;
 
-  la.load(0);
-  lb.load(0);
-  la.store(smem);
-  lb.store(smem + A_BYTES);
-  __syncthreads();
-  for (int s = 0; s < nk; ++s) {
-    char* As = smem + (s & 1) * (A_BYTES + B_BYTES);
-    char* Bs = As + A_BYTES;
-    const bool more = s + 1 < nk;
-    if (more) {
-      la.load((s + 1) * KSTEP);
-      lb.load((s + 1) * KSTEP);
-    }
-#pragma unroll
-    for (int u = 0; u < BKU; ++u) {
-      u32x4_t a[WT::FM], b[WT::FN];
-#pragma unroll
-      for (int fm = 0; fm < WT::FM; ++fm)
-        a[fm] = *(const u32x4_t*)(As + (wm * WT::TM + fm * 16 + lr) * ROWB + u * 64 + lg * 16);
-#pragma unroll
-      for (int fn = 0; fn < WT::FN; ++fn)
-        b[fn] = *(const u32x4_t*)(Bs + (wn * WT::TN + fn * 16 + lr) * ROWB + u * 64 + lg * 16);
-#pragma unroll
-      for (int fm = 0; fm < WT::FM; ++fm)
-#pragma unroll
-        for (int fn = 0; fn < WT::FN; ++fn) Mma<DT>::run(acc[fm][fn], a[fm], b[fn]);
-      if constexpr (SUMS == 1) {
-#pragma unroll
-        for (int fm = 0; fm < WT::FM; ++fm) ks[fm] = sum16_i8(a[fm], ks[fm]);
-      } else if constexpr (SUMS == 2) {
-#pragma unroll
-        for (int fn = 0; fn < WT::FN; ++fn) ks[fn] = sum16_i8(b[fn], ks[fn]);
+  if constexpr (D == 1) {
+    la.load(0);
+    lb.load(0);
+    la.store(smem);
+    lb.store(smem + A_BYTES);
+    __syncthreads();
+    for (int s = 0; s < nk; ++s) {
+      char* As = smem + (s & 1) * STAGE;
+      const bool more = s + 1 < nk;
+      if (more) {
+        la.load((s + 1) * KSTEP);
+        lb.load((s + 1) * KSTEP);
       }
+      engine_stage<DT, BM, BN, BKU, SUMS>(As, As + A_BYTES, acc, ks);
+      if (more) {
+        char* An = smem + ((s + 1) & 1) * STAGE;
+        la.store(An);
+        lb.store(An + A_BYTES);
+      }
+      __syncthreads();
     }
-    if (more) {
-      char* An = smem + ((s + 1) & 1) * (A_BYTES + B_BYTES);
-      la.store(An);
-      lb.store(An + A_BYTES);
+  } else {
+    LA pa[D];
+    LB pb[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      pa[d] = la;
+      pb[d] = lb;
+    }
+    // stages 0 .. D-1 in flight; stage 0 to LDS; stage D into copy 0
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+      if (d < nk) {
+        pa[d].load(d * KSTEP);
+        pb[d].load(d * KSTEP);
+      }
+    pa[0].store(smem);
+    pb[0].store(smem + A_BYTES);
+    if (D < nk) {
+      pa[0].load(D * KSTEP);
+      pb[0].load(D * KSTEP);
     }
     __syncthreads();
+    // One stage s (s % D == d): multiply it, write stage s+1 (copy (d+1)%D)
+    // to the other LDS stage, refill that copy with stage s+1+D.  TAIL:
+    // stage s+1 or s+1+D may not exist (the main loop knows they do, so its
+    // loads are unconditional and the counter waits stay exact).
+    auto step = [&](auto dk, auto tk, int s) {
+      constexpr int d = decltype(dk)::value, nd = (d + 1) % D;
+      constexpr bool TAIL = decltype(tk)::value;
+      // keep each stage's work in its stage: hoisted uses of a loaded
+      // register would wait for loads that are meant to stay in flight
+      __builtin_amdgcn_sched_barrier(0);
+      const char* As = smem + (d & 1) * STAGE;
+      engine_stage<DT, BM, BN, BKU, SUMS>(As, As + A_BYTES, acc, ks);
+      if (!TAIL || s + 1 < nk) {
+        char* An = smem + ((d + 1) & 1) * STAGE;
+        pa[nd].store(An);
+        pb[nd].store(An + A_BYTES);
+        if (!TAIL || s + 1 + D < nk) {
+          pa[nd].load((s + 1 + D) * KSTEP);
+          pb[nd].load((s + 1 + D) * KSTEP);
+        }
+      }
+      __syncthreads();
+    };
+    int s0 = 0;
+    // every stage of this loop has a successor and refills its copy
+    for (; s0 + 2 * D < nk; s0 += D) {
+      static_for<D>([&](auto dk) { step(dk, std::false_type{}, s0 + decltype(dk)::value); });
+    }
+    // the last stages: at most 2D
+    static_for<2 * D>([&](auto dk) {
+      constexpr int d = decltype(dk)::value;
+      const int s = s0 + d;
+      if (s < nk) step(std::integral_constant<int, d % D>{}, std::true_type{}, s);
+    });
   }
 }
 
@@ -535,6 +714,50 @@ __device__ __forceinline__ void for_each_result(const Acc (&acc)[BM / 32][BN / 3
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         f(wm * (BM / 2) + fm * 16 + lg * 4 + i, wn * (BN / 2) + fn * 16 + lr, acc[fm][fn][i]);
+}
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left alone): every vector memory
+// operation issued so far has completed.  Epilogues call it once their
+// per-channel parameters are in registers and before their first store: the
+// counter also counts stores, and a use of a loaded register behind a branch
+// would otherwise be preceded by a wait for every earlier store as well.
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// As for_each_result, with the lane's column fragment fn passed first: the
+// lane's columns are lane_col<BN>(fn), fn < BN/32, so that per-column values
+// can be read into registers before the first store (loads after stores
+// through possibly aliasing pointers would each wait for those stores).
+template <int BN>
+__device__ __forceinline__ int lane_col(int fn) {
+  return ((threadIdx.x >> 6) & 1) * (BN / 2) + fn * 16 + (threadIdx.x & 15);
+}
+// the lane's row in the tile for row fragment fm, register i
+template <int BM>
+__device__ __forceinline__ int lane_row(int fm, int i) {
+  return (threadIdx.x >> 7) * (BM / 2) + fm * 16 + ((threadIdx.x & 63) >> 4) * 4 + i;
+}
+// f(fm, fn, i, row_in_tile, col_in_tile, value) for each of this lane's results
+template <int BM, int BN, typename Acc, class F>
+__device__ __forceinline__ void for_each_result_idx(const Acc (&acc)[BM / 32][BN / 32], F&& f) {
+#pragma unroll
+  for (int fm = 0; fm < BM / 32; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < BN / 32; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f(fm, fn, i, lane_row<BM>(fm, i), lane_col<BN>(fn), acc[fm][fn][i]);
+}
+template <int BM, int BN, typename Acc, class F>
+__device__ __forceinline__ void for_each_result_fn(const Acc (&acc)[BM / 32][BN / 32], F&& f) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int lr = lane & 15, lg = lane >> 4;
+#pragma unroll
+  for (int fm = 0; fm < BM / 32; ++fm)
+#pragma unroll
+    for (int fn = 0; fn < BN / 32; ++fn)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        f(fn, wm * (BM / 2) + fm * 16 + lg * 4 + i, wn * (BN / 2) + fn * 16 + lr, acc[fm][fn][i]);
 }
 
 }  // namespace ox

@@ -4,6 +4,9 @@
 #pragma once
 
 #include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "engine.hpp"
@@ -25,41 +28,72 @@ template <> __device__ __forceinline__ void store_float<uint16_t>(uint16_t* y, f
 // L = A' (rows = i), R = B' (cols = j).  LK: A stored [M,K]; !LK: [K,M].
 // RK: B stored [N,K] (transB); !RK: [K,N].  z = batch index.
 
+// Block -> tile order.  The dispatcher deals a 1-D grid's blocks to the
+// eight XCDs in turn (block w to XCD w % 8), and each XCD has an L2 of its
+// own: XCD x is given one contiguous run of the tile order, and that order
+// walks groups of a.tile_group row tiles column by column, so that the
+// tiles an XCD runs together share their A rows and B columns in its L2.
+struct TilePos {
+  int z, row0, col0;
+};
+template <int BM, int BN>
+__device__ __forceinline__ TilePos gemm_tile_pos(const GemmArgs& a) {
+  const int nrt = (a.rows + BM - 1) / BM, nct = (a.cols + BN - 1) / BN;
+  const int nb = nrt * nct, total = nb * a.batch;
+  const int w = blockIdx.x;
+  const int q = total >> 3, rmd = total & 7, x = w & 7, j = w >> 3;
+  const int t = x * q + min(x, rmd) + j;
+  const int z = t / nb, u = t - z * nb;
+  const int g = a.tile_group;
+  const int grp = u / (g * nct), in = u - grp * (g * nct);
+  const int gr = min(g, nrt - grp * g);
+  const int tr = grp * g + in % gr, tc = in / gr;
+  return {z, tr * BM, tc * BN};
+}
+
 // One block's tile.  int8: rows are activations (x_q [M,K]), columns weight
 // channels; FLIP reads uint8 activations in their int8 view, WZ adds the
 // weight zero-point term (both chosen per launch from the parameter block).
-template <int DT, int BM, int BN, int BKU, bool LK, bool RK, bool FLIP, bool WZ>
+template <int DT, int BM, int BN, int BKU, int D, bool BUF, bool LK, bool RK, bool FLIP, bool WZ>
 __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, const I8View& q) {
   typedef typename Traits<DT>::T T;
   typedef typename Traits<DT>::Acc Acc;
 
-  const int z = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
+  const TilePos tp = gemm_tile_pos<BM, BN>(a);
+  const int z = tp.z, row0 = tp.row0, col0 = tp.col0;
   const T* L = (const T*)a.L + (int64_t)z * a.sl;
   const T* R = (const T*)a.R + (int64_t)z * a.sr;
-
-  typename std::conditional<LK, LoadRowK<DT, BM, BKU, FLIP>, LoadColK<DT, BM, BKU, FLIP>>::type la;
-  typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
-  if constexpr (LK) {
-    la.init(L, a.ldl, row0, a.rows, a.K, a.l_vec);
-  } else {
-    const int r = row0 + threadIdx.x % BM;
-    la.init_col(L + r, r < a.rows, a.ldl, a.K);
-  }
-  if constexpr (RK) {
-    lb.init(R, a.ldr, col0, a.cols, a.K, a.r_vec);
-  } else {
-    const int c = col0 + threadIdx.x % BN;
-    lb.init_col(R + c, c < a.cols, a.ldr, a.K);
-  }
 
   Acc acc[BM / 32][BN / 32];
 #pragma unroll
   for (int i = 0; i < BM / 32; ++i)
 #pragma unroll
     for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
-
   int ks[WaveTile<DT, BM, BN>::FM] = {};
-  engine_mainloop<DT, BM, BN, BKU, WZ ? 1 : 0>(la, lb, a.K, smem, acc, ks);
+
+  if constexpr (BUF) {
+    typename std::conditional<LK, LoadRowKB<DT, BM, BKU, FLIP>, LoadColKB<DT, BM, BKU, FLIP>>::type la;
+    typename std::conditional<RK, LoadRowKB<DT, BN, BKU>, LoadColKB<DT, BN, BKU>>::type lb;
+    la.init(L, a.ldl, row0, a.rows, a.K);
+    lb.init(R, a.ldr, col0, a.cols, a.K);
+    engine_mainloop<DT, BM, BN, BKU, WZ ? 1 : 0, D>(la, lb, a.K, smem, acc, ks);
+  } else {
+    typename std::conditional<LK, LoadRowK<DT, BM, BKU, FLIP>, LoadColK<DT, BM, BKU, FLIP>>::type la;
+    typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
+    if constexpr (LK) {
+      la.init(L, a.ldl, row0, a.rows, a.K, a.l_vec);
+    } else {
+      const int r = row0 + threadIdx.x % BM;
+      la.init_col(L + r, r < a.rows, a.ldl, a.K);
+    }
+    if constexpr (RK) {
+      lb.init(R, a.ldr, col0, a.cols, a.K, a.r_vec);
+    } else {
+      const int c = col0 + threadIdx.x % BN;
+      lb.init_col(R + c, c < a.cols, a.ldr, a.K);
+    }
+    engine_mainloop<DT, BM, BN, BKU, WZ ? 1 : 0, 1>(la, lb, a.K, smem, acc, ks);
+  }
 
   if constexpr (DT == DT_I8) {
     // weight zero points: acc -= w_zp[ch] * sum_k (x - x_zp) over the row,
@@ -73,34 +107,53 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, const I
     // were summed as -128 each
     constexpr int KSTEP = BKU * 4 * Traits<DT>::EPC;
     const int kzx = a.K * q.xzp - (FLIP ? 128 * ((a.K + KSTEP - 1) / KSTEP * KSTEP - a.K) : 0);
-    auto full = [&](int v, int r, int ch) -> int {
-      uint32_t u = (uint32_t)v + (uint32_t)q.bias[ch];
-      if constexpr (WZ) u -= (uint32_t)q.wzp[ch] * (uint32_t)(S[r] - kzx);
-      return (int)u;
+    // one column fragment at a time: its parameters are read before its
+    // stores (loads behind earlier stores would wait for those stores)
+    constexpr int FM = BM / 32, FN = BN / 32;
+    auto out = [&](auto yk) {
+      typedef typename decltype(yk)::type Y_T;
+      Y_T* Y = (Y_T*)a.Y + (int64_t)z * a.sy;
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn) {
+        const int col = col0 + lane_col<BN>(fn), cc = min(col, a.cols - 1);
+        const int cb = q.bias[cc], cw = WZ ? q.wzp[cc] : 0;
+        const double cm = std::is_same<Y_T, int8_t>::value ? q.mult[cc] : 0.0;
+        wait_vmem();
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = lane_row<BM>(fm, i), row = row0 + r;
+            if (row < a.rows && col < a.cols) {
+              uint32_t u = (uint32_t)acc[fm][fn][i] + (uint32_t)cb;
+              if constexpr (WZ) u -= (uint32_t)cw * (uint32_t)(S[r] - kzx);
+              if constexpr (std::is_same<Y_T, int8_t>::value)
+                Y[(int64_t)row * a.ldy + col] = (int8_t)(requant((int)u, cm, q.yzp) ^ q.ym);
+              else
+                Y[(int64_t)row * a.ldy + col] = (int)u;
+            }
+          }
+      }
     };
-    if (a.out_dt == DT_I32) {
-      int32_t* Y = (int32_t*)a.Y + (int64_t)z * a.sy;
-      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
-        const int row = row0 + r, col = col0 + c;
-        if (row < a.rows && col < a.cols) Y[(int64_t)row * a.ldy + col] = full(v, r, col);
-      });
-    } else {
-      int8_t* Y = (int8_t*)a.Y + (int64_t)z * a.sy;
-      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
-        const int row = row0 + r, col = col0 + c;
-        if (row < a.rows && col < a.cols) Y[(int64_t)row * a.ldy + col] = q.out(full(v, r, col), col);
-      });
-    }
+    if (a.out_dt == DT_I32) out(std::common_type<int32_t>{});
+    else out(std::common_type<int8_t>{});
   } else {
     T* Y = (T*)a.Y + (int64_t)z * a.sy;
     const T* bias = (const T*)a.bias;
+    // beta * bias of this lane's columns, read before any store
+    constexpr int FN = BN / 32;
+    float bc[FN];
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn)
+      bc[fn] = bias ? a.beta * to_f32(bias[min(col0 + lane_col<BN>(fn), a.cols - 1)]) : 0.0f;
+    wait_vmem();
     with_act(a.act, [&](auto act_k) {
       constexpr int ACT = decltype(act_k)::value;
-      for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+      for_each_result_fn<BM, BN>(acc, [&](int fn, int r, int c, float v) {
         const int row = row0 + r, col = col0 + c;
         if (row < a.rows && col < a.cols) {
           float o = a.alpha * v;
-          if (bias) o += a.beta * to_f32(bias[col]);
+          if (bias) o += bc[fn];
           store_float(Y + (int64_t)row * a.ldy + col, act_c<ACT>(o));
         }
       });
@@ -108,7 +161,7 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, const I
   }
 }
 
-template <int DT, int BM, int BN, int BKU, bool LK, bool RK>
+template <int DT, int BM, int BN, int BKU, int D, bool BUF, bool LK, bool RK>
 __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * Lds<BKU>::ROWB];
   I8View q;
@@ -116,31 +169,49 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const GemmArgs a) {
     q.init(a.i8);
     // uniform per launch: one of four instantiations runs
     if (q.xm) {
-      if (q.wz) gemm_tile<DT, BM, BN, BKU, LK, RK, true, true>(a, smem, q);
-      else gemm_tile<DT, BM, BN, BKU, LK, RK, true, false>(a, smem, q);
+      if (q.wz) gemm_tile<DT, BM, BN, BKU, D, BUF, LK, RK, true, true>(a, smem, q);
+      else gemm_tile<DT, BM, BN, BKU, D, BUF, LK, RK, true, false>(a, smem, q);
     } else {
-      if (q.wz) gemm_tile<DT, BM, BN, BKU, LK, RK, false, true>(a, smem, q);
-      else gemm_tile<DT, BM, BN, BKU, LK, RK, false, false>(a, smem, q);
+      if (q.wz) gemm_tile<DT, BM, BN, BKU, D, BUF, LK, RK, false, true>(a, smem, q);
+      else gemm_tile<DT, BM, BN, BKU, D, BUF, LK, RK, false, false>(a, smem, q);
     }
   } else {
-    gemm_tile<DT, BM, BN, BKU, LK, RK, false, false>(a, smem, q);
+    gemm_tile<DT, BM, BN, BKU, D, BUF, LK, RK, false, false>(a, smem, q);
   }
 }
 
-template <int DT, int BM, int BN, int BKU>
-int launch_gemm_tile_k(const GemmArgs& a, hipStream_t s) {
-  dim3 grid((a.cols + BN - 1) / BN, (a.rows + BM - 1) / BM, a.batch);
+// Row tiles per group of the tile order: an XCD's share of the tiles as a
+// g x c block of tiles whose A rows (g*BM) and B columns (c*BN) are about
+// equal in number (the least operand data for that many tiles).
+// OX_GEMM_GROUP pins g (measurements).
+template <int BM, int BN>
+int gemm_tile_group(int64_t nrt, int64_t total) {
+  int64_t g = (int64_t)(std::sqrt((double)((total + 7) / 8) * BN / BM) + 0.5);
+  if (const char* e = getenv("OX_GEMM_GROUP")) g = atoi(e);
+  return (int)std::max<int64_t>(1, std::min(g, nrt));
+}
+
+template <int DT, int BM, int BN, int BKU, int D, bool BUF>
+int launch_gemm_tile_k(const GemmArgs& a0, hipStream_t s) {
+  const int64_t nrt = (a0.rows + BM - 1) / BM, nct = (a0.cols + BN - 1) / BN;
+  const int64_t total = nrt * nct * a0.batch;
+  if (total >= ((int64_t)1 << 31)) return (int)hipErrorInvalidConfiguration;
+  GemmArgs a = a0;
+  a.tile_group = gemm_tile_group<BM, BN>(nrt, total);
+  dim3 grid((unsigned)total);
   if constexpr (DT == DT_I8) {
-    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, true>), grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, D, BUF, true, true>), grid, dim3(kThreads), 0, s, a);
   } else {
     if (a.l_kmajor && a.r_kmajor)
-      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, true>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, D, BUF, true, true>), grid, dim3(kThreads), 0, s, a);
+    else if constexpr (BUF && DT != DT_F32)
+      return (int)hipErrorInvalidValue;   // K-strided narrow operands never take BUF
     else if (a.l_kmajor)
-      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, true, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, D, BUF, true, false>), grid, dim3(kThreads), 0, s, a);
     else if (a.r_kmajor)
-      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, false, true>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, D, BUF, false, true>), grid, dim3(kThreads), 0, s, a);
     else
-      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, false, false>), grid, dim3(kThreads), 0, s, a);
+      hipLaunchKernelGGL((gemm_kernel<DT, BM, BN, BKU, D, BUF, false, false>), grid, dim3(kThreads), 0, s, a);
   }
   return (int)hipGetLastError();
 }
@@ -161,13 +232,56 @@ bool deep_k(int64_t K, int64_t blocks) {
   return (blocks <= 512 && stages >= 16) || (blocks <= 64 && stages >= 4);
 }
 
+// Stage shape of a launch, BKU x D (K units per stage x stages in flight):
+// 4 x 1 for the small tiles above; two units per stage with two stages in
+// flight for the other tiles up to 64 x 128 once K has 8 units or more (the
+// loads of four units stay in flight across the MMAs: measured 15-18%
+// faster on the 1000-row int8 FFN and QKV Gemms); 1 x 1 otherwise (128 x 128
+// would lose an occupancy level to the registers of a second stage).
+// OX_GEMM_STAGES ("1x1", "4x1", "2x2") pins one for any tile (measurements).
 template <int DT, int BM, int BN>
-int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
+int gemm_stages(const GemmArgs& a) {
+  if (const char* e = getenv("OX_GEMM_STAGES")) {
+    static const char* names[] = {"1x1", "4x1", "2x2"};
+    for (int i = 0; i < 3; ++i)
+      if (!strcmp(e, names[i])) return i;
+  }
   if constexpr (deep_k_tile<DT, BM, BN>()) {
     const int64_t blocks = (int64_t)((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) * a.batch;
-    if (deep_k<DT>(a.K, blocks)) return launch_gemm_tile_k<DT, BM, BN, 4>(a, s);
+    if (deep_k<DT>(a.K, blocks)) return 1;
   }
-  return launch_gemm_tile_k<DT, BM, BN, 1>(a, s);
+  constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
+  if (BM * BN <= 64 * 128 && (a.K + KSTEP1 - 1) / KSTEP1 >= 8) return 2;
+  return 0;
+}
+
+// Whether the branch-free buffer loaders apply: a K-contiguous operand needs
+// 16-byte aligned rows and K a multiple of 16 bytes; a K-strided one fp32
+// elements (narrower ones would be widened in registers that are still
+// loading); every byte offset a block forms from its base stays below 2^31.
+template <int DT, int BM, int BN>
+bool gemm_buf_ok(const GemmArgs& a) {
+  const int64_t es = sizeof(typename Traits<DT>::T), lim = (int64_t)1 << 31;
+  const int64_t kb = (int64_t)a.K * es;
+  auto side = [&](bool kmajor, int vec, int64_t ld, int tile) {
+    return kmajor ? vec && kb % 16 == 0 && tile * ld * es + kb < lim
+                  : es == 4 && kb * ld + tile * es < lim;
+  };
+  return side(DT == DT_I8 || a.l_kmajor, a.l_vec, a.ldl, BM) &&
+         side(DT == DT_I8 || a.r_kmajor, a.r_vec, a.ldr, BN);
+}
+
+template <int DT, int BM, int BN>
+int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
+  const int st = gemm_stages<DT, BM, BN>(a);
+  if (!gemm_buf_ok<DT, BM, BN>(a))
+    return st == 1 ? launch_gemm_tile_k<DT, BM, BN, 4, 1, false>(a, s)
+                   : launch_gemm_tile_k<DT, BM, BN, 1, 1, false>(a, s);
+  switch (st) {
+    case 1: return launch_gemm_tile_k<DT, BM, BN, 4, 1, true>(a, s);
+    case 2: return launch_gemm_tile_k<DT, BM, BN, 2, 2, true>(a, s);
+    default: return launch_gemm_tile_k<DT, BM, BN, 1, 1, true>(a, s);
+  }
 }
 
 // ---------------------------------------------------- split-K float Gemm --
@@ -339,10 +453,17 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
   int ks[WaveTile<DT, BM, BN>::FN] = {};
   engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0>(la, lb, K, smem, acc, ks);
 
-  auto out_index = [&](int m, int col) -> int64_t {
+  constexpr int FM = BM / 32, FN = BN / 32;
+  // Y[img, m, p] of output pixel col = img*HoWo + p sits at cb + m*HoWo,
+  // cb = img*M*HoWo + p: one base per lane column (clamped into range)
+  int64_t cbase[FN];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int col = min(col0 + lane_col<BN>(fn), NP - 1);
     const int im = col / HoWo;
-    return ((int64_t)im * a.M + m) * HoWo + (col - im * HoWo);
-  };
+    cbase[fn] = (int64_t)im * a.M * HoWo + (col - im * HoWo);
+  }
+  auto out_index = [&](int m, int fn) -> int64_t { return cbase[fn] + (int64_t)m * HoWo; };
   if constexpr (DT == DT_I8) {
     // weight zero points: acc -= w_zp[m] * sum over the pixel's taps of
     // (x - x_zp) (padding taps hold x_zp: zero), the column sums completed in
@@ -356,48 +477,73 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
     // under FLIP the loader's zeros past K were summed as -128 each
     constexpr int KSTEP = BKU * 4 * Traits<DT>::EPC;
     const int kzx = K * q.xzp - (FLIP ? 128 * ((K + KSTEP - 1) / KSTEP * KSTEP - K) : 0);
-    auto full = [&](int v, int c, int m) -> int {
-      uint32_t u = (uint32_t)v + (uint32_t)q.bias[m];
-      if constexpr (WZ) u -= (uint32_t)q.wzp[m] * (uint32_t)(S[c] - kzx);
-      return (int)u;
-    };
-    if (a.out_dt == DT_I32) {
-      int32_t* Y = (int32_t*)a.Y;
-      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
-        const int ml = row0 + r, col = col0 + c;
-        if (ml < Mpg && col < NP) {
-          const int m = g * Mpg + ml;
-          Y[out_index(m, col)] = full(v, c, m);
+    // one row fragment at a time: its four channels' parameters are read
+    // before its stores (loads behind earlier stores would wait for them)
+    const bool i32 = a.out_dt == DT_I32;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      int rb[4], rw[4];
+      double rm[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = g * Mpg + min(row0 + lane_row<BM>(fm, i), Mpg - 1);
+        rb[i] = q.bias[m];
+        rw[i] = WZ ? q.wzp[m] : 0;
+        rm[i] = q.mult[m];
+      }
+      wait_vmem();
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int ml = row0 + lane_row<BM>(fm, i), c = lane_col<BN>(fn), col = col0 + c;
+          if (ml < Mpg && col < NP) {
+            uint32_t u = (uint32_t)acc[fm][fn][i] + (uint32_t)rb[i];
+            if constexpr (WZ) u -= (uint32_t)rw[i] * (uint32_t)(S[c] - kzx);
+            const int64_t o = out_index(g * Mpg + ml, fn);
+            if (i32) ((int32_t*)a.Y)[o] = (int)u;
+            else ((int8_t*)a.Y)[o] = (int8_t)(requant((int)u, rm[i], q.yzp) ^ q.ym);
+          }
         }
-      });
-    } else {
-      int8_t* Y = (int8_t*)a.Y;
-      for_each_result<BM, BN>(acc, [&](int r, int c, int v) {
-        const int ml = row0 + r, col = col0 + c;
-        if (ml < Mpg && col < NP) {
-          const int m = g * Mpg + ml;
-          Y[out_index(m, col)] = q.out(full(v, c, m), m);
-        }
-      });
     }
   } else {
     T* Y = (T*)a.Y;
     const T* bias = (const T*)a.bias;
     const T* R = (const T*)a.res;     // residual, added after the bias (may be Y itself)
-    with_act(a.act, [&](auto act_k) {
-      constexpr int ACT = decltype(act_k)::value;
-      for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
-        const int ml = row0 + r, col = col0 + c;
-        if (ml < Mpg && col < NP) {
-          const int m = g * Mpg + ml;
-          const int64_t o_idx = out_index(m, col);
-          float o = v;
-          if (bias) o += to_f32(bias[m]);
-          if (R) o += to_f32(R[o_idx]);
-          store_float(Y + o_idx, act_c<ACT>(o));
+    // one row fragment at a time: its four channels' biases are read before
+    // its stores.  (A residual, rare on this kernel, is read element by
+    // element before each store: R may be Y, and hoisting more of its loads
+    // costs the kernel its occupancy in registers.)
+    auto body = [&](auto with_res) {
+      constexpr bool RES = decltype(with_res)::value;
+      with_act(a.act, [&](auto act_k) {
+        constexpr int ACT = decltype(act_k)::value;
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) {
+          float rb[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            rb[i] = bias ? to_f32(bias[g * Mpg + min(row0 + lane_row<BM>(fm, i), Mpg - 1)]) : 0.0f;
+          if constexpr (!RES) wait_vmem();
+#pragma unroll
+          for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int ml = row0 + lane_row<BM>(fm, i), col = col0 + lane_col<BN>(fn);
+              if (ml < Mpg && col < NP) {
+                const int64_t o_idx = out_index(g * Mpg + ml, fn);
+                float o = acc[fm][fn][i];
+                if (bias) o += rb[i];
+                if constexpr (RES) o += to_f32(R[o_idx]);
+                store_float(Y + o_idx, act_c<ACT>(o));
+              }
+            }
+          }
         }
       });
-    });
+    };
+    if (R) body(std::true_type{});
+    else body(std::false_type{});
   }
 }
 

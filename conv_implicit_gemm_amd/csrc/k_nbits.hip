@@ -95,10 +95,17 @@ __global__ __launch_bounds__(kThreads) void nbits_gemm_kernel(const NBitsArgs a)
 
   uint16_t* Y = (uint16_t*)a.Y;
   const uint16_t* bias = (const uint16_t*)a.bias;
-  for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
+  // the lane's columns' biases, read before any store (a load behind a
+  // store would wait for it)
+  float bc[BN / 32];
+#pragma unroll
+  for (int fn = 0; fn < BN / 32; ++fn)
+    bc[fn] = bias ? bf16_to_f32(bias[min(col0 + lane_col<BN>(fn), a.N - 1)]) : 0.0f;
+  wait_vmem();
+  for_each_result_fn<BM, BN>(acc, [&](int fn, int r, int c, float v) {
     const int row = row0 + r, col = col0 + c;
     if (row < a.M && col < a.N) {
-      if (bias) v += bf16_to_f32(bias[col]);
+      if (bias) v += bc[fn];
       Y[(int64_t)row * a.ldy + col] = f32_to_bf16(v);
     }
   });

@@ -76,6 +76,7 @@ struct GemmArgs {
   int act;
   const void* i8;         // int8 parameter block (int8 path), channel = col
   int l_vec, r_vec;       // 16-byte vector loads allowed for a K-major operand
+  int tile_group;         // row tiles per group of the block -> tile order (set at launch)
 };
 
 // A convolution (NCHW) on the tile engine: rows = output channels of one

@@ -204,6 +204,63 @@ def test_gemm_empty_reduction_writes_activation_of_bias(ox):
     assert np.array_equal(host64(Y), np.broadcast_to(oracle.act("relu6", bias), (4, 3)))
 
 
+GEMM_STAGES = ["1x1", "4x1", "2x2"]
+GEMM_TILES = ["128x128", "64x128", "128x64", "64x64", "32x64"]
+
+
+@pytest.mark.parametrize("stages", GEMM_STAGES)
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gemm_stage_shapes(ox, stages, dtype, monkeypatch):
+    # every stage shape (K units per stage x stages in flight) on every tile
+    # and operand layout: K of one stage, of fewer stages than are kept in
+    # flight, and of many with a ragged tail; rows and columns past the
+    # operands; one output row
+    monkeypatch.setenv("OX_GEMM_STAGES", stages)
+    r = np.random.default_rng(260 + GEMM_STAGES.index(stages) + (dtype == "bf16"))
+    for tile in GEMM_TILES:
+        monkeypatch.setenv("OX_FORCE_KERNEL", "mfma,tile=" + tile)
+        for (M, N, K) in [(150, 140, 1000), (70, 130, 40), (33, 200, 392), (1, 70, 520)]:
+            for ta, tb in [(0, 1), (0, 0), (1, 1), (1, 0)]:
+                say("gemm stages", stages, tile, dtype, (M, N, K), ta, tb)
+                A = synth.round_to(r.standard_normal((K, M) if ta else (M, K)), dtype)
+                B = synth.round_to(r.standard_normal((N, K) if tb else (K, N)) / math.sqrt(K), dtype)
+                bias = synth.round_to(r.uniform(-1, 1, N), dtype)
+                Y = nan_like((M, N), dtype)
+                ox.ox_gemm_fused(dev(A, dtype), dev(B, dtype), dev(bias, dtype), alpha=0.5, beta=-2.0,
+                                 transA=bool(ta), transB=bool(tb), act="relu", Y=Y)
+                torch.cuda.synchronize()
+                ref = oracle.gemm(A, B, bias, 0.5, -2.0, ta, tb, "relu")
+                assert_close(host64(Y), ref, dtype, "gemm %s %s %s" % (stages, tile, (M, N, K, ta, tb)))
+
+
+@pytest.mark.parametrize("stages", GEMM_STAGES)
+def test_qgemm_stage_shapes_bit_exact(ox, stages, monkeypatch):
+    # the int8 Gemm under every stage shape and tile, with uint8 activations
+    # (flipped on their way to LDS) and weight zero points (row sums taken
+    # from the staged operand)
+    monkeypatch.setenv("OX_GEMM_STAGES", stages)
+    r = np.random.default_rng(280 + GEMM_STAGES.index(stages))
+    for tile in GEMM_TILES:
+        monkeypatch.setenv("OX_FORCE_KERNEL", "mfma,tile=" + tile)
+        for (xu, yu, wz) in [(True, False, True), (False, True, False)]:
+            for (M, K, N) in [(150, 1088, 140), (77, 64, 45), (40, 448, 70)]:
+                say("qgemm stages", stages, tile, (xu, yu, wz), (M, K, N))
+                x, w, wzp, xzp, bq, x_s, w_s = q_inputs(r, xu, wz, (M, K), (N, K))
+                acc0, _ = oracle.qgemm(x, w, bq, xzp, wzp, x_s, w_s, 1.0, 0)
+                y_s = q_out_scale(acc0, x_s, w_s)
+                yzp = int(r.integers(0, 256)) if yu else int(r.integers(-128, 128))
+                acc, y = oracle.qgemm(x, w, bq, xzp, wzp, x_s, w_s, y_s, yzp, yu)
+                blk = ox.ox_int8_prepare(w, w_s, x_s, xzp, y_s, yzp, bq, w_zp=wzp, x_unsigned=xu,
+                                         y_unsigned=yu)
+
+                def call(xd, wd, bd, yt):
+                    od = {"i32": torch.int32, "u8": torch.uint8, "i8": torch.int8}[yt]
+                    return ox.ox_gemm_fused(xd, wd, transB=True, int8_params=bd, out_dtype=od)
+                g32, g8 = q_run(ox, blk, x, xu, w, yu, call)
+                assert np.array_equal(g32, acc), (stages, tile, M, K, N)
+                assert np.array_equal(g8, y), (stages, tile, M, K, N)
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_c1_mlp_rows(ox, dtype):
     # every row through the plain Gemm and through the split-K Gemm with a
