@@ -445,6 +445,15 @@ struct LoadColKB {
     ldb = (uint32_t)(ld * 4);
     K = K_;
   }
+  // the same with this thread's column given as a byte offset from base
+  // (the columns of a block need not be evenly spaced)
+  __device__ __forceinline__ void init_off(const T* base, uint32_t off, bool ok, int64_t ld, int K_) {
+    rs = operand_rsrc(base);
+    valid = ok;
+    vo = off;
+    ldb = (uint32_t)(ld * 4);
+    K = K_;
+  }
   __device__ __forceinline__ void load(int k0) {
     const int ch0 = threadIdx.x / BCOLS;
     const int soff = k0 * (int)ldb;

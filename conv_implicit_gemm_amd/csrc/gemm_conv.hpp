@@ -399,9 +399,11 @@ int launch_gemm_dt(const GemmArgs& a, int tile, void* stream) {
 // rows = output channels of group z (L = weights [M/g, K], K contiguous),
 // cols = output pixels over the batch, n = (img*Ho + oh)*Wo + ow.
 // KIND 0: implicit GEMM (im2col gathered on the fly); KIND 1: 1x1, stride 1,
-// no pad, where column n of image img is X[img, c, p] with p = n % (H*W).
+// no pad, where column n of image img is X[img, c, p] with p = n % (H*W);
+// KIND 2: the same 1x1 through the branch-free buffer loaders with D stages
+// in flight (fp32 operands whose byte offsets stay below 2^31).
 
-template <int DT, int BM, int BN, int BKU, int KIND, bool FLIP, bool WZ>
+template <int DT, int BM, int BN, int BKU, int KIND, bool FLIP, bool WZ, int D = 1>
 __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I8View& q) {
   typedef typename Traits<DT>::T T;
   typedef typename Traits<DT>::Acc Acc;
@@ -411,6 +413,25 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
   const int KK = a.kH * a.kW, K = cpg * KK;
   const int HoWo = a.Ho * a.Wo, HW = a.H * a.W, NP = a.N * HoWo;
 
+  Acc acc[BM / 32][BN / 32];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i)
+#pragma unroll
+    for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
+  int ks[WaveTile<DT, BM, BN>::FN] = {};
+
+  if constexpr (KIND == 2) {
+    LoadRowKB<DT, BM, BKU> la;
+    la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K);
+    LoadColKB<DT, BN, BKU, FLIP> lb;
+    const int n = col0 + threadIdx.x % BN;
+    const bool nvalid = n < NP;
+    const int img = nvalid ? n / HoWo : 0;
+    const uint32_t off = (uint32_t)((((int64_t)img * a.C + (int64_t)g * cpg) * HW + (n - img * HoWo)) *
+                                    (int64_t)sizeof(T));
+    lb.init_off((const T*)a.X, nvalid ? off : 0u, nvalid, HW, K);
+    engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0, D>(la, lb, K, smem, acc, ks);
+  } else {
   LoadRowK<DT, BM, BKU> la;
   la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K, a.w_vec);
 
@@ -444,14 +465,8 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
     else lb.pad = (T)0;
   }
 
-  Acc acc[BM / 32][BN / 32];
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i)
-#pragma unroll
-    for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
-
-  int ks[WaveTile<DT, BM, BN>::FN] = {};
   engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0>(la, lb, K, smem, acc, ks);
+  }
 
   constexpr int FM = BM / 32, FN = BN / 32;
   // Y[img, m, p] of output pixel col = img*HoWo + p sits at cb + m*HoWo,
@@ -547,7 +562,7 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
   }
 }
 
-template <int DT, int BM, int BN, int BKU, int KIND>
+template <int DT, int BM, int BN, int BKU, int KIND, int D = 1>
 __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * Lds<BKU>::ROWB];
   I8View q;
@@ -555,37 +570,70 @@ __global__ __launch_bounds__(kThreads) void conv_kernel(const ConvArgs a) {
     q.init(a.i8);
     // uniform per launch: one of four instantiations runs
     if (q.xm) {
-      if (q.wz) conv_tile<DT, BM, BN, BKU, KIND, true, true>(a, smem, q);
-      else conv_tile<DT, BM, BN, BKU, KIND, true, false>(a, smem, q);
+      if (q.wz) conv_tile<DT, BM, BN, BKU, KIND, true, true, D>(a, smem, q);
+      else conv_tile<DT, BM, BN, BKU, KIND, true, false, D>(a, smem, q);
     } else {
-      if (q.wz) conv_tile<DT, BM, BN, BKU, KIND, false, true>(a, smem, q);
-      else conv_tile<DT, BM, BN, BKU, KIND, false, false>(a, smem, q);
+      if (q.wz) conv_tile<DT, BM, BN, BKU, KIND, false, true, D>(a, smem, q);
+      else conv_tile<DT, BM, BN, BKU, KIND, false, false, D>(a, smem, q);
     }
   } else {
-    conv_tile<DT, BM, BN, BKU, KIND, false, false>(a, smem, q);
+    conv_tile<DT, BM, BN, BKU, KIND, false, false, D>(a, smem, q);
   }
 }
 
-template <int DT, int BM, int BN, int BKU>
+template <int DT, int BM, int BN, int BKU, int D = 1>
 int launch_conv_tile_k(const ConvArgs& a, int kind, hipStream_t s) {
   const int Mpg = a.M / a.group;
   const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
   dim3 grid((unsigned)((NP + BN - 1) / BN), (Mpg + BM - 1) / BM, a.group);
-  if (kind == 1)
-    hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 1>), grid, dim3(kThreads), 0, s, a);
-  else
-    hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 0>), grid, dim3(kThreads), 0, s, a);
+  if constexpr (D > 1) {
+    hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2, D>), grid, dim3(kThreads), 0, s, a);
+  } else {
+    if constexpr (DT == DT_F32)
+      if (kind == 2) {
+        hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2>), grid, dim3(kThreads), 0, s, a);
+        return (int)hipGetLastError();
+      }
+    if (kind == 1)
+      hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 1>), grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 0>), grid, dim3(kThreads), 0, s, a);
+  }
   return (int)hipGetLastError();
+}
+
+// Whether a 1x1 convolution takes the buffer loaders (KIND 2): fp32, weight
+// rows of whole 16-byte vectors, X below 2^31 bytes.  OX_CONV_PIPE=0 turns
+// it off (measurements).
+template <int DT>
+bool conv_buf_ok(const ConvArgs& a) {
+  if (DT != DT_F32 || !a.w_vec) return false;
+  if (const char* e = getenv("OX_CONV_PIPE"))
+    if (!strcmp(e, "0")) return false;
+  return (int64_t)a.N * a.C * a.H * a.W * 4 < ((int64_t)1 << 31);
 }
 
 template <int DT, int BM, int BN>
 int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
-  if constexpr (deep_k_tile<DT, BM, BN>()) {
-    const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
-    const int64_t blocks = ((NP + BN - 1) / BN) * ((a.M / a.group + BM - 1) / BM) * a.group;
-    if (deep_k<DT>((int64_t)(a.C / a.group) * a.kH * a.kW, blocks))
-      return launch_conv_tile_k<DT, BM, BN, 4>(a, kind, s);
+  const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
+  const int64_t blocks = ((NP + BN - 1) / BN) * ((a.M / a.group + BM - 1) / BM) * a.group;
+  const int64_t K = (int64_t)(a.C / a.group) * a.kH * a.kW;
+  bool deep = false;
+  if constexpr (deep_k_tile<DT, BM, BN>()) deep = deep_k<DT>(K, blocks);
+  if constexpr (DT == DT_F32) {
+    if (kind == 1 && conv_buf_ok<DT>(a)) {
+      // the stage shapes of the Gemm: 4 x 1 where the small tiles go deep,
+      // 2 x 2 for tiles up to 64 x 128 with 8 or more K units
+      constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
+      if constexpr (deep_k_tile<DT, BM, BN>())
+        if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, 2, s);
+      if constexpr (BM * BN <= 64 * 128)
+        if ((K + KSTEP1 - 1) / KSTEP1 >= 8) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, 2, s);
+      return launch_conv_tile_k<DT, BM, BN, 1>(a, 2, s);
+    }
   }
+  if constexpr (deep_k_tile<DT, BM, BN>())
+    if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, kind, s);
   return launch_conv_tile_k<DT, BM, BN, 1>(a, kind, s);
 }
 
