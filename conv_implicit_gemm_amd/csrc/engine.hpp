@@ -732,6 +732,37 @@ __device__ __forceinline__ void for_each_result(const Acc (&acc)[BM / 32][BN / 3
 // would otherwise be preceded by a wait for every earlier store as well.
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Writes a BM x BN tile of a row-major output through LDS: put(E, EROW)
+// stores each of this lane's results at E[row_in_tile * EROW + col_in_tile]
+// (E = smem + OFF bytes), then each thread copies 16-byte pieces of the
+// rows to Y (row0, col0: the tile's origin; rows / cols: Y's extent).  The
+// caller checks that the staging area fits, that Y and its row stride keep
+// every piece 16-byte aligned and that cols is a multiple of a piece, and
+// that LDS is free (every wave is past its last read of the operands).
+template <typename Y_T, int BM, int BN, int OFF, class Put>
+__device__ __forceinline__ void store_tile_rows(Y_T* Y, int64_t ldy, int row0, int col0, int rows, int cols,
+                                                char* smem, Put&& put) {
+  constexpr int V = 16 / (int)sizeof(Y_T), EROW = BN + V, PR = BN / V;
+  Y_T* E = (Y_T*)(smem + OFF);
+  put(E, EROW);
+  __syncthreads();
+#pragma unroll
+  for (int it = threadIdx.x; it < BM * PR; it += kThreads) {
+    const int r = it / PR, pc = it - r * PR;
+    const int row = row0 + r, col = col0 + pc * V;
+    if (row < rows && col < cols)
+      *(u32x4_t*)(Y + (int64_t)row * ldy + col) = *(const u32x4_t*)(E + r * EROW + pc * V);
+  }
+}
+template <typename Y_T, int BM, int BN>
+constexpr int stage_rows_bytes() { return BM * (BN + 16 / (int)sizeof(Y_T)) * (int)sizeof(Y_T); }
+// whether Y (this batch's matrix) takes store_tile_rows
+template <typename Y_T>
+__device__ __forceinline__ bool rows_vec_ok(const Y_T* Y, int64_t ldy, int cols) {
+  constexpr int V = 16 / (int)sizeof(Y_T);
+  return ((uintptr_t)Y) % 16 == 0 && ldy % V == 0 && cols % V == 0;
+}
+
 // As for_each_result, with the lane's column fragment fn passed first: the
 // lane's columns are lane_col<BN>(fn), fn < BN/32, so that per-column values
 // can be read into registers before the first store (loads after stores

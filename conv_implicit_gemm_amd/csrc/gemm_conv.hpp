@@ -110,9 +110,38 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, const I
     // one column fragment at a time: its parameters are read before its
     // stores (loads behind earlier stores would wait for those stores)
     constexpr int FM = BM / 32, FN = BN / 32;
+    constexpr int SMEM = 2 * (BM + BN) * Lds<BKU>::ROWB, SOFF = (BM * 4 + 15) / 16 * 16;
     auto out = [&](auto yk) {
       typedef typename decltype(yk)::type Y_T;
       Y_T* Y = (Y_T*)a.Y + (int64_t)z * a.sy;
+      if constexpr (SOFF + stage_rows_bytes<Y_T, BM, BN>() <= SMEM) {
+        // through LDS (after the row sums S), whole-row 16-byte stores
+        if (rows_vec_ok(Y, a.ldy, a.cols)) {
+          if constexpr (!WZ) __syncthreads();   // (WZ: the row sums' barrier did it)
+          store_tile_rows<Y_T, BM, BN, SOFF>(Y, a.ldy, row0, col0, a.rows, a.cols, smem, [&](Y_T* E, int EROW) {
+#pragma unroll
+            for (int fn = 0; fn < FN; ++fn) {
+              const int c = lane_col<BN>(fn), cc = min(col0 + c, a.cols - 1);
+              const int cb = q.bias[cc], cw = WZ ? q.wzp[cc] : 0;
+              const double cm = std::is_same<Y_T, int8_t>::value ? q.mult[cc] : 0.0;
+              wait_vmem();
+#pragma unroll
+              for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  const int r = lane_row<BM>(fm, i);
+                  uint32_t u = (uint32_t)acc[fm][fn][i] + (uint32_t)cb;
+                  if constexpr (WZ) u -= (uint32_t)cw * (uint32_t)(S[r] - kzx);
+                  if constexpr (std::is_same<Y_T, int8_t>::value)
+                    E[r * EROW + c] = (int8_t)(requant((int)u, cm, q.yzp) ^ q.ym);
+                  else
+                    E[r * EROW + c] = (int)u;
+                }
+            }
+          });
+          return;
+        }
+      }
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn) {
         const int col = col0 + lane_col<BN>(fn), cc = min(col, a.cols - 1);
@@ -147,6 +176,24 @@ __device__ __forceinline__ void gemm_tile(const GemmArgs& a, char* smem, const I
     for (int fn = 0; fn < FN; ++fn)
       bc[fn] = bias ? a.beta * to_f32(bias[min(col0 + lane_col<BN>(fn), a.cols - 1)]) : 0.0f;
     wait_vmem();
+    constexpr int SMEM = 2 * (BM + BN) * Lds<BKU>::ROWB;
+    if constexpr (stage_rows_bytes<T, BM, BN>() <= SMEM) {
+      // through LDS, whole-row 16-byte stores
+      if (rows_vec_ok(Y, a.ldy, a.cols)) {
+        __syncthreads();
+        with_act(a.act, [&](auto act_k) {
+          constexpr int ACT = decltype(act_k)::value;
+          store_tile_rows<T, BM, BN, 0>(Y, a.ldy, row0, col0, a.rows, a.cols, smem, [&](T* E, int EROW) {
+            for_each_result_fn<BM, BN>(acc, [&](int fn, int r, int c, float v) {
+              float o = a.alpha * v;
+              if (bias) o += bc[fn];
+              store_float(E + r * EROW + c, act_c<ACT>(o));
+            });
+          });
+        });
+        return;
+      }
+    }
     with_act(a.act, [&](auto act_k) {
       constexpr int ACT = decltype(act_k)::value;
       for_each_result_fn<BM, BN>(acc, [&](int fn, int r, int c, float v) {
