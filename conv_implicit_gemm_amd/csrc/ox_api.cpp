@@ -237,6 +237,13 @@ bool pwd_preferred(const ConvArgs& a) {
   return (a.C % 64 == 0 || (int64_t)a.N * a.H * a.W >= 65536) && conv_pwd_applicable(a);
 }
 
+// The register-staged 1x1 kernel, except on an odd plane with a short K: its
+// channel runs are then single pixels and the tile engine's kernel is faster
+// (measured 1.37-1.39x on 160->960 channels at 7x7).
+bool pw_preferred(const ConvArgs& a) {
+  return !((a.H * a.W) % 2 == 1 && a.C <= 192) && conv_pw_applicable(a);
+}
+
 ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, const Force& f,
                       int* kind) {
   if (a.w_packed) {
@@ -300,13 +307,13 @@ ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, 
   if (a.res) {
     // a residual input: the kernels whose epilogue reads it are the
     // pointwise kernel and the tile engine (any geometry)
-    if (is_1x1) *kind = pwd_preferred(a) ? KIND_PWD : conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
+    if (is_1x1) *kind = pwd_preferred(a) ? KIND_PWD : pw_preferred(a) ? KIND_PW : KIND_1X1;
     else *kind = KIND_IGEMM;
     return OX_OK;
   }
   if (is_dw && depthwise_rows_applicable(a)) *kind = KIND_DWR;
   else if (is_dw && depthwise_fits(a)) *kind = KIND_DW;
-  else if (is_1x1) *kind = pwd_preferred(a) ? KIND_PWD : conv_pw_applicable(a) ? KIND_PW : KIND_1X1;
+  else if (is_1x1) *kind = pwd_preferred(a) ? KIND_PWD : pw_preferred(a) ? KIND_PW : KIND_1X1;
   else if (conv_patch_applicable(a)) *kind = KIND_PATCH;
   else if (conv_smallc_applicable(a)) *kind = KIND_SMALLC;
   else *kind = KIND_IGEMM;

@@ -138,8 +138,14 @@ def test_variant_selection_sweep(ox, monkeypatch):
         if dt == "bf16" and g == 1 and k == 1 and s == 1 and C % 32 == 0:
             # the DMA-staged kernel where the plane has an even pixel count
             # (the fake pointers are aligned) and C is a multiple of 64 or the
-            # layer has at least 65536 pixels, else the register-staged one
-            want = "pwd/" if (H * W) % 2 == 0 and (C % 64 == 0 or N * H * W >= 65536) else "pw/"
+            # layer has at least 65536 pixels, else the register-staged one,
+            # except on an odd plane with C <= 192 (the tile engine's 1x1)
+            if (H * W) % 2 == 0 and (C % 64 == 0 or N * H * W >= 65536):
+                want = "pwd/"
+            elif (H * W) % 2 == 1 and C <= 192:
+                want = "1x1/"
+            else:
+                want = "pw/"
             assert name.startswith(want), (name, C, M, H, W)
         if dt == "bf16" and g == 1 and k == 3 and C % 32 == 0:
             assert name.startswith("patch/"), (name, C, M, H, W, s)
@@ -148,11 +154,17 @@ def test_variant_selection_sweep(ox, monkeypatch):
         if g == C and M == C and k == 3 and dt != "i8":
             # depthwise 3x3, pads 1: the row-segment kernel where it applies
             assert name.startswith("dwr/") == dwr_applies(dt, W, s), (name, dt, H, W, s)
-    # pinned split-K counts, including more slices than chunks
+    # pinned split-K counts, including more slices than chunks (short K on
+    # this odd plane takes the tile engine unless pw is asked for)
     for splits in ("1", "2", "7", "64"):
         monkeypatch.setenv("OX_PW_SPLITS", splits)
         for C in (32, 64, 96, 2048):
+            want = "pw/" if C > 192 else "1x1/"
+            assert ox.ox_conv2d_variant("bf16", 2, C, 7, 7, 512, 1, 1).startswith(want)
+        monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
+        for C in (32, 64, 96):
             assert ox.ox_conv2d_variant("bf16", 2, C, 7, 7, 512, 1, 1).startswith("pw/")
+        monkeypatch.delenv("OX_FORCE_KERNEL")
 
 
 def test_workspace_entry_point(ox):
