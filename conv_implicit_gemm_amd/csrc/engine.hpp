@@ -478,6 +478,68 @@ struct LoadColKB {
   }
 };
 
+// [K, cols] int8 operand whose columns come in aligned groups of four
+// consecutive bytes (a 1x1 convolution's pixels, the plane a multiple of
+// four): a task is one group of four columns and one 16-k chunk, loaded as
+// sixteen 4-byte words (one per k, four columns each, coalesced across the
+// lanes) and transposed into the four columns' 16-byte chunks by byte
+// permutes when written to LDS.  Group g's byte offset from base is given
+// per thread (kPastK: the group lies past the operand).
+template <int BCOLS, int BKU, bool FLIP = false>
+struct LoadColK4B {
+  enum { CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB, G = BCOLS / 4,
+         TOTAL = G * CPR, NCH = (TOTAL + kThreads - 1) / kThreads };
+  static_assert(BCOLS % 4 == 0 && kThreads % G == 0, "column groups must tile the block");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo;          // this thread's column group at k = 0, or kPastK
+  uint32_t ld;          // row stride in bytes
+  int K;
+  uint32_t d[NCH][16];
+
+  __device__ __forceinline__ void init_off(const int8_t* base, uint32_t off, bool ok, int64_t ld_, int K_) {
+    rs = operand_rsrc(base);
+    vo = ok ? off : kPastK;
+    ld = (uint32_t)ld_;
+    K = K_;
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int soff = k0 * (int)ld;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int t = threadIdx.x + i * kThreads, ch = t / G;
+      const bool task = TOTAL % kThreads == 0 || t < TOTAL;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int kk = ch * 16 + e;
+        const bool ok = task && vo != kPastK && k0 + kk < K;
+        d[i][e] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? vo + kk * ld : kPastK, soff, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int t = threadIdx.x + i * kThreads, ch = t / G, grp = t - ch * G;
+      if (TOTAL % kThreads == 0 || t < TOTAL) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          // byte j of each word: column 4*grp + j, k = 16ch .. 16ch+15
+          const uint32_t sel2 = (uint32_t)j | ((uint32_t)(4 + j) << 8) | 0x0c0c0000u;
+          uint32_t w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t lo = __builtin_amdgcn_perm(d[i][4 * q + 1], d[i][4 * q], sel2);
+            const uint32_t hi = __builtin_amdgcn_perm(d[i][4 * q + 3], d[i][4 * q + 2], sel2);
+            w[q] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+          }
+          *(u32x4_t*)(lds + (4 * grp + j) * ROWB + ch * 16) =
+              flip_chunk<DT_I8, FLIP>(u32x4_t{w[0], w[1], w[2], w[3]});
+        }
+      }
+    }
+  }
+};
+
 // The implicit-GEMM operand of a convolution: column = one output pixel
 // (img, oh, ow), k = (c, kh, kw) in the weight's own order, element =
 // X[img, c, oh*sh - pt + kh*dh, ow*sw - pl + kw*dw], or `pad` outside the

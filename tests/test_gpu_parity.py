@@ -1033,6 +1033,39 @@ def test_qconv_variants_bit_exact(ox, xu, yu, wz):
         assert np.array_equal(g8, y), geom
 
 
+@pytest.mark.parametrize("xu,yu,wz", QVARIANTS)
+def test_qconv_1x1_buffer_path_bit_exact(ox, xu, yu, wz, monkeypatch):
+    # int8 1x1 convolutions on planes of whole 4-byte groups take the buffer
+    # loaders (sixteen 4-column words per task, transposed into k-chunks in
+    # LDS) with the Gemm's stage shapes: every tile, ragged channels and
+    # pixel ranges, tiles straddling images, K tails, against the oracle and
+    # against the gathering loader (OX_CONV_PIPE=0)
+    r = np.random.default_rng(870 + 4 * xu + 2 * yu + wz)
+    for tile in GEMM_TILES:
+        for (N, Cin, H, W, M) in [(3, 48, 4, 7, 40), (1, 1024, 1, 1000, 72), (2, 64, 8, 8, 96),
+                                  (2, 272, 2, 6, 130)]:
+            geom = (N, Cin, H, W, M, 1, 1, 1, (0, 0, 0, 0), 1, 1)
+            say("qconv 1x1 buffer", tile, (xu, yu, wz), geom)
+            x, w, wzp, xzp, bq, x_s, w_s = q_inputs(r, xu, wz, (N, Cin, H, W), (M, Cin, 1, 1))
+            args = ((1, 1), (0, 0, 0, 0), (1, 1), 1)
+            acc0, _ = oracle.qconv2d(x, w, bq, xzp, wzp, x_s, w_s, 1.0, 0, False, *args)
+            y_s = q_out_scale(acc0, x_s, w_s)
+            yzp = int(r.integers(0, 256)) if yu else int(r.integers(-128, 128))
+            acc, y = oracle.qconv2d(x, w, bq, xzp, wzp, x_s, w_s, y_s, yzp, yu, *args)
+            blk = ox.ox_int8_prepare(w, w_s, x_s, xzp, y_s, yzp, bq, w_zp=wzp, x_unsigned=xu, y_unsigned=yu)
+
+            def call(xd, wd, bd, yt):
+                return ox.ox_conv2d_int8(xd, wd, bd, yt, *args)
+            monkeypatch.setenv("OX_FORCE_KERNEL", "1x1,tile=" + tile)
+            for pipe in ("1", "0"):
+                monkeypatch.setenv("OX_CONV_PIPE", pipe)
+                g32, g8 = q_run(ox, blk, x, xu, w, yu, call)
+                assert np.array_equal(g32, acc), (tile, pipe, geom)
+                assert np.array_equal(g8, y), (tile, pipe, geom)
+            monkeypatch.delenv("OX_CONV_PIPE")
+            monkeypatch.delenv("OX_FORCE_KERNEL")
+
+
 # ----------------------------------------------------------- MatMulNBits --
 
 def nbits_run(ox, t, a_offset=0):
