@@ -478,6 +478,62 @@ struct LoadColKB {
   }
 };
 
+// [K, cols] bf16 operand whose columns come in aligned pairs (a 1x1
+// convolution's pixels, the plane even): a task is one pair of columns and
+// one 8-k chunk, loaded as eight 4-byte words (one per k, both columns,
+// coalesced across the lanes) and split into the two columns' 16-byte
+// chunks by byte permutes when written to LDS.  The pair's byte offset from
+// base is given per thread (kPastK: past the operand).
+template <int BCOLS, int BKU>
+struct LoadColK2B {
+  enum { CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB, G = BCOLS / 2,
+         TOTAL = G * CPR, NCH = (TOTAL + kThreads - 1) / kThreads };
+  static_assert(BCOLS % 2 == 0 && kThreads % G == 0, "column pairs must tile the block");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo;          // this thread's column pair at k = 0, or kPastK
+  uint32_t ldb;         // row stride in bytes
+  int K;
+  uint32_t d[NCH][8];
+
+  __device__ __forceinline__ void init_off(const uint16_t* base, uint32_t off, bool ok, int64_t ld, int K_) {
+    rs = operand_rsrc(base);
+    vo = ok ? off : kPastK;
+    ldb = (uint32_t)(ld * 2);
+    K = K_;
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int soff = k0 * (int)ldb;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int t = threadIdx.x + i * kThreads, ch = t / G;
+      const bool task = TOTAL % kThreads == 0 || t < TOTAL;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int kk = ch * 8 + e;
+        const bool ok = task && vo != kPastK && k0 + kk < K;
+        d[i][e] = __builtin_amdgcn_raw_buffer_load_b32(rs, ok ? vo + kk * ldb : kPastK, soff, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int t = threadIdx.x + i * kThreads, ch = t / G, grp = t - ch * G;
+      if (TOTAL % kThreads == 0 || t < TOTAL) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          // half j of each word: column 2*grp + j, k = 8ch .. 8ch+7
+          const uint32_t sel = j ? 0x07060302u : 0x05040100u;
+          u32x4_t v;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = __builtin_amdgcn_perm(d[i][2 * q + 1], d[i][2 * q], sel);
+          *(u32x4_t*)(lds + (2 * grp + j) * ROWB + ch * 16) = v;
+        }
+      }
+    }
+  }
+};
+
 // [K, cols] int8 operand whose columns come in aligned groups of four
 // consecutive bytes (a 1x1 convolution's pixels, the plane a multiple of
 // four): a task is one group of four columns and one 16-k chunk, loaded as

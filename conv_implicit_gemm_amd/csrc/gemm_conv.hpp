@@ -470,13 +470,17 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
   if constexpr (KIND == 2) {
     LoadRowKB<DT, BM, BKU> la;
     la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K);
-    // this thread's column (fp32) or group of four columns (int8)
-    const int n = col0 + (DT == DT_I8 ? 4 * (threadIdx.x % (BN / 4)) : threadIdx.x % BN);
+    // this thread's column (fp32), pair of columns (bf16) or group of four
+    // columns (int8)
+    constexpr int CG = DT == DT_I8 ? 4 : DT == DT_BF16 ? 2 : 1;
+    const int n = col0 + CG * (threadIdx.x % (BN / CG));
     const bool nvalid = n < NP;
     const int img = nvalid ? n / HoWo : 0;
     const uint32_t off = (uint32_t)((((int64_t)img * a.C + (int64_t)g * cpg) * HW + (n - img * HoWo)) *
                                     (int64_t)sizeof(T));
-    typename std::conditional<DT == DT_I8, LoadColK4B<BN, BKU, FLIP>, LoadColKB<DT, BN, BKU, FLIP>>::type lb;
+    typename std::conditional<DT == DT_I8, LoadColK4B<BN, BKU, FLIP>,
+                              typename std::conditional<DT == DT_BF16, LoadColK2B<BN, BKU>,
+                                                        LoadColKB<DT, BN, BKU, FLIP>>::type>::type lb;
     lb.init_off((const T*)a.X, nvalid ? off : 0u, nvalid, HW, K);
     engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0, D>(la, lb, K, smem, acc, ks);
   } else {
@@ -637,12 +641,9 @@ int launch_conv_tile_k(const ConvArgs& a, int kind, hipStream_t s) {
   if constexpr (D > 1) {
     hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2, D>), grid, dim3(kThreads), 0, s, a);
   } else {
-    if constexpr (DT == DT_F32 || DT == DT_I8)
-      if (kind == 2) {
-        hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2>), grid, dim3(kThreads), 0, s, a);
-        return (int)hipGetLastError();
-      }
-    if (kind == 1)
+    if (kind == 2)
+      hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2>), grid, dim3(kThreads), 0, s, a);
+    else if (kind == 1)
       hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 1>), grid, dim3(kThreads), 0, s, a);
     else
       hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 0>), grid, dim3(kThreads), 0, s, a);
@@ -650,17 +651,18 @@ int launch_conv_tile_k(const ConvArgs& a, int kind, hipStream_t s) {
   return (int)hipGetLastError();
 }
 
-// Whether a 1x1 convolution takes the buffer loaders (KIND 2): fp32, or
-// int8 with planes of whole 4-byte groups and a 4-byte aligned X; weight
-// rows of whole 16-byte vectors; X below 2^31 bytes.  OX_CONV_PIPE=0 turns
-// it off (measurements).
+// Whether a 1x1 convolution takes the buffer loaders (KIND 2): fp32; bf16
+// or int8 with planes of whole 4-byte groups of pixels (2 / 4 of them) and a
+// 4-byte aligned X; weight rows of whole 16-byte vectors; X below 2^31
+// bytes.  OX_CONV_PIPE=0 turns it off (measurements).
 template <int DT>
 bool conv_buf_ok(const ConvArgs& a) {
-  if ((DT != DT_F32 && DT != DT_I8) || !a.w_vec) return false;
-  if (DT == DT_I8 && ((a.H * a.W) % 4 != 0 || ((uintptr_t)a.X) % 4 != 0)) return false;
+  constexpr int ES = DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1;
+  if (!a.w_vec) return false;
+  if (((a.H * a.W * ES) % 4 != 0 || ((uintptr_t)a.X) % 4 != 0)) return false;
   if (const char* e = getenv("OX_CONV_PIPE"))
     if (!strcmp(e, "0")) return false;
-  return (int64_t)a.N * a.C * a.H * a.W * (DT == DT_F32 ? 4 : 1) < ((int64_t)1 << 31);
+  return (int64_t)a.N * a.C * a.H * a.W * ES < ((int64_t)1 << 31);
 }
 
 template <int DT, int BM, int BN>
@@ -670,17 +672,15 @@ int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
   const int64_t K = (int64_t)(a.C / a.group) * a.kH * a.kW;
   bool deep = false;
   if constexpr (deep_k_tile<DT, BM, BN>()) deep = deep_k<DT>(K, blocks);
-  if constexpr (DT == DT_F32 || DT == DT_I8) {
-    if (kind == 1 && conv_buf_ok<DT>(a)) {
-      // the stage shapes of the Gemm: 4 x 1 where the small tiles go deep,
-      // 2 x 2 for tiles up to 64 x 128 with 8 or more K units
-      constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
-      if constexpr (deep_k_tile<DT, BM, BN>())
-        if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, 2, s);
-      if constexpr (BM * BN <= 64 * 128)
-        if ((K + KSTEP1 - 1) / KSTEP1 >= 8) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, 2, s);
-      return launch_conv_tile_k<DT, BM, BN, 1>(a, 2, s);
-    }
+  if (kind == 1 && conv_buf_ok<DT>(a)) {
+    // the stage shapes of the Gemm: 4 x 1 where the small tiles go deep,
+    // 2 x 2 for tiles up to 64 x 128 with 8 or more K units
+    constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
+    if constexpr (deep_k_tile<DT, BM, BN>())
+      if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, 2, s);
+    if constexpr (BM * BN <= 64 * 128)
+      if ((K + KSTEP1 - 1) / KSTEP1 >= 8) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, 2, s);
+    return launch_conv_tile_k<DT, BM, BN, 1>(a, 2, s);
   }
   if constexpr (deep_k_tile<DT, BM, BN>())
     if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, kind, s);

@@ -314,6 +314,33 @@ def run_conv(ox, X, Wt, b, dtype, s, pads, d, g, act, ws=False):
     return Y
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_conv_1x1_buffer_path(ox, dtype, monkeypatch):
+    # 1x1 convolutions on the tile engine through the buffer loaders (fp32
+    # columns one by one, bf16 in pixel pairs split into k-chunks as they
+    # are written to LDS) with the Gemm's stage shapes: every tile, ragged
+    # channels and pixel ranges, tiles straddling images, K tails and a K of
+    # one partial unit; against the oracle, and bit-identical to the
+    # gathering loader (OX_CONV_PIPE=0: the same sums in the same order)
+    r = np.random.default_rng(880 + (dtype == "bf16"))
+    for tile in GEMM_TILES:
+        for (N, Cin, H, W, M) in [(3, 48, 4, 7, 40), (2, 16, 10, 10, 96), (2, 576, 2, 7, 130),
+                                  (1, 1000, 1, 50, 72)]:
+            say("conv 1x1 buffer", dtype, tile, (N, Cin, H, W, M))
+            X = synth.round_to(r.standard_normal((N, Cin, H, W)), dtype)
+            Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), dtype)
+            b = synth.round_to(r.uniform(-0.5, 0.5, M), dtype)
+            monkeypatch.setenv("OX_FORCE_KERNEL", "1x1,tile=" + tile)
+            out = {}
+            for pipe in ("1", "0"):
+                monkeypatch.setenv("OX_CONV_PIPE", pipe)
+                out[pipe] = host64(run_conv(ox, X, Wt, b, dtype, (1, 1), (0, 0, 0, 0), (1, 1), 1, "relu"))
+            assert_close(out["1"], oracle.conv2d(X, Wt, b, act="relu"), dtype, "1x1 buffer %s" % tile)
+            assert np.array_equal(out["1"], out["0"]), (tile, (N, Cin, H, W, M))
+            monkeypatch.delenv("OX_CONV_PIPE")
+            monkeypatch.delenv("OX_FORCE_KERNEL")
+
+
 def test_conv_sweep_integer_inputs_exact(ox):
     # fp32 with small integer inputs: every partial sum is exact, so any
     # indexing mistake (tap, pad, stride, dilation, group) shows as a mismatch.
