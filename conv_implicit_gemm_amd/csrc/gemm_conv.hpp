@@ -280,11 +280,12 @@ bool deep_k(int64_t K, int64_t blocks) {
 }
 
 // Stage shape of a launch, BKU x D (K units per stage x stages in flight):
-// 4 x 1 for the small tiles above; two units per stage with two stages in
-// flight for the other tiles up to 64 x 128 once K has 8 units or more (the
-// loads of four units stay in flight across the MMAs: measured 15-18%
-// faster on the 1000-row int8 FFN and QKV Gemms); 1 x 1 otherwise (128 x 128
-// would lose an occupancy level to the registers of a second stage).
+// two units per stage with two stages in flight for tiles up to 64 x 128
+// once K has 8 units or more (the loads of four units stay in flight across
+// the MMAs), 1 x 1 otherwise (128 x 128 would lose an occupancy level to the
+// registers of a second stage).  Measured, bf16 (us): 1000x4096x1024 on
+// 64x128 28.1 / 30.2 / 21.3 for 1x1 / 4x1 / 2x2; 1000x1024x4096 on 32x64
+// 59.8 / 29.1 / 26.8; 256x4096x1024 on 32x64 18.7 / 10.8 / 10.4.
 // OX_GEMM_STAGES ("1x1", "4x1", "2x2") pins one for any tile (measurements).
 template <int DT, int BM, int BN>
 int gemm_stages(const GemmArgs& a) {
@@ -292,10 +293,6 @@ int gemm_stages(const GemmArgs& a) {
     static const char* names[] = {"1x1", "4x1", "2x2"};
     for (int i = 0; i < 3; ++i)
       if (!strcmp(e, names[i])) return i;
-  }
-  if constexpr (deep_k_tile<DT, BM, BN>()) {
-    const int64_t blocks = (int64_t)((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) * a.batch;
-    if (deep_k<DT>(a.K, blocks)) return 1;
   }
   constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
   if (BM * BN <= 64 * 128 && (a.K + KSTEP1 - 1) / KSTEP1 >= 8) return 2;
@@ -321,9 +318,17 @@ bool gemm_buf_ok(const GemmArgs& a) {
 template <int DT, int BM, int BN>
 int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
   const int st = gemm_stages<DT, BM, BN>(a);
-  if (!gemm_buf_ok<DT, BM, BN>(a))
-    return st == 1 ? launch_gemm_tile_k<DT, BM, BN, 4, 1, false>(a, s)
-                   : launch_gemm_tile_k<DT, BM, BN, 1, 1, false>(a, s);
+  if (!gemm_buf_ok<DT, BM, BN>(a)) {
+    // the gathering loaders, one stage in flight: four units per stage for
+    // the small tiles with a long K
+    bool deep = false;
+    if constexpr (deep_k_tile<DT, BM, BN>()) {
+      const int64_t blocks = (int64_t)((a.cols + BN - 1) / BN) * ((a.rows + BM - 1) / BM) * a.batch;
+      deep = deep_k<DT>(a.K, blocks);
+    }
+    return deep || st == 1 ? launch_gemm_tile_k<DT, BM, BN, 4, 1, false>(a, s)
+                           : launch_gemm_tile_k<DT, BM, BN, 1, 1, false>(a, s);
+  }
   switch (st) {
     case 1: return launch_gemm_tile_k<DT, BM, BN, 4, 1, true>(a, s);
     case 2: return launch_gemm_tile_k<DT, BM, BN, 2, 2, true>(a, s);
@@ -673,13 +678,20 @@ int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
   bool deep = false;
   if constexpr (deep_k_tile<DT, BM, BN>()) deep = deep_k<DT>(K, blocks);
   if (kind == 1 && conv_buf_ok<DT>(a)) {
-    // the stage shapes of the Gemm: 4 x 1 where the small tiles go deep,
-    // 2 x 2 for tiles up to 64 x 128 with 8 or more K units
-    constexpr int KSTEP1 = 4 * Traits<DT>::EPC;
-    if constexpr (deep_k_tile<DT, BM, BN>())
-      if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, 2, s);
-    if constexpr (BM * BN <= 64 * 128)
-      if ((K + KSTEP1 - 1) / KSTEP1 >= 8) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, 2, s);
+    // 4 x 1 where the small tiles go deep (the int8 conformer pointwise
+    // conv: 16.3 us against 17.8 us with 2 x 2), else the Gemm's shapes:
+    // 2 x 2 for tiles up to 64 x 128 with 8 or more K units, 1 x 1 otherwise
+    // (OX_GEMM_STAGES pins one)
+    GemmArgs ga;
+    memset(&ga, 0, sizeof(ga));
+    ga.K = (int)K;
+    int st = gemm_stages<DT, BM, BN>(ga);
+    if (deep && !getenv("OX_GEMM_STAGES")) st = 1;
+    if (st == 1) {
+      if constexpr (deep_k_tile<DT, BM, BN>()) return launch_conv_tile_k<DT, BM, BN, 4>(a, 2, s);
+    } else if (st == 2) {
+      if constexpr (BM * BN <= 64 * 128) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, 2, s);
+    }
     return launch_conv_tile_k<DT, BM, BN, 1>(a, 2, s);
   }
   if constexpr (deep_k_tile<DT, BM, BN>())
