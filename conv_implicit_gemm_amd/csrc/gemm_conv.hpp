@@ -345,37 +345,46 @@ int launch_gemm_tile(const GemmArgs& a, hipStream_t s) {
 // alpha, beta*bias and the activation.  32x64 tiles (the tile a problem
 // this small is given), four K units per stage.
 
-template <int DT, bool LK, bool RK>
+template <int DT, bool LK, bool RK, bool BUF>
 __global__ __launch_bounds__(kThreads) void gemm_splitk_kernel(const GemmArgs a, int kslice,
                                                                float* ws) {
   typedef typename Traits<DT>::T T;
-  constexpr int BM = 32, BN = 64, BKU = 4;
+  // buffer loaders: two units x two stages in flight; else four units, one
+  constexpr int BM = 32, BN = 64, BKU = BUF ? 2 : 4, D = BUF ? 2 : 1;
   __shared__ __attribute__((aligned(16))) char smem[2 * (BM + BN) * Lds<BKU>::ROWB];
   const int z = blockIdx.z, row0 = blockIdx.y * BM, col0 = blockIdx.x * BN;
   const int k0 = z * kslice;
   const int Kz = min(kslice, a.K - k0);          // >= 1: the host makes every slice non-empty
   const T* L = (const T*)a.L + (LK ? (int64_t)k0 : (int64_t)k0 * a.ldl);
   const T* R = (const T*)a.R + (RK ? (int64_t)k0 : (int64_t)k0 * a.ldr);
-  typename std::conditional<LK, LoadRowK<DT, BM, BKU>, LoadColK<DT, BM, BKU>>::type la;
-  typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
-  if constexpr (LK) {
-    la.init(L, a.ldl, row0, a.rows, Kz, a.l_vec);
-  } else {
-    const int r = row0 + threadIdx.x % BM;
-    la.init_col(L + r, r < a.rows, a.ldl, Kz);
-  }
-  if constexpr (RK) {
-    lb.init(R, a.ldr, col0, a.cols, Kz, a.r_vec);
-  } else {
-    const int c = col0 + threadIdx.x % BN;
-    lb.init_col(R + c, c < a.cols, a.ldr, Kz);
-  }
   f32x4_t acc[BM / 32][BN / 32];
 #pragma unroll
   for (int i = 0; i < BM / 32; ++i)
 #pragma unroll
     for (int j = 0; j < BN / 32; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  engine_mainloop<DT, BM, BN, BKU>(la, lb, Kz, smem, acc);
+  if constexpr (BUF) {
+    typename std::conditional<LK, LoadRowKB<DT, BM, BKU>, LoadColKB<DT, BM, BKU>>::type la;
+    typename std::conditional<RK, LoadRowKB<DT, BN, BKU>, LoadColKB<DT, BN, BKU>>::type lb;
+    la.init(L, a.ldl, row0, a.rows, Kz);
+    lb.init(R, a.ldr, col0, a.cols, Kz);
+    engine_mainloop<DT, BM, BN, BKU, 0, D>(la, lb, Kz, smem, acc);
+  } else {
+    typename std::conditional<LK, LoadRowK<DT, BM, BKU>, LoadColK<DT, BM, BKU>>::type la;
+    typename std::conditional<RK, LoadRowK<DT, BN, BKU>, LoadColK<DT, BN, BKU>>::type lb;
+    if constexpr (LK) {
+      la.init(L, a.ldl, row0, a.rows, Kz, a.l_vec);
+    } else {
+      const int r = row0 + threadIdx.x % BM;
+      la.init_col(L + r, r < a.rows, a.ldl, Kz);
+    }
+    if constexpr (RK) {
+      lb.init(R, a.ldr, col0, a.cols, Kz, a.r_vec);
+    } else {
+      const int c = col0 + threadIdx.x % BN;
+      lb.init_col(R + c, c < a.cols, a.ldr, Kz);
+    }
+    engine_mainloop<DT, BM, BN, BKU>(la, lb, Kz, smem, acc);
+  }
   float* P = ws + (int64_t)z * a.rows * a.cols;
   for_each_result<BM, BN>(acc, [&](int r, int c, float v) {
     const int row = row0 + r, col = col0 + c;
@@ -405,14 +414,27 @@ template <int DT>
 int launch_gemm_splitk_dt(const GemmArgs& a, int S, int kslice, float* ws, void* stream) {
   hipStream_t s = (hipStream_t)stream;
   dim3 grid((a.cols + 63) / 64, (a.rows + 31) / 32, S);
-  if (a.l_kmajor && a.r_kmajor)
-    hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+  // (the slices' bases move by a multiple of four units: the buffer
+  // loaders' alignment and offset conditions hold for every slice)
+  if (gemm_buf_ok<DT, 32, 64>(a)) {
+    if (a.l_kmajor && a.r_kmajor)
+      hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, true, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+    else if constexpr (DT == DT_F32) {
+      if (a.l_kmajor)
+        hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, false, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+      else if (a.r_kmajor)
+        hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, true, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+      else
+        hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, false, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+    }
+  } else if (a.l_kmajor && a.r_kmajor)
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, true, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
   else if (a.l_kmajor)
-    hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, true, false, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
   else if (a.r_kmajor)
-    hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, true>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, true, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
   else
-    hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
+    hipLaunchKernelGGL((gemm_splitk_kernel<DT, false, false, false>), grid, dim3(kThreads), 0, s, a, kslice, ws);
   const int64_t total = (int64_t)a.rows * a.cols;
   const int nb = (int)std::min<int64_t>(2048, (total + kThreads - 1) / kThreads);
   const float* wsc = ws;

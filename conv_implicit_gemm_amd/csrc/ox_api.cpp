@@ -480,6 +480,9 @@ static GemmSplit gemm_split_plan(ox_dtype t, int64_t M, int64_t N, int64_t K) {
   if (blocks >= 256) return g;
   const int64_t kstep = t == OX_F32 ? 64 : 128;   // four 64-byte units per stage
   const int64_t stages = (K + kstep - 1) / kstep;
+  // below 64 units the single pass (two stages in flight) wins: bf16 M = 64 /
+  // 256, K = 1024: 7.7 / 7.8 us against 8.5 / 9.2 us split
+  if (stages < 16) return g;
   int64_t S = std::min<int64_t>({8, 256 / blocks, stages / 4});
   if (S < 2) return g;
   const int64_t kslice = (stages + S - 1) / S * kstep;

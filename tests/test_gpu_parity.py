@@ -139,8 +139,9 @@ def test_gemm_long_k_few_tiles(ox, dtype, ta, tb):
 def test_gemm_split_k_workspace(ox, dtype, ta, tb):
     # few output tiles, long K: K slices with fp32 partials in the caller's
     # workspace, then the ordered sum with alpha, beta*bias and GELU; ragged K
-    # (a short last slice) and the MLP's 4096-deep row shape
-    for (M, N, K) in [(64, 200, 1500), (64, 1024, 4096), (37, 70, 1777)]:
+    # (a short last slice) and the MLP's 4096-deep row shape (split-K is
+    # planned from 64 K units on)
+    for (M, N, K) in [(64, 200, 2600), (64, 1024, 4096), (37, 70, 2777)]:
         say("gemm split-K", dtype, ta, tb, (M, N, K))
         r = np.random.default_rng(170 + 2 * ta + tb + K)
         A = synth.round_to(r.standard_normal((K, M) if ta else (M, K)), dtype)
