@@ -658,6 +658,61 @@ struct LoadIm2col {
   }
 };
 
+// The fp32 im2col operand through a raw buffer: the thread keeps one output
+// pixel (column) and computes each element's offset from its (c, kh, kw);
+// taps in the padding, k past K and columns past the range read zeros
+// (kPastK), so the loads carry no branch.  The chunk's first k is split
+// with two small exact divisions per stage, the rest by stepping.
+template <int BCOLS, int BKU>
+struct LoadIm2colB {
+  enum { EPC = 4, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         STEP = kThreads / BCOLS, NCH = (CPR + STEP - 1) / STEP };
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vimg;        // byte offset of this column's image (and group) plane 0
+  int ih0, iw0;
+  bool valid;
+  int H, W, HW, kH, kW, KK, dh, dw, K;
+  u32x4_t r[NCH];
+
+  __device__ __forceinline__ void load(int k0) {
+    const int ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      const int kb = k0 + ch * EPC;
+      int c = div_small(kb, KK);
+      int rr = kb - c * KK;
+      int kh = div_small(rr, kW);
+      int kw = rr - kh * kW;
+      uint32_t w[4];
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const int ih = ih0 + kh * dh, iw = iw0 + kw * dw;
+        const bool ok = valid && (CPR % STEP == 0 || ch < CPR) && kb + j < K &&
+                        (unsigned)ih < (unsigned)H && (unsigned)iw < (unsigned)W;
+        w[j] = __builtin_amdgcn_raw_buffer_load_b32(
+            rs, ok ? vimg + (uint32_t)((c * HW + ih * W + iw) * 4) : kPastK, 0, 0);
+        if (++kw == kW) {
+          kw = 0;
+          if (++kh == kH) {
+            kh = 0;
+            ++c;
+          }
+        }
+      }
+      r[i] = u32x4_t{w[0], w[1], w[2], w[3]};
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int col = threadIdx.x % BCOLS, ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      if (CPR % STEP == 0 || ch < CPR) *(u32x4_t*)(lds + col * ROWB + ch * 16) = r[i];
+    }
+  }
+};
+
 // ------------------------------------------------------------ the kernel --
 
 template <int DT, int BM, int BN> struct WaveTile {

@@ -475,7 +475,9 @@ int launch_gemm_dt(const GemmArgs& a, int tile, void* stream) {
 // KIND 0: implicit GEMM (im2col gathered on the fly); KIND 1: 1x1, stride 1,
 // no pad, where column n of image img is X[img, c, p] with p = n % (H*W);
 // KIND 2: the same 1x1 through the branch-free buffer loaders with D stages
-// in flight (fp32 operands whose byte offsets stay below 2^31).
+// in flight (fp32 columns one by one, bf16 in pixel pairs, int8 in groups of
+// four; operands whose byte offsets stay below 2^31); KIND 3: the fp32
+// implicit GEMM through them.
 
 template <int DT, int BM, int BN, int BKU, int KIND, bool FLIP, bool WZ, int D = 1>
 __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I8View& q) {
@@ -494,7 +496,32 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
     for (int j = 0; j < BN / 32; ++j) acc[i][j] = Acc{0, 0, 0, 0};
   int ks[WaveTile<DT, BM, BN>::FN] = {};
 
-  if constexpr (KIND == 2) {
+  if constexpr (KIND == 3) {
+    // fp32 implicit GEMM through the buffer loaders
+    LoadRowKB<DT, BM, BKU> la;
+    la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K);
+    LoadIm2colB<BN, BKU> lb;
+    const int n = col0 + threadIdx.x % BN;
+    const bool nvalid = n < NP;
+    const int img = nvalid ? n / HoWo : 0;
+    const int p = nvalid ? n - img * HoWo : 0;
+    const int oh = p / a.Wo, ow = p - (p / a.Wo) * a.Wo;
+    lb.rs = operand_rsrc(a.X);
+    lb.vimg = (uint32_t)(((int64_t)img * a.C + (int64_t)g * cpg) * HW * 4);
+    lb.ih0 = oh * a.sh - a.pt;
+    lb.iw0 = ow * a.sw - a.pl;
+    lb.valid = nvalid;
+    lb.H = a.H;
+    lb.W = a.W;
+    lb.HW = HW;
+    lb.kH = a.kH;
+    lb.kW = a.kW;
+    lb.KK = KK;
+    lb.dh = a.dh;
+    lb.dw = a.dw;
+    lb.K = K;
+    engine_mainloop<DT, BM, BN, BKU, 0, D>(la, lb, K, smem, acc, ks);
+  } else if constexpr (KIND == 2) {
     LoadRowKB<DT, BM, BKU> la;
     la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K);
     // this thread's column (fp32), pair of columns (bf16) or group of four
@@ -666,8 +693,18 @@ int launch_conv_tile_k(const ConvArgs& a, int kind, hipStream_t s) {
   const int64_t NP = (int64_t)a.N * a.Ho * a.Wo;
   dim3 grid((unsigned)((NP + BN - 1) / BN), (Mpg + BM - 1) / BM, a.group);
   if constexpr (D > 1) {
+    if constexpr (DT == DT_F32)
+      if (kind == 3) {
+        hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 3, D>), grid, dim3(kThreads), 0, s, a);
+        return (int)hipGetLastError();
+      }
     hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2, D>), grid, dim3(kThreads), 0, s, a);
   } else {
+    if constexpr (DT == DT_F32)
+      if (kind == 3) {
+        hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 3>), grid, dim3(kThreads), 0, s, a);
+        return (int)hipGetLastError();
+      }
     if (kind == 2)
       hipLaunchKernelGGL((conv_kernel<DT, BM, BN, BKU, 2>), grid, dim3(kThreads), 0, s, a);
     else if (kind == 1)
@@ -699,7 +736,13 @@ int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
   const int64_t K = (int64_t)(a.C / a.group) * a.kH * a.kW;
   bool deep = false;
   if constexpr (deep_k_tile<DT, BM, BN>()) deep = deep_k<DT>(K, blocks);
-  if (kind == 1 && conv_buf_ok<DT>(a)) {
+  // fp32 implicit GEMM through the buffer loaders (KIND 3): weight rows of
+  // whole 16-byte vectors, X below 2^31 bytes
+  const bool im2col_buf = DT == DT_F32 && kind == 0 && a.w_vec &&
+                          (int64_t)a.N * a.C * a.H * a.W * 4 < ((int64_t)1 << 31) &&
+                          !(getenv("OX_CONV_PIPE") && !strcmp(getenv("OX_CONV_PIPE"), "0"));
+  if ((kind == 1 && conv_buf_ok<DT>(a)) || im2col_buf) {
+    const int bk = im2col_buf ? 3 : 2;
     // 4 x 1 where the small tiles go deep (the int8 conformer pointwise
     // conv: 16.3 us against 17.8 us with 2 x 2), else the Gemm's shapes:
     // 2 x 2 for tiles up to 64 x 128 with 8 or more K units, 1 x 1 otherwise
@@ -710,11 +753,11 @@ int launch_conv_tile(const ConvArgs& a, int kind, hipStream_t s) {
     int st = gemm_stages<DT, BM, BN>(ga);
     if (deep && !getenv("OX_GEMM_STAGES")) st = 1;
     if (st == 1) {
-      if constexpr (deep_k_tile<DT, BM, BN>()) return launch_conv_tile_k<DT, BM, BN, 4>(a, 2, s);
+      if constexpr (deep_k_tile<DT, BM, BN>()) return launch_conv_tile_k<DT, BM, BN, 4>(a, bk, s);
     } else if (st == 2) {
-      if constexpr (BM * BN <= 64 * 128) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, 2, s);
+      if constexpr (BM * BN <= 64 * 128) return launch_conv_tile_k<DT, BM, BN, 2, 2>(a, bk, s);
     }
-    return launch_conv_tile_k<DT, BM, BN, 1>(a, 2, s);
+    return launch_conv_tile_k<DT, BM, BN, 1>(a, bk, s);
   }
   if constexpr (deep_k_tile<DT, BM, BN>())
     if (deep) return launch_conv_tile_k<DT, BM, BN, 4>(a, kind, s);

@@ -342,6 +342,38 @@ def test_conv_1x1_buffer_path(ox, dtype, monkeypatch):
             monkeypatch.delenv("OX_FORCE_KERNEL")
 
 
+def test_conv_igemm_f32_buffer_path(ox, monkeypatch):
+    # fp32 implicit GEMM through the buffer loaders (each element's offset
+    # from its (c, kh, kw), padding taps and k past K read as zeros) with the
+    # Gemm's stage shapes: every tile, strides, pads, dilation, groups,
+    # kernels of 1 to 7 taps a side; against the oracle and bit-identical to
+    # the gathering loader (OX_CONV_PIPE=0: the same sums in the same order)
+    r = np.random.default_rng(890)
+    geoms = [(2, 16, 9, 11, 24, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1),
+             (1, 12, 13, 10, 20, 3, 3, (2, 2), (2, 1, 0, 1), (1, 1), 2),
+             (2, 8, 12, 12, 8, 3, 3, (1, 1), (2, 2, 2, 2), (2, 2), 1),
+             (2, 64, 14, 14, 96, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1),
+             (1, 3, 30, 30, 16, 7, 7, (2, 2), (3, 3, 3, 3), (1, 1), 1),
+             (1, 130, 7, 7, 70, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 1),
+             (2, 20, 8, 9, 30, 1, 3, (1, 2), (0, 1, 0, 1), (1, 1), 1)]
+    for tile in GEMM_TILES:
+        for (N, Cin, H, W, M, kh, kw, st, pads, dil, g) in geoms:
+            say("igemm f32 buffer", tile, (N, Cin, H, W, M, kh, kw, st, pads, dil, g))
+            X = synth.round_to(r.standard_normal((N, Cin, H, W)), "f32")
+            Wt = synth.round_to(r.standard_normal((M, Cin // g, kh, kw)) / math.sqrt(Cin // g * kh * kw), "f32")
+            b = synth.round_to(r.uniform(-0.5, 0.5, M), "f32")
+            monkeypatch.setenv("OX_FORCE_KERNEL", "igemm,tile=" + tile)
+            out = {}
+            for pipe in ("1", "0"):
+                monkeypatch.setenv("OX_CONV_PIPE", pipe)
+                out[pipe] = host64(run_conv(ox, X, Wt, b, "f32", st, pads, dil, g, "relu"))
+            assert_close(out["1"], oracle.conv2d(X, Wt, b, st, pads, dil, g, act="relu"), "f32",
+                         "igemm buffer %s" % tile)
+            assert np.array_equal(out["1"], out["0"]), (tile, (N, Cin, H, W, M, kh, kw))
+            monkeypatch.delenv("OX_CONV_PIPE")
+            monkeypatch.delenv("OX_FORCE_KERNEL")
+
+
 def test_conv_sweep_integer_inputs_exact(ox):
     # fp32 with small integer inputs: every partial sum is exact, so any
     # indexing mistake (tap, pad, stride, dilation, group) shows as a mismatch.
