@@ -155,7 +155,26 @@ int choose_tile_igemm_f32(int64_t rows, int64_t cols, int64_t z) {
   return TILE_32x64;
 }
 
-enum TileRule { RULE_CONV = 0, RULE_GEMM = 1, RULE_IGEMM_F32 = 2 };
+// fp32 1x1 with K >= 64: every column element is its own 4-byte load, and
+// 64x64 (else 32x64) tiles from 256 blocks measured best (ResNet-50 batch 32,
+// us against the generic rule: 256->64 at 56² 46.3 (59.5), 256->1024 at 14²
+// 44.5 (52.5), 1024->256 at 14² 48.7 (50.9)); a K below 64 keeps the generic
+// rule (16->96 at 112², output-bound: 128x128 99.2 against 64x64 113.1).
+int choose_tile_1x1_f32(int64_t rows, int64_t cols, int64_t z) {
+  static const int order[] = {TILE_64x64, TILE_32x64};
+  for (int t : order) {
+    const int bm = tile_bm(t), bn = tile_bn(t);
+    if (rows <= 32 && bm > 32) continue;
+    // (a last row tile at most half full: 32-row tiles waste nothing there;
+    // MobileNetV2's 96-channel projections 21.9-28.4 us against 24.5-32.6)
+    if (bm == 64 && rows % 64 != 0 && rows % 64 <= 32) continue;
+    const int64_t blocks = ((rows + bm - 1) / bm) * ((cols + bn - 1) / bn) * z;
+    if (blocks >= 256) return t;
+  }
+  return TILE_32x64;
+}
+
+enum TileRule { RULE_CONV = 0, RULE_GEMM = 1, RULE_IGEMM_F32 = 2, RULE_1X1_F32 = 3 };
 
 ox_status pick_tile(const char* fn, const Force& f, int64_t rows, int64_t cols, int64_t z,
                     int* tile, int rule = RULE_CONV) {
@@ -163,7 +182,8 @@ ox_status pick_tile(const char* fn, const Force& f, int64_t rows, int64_t cols, 
   *tile = f.tile >= 0 ? f.tile
           : rule == RULE_GEMM ? choose_tile_gemm(rows, cols, z)
           : rule == RULE_IGEMM_F32 ? choose_tile_igemm_f32(rows, cols, z)
-                                   : choose_tile(rows, cols, z);
+          : rule == RULE_1X1_F32 ? choose_tile_1x1_f32(rows, cols, z)
+                                 : choose_tile(rows, cols, z);
   if ((rows + tile_bm(*tile) - 1) / tile_bm(*tile) > 65535 || z > 65535)
     return fail(OX_ERR_UNSUPPORTED, "%s: %lld rows x batch %lld exceed the launch grid", fn,
                 (long long)rows, (long long)z);
@@ -372,7 +392,8 @@ static ox_status conv_dispatch(const char* fn, const ox_conv_desc* d, ConvArgs& 
   int tile = -1;
   if (kind == KIND_IGEMM || kind == KIND_1X1) {
     st = pick_tile(fn, f, d->M / d->group, d->N * a.Ho * a.Wo, d->group, &tile,
-                   kind == KIND_IGEMM && a.dt == DT_F32 ? RULE_IGEMM_F32 : RULE_CONV);
+                   a.dt != DT_F32 ? RULE_CONV : kind == KIND_IGEMM ? RULE_IGEMM_F32
+                   : d->C / d->group >= 64 ? RULE_1X1_F32 : RULE_CONV);
     if (st) return st;
   } else if (f.tile != -1) {
     return fail(OX_ERR_INVALID_ARG, "%s: a tile does not apply to the %s kernel", fn, kind_name(kind));
@@ -1010,7 +1031,8 @@ ox_status ox_conv2d_variant(ox_dtype t, const ox_conv_desc* d, char* name, size_
   int tile = -1;
   if (kind == KIND_IGEMM || kind == KIND_1X1) {
     st = pick_tile(fn, f, d->M / d->group, d->N * Ho * Wo, d->group, &tile,
-                   kind == KIND_IGEMM && t == OX_F32 ? RULE_IGEMM_F32 : RULE_CONV);
+                   t != OX_F32 ? RULE_CONV : kind == KIND_IGEMM ? RULE_IGEMM_F32
+                   : d->C / d->group >= 64 ? RULE_1X1_F32 : RULE_CONV);
     if (st) return st;
   }
   static const char* dtn[] = {"f32", "bf16", "i8"};
