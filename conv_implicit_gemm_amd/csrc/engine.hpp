@@ -534,6 +534,54 @@ struct LoadColK2B {
   }
 };
 
+// [K, cols] bf16 operand, one column per thread at a per-thread byte offset
+// (a 1x1 convolution on an odd plane, where pixel pairs are not aligned):
+// each element is one 2-byte load and one 2-byte LDS write, so no
+// instruction touches a loaded register before the stage that stores it.
+template <int BCOLS, int BKU>
+struct LoadColK1B {
+  enum { EPC = 8, CPR = Lds<BKU>::CPR, ROWB = Lds<BKU>::ROWB,
+         STEP = kThreads / BCOLS, NCH = (CPR + STEP - 1) / STEP };
+  static_assert(kThreads % BCOLS == 0, "columns must divide the block");
+  __amdgpu_buffer_rsrc_t rs;
+  uint32_t vo;          // this column's byte offset at k = 0, or kPastK
+  uint32_t ldb;         // row stride in bytes
+  int K;
+  uint16_t e[NCH][EPC];
+
+  __device__ __forceinline__ void init_off(const uint16_t* base, uint32_t off, bool ok, int64_t ld, int K_) {
+    rs = operand_rsrc(base);
+    vo = ok ? off : kPastK;
+    ldb = (uint32_t)(ld * 2);
+    K = K_;
+  }
+  __device__ __forceinline__ void load(int k0) {
+    const int ch0 = threadIdx.x / BCOLS;
+    const int soff = k0 * (int)ldb;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+#pragma unroll
+      for (int j = 0; j < EPC; ++j) {
+        const int kk = ch * EPC + j;
+        const bool ok = vo != kPastK && (CPR % STEP == 0 || ch < CPR) && k0 + kk < K;
+        e[i][j] = __builtin_amdgcn_raw_buffer_load_b16(rs, ok ? vo + kk * ldb : kPastK, soff, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ void store(char* lds) const {
+    const int col = threadIdx.x % BCOLS, ch0 = threadIdx.x / BCOLS;
+#pragma unroll
+    for (int i = 0; i < NCH; ++i) {
+      const int ch = ch0 + i * STEP;
+      if (CPR % STEP == 0 || ch < CPR) {
+#pragma unroll
+        for (int j = 0; j < EPC; ++j) *(uint16_t*)(lds + col * ROWB + ch * 16 + j * 2) = e[i][j];
+      }
+    }
+  }
+};
+
 // [K, cols] int8 operand whose columns come in aligned groups of four
 // consecutive bytes (a 1x1 convolution's pixels, the plane a multiple of
 // four): a task is one group of four columns and one 16-k chunk, loaded as

@@ -524,19 +524,28 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
   } else if constexpr (KIND == 2) {
     LoadRowKB<DT, BM, BKU> la;
     la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K);
-    // this thread's column (fp32), pair of columns (bf16) or group of four
-    // columns (int8)
-    constexpr int CG = DT == DT_I8 ? 4 : DT == DT_BF16 ? 2 : 1;
-    const int n = col0 + CG * (threadIdx.x % (BN / CG));
-    const bool nvalid = n < NP;
-    const int img = nvalid ? n / HoWo : 0;
-    const uint32_t off = (uint32_t)((((int64_t)img * a.C + (int64_t)g * cpg) * HW + (n - img * HoWo)) *
-                                    (int64_t)sizeof(T));
-    typename std::conditional<DT == DT_I8, LoadColK4B<BN, BKU, FLIP>,
-                              typename std::conditional<DT == DT_BF16, LoadColK2B<BN, BKU>,
-                                                        LoadColKB<DT, BN, BKU, FLIP>>::type>::type lb;
-    lb.init_off((const T*)a.X, nvalid ? off : 0u, nvalid, HW, K);
-    engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0, D>(la, lb, K, smem, acc, ks);
+    // this thread's column (fp32; bf16 on an odd plane), pair of columns
+    // (bf16) or group of four columns (int8)
+    auto run = [&](auto lbk, auto cgk) {
+      typedef typename decltype(lbk)::type LB;
+      constexpr int CG = decltype(cgk)::value;
+      const int n = col0 + CG * (threadIdx.x % (BN / CG));
+      const bool nvalid = n < NP;
+      const int img = nvalid ? n / HoWo : 0;
+      const uint32_t off = (uint32_t)((((int64_t)img * a.C + (int64_t)g * cpg) * HW + (n - img * HoWo)) *
+                                      (int64_t)sizeof(T));
+      LB lb;
+      lb.init_off((const T*)a.X, nvalid ? off : 0u, nvalid, HW, K);
+      engine_mainloop<DT, BM, BN, BKU, WZ ? 2 : 0, D>(la, lb, K, smem, acc, ks);
+    };
+    if constexpr (DT == DT_I8) {
+      run(std::common_type<LoadColK4B<BN, BKU, FLIP>>{}, std::integral_constant<int, 4>{});
+    } else if constexpr (DT == DT_BF16) {
+      if (HW % 2 == 0) run(std::common_type<LoadColK2B<BN, BKU>>{}, std::integral_constant<int, 2>{});
+      else run(std::common_type<LoadColK1B<BN, BKU>>{}, std::integral_constant<int, 1>{});
+    } else {
+      run(std::common_type<LoadColKB<DT, BN, BKU, FLIP>>{}, std::integral_constant<int, 1>{});
+    }
   } else {
   LoadRowK<DT, BM, BKU> la;
   la.init((const T*)a.Wt + (int64_t)g * Mpg * K, K, row0, Mpg, K, a.w_vec);
@@ -716,14 +725,16 @@ int launch_conv_tile_k(const ConvArgs& a, int kind, hipStream_t s) {
 }
 
 // Whether a 1x1 convolution takes the buffer loaders (KIND 2): fp32; bf16
-// or int8 with planes of whole 4-byte groups of pixels (2 / 4 of them) and a
-// 4-byte aligned X; weight rows of whole 16-byte vectors; X below 2^31
-// bytes.  OX_CONV_PIPE=0 turns it off (measurements).
+// (pixel pairs on even planes with a 4-byte aligned X, single pixels
+// otherwise); int8 with planes of whole 4-byte groups and a 4-byte aligned X;
+// weight rows of whole 16-byte vectors; X below 2^31 bytes.  OX_CONV_PIPE=0
+// turns it off (measurements).
 template <int DT>
 bool conv_buf_ok(const ConvArgs& a) {
   constexpr int ES = DT == DT_F32 ? 4 : DT == DT_BF16 ? 2 : 1;
   if (!a.w_vec) return false;
-  if (((a.H * a.W * ES) % 4 != 0 || ((uintptr_t)a.X) % 4 != 0)) return false;
+  if (DT == DT_BF16 && (a.H * a.W) % 2 == 0 && ((uintptr_t)a.X) % 4 != 0) return false;
+  if (DT == DT_I8 && ((a.H * a.W) % 4 != 0 || ((uintptr_t)a.X) % 4 != 0)) return false;
   if (const char* e = getenv("OX_CONV_PIPE"))
     if (!strcmp(e, "0")) return false;
   return (int64_t)a.N * a.C * a.H * a.W * ES < ((int64_t)1 << 31);

@@ -295,11 +295,14 @@ bool pwd_preferred(const ConvArgs& a) {
   return (a.C % 64 == 0 || (int64_t)a.N * a.H * a.W >= 65536) && conv_pwd_applicable(a);
 }
 
-// The register-staged 1x1 kernel, except on an odd plane with a short K: its
-// channel runs are then single pixels and the tile engine's kernel is faster
-// (measured 1.37-1.39x on 160->960 channels at 7x7).
+// The register-staged 1x1 kernel, except on an odd plane with a short K or
+// few output channels: its channel runs are then single pixels and the tile
+// engine's kernel (buffer loaders, one 2-byte element per load) is faster
+// (MobileNetV2 at 7x7: 160->960 16.2 -> 10.3 us, 576->160 15.6 -> 9.2,
+// 960->160 17.7 -> 12.8, 960->320 22.4 -> 17.2; ResNet-50's 2048->512 stays
+// on pw: 24.1 against 30.7).
 bool pw_preferred(const ConvArgs& a) {
-  return !((a.H * a.W) % 2 == 1 && a.C <= 192) && conv_pw_applicable(a);
+  return !((a.H * a.W) % 2 == 1 && (a.C <= 192 || a.M <= 384)) && conv_pw_applicable(a);
 }
 
 ox_status select_conv(const char* fn, const ox_conv_desc* d, const ConvArgs& a, const Force& f,

@@ -139,10 +139,11 @@ def test_variant_selection_sweep(ox, monkeypatch):
             # the DMA-staged kernel where the plane has an even pixel count
             # (the fake pointers are aligned) and C is a multiple of 64 or the
             # layer has at least 65536 pixels, else the register-staged one,
-            # except on an odd plane with C <= 192 (the tile engine's 1x1)
+            # except on an odd plane with C <= 192 or M <= 384 (the tile
+            # engine's 1x1)
             if (H * W) % 2 == 0 and (C % 64 == 0 or N * H * W >= 65536):
                 want = "pwd/"
-            elif (H * W) % 2 == 1 and C <= 192:
+            elif (H * W) % 2 == 1 and (C <= 192 or M <= 384):
                 want = "1x1/"
             else:
                 want = "pw/"
