@@ -520,27 +520,28 @@ __global__ __launch_bounds__(kThreads) void conv3x3_reduce(const ConvArgs a, con
   const int tid = threadIdx.x;
   const int lane = tid & 63, part = tid >> 6;
   const int l32 = lane & 31, kg = lane >> 5;
+  const TileGeo geo = tile_geo(a, pp, tile_id, BM);
+  const int M = a.M;
+  // the bias of each value's channel, then every slice's partials
+  float bvk[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int fc = ((part * PER + k) >> 2) % FC;
+    bvk[k] = bias_bf16_at(a.bias, M, geo.m0 + wm * SUBM + fc * 32 + l32);
+  }
   f32x4_t sum[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) sum[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int s = 0; s < pp.splits; ++s) {
-    const f32x4_t* src =
-        (const f32x4_t*)pp.ws + ((int64_t)tile_id * pp.splits + s) * (kThreads * NV) + w * 64 + lane;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) sum[k] += src[(part * PER + k) * kThreads];
-  }
-  const TileGeo geo = tile_geo(a, pp, tile_id, BM);
-  const int M = a.M;
-  const uint16_t* bias = (const uint16_t*)a.bias;
+  add_slices<PER>((const f32x4_t*)pp.ws + (int64_t)tile_id * pp.splits * (kThreads * NV) + w * 64 + lane +
+                      part * PER * kThreads,
+                  kThreads * NV, kThreads, pp.splits, sum);
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = part * PER + k;             // value index (fp*FC + fc)*4 + g
       const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
-      const int m = geo.m0 + wm * SUBM + fc * 32 + l32;
-      const float bv = (bias && m < M) ? bf16_to_f32(bias[m]) : 0.0f;
+      const float bv = bvk[k];
       const uint32_t lo = pack_bf16x2(act_c<ACT>(sum[k][0] + bv), act_c<ACT>(sum[k][1] + bv));
       const uint32_t hi = pack_bf16x2(act_c<ACT>(sum[k][2] + bv), act_c<ACT>(sum[k][3] + bv));
       *(u32x2_t*)(E + (fc * 32 + l32) * EROW + fp * 32 + 8 * g + 4 * kg) = u32x2_t{lo, hi};

@@ -580,19 +580,18 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
   const int tid = threadIdx.x;
   const int lane = tid & 63, part = tid >> 6;     // first-pass lane, quarter of its values
   const int l32 = lane & 31, kg = lane >> 5;
-  f32x4_t sum[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) sum[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 2
-  for (int s = 0; s < pl.splits; ++s) {
-    const f32x4_t* src = partial_base<FP, FC>(pl.ws, (int64_t)t * pl.splits + s) + w * 64 + lane;
-#pragma unroll
-    for (int k = 0; k < PER; ++k) sum[k] += src[(part * PER + k) * kThreads];
-  }
   const int pb = t / pl.nmb;
   const int q0 = pb * BN + wn * SUBN, m0 = (t - pb * pl.nmb) * BM + wm * SUBM;
   const int HW = a.H * a.W, M = a.M, Q = a.N * HW;
-  const uint16_t* bias = (const uint16_t*)a.bias;
+  // the bias of each value's channel, then every slice's partials
+  float bvk[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) bvk[k] = bias_bf16_at(a.bias, M, m0 + (((part * PER + k) >> 2) % FC) * 32 + l32);
+  f32x4_t sum[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) sum[k] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  add_slices<PER>(partial_base<FP, FC>(pl.ws, (int64_t)t * pl.splits) + w * 64 + lane + part * PER * kThreads,
+                  kThreads * NV, kThreads, pl.splits, sum);
   const uint16_t* R = (const uint16_t*)a.res;   // residual, added after the bias
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
@@ -601,7 +600,7 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
       const int i = part * PER + k;             // value index (fp*FC + fc)*4 + g
       const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
       const int m = m0 + fc * 32 + l32;
-      const float bv = (bias && m < M) ? bf16_to_f32(bias[m]) : 0.0f;
+      const float bv = bvk[k];
       float v[4] = {sum[k][0] + bv, sum[k][1] + bv, sum[k][2] + bv, sum[k][3] + bv};
       if (R && m < M) {
 #pragma unroll

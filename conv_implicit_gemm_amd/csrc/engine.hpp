@@ -377,6 +377,40 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t operand_rsrc(const void* p) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, 0x7FFFFFFF, 0x00020000);
 }
 
+// bf16 bias of channel m as fp32: 0 where there is no bias or m >= M.  A raw
+// buffer load (a buffer of 0 bytes when bias is null), so no branch makes
+// later loads wait for it.
+__device__ __forceinline__ float bias_bf16_at(const void* bias, int M, int m) {
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(bias), (short)0, bias ? M * 2 : 0, 0x00020000);
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, m < M ? (uint32_t)m * 2u : kPastK, 0, 0));
+}
+
+// Second pass of split-K: sum[k] = ((p_0[k] + p_1[k]) + ...) + p_{S-1}[k], in
+// slice order, slice s at src + s * stride float4 values and its value k at
+// [k * kstride].  The loads of G slices go out together (a slice index past S
+// re-reads the last slice, whose value is then not added), so up to G slices
+// cost one round trip.
+template <int PER>
+__device__ __forceinline__ void add_slices(const f32x4_t* src, int64_t stride, int kstride, int S,
+                                           f32x4_t (&sum)[PER]) {
+  constexpr int G = PER <= 2 ? 8 : 4;
+  for (int s0 = 0; s0 < S; s0 += G) {
+    f32x4_t v[G][PER];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const f32x4_t* p = src + (int64_t)min(s0 + j, S - 1) * stride;
+#pragma unroll
+      for (int k = 0; k < PER; ++k) v[j][k] = p[k * kstride];
+    }
+    __builtin_amdgcn_sched_barrier(0);   // every load issued before the first add
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int k = 0; k < PER; ++k) sum[k] = s0 + j < S ? sum[k] + v[j][k] : sum[k];
+  }
+}
+
 // [rows, K] operand, row stride ld, K a multiple of EPC and rows 16-byte
 // aligned (a chunk is all inside K or all past it).
 template <int DT, int BROWS, int BKU, bool FLIP = false>

@@ -112,21 +112,6 @@ __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const P
   const int c = p - (int)fdiv(pl.c_div, (uint32_t)p) * a.C;
   const int H = a.H, Ho = a.Ho, Wo = a.Wo;
 
-  // taps and bias of channel c
-  float wf[9], bias = 0.f;
-  uint32_t wb[9];
-  if constexpr (DT == DT_F32) {
-    const float* w = (const float*)a.Wt + c * 9;
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wf[t] = w[t];
-    if (a.bias) bias = ((const float*)a.bias)[c];
-  } else {
-    const uint16_t* w = (const uint16_t*)a.Wt + c * 9;
-#pragma unroll
-    for (int t = 0; t < 9; ++t) wb[t] = w[t];
-    if (a.bias) bias = bf16_to_f32(((const uint16_t*)a.bias)[c]);
-  }
-
   // every input row of the band
   const __amdgpu_buffer_rsrc_t xr =
       __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(a.X), (short)0, (int)pl.x_bytes, 0x00020000);
@@ -139,6 +124,25 @@ __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const P
     const int r = r0 + rr;
     const bool in = valid && r >= 0 && r < H;
     load_row<ND>(xr, in ? seg0 + (uint32_t)r * rowb : kOutside, d[rr]);
+  }
+
+  // taps and bias of channel c, issued behind the rows so that both arrive
+  // in one round trip (the bias through a raw buffer of 0 bytes when there
+  // is none: no branch, whose merge would make the rows wait for it)
+  float wf[9], bias;
+  uint32_t wb[9];
+  const __amdgpu_buffer_rsrc_t br = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(a.bias), (short)0, a.bias ? a.C * E : 0, 0x00020000);
+  if constexpr (DT == DT_F32) {
+    const float* w = (const float*)a.Wt + c * 9;
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wf[t] = w[t];
+    bias = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(br, (uint32_t)c * 4u, 0, 0));
+  } else {
+    const uint16_t* w = (const uint16_t*)a.Wt + c * 9;
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wb[t] = w[t];
+    bias = bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(br, (uint32_t)c * 2u, 0, 0));
   }
 
   // halo columns of each input row (zero at the plane's left / right edge)

@@ -792,16 +792,18 @@ def test_pw_persistent_blocks(ox, grid, monkeypatch):
 
 
 @pytest.mark.parametrize("fp", ["1", "2"])
-@pytest.mark.parametrize("splits", [2, 3, 5])
+@pytest.mark.parametrize("splits", [2, 3, 5, 9])
 def test_pw_split_k(ox, splits, fp, monkeypatch):
     # split-K: slices of the channel range write fp32 partials, a second
-    # kernel adds them in slice order -- same result as the oracle, and
+    # kernel adds them in slice order (its loads go out eight slices at a
+    # time: 9 slices take two groups) -- same result as the oracle, and
     # bit-identical from run to run
     monkeypatch.setenv("OX_FORCE_KERNEL", "pw")
     monkeypatch.setenv("OX_PW_SPLITS", str(splits))
     monkeypatch.setenv("OX_PW_FP", fp)
     r = np.random.default_rng(600 + splits)
-    for ci, (N, Cin, H, W, M) in enumerate([(2, 512, 7, 7, 200), (3, 320, 6, 6, 64), (1, 256, 9, 9, 130)]):
+    for ci, (N, Cin, H, W, M) in enumerate([(2, 512, 7, 7, 200), (3, 320, 6, 6, 64), (1, 256, 9, 9, 130),
+                                            (1, 1152, 5, 5, 72)]):
         X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
         Wt = synth.round_to(r.standard_normal((M, Cin, 1, 1)) / math.sqrt(Cin), "bf16")
         b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
@@ -1342,7 +1344,8 @@ def test_patch_split_k(ox, cfg, monkeypatch):
     r = np.random.default_rng(5150 + int(cfg[0]) * 10 + int(cfg[2]))
     ran = 0
     for ci, (N, Cin, H, W, M, s, splits) in enumerate([
-            (3, 128, 7, 7, 96, 1, 2), (2, 160, 10, 9, 70, 2, 3), (4, 96, 5, 6, 130, 1, 3)]):
+            (3, 128, 7, 7, 96, 1, 2), (2, 160, 10, 9, 70, 2, 3), (4, 96, 5, 6, 130, 1, 3),
+            (1, 288, 6, 6, 40, 1, 9)]):
         X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
         Wt = synth.round_to(r.standard_normal((M, Cin, 3, 3)) / math.sqrt(9 * Cin), "bf16")
         b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
