@@ -640,21 +640,78 @@ __device__ __forceinline__ void conv_tile(const ConvArgs& a, char* smem, const I
     T* Y = (T*)a.Y;
     const T* bias = (const T*)a.bias;
     const T* R = (const T*)a.res;     // residual, added after the bias (may be Y itself)
-    // one row fragment at a time: its four channels' biases are read before
-    // its stores.  (A residual, rare on this kernel, is read element by
-    // element before each store: R may be Y, and hoisting more of its loads
-    // costs the kernel its occupancy in registers.)
+    // (A residual, rare on this kernel, is read element by element before
+    // each store: R may be Y, and hoisting more of its loads costs the
+    // kernel its occupancy in registers.)
+    // bf16 without a residual, HoWo even and Y 4-byte aligned: lanes l and
+    // l^1 hold the same four channels at two adjacent pixels, so one
+    // exchange (DPP quad_perm 1,0,3,2) per two values gives each lane a pixel
+    // pair of two of the channels, and every store writes 4 bytes (half the
+    // store instructions of element stores).  A pair never straddles two
+    // images (HoWo even), and it is inside the tile's columns whenever its
+    // first pixel is (NP even).
+    const bool pairs = DT == DT_BF16 && (HoWo & 1) == 0 && (((uintptr_t)Y) & 3) == 0;
     auto body = [&](auto with_res) {
       constexpr bool RES = decltype(with_res)::value;
+      // The biases of a row fragment are read before its stores (a wait
+      // for a load issued after stores waits for those stores too): every
+      // fragment's before the first store on tiles of up to two row
+      // fragments; one fragment at a time on 128-row tiles, whose registers
+      // would otherwise cost a block per CU.
+      constexpr bool PRE = FM <= 2;
+      float rball[PRE ? FM : 1][4];
+      auto load_rb = [&](float (&rb)[4], int fm) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          rb[i] = bias ? to_f32(bias[g * Mpg + min(row0 + lane_row<BM>(fm, i), Mpg - 1)]) : 0.0f;
+      };
+      if constexpr (PRE) {
+#pragma unroll
+        for (int fm = 0; fm < FM; ++fm) load_rb(rball[fm], fm);
+        if constexpr (!RES) wait_vmem();
+      }
       with_act(a.act, [&](auto act_k) {
         constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
         for (int fm = 0; fm < FM; ++fm) {
-          float rb[4];
+          if constexpr (!PRE) {
+            load_rb(rball[0], fm);
+            if constexpr (!RES) wait_vmem();
+          }
+          const float* rb = rball[PRE ? fm : 0];
+          if constexpr (DT == DT_BF16 && !RES) {
+            if (pairs) {
+              const bool odd = threadIdx.x & 1;
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            rb[i] = bias ? to_f32(bias[g * Mpg + min(row0 + lane_row<BM>(fm, i), Mpg - 1)]) : 0.0f;
-          if constexpr (!RES) wait_vmem();
+              for (int fn = 0; fn < FN; ++fn) {
+                float o[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                  o[i] = acc[fm][fn][i];
+                  if (bias) o[i] += rb[i];
+                  o[i] = act_c<ACT>(o[i]);
+                }
+                // the even lane keeps channels 0, 1 of its four, the odd
+                // lane channels 2, 3; each sends the partner the other two
+                auto xchg = [](float v) {
+                  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+                };
+                const float r0 = xchg(odd ? o[0] : o[2]), r1 = xchg(odd ? o[1] : o[3]);
+                const int ce = col0 + (lane_col<BN>(fn) & ~1);
+                const int ma = row0 + lane_row<BM>(fm, odd ? 2 : 0);
+                const int64_t base = cbase[fn] - (odd ? 1 : 0);
+                if (ce < NP) {
+                  if (ma < Mpg)
+                    *(uint32_t*)(Y + base + (int64_t)(g * Mpg + ma) * HoWo) =
+                        odd ? pack_bf16x2(r0, o[2]) : pack_bf16x2(o[0], r0);
+                  if (ma + 1 < Mpg)
+                    *(uint32_t*)(Y + base + (int64_t)(g * Mpg + ma + 1) * HoWo) =
+                        odd ? pack_bf16x2(r1, o[3]) : pack_bf16x2(o[1], r1);
+                }
+              }
+              continue;
+            }
+          }
 #pragma unroll
           for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
