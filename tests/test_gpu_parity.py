@@ -315,6 +315,39 @@ def run_conv(ox, X, Wt, b, dtype, s, pads, d, g, act, ws=False):
     return Y
 
 
+@pytest.mark.parametrize("kind", ["1x1", "igemm"])
+def test_conv_bf16_pair_stores(ox, kind, monkeypatch):
+    # the tile engine's bf16 conv epilogue: with an even output plane and a
+    # 4-byte aligned Y, neighbouring lanes exchange values and store pixel
+    # pairs; an odd plane or a Y two bytes off alignment takes element
+    # stores.  Every tile, ragged channel counts (M not a multiple of 4),
+    # pixel ranges that end inside a tile and grouped convolutions; against
+    # the oracle, and the pair and element paths bit-identical.
+    r = np.random.default_rng(2024 + (kind == "igemm"))
+    k = 1 if kind == "1x1" else 3
+    pads = (0, 0, 0, 0) if k == 1 else (1, 1, 1, 1)
+    for tile in GEMM_TILES:
+        monkeypatch.setenv("OX_FORCE_KERNEL", "%s,tile=%s" % (kind, tile))
+        for (N, Cin, H, W, M, g) in [(2, 32, 6, 6, 70, 1), (3, 16, 5, 5, 37, 1), (1, 64, 4, 10, 130, 2),
+                                     (2, 24, 7, 8, 6, 3), (2, 48, 9, 8, 96, 1)]:
+            if kind == "1x1" and g > 1:
+                continue      # the 1x1 path takes ungrouped convolutions only
+            X = synth.round_to(r.standard_normal((N, Cin, H, W)), "bf16")
+            Wt = synth.round_to(r.standard_normal((M, Cin // g, k, k)) / math.sqrt(Cin // g * k * k), "bf16")
+            b = synth.round_to(r.uniform(-0.5, 0.5, M), "bf16")
+            ref = oracle.conv2d(X, Wt, b, (1, 1), pads, (1, 1), g, "relu6")
+            outs = []
+            for yoff in (0, 1):
+                say("bf16 pair stores", kind, tile, (N, Cin, H, W, M, g), "Y offset", yoff)
+                Y = misaligned(nan_like((N, M, H, W), "bf16"), yoff)
+                ox.ox_conv2d_fused(dev(X, "bf16"), dev(Wt, "bf16"), dev(b, "bf16"), (1, 1), pads, (1, 1), g,
+                                   "relu6", Y=Y)
+                torch.cuda.synchronize()
+                assert_close(host64(Y), ref, "bf16", "%s %s case %s offset %d" % (kind, tile, (N, Cin, H, W, M, g), yoff))
+                outs.append(Y.clone())
+            assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_conv_1x1_buffer_path(ox, dtype, monkeypatch):
     # 1x1 convolutions on the tile engine through the buffer loaders (fp32
