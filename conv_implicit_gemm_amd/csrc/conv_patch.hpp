@@ -59,54 +59,6 @@ constexpr int patch_upt(int P, int BM) {
              : 1;
 }
 
-// Writes staged bf16 outputs to Y.  E[m - mlo][slot - slo] holds channel
-// m0 + m, pixel slot `slot` of the tile (slot = i*ppi + e: image img0 + i,
-// output pixel oh0*Wo + e of its plane) for m in [mlo, mhi) and slots in
-// [slo, shi); each image's run of output pixels is written with the widest
-// aligned vector stores.  Threads tid = 0 .. nthr-1 share the work.
-__device__ __forceinline__ void store_runs(const ConvArgs& a, const PatchPlan& pp, const uint16_t* E,
-                                           int erow, int img0, int imgs_here, int oh0, int rows_here,
-                                           int m0, int mlo, int mhi, int slo, int shi, int tid, int nthr) {
-  uint16_t* Y = (uint16_t*)a.Y;
-  const int HoWo = a.Ho * a.Wo;
-  const int L = rows_here * a.Wo;
-  const int g0 = oh0 * a.Wo;
-  const int ppi = pp.TR * a.Wo;
-  const int M = a.M;
-  int V = 8;
-  while (V > 1 && ((HoWo % V) || (g0 % V) || (ppi % V) || (L % V) || (slo % V) ||
-                   (((uintptr_t)Y) % (2 * V))))
-    V >>= 1;
-  const int mc = mhi - mlo;
-  if (mc <= 0) return;
-  for (int i = 0; i < imgs_here; ++i) {
-    const int a0 = max(slo, i * ppi), a1 = min(shi, i * ppi + L);
-    if (a1 <= a0) continue;
-    const int per_run = (a1 - a0 + V - 1) / V;
-    // a power-of-two group of threads per channel row, the rows of a pass
-    // side by side (nthr is a power of two): no division per store
-    int lg = 0;
-    while ((1 << lg) < per_run && (1 << lg) < nthr) ++lg;
-    const int tpr = 1 << lg, rpp = nthr >> lg;
-    for (int m = tid >> lg; m < mc; m += rpp)
-    for (int c = tid & (tpr - 1); c < per_run; c += tpr) {
-      const int slot = a0 + c * V;
-      const uint16_t* src = E + m * erow + (slot - slo);
-      uint16_t* dst = Y + ((int64_t)(img0 + i) * M + m0 + mlo + m) * HoWo + g0 + (slot - i * ppi);
-      if (V == 8) {
-        const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
-        *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
-      } else if (V == 4) {
-        *(u32x2_t*)dst = *(const u32x2_t*)src;
-      } else if (V == 2) {
-        *(uint32_t*)dst = *(const uint32_t*)src;
-      } else {
-        *dst = *src;
-      }
-    }
-  }
-}
-
 // Geometry of logical tile `tile_id`: first output channel, first image,
 // first output row, rows and images actually present.  The logical order
 // cuts the (pixel block x channel block) grid into ga x gb equal rectangles,
@@ -507,14 +459,14 @@ __global__ __launch_bounds__(kThreads, (WM * FC * 32 == 64 ? 2 : 1)) void conv3x
 
 // Second pass of split-K: one block per (tile, wave of the first pass); its
 // 256 threads split that wave's partial values four ways, add the slices in
-// slice order, then bias, activation, bf16, LDS staging and the runs of the
-// wave's 32*FC channels x 32*FP pixel slots.
+// slice order, then bias, activation, bf16 and stores straight from the
+// registers (four consecutive slots of one channel per value, as the first
+// pass's direct epilogue writes them).
 template <int WM, int WN, int FP, int FC>
 __global__ __launch_bounds__(kThreads) void conv3x3_reduce(const ConvArgs a, const PatchPlan pp) {
   constexpr int BM = 32 * WM * FC;
-  constexpr int SUBM = 32 * FC, SUBN = 32 * FP, EROW = SUBN + 8;
+  constexpr int SUBM = 32 * FC;
   constexpr int NV = FP * FC * 4, PER = NV / 4;
-  __shared__ __attribute__((aligned(16))) uint16_t E[SUBM * EROW];
   const int tile_id = blockIdx.x >> 2, w = blockIdx.x & 3;
   const int wm = w / WN, wn = w - (w / WN) * WN;
   const int tid = threadIdx.x;
@@ -535,23 +487,37 @@ __global__ __launch_bounds__(kThreads) void conv3x3_reduce(const ConvArgs a, con
   add_slices<PER>((const f32x4_t*)pp.ws + (int64_t)tile_id * pp.splits * (kThreads * NV) + w * 64 + lane +
                       part * PER * kThreads,
                   kThreads * NV, kThreads, pp.splits, sum);
+  uint16_t* Y = (uint16_t*)a.Y;
+  const int ppi = pp.TR * a.Wo, HoWo = a.Ho * a.Wo;
+  const int Lb = geo.rows_here * a.Wo, g0 = geo.oh0 * a.Wo;
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
       const int i = part * PER + k;             // value index (fp*FC + fc)*4 + g
       const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
-      const float bv = bvk[k];
-      const uint32_t lo = pack_bf16x2(act_c<ACT>(sum[k][0] + bv), act_c<ACT>(sum[k][1] + bv));
-      const uint32_t hi = pack_bf16x2(act_c<ACT>(sum[k][2] + bv), act_c<ACT>(sum[k][3] + bv));
-      *(u32x2_t*)(E + (fc * 32 + l32) * EROW + fp * 32 + 8 * g + 4 * kg) = u32x2_t{lo, hi};
+      const int tile = wn * FP + fp;
+      const int m = geo.m0 + wm * SUBM + fc * 32 + l32;
+      if (tile >= pp.NT || m >= M) continue;
+      const int slot = tile * 32 + 8 * g + 4 * kg;
+      const int ii = div_small(slot, ppi);
+      const int e = slot - ii * ppi;            // position in image ii's band
+      float v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = act_c<ACT>(sum[k][j] + bvk[k]);
+      const int64_t off = ((int64_t)(geo.img0 + ii) * M + m) * HoWo + g0 + e;
+      if (ii < geo.imgs_here && e + 3 < Lb && (off & 3) == 0) {
+        *(u32x2_t*)(Y + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int ij = div_small(slot + j, ppi), ej = slot + j - ij * ppi;
+          if (ij < geo.imgs_here && ej < Lb)
+            Y[((int64_t)(geo.img0 + ij) * M + m) * HoWo + g0 + ej] = (uint16_t)(pack_bf16x2(v[j], 0.f) & 0xffffu);
+        }
+      }
     }
   });
-  __syncthreads();
-  const int mlo = wm * SUBM, mhi = min(mlo + SUBM, M - geo.m0);
-  const int slo = wn * SUBN, shi = min(slo + SUBN, pp.NT * 32);
-  store_runs(a, pp, E, EROW, geo.img0, geo.imgs_here, geo.oh0, geo.rows_here, geo.m0, mlo, mhi, slo,
-             shi, tid, kThreads);
 }
 
 template <int WM, int WN, int FP>

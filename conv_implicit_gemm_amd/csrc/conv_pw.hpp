@@ -21,9 +21,9 @@
 // tiles to occupy the chip -- one of S slices of a tile's channel range
 // (split-K): a slice writes its fp32 partial tile to a workspace and
 // conv1x1_reduce adds the S partials in slice order (deterministic) and runs
-// the epilogue.  The epilogue (bias, activation, bf16 rounding) stages the
-// tile in LDS as [channel][pixel] and writes each channel's pixels with
-// aligned vector stores.
+// the epilogue from its registers.  The first pass's epilogue (bias,
+// activation, bf16 rounding) stages the tile in LDS as [channel][pixel] and
+// writes each channel's pixels with aligned vector stores.
 #pragma once
 
 #include "engine.hpp"
@@ -565,16 +565,15 @@ __global__ __launch_bounds__(kThreads, (KC == 32 && !RES) ? 3 : 2) void conv1x1_
 // Second pass of split-K.  One block per (tile, wave of the first pass):
 // its 256 threads split that wave's 64 x FP*FC*4 float4 partial values four
 // ways (more loads in flight per CU), add the S slices in slice order, apply
-// bias and activation, stage the 32*FC x 32*FP sub-tile in LDS as
-// [channel][pixel] and write the channel runs.
+// bias, residual and activation and store straight from the registers (each
+// value is four consecutive pixels of one channel).
 template <int WM, int WN, int FP, int FC>
 __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, const PwPlan pl) {
   constexpr int BN = 32 * WN * FP, BM = 32 * WM * FC;
-  constexpr int SUBM = 32 * FC, SUBN = 32 * FP, EROW = SUBN + 8;
+  constexpr int SUBM = 32 * FC, SUBN = 32 * FP;
   constexpr int NV = FP * FC * 4;           // float4 values per lane of the first pass
   constexpr int PER = NV / 4;               // of those, per thread here
   static_assert(NV % 4 == 0, "four threads per lane");
-  __shared__ __attribute__((aligned(16))) uint16_t E[SUBM * EROW];
   const int t = blockIdx.x >> 2, w = blockIdx.x & 3;
   const int wm = w / WN, wn = w - (w / WN) * WN;
   const int tid = threadIdx.x;
@@ -593,6 +592,8 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
   add_slices<PER>(partial_base<FP, FC>(pl.ws, (int64_t)t * pl.splits) + w * 64 + lane + part * PER * kThreads,
                   kThreads * NV, kThreads, pl.splits, sum);
   const uint16_t* R = (const uint16_t*)a.res;   // residual, added after the bias
+  uint16_t* Y = (uint16_t*)a.Y;
+  const bool y8 = (((uintptr_t)Y) & 7) == 0;
   with_act(a.act, [&](auto act_k) {
     constexpr int ACT = decltype(act_k)::value;
 #pragma unroll
@@ -600,48 +601,40 @@ __global__ __launch_bounds__(kThreads) void conv1x1_reduce(const ConvArgs a, con
       const int i = part * PER + k;             // value index (fp*FC + fc)*4 + g
       const int g = i & 3, fc = (i >> 2) % FC, fp = (i >> 2) / FC;
       const int m = m0 + fc * 32 + l32;
+      const int qb = q0 + fp * 32 + 8 * g + 4 * kg;   // the value's first pixel
+      if (m >= M || qb >= Q) continue;
       const float bv = bvk[k];
       float v[4] = {sum[k][0] + bv, sum[k][1] + bv, sum[k][2] + bv, sum[k][3] + bv};
-      if (R && m < M) {
+      if (R) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const int q = q0 + fp * 32 + 8 * g + 4 * kg + j;
+          const int q = qb + j;
           if (q < Q) {
             const int n = q / HW;
             v[j] += bf16_to_f32(R[((int64_t)n * M + m) * HW + (q - n * HW)]);
           }
         }
       }
-      const uint32_t lo = pack_bf16x2(act_c<ACT>(v[0]), act_c<ACT>(v[1]));
-      const uint32_t hi = pack_bf16x2(act_c<ACT>(v[2]), act_c<ACT>(v[3]));
-      *(u32x2_t*)(E + (fc * 32 + l32) * EROW + fp * 32 + 8 * g + 4 * kg) = u32x2_t{lo, hi};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = act_c<ACT>(v[j]);
+      // four consecutive pixels of one plane at an 8-byte aligned address
+      // go out as one store, any others element by element
+      const int n = qb / HW, p = qb - n * HW;
+      const int64_t off = ((int64_t)n * M + m) * HW + p;
+      if (y8 && qb + 3 < Q && p + 3 < HW && (off & 3) == 0) {
+        *(u32x2_t*)(Y + off) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+      } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = qb + j;
+          if (q < Q) {
+            const int nj = q / HW;
+            Y[((int64_t)nj * M + m) * HW + (q - nj * HW)] = (uint16_t)(pack_bf16x2(v[j], 0.f) & 0xffffu);
+          }
+        }
+      }
     }
   });
-  __syncthreads();
-  if (m0 >= M) return;
-  uint16_t* Y = (uint16_t*)a.Y;
-  const int mvalid = min(SUBM, M - m0);
-  const int V = pl.V;
-  const int per_row = SUBN / V;
-  for (int it = tid; it < mvalid * per_row; it += kThreads) {
-    const int m = it / per_row;
-    const int e = (it - m * per_row) * V;
-    const int q = q0 + e;
-    if (q >= Q) continue;
-    const int n = q / HW;
-    const uint16_t* src = E + m * EROW + e;
-    uint16_t* dst = Y + ((int64_t)n * M + m0 + m) * HW + (q - n * HW);
-    if (V == 8) {
-      const u32x2_t p0 = *(const u32x2_t*)src, p1 = *(const u32x2_t*)(src + 4);
-      *(u32x4_t*)dst = u32x4_t{p0[0], p0[1], p1[0], p1[1]};
-    } else if (V == 4) {
-      *(u32x2_t*)dst = *(const u32x2_t*)src;
-    } else if (V == 2) {
-      *(uint32_t*)dst = *(const uint32_t*)src;
-    } else {
-      *dst = *src;
-    }
-  }
 }
 
 template <int WM, int WN, int FP, int KC>
