@@ -452,10 +452,20 @@ def measured_traffic(kernel, workload, dtype):
 
 # --------------------------------------------------------- machine facts --
 
+def under_profiler():
+    """True inside a rocprofv3 run: its preloaded library initialises the GPU
+    in every child process, so a child must not go on to exec another
+    program (rocm-smi starts through /usr/bin/env python3)."""
+    return "rocprof" in os.environ.get("LD_PRELOAD", "") or any(k.startswith("ROCPROF") for k in os.environ)
+
+
 def gpu_clocks():
     """Current shader and memory clock levels as rocm-smi reports them (a
-    child process reading the driver's tables), or None."""
+    child process reading the driver's tables), or None (also under a
+    profiler, where the child is not started)."""
     import subprocess
+    if under_profiler():
+        return None
     try:
         r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
                            timeout=20)

@@ -53,15 +53,15 @@ PwPlan make(const ConvArgs& a, int WM, int KC, int FP) {
   p.lds = std::max(2 * (BM + BN) * row, BM * (BN + 8) * 2) + p.bias_lds;
   if (a.res) p.lds = std::max(p.lds, BM * (BN + 4) * 4 + p.bias_lds);   // fp32 staging of the residual epilogue
   // split-K when the tiles alone would leave many CUs idle and the channel
-  // range is long: about 192 work units of at least four chunks (a sweep
-  // of the ResNet-50 1x1 layers at batch 32: two slices for 98 tiles x 16
-  // chunks, four for 52 tiles x 32 chunks; more slices cost more in partial
-  // traffic than they gain)
+  // range is long: about 384 work units of at least four chunks (ResNet-50's
+  // 2048->512 1x1 at 7x7, batch 32, 104 tiles x 32 chunks: 1 / 2 / 3 / 4
+  // slices 34.1 / 22.4 / 21.9 / 20.2 us per call, the second pass storing
+  // from registers)
   const int64_t tiles = (int64_t)p.npb * p.nmb;
   const int nchunks = std::max(1, a.C / KC);   // (a C that KC does not divide is rejected by valid)
   int target = 1;
   if (a.ws && tiles < 192 && nchunks >= 4)
-    target = (int)std::min<int64_t>((192 + tiles - 1) / tiles, nchunks / 4);
+    target = (int)std::min<int64_t>((384 + tiles - 1) / tiles, nchunks / 4);
   if (const char* e = getenv("OX_PW_SPLITS"))
     if (a.ws) target = std::max(1, std::min(nchunks, atoi(e)));
   p.cps = (nchunks + target - 1) / target;
