@@ -467,7 +467,10 @@ __global__ __launch_bounds__(kThreads) void conv3x3_reduce(const ConvArgs a, con
   constexpr int BM = 32 * WM * FC;
   constexpr int SUBM = 32 * FC;
   constexpr int NV = FP * FC * 4, PER = NV / 4;
-  const int tile_id = blockIdx.x >> 2, w = blockIdx.x & 3;
+  // the first pass's order (xcd_tile over tile-major units): each XCD adds
+  // the partials of the tiles its L2 wrote
+  const int r = xcd_tile(blockIdx.x, gridDim.x);
+  const int tile_id = r >> 2, w = r & 3;
   const int wm = w / WN, wn = w - (w / WN) * WN;
   const int tid = threadIdx.x;
   const int lane = tid & 63, part = tid >> 6;
