@@ -2,7 +2,7 @@
 // BatchNormalization + activation (a BatchNorm that cannot be folded into a
 // convolution, e.g. the pre-activation BN -> ReLU of a ResNet-v2 block),
 // MaxPool and GlobalAveragePool (NCHW).  No MFMA: each reads its input once
-// and writes its output once, so each is judged against HBM bandwidth.
+// and writes its output once, so each is measured against HBM bandwidth.
 #include <algorithm>
 #include <cmath>
 
