@@ -26,7 +26,9 @@
 // v_mov_dpp each) and are zero at the plane's edges (the first and last lane
 // of a band row).
 //
-// Arithmetic, fp32: 9 FMAs per output.  bf16: the inputs stay packed as
+// Arithmetic, fp32: 9 FMAs per output.  bf16 rows of odd width: one output
+// per lane (2-byte loads), widened to fp32 and 9 FMAs per output.  Other
+// bf16: the inputs stay packed as
 // pairs at even columns, and v_dot2_f32_bf16 (two bf16 products and an fp32
 // addend) takes two taps per instruction: an output at an even column is
 // (w1, w2).(x[c], x[c+1]) + (0, w0).(x[c-2], x[c-1]); one at an odd column is
@@ -73,9 +75,12 @@ __device__ __forceinline__ uint32_t from_right(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x130, 0xf, 0xf, false);   // wave_shl:1
 }
 
+// ND dwords of a segment (ND = 0: one 2-byte element, zero-extended)
 template <int ND>
 __device__ __forceinline__ void load_row(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t* d) {
-  if constexpr (ND == 1) {
+  if constexpr (ND == 0) {
+    d[0] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+  } else if constexpr (ND == 1) {
     d[0] = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
   } else if constexpr (ND == 2) {
     const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
@@ -94,10 +99,14 @@ template <int DT, int ST, int V, int TR>
 __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const Plan pl) {
   constexpr int E = DT == DT_F32 ? 4 : 2;
   constexpr int LB = V * ST * E;                         // bytes of a lane's input row segment
-  constexpr int ND = LB / 4;                             // its dwords
+  constexpr int ND = LB / 4;                             // its dwords (0: one bf16 element)
+  constexpr int NR = ND > 0 ? ND : 1;                    // registers of a row segment
   constexpr int RIN = ST == 1 ? TR + 2 : 2 * TR + 1;     // input rows of a band
-  static_assert(LB == 4 || LB == 8 || LB == 16, "segment load width");
-  static_assert(DT == DT_F32 || ST == 2 || V % 2 == 0, "bf16 stride-1 segments hold whole pairs");
+  // bf16, stride 1, one output per lane: rows of odd width (pairs would
+  // straddle rows), arithmetic in fp32 on the widened elements
+  constexpr bool WIDE1 = DT == DT_BF16 && ST == 1 && V == 1;
+  static_assert(LB == 4 || LB == 8 || LB == 16 || (WIDE1 && LB == 2), "segment load width");
+  static_assert(DT == DT_F32 || ST == 2 || V % 2 == 0 || WIDE1, "bf16 stride-1 segments hold whole pairs");
   typedef typename std::conditional<DT == DT_F32, float, uint16_t>::type T;
 
   const int lane = threadIdx.x & 63;
@@ -118,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const P
   const uint32_t seg0 = (uint32_t)p * (uint32_t)(H * a.W * E) + (uint32_t)(j * LB);
   const uint32_t rowb = (uint32_t)(a.W * E);
   const int r0 = oh0 * ST - 1;
-  uint32_t d[RIN][ND];
+  uint32_t d[RIN][NR];
 #pragma unroll
   for (int rr = 0; rr < RIN; ++rr) {
     const int r = r0 + rr;
@@ -150,7 +159,7 @@ __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const P
   uint32_t hl[RIN], hr[RIN];
 #pragma unroll
   for (int rr = 0; rr < RIN; ++rr) {
-    const uint32_t l = from_left(d[rr][ND - 1]);
+    const uint32_t l = from_left(d[rr][NR - 1]);
     hl[rr] = first ? 0u : l;
     if constexpr (ST == 1) {
       const uint32_t r = from_right(d[rr][0]);
@@ -159,8 +168,12 @@ __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const P
   }
 
   // bf16 tap pairs per kernel row: (w1, w2), (0, w0), (w0, w1), (w2, 0)
+  // (one output per lane: the taps widened instead)
   uint32_t pa[3], pb[3], pc[3], pd[3];
-  if constexpr (DT == DT_BF16) {
+  if constexpr (WIDE1) {
+#pragma unroll
+    for (int t = 0; t < 9; ++t) wf[t] = bf16_to_f32((uint16_t)wb[t]);
+  } else if constexpr (DT == DT_BF16) {
 #pragma unroll
     for (int kh = 0; kh < 3; ++kh) {
       pa[kh] = wb[3 * kh + 1] | (wb[3 * kh + 2] << 16);
@@ -183,7 +196,11 @@ __global__ __launch_bounds__(kThreads) void dw3x3_rows(const ConvArgs a, const P
       for (int kh = 0; kh < 3; ++kh) {
         const int rr = ST * o + kh;
         const uint32_t* x = d[rr];
-        if constexpr (DT == DT_BF16 && ST == 1) {
+        if constexpr (WIDE1) {
+          acc[0] = fmaf(wf[3 * kh], __uint_as_float(hl[rr] << 16), acc[0]);
+          acc[0] = fmaf(wf[3 * kh + 1], __uint_as_float(x[0] << 16), acc[0]);
+          acc[0] = fmaf(wf[3 * kh + 2], __uint_as_float(hr[rr] << 16), acc[0]);
+        } else if constexpr (DT == DT_BF16 && ST == 1) {
 #pragma unroll
           for (int m = 0; m < ND; ++m) {
             acc[2 * m] = dot2(x[m], pa[kh], acc[2 * m]);
@@ -271,16 +288,17 @@ bool make_plan(const ConvArgs& a, Plan* out) {
   // row holds Wo * s of them (stride 2 needs an even width; bf16 stride 1
   // keeps pairs at even columns, so an even width too)
   if (a.W != a.Wo * s) return false;
-  if (bf && s == 1 && a.W % 2 != 0) return false;
+  // bf16 at stride 1: pairs on even widths, one output per lane on odd ones
+  const bool odd1 = bf && s == 1 && a.W % 2 != 0;
   const int64_t P = (int64_t)a.N * a.C, HW = (int64_t)a.H * a.W;
   if (P * HW * E >= ((int64_t)1 << 31) || P * a.Ho * a.Wo >= ((int64_t)1 << 31)) return false;
   int vmax = 8;
   if (const char* e = getenv("OX_DWR_V")) vmax = atoi(e);
   Plan p;
   p.V = 0;
-  for (int V = 8; V >= 1; V /= 2) {
+  for (int V = odd1 ? 1 : 8; V >= 1; V /= 2) {
     const int lb = V * s * E;
-    if (V > vmax || lb > 16 || lb < 4 || (bf && s == 1 && V % 2)) continue;
+    if (V > vmax || lb > 16 || (lb < 4 && !odd1) || (bf && s == 1 && V % 2 && !odd1)) continue;
     if (a.Wo % V || a.Wo / V > 64 || ((uintptr_t)a.X % lb)) continue;
     p.V = V;
     break;
@@ -319,7 +337,8 @@ int launch(const ConvArgs& a, const Plan& p, hipStream_t s) {
     if (a.sh == 1) {
       if (p.V == 8) return launch_v<DT_BF16, 1, 8>(a, p, s);
       if (p.V == 4) return launch_v<DT_BF16, 1, 4>(a, p, s);
-      return launch_v<DT_BF16, 1, 2>(a, p, s);
+      if (p.V == 2) return launch_v<DT_BF16, 1, 2>(a, p, s);
+      return launch_v<DT_BF16, 1, 1>(a, p, s);
     }
     if (p.V == 4) return launch_v<DT_BF16, 2, 4>(a, p, s);
     if (p.V == 2) return launch_v<DT_BF16, 2, 2>(a, p, s);

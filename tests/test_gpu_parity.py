@@ -531,8 +531,9 @@ DWR_CASES = [
     (1, 5, 9, 10, 1), (2, 3, 13, 6, 2), (1, 2, 1, 2, 1), (2, 7, 3, 2, 2), (1, 300, 4, 4, 1),
     (1, 2, 6, 512, 1), (1, 3, 900, 4, 1), (2, 5, 21, 40, 1),
 ]
-# fp32 only: odd widths at stride 1 (lanes of one output each)
-DWR_F32_ODD = [(2, 12, 7, 7, 1), (1, 3, 5, 9, 1), (2, 5, 11, 23, 1)]
+# odd widths at stride 1 (lanes of one output each; bf16 2-byte loads),
+# up to 63 lanes a row
+DWR_ODD = [(2, 12, 7, 7, 1), (1, 3, 5, 9, 1), (2, 5, 11, 23, 1), (1, 4, 6, 63, 1)]
 
 
 @pytest.mark.parametrize("tr,vmax", [(None, None), ("4", None), ("8", None), ("8", "2"), ("4", "1")])
@@ -547,7 +548,7 @@ def test_dwr_cases(ox, dtype, tr, vmax, monkeypatch):
         monkeypatch.setenv("OX_DWR_TR", tr)
     if vmax:
         monkeypatch.setenv("OX_DWR_V", vmax)
-    cases = DWR_CASES + (DWR_F32_ODD if dtype == "f32" else [])
+    cases = DWR_CASES + DWR_ODD
     for ci, (N, Cc, H, W, st) in enumerate(cases):
         act = ["relu6", "none", "relu", "gelu"][ci % 4]
         r = np.random.default_rng(5100 + ci)
@@ -576,13 +577,14 @@ def test_dwr_cases(ox, dtype, tr, vmax, monkeypatch):
 
 def test_dwr_selection_and_misalignment(ox, monkeypatch):
     # the row kernel is chosen for 3x3 pads-1 depthwise convs it applies to;
-    # bf16 with an odd width, other pads, or an X whose alignment admits no
-    # segment load take the staged-band kernel; a Y off its store width is
-    # written element by element
+    # rows wider than 64 lanes of one output (bf16, odd width), other pads,
+    # or an X whose alignment admits no segment load take the staged-band
+    # kernel; a Y off its store width is written element by element
     assert ox.ox_conv2d_variant("bf16", 2, 32, 56, 56, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
     assert ox.ox_conv2d_variant("f32", 2, 32, 56, 56, 32, 3, 3, (2, 2), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
     assert ox.ox_conv2d_variant("f32", 2, 32, 7, 7, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
-    assert ox.ox_conv2d_variant("bf16", 2, 32, 7, 7, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dw/")
+    assert ox.ox_conv2d_variant("bf16", 2, 32, 7, 7, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dwr/")
+    assert ox.ox_conv2d_variant("bf16", 2, 32, 9, 65, 32, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 32).startswith("dw/")
     assert ox.ox_conv2d_variant("bf16", 2, 32, 8, 8, 32, 3, 3, (1, 1), (0, 0, 0, 0), (1, 1), 32).startswith("dw/")
     assert ox.ox_conv2d_variant("bf16", 1, 4, 8, 1040, 4, 3, 3, (1, 1), (1, 1, 1, 1), (1, 1), 4).startswith("dw/")
     r = np.random.default_rng(5300)
