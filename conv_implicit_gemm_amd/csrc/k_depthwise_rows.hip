@@ -307,9 +307,11 @@ bool make_plan(const ConvArgs& a, Plan* out) {
   p.nseg = a.Wo / p.V;
   p.gpw = 64 / p.nseg;
   // four output rows per band: with inputs coming from HBM, four beat eight
-  // on every MobileNetV2 layer measured (more, shorter-lived waves; the
-  // extra halo rows are L2 hits); eight on request
-  p.TR = 4;
+  // on every MobileNetV2 layer of 14 rows or more (more, shorter-lived
+  // waves; the extra halo rows are L2 hits); eight where they cover a plane
+  // of 5 to 8 rows in one band (the 7x7 layers: 11.5 -> 10.3 us bf16); eight
+  // on request
+  p.TR = a.Ho > 4 && a.Ho <= 8 ? 8 : 4;
   if (const char* e = getenv("OX_DWR_TR")) p.TR = atoi(e) == 8 ? 8 : 4;
   p.nb = (a.Ho + p.TR - 1) / p.TR;
   if (P * p.nb >= ((int64_t)1 << 31)) return false;
